@@ -1,0 +1,16 @@
+"""CPU oracle for the TokenGate gated-prefill path.
+
+TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
+benchmark's CPU-baseline leg.  It shares no code with the HIP library.
+"""
+from .tokengate_ref import (  # noqa: F401
+    compact,
+    gate_score,
+    gated_attention,
+    gated_attention_gate_form,
+    score_rows,
+    seq_rmsnorm,
+    temperature_ratio,
+    topk_select,
+    widen,
+)

@@ -1,0 +1,273 @@
+"""Plain CPU oracle for the TokenGate gated-prefill path (fp64).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path never does, and it
+shares no code with the HIP library.
+
+Source: "TokenGate: Adapting LLMs for Fast and Memory-Efficient Prefill with
+Learned Token Pruning" (the paper), Section 4 ("Scoring Network", "Top-K
+Selector", token-gated attention with its "Head-wise" and "Temperature
+Scaling" paragraphs, and "Putting everything together") and Appendix C.4.
+The paper's display equations did not survive extraction; every formula below
+is the plainest reading of the surrounding prose, and the readings are listed
+where they are used.
+
+Every function is the definition written out, in float64, over the exact
+values the GPU sees (bf16 inputs are widened exactly).  Library primitives
+(matrix products, a stable sort) serve as single steps; nothing is blocked,
+fused or reordered beyond processing independent rows in chunks to bound
+memory.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+closed forms, invariants stated by the paper, torch CPU library routines on
+special cases, and brute force on tiny inputs.  The temperature's log-ratio
+form (Eq. 7) is a reading of the prose; it is pinned to that reading's closed
+form and to the paper's statement that the temperature is 1 at full context,
+but the reading itself is not fixed by the paper.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LOG2E = 1.4426950408889634
+
+
+def widen(x) -> np.ndarray:
+    """Exact float64 copy of an fp32 array or of bf16 bit patterns (uint16)."""
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Eq. 1 + Eq. 3 (first half): row RMSNorm of the post-attention residual and
+# the scoring MLP.  Paper, Section 4, "Scoring Network"; Appendix C.4 (the
+# scorer reads the normalised residual after layer L's mixer).
+#
+# Readings: RMSNorm with weight w and eps inside the square root; the MLP is
+# Linear(d,h) + b1 -> SiLU -> Linear(h,1) + b2 (the activation named by the
+# workload shapes "d->h->1 SiLU").
+# --------------------------------------------------------------------------
+def score_rows(rows, norm_w, W1, b1, w2, b2, eps_row: float) -> np.ndarray:
+    """Raw score b~ for each given residual row ``rows[R, d]`` -> ``[R]``."""
+    a = widen(rows)
+    w = widen(norm_w)
+    W = widen(W1)
+    c1 = widen(b1)
+    v2 = widen(w2)
+    c2 = float(widen(b2).reshape(-1)[0])
+    d = a.shape[-1]
+    out = np.empty(a.shape[0], np.float64)
+    step = 4096
+    for s in range(0, a.shape[0], step):
+        x = a[s:s + step]
+        ms = np.sum(x * x, axis=1) / d                  # mean square of the row
+        xt = x / np.sqrt(ms + eps_row)[:, None] * w[None, :]   # Eq. 1
+        u = xt @ W.T + c1[None, :]                      # first linear layer
+        act = u / (1.0 + np.exp(-u))                    # SiLU
+        out[s:s + step] = act @ v2 + c2                 # second linear layer
+    return out
+
+
+def gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float) -> np.ndarray:
+    """Raw scores ``[B, N]`` for a residual ``[B, N, d]``.
+
+    Tokens ``j < r`` form the non-prunable set N (the question, which comes
+    first in the prompt x = [x_R, x_D]); their score is fixed to 0.
+    """
+    a = np.asarray(resid)
+    B, N, _ = a.shape
+    out = np.zeros((B, N), np.float64)
+    for bi in range(B):
+        if N > r:
+            out[bi, r:] = score_rows(a[bi, r:], norm_w, W1, b1, w2, b2, eps_row)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Eq. 3 (second half): RMSNorm of the scalar scores along the sequence.
+# Paper, Section 4, "Scoring Network": scores are normalised along the
+# sequence with RMSNorm and fixed to zero on the non-prunable tokens; a
+# zero-output MLP gives b = 0 everywhere.
+#
+# Readings: the mean square runs over the prunable span only, there is no
+# learnable gain, and eps sits inside the square root (so 0 maps to 0).
+# --------------------------------------------------------------------------
+def seq_rmsnorm(score_raw, r: int, eps_seq: float) -> np.ndarray:
+    s = widen(score_raw)
+    B, N = s.shape
+    out = np.zeros((B, N), np.float64)
+    P = N - r
+    if P <= 0:
+        return out
+    for bi in range(B):
+        x = s[bi, r:]
+        ms = np.sum(x * x) / P
+        out[bi, r:] = x / math.sqrt(ms + eps_seq)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Eq. 4: top-K selector.  Paper, Section 4, "Top-K Selector": S holds the K
+# highest-scoring prunable tokens plus every non-prunable token.
+#
+# Readings: K' = min(K, |P|); equal scores go to the lower index; -0.0 and
+# +0.0 are equal; a NaN score ranks below every number (including -inf).
+# --------------------------------------------------------------------------
+def topk_select(score, r: int, K: int) -> np.ndarray:
+    """Keep mask ``[B, N]`` (uint8) holding exactly r + min(K, N-r) ones."""
+    s = widen(score)
+    B, N = s.shape
+    keep = np.zeros((B, N), np.uint8)
+    keep[:, :r] = 1
+    P = N - r
+    Kp = min(K, P)
+    if Kp <= 0:
+        return keep
+    idx = np.arange(P)
+    for bi in range(B):
+        b = s[bi, r:]
+        is_nan = np.isnan(b)
+        neg = np.where(is_nan, 0.0, -b)
+        # ascending order of (is_nan, -b, index): a stable total order
+        order = np.lexsort((idx, neg, is_nan))
+        keep[bi, r + order[:Kp]] = 1
+    return keep
+
+
+# --------------------------------------------------------------------------
+# Compaction.  Paper, Section 4, "Top-K Selector" (the residual stream of
+# pruned tokens stops at layer L; S continues through the layer-L MLP and the
+# layers above) and Appendix C.4 (kept tokens keep their original positions).
+#
+# Readings: S keeps ascending original order; the un-normalised residual is
+# copied bit for bit; the kept index doubles as the original position.
+# --------------------------------------------------------------------------
+def compact(resid, keep, score):
+    """Return ``kept_idx [B, M]`` int32, ``resid_S [B, M, d]`` (same dtype and
+    bits as ``resid``) and ``b_S [B, M]`` (the scores of the kept tokens)."""
+    a = np.asarray(resid)
+    k = np.asarray(keep)
+    sc = np.asarray(score)
+    B, N = k.shape
+    counts = [int(sum(1 for j in range(N) if k[bi, j])) for bi in range(B)]
+    if len(set(counts)) != 1:
+        raise ValueError("every batch row must keep the same number of tokens")
+    M = counts[0]
+    kept_idx = np.zeros((B, M), np.int32)
+    resid_S = np.zeros((B, M) + a.shape[2:], a.dtype)
+    b_S = np.zeros((B, M), sc.dtype)
+    for bi in range(B):
+        dst = 0                       # running count of kept tokens before j
+        for j in range(N):
+            if k[bi, j]:
+                kept_idx[bi, dst] = j
+                resid_S[bi, dst] = a[bi, j]
+                b_S[bi, dst] = sc[bi, j]
+                dst += 1
+    return kept_idx, resid_S, b_S
+
+
+# --------------------------------------------------------------------------
+# Eq. 7: temperature.  Paper, Section 4, "Temperature Scaling": pruning
+# shrinks the number of keys query i sees from its original position count
+# p_i to its rank count m_i among kept tokens; the learnable positive
+# temperature is scaled by the log-ratio of the two counts and is 1 at full
+# context.
+#
+# Reading: tau_i = temp * ln(p_i) / ln(m_i) with 1-based counts
+# p_i = pos_i + 1, m_i = i + 1; the ratio is exactly 1 when p_i == m_i, and
+# counts below 2 are clamped to 2 otherwise.
+# --------------------------------------------------------------------------
+def temperature_ratio(pos_i: int, i: int) -> float:
+    p = int(pos_i) + 1
+    m = int(i) + 1
+    if p == m:
+        return 1.0
+    return math.log(max(p, 2)) / math.log(max(m, 2))
+
+
+# --------------------------------------------------------------------------
+# Eq. 8 (= Eq. 5 with Eq. 6 substituted): token-gated causal GQA attention.
+# Paper, Section 4, token-gated attention, "Head-wise", "Putting everything
+# together"; Appendix C.4 (applied in the full-attention layers above L).
+#
+#   z_ij = (q_i . k_j) * sm_scale / tau_{h,i} + gain_h * b_j,   j <= i
+#   O_i  = sum_j softmax_j(z_i) v_j,   lse_i = log sum_j exp(z_ij)
+#
+# Readings: q-head h reads kv-head h // (Hq / Hkv); the gain multiplies the
+# key score outside the temperature; causality runs over kept order.
+# --------------------------------------------------------------------------
+def gated_attention(q, k, v, b_S, pos, gain, temp, sm_scale: float, rows=None,
+                    chunk: int = 1024):
+    """Return ``(O, lse)``: ``O [B, R, Hq, dh]`` and ``lse [B, Hq, R]`` in fp64,
+    for the query rows ``rows`` (all rows when None)."""
+    Q = widen(q)
+    Kx = widen(k)
+    V = widen(v)
+    b = widen(b_S)
+    P = np.asarray(pos)
+    g = widen(gain)
+    t = widen(temp)
+    B, M, Hq, dh = Q.shape
+    Hkv = Kx.shape[2]
+    group = Hq // Hkv
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    R = rows.shape[0]
+    O = np.zeros((B, R, Hq, dh), np.float64)
+    lse = np.zeros((B, Hq, R), np.float64)
+    for bi in range(B):
+        for h in range(Hq):
+            kv = h // group
+            Kh = Kx[bi, :, kv, :]
+            Vh = V[bi, :, kv, :]
+            for s in range(0, R, chunk):
+                rr = rows[s:s + chunk]
+                tau = t[h] * np.array([temperature_ratio(P[bi, i], i) for i in rr])
+                logits = (Q[bi, rr, h, :] @ Kh.T) * sm_scale / tau[:, None]
+                z = logits + g[h] * b[bi][None, :]
+                causal = np.arange(M)[None, :] <= rr[:, None]
+                z = np.where(causal, z, -np.inf)
+                zmax = np.max(z, axis=1, keepdims=True)
+                e = np.exp(z - zmax)
+                den = np.sum(e, axis=1, keepdims=True)
+                O[bi, s:s + chunk, h, :] = (e @ Vh) / den
+                lse[bi, h, s:s + chunk] = zmax[:, 0] + np.log(den[:, 0])
+    return O, lse
+
+
+def gated_attention_gate_form(q, k, v, b_S, pos, gain, temp, sm_scale: float, rows=None):
+    """The same attention in its unsimplified form (Eq. 5 with Eq. 6).
+
+    The gate value of each kept key is ``g_j = softmax_j(gain_h * b_j)`` over
+    all kept keys; the attention weight of key j for query i is
+    ``g_j * exp(s_ij / tau) / sum_{k<=i} g_k * exp(s_ik / tau)``.  The softmax
+    normaliser of g is one constant per head and cancels, which is why Eq. 8
+    is a plain additive logit bias.
+    """
+    Q = widen(q)
+    Kx = widen(k)
+    V = widen(v)
+    b = widen(b_S)
+    P = np.asarray(pos)
+    gn = widen(gain)
+    t = widen(temp)
+    B, M, Hq, dh = Q.shape
+    group = Hq // Kx.shape[2]
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    O = np.zeros((B, rows.shape[0], Hq, dh), np.float64)
+    for bi in range(B):
+        for h in range(Hq):
+            kv = h // group
+            x = gn[h] * b[bi]
+            gate = np.exp(x - x.max())
+            gate = gate / gate.sum()                       # Eq. 6
+            for n, i in enumerate(rows):
+                tau = t[h] * temperature_ratio(P[bi, i], i)
+                s = (Kx[bi, :i + 1, kv, :] @ Q[bi, i, h, :]) * sm_scale / tau
+                wgt = gate[:i + 1] * np.exp(s - s.max())   # Eq. 5
+                O[bi, n, h, :] = (wgt @ V[bi, :i + 1, kv, :]) / wgt.sum()
+    return O
