@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Gated-prefill benchmark on one MI355X.
+
+Default workload (stage_32k): the full gated-prefill stage at Qwen3-1.7B
+shape -- N = 32768 tokens (r = 64 question tokens), d = 2048 bf16 residual,
+gate MLP 2048 -> 256 -> 1, K = 3277 (10 %) kept, then 24 upper-layer
+token-gated causal GQA attention calls (16q / 8kv heads, d_h 128) on the
+compacted stream.
+
+One step = one pass of the whole path over one input:
+    tg_gate_score -> tg_seq_rmsnorm -> tg_topk_select -> tg_compact
+    -> 24 x tg_gated_attention
+with every input already resident in HBM.  The residual is rotated over
+several copies (> the 256 MiB Infinity Cache) so the HBM-bound kernels read
+HBM.  The per-layer Q/K/V are the upper layers' projections of the compacted
+stream (seeded random weights); they are produced before the timed region by
+plain bf16 GEMMs outside the library and are timed separately ("glue").
+
+Prints ONE JSON line: tokens/s = N / (GPU time per step), the roofline of
+the dominant kernel (gated attention, bf16 MFMA), per-kernel figures and the
+CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill tokens/s at N=16k–128k; HBM GB/s % and MFMA % of peak"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(kernel_file: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they
+    were taken on the current source of the kernel; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+        src = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc", kernel_file)
+        ent = t.get(kernel_file)
+        if not ent or ent.get("source_sha256") != _sha(src):
+            return None
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+class Events:
+    """Pairs of HIP events (torch's current stream: the stream the library
+    launches on) around each named launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def around(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        r = fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+        return r
+
+    def avg_us(self, name):
+        ps = self.pairs.get(name, [])
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+
+    def count(self, name):
+        return len(self.pairs.get(name, []))
+
+
+def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    raw = oracle.gate_score(c.resid, c.r, c.norm_w, c.W1, c.b1, c.w2, c.b2, c.eps_row)
+    b = oracle.seq_rmsnorm(raw, c.r, c.eps_seq)
+    keep = oracle.topk_select(b.astype(np.float32), c.r, c.K)
+    oracle.compact(c.resid, keep, b.astype(np.float32))
+    t_gate = time.perf_counter() - t0
+    q, k, v = layer0_qkv
+    M = q.shape[1]
+    R = min(M, max_rows)
+    rows = np.linspace(0, M - 1, R).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.gated_attention(q, k, v, b_S, kept_idx, gain, temp, q.shape[-1] ** -0.5, rows=rows)
+    t_rows = time.perf_counter() - t0
+    t_layer = t_rows * M / R
+    per_step = t_gate + n_layers * t_layer
+    return {
+        "value": c.N / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"gate (score, seq-norm, top-K, compaction) on the full N={c.N} input: {t_gate:.2f} s; "
+                   f"one attention layer on {R} of {M} query rows (all {q.shape[2]} heads): {t_rows:.2f} s, "
+                   f"extrapolated linearly to {M} rows x {n_layers} layers"),
+        "seconds_per_step": per_step,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stage_32k", choices=["stage_32k", "gate_16k", "sweep_128k"])
+    ap.add_argument("--frac", type=float, default=0.10, help="budget fraction for sweep_128k")
+    ap.add_argument("--layers", type=int, default=None, help="upper layers (default: 24 for stage_32k, else 1)")
+    ap.add_argument("--copies", type=int, default=0, help="residual copies rotated per step (0: enough for 512 MiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; the gated-prefill path runs on a single MI355X "
+              "(multi-GPU sharding is described in DESIGN.md, not run). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import learned_token_pruning_07_amd as tg
+    from learned_token_pruning_07_amd import stage_glue
+    from learned_token_pruning_07_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tg.load_library()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- inputs ----------------
+    if args.workload == "stage_32k":
+        c = wl.preset_gate_case("stage_32k")
+        n_layers = 24 if args.layers is None else args.layers
+    elif args.workload == "gate_16k":
+        c = wl.preset_gate_case("gate_16k")
+        n_layers = 0 if args.layers is None else args.layers
+    else:
+        c = wl.preset_gate_case("sweep_128k", K=int(round(args.frac * (131072 - 128))))
+        n_layers = 1 if args.layers is None else args.layers
+    N, r, K, d, h, M = c.N, c.r, c.K, c.d, c.h, c.M
+    heads = wl.STAGE_HEADS
+    log(f"workload {args.workload}: N={N} r={r} K={K} M={M} d={d} h={h} layers={n_layers}")
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    resid0 = bits(c.resid)
+    row_bytes = d * 2
+    ncopy = args.copies or max(1, -(-(512 << 20) // (N * row_bytes)))
+    resids = [resid0] + [resid0.clone() for _ in range(ncopy - 1)]
+    norm_w, W1, w2 = bits(c.norm_w), bits(c.W1), bits(c.w2)
+    b1, b2 = torch.from_numpy(c.b1).to(dev), torch.from_numpy(c.b2).to(dev)
+    # preallocated outputs: nothing is allocated inside a step
+    score = torch.empty((1, N), dtype=torch.float32, device=dev)
+    keep = torch.empty((1, N), dtype=torch.uint8, device=dev)
+    kept_idx = torch.empty((1, M), dtype=torch.int32, device=dev)
+    resid_S = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
+    b_S = torch.empty((1, M), dtype=torch.float32, device=dev)
+
+    def gate(x, ev=None):
+        run = (lambda name, fn: ev.around(name, fn)) if ev else (lambda name, fn: fn())
+        run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score))
+        run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score))
+        run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep))
+        run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
+                                              score_out=b_S))
+
+    gate(resid0)
+    torch.cuda.synchronize()
+
+    # upper-layer Q/K/V (glue, outside the library and outside the timed step)
+    layers = stage_glue.stage_layers(n_layers, d, **heads) if n_layers else []
+    qkv = [p.qkv(resid_S) for p in layers]
+    attn_out = torch.empty((1, M, heads["Hq"], heads["dh"]), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    glue_ms = 0.0
+    if layers:
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for p in layers:
+            p.qkv(resid_S)
+        g0.record()
+        for _ in range(3):
+            for p in layers:
+                p.qkv(resid_S)
+        g1.record()
+        torch.cuda.synchronize()
+        glue_ms = g0.elapsed_time(g1) / 3
+
+    def step(i, ev=None):
+        gate(resids[i % ncopy], ev)
+        for l, p in enumerate(layers):
+            q, k, v = qkv[l]
+            fn = (lambda q=q, k=k, v=v, p=p: tg.tg_gated_attention(q, k, v, b_S, kept_idx, p.gain, p.temp,
+                                                                   out=attn_out))
+            if ev:
+                ev.around("gated_attention", fn)
+            else:
+                fn()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---------------- timed region ----------------
+    # an event pair around every launch gives per-kernel durations on the
+    # library's stream; the outer pair gives the time per step
+    ev = Events(torch)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies)")
+
+    # ---------------- figures ----------------
+    e = 2
+    P = N - r
+    algo = {
+        "gate_score": dict(bytes=P * d * e + h * d * e + 4 * N, flops=2 * P * d * h, bound="hbm"),
+        "seq_rmsnorm": dict(bytes=4 * P + 4 * N, flops=2 * P, bound="latency"),
+        "topk_select": dict(bytes=4 * P + N, flops=0, bound="latency"),
+        "compact": dict(bytes=N + 2 * M * d * e + 12 * M, flops=0, bound="hbm"),
+    }
+    if layers:
+        Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+        algo["gated_attention"] = dict(bytes=M * dh * e * (2 * Hq + 2 * Hkv) + 8 * M,
+                                       flops=2 * dh * Hq * M * (M + 1), bound="mfma")
+    kernels = {}
+    for name, a in algo.items():
+        us = ev.avg_us(name)
+        ent = {"avg_us": round(us, 3), "launches_per_step": ev.count(name) // args.steps,
+               "algorithmic_bytes": a["bytes"], "algorithmic_flops": a["flops"]}
+        gbs = a["bytes"] / (us * 1e-6) / 1e9
+        ent["achieved_GBs"] = round(gbs, 1)
+        ent["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+        if a["flops"]:
+            tf = a["flops"] / (us * 1e-6) / 1e12
+            ent["achieved_TFLOPs"] = round(tf, 2)
+            ent["mfma_frac"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        kernels[name] = ent
+    kernel_us_sum = sum(kernels[n]["avg_us"] * kernels[n]["launches_per_step"] for n in kernels)
+    gate_us = sum(kernels[n]["avg_us"] for n in ("gate_score", "seq_rmsnorm", "topk_select", "compact"))
+    gate_bytes = sum(algo[n]["bytes"] for n in ("gate_score", "seq_rmsnorm", "topk_select", "compact"))
+
+    if layers:
+        dom, dom_file = "gated_attention", "gated_attention.hip"
+        a = kernels[dom]
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": a["achieved_TFLOPs"], "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": a["mfma_frac"], "traffic": None}
+    else:
+        dom, dom_file = "gate_score", "gate_score.hip"
+        a = kernels[dom]
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": a["achieved_GBs"], "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": a["hbm_frac"], "traffic": None}
+    roofline["traffic"] = _traffic(dom_file)
+
+    value = N / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded PCG64 draws with the workload's shapes and distributions",
+        "config": {"workload": args.workload, "N": N, "r": r, "K": K, "M": M, "d": d, "h": h, "layers": n_layers,
+                   "Hq": heads["Hq"], "Hkv": heads["Hkv"], "d_h": heads["dh"], "batch": 1,
+                   "residual_copies": ncopy},
+        "roofline": roofline,
+        "kernels": kernels,
+        "gate_op": {"avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
+                    "achieved_GBs": round(gate_bytes / (gate_us * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(gate_bytes / (gate_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "library_kernel_tokens_per_s": round(N / (kernel_us_sum * 1e-6), 1),
+        "glue_qkv_ms_per_step": round(glue_ms, 4),
+        "tokens_per_s_with_glue": round(N / ((ms_per_step + glue_ms) * 1e-3), 1),
+    }
+
+    if not args.no_cpu_baseline and layers:
+        log("timing the CPU oracle on a bounded sample")
+        q, k, v = qkv[0]
+        host = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        out["cpu_baseline"] = cpu_baseline(c, (host(q), host(k), host(v)), kept_idx.cpu().numpy(),
+                                           b_S.cpu().numpy(), layers[0].gain.cpu().numpy(),
+                                           layers[0].temp.cpu().numpy(), n_layers)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate gated-prefill library (MI355X, gfx950).
+ *
+ * The library implements the inference hot path of TokenGate ("TokenGate:
+ * Adapting LLMs for Fast and Memory-Efficient Prefill with Learned Token
+ * Pruning", Section 4): at gate layer L every prunable token is scored by a
+ * small MLP over its RMS-normalised post-attention residual, the scores are
+ * RMS-normalised along the sequence, the top-K prunable tokens plus every
+ * non-prunable token are kept, the residual stream is compacted to the kept
+ * set, and the layers above L run token-gated causal GQA attention whose
+ * logits carry each kept key's score through a per-head gain and a
+ * temperature.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Tensors are dense, row-major and
+ *    contiguous in the order the shapes are written.
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL means the default stream).  Nothing synchronises and nothing is
+ *    copied device -> host.
+ *  - Return value: TG_OK (0) or a tg_status code.  Arguments are validated
+ *    before anything is enqueued; on any error nothing is enqueued and
+ *    tg_last_error() describes the problem.  No C++ exception crosses the ABI.
+ *  - Results are deterministic: the same inputs give the same output bits.
+ *  - Batch rows are independent; every batch row has the same N, r and K.
+ *  - The non-prunable tokens (the question x_R of the prompt x = [x_R, x_D])
+ *    are the first r tokens of each sequence; tokens r..N-1 are prunable.
+ *  - bf16 is IEEE bfloat16 stored in 16 bits; fp32 is IEEE binary32.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TG_OK = 0,
+  TG_EINVAL = 1,        /* null pointer, bad size, bad alignment */
+  TG_EUNSUPPORTED = 2,  /* a valid request this build does not implement */
+  TG_EHIP = 3           /* a HIP launch or runtime error */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+typedef enum {
+  TG_OP_GATE_SCORE = 0,
+  TG_OP_SEQ_RMSNORM = 1,
+  TG_OP_TOPK_SELECT = 2,
+  TG_OP_COMPACT = 3,
+  TG_OP_GATED_ATTENTION = 4
+} tg_op;
+
+/*
+ * tg_gate_score -- row RMSNorm of the post-attention residual followed by the
+ * scoring MLP (paper Section 4, "Scoring Network", Eq. 1 and the first half
+ * of Eq. 3; Appendix C.4 for the residual after layer L's mixer).
+ *
+ * For every batch row and every prunable token j in [r, N):
+ *     a~_j  = a_j * norm_w / sqrt(mean_c(a_j[c]^2) + eps_row)
+ *     u     = W1 a~_j + b1                      (h values)
+ *     out_j = sum_k w2[k] * silu(u[k]) + b2[0]  silu(x) = x / (1 + exp(-x))
+ * and out_j = 0 for j < r.
+ *
+ *   resid     [B, N, d]  dtype `dt` (TG_BF16 or TG_F32), 16-byte aligned
+ *   norm_w    [d]        dtype `dt`   RMSNorm weight
+ *   W1        [h, d]     dtype `dt`   first linear layer (PyTorch Linear layout)
+ *   b1        [h]        fp32
+ *   w2        [h]        dtype `dt`   second linear layer (one output)
+ *   b2        [1]        fp32
+ *   score_raw [B, N]     fp32 output (the raw score b~)
+ *   ws, ws_bytes         workspace; pass tg_workspace_size(TG_OP_GATE_SCORE,...)
+ *                        bytes (0 today: ws may be NULL)
+ * Supported: TG_BF16 with d % 8 == 0 and h in {64, 128, 256} (bf16 MFMA,
+ * fp32 accumulation); TG_F32 with d % 4 == 0, d <= 4096 and h <= 1024 (fp32
+ * FMA).  Other shapes return TG_EUNSUPPORTED.
+ */
+int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r,
+                  const void* norm_w, float eps_row,
+                  const void* W1, const float* b1, int h,
+                  const void* w2, const float* b2,
+                  float* score_raw, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tg_seq_rmsnorm -- RMSNorm of the scalar scores along the sequence (paper
+ * Section 4, "Scoring Network", second half of Eq. 3; scores of
+ * non-prunable tokens are fixed to zero).
+ *
+ * For every batch row, with P = N - r:
+ *     ms    = (1/P) * sum_{j in [r,N)} score_raw[j]^2
+ *     out_j = score_raw[j] / sqrt(ms + eps_seq)   for j >= r,   0 for j < r.
+ * With P == 0 every output is 0.  The reduction order is fixed.
+ *
+ *   score_raw [B, N] fp32 in;  score [B, N] fp32 out (may alias score_raw)
+ *   ws, ws_bytes     workspace (0 bytes today)
+ */
+int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq,
+                   float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tg_topk_select -- top-K selector (paper Section 4, "Top-K Selector", Eq. 4):
+ * keep the K' = min(K, N - r) highest-scoring prunable tokens and every
+ * non-prunable token.
+ *
+ * Order: higher score first; equal scores go to the lower index; -0.0 and
+ * +0.0 are equal; NaN ranks below every number, -inf included.  The order is
+ * total, so exactly r + K' tokens are kept per batch row.
+ *
+ *   score [B, N] fp32 in;   keep [B, N] uint8 out (1 = kept, 0 = pruned)
+ *   K >= 0 (K >= N - r keeps everything)
+ *   ws, ws_bytes     workspace (0 bytes today)
+ */
+int tg_topk_select(const float* score, int B, int N, int r, int K,
+                   uint8_t* keep, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tg_compact -- compaction of the residual stream to the kept set (paper
+ * Section 4, "Top-K Selector": pruned tokens stop at layer L and the kept set
+ * continues; Appendix C.4: kept tokens keep their original positions).
+ *
+ * Kept tokens are listed in ascending original order:
+ *     kept_idx[m]   = j, the m-th kept token (also its original position)
+ *     resid_out[m]  = resid[j]     (bit copy of the un-normalised residual)
+ *     score_out[m]  = score[j]
+ *
+ *   resid     [B, N, d] dtype `dt`, 16-byte aligned; keep [B, N] uint8
+ *   score     [B, N] fp32
+ *   M         number of ones in every batch row of keep (the caller knows it:
+ *             M = r + min(K, N - r) after tg_topk_select).  The library cannot
+ *             check the count without a device->host read; a wrong M leaves
+ *             rows unwritten or writes past M.
+ *   kept_idx  [B, M] int32 out; resid_out [B, M, d] dtype `dt` out;
+ *   score_out [B, M] fp32 out
+ * Requires d * sizeof(dt) % 16 == 0.
+ */
+int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* keep,
+               const float* score, int M, int32_t* kept_idx, void* resid_out,
+               float* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tg_gated_attention -- token-gated causal GQA attention over the kept set
+ * (paper Section 4: token-gated attention Eq. 5, head-wise gain Eq. 6,
+ * temperature Eq. 7, combined as the key-bias form Eq. 8; Appendix C.4).
+ *
+ * For batch row b, query head h (kv head g = h / (Hq / Hkv)), kept rank i and
+ * key rank j <= i:
+ *     ratio_i = 1 if pos[i] == i, else ln(max(pos[i]+1, 2)) / ln(max(i+1, 2))
+ *     z_ij    = (q_i . k_j) * sm_scale / (temp[h] * ratio_i) + gain[h] * key_score[j]
+ *     out_i   = sum_j softmax_j(z_i) v_j
+ *     lse_i   = ln sum_j exp(z_ij)
+ * gain and temp are the effective (already positive) values; pos holds the
+ * original positions of the kept tokens (kept_idx), or 0..M-1 for full-context
+ * behaviour (ratio 1).
+ *
+ *   q   [B, M, Hq, d_h] bf16,   k, v [B, M, Hkv, d_h] bf16  (16-byte aligned)
+ *   key_score [B, M] fp32,  pos [B, M] int32,  gain [Hq] fp32,  temp [Hq] fp32
+ *   out [B, M, Hq, d_h] bf16 (fp32 accumulate, round to nearest even)
+ *   lse [B, Hq, M] fp32, or NULL to skip it
+ * Supported: d_h in {64, 128}; Hq / Hkv in {1, 2, 4}.  M == 0 is a no-op.
+ */
+int tg_gated_attention(const void* q, const void* k, const void* v,
+                       int B, int M, int Hq, int Hkv, int d_h,
+                       const float* key_score, const int32_t* pos,
+                       const float* gain, const float* temp, float sm_scale,
+                       void* out, float* lse, void* stream);
+
+/* Workspace bytes an entry point needs for the given sizes (0 when none). */
+size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
+
+/* Message describing the last non-zero status returned on this thread. */
+const char* tg_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

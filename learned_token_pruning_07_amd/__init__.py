@@ -1,0 +1,226 @@
+"""TokenGate gated-prefill path on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libtokengate.so`` (C ABI declared in
+``include/tokengate.h``).  Each function takes torch tensors that already live
+on the GPU, checks their dtype/shape/contiguity, and passes raw device
+pointers plus torch's current HIP stream to the library.  Every step of the
+path runs in the library's HIP kernels; nothing here computes.
+
+If the shared library has not been built, every call raises: there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtokengate.so")
+
+TG_OK, TG_EINVAL, TG_EUNSUPPORTED, TG_EHIP = 0, 1, 2, 3
+TG_F32, TG_BF16 = 0, 1
+TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION = range(5)
+
+EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
+            "tg_workspace_size", "tg_last_error", "tg_version")
+
+_lib = None
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[tg status {code}] {msg}")
+        self.code = code
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libtokengate.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it first (python -m learned_token_pruning_07_amd._build)")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.tg_gate_score.argtypes = [vp, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
+    lib.tg_seq_rmsnorm.argtypes = [vp, i, i, i, f, vp, vp, sz, vp]
+    lib.tg_topk_select.argtypes = [vp, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_compact.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp]
+    lib.tg_gated_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.tg_workspace_size.restype = sz
+    lib.tg_last_error.argtypes = []
+    lib.tg_last_error.restype = ctypes.c_char_p
+    lib.tg_version.argtypes = []
+    lib.tg_version.restype = i
+    for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention"):
+        getattr(lib, name).restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(code: int) -> None:
+    if code != TG_OK:
+        msg = load_library().tg_last_error().decode(errors="replace")
+        raise TokenGateError(code, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    if t.dtype == torch.float32:
+        return TG_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+# --------------------------------------------------------------- entry points
+def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None, stream=None):
+    """Row RMSNorm + scoring MLP -> raw scores ``[B, N]`` fp32 (0 for j < r)."""
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    h = W1.shape[0]
+    _need(norm_w, "norm_w", resid.dtype, (d,))
+    _need(W1, "W1", resid.dtype, (h, d))
+    _need(b1, "b1", torch.float32, (h,))
+    _need(w2, "w2", resid.dtype, (h,))
+    _need(b2, "b2", torch.float32, (1,))
+    if score_raw is None:
+        score_raw = torch.empty((B, N), dtype=torch.float32, device=resid.device)
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, _ptr(norm_w), eps_row, _ptr(W1), _ptr(b1), h,
+                             _ptr(w2), _ptr(b2), _ptr(score_raw), None, 0, _stream(stream)))
+    return score_raw
+
+
+def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, stream=None):
+    """Sequence RMSNorm of the raw scores -> ``[B, N]`` fp32 (0 for j < r)."""
+    lib = load_library()
+    _need(score_raw, "score_raw", torch.float32)
+    B, N = score_raw.shape
+    if score is None:
+        score = torch.empty_like(score_raw)
+    _need(score, "score", torch.float32, (B, N))
+    _check(lib.tg_seq_rmsnorm(_ptr(score_raw), B, N, r, eps_seq, _ptr(score), None, 0, _stream(stream)))
+    return score
+
+
+def tg_topk_select(score, r: int, K: int, keep=None, stream=None):
+    """Keep mask ``[B, N]`` uint8 with r + min(K, N - r) ones per row."""
+    lib = load_library()
+    _need(score, "score", torch.float32)
+    B, N = score.shape
+    if keep is None:
+        keep = torch.empty((B, N), dtype=torch.uint8, device=score.device)
+    _need(keep, "keep", torch.uint8, (B, N))
+    _check(lib.tg_topk_select(_ptr(score), B, N, r, K, _ptr(keep), None, 0, _stream(stream)))
+    return keep
+
+
+def kept_count(N: int, r: int, K: int) -> int:
+    """M = r + min(K, N - r): the number of kept tokens per sequence."""
+    return r + max(0, min(K, N - r))
+
+
+def tg_compact(resid, keep, score, M: int, kept_idx=None, resid_out=None, score_out=None, stream=None):
+    """Compact the residual stream to the kept set.
+
+    Returns ``(kept_idx [B, M] int32, resid_out [B, M, d], score_out [B, M] fp32)``.
+    """
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    _need(keep, "keep", torch.uint8, (B, N))
+    _need(score, "score", torch.float32, (B, N))
+    dev = resid.device
+    if kept_idx is None:
+        kept_idx = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if resid_out is None:
+        resid_out = torch.empty((B, M, d), dtype=resid.dtype, device=dev)
+    if score_out is None:
+        score_out = torch.empty((B, M), dtype=torch.float32, device=dev)
+    _need(kept_idx, "kept_idx", torch.int32, (B, M))
+    _need(resid_out, "resid_out", resid.dtype, (B, M, d))
+    _need(score_out, "score_out", torch.float32, (B, M))
+    _check(lib.tg_compact(_ptr(resid), _dt(resid), B, N, d, _ptr(keep), _ptr(score), M, _ptr(kept_idx),
+                          _ptr(resid_out), _ptr(score_out), None, 0, _stream(stream)))
+    return kept_idx, resid_out, score_out
+
+
+def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | None = None, out=None,
+                       lse=None, want_lse: bool = False, stream=None):
+    """Token-gated causal GQA attention.  q ``[B, M, Hq, dh]``, k/v ``[B, M, Hkv, dh]`` bf16.
+
+    Returns ``out`` (and ``lse [B, Hq, M]`` when ``want_lse`` or ``lse`` is given).
+    """
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    B, M, Hq, dh = q.shape
+    Hkv = k.shape[2]
+    _need(k, "k", torch.bfloat16, (B, M, Hkv, dh))
+    _need(v, "v", torch.bfloat16, (B, M, Hkv, dh))
+    _need(key_score, "key_score", torch.float32, (B, M))
+    _need(pos, "pos", torch.int32, (B, M))
+    _need(gain, "gain", torch.float32, (Hq,))
+    _need(temp, "temp", torch.float32, (Hq,))
+    if sm_scale is None:
+        sm_scale = dh ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (B, M, Hq, dh))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, M))
+    _check(lib.tg_gated_attention(_ptr(q), _ptr(k), _ptr(v), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
+                                  _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def tg_workspace_size(op: int, B: int, N: int, d: int, h: int, K: int) -> int:
+    return int(load_library().tg_workspace_size(op, B, N, d, h, K))
+
+
+def tg_version() -> int:
+    return int(load_library().tg_version())
+
+
+def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e-6, eps_seq=1e-6, stream=None):
+    """The gate at layer L, end to end: score -> sequence norm -> top-K -> compaction.
+
+    Returns ``(kept_idx, resid_S, b_S, keep, score)``.  Four library calls on
+    one stream, no host synchronisation (M is known on the host).
+    """
+    B, N, _ = resid.shape
+    raw = tg_gate_score(resid, r, norm_w, W1, b1, w2, b2, eps_row, stream=stream)
+    score = tg_seq_rmsnorm(raw, r, eps_seq, score=raw, stream=stream)
+    keep = tg_topk_select(score, r, K, stream=stream)
+    M = kept_count(N, r, K)
+    kept_idx, resid_S, b_S = tg_compact(resid, keep, score, M, stream=stream)
+    return kept_idx, resid_S, b_S, keep, score

@@ -1,0 +1,144 @@
+// C-ABI front end of the TokenGate library: argument validation, dispatch,
+// error reporting.  Every check runs before anything is enqueued; no HIP call
+// is made on a path that returns an error status.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/tokengate.h"
+#include "tg_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TG_OK;
+  return fail(TG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+size_t dt_size(int dt) { return dt == TG_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int tg_version(void) { return 10000; }
+
+const char* tg_last_error(void) { return g_err; }
+
+size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
+  (void)op; (void)B; (void)N; (void)d; (void)h; (void)K;
+  return 0;
+}
+
+int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
+                  const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
+                  void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_gate_score: unknown dtype %d", dt);
+  if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "tg_gate_score: B, N, d, h must be > 0");
+  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_gate_score: r=%d outside [0, N=%d]", r, N);
+  if (!resid || !norm_w || !W1 || !b1 || !w2 || !b2 || !score_raw)
+    return fail(TG_EINVAL, "tg_gate_score: null pointer argument");
+  if (!(eps_row >= 0.0f)) return fail(TG_EINVAL, "tg_gate_score: eps_row must be >= 0");
+  if ((long long)B * N * d > (1LL << 40)) return fail(TG_EINVAL, "tg_gate_score: tensor too large");
+  if (!aligned16(resid) || !aligned16(W1) || !aligned16(norm_w) || !aligned4(score_raw) || !aligned4(b1) ||
+      !aligned4(b2))
+    return fail(TG_EINVAL, "tg_gate_score: resid, W1 and norm_w must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dt == TG_BF16) {
+    if (d % 8 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 needs d %% 8 == 0 (d=%d)", d);
+    if (h != 64 && h != 128 && h != 256)
+      return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 supports h in {64,128,256} (h=%d)", h);
+    return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r,
+                                                 static_cast<const uint16_t*>(norm_w), eps_row,
+                                                 static_cast<const uint16_t*>(W1), b1, h,
+                                                 static_cast<const uint16_t*>(w2), b2, score_raw, s),
+                      "tg_gate_score");
+  }
+  if (d % 4 != 0 || d > 4096 || h > 1024)
+    return fail(TG_EUNSUPPORTED, "tg_gate_score: fp32 needs d %% 4 == 0, d <= 4096, h <= 1024");
+  return hip_status(tg::launch_gate_score_f32(static_cast<const float*>(resid), B, N, d, r,
+                                              static_cast<const float*>(norm_w), eps_row,
+                                              static_cast<const float*>(W1), b1, h, static_cast<const float*>(w2),
+                                              b2, score_raw, s),
+                    "tg_gate_score");
+}
+
+int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq, float* score, void* ws,
+                   size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_seq_rmsnorm: B, N must be > 0");
+  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_seq_rmsnorm: r=%d outside [0, N=%d]", r, N);
+  if (!score_raw || !score) return fail(TG_EINVAL, "tg_seq_rmsnorm: null pointer argument");
+  if (!aligned4(score_raw) || !aligned4(score)) return fail(TG_EINVAL, "tg_seq_rmsnorm: misaligned pointer");
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "tg_seq_rmsnorm: eps_seq must be >= 0");
+  return hip_status(tg::launch_seq_rmsnorm(score_raw, B, N, r, eps_seq, score, reinterpret_cast<hipStream_t>(stream)),
+                    "tg_seq_rmsnorm");
+}
+
+int tg_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws, size_t ws_bytes,
+                   void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_topk_select: B, N must be > 0");
+  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_topk_select: r=%d outside [0, N=%d]", r, N);
+  if (K < 0) return fail(TG_EINVAL, "tg_topk_select: K=%d must be >= 0", K);
+  if (!score || !keep) return fail(TG_EINVAL, "tg_topk_select: null pointer argument");
+  if (!aligned4(score)) return fail(TG_EINVAL, "tg_topk_select: misaligned score");
+  return hip_status(tg::launch_topk_select(score, B, N, r, K, keep, reinterpret_cast<hipStream_t>(stream)),
+                    "tg_topk_select");
+}
+
+int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* keep, const float* score, int M,
+               int32_t* kept_idx, void* resid_out, float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_compact: unknown dtype %d", dt);
+  if (B <= 0 || N <= 0 || d <= 0) return fail(TG_EINVAL, "tg_compact: B, N, d must be > 0");
+  if (M < 0 || M > N) return fail(TG_EINVAL, "tg_compact: M=%d outside [0, N=%d]", M, N);
+  if (!resid || !keep || !score || (M > 0 && (!kept_idx || !resid_out || !score_out)))
+    return fail(TG_EINVAL, "tg_compact: null pointer argument");
+  const size_t row_bytes = (size_t)d * dt_size(dt);
+  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "tg_compact: row bytes must be a multiple of 16");
+  if (!aligned16(resid) || (M > 0 && !aligned16(resid_out)) || !aligned4(score) ||
+      (M > 0 && (!aligned4(kept_idx) || !aligned4(score_out))))
+    return fail(TG_EINVAL, "tg_compact: misaligned pointer");
+  return hip_status(tg::launch_compact(resid, row_bytes, B, N, keep, score, M, kept_idx, resid_out, score_out,
+                                       reinterpret_cast<hipStream_t>(stream)),
+                    "tg_compact");
+}
+
+int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,
+                       const float* key_score, const int32_t* pos, const float* gain, const float* temp,
+                       float sm_scale, void* out, float* lse, void* stream) {
+  if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "tg_gated_attention: bad sizes");
+  if (Hq % Hkv != 0) return fail(TG_EINVAL, "tg_gated_attention: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if (M == 0) return TG_OK;
+  if (!q || !k || !v || !key_score || !pos || !gain || !temp || !out)
+    return fail(TG_EINVAL, "tg_gated_attention: null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(key_score) ||
+      !aligned4(pos) || !aligned4(gain) || !aligned4(temp) || (lse && !aligned4(lse)))
+    return fail(TG_EINVAL, "tg_gated_attention: misaligned pointer");
+  if (!(sm_scale > 0.0f)) return fail(TG_EINVAL, "tg_gated_attention: sm_scale must be > 0");
+  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "tg_gated_attention: d_h=%d not in {64,128}", d_h);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4)
+    return fail(TG_EUNSUPPORTED, "tg_gated_attention: Hq/Hkv=%d not in {1,2,4}", G);
+  return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                               static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
+                                               pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    "tg_gated_attention");
+}
+
+}  // extern "C"

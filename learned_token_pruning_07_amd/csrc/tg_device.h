@@ -1,0 +1,94 @@
+// Device-side helpers shared by the TokenGate HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 values -> two bf16 (round to nearest even) packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Wave64 reductions (fixed butterfly order: deterministic).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a whole block (blockDim.x a multiple of 64, at most
+// 1024 threads).  `s_wave` holds >= 16 words of LDS.  Returns the exclusive
+// prefix of `v`; `total` receives the block total.  Contains barriers: every
+// thread of the block must call it.
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint32_t incl = wave_incl_scan_u32(v);
+  if (lane == 63) s_wave[wid] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    uint32_t t = s_wave[w];
+    before += (w < wid) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+// Workgroup id remapped so that consecutive logical ids land on the same XCD.
+// The hardware hands workgroups to the 8 XCDs round-robin; this bijection
+// gives XCD x the contiguous logical range [x*q + min(x, rem), ...).
+__device__ __forceinline__ int xcd_logical_id(int id, int total) {
+  const int q = total >> 3, rem = total & 7;
+  const int x = id & 7;
+  return x * q + (x < rem ? x : rem) + (id >> 3);
+}
+
+}  // namespace tg

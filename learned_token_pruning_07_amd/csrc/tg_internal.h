@@ -1,0 +1,36 @@
+// Host-side launchers of the TokenGate kernels.  Arguments are validated by the
+// C-ABI front end (tg_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tg {
+
+hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r,
+                                  const uint16_t* norm_w, float eps_row, const uint16_t* W1,
+                                  const float* b1, int h, const uint16_t* w2, const float* b2,
+                                  float* out, hipStream_t s);
+
+hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r,
+                                 const float* norm_w, float eps_row, const float* W1,
+                                 const float* b1, int h, const float* w2, const float* b2,
+                                 float* out, hipStream_t s);
+
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out,
+                              hipStream_t s);
+
+hipError_t launch_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep,
+                              hipStream_t s);
+
+hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,
+                          const float* score, int M, int32_t* kept_idx, void* resid_out,
+                          float* score_out, hipStream_t s);
+
+hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
+                                  int M, int Hq, int Hkv, int dh, const float* key_score,
+                                  const int32_t* pos, const float* gain, const float* temp,
+                                  float sm_scale, uint16_t* out, float* lse, hipStream_t s);
+
+}  // namespace tg
