@@ -197,6 +197,7 @@ def main():
     layers = stage_glue.stage_layers(n_layers, d, **heads) if n_layers else []
     qkv = [p.qkv(resid_S) for p in layers]
     attn_out = torch.empty((1, M, heads["Hq"], heads["dh"]), dtype=torch.bfloat16, device=dev)
+    attn_ws = tg.attention_workspace(1, M, heads["Hkv"], heads["dh"], dev)
     torch.cuda.synchronize()
     glue_ms = 0.0
     if layers:
@@ -216,7 +217,7 @@ def main():
         for l, p in enumerate(layers):
             q, k, v = qkv[l]
             fn = (lambda q=q, k=k, v=v, p=p: tg.tg_gated_attention(q, k, v, b_S, kept_idx, p.gain, p.temp,
-                                                                   out=attn_out))
+                                                                   out=attn_out, ws=attn_ws))
             if ev:
                 ev.around("gated_attention", fn)
             else:

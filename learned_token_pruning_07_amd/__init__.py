@@ -49,7 +49,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_seq_rmsnorm.argtypes = [vp, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select.argtypes = [vp, i, i, i, i, vp, vp, sz, vp]
     lib.tg_compact.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp]
-    lib.tg_gated_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp]
+    lib.tg_gated_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
@@ -173,11 +173,19 @@ def tg_compact(resid, keep, score, M: int, kept_idx=None, resid_out=None, score_
     return kept_idx, resid_out, score_out
 
 
+def attention_workspace(B: int, M: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for tg_gated_attention at these sizes."""
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, 0, 0))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
 def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | None = None, out=None,
-                       lse=None, want_lse: bool = False, stream=None):
+                       lse=None, want_lse: bool = False, ws=None, stream=None):
     """Token-gated causal GQA attention.  q ``[B, M, Hq, dh]``, k/v ``[B, M, Hkv, dh]`` bf16.
 
     Returns ``out`` (and ``lse [B, Hq, M]`` when ``want_lse`` or ``lse`` is given).
+    ``ws`` is a uint8 GPU tensor from :func:`attention_workspace` (allocated
+    here when omitted).
     """
     lib = load_library()
     _need(q, "q", torch.bfloat16)
@@ -198,8 +206,12 @@ def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | No
         lse = torch.empty((B, Hq, M), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, M))
+    if ws is None:
+        ws = attention_workspace(B, M, Hkv, dh, q.device)
+    _need(ws, "ws", torch.uint8)
     _check(lib.tg_gated_attention(_ptr(q), _ptr(k), _ptr(v), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
-                                  _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+                                  _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
     return (out, lse) if lse is not None else out
 
 

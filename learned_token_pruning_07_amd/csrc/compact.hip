@@ -16,10 +16,13 @@ namespace tg {
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 16;
+constexpr int kScanItems = 32;  // consecutive tokens per thread per chunk
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 4;
 
+// Every load of a chunk (keep flags and scores of kScanItems consecutive
+// tokens per thread) is issued before the block-wide scan, so a chunk costs
+// one memory round trip.
 __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_t* __restrict__ keep,
                                                                     const float* __restrict__ score, int N,
                                                                     int M, int32_t* __restrict__ kept_idx,
@@ -31,25 +34,44 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
   int32_t* ki = kept_idx + (size_t)b * M;
   float* so = score_out + (size_t)b * M;
   const int tid = threadIdx.x;
+  const bool vec = ((reinterpret_cast<uintptr_t>(kp) | reinterpret_cast<uintptr_t>(sc)) & 15u) == 0;
   uint32_t base = 0;
   for (int c0 = 0; c0 < N; c0 += kScanThreads * kScanItems) {
+    const int j0 = c0 + tid * kScanItems;
     uint8_t flags[kScanItems];
+    float sv[kScanItems];
+    if (vec && j0 + kScanItems <= N) {
+#pragma unroll
+      for (int q = 0; q < kScanItems / 16; ++q) {
+        const u32x4 w = load16(kp + j0 + q * 16);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) flags[q * 16 + e] = ((w[e >> 2] >> ((e & 3) * 8)) & 0xFFu) != 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kScanItems / 4; ++q) {
+        const u32x4 w = load16(sc + j0 + q * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[q * 4 + e] = __uint_as_float(w[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanItems; ++e) {
+        const int j = j0 + e;
+        flags[e] = (j < N && kp[j] != 0) ? 1 : 0;
+        sv[e] = j < N ? sc[j] : 0.0f;
+      }
+    }
     uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < kScanItems; ++e) {
-      const int j = c0 + tid * kScanItems + e;
-      flags[e] = (j < N && kp[j] != 0) ? 1 : 0;
-      cnt += flags[e];
-    }
+    for (int e = 0; e < kScanItems; ++e) cnt += flags[e];
     uint32_t tot;
     uint32_t dst = base + block_excl_scan_u32(cnt, s_wave, tot);
 #pragma unroll
     for (int e = 0; e < kScanItems; ++e) {
       if (flags[e]) {
-        const int j = c0 + tid * kScanItems + e;
         if ((int)dst < M) {
-          ki[dst] = j;
-          so[dst] = sc[j];
+          ki[dst] = j0 + e;
+          so[dst] = sv[e];
         }
         ++dst;
       }

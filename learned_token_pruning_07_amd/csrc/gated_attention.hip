@@ -5,7 +5,8 @@
 //   z_ij = (q_i . k_j) * sm_scale / (temp_h * ratio_i) + gain_h * b_j,  j <= i
 //   ratio_i = 1 if pos_i == i else ln(max(pos_i+1, 2)) / ln(max(i+1, 2))
 //
-// Flash-style forward on gfx950, bf16 MFMA 32x32x16 with fp32 accumulation.
+// Flash-style forward on gfx950: Q.K^T on bf16 MFMA 32x32x16, P.V on fp16 MFMA
+// 32x32x16, fp32 accumulation, fp32 softmax.
 //  * Workgroup = 4 waves = the G query heads of one KV head x (4/G) groups of
 //    32 query rows, so every K/V tile staged in LDS serves G heads.
 //  * Scores are computed transposed, S^T = K Q^T: a lane owns one query and
@@ -16,9 +17,15 @@
 //  * The logit is formed in the log2 domain with one FMA per element:
 //    z = s * (sm_scale*log2e/tau_i) + (gain_h*log2e) * b_j, the key term
 //    pre-multiplied per head when the tile is staged.
-//  * K tiles are stored row-major, V tiles transposed (V^T, key-contiguous);
-//    both padded so fragment reads and transposing writes avoid bank
-//    conflicts.  Tiles are double-buffered through registers.
+//  * The P.V product runs in fp16 (v_mfma_f32_32x32x16_f16): the softmax
+//    numerator P lies in [0, 1], where fp16 keeps 11 significant bits against
+//    bf16's 8, so rounding P costs 8x less.  V is converted once per call by
+//    a prepass into V^T (key-contiguous) fp16 scaled by 2^-8: bf16 values
+//    convert exactly up to |v| = 65504 * 2^8 (larger values saturate), values
+//    below 2^-6 land in fp16's subnormal range with an absolute error under
+//    2^-16.  The 2^8 is folded into the final 1/l.
+//  * K tiles are stored row-major (bf16) and V^T tiles key-contiguous (fp16)
+//    in LDS, padded rows, double-buffered through registers.
 //  * Grid: heaviest causal query blocks first, remapped so that every
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
@@ -32,9 +39,42 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;  // keys per tile
 
+constexpr int kVScaleLog2 = 8;  // V^T holds fp16(V * 2^-8)
+
+// V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled, zero-padded to Mp).
+template <int DH>
+__global__ __launch_bounds__(kThreads) void v_to_f16t_kernel(const uint16_t* __restrict__ v, int M, int Mp, int Hkv,
+                                                             uint16_t* __restrict__ vt) {
+  __shared__ uint16_t sT[DH][kBK + 2];
+  const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const float scale = 1.0f / (float)(1 << kVScaleLog2);
+  for (int c = tid; c < kBK * DH / 8; c += kThreads) {
+    const int key = c / (DH / 8), part = c % (DH / 8);
+    const int m = m0 + key;
+    const u32x4 w = m < M ? load16(v + (((size_t)b * M + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // round toward zero: exact for every in-range value, saturates beyond
+      const uint32_t h2 =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[i]) * scale, bf16_hi(w[i]) * scale));
+      sT[part * 8 + 2 * i][key] = (uint16_t)(h2 & 0xFFFFu);
+      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < DH * (kBK / 8); c += kThreads) {
+    const int d = c / (kBK / 8), kc = c % (kBK / 8);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (uint32_t)sT[d][kc * 8 + 2 * i] | ((uint32_t)sT[d][kc * 8 + 2 * i + 1] << 16);
+    store16(vt + (((size_t)b * Hkv + g) * DH + d) * Mp + m0 + kc * 8, o);
+  }
+}
+
 template <int DH, int G>
-__global__ __launch_bounds__(kThreads) void gated_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int M,
+__global__ __launch_bounds__(kThreads, 2) void gated_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt, int M, int Mp,
     int Hq, int Hkv, const float* __restrict__ key_score, const int32_t* __restrict__ pos,
     const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nqb, int total_wg) {
@@ -43,10 +83,10 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
   constexpr int KS = DH / 16;      // k-steps of S^T = K Q^T
   constexpr int DT = DH / 32;      // 32-row tiles of O^T
   constexpr int LDK = DH + 8;      // sK row stride (bf16)
-  constexpr int LDV = kBK + 4;     // sVt row stride (bf16)
+  constexpr int LDV = kBK + 8;     // sVt row stride (fp16), 16-byte aligned rows
   constexpr int KCH = kBK * DH / 8;          // 16-byte chunks of a K tile
   constexpr int KL = KCH / kThreads;         // per thread
-  constexpr int VCH = (kBK / 2) * (DH / 8);  // key-pair chunks of a V tile
+  constexpr int VCH = DH * (kBK / 8);        // 16-byte chunks of a V^T tile
   constexpr int VL = VCH / kThreads;
   static_assert(KL >= 1 && VL >= 1, "tile shape");
 
@@ -54,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2][DH * LDV];
   __shared__ __attribute__((aligned(16))) float sBias[2][G][kBK];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: branches on it stay scalar
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bg = logical / nqb;
   const int qb = nqb - 1 - (logical - bg * nqb);
@@ -88,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
   }
 
   // ---- tile staging ----
-  u32x4 rk[KL], rv0[VL], rv1[VL];
+  const uint16_t* vt_g = vt + ((size_t)b * Hkv + g) * DH * Mp;
+  u32x4 rk[KL], rv[VL];
   float rb = 0.0f;
   auto load_tile = [&](int kb) {
     const int key0 = kb * kBK;
@@ -102,11 +144,8 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
 #pragma unroll
     for (int e = 0; e < VL; ++e) {
       const int c = tid + kThreads * e;
-      const int kp = c % 32, j = c / 32;
-      const int dc = (j & ~3) | ((j & 1) << 1) | ((j >> 1) & 1);
-      const int k0 = key0 + 2 * kp;
-      rv0[e] = k0 < M ? load16(v + (((size_t)b * M + k0) * Hkv + g) * DH + dc * 8) : u32x4{0, 0, 0, 0};
-      rv1[e] = k0 + 1 < M ? load16(v + (((size_t)b * M + k0 + 1) * Hkv + g) * DH + dc * 8) : u32x4{0, 0, 0, 0};
+      const int d = c / (kBK / 8), kc = c % (kBK / 8);
+      rv[e] = load16(vt_g + (size_t)d * Mp + key0 + kc * 8);  // Mp is padded and zero-filled
     }
     if (tid < G * kBK) {
       const int kk = key0 + (tid % kBK);
@@ -123,15 +162,8 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
 #pragma unroll
     for (int e = 0; e < VL; ++e) {
       const int c = tid + kThreads * e;
-      const int kp = c % 32, j = c / 32;
-      const int dc = (j & ~3) | ((j & 1) << 1) | ((j >> 1) & 1);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sVt[buf][(dc * 8) * LDV + 2 * kp]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = rv0[e][w], c2 = rv1[e][w];
-        dst[(2 * w) * (LDV / 2)] = (a & 0xFFFFu) | (c2 << 16);
-        dst[(2 * w + 1) * (LDV / 2)] = (a >> 16) | (c2 & 0xFFFF0000u);
-      }
+      const int d = c / (kBK / 8), kc = c % (kBK / 8);
+      store16(&sVt[buf][d * LDV + kc * 8], rv[e]);
     }
     if (tid < G * kBK) {
       const int hh = tid / kBK;
@@ -150,94 +182,105 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
   store_tile(0);
   __syncthreads();
 
+  // One 64-key tile for this wave's 32 queries.  `diag` (wave-uniform): the
+  // tile reaches past the wave's first query (diagonal or ragged tail), so
+  // keys after the query are masked; every other tile skips that block.
+  auto tile = [&](int buf, int key0, bool diag) {
+    // S^T = K Q^T for the two 32-key halves, the two accumulation chains
+    // interleaved so consecutive MFMAs are independent
+    f32x16 s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.0f;
+      s1[i] = 0.0f;
+    }
+    const uint16_t* kr0 = &sK[buf][ql * LDK + gq * 8];
+    const uint16_t* kr1 = kr0 + 32 * LDK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr0 + ks * 16);
+      const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kr1 + ks * 16);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s1, 0, 0, 0);
+    }
+    // logits (log2 domain); lane holds keys 32T + 8(i/4) + 4gq + (i%4)
+    auto logits = [&](f32x16& st, int T) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(&sBias[buf][hloc][T * 32 + i4 * 8 + gq * 4]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i4 * 4 + i] = fmaf(st[i4 * 4 + i], cq, bb[i]);
+      }
+    };
+    logits(s0, 0);
+    logits(s1, 1);
+    if (diag) {
+      // key offset inside the tile (minus this lane's 4*gq) beyond thr => masked
+      const int thr = qi - key0 - gq * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = (i >> 2) * 8 + (i & 3);
+        s0[i] = off > thr ? -INFINITY : s0[i];
+        s1[i] = off + 32 > thr ? -INFINITY : s1[i];
+      }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(s0[i], s1[i]));
+    mloc = pair_max(mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.0f;
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(s0[i] - m_new);
+      const float p1 = __builtin_amdgcn_exp2f(s0[i + 1] - m_new);
+      const float p2 = __builtin_amdgcn_exp2f(s1[i] - m_new);
+      const float p3 = __builtin_amdgcn_exp2f(s1[i + 1] - m_new);
+      lsum += (p0 + p1) + (p2 + p3);
+      pk[0][i / 2] = pack_f16x2(p0, p1);
+      pk[1][i / 2] = pack_f16x2(p2, p3);
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+    if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+    // O^T += V^T P^T over 4 steps of 16 keys
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int T = st >> 1, h8 = (st & 1) * 4;
+      const u32x4 pw = {pk[T][h8], pk[T][h8 + 1], pk[T][h8 + 2], pk[T][h8 + 3]};
+      const f16x8 pf = as_f16x8(pw);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const uint16_t* vr = &sVt[buf][(t * 32 + ql) * LDV + st * 16 + gq * 4];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+        const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw), pf, o[t], 0, 0, 0);
+      }
+    }
+  };
+
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
     const bool more = kb + 1 < nkb;
     if (more) load_tile(kb + 1);
-
     const int key0 = kb * kBK;
-    if (wave_rows && key0 <= rbase + 31) {
-      // S^T = K Q^T for the two 32-key halves of the tile
-      f32x16 s[2];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[T][i] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(&sK[buf][(T * 32 + ql) * LDK + ks * 16 + gq * 8]);
-          s[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[T], 0, 0, 0);
-        }
-      }
-      // logits (log2 domain); lane holds keys 32T + 8(i/4) + 4gq + (i%4)
-      const bool diag = key0 + kBK - 1 > rbase;
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 bb = *reinterpret_cast<const f32x4*>(&sBias[buf][hloc][T * 32 + i4 * 8 + gq * 4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float z = fmaf(s[T][i4 * 4 + i], cq, bb[i]);
-            if (diag) {
-              const int key = key0 + T * 32 + i4 * 8 + gq * 4 + i;
-              z = key > qi ? -INFINITY : z;
-            }
-            s[T][i4 * 4 + i] = z;
-            mloc = fmaxf(mloc, z);
-          }
-        }
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.0f;
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(s[T][i] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(s[T][i + 1] - m_new);
-          lsum += p0 + p1;
-          pk[T][i / 2] = pack_bf16x2(p0, p1);
-        }
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-      if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-      }
-      // O^T += V^T P^T over 4 steps of 16 keys
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int T = st >> 1, h8 = (st & 1) * 4;
-        const u32x4 pw = {pk[T][h8], pk[T][h8 + 1], pk[T][h8 + 2], pk[T][h8 + 3]};
-        const bf16x8 pf = as_bf16x8(pw);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const uint16_t* vr = &sVt[buf][(t * 32 + ql) * LDV + st * 16 + gq * 4];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-          const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pf, o[t], 0, 0, 0);
-        }
-      }
-    }
-
+    if (wave_rows && key0 <= rbase + 31) tile(buf, key0, key0 + kBK - 1 > rbase);  // wave-uniform
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   if (!wave_rows) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   if (!q_ok) return;
-  const float inv = 1.0f / l_tot;
+  const float inv = (float)(1 << kVScaleLog2) / l_tot;
   uint16_t* op = out + (((size_t)b * M + qi) * Hq + hq) * DH;
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -256,26 +299,37 @@ __global__ __launch_bounds__(kThreads) void gated_attn_kernel(
 template <int DH, int G>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq, int Hkv,
                     const float* ks, const int32_t* pos, const float* gain, const float* temp, float sm_scale,
-                    uint16_t* out, float* lse, hipStream_t s) {
+                    uint16_t* out, float* lse, uint16_t* vt, hipStream_t s) {
   constexpr int BQ = 32 * (4 / G);
+  const int Mp = (M + kBK - 1) / kBK * kBK;
+  hipLaunchKernelGGL((v_to_f16t_kernel<DH>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, M, Mp, Hkv, vt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int nqb = (M + BQ - 1) / BQ;
   const long long total = (long long)nqb * Hkv * B;
   if (total <= 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G>), dim3((unsigned)total), dim3(kThreads), 0, s, q, k, v, M, Hq,
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G>), dim3((unsigned)total), dim3(kThreads), 0, s, q, k, vt, M, Mp, Hq,
                      Hkv, ks, pos, gain, temp, sm_scale, out, lse, nqb, (int)total);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gated_attention_workspace(int B, int M, int Hkv, int dh) {
+  const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
+  return (size_t)B * Hkv * dh * Mp * 2;
+}
+
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq,
                                   int Hkv, int dh, const float* key_score, const int32_t* pos, const float* gain,
-                                  const float* temp, float sm_scale, uint16_t* out, float* lse, hipStream_t s) {
+                                  const float* temp, float sm_scale, uint16_t* out, float* lse, void* ws,
+                                  hipStream_t s) {
   const int G = Hq / Hkv;
-#define TG_ATTN_CASE(DHV, GV)                                                                               \
-  if (dh == DHV && G == GV)                                                                                 \
-    return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, s);
+  uint16_t* vt = static_cast<uint16_t*>(ws);
+#define TG_ATTN_CASE(DHV, GV)                                                                                \
+  if (dh == DHV && G == GV)                                                                                  \
+    return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, s);
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 4)

@@ -38,7 +38,12 @@ int tg_version(void) { return 10000; }
 const char* tg_last_error(void) { return g_err; }
 
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
-  (void)op; (void)B; (void)N; (void)d; (void)h; (void)K;
+  (void)h; (void)K;
+  if (op == TG_OP_GATED_ATTENTION) {
+    if (B <= 0 || N <= 0 || d <= 0) return 0;
+    // d = Hkv * d_h; the V^T copy is B * Hkv * d_h * round_up(M, 64) fp16 values
+    return tg::gated_attention_workspace(B, N, 1, d);
+  }
   return 0;
 }
 
@@ -120,7 +125,7 @@ int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* ke
 
 int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,
                        const float* key_score, const int32_t* pos, const float* gain, const float* temp,
-                       float sm_scale, void* out, float* lse, void* stream) {
+                       float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "tg_gated_attention: bad sizes");
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "tg_gated_attention: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
   if (M == 0) return TG_OK;
@@ -134,9 +139,13 @@ int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4)
     return fail(TG_EUNSUPPORTED, "tg_gated_attention: Hq/Hkv=%d not in {1,2,4}", G);
+  const size_t need = tg::gated_attention_workspace(B, M, Hkv, d_h);
+  if (!ws || ws_bytes < need)
+    return fail(TG_EINVAL, "tg_gated_attention: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gated_attention: misaligned workspace");
   return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
-                                               pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse,
+                                               pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse, ws,
                                                reinterpret_cast<hipStream_t>(stream)),
                     "tg_gated_attention");
 }

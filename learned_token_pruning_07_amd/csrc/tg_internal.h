@@ -31,6 +31,9 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                   int M, int Hq, int Hkv, int dh, const float* key_score,
                                   const int32_t* pos, const float* gain, const float* temp,
-                                  float sm_scale, uint16_t* out, float* lse, hipStream_t s);
+                                  float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s);
+
+// Workspace bytes of launch_gated_attention: the fp16 V^T copy.
+size_t gated_attention_workspace(int B, int M, int Hkv, int dh);
 
 }  // namespace tg

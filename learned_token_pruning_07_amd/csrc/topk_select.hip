@@ -22,7 +22,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kLdsKeys = 32768;
-constexpr int kItems = 8;  // consecutive keys per thread in the final pass
+constexpr int kItems = 16;  // consecutive keys per thread in the final pass
+constexpr int kBatch = 16;  // loads in flight per thread when the keys are re-read from global memory
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,7 +55,19 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 
   const bool cached = P <= kLdsKeys;
   if (cached) {
-    for (int j = tid; j < P; j += kThreads) s_keys[j] = order_key(sc[j]);
+    // all loads of a thread are issued before any is used (latency-bound)
+    constexpr int kLoad = kLdsKeys / kThreads;
+    float f[kLoad];
+#pragma unroll
+    for (int e = 0; e < kLoad; ++e) {
+      const int j = e * kThreads + tid;
+      f[e] = j < P ? sc[j] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kLoad; ++e) {
+      const int j = e * kThreads + tid;
+      if (j < P) s_keys[j] = order_key(f[e]);
+    }
   }
 
   uint32_t prefix = 0, pmask = 0, krem = (uint32_t)Kp;
@@ -64,9 +77,26 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < nb; i += kThreads) s_hist[i] = 0;
     __syncthreads();
-    for (int j = tid; j < P; j += kThreads) {
-      const uint32_t key = cached ? s_keys[j] : order_key(sc[j]);
-      if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+    if (cached) {
+      for (int j = tid; j < P; j += kThreads) {
+        const uint32_t key = s_keys[j];
+        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    } else {
+      for (int c0 = 0; c0 < P; c0 += kThreads * kBatch) {
+        float f[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int j = c0 + e * kThreads + tid;
+          f[e] = j < P ? sc[j] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int j = c0 + e * kThreads + tid;
+          const uint32_t key = order_key(f[e]);
+          if (j < P && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
     }
     __syncthreads();
     // Bins in descending digit order; thread t owns descending bins

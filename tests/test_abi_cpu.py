@@ -42,8 +42,11 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_workspace(lib):
     assert lib.tg_version() == 10000
-    for op in range(5):
+    for op in range(4):
         assert lib.tg_workspace_size(op, 1, 16384, 2048, 256, 1638) == 0
+    # attention: fp16 V^T copy, kept length padded to 64 keys
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 0, 0) == 8 * 128 * 3392 * 2
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 0, 0) == 2 * 2 * 64 * 64 * 2
 
 
 def _err(lib):
@@ -99,10 +102,11 @@ def test_compact_validation(lib):
 def test_attention_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, M=64, Hq=16, Hkv=8, dh=128, ks=FAKE, pos=FAKE, gain=FAKE, temp=FAKE,
-                 scale=0.088, out=FAKE, lse=NULL)
+                 scale=0.088, out=FAKE, lse=NULL, ws=FAKE, ws_bytes=1 << 30)
         a.update(kw)
         return lib.tg_gated_attention(a["q"], a["k"], a["v"], a["B"], a["M"], a["Hq"], a["Hkv"], a["dh"], a["ks"],
-                                      a["pos"], a["gain"], a["temp"], a["scale"], a["out"], a["lse"], None)
+                                      a["pos"], a["gain"], a["temp"], a["scale"], a["out"], a["lse"], a["ws"],
+                                      a["ws_bytes"], None)
 
     assert call(Hkv=5) == tgb.TG_EINVAL and "multiple" in _err(lib)
     assert call(dh=96) == tgb.TG_EUNSUPPORTED
@@ -112,6 +116,9 @@ def test_attention_validation(lib):
     assert call(scale=0.0) == tgb.TG_EINVAL
     assert call(B=0) == tgb.TG_EINVAL
     assert call(M=0, q=NULL) == tgb.TG_OK             # empty kept set: a no-op that touches nothing
+    assert call(ws=NULL) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(ws_bytes=1000) == tgb.TG_EINVAL
+    assert call(ws=FAKE_ODD) == tgb.TG_EINVAL
 
 
 def test_python_binding_refuses_cpu_tensors():
