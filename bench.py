@@ -181,10 +181,12 @@ def main():
     kept_idx = torch.empty((1, M), dtype=torch.int32, device=dev)
     resid_S = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
     b_S = torch.empty((1, M), dtype=torch.float32, device=dev)
+    gate_ws = tg.gate_workspace(h, d, dev)
 
     def gate(x, ev=None):
         run = (lambda name, fn: ev.around(name, fn)) if ev else (lambda name, fn: fn())
-        run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score))
+        run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
+                                                   ws=gate_ws))
         run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score))
         run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep))
         run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,

@@ -72,11 +72,14 @@ typedef enum {
  *   w2        [h]        dtype `dt`   second linear layer (one output)
  *   b2        [1]        fp32
  *   score_raw [B, N]     fp32 output (the raw score b~)
- *   ws, ws_bytes         workspace; pass tg_workspace_size(TG_OP_GATE_SCORE,...)
- *                        bytes (0 today: ws may be NULL)
- * Supported: TG_BF16 with d % 8 == 0 and h in {64, 128, 256} (bf16 MFMA,
- * fp32 accumulation); TG_F32 with d % 4 == 0, d <= 4096 and h <= 1024 (fp32
- * FMA).  Other shapes return TG_EUNSUPPORTED.
+ *   ws, ws_bytes         workspace of at least tg_workspace_size(TG_OP_GATE_SCORE,
+ *                        B, N, d, h, K) = h * d * 2 bytes, 16-byte aligned (holds
+ *                        W1 with the RMSNorm weight folded in; bf16 path only,
+ *                        may be NULL for TG_F32)
+ * Supported: TG_BF16 with d % 64 == 0, h in {64, 128, 256} and at most 2 GiB
+ * per batch row (bf16 MFMA, fp32 accumulation; the product W1 * norm_w is
+ * rounded to bf16, exact when norm_w is 1); TG_F32 with d % 4 == 0,
+ * d <= 4096 and h <= 1024 (fp32 FMA).  Other shapes return TG_EUNSUPPORTED.
  */
 int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r,
                   const void* norm_w, float eps_row,

@@ -100,8 +100,18 @@ def _dt(t: torch.Tensor) -> int:
 
 
 # --------------------------------------------------------------- entry points
-def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None, stream=None):
-    """Row RMSNorm + scoring MLP -> raw scores ``[B, N]`` fp32 (0 for j < r)."""
+def gate_workspace(h: int, d: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for tg_gate_score at these sizes."""
+    n = int(load_library().tg_workspace_size(TG_OP_GATE_SCORE, 1, 1, d, h, 0))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None, ws=None,
+                  stream=None):
+    """Row RMSNorm + scoring MLP -> raw scores ``[B, N]`` fp32 (0 for j < r).
+
+    ``ws`` is a uint8 GPU tensor from :func:`gate_workspace` (allocated here
+    when omitted)."""
     lib = load_library()
     _need(resid, "resid")
     B, N, d = resid.shape
@@ -114,8 +124,11 @@ def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, 
     if score_raw is None:
         score_raw = torch.empty((B, N), dtype=torch.float32, device=resid.device)
     _need(score_raw, "score_raw", torch.float32, (B, N))
+    if ws is None:
+        ws = gate_workspace(h, d, resid.device)
+    _need(ws, "ws", torch.uint8)
     _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, _ptr(norm_w), eps_row, _ptr(W1), _ptr(b1), h,
-                             _ptr(w2), _ptr(b2), _ptr(score_raw), None, 0, _stream(stream)))
+                             _ptr(w2), _ptr(b2), _ptr(score_raw), _ptr(ws), ws.numel(), _stream(stream)))
     return score_raw
 
 
@@ -223,14 +236,15 @@ def tg_version() -> int:
     return int(load_library().tg_version())
 
 
-def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e-6, eps_seq=1e-6, stream=None):
+def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e-6, eps_seq=1e-6, ws=None,
+                       stream=None):
     """The gate at layer L, end to end: score -> sequence norm -> top-K -> compaction.
 
     Returns ``(kept_idx, resid_S, b_S, keep, score)``.  Four library calls on
     one stream, no host synchronisation (M is known on the host).
     """
     B, N, _ = resid.shape
-    raw = tg_gate_score(resid, r, norm_w, W1, b1, w2, b2, eps_row, stream=stream)
+    raw = tg_gate_score(resid, r, norm_w, W1, b1, w2, b2, eps_row, ws=ws, stream=stream)
     score = tg_seq_rmsnorm(raw, r, eps_seq, score=raw, stream=stream)
     keep = tg_topk_select(score, r, K, stream=stream)
     M = kept_count(N, r, K)

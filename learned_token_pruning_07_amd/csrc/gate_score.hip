@@ -3,18 +3,28 @@
 //     a~_j = a_j * w / sqrt(mean(a_j^2) + eps),   b~_j = w2 . silu(W1 a~_j + b1) + b2
 // and b~_j = 0 for the non-prunable tokens j < r.
 //
-// bf16 path (the HBM-bound one): one workgroup of 4 waves owns a tile of
-// kRows tokens and ALL h hidden units, so the h -> 1 reduction closes inside
-// the workgroup (no cross-workgroup traffic, fixed summation order).
-//  * The residual tile streams HBM -> registers (non-temporal: read once) ->
-//    LDS in 64-column chunks, double-buffered.  On the way the row's sum of
-//    squares is accumulated and the RMSNorm weight is applied; the 1/rms
-//    factor is folded into the epilogue: W1 (w (.) a) * inv_rms.
-//  * Wave w computes all kRows tokens x its h/4 hidden units with
-//    v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  Its W1 slice streams from
-//    L2 (W1 is 1 MiB at d=2048, h=256, shared by every workgroup) straight
-//    into MFMA B-fragments, one chunk ahead.
-//  * Epilogue: u = acc * inv_rms + b1, silu, times w2, summed over the wave's
+// bf16 path (the HBM-bound one):
+//  * A prepass folds the RMSNorm weight into the first layer once per call,
+//    W1w = bf16(W1 * diag(w)) (exact when w = 1), so that W1 a~_j =
+//    (W1w a_j) / rms(a_j) and the residual enters the MFMA untouched.  It
+//    writes W1w in fragment order: the 64 lanes' B fragments of one
+//    (chunk, k-step, wave, column tile) are 1 KiB contiguous, so every
+//    fragment load reads whole cache lines.
+//  * One workgroup of 4 waves owns a tile of ROWS tokens and ALL h hidden
+//    units, so the h -> 1 reduction closes inside the workgroup (no
+//    cross-workgroup traffic, fixed summation order).
+//  * The residual tile streams HBM -> registers -> LDS in 64-column chunks:
+//    loads run kDepth chunks ahead in a register ring (enough bytes in flight
+//    per CU to cover HBM latency), LDS is double-buffered.  Wave w computes
+//    every row of the tile x its h/4 hidden units with
+//    v_mfma_f32_16x16x32_bf16 (fp32 accumulate), its W1w slice streaming from
+//    L2 straight into B fragments one chunk ahead.  All global loads are raw
+//    buffer loads with a scalar chunk offset: the loop issues no address
+//    arithmetic and no per-element VALU work.
+//  * Each row's sum of squares comes from the matrix cores too: wave w also
+//    multiplies its own row tile's A fragment with itself, whose diagonal is
+//    sum_k a_jk^2 (fp32 accumulation of exact bf16 products).
+//  * Epilogue: u = acc / rms + b1, silu, times w2, summed over the wave's
 //    hidden units (16-lane butterfly), then over the 4 waves in LDS in fixed
 //    order.
 // fp32 path (small parity workloads): plain fp32 FMA with the normalised rows
@@ -30,89 +40,105 @@ constexpr int kWaves = 4;
 constexpr int kKC = 64;             // residual columns per chunk
 constexpr int kLda = kKC + 8;       // padded LDS row (bf16): conflict-free fragment reads
 constexpr int kTpr = kKC / 8;       // threads per row per chunk (16 bytes each)
+constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
+constexpr int kDepth = 4;           // residual chunks in flight per workgroup
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
 
+// Fragment-order W1w: 16-byte unit u = (((c * 2 + ks) * kWaves + w) * CT + ct) * 64 + l holds
+// bf16(W1[n][k + i] * norm_w[k + i]), i < 8, with n = w * (h / kWaves) + ct * 16 + (l & 15) and
+// k = c * kKC + ks * 32 + (l >> 4) * 8: the B fragment lane l of wave w feeds to its
+// MFMAs for column tile ct in k-step ks of chunk c.
+__global__ __launch_bounds__(kThreads) void fold_norm_weight_kernel(const uint16_t* __restrict__ W1,
+                                                                    const uint16_t* __restrict__ w, int d, int h,
+                                                                    uint16_t* __restrict__ W1f) {
+  const int u = blockIdx.x * kThreads + threadIdx.x;
+  const int CT = h / (kWaves * 16);
+  if (u >= h * d / 8) return;
+  const int l = u & 63;
+  int q = u >> 6;
+  const int ct = q % CT;
+  q /= CT;
+  const int wv = q % kWaves;
+  q /= kWaves;  // q = c * 2 + ks
+  const int n = wv * (h / kWaves) + ct * 16 + (l & 15);
+  const int k = q * 32 + (l >> 4) * 8;
+  const u32x4 a = load16(W1 + (size_t)n * d + k), s = load16(w + k);
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(bf16_lo(a[j]) * bf16_lo(s[j]), bf16_hi(a[j]) * bf16_hi(s[j]));
+  store16(W1f + (size_t)u * 8, o);
+}
+
 template <int H, int ROWS>
-__global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(
-    const uint16_t* __restrict__ resid, int N, int d, int r, const uint16_t* __restrict__ norm_w, float eps_row,
-    const uint16_t* __restrict__ W1, const float* __restrict__ b1, const uint16_t* __restrict__ w2,
-    const float* __restrict__ b2, float* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
+                                                                   int d, int r, float eps_row,
+                                                                   const uint16_t* __restrict__ W1w,
+                                                                   const float* __restrict__ b1,
+                                                                   const uint16_t* __restrict__ w2,
+                                                                   const float* __restrict__ b2,
+                                                                   float* __restrict__ out) {
   constexpr int RT = ROWS / 16;               // 16-row MFMA tiles (each wave covers every row)
   constexpr int CT = H / (kWaves * 16);       // 16-column MFMA tiles per wave
   constexpr int AL = ROWS * kTpr / kThreads;  // 16-byte residual loads per thread per chunk
-  static_assert(AL >= 1 && CT >= 1, "tile shape");
+  constexpr int GR = RT / kWaves;             // row tiles whose sum of squares this wave computes
+  static_assert(AL >= 1 && CT >= 1 && GR >= 1, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * kLda];
   __shared__ float s_inv[ROWS];
   __shared__ float s_part[kWaves][ROWS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
   const int row0 = r + blockIdx.x * ROWS;
-  const uint16_t* Rb = resid + (size_t)b * N * d;
   float* ob = out + (size_t)b * N;
 
   for (int j = blockIdx.x * kThreads + tid; j < r; j += gridDim.x * kThreads) ob[j] = 0.0f;
   if (row0 >= N) return;  // whole workgroup: no barrier is skipped by part of it
 
-  // residual staging slots: slot e covers row (tid + 256 e) / kTpr, columns kp*8..kp*8+7
+  // residual tile: rows past N read as 0 through the buffer range check
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(resid + ((size_t)b * N + row0) * d), (short)0, (int)((size_t)(N - row0) * d * 2),
+      kBufferConfig);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W1w), (short)0, (int)((size_t)H * d * 2), kBufferConfig);
+  // slot e of this thread: row (tid + 256 e) / kTpr, columns kp*8 .. kp*8+7 of each chunk
   const int kp = tid % kTpr;
-  int a_row[AL];
-  bool a_ok[AL];
+  int a_off[AL], a_lds[AL];
 #pragma unroll
   for (int e = 0; e < AL; ++e) {
-    a_row[e] = (tid + kThreads * e) / kTpr;
-    a_ok[e] = row0 + a_row[e] < N;
+    const int row = (tid + kThreads * e) / kTpr;
+    a_off[e] = (row * d + kp * 8) * 2;
+    a_lds[e] = row * kLda + kp * 8;
   }
-  float ss[AL];
-#pragma unroll
-  for (int e = 0; e < AL; ++e) ss[e] = 0.0f;
-
-  // W1 rows this lane feeds into its B fragments
+  // this lane's B fragments in the fragment-ordered W1w (see fold_norm_weight_kernel)
   const int ncol0 = wid * (H / kWaves) + (lane & 15);
   const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide k-step
+  constexpr int kStepBytes = kWaves * CT * 64 * 16;  // one (chunk, k-step) of W1w
+  int w_off[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) w_off[ct] = ((wid * CT + ct) * 64 + lane) * 16;
 
-  const int nch = (d + kKC - 1) / kKC;
-  u32x4 ra[AL], rw;
+  const int nch = d / kKC;
+  u32x4 ra[kDepth][AL];  // register ring: chunk c lives in slot c % kDepth
   u32x4 bcur[2][CT], bnext[2][CT];
-
-  auto load_a = [&](int c) {
-    const int k = c * kKC + kp * 8;
-    const bool kin = k < d;
-    rw = kin ? load16(norm_w + k) : u32x4{0, 0, 0, 0};
+  auto load_a = [&](int c, u32x4 (&dst)[AL]) {
 #pragma unroll
     for (int e = 0; e < AL; ++e)
-      ra[e] = (kin && a_ok[e]) ? load16_stream(Rb + (size_t)(row0 + a_row[e]) * d + k) : u32x4{0, 0, 0, 0};
+      dst[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[e], c * kKC * 2, 0));
   };
-  auto store_a = [&](int buf) {
-    float w[8];
+  auto store_a = [&](int buf, const u32x4 (&src)[AL]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[2 * i] = bf16_lo(rw[i]);
-      w[2 * i + 1] = bf16_hi(rw[i]);
-    }
-#pragma unroll
-    for (int e = 0; e < AL; ++e) {
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = bf16_lo(ra[e][i]), hi = bf16_hi(ra[e][i]);
-        ss[e] = fmaf(lo, lo, ss[e]);
-        ss[e] = fmaf(hi, hi, ss[e]);
-        o[i] = pack_bf16x2(lo * w[2 * i], hi * w[2 * i + 1]);
-      }
-      store16(&sA[buf][a_row[e] * kLda + kp * 8], o);
-    }
+    for (int e = 0; e < AL; ++e) store16(&sA[buf][a_lds[e]], src[e]);
   };
   auto load_b = [&](int c, u32x4 (&dst)[2][CT]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int k = c * kKC + ks * 32 + kq;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        dst[ks][ct] = k < d ? load16(W1 + (size_t)(ncol0 + ct * 16) * d + k) : u32x4{0, 0, 0, 0};
-    }
+        dst[ks][ct] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ct], (c * 2 + ks) * kStepBytes, 0));
   };
 
   f32x4 acc[RT][CT];
@@ -120,49 +146,69 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 gram[GR];
+#pragma unroll
+  for (int i = 0; i < GR; ++i) gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+    if (j < nch) load_a(j, ra[j]);
   load_b(0, bcur);
-  store_a(0);
+  store_a(0, ra[0]);
   __syncthreads();
 
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nch;
-    if (more) {
-      load_a(c + 1);
-      load_b(c + 1, bnext);
+  // chunk c: MFMAs on LDS buffer c & 1 while chunk c + kDepth loads into the
+  // ring slot chunk c just vacated and chunk c + 1 moves ring -> LDS
+  for (int c0 = 0; c0 < nch; c0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int c = c0 + j;
+      if (c < nch) {  // uniform
+        const int buf = j & 1;  // == c & 1 (kDepth is even)
+        const bool more = c + 1 < nch;
+        if (c + kDepth < nch) load_a(c + kDepth, ra[j]);
+        if (more) load_b(c + 1, bnext);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 af[RT];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            af[rt] = *reinterpret_cast<const bf16x8*>(&sA[buf][(rt * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], as_bf16x8(bcur[ks][ct]), acc[rt][ct],
+                                                                    0, 0, 0);
+          // Gram tile of this wave's rows: its diagonal is the rows' sum of squares
+#pragma unroll
+          for (int i = 0; i < GR; ++i) {
+            const bf16x8 gf = *reinterpret_cast<const bf16x8*>(
+                &sA[buf][((wid + kWaves * i) * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
+            gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, gf, gram[i], 0, 0, 0);
+          }
+        }
+        if (more) {
+          store_a(buf ^ 1, ra[(j + 1) % kDepth]);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) bcur[ks][ct] = bnext[ks][ct];
+        }
+        __syncthreads();
+      }
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        af[rt] = *reinterpret_cast<const bf16x8*>(&sA[buf][(rt * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], as_bf16x8(bcur[ks][ct]), acc[rt][ct], 0,
-                                                                0, 0);
-    }
-    if (more) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) bcur[ks][ct] = bnext[ks][ct];
-    }
-    __syncthreads();
   }
 
-  // 1/rms per row: the kTpr threads of a row are consecutive lanes
+  // 1/rms per row: diagonal element (m, m) of a 16x16 C tile sits in lane
+  // m + 16 * (m / 4), register m % 4
 #pragma unroll
-  for (int e = 0; e < AL; ++e) {
-    float t = ss[e];
-#pragma unroll
-    for (int o = 1; o < kTpr; o <<= 1) t += __shfl_xor(t, o, 64);
-    if (kp == 0) s_inv[a_row[e]] = 1.0f / sqrtf(t / (float)d + eps_row);
+  for (int i = 0; i < GR; ++i) {
+    const int m = lane & 15;
+    if ((lane >> 4) == (m >> 2)) {
+      const float ssq = gram[i][m & 3];
+      s_inv[(wid + kWaves * i) * 16 + m] = 1.0f / sqrtf(ssq / (float)d + eps_row);
+    }
   }
   __syncthreads();
 
@@ -256,29 +302,37 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
 }
 
 template <int H>
-hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, const uint16_t* norm_w, float eps,
-                         const uint16_t* W1, const float* b1, const uint16_t* w2, const float* b2, float* out,
-                         hipStream_t s) {
+hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, float eps, const uint16_t* W1w,
+                         const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
+  // 64-token tiles: 128-token tiles halve the W1 bytes per token but need
+  // more registers than two waves per SIMD allow, and measure slower
   constexpr int ROWS = 64;
   const int P = N - r;
   const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
-  hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS>), dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r,
-                     norm_w, eps, W1, b1, w2, b2, out);
+  hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS>), dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, eps,
+                     W1w, b1, w2, b2, out);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gate_score_workspace(int h, int d) { return (size_t)h * d * 2; }
+
 hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, const uint16_t* norm_w,
                                   float eps_row, const uint16_t* W1, const float* b1, int h, const uint16_t* w2,
-                                  const float* b2, float* out, hipStream_t s) {
+                                  const float* b2, float* out, void* ws, hipStream_t s) {
+  uint16_t* W1w = static_cast<uint16_t*>(ws);
+  hipLaunchKernelGGL(fold_norm_weight_kernel, dim3((h * d / 8 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                     W1, norm_w, d, h, W1w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (h) {
     case 64:
-      return launch_bf16_h<64>(resid, B, N, d, r, norm_w, eps_row, W1, b1, w2, b2, out, s);
+      return launch_bf16_h<64>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
     case 128:
-      return launch_bf16_h<128>(resid, B, N, d, r, norm_w, eps_row, W1, b1, w2, b2, out, s);
+      return launch_bf16_h<128>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
     case 256:
-      return launch_bf16_h<256>(resid, B, N, d, r, norm_w, eps_row, W1, b1, w2, b2, out, s);
+      return launch_bf16_h<256>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
     default:
       return hipErrorInvalidValue;
   }

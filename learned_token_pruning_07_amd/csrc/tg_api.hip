@@ -38,7 +38,11 @@ int tg_version(void) { return 10000; }
 const char* tg_last_error(void) { return g_err; }
 
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
-  (void)h; (void)K;
+  (void)K;
+  if (op == TG_OP_GATE_SCORE) {
+    if (d <= 0 || h <= 0) return 0;
+    return tg::gate_score_workspace(h, d);  // the RMSNorm weight folded into W1 (bf16)
+  }
   if (op == TG_OP_GATED_ATTENTION) {
     if (B <= 0 || N <= 0 || d <= 0) return 0;
     // d = Hkv * d_h; the V^T copy is B * Hkv * d_h * round_up(M, 64) fp16 values
@@ -50,7 +54,6 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
 int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
                   const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
                   void* ws, size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_gate_score: unknown dtype %d", dt);
   if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "tg_gate_score: B, N, d, h must be > 0");
   if (r < 0 || r > N) return fail(TG_EINVAL, "tg_gate_score: r=%d outside [0, N=%d]", r, N);
@@ -63,13 +66,19 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const v
     return fail(TG_EINVAL, "tg_gate_score: resid, W1 and norm_w must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dt == TG_BF16) {
-    if (d % 8 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 needs d %% 8 == 0 (d=%d)", d);
+    if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 needs d %% 64 == 0 (d=%d)", d);
     if (h != 64 && h != 128 && h != 256)
       return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 supports h in {64,128,256} (h=%d)", h);
+    const size_t need = tg::gate_score_workspace(h, d);
+    if (!ws || ws_bytes < need)
+      return fail(TG_EINVAL, "tg_gate_score: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gate_score: misaligned workspace");
+    if ((size_t)(N - r) * d * 2 > 0x7FFFFFFFull)
+      return fail(TG_EUNSUPPORTED, "tg_gate_score: a batch row above 2 GiB");
     return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r,
                                                  static_cast<const uint16_t*>(norm_w), eps_row,
                                                  static_cast<const uint16_t*>(W1), b1, h,
-                                                 static_cast<const uint16_t*>(w2), b2, score_raw, s),
+                                                 static_cast<const uint16_t*>(w2), b2, score_raw, ws, s),
                       "tg_gate_score");
   }
   if (d % 4 != 0 || d > 4096 || h > 1024)

@@ -11,7 +11,10 @@ namespace tg {
 hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r,
                                   const uint16_t* norm_w, float eps_row, const uint16_t* W1,
                                   const float* b1, int h, const uint16_t* w2, const float* b2,
-                                  float* out, hipStream_t s);
+                                  float* out, void* ws, hipStream_t s);
+
+// Workspace bytes of launch_gate_score_bf16: the norm-weight-folded W1.
+size_t gate_score_workspace(int h, int d);
 
 hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r,
                                  const float* norm_w, float eps_row, const float* W1,

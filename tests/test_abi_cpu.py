@@ -42,7 +42,9 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_workspace(lib):
     assert lib.tg_version() == 10000
-    for op in range(4):
+    # scorer: W1 with the RMSNorm weight folded in (bf16)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATE_SCORE, 1, 16384, 2048, 256, 1638) == 256 * 2048 * 2
+    for op in (tgb.TG_OP_SEQ_RMSNORM, tgb.TG_OP_TOPK_SELECT, tgb.TG_OP_COMPACT):
         assert lib.tg_workspace_size(op, 1, 16384, 2048, 256, 1638) == 0
     # attention: fp16 V^T copy, kept length padded to 64 keys
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 0, 0) == 8 * 128 * 3392 * 2
@@ -55,12 +57,12 @@ def _err(lib):
 
 def test_gate_score_validation(lib):
     args = dict(resid=FAKE, dt=tgb.TG_BF16, B=1, N=128, d=256, r=4, norm_w=FAKE, eps=1e-6, W1=FAKE, b1=FAKE,
-                h=256, w2=FAKE, b2=FAKE, out=FAKE)
+                h=256, w2=FAKE, b2=FAKE, out=FAKE, ws=NULL, ws_bytes=0)
 
     def call(**kw):
         a = dict(args, **kw)
         return lib.tg_gate_score(a["resid"], a["dt"], a["B"], a["N"], a["d"], a["r"], a["norm_w"], a["eps"],
-                                 a["W1"], a["b1"], a["h"], a["w2"], a["b2"], a["out"], None, 0, None)
+                                 a["W1"], a["b1"], a["h"], a["w2"], a["b2"], a["out"], a["ws"], a["ws_bytes"], None)
 
     assert call(resid=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
     assert call(N=0) == tgb.TG_EINVAL
@@ -69,6 +71,10 @@ def test_gate_score_validation(lib):
     assert call(dt=7) == tgb.TG_EINVAL
     assert call(resid=FAKE_ODD) == tgb.TG_EINVAL and "aligned" in _err(lib)
     assert call(d=250) == tgb.TG_EUNSUPPORTED
+    assert call(d=136) == tgb.TG_EUNSUPPORTED              # bf16 MFMA path streams 64-column chunks
+    assert call() == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(ws=FAKE, ws_bytes=1000) == tgb.TG_EINVAL
+    assert call(ws=FAKE_ODD, ws_bytes=1 << 20) == tgb.TG_EINVAL
     assert call(h=96) == tgb.TG_EUNSUPPORTED
     assert call(dt=tgb.TG_F32, d=8192) == tgb.TG_EUNSUPPORTED
     assert call(eps=-1.0) == tgb.TG_EINVAL

@@ -28,7 +28,7 @@ def _oracle_scores(c, resid=None):
 @pytest.mark.parametrize("h,N,r,d,B,extras", [
     (256, 1000, 37, 512, 2, False),
     (256, 777, 64, 2048, 1, True),
-    (128, 300, 0, 136, 1, True),
+    (128, 300, 0, 192, 1, True),
     (64, 130, 129, 64, 1, False),
     (256, 64, 64, 256, 1, False),
 ])
