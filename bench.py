@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="upper layers (default: 24 for stage_32k, else 1)")
     ap.add_argument("--copies", type=int, default=0, help="residual copies rotated per step (0: enough for 512 MiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 1 GiB (5 times): the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -145,9 +148,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    tg.load_library()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}), flush=True)
+        return
+    tg.load_library()
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
