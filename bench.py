@@ -211,7 +211,7 @@ def main():
     layers = stage_glue.stage_layers(n_layers, d, **heads) if n_layers else []
     qkv = [p.qkv(resid_S) for p in layers]
     attn_out = torch.empty((1, M, heads["Hq"], heads["dh"]), dtype=torch.bfloat16, device=dev)
-    attn_ws = tg.attention_workspace(1, M, heads["Hkv"], heads["dh"], dev)
+    attn_ws = tg.attention_workspace(1, M, heads["Hq"], heads["Hkv"], heads["dh"], dev)
     torch.cuda.synchronize()
     glue_ms = 0.0
     if layers:

@@ -163,8 +163,9 @@ int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* ke
  *   out [B, M, Hq, d_h] bf16 (fp32 accumulate, round to nearest even)
  *   lse [B, Hq, M] fp32, or NULL to skip it
  *   ws, ws_bytes  workspace of at least tg_workspace_size(TG_OP_GATED_ATTENTION,
- *                 B, M, Hkv * d_h, 0, 0) bytes, 16-byte aligned (holds an fp16
- *                 transposed copy of V; contents need no initialisation)
+ *                 B, M, Hkv * d_h, Hq, 0) bytes, 16-byte aligned (holds an fp16
+ *                 transposed copy of V and the per-head key-score term
+ *                 gain[h] * key_score[j]; contents need no initialisation)
  * Precision: Q.K^T runs on bf16 MFMA; the softmax numerator and V enter the
  * P.V product as fp16 (V scaled by 2^-8, so |v| up to 1.6e7 is exact and
  * larger magnitudes saturate).
@@ -177,7 +178,8 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
- * For TG_OP_GATED_ATTENTION pass N = M (kept length) and d = Hkv * d_h. */
+ * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
+ * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq). */
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
 
 /* Message describing the last non-zero status returned on this thread. */

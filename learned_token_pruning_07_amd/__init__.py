@@ -186,9 +186,9 @@ def tg_compact(resid, keep, score, M: int, kept_idx=None, resid_out=None, score_
     return kept_idx, resid_out, score_out
 
 
-def attention_workspace(B: int, M: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
+def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
     """A workspace tensor large enough for tg_gated_attention at these sizes."""
-    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, 0, 0))
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, Hq, 0))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -220,7 +220,7 @@ def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | No
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, M))
     if ws is None:
-        ws = attention_workspace(B, M, Hkv, dh, q.device)
+        ws = attention_workspace(B, M, Hq, Hkv, dh, q.device)
     _need(ws, "ws", torch.uint8)
     _check(lib.tg_gated_attention(_ptr(q), _ptr(k), _ptr(v), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
                                   _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),

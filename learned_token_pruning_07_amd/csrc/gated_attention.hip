@@ -20,17 +20,26 @@
 //    order inside each 16-key step is permuted identically on both operands.
 //  * The logit is formed in the log2 domain with one FMA per element:
 //    z = s * (sm_scale*log2e/tau_i) + (gain_h*log2e) * b_j, the key term
-//    pre-multiplied per head when the tile is staged.
+//    pre-multiplied per head by the prepass.
 //  * The P.V product runs in fp16 (v_mfma_f32_32x32x16_f16): the softmax
 //    numerator P lies in [0, 1], where fp16 keeps 11 significant bits against
 //    bf16's 8, so rounding P costs 8x less.  V is converted once per call by
 //    a prepass into V^T (key-contiguous) fp16 scaled by 2^-8: bf16 values
 //    convert exactly up to |v| = 65504 * 2^8 (larger values saturate), values
 //    below 2^-6 land in fp16's subnormal range with an absolute error under
-//    2^-16.  The 2^8 is folded into the final 1/l.
-//  * K tiles are stored row-major (bf16) and V^T tiles key-contiguous (fp16)
-//    in LDS, padded rows, double-buffered through registers (each group
-//    stages its own tiles: 4 tiles of 36 KiB resident per workgroup).
+//    2^-16.  The 2^8 is folded into the final 1/l.  Inside every 16-key group
+//    of V^T the middle two quads of keys are swapped, so that the 8 keys one
+//    lane contributes to a 16-key P.V step (4 at 4*gq, 4 at 8 + 4*gq) form
+//    one 16-byte chunk.
+//  * Tiles travel from global memory straight into LDS (buffer loads with the
+//    LDS-destination bit: each lane's 16 bytes land at the wave's LDS base +
+//    16 * lane), double-buffered per group, so staging costs no registers and
+//    no LDS store instructions.  K rows (bf16) and V^T rows (fp16, 64 keys)
+//    are unpadded with their 16-byte chunks XOR-swizzled by (row & 7), which
+//    keeps the fragment reads free of bank conflicts; the lane-to-chunk map of
+//    each load applies the same swizzle.  The prepass also writes the
+//    key-score term of every query head, gain_h * log2(e) * b_j, so that tile
+//    too is a plain copy.
 //  * Grid: heaviest causal query blocks first, remapped so that every
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
@@ -59,10 +68,25 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled, zero-padded to Mp).
+// Key stored in slot s of a V^T tile row: the middle two quads of each
+// 16-key group are swapped.
+__device__ __forceinline__ int vt_slot_key(int s) {
+  const int q = (s >> 2) & 3;
+  const int kq = q == 1 ? 2 : (q == 2 ? 1 : q);
+  return (s & ~15) | (kq << 2) | (s & 3);
+}
+
+// Prepass, per 64-key block of KV head g:
+//   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
+//   in slot order, zero beyond M);
+//   key-score term kb [B, Hq, Mp] fp32 = gain_h * log2(e) * key_score for the
+//   G query heads of g (zero beyond M).
 template <int DH>
-__global__ __launch_bounds__(kThreads) void v_to_f16t_kernel(const uint16_t* __restrict__ v, int M, int Mp, int Hkv,
-                                                             uint16_t* __restrict__ vt) {
+__global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* __restrict__ v,
+                                                                const float* __restrict__ key_score,
+                                                                const float* __restrict__ gain, int M, int Mp,
+                                                                int Hkv, int G, uint16_t* __restrict__ vt,
+                                                                float* __restrict__ kbias) {
   __shared__ uint16_t sT[DH][kBK + 2];
   const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -80,12 +104,18 @@ __global__ __launch_bounds__(kThreads) void v_to_f16t_kernel(const uint16_t* __r
       sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
     }
   }
+  const int Hq = Hkv * G;
+  for (int c = tid; c < G * kBK; c += kThreads) {
+    const int hq = g * G + c / kBK, m = m0 + c % kBK;
+    kbias[((size_t)b * Hq + hq) * Mp + m] = m < M ? key_score[(size_t)b * M + m] * (gain[hq] * kLog2e) : 0.0f;
+  }
   __syncthreads();
   for (int c = tid; c < DH * (kBK / 8); c += kThreads) {
     const int d = c / (kBK / 8), kc = c % (kBK / 8);
     u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (uint32_t)sT[d][kc * 8 + 2 * i] | ((uint32_t)sT[d][kc * 8 + 2 * i + 1] << 16);
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i)] | ((uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i + 1)] << 16);
     store16(vt + (((size_t)b * Hkv + g) * DH + d) * Mp + m0 + kc * 8, o);
   }
 }
@@ -93,30 +123,45 @@ __global__ __launch_bounds__(kThreads) void v_to_f16t_kernel(const uint16_t* __r
 constexpr int kGroups = 2;                         // wave groups splitting a key range
 constexpr int kAttnThreads = kThreads * kGroups;   // 8 waves, 2 per SIMD
 
+// Raw buffer loads of 16 or 4 bytes per lane into LDS: lane l's data lands at
+// lds + 16 l (or 4 l); lds is wave-uniform.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset,
+                                                     int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset,
+                                           0, 0);
+}
+__device__ __forceinline__ void buffer_load4_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voffset, soffset, 0,
+                                           0);
+}
+// s_waitcnt vmcnt(0): wait for every load of this wave, LDS-destination ones included
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int DH, int G>
 __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt, int M, int Mp,
-    int Hq, int Hkv, const float* __restrict__ key_score, const int32_t* __restrict__ pos,
-    const float* __restrict__ gain, const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int nqb, int total_wg) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
+    const float* __restrict__ kbias, int M, int Mp, int Hq, int Hkv, const int32_t* __restrict__ pos,
+    const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb,
+    int total_wg) {
   constexpr int RG = 4 / G;        // 32-row groups per head
   constexpr int BQ = 32 * RG;      // query rows per workgroup
   constexpr int KS = DH / 16;      // k-steps of S^T = K Q^T
   constexpr int DT = DH / 32;      // 32-row tiles of O^T
-  constexpr int LDK = DH + 8;      // sK row stride (bf16)
-  constexpr int LDV = kBK + 4;     // sVt row stride (fp16): 34 dwords, conflict-free 8-byte reads
-  constexpr int KCH = kBK * DH / 8;          // 16-byte chunks of a K tile
-  constexpr int KL = KCH / kThreads;         // per thread
-  constexpr int VCH = DH * (kBK / 8);        // 16-byte chunks of a V^T tile
-  constexpr int VL = VCH / kThreads;
-  static_assert(KL >= 1 && VL >= 1, "tile shape");
+  constexpr int KROW = DH * 2;      // bytes of a K row in LDS (unpadded, swizzled)
+  constexpr int KCH = DH / 8;       // its 16-byte chunks
+  constexpr int VROW = kBK * 2;     // bytes of a V^T row (64 keys, fp16)
+  constexpr int TILE = kBK * DH * 2;           // bytes of a K tile = bytes of a V^T tile
+  constexpr int NI = TILE / 1024 / 4;          // 1 KiB loads per wave per tile, for each of K and V^T
+  constexpr int BIAS = G * kBK * 4;            // bytes of a key-score tile (G heads)
+  constexpr int V_BASE = 2 * kGroups * TILE, B_BASE = 4 * kGroups * TILE;
+  constexpr int LDS_BYTES = B_BASE + 2 * kGroups * BIAS;
+  static_assert(NI >= 1 && NI * 4 * 1024 == TILE, "tile shape");
 
   constexpr int NV = DT * 16 + 2;            // floats per lane handed over in the merge
-  static_assert(4 * 64 * NV * 4 <= (int)sizeof(uint16_t) * 2 * kGroups * kBK * LDK, "merge buffer");
+  static_assert(4 * 64 * NV * 4 <= B_BASE, "merge buffer");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kGroups][kBK * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][kGroups][DH * LDV];
-  __shared__ __attribute__((aligned(16))) float sBias[2][kGroups][G][kBK];
+  // [buf][group] K tiles, then [buf][group] V^T tiles, then [buf][group][head] key-score tiles
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wall = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: branches stay scalar
@@ -156,69 +201,55 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   }
 
   // ---- tile staging ----
-  // Raw buffer loads: each thread's offset is fixed for the whole loop.  K and
-  // the key scores get a resource per tile (base advanced to the tile, size
-  // shrunk to what is left; scalar work only), so the hardware range check
-  // returns 0 for keys >= M -- the check covers the per-lane offset only, not
-  // a scalar offset.  V^T is padded to Mp keys and zero-filled, so its tiles
-  // are always in range and share one resource with a scalar tile offset.
+  // Raw buffer loads with an LDS destination; each lane's byte offset is fixed
+  // for the whole loop.  K gets a resource per tile (base advanced to the
+  // tile, size shrunk to what is left; scalar work only), so the hardware
+  // range check returns 0 for keys >= M -- the check covers the per-lane
+  // offset only, not a scalar offset.  V^T and the key-score rows are padded
+  // to Mp keys, so their tiles are always in range and take a scalar offset.
   const uint16_t* k_base = k + ((size_t)b * M * Hkv + g) * DH;
   const long long k_bytes = (((long long)M - 1) * Hkv + 1) * DH * 2;  // up to the end of head g's last row
-  const float* b_base = key_score + (size_t)b * M;
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(vt + ((size_t)b * Hkv + g) * DH * Mp), (short)0, (int)((size_t)DH * Mp * 2),
       kBufferConfig);
-  int k_off[KL], v_off[VL];
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(kbias + ((size_t)b * Hq + g * G) * Mp), (short)0, G * Mp * 4, kBufferConfig);
+  // Load e of this wave fills LDS bytes [1024 C, 1024 C + 1024) of the tile,
+  // C = wid * NI + e: 16-byte slot Y = 64 C + lane sits at row Y / chunks-per-row,
+  // position p, and holds chunk p ^ (row & 7) of that row.
+  int k_off[NI], v_off[NI];
 #pragma unroll
-  for (int e = 0; e < KL; ++e) {
-    const int c = tid + kThreads * e;
-    k_off[e] = ((c / (DH / 8)) * Hkv * DH + (c % (DH / 8)) * 8) * 2;
+  for (int e = 0; e < NI; ++e) {
+    const int Y = (wid * NI + e) * 64 + lane;
+    const int kr = Y / KCH, kc = (Y % KCH) ^ (kr & 7);
+    k_off[e] = kr * Hkv * DH * 2 + kc * 16;
+    const int vr = Y / (VROW / 16), vc = (Y % (VROW / 16)) ^ (vr & 7);
+    v_off[e] = vr * Mp * 2 + vc * 16;
   }
-#pragma unroll
-  for (int e = 0; e < VL; ++e) {
-    const int c = tid + kThreads * e;
-    v_off[e] = ((c / (kBK / 8)) * Mp + (c % (kBK / 8)) * 8) * 2;
-  }
-  const int b_off = (tid % kBK) * 4;
-  u32x4 rk[KL], rv[VL];
-  float rb = 0.0f;
-  auto load_tile = [&](int kb) {
+  auto k_tile = [&](int buf) { return smem + (buf * kGroups + grp) * TILE; };
+  auto v_tile = [&](int buf) { return smem + V_BASE + (buf * kGroups + grp) * TILE; };
+  auto b_tile = [&](int buf) { return reinterpret_cast<float*>(smem + B_BASE + (buf * kGroups + grp) * BIAS); };
+  auto issue_tile = [&](int kb, int buf) {
     const int key0 = kb * kBK;
     const long long k_skip = (long long)key0 * Hkv * DH * 2;
     const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(k_base + (size_t)key0 * Hkv * DH), (short)0, (int)(k_bytes - k_skip), kBufferConfig);
+    unsigned char* kd = k_tile(buf) + wid * NI * 1024;
+    unsigned char* vd = v_tile(buf) + wid * NI * 1024;
 #pragma unroll
-    for (int e = 0; e < KL; ++e)
-      rk[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, k_off[e], 0, 0));
+    for (int e = 0; e < NI; ++e)
+      buffer_load16_to_lds(k_rsrc, kd + e * 1024, k_off[e], 0);
 #pragma unroll
-    for (int e = 0; e < VL; ++e)
-      rv[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, v_off[e], key0 * 2, 0));
-    if (tid < G * kBK) {
-      const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(b_base + key0), (short)0, (M - key0) * 4, kBufferConfig);
-      rb = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b_rsrc, b_off, 0, 0));
-    }
+    for (int e = 0; e < NI; ++e)
+      buffer_load16_to_lds(v_rsrc, vd + e * 1024, v_off[e], key0 * 2);
+    if (wid < G)  // one 256-byte row per query head
+      buffer_load4_to_lds(b_rsrc, b_tile(buf) + wid * kBK, (wid * Mp + lane) * 4, key0 * 4);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < KL; ++e) {
-      const int c = tid + kThreads * e;
-      const int key = c / (DH / 8), part = c % (DH / 8);
-      store16(&sK[buf][grp][key * LDK + part * 8], rk[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < VL; ++e) {
-      const int c = tid + kThreads * e;
-      const int d = c / (kBK / 8), kc = c % (kBK / 8);
-      u32x2* dst = reinterpret_cast<u32x2*>(&sVt[buf][grp][d * LDV + kc * 8]);
-      dst[0] = u32x2{rv[e][0], rv[e][1]};
-      dst[1] = u32x2{rv[e][2], rv[e][3]};
-    }
-    if (tid < G * kBK) {
-      const int hh = tid / kBK;
-      sBias[buf][grp][hh][tid % kBK] = rb * (gain[g * G + hh] * kLog2e);
-    }
-  };
+  // this lane's fragment chunks: K row ql (and ql + 32) chunk 2ks + gq; V^T row
+  // 32t + ql chunk 2st + gq -- both swizzled by ql & 7
+  const int q7 = ql & 7;
+  auto k_frag_off = [&](int ks) { return ql * KROW + (((2 * ks + gq) ^ q7) << 4); };
+  auto v_frag_off = [&](int st) { return ql * VROW + (((2 * st + gq) ^ q7) << 4); };
 
   f32x16 o[DT];
 #pragma unroll
@@ -239,12 +270,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
       s0[i] = 0.0f;
       s1[i] = 0.0f;
     }
-    const uint16_t* kr0 = &sK[buf][grp][ql * LDK + gq * 8];
-    const uint16_t* kr1 = kr0 + 32 * LDK;
+    const unsigned char* kt = k_tile(buf);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kr0 + ks * 16);
-      const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kr1 + ks * 16);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks));
+      const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks) + 32 * KROW);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s1, 0, 0, 0);
     }
@@ -252,7 +282,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
     auto logits = [&](f32x16& st, int T) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(&sBias[buf][grp][hloc][T * 32 + i4 * 8 + gq * 4]);
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(b_tile(buf) + hloc * kBK + T * 32 + i4 * 8 + gq * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[i4 * 4 + i] = fmaf(st[i4 * 4 + i], cq, bb[i]);
       }
@@ -269,10 +299,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
         s1[i] = off + 32 > thr ? -INFINITY : s1[i];
       }
     }
-    float mloc = -INFINITY;
+    // tile max: a max3 tree over the 32 logits, then the partner lane's
+    float x[11];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mloc = max3f(mloc, s0[i], s1[i]);
-    mloc = pair_max(mloc);
+    for (int j = 0; j < 5; ++j) {
+      x[2 * j] = max3f(s0[3 * j], s0[3 * j + 1], s0[3 * j + 2]);
+      x[2 * j + 1] = max3f(s1[3 * j], s1[3 * j + 1], s1[3 * j + 2]);
+    }
+    x[10] = max3f(s0[15], s1[15], s1[15]);
+    float mloc = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], max3f(x[8], x[9], x[10])));
+    {
+      const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
+      mloc = max3f(__uint_as_float(pr[0]), __uint_as_float(pr[1]), __uint_as_float(pr[1]));
+    }
     if (__ballot(mloc > m_run + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_run, mloc);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -307,35 +346,31 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
       const f16x8 pf = as_f16x8(pw);
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const uint16_t* vr = &sVt[buf][grp][(t * 32 + ql) * LDV + st * 16 + gq * 4];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-        const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(v_tile(buf) + t * 32 * VROW + v_frag_off(st));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw), pf, o[t], 0, 0, 0);
       }
     }
   };
 
   // group grp owns tiles grp, grp + 2, ...; both groups meet at every barrier
+  // (a buffer is refilled only after the barrier that ends its last use, and
+  // read only after the barrier that follows its loads' completion)
   const int nit = (nkb + kGroups - 1) / kGroups;
-  if (grp < nkb) {
-    load_tile(grp);
-    store_tile(0);
-  }
+  if (grp < nkb) issue_tile(grp, 0);
+  wait_vmem();
   __syncthreads();
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1;
     const int kb = it * kGroups + grp;
-    const bool more = kb + kGroups < nkb;
-    if (more) load_tile(kb + kGroups);
+    if (kb + kGroups < nkb) issue_tile(kb + kGroups, buf ^ 1);
     const int key0 = kb * kBK;
     if (kb < nkb && wave_rows && key0 <= rbase + 31) tile(buf, key0, key0 + kBK - 1 > rbase);  // wave-uniform
-    if (more) store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
   // merge the two groups' online-softmax states (the tile buffers are free now)
-  float* sm = reinterpret_cast<float*>(&sK[0][0][0]);
+  float* sm = reinterpret_cast<float*>(smem);
   const int slot = wid * 64 + lane;
   if (grp == 1) {
     sm[slot] = m_run;
@@ -382,26 +417,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
 template <int DH, int G>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq, int Hkv,
                     const float* ks, const int32_t* pos, const float* gain, const float* temp, float sm_scale,
-                    uint16_t* out, float* lse, uint16_t* vt, hipStream_t s) {
+                    uint16_t* out, float* lse, uint16_t* vt, float* kbias, hipStream_t s) {
   constexpr int BQ = 32 * (4 / G);
   const int Mp = (M + kBK - 1) / kBK * kBK;
-  hipLaunchKernelGGL((v_to_f16t_kernel<DH>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, M, Mp, Hkv, vt);
+  hipLaunchKernelGGL((attn_prepass_kernel<DH>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain, M, Mp,
+                     Hkv, G, vt, kbias);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (M + BQ - 1) / BQ;
   const long long total = (long long)nqb * Hkv * B;
   if (total <= 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt, M, Mp, Hq,
-                     Hkv, ks, pos, gain, temp, sm_scale, out, lse, nqb, (int)total);
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt, kbias, M,
+                     Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t gated_attention_workspace(int B, int M, int Hkv, int dh) {
+// fp16 V^T [B, Hkv, dh, Mp], then the fp32 key-score terms [B, Hq, Mp]
+size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
   const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
-  return (size_t)B * Hkv * dh * Mp * 2;
+  return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)Hq * 4);
 }
 
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq,
@@ -409,10 +446,13 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
                                   const float* temp, float sm_scale, uint16_t* out, float* lse, void* ws,
                                   hipStream_t s) {
   const int G = Hq / Hkv;
+  const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
   uint16_t* vt = static_cast<uint16_t*>(ws);
-#define TG_ATTN_CASE(DHV, GV)                                                                                \
-  if (dh == DHV && G == GV)                                                                                  \
-    return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, s);
+  float* kbias = reinterpret_cast<float*>(vt + (size_t)B * Hkv * dh * Mp);
+#define TG_ATTN_CASE(DHV, GV)                                                                                   \
+  if (dh == DHV && G == GV)                                                                                     \
+    return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, kbias, \
+                             s);
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 4)

@@ -44,9 +44,10 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     return tg::gate_score_workspace(h, d);  // the RMSNorm weight folded into W1 (bf16)
   }
   if (op == TG_OP_GATED_ATTENTION) {
-    if (B <= 0 || N <= 0 || d <= 0) return 0;
-    // d = Hkv * d_h; the V^T copy is B * Hkv * d_h * round_up(M, 64) fp16 values
-    return tg::gated_attention_workspace(B, N, 1, d);
+    if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return 0;
+    // d = Hkv * d_h, h = Hq: an fp16 V^T copy (B * Hkv * d_h * round_up(M, 64)
+    // values) and the fp32 key-score term of every query head (B * Hq * round_up(M, 64))
+    return tg::gated_attention_workspace(B, N, h, 1, d);
   }
   return 0;
 }
@@ -148,7 +149,7 @@ int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4)
     return fail(TG_EUNSUPPORTED, "tg_gated_attention: Hq/Hkv=%d not in {1,2,4}", G);
-  const size_t need = tg::gated_attention_workspace(B, M, Hkv, d_h);
+  const size_t need = tg::gated_attention_workspace(B, M, Hq, Hkv, d_h);
   if (!ws || ws_bytes < need)
     return fail(TG_EINVAL, "tg_gated_attention: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gated_attention: misaligned workspace");

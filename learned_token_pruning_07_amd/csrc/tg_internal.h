@@ -37,6 +37,6 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
                                   float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s);
 
 // Workspace bytes of launch_gated_attention: the fp16 V^T copy.
-size_t gated_attention_workspace(int B, int M, int Hkv, int dh);
+size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh);
 
 }  // namespace tg

@@ -46,9 +46,10 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_GATE_SCORE, 1, 16384, 2048, 256, 1638) == 256 * 2048 * 2
     for op in (tgb.TG_OP_SEQ_RMSNORM, tgb.TG_OP_TOPK_SELECT, tgb.TG_OP_COMPACT):
         assert lib.tg_workspace_size(op, 1, 16384, 2048, 256, 1638) == 0
-    # attention: fp16 V^T copy, kept length padded to 64 keys
-    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 0, 0) == 8 * 128 * 3392 * 2
-    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 0, 0) == 2 * 2 * 64 * 64 * 2
+    # attention: fp16 V^T copy and fp32 per-head key-score terms, kept length padded to 64 keys
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == 3392 * (8 * 128 * 2 + 16 * 4)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 0) == 2 * 64 * (2 * 64 * 2 + 4 * 4)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 0, 0) == 0   # Hq is required
 
 
 def _err(lib):
