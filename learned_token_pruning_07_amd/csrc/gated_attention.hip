@@ -91,23 +91,32 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
   const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const float scale = 1.0f / (float)(1 << kVScaleLog2);
-  for (int c = tid; c < kBK * DH / 8; c += kThreads) {
+  constexpr int NL = kBK * DH / 8 / kThreads;  // 16-byte loads per thread, all issued before any use
+  u32x4 w[NL];
+#pragma unroll
+  for (int e = 0; e < NL; ++e) {
+    const int c = tid + e * kThreads;
     const int key = c / (DH / 8), part = c % (DH / 8);
     const int m = m0 + key;
-    const u32x4 w = m < M ? load16(v + (((size_t)b * M + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // round toward zero: exact for every in-range value, saturates beyond
-      const uint32_t h2 =
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[i]) * scale, bf16_hi(w[i]) * scale));
-      sT[part * 8 + 2 * i][key] = (uint16_t)(h2 & 0xFFFFu);
-      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
-    }
+    w[e] = m < M ? load16(v + (((size_t)b * M + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
   }
   const int Hq = Hkv * G;
   for (int c = tid; c < G * kBK; c += kThreads) {
     const int hq = g * G + c / kBK, m = m0 + c % kBK;
     kbias[((size_t)b * Hq + hq) * Mp + m] = m < M ? key_score[(size_t)b * M + m] * (gain[hq] * kLog2e) : 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < NL; ++e) {
+    const int c = tid + e * kThreads;
+    const int key = c / (DH / 8), part = c % (DH / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // round toward zero: exact for every in-range value, saturates beyond
+      const uint32_t h2 = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e][i]) * scale, bf16_hi(w[e][i]) * scale));
+      sT[part * 8 + 2 * i][key] = (uint16_t)(h2 & 0xFFFFu);
+      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
+    }
   }
   __syncthreads();
   for (int c = tid; c < DH * (kBK / 8); c += kThreads) {
