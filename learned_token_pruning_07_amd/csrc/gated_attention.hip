@@ -193,22 +193,6 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   const bool q_ok = qi < M;
   const bool wave_rows = rbase < M;
 
-  // per-query logit scale in the log2 domain
-  float cq = 0.0f;
-  if (q_ok) {
-    const int p = pos[(size_t)b * M + qi];
-    float ratio = 1.0f;
-    if (p != qi) ratio = logf((float)max(p + 1, 2)) / logf((float)max(qi + 1, 2));
-    cq = sm_scale * kLog2e / (temp[hq] * ratio);
-  }
-
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp = q + (((size_t)b * M + (q_ok ? qi : 0)) * Hq + hq) * DH + gq * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? load16(qp + ks * 16) : u32x4{0, 0, 0, 0});
-  }
-
   // ---- tile staging ----
   // Raw buffer loads with an LDS destination; each lane's byte offset is fixed
   // for the whole loop.  K gets a resource per tile (base advanced to the
@@ -260,6 +244,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   auto k_frag_off = [&](int ks) { return ql * KROW + (((2 * ks + gq) ^ q7) << 4); };
   auto v_frag_off = [&](int st) { return ql * VROW + (((2 * st + gq) ^ q7) << 4); };
 
+  bf16x8 qf[KS];      // this lane's Q fragments (filled in the prologue below)
+  float cq = 0.0f;    // per-query logit scale in the log2 domain
   f32x16 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
@@ -366,7 +352,21 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   // read only after the barrier that follows its loads' completion)
   const int nit = (nkb + kGroups - 1) / kGroups;
   if (grp < nkb) issue_tile(grp, 0);
+  // Q fragments and the original position are requested while the first
+  // tile is in flight; one wait covers all of them
+  {
+    const uint16_t* qp = q + (((size_t)b * M + (q_ok ? qi : 0)) * Hq + hq) * DH + gq * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? load16(qp + ks * 16) : u32x4{0, 0, 0, 0});
+  }
+  const int p_orig = pos[(size_t)b * M + (q_ok ? qi : 0)];
+  const float t_h = temp[hq];
   wait_vmem();
+  if (q_ok) {
+    float ratio = 1.0f;
+    if (p_orig != qi) ratio = logf((float)max(p_orig + 1, 2)) / logf((float)max(qi + 1, 2));
+    cq = sm_scale * kLog2e / (t_h * ratio);
+  }
   __syncthreads();
   for (int it = 0; it < nit; ++it) {
     const int buf = it & 1;
@@ -378,21 +378,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
     __syncthreads();
   }
 
-  // merge the two groups' online-softmax states (the tile buffers are free now)
-  float* sm = reinterpret_cast<float*>(smem);
+  // merge the two groups' online-softmax states (the tile buffers are free
+  // now): group 1 hands over m, l and O as 16-byte vectors per lane
+  f32x4* sm4 = reinterpret_cast<f32x4*>(smem);
   const int slot = wid * 64 + lane;
   if (grp == 1) {
-    sm[slot] = m_run;
-    sm[256 + slot] = l_run;
+    sm4[slot] = f32x4{m_run, l_run, 0.0f, 0.0f};
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sm[(2 + t * 16 + i) * 256 + slot] = o[t][i];
+      for (int i4 = 0; i4 < 4; ++i4)
+        sm4[(1 + t * 4 + i4) * 256 + slot] =
+            f32x4{o[t][i4 * 4], o[t][i4 * 4 + 1], o[t][i4 * 4 + 2], o[t][i4 * 4 + 3]};
   }
   __syncthreads();
   if (grp == 1) return;
   {
-    const float m1 = sm[slot], l1 = sm[256 + slot];
+    const f32x4 ml = sm4[slot];
+    const float m1 = ml[0], l1 = ml[1];
     const float m = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
@@ -401,26 +404,43 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] = o[t][i] * a0 + sm[(2 + t * 16 + i) * 256 + slot] * a1;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 o1 = sm4[(1 + t * 4 + i4) * 256 + slot];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i4 * 4 + i] = o[t][i4 * 4 + i] * a0 + o1[i] * a1;
+      }
   }
 
   if (!wave_rows) return;
   const float l_tot = pair_sum(l_run);
-  if (!q_ok) return;
   const float inv = (float)(1 << kVScaleLog2) / l_tot;
-  uint16_t* op = out + (((size_t)b * M + qi) * Hq + hq) * DH;
+  // Output rows leave through LDS so that each store writes whole 16-byte
+  // pieces of a row: the wave's 32 x DH bf16 block is written row-major with
+  // the 16-byte chunks of row r XOR-swizzled by r & 15, then read back 16
+  // bytes per lane.  The region lies past the merge vectors and belongs to
+  // this wave alone, and LDS operations of one wave complete in order.
+  constexpr int OROW = DH * 2;  // bytes of an output row
+  unsigned char* ob = smem + (1 + DT * 4) * 256 * 16 + wid * 32 * OROW;
+  static_assert((1 + DT * 4) * 256 * 16 + 4 * 32 * OROW <= LDS_BYTES, "output staging");
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int d0 = t * 32 + i4 * 8 + gq * 4;
+      // d = 32t + 8 i4 + 4gq + (0..3): chunk 4t + i4 of the row, half gq
       u32x2 w;
       w[0] = pack_bf16x2(o[t][i4 * 4 + 0] * inv, o[t][i4 * 4 + 1] * inv);
       w[1] = pack_bf16x2(o[t][i4 * 4 + 2] * inv, o[t][i4 * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + d0) = w;
+      const int chunk = (t * 4 + i4) ^ (ql & (KCH - 1));
+      *reinterpret_cast<u32x2*>(ob + ql * OROW + chunk * 16 + gq * 8) = w;
     }
+  constexpr int RPI = 64 / KCH;  // rows per 64-lane store
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int r = r0 + lane / KCH, c = lane % KCH;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(ob + r * OROW + ((c ^ (r & (KCH - 1))) * 16));
+    if (rbase + r < M) store16(out + (((size_t)b * M + rbase + r) * Hq + hq) * DH + c * 8, w);
   }
-  if (lse != nullptr && gq == 0) lse[((size_t)b * Hq + hq) * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  if (lse != nullptr && gq == 0 && q_ok) lse[((size_t)b * Hq + hq) * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 template <int DH, int G>
