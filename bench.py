@@ -60,28 +60,38 @@ def _traffic(kernel_file: str):
 
 
 class Events:
-    """Pairs of HIP events (torch's current stream: the stream the library
-    launches on) around each named launch."""
+    """HIP events on torch's current stream (the stream the library launches
+    on) at the boundaries between the phases of a step: one event ends a phase
+    and starts the next, so a step records 6 events rather than a pair per
+    call (each record costs a few microseconds of GPU time between kernels).
+    A phase is one library call, or the run of consecutive calls of one entry
+    point; its per-call average is the phase time over the calls it holds."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.pairs = {}
+        self.spans = {}   # name -> [(start_event, end_event, calls)]
+        self.last = None
 
-    def around(self, name, fn):
-        t = self.torch
-        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record()
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.last = e
+        return e
+
+    def phase(self, name, fn, calls=1):
+        a = self.last if self.last is not None else self.mark()
         r = fn()
-        b.record()
-        self.pairs.setdefault(name, []).append((a, b))
+        b = self.mark()
+        self.spans.setdefault(name, []).append((a, b, calls))
         return r
 
     def avg_us(self, name):
-        ps = self.pairs.get(name, [])
-        return 1000.0 * sum(a.elapsed_time(b) for a, b in ps) / max(1, len(ps))
+        ps = self.spans.get(name, [])
+        n = sum(c for _, _, c in ps)
+        return 1000.0 * sum(a.elapsed_time(b) for a, b, _ in ps) / max(1, n)
 
     def count(self, name):
-        return len(self.pairs.get(name, []))
+        return sum(c for _, _, c in self.spans.get(name, []))
 
 
 def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
@@ -196,7 +206,7 @@ def main():
     gate_ws = tg.gate_workspace(h, d, dev)
 
     def gate(x, ev=None):
-        run = (lambda name, fn: ev.around(name, fn)) if ev else (lambda name, fn: fn())
+        run = (lambda name, fn: ev.phase(name, fn)) if ev else (lambda name, fn: fn())
         run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
                                                    ws=gate_ws))
         run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score))
@@ -226,31 +236,31 @@ def main():
         torch.cuda.synchronize()
         glue_ms = g0.elapsed_time(g1) / 3
 
-    def step(i, ev=None):
-        gate(resids[i % ncopy], ev)
+    def attention_layers():
         for l, p in enumerate(layers):
             q, k, v = qkv[l]
-            fn = (lambda q=q, k=k, v=v, p=p: tg.tg_gated_attention(q, k, v, b_S, kept_idx, p.gain, p.temp,
-                                                                   out=attn_out, ws=attn_ws))
-            if ev:
-                ev.around("gated_attention", fn)
-            else:
-                fn()
+            tg.tg_gated_attention(q, k, v, b_S, kept_idx, p.gain, p.temp, out=attn_out, ws=attn_ws)
+
+    def step(i, ev=None):
+        gate(resids[i % ncopy], ev)
+        if ev and layers:
+            ev.phase("gated_attention", attention_layers, calls=len(layers))
+        else:
+            attention_layers()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # ---------------- timed region ----------------
-    # an event pair around every launch gives per-kernel durations on the
-    # library's stream; the outer pair gives the time per step
+    # events at the phase boundaries of every step give per-call durations on
+    # the library's stream; the first and last of them bracket the K steps
     ev = Events(torch)
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
+    t_start = ev.mark()
     for i in range(args.steps):
         step(i, ev)
-    t_end.record()
+    t_end = ev.last
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies)")

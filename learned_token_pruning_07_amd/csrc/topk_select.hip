@@ -11,8 +11,11 @@
 //  3. A final pass in index order keeps key > T, and key == T for the first
 //     k_eq such tokens by index (block-wide prefix count), which is the
 //     lower-index tie-break.
-// The keys stay in LDS when the prunable span fits (<= 32768 keys, 128 KiB);
-// longer spans re-read the scores from global memory (L2-resident) per pass.
+// The keys stay in LDS when the prunable span fits (<= 32768 keys, 136 KiB
+// with one padding word after every 16 keys, so that both the coalesced
+// passes and the final pass's 16 consecutive keys per thread read without
+// bank conflicts); longer spans re-read the scores from global memory
+// (L2-resident) per pass.
 // Integer counting only: the mask is exact and deterministic.
 #include "tg_device.h"
 #include "tg_internal.h"
@@ -22,6 +25,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kLdsKeys = 32768;
+__device__ __forceinline__ int key_slot(int j) { return j + (j >> 4); }  // padded LDS position of key j
 constexpr int kItems = 16;  // consecutive keys per thread in the final pass
 constexpr int kBatch = 16;  // loads in flight per thread when the keys are re-read from global memory
 
@@ -34,7 +38,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ score, int N, int r,
                                                                int K, uint8_t* __restrict__ keep) {
-  __shared__ uint32_t s_keys[kLdsKeys];
+  __shared__ uint32_t s_keys[kLdsKeys + kLdsKeys / 16];
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_wave[16];
   __shared__ uint32_t s_sel[2];
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 #pragma unroll
     for (int e = 0; e < kLoad; ++e) {
       const int j = e * kThreads + tid;
-      if (j < P) s_keys[j] = order_key(f[e]);
+      if (j < P) s_keys[key_slot(j)] = order_key(f[e]);
     }
   }
 
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     __syncthreads();
     if (cached) {
       for (int j = tid; j < P; j += kThreads) {
-        const uint32_t key = s_keys[j];
+        const uint32_t key = s_keys[key_slot(j)];
         if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
       }
     } else {
@@ -125,7 +129,10 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   const uint32_t T = prefix;  // exact key of the K'-th largest score
   const uint32_t k_eq = krem;  // how many keys equal to T are kept
 
-  // Final pass in index order.
+  // Final pass in index order.  Each thread decides kItems consecutive
+  // tokens and writes them as one 16-byte store when the row allows it.
+  static_assert(kItems == 16, "one 16-byte store per thread");
+  const bool vec_store = ((reinterpret_cast<uintptr_t>(kp + r)) & 15u) == 0;
   uint32_t base = 0;  // number of keys == T before the current chunk
   for (int c0 = 0; c0 < P; c0 += kThreads * kItems) {
     uint32_t keys[kItems];
@@ -133,24 +140,33 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
       const int j = c0 + tid * kItems + e;
-      keys[e] = j < P ? (cached ? s_keys[j] : order_key(sc[j])) : 0u;
+      keys[e] = j < P ? (cached ? s_keys[key_slot(j)] : order_key(sc[j])) : 0u;
       n_eq += (j < P && keys[e] == T) ? 1u : 0u;
     }
     uint32_t tot;
     uint32_t rank = base + block_excl_scan_u32(n_eq, s_wave, tot);
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
       const int j = c0 + tid * kItems + e;
+      uint32_t v = 0;
       if (j < P) {
-        uint8_t v = 0;
         if (keys[e] > T) {
           v = 1;
         } else if (keys[e] == T) {
-          v = rank < k_eq ? 1 : 0;
+          v = rank < k_eq ? 1u : 0u;
           ++rank;
         }
-        kp[r + j] = v;
       }
+      packed[e >> 2] |= v << (8 * (e & 3));
+    }
+    const int j0 = c0 + tid * kItems;
+    if (vec_store && j0 + kItems <= P) {
+      store16(kp + r + j0, u32x4{packed[0], packed[1], packed[2], packed[3]});
+    } else {
+#pragma unroll
+      for (int e = 0; e < kItems; ++e)
+        if (j0 + e < P) kp[r + j0 + e] = (uint8_t)(packed[e >> 2] >> (8 * (e & 3)));
     }
     base += tot;
   }
