@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   __shared__ uint32_t s_keys[kLdsKeys + kLdsKeys / 16];
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_wave[16];
-  __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_sel[3];
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -58,8 +58,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   }
 
   const bool cached = P <= kLdsKeys;
+  for (int i = tid; i < 2048; i += kThreads) s_hist[i] = 0;
+  __syncthreads();
   if (cached) {
-    // all loads of a thread are issued before any is used (latency-bound)
+    // all loads of a thread are issued before any is used (latency-bound);
+    // the first pass's histogram (digit [31:21]) is counted on the way in
     constexpr int kLoad = kLdsKeys / kThreads;
     float f[kLoad];
 #pragma unroll
@@ -70,7 +73,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 #pragma unroll
     for (int e = 0; e < kLoad; ++e) {
       const int j = e * kThreads + tid;
-      if (j < P) s_keys[key_slot(j)] = order_key(f[e]);
+      if (j < P) {
+        const uint32_t key = order_key(f[e]);
+        s_keys[key_slot(j)] = key;
+        atomicAdd(&s_hist[key >> 21], 1u);
+      }
     }
   }
 
@@ -79,9 +86,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += kThreads) s_hist[i] = 0;
-    __syncthreads();
-    if (cached) {
+    if (pass > 0 || !cached) {  // (the cached first pass was counted during the load)
+      if (pass > 0)
+        for (int i = tid; i < nb; i += kThreads) s_hist[i] = 0;
+      __syncthreads();
+    }
+    if (cached && pass == 0) {
+      // counted during the load
+    } else if (cached) {
       for (int j = tid; j < P; j += kThreads) {
         const uint32_t key = s_keys[key_slot(j)];
         if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
@@ -117,6 +129,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       if (cum < krem && cum + c >= krem) {
         s_sel[0] = (uint32_t)digit;
         s_sel[1] = krem - cum;
+        s_sel[2] = c;  // keys sharing the selected prefix (after the last pass: keys equal to T)
       }
       cum += c;
     }
@@ -128,6 +141,31 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   }
   const uint32_t T = prefix;  // exact key of the K'-th largest score
   const uint32_t k_eq = krem;  // how many keys equal to T are kept
+  const uint32_t n_eq_all = s_sel[2];  // how many keys equal T
+
+  if (k_eq == n_eq_all) {
+    // Every key equal to T is kept (always so for distinct scores): keep is
+    // key >= T, with no index-order ranking.
+    static_assert(kItems == 16, "one 16-byte store per thread");
+    const bool vec = ((reinterpret_cast<uintptr_t>(kp + r)) & 15u) == 0;
+    for (int j0 = tid * kItems; j0 < P; j0 += kThreads * kItems) {
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < kItems; ++e) {
+        const int j = j0 + e;
+        const uint32_t key = j < P ? (cached ? s_keys[key_slot(j)] : order_key(sc[j])) : 0u;
+        packed[e >> 2] |= (j < P && key >= T ? 1u : 0u) << (8 * (e & 3));
+      }
+      if (vec && j0 + kItems <= P) {
+        store16(kp + r + j0, u32x4{packed[0], packed[1], packed[2], packed[3]});
+      } else {
+#pragma unroll
+        for (int e = 0; e < kItems; ++e)
+          if (j0 + e < P) kp[r + j0 + e] = (uint8_t)(packed[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+    return;
+  }
 
   // Final pass in index order.  Each thread decides kItems consecutive
   // tokens and writes them as one 16-byte store when the row allows it.
