@@ -4,9 +4,12 @@
 // original positions).
 //
 // Two kernels on the same stream:
-//  * compact_scan: one workgroup per batch row runs a block-wide exclusive
-//    prefix count over the keep mask and writes, in ascending original order,
-//    kept_idx[m] = j and score_out[m] = score[j] (a few hundred KiB at most).
+//  * compact_scan: workgroup c of a batch row takes tokens [c S, c S + S),
+//    S = kScanChunk.  It counts the set bytes of the mask before its chunk
+//    itself (at most N bytes, L2-resident: no cross-workgroup traffic and no
+//    workspace), runs a block-wide exclusive prefix count over its chunk and
+//    writes, in ascending original order, kept_idx[m] = j and
+//    score_out[m] = score[j].
 //  * compact_gather: a streaming 16-byte row copy resid_out[m] = resid[kept_idx[m]],
 //    the HBM-bound part (2 * M * row_bytes).
 #include "tg_device.h"
@@ -15,68 +18,88 @@
 namespace tg {
 namespace {
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 32;  // consecutive tokens per thread per chunk
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;                             // consecutive tokens per thread
+constexpr int kScanChunk = kScanThreads * kScanItems;     // tokens per workgroup
+constexpr int kCountUnroll = 8;                           // 16-byte mask loads in flight per thread
 constexpr int kGatherThreads = 256;
 constexpr int kGatherUnroll = 4;
 
-// Every load of a chunk (keep flags and scores of kScanItems consecutive
-// tokens per thread) is issued before the block-wide scan, so a chunk costs
-// one memory round trip.
+// number of non-zero bytes of a 32-bit word
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+  const uint32_t hi = ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w;
+  return __builtin_popcount(hi & 0x80808080u);
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_wave) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) s_wave[wid] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) t += s_wave[w];
+  __syncthreads();
+  return t;
+}
+
 __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_t* __restrict__ keep,
                                                                     const float* __restrict__ score, int N,
                                                                     int M, int32_t* __restrict__ kept_idx,
                                                                     float* __restrict__ score_out) {
-  __shared__ uint32_t s_wave[16];
-  const int b = blockIdx.x;
+  __shared__ uint32_t s_wave[kScanThreads / 64];
+  const int b = blockIdx.y;
   const uint8_t* kp = keep + (size_t)b * N;
   const float* sc = score + (size_t)b * N;
   int32_t* ki = kept_idx + (size_t)b * M;
   float* so = score_out + (size_t)b * M;
   const int tid = threadIdx.x;
-  const bool vec = ((reinterpret_cast<uintptr_t>(kp) | reinterpret_cast<uintptr_t>(sc)) & 15u) == 0;
-  uint32_t base = 0;
-  for (int c0 = 0; c0 < N; c0 += kScanThreads * kScanItems) {
-    const int j0 = c0 + tid * kScanItems;
-    uint8_t flags[kScanItems];
-    float sv[kScanItems];
-    if (vec && j0 + kScanItems <= N) {
+  const int c0 = blockIdx.x * kScanChunk;
+
+  // this chunk: kScanItems consecutive tokens per thread (requested first, so
+  // their latency overlaps the count below)
+  const int j0 = c0 + tid * kScanItems;
+  uint32_t flags = 0;  // bit e: token j0 + e is kept
+  float sv[kScanItems];
 #pragma unroll
-      for (int q = 0; q < kScanItems / 16; ++q) {
-        const u32x4 w = load16(kp + j0 + q * 16);
+  for (int e = 0; e < kScanItems; ++e) {
+    const int j = j0 + e;
+    flags |= (j < N && kp[j] != 0) ? (1u << e) : 0u;
+    sv[e] = j < N ? sc[j] : 0.0f;
+  }
+
+  // ones before this chunk; every load of a batch is issued before any is used
+  uint32_t cnt = 0;
+  if ((reinterpret_cast<uintptr_t>(kp) & 15u) == 0) {
+    const int n16 = c0 / 16;  // c0 is a multiple of 16
+    for (int q0 = 0; q0 < n16; q0 += kScanThreads * kCountUnroll) {
+      u32x4 w[kCountUnroll];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) flags[q * 16 + e] = ((w[e >> 2] >> ((e & 3) * 8)) & 0xFFu) != 0;
+      for (int u = 0; u < kCountUnroll; ++u) {
+        const int q = q0 + u * kScanThreads + tid;
+        w[u] = q < n16 ? load16(kp + (size_t)q * 16) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int q = 0; q < kScanItems / 4; ++q) {
-        const u32x4 w = load16(sc + j0 + q * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sv[q * 4 + e] = __uint_as_float(w[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < kScanItems; ++e) {
-        const int j = j0 + e;
-        flags[e] = (j < N && kp[j] != 0) ? 1 : 0;
-        sv[e] = j < N ? sc[j] : 0.0f;
-      }
+      for (int u = 0; u < kCountUnroll; ++u)
+        cnt += nonzero_bytes(w[u][0]) + nonzero_bytes(w[u][1]) + nonzero_bytes(w[u][2]) + nonzero_bytes(w[u][3]);
     }
-    uint32_t cnt = 0;
+  } else {
+    for (int j = tid; j < c0; j += kScanThreads) cnt += kp[j] != 0 ? 1u : 0u;
+  }
+  const uint32_t base = block_sum_u32(cnt, s_wave);
+
+  uint32_t tot;
+  uint32_t dst = base + block_excl_scan_u32(__builtin_popcount(flags), s_wave, tot);
 #pragma unroll
-    for (int e = 0; e < kScanItems; ++e) cnt += flags[e];
-    uint32_t tot;
-    uint32_t dst = base + block_excl_scan_u32(cnt, s_wave, tot);
-#pragma unroll
-    for (int e = 0; e < kScanItems; ++e) {
-      if (flags[e]) {
-        if ((int)dst < M) {
-          ki[dst] = j0 + e;
-          so[dst] = sv[e];
-        }
-        ++dst;
+  for (int e = 0; e < kScanItems; ++e) {
+    if (flags & (1u << e)) {
+      if ((int)dst < M) {
+        ki[dst] = j0 + e;
+        so[dst] = sv[e];
       }
+      ++dst;
     }
-    base += tot;
   }
 }
 
@@ -122,8 +145,8 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
                           const float* score, int M, int32_t* kept_idx, void* resid_out, float* score_out,
                           hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_scan_kernel, dim3(B), dim3(kScanThreads), 0, s, keep, score, N, M, kept_idx,
-                     score_out);
+  hipLaunchKernelGGL(compact_scan_kernel, dim3((N + kScanChunk - 1) / kScanChunk, B), dim3(kScanThreads), 0, s,
+                     keep, score, N, M, kept_idx, score_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t total = (size_t)M * (row_bytes / 16);
