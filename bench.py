@@ -204,13 +204,15 @@ def main():
     resid_S = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
     b_S = torch.empty((1, M), dtype=torch.float32, device=dev)
     gate_ws = tg.gate_workspace(h, d, dev)
+    seq_ws = tg.seq_rmsnorm_workspace(1, N, dev)   # None up to N = 32768
+    topk_ws = tg.topk_workspace(1, N, dev)
 
     def gate(x, ev=None):
         run = (lambda name, fn: ev.phase(name, fn)) if ev else (lambda name, fn: fn())
         run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
                                                    ws=gate_ws))
-        run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score))
-        run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep))
+        run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws))
+        run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws))
         run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
                                               score_out=b_S))
 

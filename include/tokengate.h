@@ -98,7 +98,10 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r,
  * With P == 0 every output is 0.  The reduction order is fixed.
  *
  *   score_raw [B, N] fp32 in;  score [B, N] fp32 out (may alias score_raw)
- *   ws, ws_bytes     workspace (0 bytes today)
+ *   ws, ws_bytes     workspace of tg_workspace_size(TG_OP_SEQ_RMSNORM, B, N,
+ *                    ...) bytes, 16-byte aligned: none for N <= 32768, else
+ *                    8 * B * ceil(N / 8192) (fp64 partial sums; contents need
+ *                    no initialisation)
  */
 int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq,
                    float* score, void* ws, size_t ws_bytes, void* stream);
@@ -114,7 +117,9 @@ int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq,
  *
  *   score [B, N] fp32 in;   keep [B, N] uint8 out (1 = kept, 0 = pruned)
  *   K >= 0 (K >= N - r keeps everything)
- *   ws, ws_bytes     workspace (0 bytes today)
+ *   ws, ws_bytes     workspace of tg_workspace_size(TG_OP_TOPK_SELECT, B, N,
+ *                    ...) bytes, 16-byte aligned: none for N <= 32768, else
+ *                    20496 * B (digit histograms, cleared by the call itself)
  */
 int tg_topk_select(const float* score, int B, int N, int r, int K,
                    uint8_t* keep, void* ws, size_t ws_bytes, void* stream);
@@ -179,7 +184,8 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
 
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
  * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
- * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq). */
+ * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq).
+ * TG_OP_SEQ_RMSNORM and TG_OP_TOPK_SELECT depend on B and N only. */
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
 
 /* Message describing the last non-zero status returned on this thread. */

@@ -132,27 +132,59 @@ def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, 
     return score_raw
 
 
-def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, stream=None):
-    """Sequence RMSNorm of the raw scores -> ``[B, N]`` fp32 (0 for j < r)."""
+def _op_workspace(op: int, B: int, N: int, device) -> torch.Tensor | None:
+    n = int(load_library().tg_workspace_size(op, B, N, 0, 0, 0))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def seq_rmsnorm_workspace(B: int, N: int, device="cuda") -> torch.Tensor | None:
+    """A workspace for tg_seq_rmsnorm at these sizes (None when it needs none: N <= 32768)."""
+    return _op_workspace(TG_OP_SEQ_RMSNORM, B, N, device)
+
+
+def topk_workspace(B: int, N: int, device="cuda") -> torch.Tensor | None:
+    """A workspace for tg_topk_select at these sizes (None when it needs none: N <= 32768)."""
+    return _op_workspace(TG_OP_TOPK_SELECT, B, N, device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    _need(ws, "ws", torch.uint8)
+    return _ptr(ws), ws.numel()
+
+
+def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, ws=None, stream=None):
+    """Sequence RMSNorm of the raw scores -> ``[B, N]`` fp32 (0 for j < r).
+
+    ``ws``: from :func:`seq_rmsnorm_workspace` (allocated here when needed and omitted)."""
     lib = load_library()
     _need(score_raw, "score_raw", torch.float32)
     B, N = score_raw.shape
     if score is None:
         score = torch.empty_like(score_raw)
     _need(score, "score", torch.float32, (B, N))
-    _check(lib.tg_seq_rmsnorm(_ptr(score_raw), B, N, r, eps_seq, _ptr(score), None, 0, _stream(stream)))
+    if ws is None:
+        ws = seq_rmsnorm_workspace(B, N, score_raw.device)
+    wp, wn = _ws_args(ws)
+    _check(lib.tg_seq_rmsnorm(_ptr(score_raw), B, N, r, eps_seq, _ptr(score), wp, wn, _stream(stream)))
     return score
 
 
-def tg_topk_select(score, r: int, K: int, keep=None, stream=None):
-    """Keep mask ``[B, N]`` uint8 with r + min(K, N - r) ones per row."""
+def tg_topk_select(score, r: int, K: int, keep=None, ws=None, stream=None):
+    """Keep mask ``[B, N]`` uint8 with r + min(K, N - r) ones per row.
+
+    ``ws``: from :func:`topk_workspace` (allocated here when needed and omitted)."""
     lib = load_library()
     _need(score, "score", torch.float32)
     B, N = score.shape
     if keep is None:
         keep = torch.empty((B, N), dtype=torch.uint8, device=score.device)
     _need(keep, "keep", torch.uint8, (B, N))
-    _check(lib.tg_topk_select(_ptr(score), B, N, r, K, _ptr(keep), None, 0, _stream(stream)))
+    if ws is None:
+        ws = topk_workspace(B, N, score.device)
+    wp, wn = _ws_args(ws)
+    _check(lib.tg_topk_select(_ptr(score), B, N, r, K, _ptr(keep), wp, wn, _stream(stream)))
     return keep
 
 
@@ -237,7 +269,7 @@ def tg_version() -> int:
 
 
 def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e-6, eps_seq=1e-6, ws=None,
-                       stream=None):
+                       seq_ws=None, topk_ws=None, stream=None):
     """The gate at layer L, end to end: score -> sequence norm -> top-K -> compaction.
 
     Returns ``(kept_idx, resid_S, b_S, keep, score)``.  Four library calls on
@@ -245,8 +277,8 @@ def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e
     """
     B, N, _ = resid.shape
     raw = tg_gate_score(resid, r, norm_w, W1, b1, w2, b2, eps_row, ws=ws, stream=stream)
-    score = tg_seq_rmsnorm(raw, r, eps_seq, score=raw, stream=stream)
-    keep = tg_topk_select(score, r, K, stream=stream)
+    score = tg_seq_rmsnorm(raw, r, eps_seq, score=raw, ws=seq_ws, stream=stream)
+    keep = tg_topk_select(score, r, K, ws=topk_ws, stream=stream)
     M = kept_count(N, r, K)
     kept_idx, resid_S, b_S = tg_compact(resid, keep, score, M, stream=stream)
     return kept_idx, resid_S, b_S, keep, score

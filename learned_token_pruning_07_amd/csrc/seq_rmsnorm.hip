@@ -3,13 +3,15 @@
 // divided by their root mean square over the prunable span; the scores of the
 // non-prunable tokens are fixed to 0.
 //
-// One workgroup per batch row.  The data is at most N * 4 bytes (512 KiB at
-// N = 128k), so the kernel is latency-bound: each thread issues all of its
-// 16-byte loads for a chunk of kThreads * kVec * 4 scores before using any,
-// and keeps them in registers for the scaling pass when the row fits one
-// chunk.  Each thread's sum of squares over a chunk (32 terms) is fp32;
-// chunk, thread and wave partials are combined in fp64 in a fixed order
-// (deterministic).
+// Rows of up to 32768 scores: one workgroup per batch row.  The kernel is
+// latency-bound: each thread issues all of its 16-byte loads for the row
+// before using any and keeps them in registers for the scaling pass.
+// Longer rows: two launches over slices of kSlice scores -- fp64 partial sums
+// of squares per slice into the workspace, then every slice's workgroup sums
+// the row's partials in index order and scales its own slice (so the
+// in-place call is safe: no slice is written before every sum is taken).
+// Each thread's sum of squares (32 terms) is fp32; thread, wave, slice and
+// chunk partials are combined in fp64 in a fixed order (deterministic).
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -89,10 +91,90 @@ __global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, 
   }
 }
 
+// ---- rows longer than one chunk ----
+constexpr int kSliceThreads = 256;
+constexpr int kSlice = kSliceThreads * kVec * 4;  // 8192 scores per workgroup
+
+__device__ __forceinline__ double block_sum_f64(double v, double* s_part) {
+  v = wave_sum_f64(v);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kSliceThreads / 64; ++w) t += s_part[w];
+  return t;
+}
+
+// partial[b, c] = sum of squares of the prunable scores in slice c of row b
+__global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* in, int N, int r,
+                                                                  double* __restrict__ partial) {
+  __shared__ double s_part[kSliceThreads / 64];
+  const int b = blockIdx.y, c0 = blockIdx.x * kSlice, tid = threadIdx.x;
+  const float* x = in + (size_t)b * N;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+  f32x4 v[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, vec);
+  float part = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(v[e][i], v[e][i], part);
+  const double t = block_sum_f64((double)part, s_part);
+  if (tid == 0) partial[(size_t)b * gridDim.x + blockIdx.x] = t;
+}
+
+// Every workgroup of row b sums the row's partials in index order (the same
+// value in each), then scales its own slice.
+__global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* in, int N, int r, float eps,
+                                                                  const double* __restrict__ partial, int nblk,
+                                                                  float* out) {
+  __shared__ double s_part[kSliceThreads / 64];
+  const int b = blockIdx.y, c0 = blockIdx.x * kSlice, tid = threadIdx.x;
+  const float* x = in + (size_t)b * N;
+  float* y = out + (size_t)b * N;
+  const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
+  f32x4 v[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, vec);
+  double acc = 0.0;
+  for (int c = tid; c < nblk; c += kSliceThreads) acc += partial[(size_t)b * nblk + c];
+  const double t = block_sum_f64(acc, s_part);
+  const int P = N - r;
+  const double scale = P > 0 ? 1.0 / sqrt(t / (double)P + (double)eps) : 0.0;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const int j = c0 + (e * kSliceThreads + tid) * 4;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
+    if (vec && j + 4 <= N) {
+      *reinterpret_cast<f32x4*>(y + j) = o;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j + i < N) y[j + i] = o[i];
+    }
+  }
+}
+
 }  // namespace
 
-hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(seq_rmsnorm_kernel, dim3(B), dim3(kThreads), 0, s, in, N, r, eps, out);
+size_t seq_rmsnorm_workspace(int B, int N) {
+  return N > kChunk ? (size_t)B * ((N + kSlice - 1) / kSlice) * sizeof(double) : 0;
+}
+
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out, void* ws,
+                              hipStream_t s) {
+  if (N <= kChunk) {
+    hipLaunchKernelGGL(seq_rmsnorm_kernel, dim3(B), dim3(kThreads), 0, s, in, N, r, eps, out);
+    return hipGetLastError();
+  }
+  const int nblk = (N + kSlice - 1) / kSlice;
+  double* partial = static_cast<double*>(ws);
+  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, eps, partial, nblk, out);
   return hipGetLastError();
 }
 

@@ -43,6 +43,14 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     if (d <= 0 || h <= 0) return 0;
     return tg::gate_score_workspace(h, d);  // the RMSNorm weight folded into W1 (bf16)
   }
+  if (op == TG_OP_TOPK_SELECT) {
+    if (B <= 0 || N <= 0) return 0;
+    return tg::topk_select_workspace(B, N);  // digit histograms, rows longer than 32768 only
+  }
+  if (op == TG_OP_SEQ_RMSNORM) {
+    if (B <= 0 || N <= 0) return 0;
+    return tg::seq_rmsnorm_workspace(B, N);  // fp64 partial sums, rows longer than 32768 only
+  }
   if (op == TG_OP_GATED_ATTENTION) {
     if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return 0;
     // d = Hkv * d_h, h = Hq: an fp16 V^T copy (B * Hkv * d_h * round_up(M, 64)
@@ -93,25 +101,36 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const v
 
 int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq, float* score, void* ws,
                    size_t ws_bytes, void* stream) {
-  (void)ws; (void)ws_bytes;
   if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_seq_rmsnorm: B, N must be > 0");
   if (r < 0 || r > N) return fail(TG_EINVAL, "tg_seq_rmsnorm: r=%d outside [0, N=%d]", r, N);
   if (!score_raw || !score) return fail(TG_EINVAL, "tg_seq_rmsnorm: null pointer argument");
   if (!aligned4(score_raw) || !aligned4(score)) return fail(TG_EINVAL, "tg_seq_rmsnorm: misaligned pointer");
   if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "tg_seq_rmsnorm: eps_seq must be >= 0");
-  return hip_status(tg::launch_seq_rmsnorm(score_raw, B, N, r, eps_seq, score, reinterpret_cast<hipStream_t>(stream)),
+  const size_t need = tg::seq_rmsnorm_workspace(B, N);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(TG_EINVAL, "tg_seq_rmsnorm: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_seq_rmsnorm: misaligned workspace");
+  }
+  return hip_status(tg::launch_seq_rmsnorm(score_raw, B, N, r, eps_seq, score, ws,
+                                           reinterpret_cast<hipStream_t>(stream)),
                     "tg_seq_rmsnorm");
 }
 
 int tg_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws, size_t ws_bytes,
                    void* stream) {
-  (void)ws; (void)ws_bytes;
   if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_topk_select: B, N must be > 0");
   if (r < 0 || r > N) return fail(TG_EINVAL, "tg_topk_select: r=%d outside [0, N=%d]", r, N);
   if (K < 0) return fail(TG_EINVAL, "tg_topk_select: K=%d must be >= 0", K);
   if (!score || !keep) return fail(TG_EINVAL, "tg_topk_select: null pointer argument");
   if (!aligned4(score)) return fail(TG_EINVAL, "tg_topk_select: misaligned score");
-  return hip_status(tg::launch_topk_select(score, B, N, r, K, keep, reinterpret_cast<hipStream_t>(stream)),
+  const size_t need = tg::topk_select_workspace(B, N);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(TG_EINVAL, "tg_topk_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_topk_select: misaligned workspace");
+  }
+  return hip_status(tg::launch_topk_select(score, B, N, r, K, keep, ws, reinterpret_cast<hipStream_t>(stream)),
                     "tg_topk_select");
 }
 

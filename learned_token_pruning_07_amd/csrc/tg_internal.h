@@ -21,10 +21,12 @@ hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r,
                                  const float* b1, int h, const float* w2, const float* b2,
                                  float* out, hipStream_t s);
 
-hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out,
+size_t seq_rmsnorm_workspace(int B, int N);
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out, void* ws,
                               hipStream_t s);
 
-hipError_t launch_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep,
+size_t topk_select_workspace(int B, int N);
+hipError_t launch_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws,
                               hipStream_t s);
 
 hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,

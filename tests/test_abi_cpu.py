@@ -46,6 +46,12 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_GATE_SCORE, 1, 16384, 2048, 256, 1638) == 256 * 2048 * 2
     for op in (tgb.TG_OP_SEQ_RMSNORM, tgb.TG_OP_TOPK_SELECT, tgb.TG_OP_COMPACT):
         assert lib.tg_workspace_size(op, 1, 16384, 2048, 256, 1638) == 0
+        assert lib.tg_workspace_size(op, 1, 32768, 2048, 256, 1638) == 0
+    # rows beyond 32768 tokens: fp64 partial sums per 8192-score slice; digit histograms
+    assert lib.tg_workspace_size(tgb.TG_OP_SEQ_RMSNORM, 2, 131072, 0, 0, 0) == 2 * 16 * 8
+    assert lib.tg_workspace_size(tgb.TG_OP_SEQ_RMSNORM, 1, 32769, 0, 0, 0) == 5 * 8
+    assert lib.tg_workspace_size(tgb.TG_OP_TOPK_SELECT, 2, 131072, 0, 0, 0) == 2 * (2048 + 2048 + 1024 + 4) * 4
+    assert lib.tg_workspace_size(tgb.TG_OP_COMPACT, 1, 131072, 2048, 0, 0) == 0
     # attention: fp16 V^T copy and fp32 per-head key-score terms, kept length padded to 64 keys
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == 3392 * (8 * 128 * 2 + 16 * 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 0) == 2 * 64 * (2 * 64 * 2 + 4 * 4)
@@ -89,6 +95,14 @@ def test_seq_rmsnorm_and_topk_validation(lib):
     assert "K=-1" in _err(lib)
     assert lib.tg_topk_select(FAKE, 1, 10, 0, 3, NULL, None, 0, None) == tgb.TG_EINVAL
     assert lib.tg_topk_select(FAKE, 1, 10, 12, 3, FAKE, None, 0, None) == tgb.TG_EINVAL
+    # long rows need a workspace
+    assert lib.tg_seq_rmsnorm(FAKE, 1, 40000, 0, 1e-6, FAKE, None, 0, None) == tgb.TG_EINVAL
+    assert "workspace" in _err(lib)
+    assert lib.tg_seq_rmsnorm(FAKE, 1, 40000, 0, 1e-6, FAKE, FAKE, 8, None) == tgb.TG_EINVAL
+    assert lib.tg_seq_rmsnorm(FAKE, 1, 40000, 0, 1e-6, FAKE, FAKE_ODD, 1 << 20, None) == tgb.TG_EINVAL
+    assert lib.tg_topk_select(FAKE, 1, 40000, 0, 3, FAKE, None, 0, None) == tgb.TG_EINVAL
+    assert "workspace" in _err(lib)
+    assert lib.tg_topk_select(FAKE, 1, 40000, 0, 3, FAKE, FAKE, 100, None) == tgb.TG_EINVAL
 
 
 def test_compact_validation(lib):

@@ -115,6 +115,8 @@ def _scores(kind, B, N, seed):
     ("normal", 1, 70000, 5, 7000),       # prunable span beyond the LDS key cache
     ("coarse", 1, 131072, 128, 13094),
     ("const", 1, 40000, 0, 19999),
+    ("ties", 2, 50000, 7, 20000),        # multi-launch path, ties straddling the budget, two rows
+    ("normal", 3, 33000, 100, 3290),     # multi-launch path, distinct scores, three rows
     ("normal", 1, 1000, 10, 0),
     ("normal", 1, 1000, 10, 990),
     ("normal", 1, 1000, 10, 5000),
