@@ -42,6 +42,9 @@ constexpr int kLda = kKC + 8;       // padded LDS row (bf16): conflict-free frag
 constexpr int kTpr = kKC / 8;       // threads per row per chunk (16 bytes each)
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
 constexpr int kDepth = 4;           // residual chunks in flight per workgroup
+constexpr int kWDepth = 3;          // W1w fragment chunks resident per wave (two in flight)
+constexpr int kUnroll = 12;         // chunk loop unroll: a multiple of 2, kDepth and kWDepth
+constexpr int kTallTileMinBlocks = 240;  // 128-token tiles once they give about every CU of the chip a workgroup
 
 __device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
 
@@ -70,23 +73,24 @@ __global__ __launch_bounds__(kThreads) void fold_norm_weight_kernel(const uint16
   store16(W1f + (size_t)u * 8, o);
 }
 
-template <int H, int ROWS>
-__global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
+template <int H, int ROWS, int WAVES, int NCH_FIXED>
+__global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
                                                                    int d, int r, float eps_row,
                                                                    const uint16_t* __restrict__ W1w,
                                                                    const float* __restrict__ b1,
                                                                    const uint16_t* __restrict__ w2,
                                                                    const float* __restrict__ b2,
                                                                    float* __restrict__ out) {
+  constexpr int THREADS = 64 * WAVES;
   constexpr int RT = ROWS / 16;               // 16-row MFMA tiles (each wave covers every row)
-  constexpr int CT = H / (kWaves * 16);       // 16-column MFMA tiles per wave
-  constexpr int AL = ROWS * kTpr / kThreads;  // 16-byte residual loads per thread per chunk
-  constexpr int GR = RT / kWaves;             // row tiles whose sum of squares this wave computes
-  static_assert(AL >= 1 && CT >= 1 && GR >= 1, "tile shape");
+  constexpr int CT = H / (WAVES * 16);        // 16-column MFMA tiles per wave
+  constexpr int AL = ROWS * kTpr / THREADS;   // 16-byte residual loads per thread per chunk
+  constexpr int GR = RT / WAVES;              // row tiles whose sum of squares this wave computes
+  static_assert(AL >= 1 && CT >= 1 && GR >= 1 && AL * THREADS == ROWS * kTpr && GR * WAVES == RT, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * kLda];
   __shared__ float s_inv[ROWS];
-  __shared__ float s_part[kWaves][ROWS];
+  __shared__ float s_part[WAVES][ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
   const int row0 = r + blockIdx.x * ROWS;
   float* ob = out + (size_t)b * N;
 
-  for (int j = blockIdx.x * kThreads + tid; j < r; j += gridDim.x * kThreads) ob[j] = 0.0f;
+  for (int j = blockIdx.x * THREADS + tid; j < r; j += gridDim.x * THREADS) ob[j] = 0.0f;
   if (row0 >= N) return;  // whole workgroup: no barrier is skipped by part of it
 
   // residual tile: rows past N read as 0 through the buffer range check
@@ -108,21 +112,21 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
   int a_off[AL], a_lds[AL];
 #pragma unroll
   for (int e = 0; e < AL; ++e) {
-    const int row = (tid + kThreads * e) / kTpr;
+    const int row = (tid + THREADS * e) / kTpr;
     a_off[e] = (row * d + kp * 8) * 2;
     a_lds[e] = row * kLda + kp * 8;
   }
   // this lane's B fragments in the fragment-ordered W1w (see fold_norm_weight_kernel)
-  const int ncol0 = wid * (H / kWaves) + (lane & 15);
+  const int ncol0 = wid * (H / WAVES) + (lane & 15);
   const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide k-step
-  constexpr int kStepBytes = kWaves * CT * 64 * 16;  // one (chunk, k-step) of W1w
+  constexpr int kStepBytes = WAVES * CT * 64 * 16;  // one (chunk, k-step) of W1w: H / 16 KiB
   int w_off[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) w_off[ct] = ((wid * CT + ct) * 64 + lane) * 16;
 
-  const int nch = d / kKC;
-  u32x4 ra[kDepth][AL];  // register ring: chunk c lives in slot c % kDepth
-  u32x4 bcur[2][CT], bnext[2][CT];
+  const int nch = NCH_FIXED > 0 ? NCH_FIXED : d / kKC;
+  u32x4 ra[kDepth][AL];        // residual ring: chunk c lives in slot c % kDepth
+  u32x4 wb[kWDepth][2][CT];    // W1w fragment ring: chunk c lives in slot c % kWDepth
   auto load_a = [&](int c, u32x4 (&dst)[AL]) {
 #pragma unroll
     for (int e = 0; e < AL; ++e)
@@ -151,23 +155,32 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
   for (int i = 0; i < GR; ++i) gram[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
+  for (int j = 0; j < kWDepth - 1; ++j)
+    if (j < nch) load_b(j, wb[j]);
+#pragma unroll
   for (int j = 0; j < kDepth; ++j)
     if (j < nch) load_a(j, ra[j]);
-  load_b(0, bcur);
   store_a(0, ra[0]);
   __syncthreads();
 
-  // chunk c: MFMAs on LDS buffer c & 1 while chunk c + kDepth loads into the
-  // ring slot chunk c just vacated and chunk c + 1 moves ring -> LDS
-  for (int c0 = 0; c0 < nch; c0 += kDepth) {
+  // chunk c: MFMAs on LDS buffer c & 1 with W1w slot c % kWDepth, while the
+  // W1w fragments of chunk c + kWDepth - 1 and then residual chunk c + kDepth
+  // load into the slots that chunks c - 1 and c vacated, and chunk c + 1 moves
+  // ring -> LDS.  Vector loads retire in order, so each wait for a chunk's
+  // W1w fragments also waits for the residual chunks issued before them:
+  // issuing the fragments first keeps the residual kDepth - 1 chunks ahead.
+  constexpr int kOuterUnroll = NCH_FIXED > 0 ? (NCH_FIXED + kUnroll - 1) / kUnroll : 1;
+#pragma unroll kOuterUnroll
+  for (int c0 = 0; c0 < nch; c0 += kUnroll) {
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
+    for (int j = 0; j < kUnroll; ++j) {
       const int c = c0 + j;
       if (c < nch) {  // uniform
-        const int buf = j & 1;  // == c & 1 (kDepth is even)
+        const int buf = j & 1;  // == c & 1 (kUnroll is even)
         const bool more = c + 1 < nch;
-        if (c + kDepth < nch) load_a(c + kDepth, ra[j]);
-        if (more) load_b(c + 1, bnext);
+        const u32x4 (&bcur)[2][CT] = wb[j % kWDepth];
+        if (c + kWDepth - 1 < nch) load_b(c + kWDepth - 1, wb[(j + kWDepth - 1) % kWDepth]);
+        if (c + kDepth < nch) load_a(c + kDepth, ra[j % kDepth]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 af[RT];
@@ -184,17 +197,11 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
 #pragma unroll
           for (int i = 0; i < GR; ++i) {
             const bf16x8 gf = *reinterpret_cast<const bf16x8*>(
-                &sA[buf][((wid + kWaves * i) * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
+                &sA[buf][((wid + WAVES * i) * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
             gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, gf, gram[i], 0, 0, 0);
           }
         }
-        if (more) {
-          store_a(buf ^ 1, ra[(j + 1) % kDepth]);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) bcur[ks][ct] = bnext[ks][ct];
-        }
+        if (more) store_a(buf ^ 1, ra[(j + 1) % kDepth]);
         __syncthreads();
       }
     }
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
     const int m = lane & 15;
     if ((lane >> 4) == (m >> 2)) {
       const float ssq = gram[i][m & 3];
-      s_inv[(wid + kWaves * i) * 16 + m] = 1.0f / sqrtf(ssq / (float)d + eps_row);
+      s_inv[(wid + WAVES * i) * 16 + m] = 1.0f / sqrtf(ssq / (float)d + eps_row);
     }
   }
   __syncthreads();
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gate_score_bf16_kernel(const uint16_
   if (tid < ROWS && row0 + tid < N) {
     float v = s_part[0][tid];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) v += s_part[w][tid];
+    for (int w = 1; w < WAVES; ++w) v += s_part[w][tid];
     ob[row0 + tid] = v + b2[0];
   }
 }
@@ -301,17 +308,36 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
   }
 }
 
+template <int H, int ROWS, int WAVES>
+hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, float eps, const uint16_t* W1w,
+                       const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
+  const int P = N - r;
+  const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
+  // d = 2048 (the model width) gets a fully unrolled chunk loop: the compiler
+  // then counts outstanding loads exactly instead of waiting for all of them
+  // at the loop's back edge, which would void the prefetch ring
+  if (d == 2048)
+    hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 32>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid,
+                       N, d, r, eps, W1w, b1, w2, b2, out);
+  else
+    hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 0>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid, N,
+                       d, r, eps, W1w, b1, w2, b2, out);
+  return hipGetLastError();
+}
+
 template <int H>
 hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, float eps, const uint16_t* W1w,
                          const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
-  // 64-token tiles: 128-token tiles halve the W1 bytes per token but need
-  // more registers than two waves per SIMD allow, and measure slower
-  constexpr int ROWS = 64;
+  // Every workgroup streams all of W1w through L1, so W1 bytes per token fall
+  // with the tile height: 128-token tiles of 8 waves (each wave with the
+  // registers of the 64-token layout's waves) once they still give about
+  // every CU a workgroup, else 64-token tiles of 4 waves.
   const int P = N - r;
-  const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
-  hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS>), dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, eps,
-                     W1w, b1, w2, b2, out);
-  return hipGetLastError();
+  if constexpr (H >= 128) {
+    if ((long long)B * ((P + 127) / 128) >= kTallTileMinBlocks)
+      return launch_rows<H, 128, 8>(resid, B, N, d, r, eps, W1w, b1, w2, b2, out, s);
+  }
+  return launch_rows<H, 64, 4>(resid, B, N, d, r, eps, W1w, b1, w2, b2, out, s);
 }
 
 }  // namespace
