@@ -14,32 +14,44 @@
 //    states in LDS at the end: the longest causal row runs as two
 //    independent chains, one per wave slot of each SIMD.
 //  * Scores are computed transposed, S^T = K Q^T: a lane owns one query and
-//    16 keys of a 32-key tile, so the row max/sum is an in-lane reduction
-//    plus one exchange with the partner lane (l ^ 32).  The softmax numerator
-//    P^T is then already in B-fragment layout for O^T += V^T P^T; the key
-//    order inside each 16-key step is permuted identically on both operands.
-//  * The logit is formed in the log2 domain with one FMA per element:
-//    z = s * (sm_scale*log2e/tau_i) + (gain_h*log2e) * b_j, the key term
-//    pre-multiplied per head by the prepass.
+//    16 keys of a 32-key half tile, so the row max/sum is an in-lane
+//    reduction plus one exchange with the partner lane (l ^ 32).  The softmax
+//    numerator P^T is then already in B-fragment layout for O^T += V^T P^T;
+//    the key order inside each 16-key step is permuted identically on both
+//    operands.
+//  * Software pipeline over 32-key half tiles: step h issues the score MFMAs
+//    of half h + 1 and the P.V MFMAs of half h - 1 while the vector ALUs run
+//    the softmax of half h, so the matrix cores never wait for the wave's own
+//    softmax.  In steady state the step is a fixed issue order (scheduling
+//    fences): every slot holds one MFMA, the LDS read of the fragment three
+//    slots ahead and a share of the softmax.
+//  * Steady-state scores are relative to the running max m: the score
+//    accumulator starts from -m / (scale of the query) instead of 0, so the
+//    logit FMA yields z - m and feeds exp2 directly.  The max is not
+//    recomputed every half: a half whose row sum exceeds 2^15 (a numerator
+//    that may leave fp16's range) takes a rare path that moves m to the
+//    row's true max and redoes that half.
 //  * The P.V product runs in fp16 (v_mfma_f32_32x32x16_f16): the softmax
-//    numerator P lies in [0, 1], where fp16 keeps 11 significant bits against
-//    bf16's 8, so rounding P costs 8x less.  V is converted once per call by
-//    a prepass into V^T (key-contiguous) fp16 scaled by 2^-8: bf16 values
-//    convert exactly up to |v| = 65504 * 2^8 (larger values saturate), values
-//    below 2^-6 land in fp16's subnormal range with an absolute error under
-//    2^-16.  The 2^8 is folded into the final 1/l.  Inside every 16-key group
-//    of V^T the middle two quads of keys are swapped, so that the 8 keys one
-//    lane contributes to a 16-key P.V step (4 at 4*gq, 4 at 8 + 4*gq) form
-//    one 16-byte chunk.
+//    numerator P lies in [0, 2^15], where fp16 keeps 11 significant bits
+//    against bf16's 8, so rounding P costs 8x less.  V is converted once per
+//    call by a prepass into V^T (key-contiguous) fp16 scaled by 2^-8: bf16
+//    values convert exactly up to |v| = 65504 * 2^8 (larger values saturate),
+//    values below 2^-6 land in fp16's subnormal range with an absolute error
+//    under 2^-16.  The 2^8 is folded into the final 1/l.  Inside every 16-key
+//    group of V^T the middle two quads of keys are swapped, so that the 8
+//    keys one lane contributes to a 16-key P.V step (4 at 4*gq, 4 at
+//    8 + 4*gq) form one 16-byte chunk.
 //  * Tiles travel from global memory straight into LDS (buffer loads with the
 //    LDS-destination bit: each lane's 16 bytes land at the wave's LDS base +
-//    16 * lane), double-buffered per group, so staging costs no registers and
-//    no LDS store instructions.  K rows (bf16) and V^T rows (fp16, 64 keys)
-//    are unpadded with their 16-byte chunks XOR-swizzled by (row & 7), which
-//    keeps the fragment reads free of bank conflicts; the lane-to-chunk map of
-//    each load applies the same swizzle.  The prepass also writes the
-//    key-score term of every query head, gain_h * log2(e) * b_j, so that tile
-//    too is a plain copy.
+//    16 * lane), so staging costs no registers and no LDS store
+//    instructions.  Every load is issued one iteration before the first
+//    iteration that reads it; K and V^T tiles are read within one iteration
+//    (two-slot rings per group), key scores across two (three-slot ring).
+//    K rows (bf16) and V^T rows (fp16, 64 keys) are unpadded with their
+//    16-byte chunks XOR-swizzled by (row & 7), which keeps the fragment reads
+//    free of bank conflicts; the lane-to-chunk map of each load applies the
+//    same swizzle.  The prepass also writes the key-score term of every query
+//    head, gain_h * log2(e) * b_j, so that tile too is a plain copy.
 //  * Grid: heaviest causal query blocks first, remapped so that every
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
@@ -55,9 +67,9 @@ constexpr int kBK = 64;  // keys per tile
 
 constexpr int kVScaleLog2 = 8;  // V^T holds fp16(V * 2^-8)
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
-// The running max is only moved (and the accumulator rescaled) when a tile's
-// max exceeds it by more than this many log2 units; P stays <= 2^8, well
-// inside fp16.
+// Outside the steady state the running max is only moved (and the
+// accumulator rescaled) when a half tile's max exceeds it by more than this
+// many log2 units; P stays <= 2^8 there.
 constexpr float kRescaleSlack = 8.0f;
 
 // max(a, b, c) as one v_max3_f32.  (The compiler's fmaxf adds a quieting
@@ -147,7 +159,7 @@ __device__ __forceinline__ void buffer_load4_to_lds(__amdgpu_buffer_rsrc_t rsrc,
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DH, int G>
-__global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     const float* __restrict__ kbias, int M, int Mp, int Hq, int Hkv, const int32_t* __restrict__ pos,
     const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb,
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   constexpr int NI = TILE / 1024 / 4;          // 1 KiB loads per wave per tile, for each of K and V^T
   constexpr int BIAS = G * kBK * 4;            // bytes of a key-score tile (G heads)
   constexpr int V_BASE = 2 * kGroups * TILE, B_BASE = 4 * kGroups * TILE;
-  constexpr int LDS_BYTES = B_BASE + 2 * kGroups * BIAS;
+  constexpr int LDS_BYTES = B_BASE + 3 * kGroups * BIAS;
   static_assert(NI >= 1 && NI * 4 * 1024 == TILE, "tile shape");
 
   constexpr int NV = DT * 16 + 2;            // floats per lane handed over in the merge
@@ -222,21 +234,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
   auto k_tile = [&](int buf) { return smem + (buf * kGroups + grp) * TILE; };
   auto v_tile = [&](int buf) { return smem + V_BASE + (buf * kGroups + grp) * TILE; };
   auto b_tile = [&](int buf) { return reinterpret_cast<float*>(smem + B_BASE + (buf * kGroups + grp) * BIAS); };
-  auto issue_tile = [&](int kb, int buf) {
-    const int key0 = kb * kBK;
+  // Group tile t is key tile grp + 2 t.  Its K rows, V^T rows and key-score
+  // rows are requested at different iterations (see the loop below): K and
+  // V^T into two-slot rings (slot t & 1), key scores into a three-slot ring
+  // (slot t % 3).
+  auto issue_k = [&](int t) __attribute__((always_inline)) {
+    const int key0 = (grp + kGroups * t) * kBK;
     const long long k_skip = (long long)key0 * Hkv * DH * 2;
     const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(k_base + (size_t)key0 * Hkv * DH), (short)0, (int)(k_bytes - k_skip), kBufferConfig);
-    unsigned char* kd = k_tile(buf) + wid * NI * 1024;
-    unsigned char* vd = v_tile(buf) + wid * NI * 1024;
+    unsigned char* kd = k_tile(t & 1) + wid * NI * 1024;
+#pragma unroll
+    for (int e = 0; e < NI; ++e) buffer_load16_to_lds(k_rsrc, kd + e * 1024, k_off[e], 0);
+  };
+  auto issue_v = [&](int t) __attribute__((always_inline)) {
+    unsigned char* vd = v_tile(t & 1) + wid * NI * 1024;
 #pragma unroll
     for (int e = 0; e < NI; ++e)
-      buffer_load16_to_lds(k_rsrc, kd + e * 1024, k_off[e], 0);
-#pragma unroll
-    for (int e = 0; e < NI; ++e)
-      buffer_load16_to_lds(v_rsrc, vd + e * 1024, v_off[e], key0 * 2);
+      buffer_load16_to_lds(v_rsrc, vd + e * 1024, v_off[e], (grp + kGroups * t) * kBK * 2);
+  };
+  auto issue_b = [&](int t) __attribute__((always_inline)) {
     if (wid < G)  // one 256-byte row per query head
-      buffer_load4_to_lds(b_rsrc, b_tile(buf) + wid * kBK, (wid * Mp + lane) * 4, key0 * 4);
+      buffer_load4_to_lds(b_rsrc, b_tile(t % 3) + wid * kBK, (wid * Mp + lane) * 4, (grp + kGroups * t) * kBK * 4);
   };
   // this lane's fragment chunks: K row ql (and ql + 32) chunk 2ks + gq; V^T row
   // 32t + ql chunk 2st + gq -- both swizzled by ql & 7
@@ -253,105 +272,244 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
     for (int i = 0; i < 16; ++i) o[t][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  // One 64-key tile for this wave's 32 queries.  `diag` (wave-uniform): the
-  // tile reaches past the wave's first query (diagonal or ragged tail), so
-  // keys after the query are masked; every other tile skips that block.
-  auto tile = [&](int buf, int key0, bool diag) {
-    // S^T = K Q^T for the two 32-key halves, the two accumulation chains
-    // interleaved so consecutive MFMAs are independent
-    f32x16 s0, s1;
+  // The pipeline runs over half tiles of 32 keys: half h of the group is keys
+  // [key0, key0 + 32) of group tile h >> 1, key0 = (grp + 2 (h >> 1)) * 64 + 32 (h & 1).
+  auto h_key0 = [&](int h) { return (grp + kGroups * (h >> 1)) * kBK + 32 * (h & 1); };
+  // the wave computes half h: its tile exists and it starts at or before the wave's last query
+  auto h_mine = [&](int h) { return h >= 0 && grp + kGroups * (h >> 1) < nkb && wave_rows && h_key0(h) <= rbase + 31; };
+
+  // S^T = K Q^T of half h: one 32 x 32 accumulation chain over DH
+  auto qk = [&](int h, f32x16& s) __attribute__((always_inline)) {
+    const unsigned char* kt = k_tile((h >> 1) & 1) + (h & 1) * 32 * KROW;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.0f;
-      s1[i] = 0.0f;
-    }
-    const unsigned char* kt = k_tile(buf);
+    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks));
-      const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks) + 32 * KROW);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qf[ks], s1, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
     }
-    // logits (log2 domain); lane holds keys 32T + 8(i/4) + 4gq + (i%4)
-    auto logits = [&](f32x16& st, int T) {
+  };
+  // O^T += V^T P^T over the two 16-key steps of half h
+  auto pv = [&](int h, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
+    const unsigned char* vt_l = v_tile((h >> 1) & 1);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(b_tile(buf) + hloc * kBK + T * 32 + i4 * 8 + gq * 4);
+    for (int sh = 0; sh < 2; ++sh) {
+      const u32x4 pw = {pk[sh * 4], pk[sh * 4 + 1], pk[sh * 4 + 2], pk[sh * 4 + 3]};
+      const f16x8 pf = as_f16x8(pw);
+      const int st = (h & 1) * 2 + sh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i4 * 4 + i] = fmaf(st[i4 * 4 + i], cq, bb[i]);
+      for (int t = 0; t < DT; ++t) {
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(vt_l + t * 32 * VROW + v_frag_off(st));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw), pf, o[t], 0, 0, 0);
       }
-    };
-    logits(s0, 0);
-    logits(s1, 1);
+    }
+  };
+  // Online softmax of half h's scores, without branches: the running max
+  // moves by a select, and the accumulator rescale this implies is left to
+  // the caller, which applies `alpha` after the P.V products issued before
+  // it.  `diag`: keys after the lane's query are masked.
+  auto softmax = [&](int h, f32x16& s, bool diag, uint32_t (&pk)[8], bool& resc,
+                     float& alpha) __attribute__((always_inline)) {
+    const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (h & 1) * 32 + gq * 4;
+    // logits (log2 domain); lane holds keys key0 + 8(i/4) + 4gq + (i%4)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(bt + i4 * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i4 * 4 + i] = fmaf(s[i4 * 4 + i], cq, bb[i]);
+    }
     if (diag) {
-      // key offset inside the tile (minus this lane's 4*gq) beyond thr => masked
-      const int thr = qi - key0 - gq * 4;
+      // key offset inside the half (minus this lane's 4*gq) beyond thr => masked
+      const int thr = qi - h_key0(h) - gq * 4;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = (i >> 2) * 8 + (i & 3);
-        s0[i] = off > thr ? -INFINITY : s0[i];
-        s1[i] = off + 32 > thr ? -INFINITY : s1[i];
-      }
+      for (int i = 0; i < 16; ++i) s[i] = (i >> 2) * 8 + (i & 3) > thr ? -INFINITY : s[i];
     }
-    // tile max: a max3 tree over the 32 logits, then the partner lane's
-    float x[11];
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      x[2 * j] = max3f(s0[3 * j], s0[3 * j + 1], s0[3 * j + 2]);
-      x[2 * j + 1] = max3f(s1[3 * j], s1[3 * j + 1], s1[3 * j + 2]);
-    }
-    x[10] = max3f(s0[15], s1[15], s1[15]);
-    float mloc = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], max3f(x[8], x[9], x[10])));
+    // max: a max3 tree over the 16 logits, then the partner lane's
+    const float x0 = max3f(s[0], s[1], s[2]), x1 = max3f(s[3], s[4], s[5]), x2 = max3f(s[6], s[7], s[8]);
+    const float x3 = max3f(s[9], s[10], s[11]), x4 = max3f(s[12], s[13], s[14]);
+    float mloc = max3f(max3f(x0, x1, x2), x3, max3f(x4, s[15], s[15]));
     {
       const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc), false, false);
       mloc = max3f(__uint_as_float(pr[0]), __uint_as_float(pr[1]), __uint_as_float(pr[1]));
     }
-    if (__ballot(mloc > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    resc = __ballot(mloc > m_run + kRescaleSlack) != 0;  // wave-uniform
+    const float m_new = resc ? fmaxf(m_run, mloc) : m_run;
+    alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    // (a lane with no visible key yet keeps m_run = -inf; its logits are all
+    // -inf too, and a finite reference keeps exp2 at 0 instead of NaN)
+    const float mref = m_run == -INFINITY ? 0.0f : m_run;
+    // numerators (rounded to fp16 for the P.V product) and their fp32 row sum
+    float l0 = 0.0f, l1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const float p0 = __builtin_amdgcn_exp2f(s[i] - mref), p1 = __builtin_amdgcn_exp2f(s[i + 1] - mref);
+      const float p2 = __builtin_amdgcn_exp2f(s[i + 2] - mref), p3 = __builtin_amdgcn_exp2f(s[i + 3] - mref);
+      l0 += p0 + p1;
+      l1 += p2 + p3;
+      pk[i / 2] = pack_f16x2(p0, p1);
+      pk[i / 2 + 1] = pack_f16x2(p2, p3);
+    }
+    l_run = fmaf(l_run, alpha, l0 + l1);
+  };
+  auto rescale = [&](bool resc, float alpha) __attribute__((always_inline)) {
+    if (resc) {
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
-    // (a lane with no visible key yet keeps m_run = -inf; its logits are all
-    // -inf too, and a finite reference keeps exp2 at 0 instead of NaN)
-    const float mref = m_run == -INFINITY ? 0.0f : m_run;
-    // numerators (rounded to fp16 for the P.V product) and their fp32 row sum
-    uint32_t pk[2][8];
-    float l0 = 0.0f, l1 = 0.0f;
+  };
+  // Pipeline step h: the scores of half h + 1 and the P.V product of half
+  // h - 1 run on the matrix cores while the vector ALUs run the softmax of
+  // half h, so the wave always has MFMA work that does not wait on its own
+  // softmax.  fast_step is the steady state (half h + 1 is computed by the
+  // wave, hence half h lies wholly before its first query and h - 1 >= 0 is
+  // computed too); step handles every case.
+  // Steady-state scores are kept relative to the running max: the score
+  // MFMA starts from cm = -m_run / cq instead of 0, so the logit FMA yields
+  // z - m_run directly.  The running max is then not recomputed every half:
+  // a half whose numerators could leave fp16 range (row sum > 2^15) takes a
+  // rare path that rescales with the true max.
+  f32x16 cm;
+  auto cm_value = [&]() { return (m_run == -INFINITY || cq == 0.0f) ? 0.0f : -m_run / cq; };
+  auto fast_step = [&](int h, f32x16& s, f32x16& sn, uint32_t (&pc)[8],
+                       const uint32_t (&pp)[8]) __attribute__((always_inline)) {
+    // NS = 2 KS issue slots: even slot k runs k-step k/2 of the scores of
+    // half h + 1, odd slot k runs P.V step k/2 of half h - 1 (16-key step
+    // (k/2) / DT, output tile (k/2) % DT).  Each slot also issues the LDS
+    // read of the fragment three slots ahead and a share of the softmax of
+    // half h (13 shares spread over the slots).  Scheduling fences keep
+    // this order.
+    constexpr int NS = 2 * KS;
+    static_assert(2 * DT == KS && 16 % NS == 0, "slot plan");
+    const unsigned char* kt = k_tile(((h + 1) >> 1) & 1) + ((h + 1) & 1) * 32 * KROW;
+    const unsigned char* vtl = v_tile(((h - 1) >> 1) & 1);
+    const int vst0 = ((h - 1) & 1) * 2;
+    const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (h & 1) * 32 + gq * 4;
+    u32x4 fr[NS];
+    auto read_frag = [&](int r) __attribute__((always_inline)) {
+      if (r & 1) {
+        const int p = r >> 1;
+        fr[r] = *reinterpret_cast<const u32x4*>(vtl + (p % DT) * 32 * VROW + v_frag_off(vst0 + p / DT));
+      } else {
+        fr[r] = *reinterpret_cast<const u32x4*>(kt + k_frag_off(r >> 1));
+      }
+    };
+    f32x4 bb[4];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(s0[i] - mref), p1 = __builtin_amdgcn_exp2f(s0[i + 1] - mref);
-      const float p2 = __builtin_amdgcn_exp2f(s1[i] - mref), p3 = __builtin_amdgcn_exp2f(s1[i + 1] - mref);
-      l0 += p0 + p1;
-      l1 += p2 + p3;
-      pk[0][i / 2] = pack_f16x2(p0, p1);
-      pk[1][i / 2] = pack_f16x2(p2, p3);
+    for (int i4 = 0; i4 < 4; ++i4) bb[i4] = *reinterpret_cast<const f32x4*>(bt + i4 * 8);
+#pragma unroll
+    for (int r = 0; r < 3 && r < NS; ++r) read_frag(r);
+    f16x8 pf[2];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      const u32x4 pw = {pp[sh * 4], pp[sh * 4 + 1], pp[sh * 4 + 2], pp[sh * 4 + 3]};
+      pf[sh] = as_f16x8(pw);
     }
-    l_run += l0 + l1;
-    // O^T += V^T P^T over 4 steps of 16 keys
+    const float l_prev = l_run;
+    __builtin_amdgcn_sched_barrier(0);
+    float l = 0.f;
+    bool ovf = false;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int T = st >> 1, h8 = (st & 1) * 4;
-      const u32x4 pw = {pk[T][h8], pk[T][h8 + 1], pk[T][h8 + 2], pk[T][h8 + 3]};
-      const f16x8 pf = as_f16x8(pw);
+    for (int k = 0; k < NS; ++k) {
+      if (k + 3 < NS) read_frag(k + 3);
+      if ((k & 1) == 0) {
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[k]), qf[k >> 1], k == 0 ? cm : sn, 0, 0, 0);
+      } else {
+        const int p = k >> 1;
+        o[p % DT] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(fr[k]), pf[p / DT], o[p % DT], 0, 0, 0);
+      }
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(v_tile(buf) + t * 32 * VROW + v_frag_off(st));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw), pf, o[t], 0, 0, 0);
+      for (int v = k * 16 / NS; v < (k + 1) * 16 / NS; ++v) {  // softmax shares of this slot
+        if (v < 4) {  // z - m_run (log2 domain) of keys 8v + 4gq + (0..3)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[v * 4 + i] = fmaf(s[v * 4 + i], cq, bb[v][i]);
+        }
+        if (v >= 4 && v < 12) {  // numerators 2(v-4), 2(v-4)+1
+          const int e = 2 * (v - 4);
+          const float p0 = __builtin_amdgcn_exp2f(s[e]), p1 = __builtin_amdgcn_exp2f(s[e + 1]);
+          l += p0 + p1;
+          pc[e / 2] = pack_f16x2(p0, p1);
+          asm volatile("" ::"v"(pc[e / 2]));  // computed in this slot, not sunk to its later use
+        }
+        if (v == 12) {
+          ovf = __ballot(!(l <= 32768.0f)) != 0;  // wave-uniform; catches inf too
+          l_run = l_prev + l;
+          asm volatile("" ::"v"(l_run));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ovf) {
+      // some numerator left the safe range: move the reference up to the
+      // row's true max and redo this half's numerators
+      const float x0 = max3f(s[0], s[1], s[2]), x1 = max3f(s[3], s[4], s[5]), x2 = max3f(s[6], s[7], s[8]);
+      const float x3 = max3f(s[9], s[10], s[11]), x4 = max3f(s[12], s[13], s[14]);
+      float mloc = max3f(max3f(x0, x1, x2), x3, max3f(x4, s[15], s[15]));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float d = fmaxf(mloc, 0.0f);
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      m_run += d;
+      float l2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(s[e] - d), p1 = __builtin_amdgcn_exp2f(s[e + 1] - d);
+        l2 += p0 + p1;
+        pc[e / 2] = pack_f16x2(p0, p1);
+      }
+      l_run = fmaf(l_prev, alpha, l2);
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+      // the scores of half h + 1 were started from the old reference
+      const float dq = cq == 0.0f ? 0.0f : d / cq;
+      const float mc = cm_value();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sn[i] -= dq;
+        cm[i] = mc;
       }
     }
   };
+  auto step = [&](int h, f32x16& s_cur, f32x16& s_next, uint32_t (&p_cur)[8],
+                  const uint32_t (&p_prev)[8]) __attribute__((always_inline)) {
+    bool resc = false;
+    float alpha = 1.0f;
+    if (h_mine(h - 1)) pv(h - 1, p_prev);
+    if (h_mine(h)) softmax(h, s_cur, h_key0(h) + 31 > rbase, p_cur, resc, alpha);
+    if (h_mine(h + 1)) qk(h + 1, s_next);
+    rescale(resc, alpha);
+  };
 
-  // group grp owns tiles grp, grp + 2, ...; both groups meet at every barrier
-  // (a buffer is refilled only after the barrier that ends its last use, and
-  // read only after the barrier that follows its loads' completion)
-  const int nit = (nkb + kGroups - 1) / kGroups;
-  if (grp < nkb) issue_tile(grp, 0);
+  // Staging: iteration i (pipeline steps 2i + 1 and 2i + 2) reads K of group
+  // tile i + 1, V^T of tile i and key scores of tiles i and i + 1, and
+  // requests K of tile i + 2, V^T of tile i + 1 and key scores of tile i + 2
+  // into the slots whose last reads ended at the previous iteration's
+  // barrier; its loads complete before its own closing barrier.
+  const int nit = (nkb + kGroups - 1) / kGroups;  // tiles of group 0 (group 1 has as many or one fewer)
+  auto t_exists = [&](int t) { return grp + kGroups * t < nkb; };
+  // Leading iterations in which every wave of the workgroup is in steady
+  // state for both steps: half 2i + 3 must be computed by the wave with the
+  // lowest rows (rbase = q0) in either group.
+  int n_steady = nit;
+#pragma unroll
+  for (int gg = 0; gg < kGroups; ++gg) {
+    const int nt = (nkb - gg + kGroups - 1) / kGroups;  // tiles of group gg
+    const int X = q0 + 31 - kBK * gg;                   // last visible key offset past the group's first tile
+    int hmax = -1;                                      // last half the lowest wave of group gg computes
+    if (X >= 0 && nt > 0) {
+      const int tm = min(nt - 1, X / (kGroups * kBK));
+      hmax = 2 * tm + ((X - kGroups * kBK * tm) >= 32 ? 1 : 0);
+    }
+    n_steady = min(n_steady, hmax >= 3 ? ((hmax - 3) >> 1) + 1 : 0);
+  }
+  n_steady = __builtin_amdgcn_readfirstlane(n_steady);
+  if (t_exists(0)) {
+    issue_k(0);
+    issue_b(0);
+  }
   // Q fragments and the original position are requested while the first
   // tile is in flight; one wait covers all of them
   {
@@ -368,12 +526,51 @@ __global__ __launch_bounds__(kAttnThreads, 2) void gated_attn_kernel(
     cq = sm_scale * kLog2e / (t_h * ratio);
   }
   __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const int buf = it & 1;
-    const int kb = it * kGroups + grp;
-    if (kb + kGroups < nkb) issue_tile(kb + kGroups, buf ^ 1);
-    const int key0 = kb * kBK;
-    if (kb < nkb && wave_rows && key0 <= rbase + 31) tile(buf, key0, key0 + kBK - 1 > rbase);  // wave-uniform
+  if (t_exists(1)) {
+    issue_k(1);
+    issue_b(1);
+  }
+  if (t_exists(0)) issue_v(0);
+  f32x16 sa, sb;
+  uint32_t pa[8], pb[8];
+  if (h_mine(0)) qk(0, sa);
+  step(0, sa, sb, pa, pb);  // no P.V yet: half -1 is never computed
+  wait_vmem();
+  __syncthreads();
+  auto stage = [&](int i) __attribute__((always_inline)) {
+    if (t_exists(i + 2)) {
+      issue_k(i + 2);
+      issue_b(i + 2);
+    }
+    if (t_exists(i + 1)) issue_v(i + 1);
+  };
+  int i = 0;
+  if (n_steady > 0) {
+    // enter the relative form: the pending scores of half 1 and the
+    // accumulator start value
+    const float mc = cm_value();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      cm[e] = mc;
+      sb[e] += mc;
+    }
+    auto iter = [&](int it) __attribute__((always_inline)) {
+      stage(it);
+      fast_step(2 * it + 1, sb, sa, pb, pa);
+      fast_step(2 * it + 2, sa, sb, pa, pb);
+      wait_vmem();
+      __syncthreads();
+    };
+    // two iterations per trip: the ring slots of every access are then fixed
+    for (; i < n_steady; ++i) iter(i);
+    // leave it: the pending scores go back to the plain form
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sb[e] -= cm[e];
+  }
+  for (; i < nit; ++i) {
+    stage(i);
+    step(2 * i + 1, sb, sa, pb, pa);
+    step(2 * i + 2, sa, sb, pa, pb);
     wait_vmem();
     __syncthreads();
   }
