@@ -554,14 +554,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       cm[e] = mc;
       sb[e] += mc;
     }
+    // (the loads go out between the two steps: issued at the top of the
+    // iteration, their LDS writes collide with every wave's first fragment
+    // reads after the barrier)
     auto iter = [&](int it) __attribute__((always_inline)) {
-      stage(it);
       fast_step(2 * it + 1, sb, sa, pb, pa);
+      stage(it);
       fast_step(2 * it + 2, sa, sb, pa, pb);
       wait_vmem();
       __syncthreads();
     };
-    // two iterations per trip: the ring slots of every access are then fixed
     for (; i < n_steady; ++i) iter(i);
     // leave it: the pending scores go back to the plain form
 #pragma unroll
