@@ -72,6 +72,11 @@ constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 f
 // many log2 units; P stays <= 2^8 there.
 constexpr float kRescaleSlack = 8.0f;
 
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 // max(a, b, c) as one v_max3_f32.  (The compiler's fmaxf adds a quieting
 // v_max_f32 x,x,x per operand in IEEE mode; the logits here are never NaN.)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -178,8 +183,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   constexpr int LDS_BYTES = B_BASE + 3 * kGroups * BIAS;
   static_assert(NI >= 1 && NI * 4 * 1024 == TILE, "tile shape");
 
-  constexpr int NV = DT * 16 + 2;            // floats per lane handed over in the merge
-  static_assert(4 * 64 * NV * 4 <= B_BASE, "merge buffer");
 
   // [buf][group] K tiles, then [buf][group] V^T tiles, then [buf][group][head] key-score tiles
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
@@ -577,23 +580,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     __syncthreads();
   }
 
-  // merge the two groups' online-softmax states (the tile buffers are free
-  // now): group 1 hands over m, l and O as 16-byte vectors per lane
+  // Merge the two groups' online-softmax states (the tile buffers are free
+  // now).  Each group finalises half of the output columns: group g keeps
+  // O^T tiles [g DT/2, (g+1) DT/2) and hands its other tiles, with m and l,
+  // to the other group as 16-byte vectors per lane.  (The group number is
+  // made a constant of each branch so that o[] keeps static indices.)
+  constexpr int DH2 = DT / 2;  // O^T tiles finalised per group
+  static_assert(2 * DH2 == DT, "column split");
   f32x4* sm4 = reinterpret_cast<f32x4*>(smem);
   const int slot = wid * 64 + lane;
-  if (grp == 1) {
-    sm4[slot] = f32x4{m_run, l_run, 0.0f, 0.0f};
+  // LDS: [group][256] (m, l), then [receiving group][tile][i4][256] O values
+  auto o_slot = [&](int dst, int j, int i4) { return 512 + ((dst * DH2 + j) * 4 + i4) * 256 + slot; };
+  // Output rows leave through LDS so that each store writes whole 16-byte
+  // pieces: the wave's 32 rows x (its group's DH/2 columns) bf16 block is
+  // written row-major with the 16-byte chunks of row r XOR-swizzled by r,
+  // then read back 16 bytes per lane.  The region lies past the merge
+  // vectors and belongs to this wave alone, and LDS operations of one wave
+  // complete in order.
+  constexpr int HROW = DH;        // bytes of half an output row
+  constexpr int HCH = HROW / 16;  // its 16-byte chunks
+  static_assert((512 + 2 * DH2 * 4 * 256) * 16 + kGroups * 4 * 32 * HROW <= LDS_BYTES, "merge and output staging");
+  auto hand_over = [&](auto gc) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value, og = 1 - g;
+    sm4[g * 256 + slot] = f32x4{m_run, l_run, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int j = 0; j < DH2; ++j)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        sm4[(1 + t * 4 + i4) * 256 + slot] =
-            f32x4{o[t][i4 * 4], o[t][i4 * 4 + 1], o[t][i4 * 4 + 2], o[t][i4 * 4 + 3]};
-  }
-  __syncthreads();
-  if (grp == 1) return;
-  {
-    const f32x4 ml = sm4[slot];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int t = og * DH2 + j;
+        sm4[o_slot(og, j, i4)] = f32x4{o[t][i4 * 4], o[t][i4 * 4 + 1], o[t][i4 * 4 + 2], o[t][i4 * 4 + 3]};
+      }
+  };
+  auto finish = [&](auto gc) __attribute__((always_inline)) {
+    constexpr int g = decltype(gc)::value, og = 1 - g;
+    const f32x4 ml = sm4[og * 256 + slot];
     const float m1 = ml[0], l1 = ml[1];
     const float m = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
@@ -601,45 +621,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     m_run = m;
     l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int j = 0; j < DH2; ++j)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 o1 = sm4[(1 + t * 4 + i4) * 256 + slot];
+        const int t = g * DH2 + j;
+        const f32x4 o1 = sm4[o_slot(g, j, i4)];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i4 * 4 + i] = o[t][i4 * 4 + i] * a0 + o1[i] * a1;
       }
-  }
-
-  if (!wave_rows) return;
-  const float l_tot = pair_sum(l_run);
-  const float inv = (float)(1 << kVScaleLog2) / l_tot;
-  // Output rows leave through LDS so that each store writes whole 16-byte
-  // pieces of a row: the wave's 32 x DH bf16 block is written row-major with
-  // the 16-byte chunks of row r XOR-swizzled by r & 15, then read back 16
-  // bytes per lane.  The region lies past the merge vectors and belongs to
-  // this wave alone, and LDS operations of one wave complete in order.
-  constexpr int OROW = DH * 2;  // bytes of an output row
-  unsigned char* ob = smem + (1 + DT * 4) * 256 * 16 + wid * 32 * OROW;
-  static_assert((1 + DT * 4) * 256 * 16 + 4 * 32 * OROW <= LDS_BYTES, "output staging");
+    if (!wave_rows) return;
+    const float l_tot = pair_sum(l_run);
+    const float inv = (float)(1 << kVScaleLog2) / l_tot;
+    unsigned char* ob = smem + (512 + 2 * DH2 * 4 * 256) * 16 + wall * 32 * HROW;
 #pragma unroll
-  for (int t = 0; t < DT; ++t)
+    for (int j = 0; j < DH2; ++j)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      // d = 32t + 8 i4 + 4gq + (0..3): chunk 4t + i4 of the row, half gq
-      u32x2 w;
-      w[0] = pack_bf16x2(o[t][i4 * 4 + 0] * inv, o[t][i4 * 4 + 1] * inv);
-      w[1] = pack_bf16x2(o[t][i4 * 4 + 2] * inv, o[t][i4 * 4 + 3] * inv);
-      const int chunk = (t * 4 + i4) ^ (ql & (KCH - 1));
-      *reinterpret_cast<u32x2*>(ob + ql * OROW + chunk * 16 + gq * 8) = w;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        // d = 32t + 8 i4 + 4gq + (0..3), t = g DH2 + j: chunk 4j + i4 of the half row, half gq
+        const int t = g * DH2 + j;
+        u32x2 w;
+        w[0] = pack_bf16x2(o[t][i4 * 4 + 0] * inv, o[t][i4 * 4 + 1] * inv);
+        w[1] = pack_bf16x2(o[t][i4 * 4 + 2] * inv, o[t][i4 * 4 + 3] * inv);
+        const int chunk = (j * 4 + i4) ^ (ql & (HCH - 1));
+        *reinterpret_cast<u32x2*>(ob + ql * HROW + chunk * 16 + gq * 8) = w;
+      }
+    constexpr int RPI = 64 / HCH;  // rows per 64-lane store
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int r = r0 + lane / HCH, c = lane % HCH;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(ob + r * HROW + ((c ^ (r & (HCH - 1))) * 16));
+      if (rbase + r < M) store16(out + (((size_t)b * M + rbase + r) * Hq + hq) * DH + g * (DH / 2) + c * 8, w);
     }
-  constexpr int RPI = 64 / KCH;  // rows per 64-lane store
-#pragma unroll
-  for (int r0 = 0; r0 < 32; r0 += RPI) {
-    const int r = r0 + lane / KCH, c = lane % KCH;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(ob + r * OROW + ((c ^ (r & (KCH - 1))) * 16));
-    if (rbase + r < M) store16(out + (((size_t)b * M + rbase + r) * Hq + hq) * DH + c * 8, w);
-  }
-  if (lse != nullptr && gq == 0 && q_ok) lse[((size_t)b * Hq + hq) * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (lse != nullptr && g == 0 && gq == 0 && q_ok)
+      lse[((size_t)b * Hq + hq) * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
+  };
+  if (grp == 0)
+    hand_over(IntConst<0>{});
+  else
+    hand_over(IntConst<1>{});
+  __syncthreads();
+  if (grp == 0)
+    finish(IntConst<0>{});
+  else
+    finish(IntConst<1>{});
 }
 
 template <int DH, int G>
