@@ -376,27 +376,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   // rare path that rescales with the true max.
   f32x16 cm;
   auto cm_value = [&]() { return (m_run == -INFINITY || cq == 0.0f) ? 0.0f : -m_run / cq; };
-  auto fast_step = [&](int h, f32x16& s, f32x16& sn, uint32_t (&pc)[8],
-                       const uint32_t (&pp)[8]) __attribute__((always_inline)) {
+  // This lane's fragment chunks, as loop-invariant LDS offsets: with
+  // c = q7 >> 1 and e = q7 & 1, chunk (2j + gq) ^ q7 = 2 (j ^ c) + (gq ^ e),
+  // so K k-step ks sits at k_lane[ks & 3] + 128 (ks >> 2) and V^T step st at
+  // v_lane[st]; ring slot and half tile only add constants.
+  int k_lane[4], v_lane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sw = 32 * (j ^ (q7 >> 1)) + 16 * (gq ^ (q7 & 1));
+    k_lane[j] = grp * TILE + ql * KROW + sw;
+    v_lane[j] = V_BASE + grp * TILE + ql * VROW + sw;
+  }
+  // Steady-state step: SB = 0 for an iteration's first step (h = 2i + 1),
+  // 1 for its second (h = 2i + 2); kb / vb are the lane bases of the
+  // iteration's K slot (tile i + 1) and V^T slot (tile i).
+  auto fast_step = [&](int h, f32x16& s, f32x16& sn, uint32_t (&pc)[8], const uint32_t (&pp)[8],
+                       const int (&kb)[4], const int (&vb)[4], auto step_c) __attribute__((always_inline)) {
     // NS = 2 KS issue slots: even slot k runs k-step k/2 of the scores of
     // half h + 1, odd slot k runs P.V step k/2 of half h - 1 (16-key step
     // (k/2) / DT, output tile (k/2) % DT).  Each slot also issues the LDS
     // read of the fragment three slots ahead and a share of the softmax of
     // half h (13 shares spread over the slots).  Scheduling fences keep
     // this order.
+    constexpr int SB = decltype(step_c)::value;
     constexpr int NS = 2 * KS;
     static_assert(2 * DT == KS && 16 % NS == 0, "slot plan");
-    const unsigned char* kt = k_tile(((h + 1) >> 1) & 1) + ((h + 1) & 1) * 32 * KROW;
-    const unsigned char* vtl = v_tile(((h - 1) >> 1) & 1);
-    const int vst0 = ((h - 1) & 1) * 2;
-    const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (h & 1) * 32 + gq * 4;
+    const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (1 - SB) * 32 + gq * 4;
     u32x4 fr[NS];
     auto read_frag = [&](int r) __attribute__((always_inline)) {
       if (r & 1) {
         const int p = r >> 1;
-        fr[r] = *reinterpret_cast<const u32x4*>(vtl + (p % DT) * 32 * VROW + v_frag_off(vst0 + p / DT));
+        fr[r] = *reinterpret_cast<const u32x4*>(smem + vb[2 * SB + p / DT] + (p % DT) * 32 * VROW);
       } else {
-        fr[r] = *reinterpret_cast<const u32x4*>(kt + k_frag_off(r >> 1));
+        const int ks = r >> 1;
+        fr[r] = *reinterpret_cast<const u32x4*>(smem + kb[ks & 3] + SB * 32 * KROW + 128 * (ks >> 2));
       }
     };
     f32x4 bb[4];
@@ -561,9 +574,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     // iteration, their LDS writes collide with every wave's first fragment
     // reads after the barrier)
     auto iter = [&](int it) __attribute__((always_inline)) {
-      fast_step(2 * it + 1, sb, sa, pb, pa);
+      // ring slots of this iteration: K of tile it + 1, V^T of tile it
+      int kb[4], vb[4];
+      const int koff = ((it + 1) & 1) * kGroups * TILE, voff = (it & 1) * kGroups * TILE;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kb[j] = k_lane[j] + koff;
+        vb[j] = v_lane[j] + voff;
+      }
+      fast_step(2 * it + 1, sb, sa, pb, pa, kb, vb, IntConst<0>{});
       stage(it);
-      fast_step(2 * it + 2, sa, sb, pa, pb);
+      fast_step(2 * it + 2, sa, sb, pa, pb, kb, vb, IntConst<1>{});
       wait_vmem();
       __syncthreads();
     };
