@@ -8,8 +8,10 @@ token-gated causal GQA attention calls (16q / 8kv heads, d_h 128) on the
 compacted stream.
 
 One step = one pass of the whole path over one input:
-    tg_gate_score -> tg_seq_rmsnorm -> tg_topk_select -> tg_compact
+    tg_gate_score -> tg_gate_select (sequence norm, top-K, compaction)
     -> 24 x tg_gated_attention
+(--separate-gate runs tg_seq_rmsnorm, tg_topk_select and tg_compact instead
+of tg_gate_select; the results are the same bit for bit)
 with every input already resident in HBM.  The residual is rotated over
 several copies (> the 256 MiB Infinity Cache) so the HBM-bound kernels read
 HBM.  The per-layer Q/K/V are the upper layers' projections of the compacted
@@ -137,6 +139,8 @@ def main():
     ap.add_argument("--frac", type=float, default=0.10, help="budget fraction for sweep_128k")
     ap.add_argument("--layers", type=int, default=None, help="upper layers (default: 24 for stage_32k, else 1)")
     ap.add_argument("--copies", type=int, default=0, help="residual copies rotated per step (0: enough for 512 MiB)")
+    ap.add_argument("--separate-gate", action="store_true",
+                    help="run sequence norm, top-K and compaction as three calls instead of tg_gate_select")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the reference for "
@@ -206,15 +210,22 @@ def main():
     gate_ws = tg.gate_workspace(h, d, dev)
     seq_ws = tg.seq_rmsnorm_workspace(1, N, dev)   # None up to N = 32768
     topk_ws = tg.topk_workspace(1, N, dev)
+    sel_ws = tg.gate_select_workspace(1, N, dev)   # None up to N = 32768
+    sel_phases = ("seq_rmsnorm", "topk_select", "compact") if args.separate_gate else ("gate_select",)
 
     def gate(x, ev=None):
         run = (lambda name, fn: ev.phase(name, fn)) if ev else (lambda name, fn: fn())
         run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
                                                    ws=gate_ws))
-        run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws))
-        run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws))
-        run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
-                                              score_out=b_S))
+        if args.separate_gate:
+            run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws))
+            run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws))
+            run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
+                                                  score_out=b_S))
+        else:
+            run("gate_select", lambda: tg.tg_gate_select(score, x, r, K, c.eps_seq, score=score, keep=keep,
+                                                          kept_idx=kept_idx, resid_out=resid_S, score_out=b_S,
+                                                          ws=sel_ws))
 
     gate(resid0)
     torch.cuda.synchronize()
@@ -270,12 +281,15 @@ def main():
     # ---------------- figures ----------------
     e = 2
     P = N - r
-    algo = {
-        "gate_score": dict(bytes=P * d * e + h * d * e + 4 * N, flops=2 * P * d * h, bound="hbm"),
-        "seq_rmsnorm": dict(bytes=4 * P + 4 * N, flops=2 * P, bound="latency"),
-        "topk_select": dict(bytes=4 * P + N, flops=0, bound="latency"),
-        "compact": dict(bytes=N + 2 * M * d * e + 12 * M, flops=0, bound="hbm"),
-    }
+    algo = {"gate_score": dict(bytes=P * d * e + h * d * e + 4 * N, flops=2 * P * d * h, bound="hbm")}
+    if args.separate_gate:
+        algo["seq_rmsnorm"] = dict(bytes=4 * P + 4 * N, flops=2 * P, bound="latency")
+        algo["topk_select"] = dict(bytes=4 * P + N, flops=0, bound="latency")
+        algo["compact"] = dict(bytes=N + 2 * M * d * e + 12 * M, flops=0, bound="hbm")
+    else:
+        # raw scores in, normalised scores, keep mask, kept_idx and kept scores
+        # out, kept_idx read back by the gather, kept rows read and written
+        algo["gate_select"] = dict(bytes=4 * P + 4 * N + N + 12 * M + 2 * M * d * e, flops=2 * P, bound="latency")
     if layers:
         Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
         algo["gated_attention"] = dict(bytes=M * dh * e * (2 * Hq + 2 * Hkv) + 8 * M,
@@ -294,8 +308,8 @@ def main():
             ent["mfma_frac"] = round(tf / PEAK_BF16_TFLOPS, 4)
         kernels[name] = ent
     kernel_us_sum = sum(kernels[n]["avg_us"] * kernels[n]["launches_per_step"] for n in kernels)
-    gate_us = sum(kernels[n]["avg_us"] for n in ("gate_score", "seq_rmsnorm", "topk_select", "compact"))
-    gate_bytes = sum(algo[n]["bytes"] for n in ("gate_score", "seq_rmsnorm", "topk_select", "compact"))
+    gate_us = sum(kernels[n]["avg_us"] for n in ("gate_score",) + sel_phases)
+    gate_bytes = sum(algo[n]["bytes"] for n in ("gate_score",) + sel_phases)
 
     if layers:
         dom, dom_file = "gated_attention", "gated_attention.hip"
@@ -320,7 +334,8 @@ def main():
                    "residual_copies": ncopy},
         "roofline": roofline,
         "kernels": kernels,
-        "gate_op": {"avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
+        "gate_op": {"calls": ["tg_gate_score"] + ["tg_" + n for n in sel_phases],
+                    "avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
                     "achieved_GBs": round(gate_bytes / (gate_us * 1e-6) / 1e9, 1),
                     "hbm_frac": round(gate_bytes / (gate_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "library_kernel_tokens_per_s": round(N / (kernel_us_sum * 1e-6), 1),

@@ -51,7 +51,8 @@ typedef enum {
   TG_OP_SEQ_RMSNORM = 1,
   TG_OP_TOPK_SELECT = 2,
   TG_OP_COMPACT = 3,
-  TG_OP_GATED_ATTENTION = 4
+  TG_OP_GATED_ATTENTION = 4,
+  TG_OP_GATE_SELECT = 5
 } tg_op;
 
 /*
@@ -147,6 +148,35 @@ int tg_topk_select(const float* score, int B, int N, int r, int K,
 int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* keep,
                const float* score, int M, int32_t* kept_idx, void* resid_out,
                float* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tg_gate_select -- tg_seq_rmsnorm, tg_topk_select and tg_compact in one call
+ * (paper Section 4: the sequence RMSNorm of the scores, second half of Eq. 3;
+ * the Top-K Selector, Eq. 4; compaction to the kept set, Appendix C.4).
+ *
+ * Every output is bit-identical to the three calls in sequence with
+ * M = r + min(K, N - r):
+ *     score     = tg_seq_rmsnorm(score_raw)
+ *     keep      = tg_topk_select(score, K)
+ *     kept_idx, resid_out, score_out = tg_compact(resid, keep, score, M)
+ * Rows of up to 32768 tokens take two launches (one workgroup per batch row
+ * normalises, selects and writes the kept indices and scores; then the row
+ * gather); longer rows run the three calls.
+ *
+ *   score_raw [B, N] fp32 in;  score [B, N] fp32 out (may alias score_raw)
+ *   keep [B, N] uint8 out;  resid [B, N, d] dtype `dt`, 16-byte aligned
+ *   kept_idx [B, M] int32, resid_out [B, M, d] dtype `dt`, score_out [B, M]
+ *   fp32 out
+ *   ws, ws_bytes     workspace of tg_workspace_size(TG_OP_GATE_SELECT, B, N,
+ *                    ...) bytes, 16-byte aligned: none for N <= 32768, else
+ *                    the larger of the TG_OP_SEQ_RMSNORM and TG_OP_TOPK_SELECT
+ *                    workspaces (contents need no initialisation)
+ * Requires d * sizeof(dt) % 16 == 0 and K >= 0.
+ */
+int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, int K,
+                   const void* resid, int dt, int d, float* score, uint8_t* keep,
+                   int32_t* kept_idx, void* resid_out, float* score_out,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tg_gated_attention -- token-gated causal GQA attention over the kept set

@@ -21,9 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libtokengate.so")
 
 TG_OK, TG_EINVAL, TG_EUNSUPPORTED, TG_EHIP = 0, 1, 2, 3
 TG_F32, TG_BF16 = 0, 1
-TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION = range(5)
+TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION, TG_OP_GATE_SELECT = range(6)
 
-EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
+EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
@@ -50,13 +50,15 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_topk_select.argtypes = [vp, i, i, i, i, vp, vp, sz, vp]
     lib.tg_compact.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
+    lib.tg_gate_select.argtypes = [vp, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
     lib.tg_last_error.restype = ctypes.c_char_p
     lib.tg_version.argtypes = []
     lib.tg_version.restype = i
-    for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention"):
+    for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
+                 "tg_gate_select"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -218,6 +220,48 @@ def tg_compact(resid, keep, score, M: int, kept_idx=None, resid_out=None, score_
     return kept_idx, resid_out, score_out
 
 
+def gate_select_workspace(B: int, N: int, device="cuda") -> torch.Tensor | None:
+    """A workspace for tg_gate_select at these sizes (None when it needs none: N <= 32768)."""
+    return _op_workspace(TG_OP_GATE_SELECT, B, N, device)
+
+
+def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, score=None, keep=None, kept_idx=None,
+                   resid_out=None, score_out=None, ws=None, stream=None):
+    """tg_seq_rmsnorm, tg_topk_select and tg_compact in one call (bit-identical results).
+
+    Returns ``(kept_idx [B, M] int32, resid_out [B, M, d], score_out [B, M] fp32, keep [B, N] uint8,
+    score [B, N] fp32)`` with ``M = r + min(K, N - r)``.  ``score`` may be ``score_raw`` (in place).
+    ``ws``: from :func:`gate_select_workspace` (allocated here when needed and omitted).
+    """
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    dev = resid.device
+    M = kept_count(N, r, K)
+    if score is None:
+        score = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, N), dtype=torch.uint8, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if resid_out is None:
+        resid_out = torch.empty((B, M, d), dtype=resid.dtype, device=dev)
+    if score_out is None:
+        score_out = torch.empty((B, M), dtype=torch.float32, device=dev)
+    _need(score, "score", torch.float32, (B, N))
+    _need(keep, "keep", torch.uint8, (B, N))
+    _need(kept_idx, "kept_idx", torch.int32, (B, M))
+    _need(resid_out, "resid_out", resid.dtype, (B, M, d))
+    _need(score_out, "score_out", torch.float32, (B, M))
+    if ws is None:
+        ws = gate_select_workspace(B, N, dev)
+    wp, wn = _ws_args(ws)
+    _check(lib.tg_gate_select(_ptr(score_raw), B, N, r, eps_seq, K, _ptr(resid), _dt(resid), d, _ptr(score),
+                              _ptr(keep), _ptr(kept_idx), _ptr(resid_out), _ptr(score_out), wp, wn, _stream(stream)))
+    return kept_idx, resid_out, score_out, keep, score
+
+
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
     """A workspace tensor large enough for tg_gated_attention at these sizes."""
     n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, Hq, 0))
@@ -269,16 +313,15 @@ def tg_version() -> int:
 
 
 def gated_prefill_gate(resid, r: int, K: int, norm_w, W1, b1, w2, b2, eps_row=1e-6, eps_seq=1e-6, ws=None,
-                       seq_ws=None, topk_ws=None, stream=None):
+                       sel_ws=None, stream=None):
     """The gate at layer L, end to end: score -> sequence norm -> top-K -> compaction.
 
-    Returns ``(kept_idx, resid_S, b_S, keep, score)``.  Four library calls on
-    one stream, no host synchronisation (M is known on the host).
+    Returns ``(kept_idx, resid_S, b_S, keep, score)``.  Two library calls
+    (tg_gate_score, tg_gate_select) on one stream, no host synchronisation
+    (M is known on the host).  ``ws``: the scorer's workspace; ``sel_ws``:
+    tg_gate_select's.
     """
-    B, N, _ = resid.shape
     raw = tg_gate_score(resid, r, norm_w, W1, b1, w2, b2, eps_row, ws=ws, stream=stream)
-    score = tg_seq_rmsnorm(raw, r, eps_seq, score=raw, ws=seq_ws, stream=stream)
-    keep = tg_topk_select(score, r, K, ws=topk_ws, stream=stream)
-    M = kept_count(N, r, K)
-    kept_idx, resid_S, b_S = tg_compact(resid, keep, score, M, stream=stream)
+    kept_idx, resid_S, b_S, keep, score = tg_gate_select(raw, resid, r, K, eps_seq, score=raw, ws=sel_ws,
+                                                         stream=stream)
     return kept_idx, resid_S, b_S, keep, score

@@ -141,6 +141,18 @@ __global__ __launch_bounds__(kGatherThreads) void compact_gather_kernel(const ui
 
 }  // namespace
 
+hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
+                                 const int32_t* kept_idx, void* resid_out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  const size_t total = (size_t)M * (row_bytes / 16);
+  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
+  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
+                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, M, kept_idx,
+                     reinterpret_cast<uint8_t*>(resid_out));
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,
                           const float* score, int M, int32_t* kept_idx, void* resid_out, float* score_out,
                           hipStream_t s) {
@@ -149,13 +161,7 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
                      keep, score, N, M, kept_idx, score_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t total = (size_t)M * (row_bytes / 16);
-  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
-  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
-  hipLaunchKernelGGL(compact_gather_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
-                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, M, kept_idx,
-                     reinterpret_cast<uint8_t*>(resid_out));
-  return hipGetLastError();
+  return launch_compact_gather(resid, row_bytes, B, N, M, kept_idx, resid_out, s);
 }
 
 }  // namespace tg

@@ -12,30 +12,20 @@
 // in-place call is safe: no slice is written before every sum is taken).
 // Each thread's sum of squares (32 terms) is fp32; thread, wave, slice and
 // chunk partials are combined in fp64 in a fixed order (deterministic).
+#include "select_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
 namespace tg {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kVec = 8;                       // 16-byte loads per thread per chunk
-constexpr int kChunk = kThreads * kVec * 4;  // 32768 scores
+using sel::load_scores;
+constexpr int kThreads = sel::kRowThreads;
+constexpr int kVec = sel::kRowVec;           // 16-byte loads per thread
+constexpr int kChunk = sel::kRowChunk;      // 32768 scores: the single-workgroup limit
 
-__device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r, bool vec) {
-  f32x4 v;
-  if (vec && j + 4 <= N) {
-    v = *reinterpret_cast<const f32x4*>(x + j);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = j + i < N ? x[j + i] : 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = j + i >= r ? v[i] : 0.0f;
-  return v;
-}
-
-// `in` and `out` may alias (in-place normalisation).
+// Rows of up to kChunk scores.  `in` and `out` may alias (in-place
+// normalisation): every score is read before the barriers of the reduction.
 __global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, int N, int r, float eps,
                                                                float* out) {
   __shared__ double s_part[kThreads / 64];
@@ -44,49 +34,24 @@ __global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, 
   const int b = blockIdx.x;
   const float* x = in + (size_t)b * N;
   float* y = out + (size_t)b * N;
-  const int P = N - r;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
 
   f32x4 v[kVec];
-  double acc = 0.0;
-  for (int c0 = 0; c0 < N; c0 += kChunk) {
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kThreads + tid) * 4, N, r, vec);
-    float part = 0.0f;
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, (e * kThreads + tid) * 4, N, r, vec);
+  const double scale = sel::row_inv_rms(v, N - r, eps, s_part, &s_scale);
 #pragma unroll
-    for (int e = 0; e < kVec; ++e)
+  for (int e = 0; e < kVec; ++e) {
+    const int j = (e * kThreads + tid) * 4;
+    f32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(v[e][i], v[e][i], part);
-    acc += (double)part;
-  }
-  acc = wave_sum_f64(acc);
-  if ((tid & 63) == 0) s_part[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) t += s_part[w];
-    s_scale = P > 0 ? 1.0 / sqrt(t / (double)P + (double)eps) : 0.0;
-  }
-  __syncthreads();
-  const double scale = s_scale;
-  for (int c0 = 0; c0 < N; c0 += kChunk) {
-    if (N > kChunk) {  // otherwise the single chunk is still in registers (read before the barrier)
+    for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
+    if (vec && j + 4 <= N) {
+      *reinterpret_cast<f32x4*>(y + j) = o;
+    } else {
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kThreads + tid) * 4, N, r, vec);
-    }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const int j = c0 + (e * kThreads + tid) * 4;
-      f32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
-      if (vec && j + 4 <= N) {
-        *reinterpret_cast<f32x4*>(y + j) = o;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (j + i < N) y[j + i] = o[i];
-      }
+      for (int i = 0; i < 4; ++i)
+        if (j + i < N) y[j + i] = o[i];
     }
   }
 }

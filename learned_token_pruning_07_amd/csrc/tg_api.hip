@@ -51,6 +51,10 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     if (B <= 0 || N <= 0) return 0;
     return tg::seq_rmsnorm_workspace(B, N);  // fp64 partial sums, rows longer than 32768 only
   }
+  if (op == TG_OP_GATE_SELECT) {
+    if (B <= 0 || N <= 0) return 0;
+    return tg::gate_select_workspace(B, N);  // rows longer than 32768 only
+  }
   if (op == TG_OP_GATED_ATTENTION) {
     if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return 0;
     // d = Hkv * d_h, h = Hq: an fp16 V^T copy (B * Hkv * d_h * round_up(M, 64)
@@ -150,6 +154,33 @@ int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* ke
   return hip_status(tg::launch_compact(resid, row_bytes, B, N, keep, score, M, kept_idx, resid_out, score_out,
                                        reinterpret_cast<hipStream_t>(stream)),
                     "tg_compact");
+}
+
+int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, int K, const void* resid, int dt,
+                   int d, float* score, uint8_t* keep, int32_t* kept_idx, void* resid_out, float* score_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_gate_select: unknown dtype %d", dt);
+  if (B <= 0 || N <= 0 || d <= 0) return fail(TG_EINVAL, "tg_gate_select: B, N, d must be > 0");
+  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_gate_select: r=%d outside [0, N=%d]", r, N);
+  if (K < 0) return fail(TG_EINVAL, "tg_gate_select: K=%d must be >= 0", K);
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "tg_gate_select: eps_seq must be >= 0");
+  const int M = r + (K < N - r ? K : N - r);
+  if (!score_raw || !score || !keep || !resid || (M > 0 && (!kept_idx || !resid_out || !score_out)))
+    return fail(TG_EINVAL, "tg_gate_select: null pointer argument");
+  const size_t row_bytes = (size_t)d * dt_size(dt);
+  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_select: row bytes must be a multiple of 16");
+  if (!aligned4(score_raw) || !aligned4(score) || !aligned16(resid) ||
+      (M > 0 && (!aligned16(resid_out) || !aligned4(kept_idx) || !aligned4(score_out))))
+    return fail(TG_EINVAL, "tg_gate_select: misaligned pointer");
+  const size_t need = tg::gate_select_workspace(B, N);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(TG_EINVAL, "tg_gate_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gate_select: misaligned workspace");
+  }
+  return hip_status(tg::launch_gate_select(score_raw, B, N, r, eps_seq, K, resid, row_bytes, score, keep, kept_idx,
+                                           resid_out, score_out, ws, reinterpret_cast<hipStream_t>(stream)),
+                    "tg_gate_select");
 }
 
 int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,

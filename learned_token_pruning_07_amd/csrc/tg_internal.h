@@ -33,6 +33,17 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
                           const float* score, int M, int32_t* kept_idx, void* resid_out,
                           float* score_out, hipStream_t s);
 
+// resid_out[m] = resid[kept_idx[m]] for m < M (the row gather of launch_compact)
+hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
+                                 const int32_t* kept_idx, void* resid_out, hipStream_t s);
+
+// launch_seq_rmsnorm + launch_topk_select + launch_compact in sequence, bit
+// for bit (M = r + min(K, N - r)); two launches for rows of up to 32768 tokens.
+size_t gate_select_workspace(int B, int N);
+hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, float eps, int K, const void* resid,
+                              size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
+                              void* resid_out, float* score_kept, void* ws, hipStream_t s);
+
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                   int M, int Hq, int Hkv, int dh, const float* key_score,
                                   const int32_t* pos, const float* gain, const float* temp,

@@ -20,28 +20,23 @@
 // every workgroup re-derives the previous digits from the previous
 // histogram), and the final pass.
 // Integer counting only: the mask is exact and deterministic.
+#include "select_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
 namespace tg {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kLdsKeys = 32768;
-__device__ __forceinline__ int key_slot(int j) { return j + (j >> 4); }  // padded LDS position of key j
+using sel::key_slot;
+using sel::order_key;
+constexpr int kThreads = sel::kRowThreads;
+constexpr int kLdsKeys = sel::kLdsKeys;
 constexpr int kItems = 16;  // consecutive keys per thread in the final pass
-constexpr int kBatch = 16;  // loads in flight per thread when the keys are re-read from global memory
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
-  if (u == 0x80000000u) u = 0u;                      // -0.0 -> +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
+// Spans of up to kLdsKeys prunable tokens (and the trivial budgets of any span).
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ score, int N, int r,
                                                                int K, uint8_t* __restrict__ keep) {
-  __shared__ uint32_t s_keys[kLdsKeys + kLdsKeys / 16];
+  __shared__ uint32_t s_keys[sel::kLdsKeyWords];
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_wave[16];
   __shared__ uint32_t s_sel[3];
@@ -60,12 +55,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     return;
   }
 
-  const bool cached = P <= kLdsKeys;
   for (int i = tid; i < 2048; i += kThreads) s_hist[i] = 0;
   __syncthreads();
-  if (cached) {
+  {
     // all loads of a thread are issued before any is used (latency-bound);
-    // the first pass's histogram (digit [31:21]) is counted on the way in
+    // the first digit's histogram is counted on the way in
     constexpr int kLoad = kLdsKeys / kThreads;
     float f[kLoad];
 #pragma unroll
@@ -83,83 +77,22 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       }
     }
   }
+  const sel::Threshold th = sel::radix_select_lds(s_keys, P, (uint32_t)Kp, s_hist, s_wave, s_sel);
+  const uint32_t T = th.T, k_eq = th.k_eq;
 
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)Kp;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    if (pass > 0 || !cached) {  // (the cached first pass was counted during the load)
-      if (pass > 0)
-        for (int i = tid; i < nb; i += kThreads) s_hist[i] = 0;
-      __syncthreads();
-    }
-    if (cached && pass == 0) {
-      // counted during the load
-    } else if (cached) {
-      for (int j = tid; j < P; j += kThreads) {
-        const uint32_t key = s_keys[key_slot(j)];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-    } else {
-      for (int c0 = 0; c0 < P; c0 += kThreads * kBatch) {
-        float f[kBatch];
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-          const int j = c0 + e * kThreads + tid;
-          f[e] = j < P ? sc[j] : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < kBatch; ++e) {
-          const int j = c0 + e * kThreads + tid;
-          const uint32_t key = order_key(f[e]);
-          if (j < P && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-        }
-      }
-    }
-    __syncthreads();
-    // Bins in descending digit order; thread t owns descending bins
-    // [t*per, t*per + per).  Find the bin where the running count from the top
-    // first reaches krem.
-    const int per = nb / kThreads;  // 2 or 1
-    uint32_t local = 0;
-    for (int e = 0; e < per; ++e) local += s_hist[nb - 1 - (tid * per + e)];
-    uint32_t tot;
-    uint32_t cum = block_excl_scan_u32(local, s_wave, tot);
-    for (int e = 0; e < per; ++e) {
-      const int digit = nb - 1 - (tid * per + e);
-      const uint32_t c = s_hist[digit];
-      if (cum < krem && cum + c >= krem) {
-        s_sel[0] = (uint32_t)digit;
-        s_sel[1] = krem - cum;
-        s_sel[2] = c;  // keys sharing the selected prefix (after the last pass: keys equal to T)
-      }
-      cum += c;
-    }
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    krem = s_sel[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;  // exact key of the K'-th largest score
-  const uint32_t k_eq = krem;  // how many keys equal to T are kept
-  const uint32_t n_eq_all = s_sel[2];  // how many keys equal T
-
-  if (k_eq == n_eq_all) {
+  static_assert(kItems == 16, "one 16-byte store per thread");
+  const bool vec_store = ((reinterpret_cast<uintptr_t>(kp + r)) & 15u) == 0;
+  if (k_eq == th.n_eq) {
     // Every key equal to T is kept (always so for distinct scores): keep is
     // key >= T, with no index-order ranking.
-    static_assert(kItems == 16, "one 16-byte store per thread");
-    const bool vec = ((reinterpret_cast<uintptr_t>(kp + r)) & 15u) == 0;
     for (int j0 = tid * kItems; j0 < P; j0 += kThreads * kItems) {
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < kItems; ++e) {
         const int j = j0 + e;
-        const uint32_t key = j < P ? (cached ? s_keys[key_slot(j)] : order_key(sc[j])) : 0u;
-        packed[e >> 2] |= (j < P && key >= T ? 1u : 0u) << (8 * (e & 3));
+        packed[e >> 2] |= (j < P && s_keys[key_slot(j)] >= T ? 1u : 0u) << (8 * (e & 3));
       }
-      if (vec && j0 + kItems <= P) {
+      if (vec_store && j0 + kItems <= P) {
         store16(kp + r + j0, u32x4{packed[0], packed[1], packed[2], packed[3]});
       } else {
 #pragma unroll
@@ -172,8 +105,6 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 
   // Final pass in index order.  Each thread decides kItems consecutive
   // tokens and writes them as one 16-byte store when the row allows it.
-  static_assert(kItems == 16, "one 16-byte store per thread");
-  const bool vec_store = ((reinterpret_cast<uintptr_t>(kp + r)) & 15u) == 0;
   uint32_t base = 0;  // number of keys == T before the current chunk
   for (int c0 = 0; c0 < P; c0 += kThreads * kItems) {
     uint32_t keys[kItems];
@@ -181,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
       const int j = c0 + tid * kItems + e;
-      keys[e] = j < P ? (cached ? s_keys[key_slot(j)] : order_key(sc[j])) : 0u;
+      keys[e] = j < P ? s_keys[key_slot(j)] : 0u;
       n_eq += (j < P && keys[e] == T) ? 1u : 0u;
     }
     uint32_t tot;

@@ -52,6 +52,9 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_SEQ_RMSNORM, 1, 32769, 0, 0, 0) == 5 * 8
     assert lib.tg_workspace_size(tgb.TG_OP_TOPK_SELECT, 2, 131072, 0, 0, 0) == 2 * (2048 + 2048 + 1024 + 4) * 4
     assert lib.tg_workspace_size(tgb.TG_OP_COMPACT, 1, 131072, 2048, 0, 0) == 0
+    # fused selection: none up to 32768 tokens, else the larger of the two it runs in sequence
+    assert lib.tg_workspace_size(tgb.TG_OP_GATE_SELECT, 1, 32768, 2048, 0, 0) == 0
+    assert lib.tg_workspace_size(tgb.TG_OP_GATE_SELECT, 2, 131072, 2048, 0, 0) == 2 * (2048 + 2048 + 1024 + 4) * 4
     # attention: fp16 V^T copy and fp32 per-head key-score terms, kept length padded to 64 keys
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == 3392 * (8 * 128 * 2 + 16 * 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 0) == 2 * 64 * (2 * 64 * 2 + 4 * 4)
@@ -118,6 +121,28 @@ def test_compact_validation(lib):
     assert call(ki=NULL) == tgb.TG_EINVAL
     assert call(d=4) == tgb.TG_EUNSUPPORTED      # 8-byte rows
     assert call(ro=FAKE_ODD) == tgb.TG_EINVAL
+
+
+def test_gate_select_validation(lib):
+    def call(**kw):
+        a = dict(raw=FAKE, B=1, N=100, r=4, eps=1e-6, K=10, resid=FAKE, dt=tgb.TG_BF16, d=64, score=FAKE, keep=FAKE,
+                 ki=FAKE, ro=FAKE, so=FAKE, ws=NULL, ws_bytes=0)
+        a.update(kw)
+        return lib.tg_gate_select(a["raw"], a["B"], a["N"], a["r"], a["eps"], a["K"], a["resid"], a["dt"], a["d"],
+                                  a["score"], a["keep"], a["ki"], a["ro"], a["so"], a["ws"], a["ws_bytes"], None)
+
+    assert call(raw=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert call(K=-1) == tgb.TG_EINVAL and "K=-1" in _err(lib)
+    assert call(r=101) == tgb.TG_EINVAL and "outside" in _err(lib)
+    assert call(dt=3) == tgb.TG_EINVAL
+    assert call(d=4) == tgb.TG_EUNSUPPORTED      # 8-byte rows
+    assert call(ro=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+    assert call(eps=-1.0) == tgb.TG_EINVAL
+    assert call(ki=NULL) == tgb.TG_EINVAL
+    # long rows need the workspace of the calls they run
+    assert call(N=40000) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(N=40000, ws=FAKE, ws_bytes=100) == tgb.TG_EINVAL
+    assert call(N=40000, ws=FAKE_ODD, ws_bytes=1 << 20) == tgb.TG_EINVAL
 
 
 def test_attention_validation(lib):

@@ -156,6 +156,59 @@ def test_compact_bit_exact(dtype, B, N, d, r, K):
     np.testing.assert_array_equal(score_out.cpu().numpy().view(np.uint32), bs.view(np.uint32))
 
 
+# ------------------------------------------------ fused gate selection --
+@pytest.mark.parametrize("kind,dtype,B,N,r,K,d,inplace", [
+    ("normal", "bf16", 2, 5000, 17, 500, 64, False),
+    ("coarse", "bf16", 1, 16384, 64, 1638, 2048, False),   # the 16k gate's shape, many ties
+    ("coarse", "f32", 2, 3000, 5, 1234, 256, True),         # ties straddling the budget, in place
+    ("const", "f32", 1, 1000, 0, 499, 8, False),            # every key equal: index order decides
+    ("normal", "bf16", 1, 32768, 64, 3277, 64, False),      # the largest single-workgroup row
+    ("normal", "bf16", 1, 40000, 5, 4000, 64, False),       # longer rows: the separate kernels
+    ("normal", "bf16", 1, 1000, 10, 0, 64, False),          # K = 0: only the prefix
+    ("normal", "f32", 1, 1000, 10, 5000, 8, False),         # K >= N - r: everything
+    ("normal", "bf16", 1, 64, 64, 3, 64, False),            # no prunable token
+    ("normal", "bf16", 2, 33, 0, 3, 64, False),
+])
+def test_gate_select_matches_separate_calls(kind, dtype, B, N, r, K, d, inplace):
+    say(f"gate_select {kind} {dtype} B={B} N={N} r={r} K={K} d={d}")
+    raw = _scores(kind, B, N, N + K + d) * 3.0
+    raw[:, :r] = 0.0
+    c = wl.gate_case(N=N, r=r, d=d, h=8, K=K, dtype=dtype, seed=N + d, B=B)
+    put = dev_bits if dtype == "bf16" else dev
+    resid = put(c.resid)
+    M = tg.kept_count(N, r, K)
+    # separate calls
+    s_ref = tg.tg_seq_rmsnorm(dev(raw), r, 1e-6)
+    keep_ref = tg.tg_topk_select(s_ref, r, K)
+    ki_ref, ro_ref, so_ref = tg.tg_compact(resid, keep_ref, s_ref, M)
+    # fused call, outputs poison-filled
+    x = dev(raw)
+    score = x if inplace else poison_f32((B, N))
+    keep = torch.full((B, N), 7, dtype=torch.uint8, device=DEV)
+    kept_idx = torch.full((B, M), -7, dtype=torch.int32, device=DEV)
+    resid_out = torch.full((B, M, d), float("nan"), dtype=resid.dtype, device=DEV)
+    score_out = poison_f32((B, M))
+    tg.tg_gate_select(x, resid, r, K, 1e-6, score=score, keep=keep, kept_idx=kept_idx, resid_out=resid_out,
+                      score_out=score_out)
+    bits = lambda t: t.cpu().numpy().view(np.uint8)
+    np.testing.assert_array_equal(bits(score), bits(s_ref))
+    np.testing.assert_array_equal(keep.cpu().numpy(), keep_ref.cpu().numpy())
+    np.testing.assert_array_equal(kept_idx.cpu().numpy(), ki_ref.cpu().numpy())
+    np.testing.assert_array_equal(bits(resid_out.view(torch.uint8)), bits(ro_ref.view(torch.uint8)))
+    np.testing.assert_array_equal(bits(score_out), bits(so_ref))
+    # and against the oracle: the norm within the fp32 bar, the selection and
+    # compaction exactly on the scores the GPU produced
+    got = score.cpu().numpy()
+    assert_close(got, oracle.seq_rmsnorm(raw, r, 1e-6), TOL_F32, "gate_select score")
+    k_or = oracle.topk_select(got, r, K)
+    np.testing.assert_array_equal(keep.cpu().numpy(), k_or)
+    ki, rs, bs = oracle.compact(c.resid, k_or, got)
+    np.testing.assert_array_equal(kept_idx.cpu().numpy(), ki)
+    got_rows = host_bits(resid_out) if dtype == "bf16" else resid_out.cpu().numpy()
+    np.testing.assert_array_equal(got_rows.view(np.uint8), rs.view(np.uint8))
+    np.testing.assert_array_equal(score_out.cpu().numpy().view(np.uint32), bs.view(np.uint32))
+
+
 # --------------------------------------------------------------- attention --
 def _attn_run(c, b, want_lse=True):
     q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
