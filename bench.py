@@ -12,7 +12,10 @@ One step = one pass of the whole path over one input:
     -> 24 x tg_gated_attention
 (--separate-gate runs tg_seq_rmsnorm, tg_topk_select and tg_compact instead
 of tg_gate_select; the results are the same bit for bit)
-with every input already resident in HBM.  The residual is rotated over
+with every input already resident in HBM.  Calls are launched directly on
+one stream with no host synchronisation; --graph captures each phase of a
+step (each gate call, the run of attention calls) once as a HIP graph and
+replays it instead.  The residual is rotated over
 several copies (> the 256 MiB Infinity Cache) so the HBM-bound kernels read
 HBM.  The per-layer Q/K/V are the upper layers' projections of the compacted
 stream (seeded random weights); they are produced before the timed region by
@@ -141,6 +144,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="residual copies rotated per step (0: enough for 512 MiB)")
     ap.add_argument("--separate-gate", action="store_true",
                     help="run sequence norm, top-K and compaction as three calls instead of tg_gate_select")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each phase of a step as a HIP graph once and replay it (slower on this ROCm: "
+                         "a replay costs several microseconds more than direct launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the reference for "
@@ -213,21 +219,23 @@ def main():
     sel_ws = tg.gate_select_workspace(1, N, dev)   # None up to N = 32768
     sel_phases = ("seq_rmsnorm", "topk_select", "compact") if args.separate_gate else ("gate_select",)
 
-    def gate(x, ev=None):
-        run = (lambda name, fn: ev.phase(name, fn)) if ev else (lambda name, fn: fn())
-        run("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
-                                                   ws=gate_ws))
+    def gate_calls(x):
+        """The gate's library calls on residual x, as (phase name, call)."""
+        calls = [("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
+                                                          ws=gate_ws))]
         if args.separate_gate:
-            run("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws))
-            run("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws))
-            run("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
-                                                  score_out=b_S))
+            calls += [("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws)),
+                      ("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws)),
+                      ("compact", lambda: tg.tg_compact(x, keep, score, M, kept_idx=kept_idx, resid_out=resid_S,
+                                                         score_out=b_S))]
         else:
-            run("gate_select", lambda: tg.tg_gate_select(score, x, r, K, c.eps_seq, score=score, keep=keep,
-                                                          kept_idx=kept_idx, resid_out=resid_S, score_out=b_S,
-                                                          ws=sel_ws))
+            calls += [("gate_select", lambda: tg.tg_gate_select(score, x, r, K, c.eps_seq, score=score, keep=keep,
+                                                                 kept_idx=kept_idx, resid_out=resid_S,
+                                                                 score_out=b_S, ws=sel_ws))]
+        return calls
 
-    gate(resid0)
+    for _, fn in gate_calls(resid0):
+        fn()
     torch.cuda.synchronize()
 
     # upper-layer Q/K/V (glue, outside the library and outside the timed step)
@@ -254,12 +262,40 @@ def main():
             q, k, v = qkv[l]
             tg.tg_gated_attention(q, k, v, b_S, kept_idx, p.gain, p.temp, out=attn_out, ws=attn_ws)
 
+    def step_phases(i):
+        """(phase name, call, library calls in it) of step i; the residual copy rotates."""
+        ph = [(name, fn, 1) for name, fn in gate_calls(resids[i % ncopy])]
+        if layers:
+            ph.append(("gated_attention", attention_layers, len(layers)))
+        return ph
+
+    graphs = {}
+    if args.graph:
+        # each phase of a step is captured once as a HIP graph (per residual
+        # copy for the gate phases) and replayed; events between the replays
+        # time the phases.  The calls allocate nothing, so capture is legal.
+        for i in range(ncopy):  # eager warm-up of every call shape first
+            for _, fn, _ in step_phases(i):
+                fn()
+        torch.cuda.synchronize()
+        for i in range(ncopy):
+            for name, fn, _ in step_phases(i):
+                key = (i if name != "gated_attention" else 0, name)
+                if key not in graphs:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        fn()
+                    graphs[key] = g
+        torch.cuda.synchronize()
+
     def step(i, ev=None):
-        gate(resids[i % ncopy], ev)
-        if ev and layers:
-            ev.phase("gated_attention", attention_layers, calls=len(layers))
-        else:
-            attention_layers()
+        for name, fn, calls in step_phases(i):
+            if graphs:
+                fn = graphs[(i % ncopy if name != "gated_attention" else 0, name)].replay
+            if ev:
+                ev.phase(name, fn, calls=calls)
+            else:
+                fn()
 
     for i in range(args.warmup):
         step(i)
@@ -276,7 +312,8 @@ def main():
     t_end = ev.last
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies)")
+    log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies, "
+        f"{'HIP graph replays' if args.graph else 'direct launches'})")
 
     # ---------------- figures ----------------
     e = 2
@@ -334,6 +371,7 @@ def main():
                    "residual_copies": ncopy},
         "roofline": roofline,
         "kernels": kernels,
+        "launch": "hip_graph" if args.graph else "direct",
         "gate_op": {"calls": ["tg_gate_score"] + ["tg_" + n for n in sel_phases],
                     "avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
                     "achieved_GBs": round(gate_bytes / (gate_us * 1e-6) / 1e9, 1),
