@@ -570,9 +570,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       cm[e] = mc;
       sb[e] += mc;
     }
-    // (the loads go out between the two steps: issued at the top of the
-    // iteration, their LDS writes collide with every wave's first fragment
-    // reads after the barrier)
+    // The two groups issue their loads at different points: group 1 at the
+    // top of the iteration, group 0 between the two steps.  The two waves
+    // sharing a SIMD (one of each group) then leave the barrier out of
+    // phase -- one issues loads while the other starts its matrix work --
+    // instead of contending for the same slots in lockstep, and the wave
+    // that the SIMD favours (group 0) takes the later load slot.
     auto iter = [&](int it) __attribute__((always_inline)) {
       // ring slots of this iteration: K of tile it + 1, V^T of tile it
       int kb[4], vb[4];
@@ -582,8 +585,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
         kb[j] = k_lane[j] + koff;
         vb[j] = v_lane[j] + voff;
       }
+      if (grp == 1) stage(it);
       fast_step(2 * it + 1, sb, sa, pb, pa, kb, vb, IntConst<0>{});
-      stage(it);
+      if (grp == 0) stage(it);
       fast_step(2 * it + 2, sa, sb, pa, pb, kb, vb, IntConst<1>{});
       wait_vmem();
       __syncthreads();
