@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
                                                                     const float* __restrict__ score, int N,
                                                                     int M, int32_t* __restrict__ kept_idx,
                                                                     float* __restrict__ score_out) {
-  __shared__ uint32_t s_wave[kScanThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wave[kScanThreads / 64];
   const int b = blockIdx.y;
   const uint8_t* kp = keep + (size_t)b * N;
   const float* sc = score + (size_t)b * N;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
   const uint32_t base = block_sum_u32(cnt, s_wave);
 
   uint32_t tot;
-  uint32_t dst = base + block_excl_scan_u32(__builtin_popcount(flags), s_wave, tot);
+  uint32_t dst = base + block_excl_scan_u32<kScanThreads / 64>(__builtin_popcount(flags), s_wave, tot);
 #pragma unroll
   for (int e = 0; e < kScanItems; ++e) {
     if (flags & (1u << e)) {

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
                                                                float* __restrict__ score_kept) {
   __shared__ uint32_t s_keys[sel::kLdsKeyWords];
   __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_wave[16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wave[16];
   __shared__ uint32_t s_sel[3];
   __shared__ double s_part[kThreads / 64];
   __shared__ double s_scale;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
       n_eq += (j < P && keys[e] == T) ? 1u : 0u;
     }
     uint32_t eq_tot = 0, rank = 0;
-    if (!all_ties) rank = eq_base + block_excl_scan_u32(n_eq, s_wave, eq_tot);  // (block-uniform branch)
+    if (!all_ties) rank = eq_base + block_excl_scan_u32<kThreads / 64>(n_eq, s_wave, eq_tot);  // (block-uniform branch)
     uint32_t flags = 0;  // bit e: token j0 + e is kept
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
       flags |= kept ? (1u << e) : 0u;
     }
     uint32_t tot;
-    uint32_t dst = out_base + block_excl_scan_u32(__builtin_popcount(flags), s_wave, tot);
+    uint32_t dst = out_base + block_excl_scan_u32<kThreads / 64>(__builtin_popcount(flags), s_wave, tot);
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
@@ -148,7 +148,10 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
       if (flags & (1u << e)) {
         if ((int)dst < M) {  // exactly M tokens are kept; never write past the row
           ki[dst] = r + j0 + e;
-          sk[dst] = y[r + j0 + e];
+          // the key holds the score exactly, except that -0.0 and +0.0 share
+          // a key and every NaN maps to key 0: only those re-read the score
+          const float from_key = sel::key_score(keys[e]);
+          sk[dst] = (keys[e] == 0u || from_key == 0.0f) ? y[r + j0 + e] : from_key;
         }
         ++dst;
       }

@@ -70,6 +70,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score of a key (the inverse of order_key for every non-NaN score other
+// than -0.0, which comes back as +0.0).
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // Result of the radix select over one row's prunable keys.
 struct Threshold {
   uint32_t T;     // exact key of the K'-th largest
@@ -105,7 +111,7 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
     uint32_t local = 0;
     for (int e = 0; e < per; ++e) local += s_hist[nb - 1 - (tid * per + e)];
     uint32_t tot;
-    uint32_t cum = block_excl_scan_u32(local, s_wave, tot);
+    uint32_t cum = block_excl_scan_u32<kRowThreads / 64>(local, s_wave, tot);
     for (int e = 0; e < per; ++e) {
       const int digit = nb - 1 - (tid * per + e);
       const uint32_t c = s_hist[digit];

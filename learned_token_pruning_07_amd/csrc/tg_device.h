@@ -70,33 +70,43 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves: a
+// Hillis-Steele scan inside each 16-lane row (shifts 1, 2, 4, 8; lanes
+// shifted in from outside the row read 0), then the last lane of row 0 is
+// added to row 1 and of row 2 to row 3 (row_bcast:15), and the last lane of
+// row 1 to rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false);
   return x;
 }
 
-// Exclusive prefix sum over a whole block (blockDim.x a multiple of 64, at most
-// 1024 threads).  `s_wave` holds >= 16 words of LDS.  Returns the exclusive
-// prefix of `v`; `total` receives the block total.  Contains barriers: every
-// thread of the block must call it.
+// Exclusive prefix sum over a whole block of NW waves (blockDim.x == 64 NW,
+// NW a multiple of 4, at most 16).  `s_wave` holds NW words of LDS, 16-byte
+// aligned.  Returns the exclusive prefix of `v`; `total` receives the block
+// total.  Contains barriers: every thread of the block must call it.
+template <int NW>
 __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s_wave, uint32_t& total) {
+  static_assert(NW % 4 == 0 && NW <= 16, "wave count");
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
-  uint32_t incl = wave_incl_scan_u32(v);
+  const uint32_t incl = wave_incl_scan_u32(v);
   if (lane == 63) s_wave[wid] = incl;
   __syncthreads();
   uint32_t before = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    uint32_t t = s_wave[w];
-    before += (w < wid) ? t : 0u;
-    tot += t;
+#pragma unroll
+  for (int q = 0; q < NW / 4; ++q) {
+    const u32x4 t = reinterpret_cast<const u32x4*>(s_wave)[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      before += (4 * q + i < wid) ? t[i] : 0u;
+      tot += t[i];
+    }
   }
   __syncthreads();
   total = tot;

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
                                                                int K, uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_keys[sel::kLdsKeyWords];
   __shared__ uint32_t s_hist[2048];
-  __shared__ uint32_t s_wave[16];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wave[16];
   __shared__ uint32_t s_sel[3];
 
   const int tid = threadIdx.x;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       n_eq += (j < P && keys[e] == T) ? 1u : 0u;
     }
     uint32_t tot;
-    uint32_t rank = base + block_excl_scan_u32(n_eq, s_wave, tot);
+    uint32_t rank = base + block_excl_scan_u32<kThreads / 64>(n_eq, s_wave, tot);
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
@@ -176,7 +176,7 @@ __device__ void select_digit(const uint32_t* hist, int nb, uint32_t krem, uint32
   uint32_t local = 0;
   for (int e = 0; e < per; ++e) local += hist[nb - 1 - (tid * per + e)];
   uint32_t tot;
-  uint32_t cum = block_excl_scan_u32(local, s_wave, tot);
+  uint32_t cum = block_excl_scan_u32<kMThreads / 64>(local, s_wave, tot);
   for (int e = 0; e < per; ++e) {
     const int digit = nb - 1 - (tid * per + e);
     const uint32_t c = hist[digit];
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __res
                                                               uint32_t* __restrict__ ws) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_prev[2048];
-  __shared__ uint32_t s_wave[kMThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wave[kMThreads / 64];
   __shared__ uint32_t s_sel[3];
   const int tid = threadIdx.x, b = blockIdx.y, c0 = blockIdx.x * kMChunk;
   const float* sc = score + (size_t)b * N + r;
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __re
                                                                const uint32_t* __restrict__ ws,
                                                                uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_prev[1024];
-  __shared__ uint32_t s_wave[kMThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t s_wave[kMThreads / 64];
   __shared__ uint32_t s_sel[3];
   const int tid = threadIdx.x, b = blockIdx.y, c0 = blockIdx.x * kMChunk;
   const float* sc = score + (size_t)b * N + r;
@@ -276,12 +276,12 @@ __global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __re
     uint32_t before = 0;
     for (int j = tid; j < c0; j += kMThreads) before += order_key(sc[j]) == T ? 1u : 0u;
     uint32_t tot;
-    before = block_excl_scan_u32(before, s_wave, tot);
+    before = block_excl_scan_u32<kMThreads / 64>(before, s_wave, tot);
     const uint32_t base = tot;
     uint32_t mine = 0;
 #pragma unroll
     for (int e = 0; e < kMItems; ++e) mine += (j0 + e < P && key[e] == T) ? 1u : 0u;
-    rank = base + block_excl_scan_u32(mine, s_wave, tot);
+    rank = base + block_excl_scan_u32<kMThreads / 64>(mine, s_wave, tot);
   }
   uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
