@@ -143,18 +143,21 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
     uint32_t dst = out_base + block_excl_scan_u32<kThreads / 64>(__builtin_popcount(flags), s_wave, tot);
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      packed[e >> 2] |= ((flags >> e) & 1u) << (8 * (e & 3));
-      if (flags & (1u << e)) {
-        if ((int)dst < M) {  // exactly M tokens are kept; never write past the row
-          ki[dst] = r + j0 + e;
-          // the key holds the score exactly, except that -0.0 and +0.0 share
-          // a key and every NaN maps to key 0: only those re-read the score
-          const float from_key = sel::key_score(keys[e]);
-          sk[dst] = (keys[e] == 0u || from_key == 0.0f) ? y[r + j0 + e] : from_key;
-        }
-        ++dst;
+    for (int e = 0; e < kItems; ++e) packed[e >> 2] |= ((flags >> e) & 1u) << (8 * (e & 3));
+    // one pair of stores per kept token of this thread, ranks dst, dst + 1, ...
+    // (a loop over the set bits: the wave issues as many store rounds as its
+    // busiest lane has kept tokens, not one per item)
+    for (uint32_t f = flags; f != 0u; f &= f - 1u) {
+      const int e = __builtin_ctz(f);
+      if ((int)dst < M) {  // exactly M tokens are kept; never write past the row
+        const uint32_t key = s_keys[sel::key_slot(j0 + e)];
+        ki[dst] = r + j0 + e;
+        // the key holds the score exactly, except that -0.0 and +0.0 share a
+        // key and every NaN maps to key 0: only those re-read the score
+        const float from_key = sel::key_score(key);
+        sk[dst] = (key == 0u || from_key == 0.0f) ? y[r + j0 + e] : from_key;
       }
+      ++dst;
     }
     if (vec_store && j0 + kItems <= P) {
       store16(kp + r + j0, u32x4{packed[0], packed[1], packed[2], packed[3]});
