@@ -98,9 +98,20 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
     if (pass > 0) {
       for (int i = tid; i < nb; i += kRowThreads) s_hist[i] = 0;
       __syncthreads();
-      for (int j = tid; j < P; j += kRowThreads) {
-        const uint32_t key = s_keys[key_slot(j)];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      // batches of kBatch keys per thread: every LDS read of a batch is issued
+      // before any is tested
+      constexpr int kBatch = 8;
+      for (int j0 = tid; j0 < P; j0 += kBatch * kRowThreads) {
+        uint32_t key[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int j = j0 + u * kRowThreads;
+          key[u] = j < P ? s_keys[key_slot(j)] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (j0 + u * kRowThreads < P && (key[u] & pmask) == prefix)
+            atomicAdd(&s_hist[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
       }
     }
     __syncthreads();
