@@ -127,22 +127,30 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
   const int nch = NCH_FIXED > 0 ? NCH_FIXED : d / kKC;
   u32x4 ra[kDepth][AL];        // residual ring: chunk c lives in slot c % kDepth
   u32x4 wb[kWDepth][2][CT];    // W1w fragment ring: chunk c lives in slot c % kWDepth
+  // Workgroups start their pass over d at different chunks (logical chunk c
+  // is chunk (c + rot) mod nch of the row), so the workgroups of an XCD, which
+  // all stream the same W1w fragments, do not ask for the same L2 lines at the
+  // same time.  Only the fp32 summation order of a tile's rows depends on it.
+  const int rot = (int)(blockIdx.x % (unsigned)nch);
+  auto phys = [&](int c) { int p = c + rot; p = p >= nch ? p - nch : p; return p; };
   auto load_a = [&](int c, u32x4 (&dst)[AL]) {
+    const int pc = phys(c);
 #pragma unroll
     for (int e = 0; e < AL; ++e)
-      dst[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[e], c * kKC * 2, 0));
+      dst[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[e], pc * kKC * 2, 0));
   };
   auto store_a = [&](int buf, const u32x4 (&src)[AL]) {
 #pragma unroll
     for (int e = 0; e < AL; ++e) store16(&sA[buf][a_lds[e]], src[e]);
   };
   auto load_b = [&](int c, u32x4 (&dst)[2][CT]) {
+    const int pc = phys(c);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
         dst[ks][ct] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ct], (c * 2 + ks) * kStepBytes, 0));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, w_off[ct], (pc * 2 + ks) * kStepBytes, 0));
   };
 
   f32x4 acc[RT][CT];
