@@ -31,6 +31,9 @@ def _oracle_scores(c, resid=None):
     (128, 300, 0, 192, 1, True),
     (64, 130, 129, 64, 1, False),
     (256, 64, 64, 256, 1, False),
+    # enough rows for the 128-token tiles (2 x 120 workgroups)
+    (256, 15400, 40, 256, 2, False),
+    (128, 15400, 40, 192, 2, True),
 ])
 def test_gate_score_bf16(h, N, r, d, B, extras):
     say(f"gate_score bf16 h={h} N={N} r={r} d={d} B={B}")
