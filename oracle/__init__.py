@@ -8,6 +8,10 @@ from .tokengate_ref import (  # noqa: F401
     gate_score,
     gated_attention,
     gated_attention_gate_form,
+    gated_attention_rope,
+    bf16_round,
+    rope,
+    rope_inv_freq,
     score_rows,
     seq_rmsnorm,
     temperature_ratio,

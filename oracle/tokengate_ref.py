@@ -271,3 +271,60 @@ def gated_attention_gate_form(q, k, v, b_S, pos, gain, temp, sm_scale: float, ro
                 wgt = gate[:i + 1] * np.exp(s - s.max())   # Eq. 5
                 O[bi, n, h, :] = (wgt @ V[bi, :i + 1, kv, :]) / wgt.sum()
     return O
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding on the original positions.  The paper keeps every
+# kept token's original position for the position encoding of the layers
+# above L (Appendix C.4) but does not define the encoding itself.
+#
+# Reading: the rotate-half rotary embedding of the model family the pages
+# evaluate.  For a head vector x of even width d at position p, each pair
+# (x_i, x_{i+d/2}), i < d/2, is rotated by the angle p * base^(-2i/d).  The
+# rotated q and k enter the attention products as bf16 (round to nearest
+# even), as the model's own q/k tensors are bf16.
+# --------------------------------------------------------------------------
+def rope_inv_freq(d: int, base: float) -> np.ndarray:
+    """base^(-2i/d), i < d/2, in float64."""
+    return np.power(float(base), -2.0 * np.arange(d // 2, dtype=np.float64) / d)
+
+
+def rope(x, pos, base: float) -> np.ndarray:
+    """Rotated copy (float64) of x [B, M, H, d] at positions pos [B, M]."""
+    X = widen(x)
+    d = X.shape[-1]
+    h = d // 2
+    ang = np.asarray(pos, np.float64)[:, :, None] * rope_inv_freq(d, base)[None, None, :]
+    c = np.cos(ang)[:, :, None, :]
+    s = np.sin(ang)[:, :, None, :]
+    x1, x2 = X[..., :h], X[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def bf16_round(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float64 values, rounded to nearest even
+    directly from float64 (no intermediate fp32 rounding).  Zeros and values
+    in bf16's normal range only."""
+    a = np.ascontiguousarray(np.asarray(x, np.float64))
+    u = a.view(np.uint64)
+    mag = u & np.uint64(0x7FFFFFFFFFFFFFFF)
+    exp = (mag >> np.uint64(52)).astype(np.int64) - 1023
+    nz = mag != 0
+    if np.any(nz & ((exp < -126) | (exp > 127))):
+        raise ValueError("bf16_round: value outside bf16's normal range")
+    top = u >> np.uint64(45)                        # sign, exponent, 7 mantissa bits
+    rem = u & np.uint64((1 << 45) - 1)
+    half = np.uint64(1 << 44)
+    up = (rem > half) | ((rem == half) & ((top & np.uint64(1)) == np.uint64(1)))
+    top = top + up.astype(np.uint64)
+    r64 = (top << np.uint64(45)).view(np.float64)   # exactly representable in bf16
+    bits = (r64.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(nz, bits, (u >> np.uint64(48)).astype(np.uint16))  # keep the sign of zeros
+
+
+def gated_attention_rope(q, k, v, b_S, pos, gain, temp, sm_scale: float, base: float, rows=None):
+    """Token-gated attention (gated_attention) on the rotary-embedded q and k:
+    q and k rotated at the original positions pos, rounded to bf16, then Eq. 8."""
+    qr = bf16_round(rope(q, pos, base))
+    kr = bf16_round(rope(k, pos, base))
+    return gated_attention(qr, kr, v, b_S, pos, gain, temp, sm_scale, rows=rows)

@@ -142,3 +142,73 @@ def test_sampled_rows_equal_full_rows():
     Os, ls = oracle.gated_attention(c.q, c.k, c.v, c.b_raw, c.pos, c.gain, c.temp, c.sm_scale, rows=rows)
     np.testing.assert_array_equal(Os, O[:, rows])
     np.testing.assert_array_equal(ls, lse[:, :, rows])
+
+
+# ------------------------------------------------------------ rotary (RoPE) --
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(3).standard_normal((1, 5, 2, 8))
+    y = oracle.rope(x.astype(np.float32), np.zeros((1, 5), np.int64), 10000.0)
+    np.testing.assert_array_equal(y, x.astype(np.float32).astype(np.float64))
+
+
+def test_rope_is_complex_rotation():
+    # independent form: pair (x_i, x_{i+d/2}) as the complex number
+    # x_i + 1j x_{i+d/2}, multiplied by exp(1j * p * base^(-2i/d))
+    rng = np.random.default_rng(4)
+    d, base = 16, 500.0
+    x = rng.standard_normal((2, 7, 3, d)).astype(np.float32)
+    pos = rng.integers(0, 100000, (2, 7))
+    y = oracle.rope(x, pos, base)
+    z = x[..., : d // 2].astype(np.float64) + 1j * x[..., d // 2:].astype(np.float64)
+    theta = pos[:, :, None, None].astype(np.float64) * base ** (-np.arange(d // 2) * 2.0 / d)
+    w = z * np.exp(1j * theta)
+    np.testing.assert_allclose(y[..., : d // 2], w.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(y[..., d // 2:], w.imag, rtol=0, atol=1e-12)
+
+
+def test_rope_preserves_pair_norms_and_depends_on_relative_position():
+    rng = np.random.default_rng(5)
+    d, base = 64, 1e6
+    q = rng.standard_normal((1, 1, 1, d))
+    k = rng.standard_normal((1, 1, 1, d))
+    y = oracle.rope(q, np.array([[12345]]), base)
+    h = d // 2
+    np.testing.assert_allclose(y[..., :h] ** 2 + y[..., h:] ** 2, q[..., :h] ** 2 + q[..., h:] ** 2, rtol=1e-12)
+    # q.k after rotation depends only on the position difference
+    dots = []
+    for shift in (0, 1000, 70000):
+        qr = oracle.rope(q, np.array([[300 + shift]]), base)
+        kr = oracle.rope(k, np.array([[17 + shift]]), base)
+        dots.append(float(np.sum(qr * kr)))
+    np.testing.assert_allclose(dots, dots[0], rtol=0, atol=1e-9)
+
+
+def test_bf16_round_matches_torch_on_fp32_values_and_ties():
+    x = np.random.default_rng(6).standard_normal(50000).astype(np.float32)
+    one_half = np.float32(1.5).view(np.uint32)
+    ties = np.array([one_half | 0x8000, (one_half + 0x10000) | 0x8000, 0xBF818000], np.uint32).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 3e38, -1e-30], np.float32)])
+    got = oracle.bf16_round(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    # ties go to the even neighbour
+    assert list(got[-7:-4]) == [0x3FC0, 0x3FC2, 0xBF82]
+
+
+def test_bf16_round_rounds_float64_once():
+    # 1 + 2^-8 + 2^-30 is just above the midpoint between bf16 1.0 and the next
+    # value: direct rounding goes up, rounding through fp32 first (which drops
+    # the 2^-30) lands on the tie and goes to even (down)
+    x = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30])
+    assert oracle.bf16_round(x)[0] == 0x3F81
+    assert torch.tensor(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).item() == 0x3F80
+
+
+def test_rope_attention_at_position_zero_equals_plain():
+    c = wl.attn_case(M=40, Hq=4, Hkv=2, dh=16, seed=8, r_zero=40, gain=1.0, temp=1.0)
+    zeros = np.zeros((1, 40), np.int64)
+    b = np.zeros((1, 40), np.float32)
+    O1, L1 = oracle.gated_attention_rope(c.q, c.k, c.v, b, zeros, c.gain, c.temp, c.sm_scale, 10000.0)
+    O2, L2 = oracle.gated_attention(c.q, c.k, c.v, b, zeros, c.gain, c.temp, c.sm_scale)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
