@@ -52,7 +52,8 @@ typedef enum {
   TG_OP_TOPK_SELECT = 2,
   TG_OP_COMPACT = 3,
   TG_OP_GATED_ATTENTION = 4,
-  TG_OP_GATE_SELECT = 5
+  TG_OP_GATE_SELECT = 5,
+  TG_OP_GATED_ATTENTION_ROPE = 6
 } tg_op;
 
 /*
@@ -212,9 +213,40 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
                        const float* gain, const float* temp, float sm_scale,
                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tg_gated_attention_rope -- tg_gated_attention on rotary-embedded queries and
+ * keys.  The paper keeps every kept token's original position for the
+ * position encoding of the layers above the gate (Appendix C.4); this entry
+ * point applies the rotate-half rotary embedding at those positions (`pos`)
+ * before the attention, so q and k can be passed un-rotated:
+ *     for each head vector x (width d_h) of q and k at kept rank i,
+ *     pair (x_j, x_{j + d_h/2}), j < d_h/2, turns by the angle
+ *     pos[i] * rope_base^(-2 j / d_h):
+ *       x'_j          = x_j cos a - x_{j+d_h/2} sin a
+ *       x'_{j+d_h/2}  = x_{j+d_h/2} cos a + x_j sin a
+ * and the rotated q', k' (rounded to bf16, nearest even) replace q, k in the
+ * definition of tg_gated_attention (pos also keeps its role in the
+ * temperature).  The angle is formed and reduced modulo 2 pi in fp64; its
+ * sine and cosine and the rotation are fp32.
+ *
+ *   arguments as tg_gated_attention, plus rope_base (> 1, e.g. 1e6)
+ *   ws, ws_bytes     workspace of at least tg_workspace_size(
+ *                    TG_OP_GATED_ATTENTION_ROPE, B, M, Hkv * d_h, Hq, d_h) bytes,
+ *                    16-byte aligned (tg_gated_attention's workspace followed
+ *                    by the rotated q and k; contents need no initialisation)
+ */
+int tg_gated_attention_rope(const void* q, const void* k, const void* v,
+                            int B, int M, int Hq, int Hkv, int d_h,
+                            const float* key_score, const int32_t* pos,
+                            const float* gain, const float* temp, float sm_scale,
+                            double rope_base, void* out, float* lse, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
  * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
  * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq).
+ * For TG_OP_GATED_ATTENTION_ROPE pass the same and K = d_h; the size adds
+ * 2 * B * M * (Hq + Hkv) * d_h.
  * TG_OP_SEQ_RMSNORM and TG_OP_TOPK_SELECT depend on B and N only. */
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
 

@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_PKG, "libtokengate.so")
 
 TG_OK, TG_EINVAL, TG_EUNSUPPORTED, TG_EHIP = 0, 1, 2, 3
 TG_F32, TG_BF16 = 0, 1
-TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION, TG_OP_GATE_SELECT = range(6)
+(TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION, TG_OP_GATE_SELECT,
+ TG_OP_GATED_ATTENTION_ROPE) = range(7)
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
-            "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_rope", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_compact.argtypes = [vp, i, i, i, i, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_gate_select.argtypes = [vp, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tg_gated_attention_rope.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, ctypes.c_double, vp, vp,
+                                            vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
@@ -58,7 +61,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_version.argtypes = []
     lib.tg_version.restype = i
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
-                 "tg_gate_select"):
+                 "tg_gate_select", "tg_gated_attention_rope"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -268,14 +271,8 @@ def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | None = None, out=None,
-                       lse=None, want_lse: bool = False, ws=None, stream=None):
-    """Token-gated causal GQA attention.  q ``[B, M, Hq, dh]``, k/v ``[B, M, Hkv, dh]`` bf16.
-
-    Returns ``out`` (and ``lse [B, Hq, M]`` when ``want_lse`` or ``lse`` is given).
-    ``ws`` is a uint8 GPU tensor from :func:`attention_workspace` (allocated
-    here when omitted).
-    """
+def _attention_call(entry, q, k, v, key_score, pos, gain, temp, sm_scale, out, lse, want_lse, ws, stream,
+                    rope_base=None):
     lib = load_library()
     _need(q, "q", torch.bfloat16)
     B, M, Hq, dh = q.shape
@@ -296,12 +293,43 @@ def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | No
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, M))
     if ws is None:
-        ws = attention_workspace(B, M, Hq, Hkv, dh, q.device)
+        ws = (attention_workspace(B, M, Hq, Hkv, dh, q.device) if rope_base is None
+              else attention_rope_workspace(B, M, Hq, Hkv, dh, q.device))
     _need(ws, "ws", torch.uint8)
-    _check(lib.tg_gated_attention(_ptr(q), _ptr(k), _ptr(v), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
-                                  _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
-                                  ws.numel(), _stream(stream)))
+    args = [_ptr(q), _ptr(k), _ptr(v), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos), _ptr(gain), _ptr(temp),
+            float(sm_scale)]
+    if rope_base is not None:
+        args.append(float(rope_base))
+    args += [_ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)]
+    _check(getattr(lib, entry)(*args))
     return (out, lse) if lse is not None else out
+
+
+def tg_gated_attention(q, k, v, key_score, pos, gain, temp, sm_scale: float | None = None, out=None,
+                       lse=None, want_lse: bool = False, ws=None, stream=None):
+    """Token-gated causal GQA attention.  q ``[B, M, Hq, dh]``, k/v ``[B, M, Hkv, dh]`` bf16.
+
+    Returns ``out`` (and ``lse [B, Hq, M]`` when ``want_lse`` or ``lse`` is given).
+    ``ws`` is a uint8 GPU tensor from :func:`attention_workspace` (allocated
+    here when omitted).
+    """
+    return _attention_call("tg_gated_attention", q, k, v, key_score, pos, gain, temp, sm_scale, out, lse,
+                           want_lse, ws, stream)
+
+
+def attention_rope_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for tg_gated_attention_rope at these sizes."""
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION_ROPE, B, M, Hkv * dh, Hq, dh))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def tg_gated_attention_rope(q, k, v, key_score, pos, gain, temp, rope_base: float, sm_scale: float | None = None,
+                            out=None, lse=None, want_lse: bool = False, ws=None, stream=None):
+    """tg_gated_attention on q and k rotated by the rotary embedding at the
+    original positions ``pos`` (base ``rope_base``); q and k are passed
+    un-rotated.  ``ws`` from :func:`attention_rope_workspace`."""
+    return _attention_call("tg_gated_attention_rope", q, k, v, key_score, pos, gain, temp, sm_scale, out, lse,
+                           want_lse, ws, stream, rope_base=rope_base)
 
 
 def tg_workspace_size(op: int, B: int, N: int, d: int, h: int, K: int) -> int:

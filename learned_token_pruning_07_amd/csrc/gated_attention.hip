@@ -93,20 +93,58 @@ __device__ __forceinline__ int vt_slot_key(int s) {
   return (s & ~15) | (kq << 2) | (s & 3);
 }
 
+// Rotary position embedding inputs of the prepass: q, k and the positions,
+// the base, and where the rotated copies go (same layouts as q and k).
+struct RopeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* pos;
+  double base;
+  uint16_t* qr;
+  uint16_t* kr;
+};
+
+// Rotates one head row (x_i, x_{i+DH/2}) pairs i = i0 .. i0 + 7 by the angles
+// whose cosines and sines are c[], s[] (fp32, products fused), rounding the
+// results to bf16 (nearest even).
+template <int DH>
+__device__ __forceinline__ void rope_row8(const uint16_t* src, uint16_t* dst, int i0, const float (&c)[8],
+                                          const float (&s)[8]) {
+  constexpr int HALF = DH / 2;
+  const u32x4 a = load16(src + i0), bv = load16(src + HALF + i0);
+  u32x4 oa, ob;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x1l = bf16_lo(a[j]), x1h = bf16_hi(a[j]), x2l = bf16_lo(bv[j]), x2h = bf16_hi(bv[j]);
+    const int il = 2 * j, ih = 2 * j + 1;
+    oa[j] = pack_bf16x2(fmaf(x1l, c[il], -(x2l * s[il])), fmaf(x1h, c[ih], -(x2h * s[ih])));
+    ob[j] = pack_bf16x2(fmaf(x2l, c[il], x1l * s[il]), fmaf(x2h, c[ih], x1h * s[ih]));
+  }
+  store16(dst + i0, oa);
+  store16(dst + HALF + i0, ob);
+}
+
 // Prepass, per 64-key block of KV head g:
 //   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
 //   in slot order, zero beyond M);
 //   key-score term kb [B, Hq, Mp] fp32 = gain_h * log2(e) * key_score for the
-//   G query heads of g (zero beyond M).
-template <int DH>
+//   G query heads of g (zero beyond M);
+//   with ROPE, also the rotary embedding of the block's K rows (head g) and Q
+//   rows (the G query heads of g) at their original positions (the rotate-
+//   half form: pair (x_i, x_{i+DH/2}) turns by pos * base^(-2i/DH)).  The
+//   angle is formed and reduced modulo 2 pi in fp64, so that its fp32 sine
+//   and cosine are accurate to a few ulp at any position.
+template <int DH, bool ROPE>
 __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* __restrict__ v,
                                                                 const float* __restrict__ key_score,
                                                                 const float* __restrict__ gain, int M, int Mp,
                                                                 int Hkv, int G, uint16_t* __restrict__ vt,
-                                                                float* __restrict__ kbias) {
+                                                                float* __restrict__ kbias, RopeArgs ra) {
   __shared__ uint16_t sT[DH][kBK + 2];
+  __shared__ double s_freq[DH / 2];
   const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
+  if (ROPE && tid < DH / 2) s_freq[tid] = pow(ra.base, -2.0 * (double)tid / (double)DH);  // (ordered by the barrier below)
   const float scale = 1.0f / (float)(1 << kVScaleLog2);
   constexpr int NL = kBK * DH / 8 / kThreads;  // 16-byte loads per thread, all issued before any use
   u32x4 w[NL];
@@ -143,6 +181,30 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     for (int i = 0; i < 4; ++i)
       o[i] = (uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i)] | ((uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i + 1)] << 16);
     store16(vt + (((size_t)b * Hkv + g) * DH + d) * Mp + m0 + kc * 8, o);
+  }
+  if constexpr (ROPE) {
+    constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
+    constexpr double kInv2Pi = 0.15915494309189535, k2PiHi = 6.283185307179586, k2PiLo = 2.4492935982947064e-16;
+    const int Hq = Hkv * G;
+    for (int t = tid; t < kBK * PG; t += kThreads) {
+      const int key = t / PG, i0 = (t % PG) * 8, m = m0 + key;
+      if (m >= M) continue;
+      const double p = (double)ra.pos[(size_t)b * M + m];
+      float c[8], sn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double th = p * s_freq[i0 + i];
+        const double n = rint(th * kInv2Pi);
+        const double red = fma(-n, k2PiLo, fma(-n, k2PiHi, th));  // th - 2 pi n, |red| <= pi (+ rounding)
+        sincosf((float)red, &sn[i], &c[i]);
+      }
+      const size_t krow = (((size_t)b * M + m) * Hkv + g) * DH;
+      rope_row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
+      for (int hh = 0; hh < G; ++hh) {
+        const size_t qrow = (((size_t)b * M + m) * Hq + g * G + hh) * DH;
+        rope_row8<DH>(ra.q + qrow, ra.qr + qrow, i0, c, sn);
+      }
+    }
   }
 }
 
@@ -694,11 +756,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
 template <int DH, int G>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq, int Hkv,
                     const float* ks, const int32_t* pos, const float* gain, const float* temp, float sm_scale,
-                    uint16_t* out, float* lse, uint16_t* vt, float* kbias, hipStream_t s) {
+                    uint16_t* out, float* lse, uint16_t* vt, float* kbias, const RopeArgs* rope, hipStream_t s) {
   constexpr int BQ = 32 * (4 / G);
   const int Mp = (M + kBK - 1) / kBK * kBK;
-  hipLaunchKernelGGL((attn_prepass_kernel<DH>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain, M, Mp,
-                     Hkv, G, vt, kbias);
+  if (rope != nullptr) {
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, true>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain,
+                       M, Mp, Hkv, G, vt, kbias, *rope);
+    q = rope->qr;  // the main kernel reads the rotated copies
+    k = rope->kr;
+  } else {
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain,
+                       M, Mp, Hkv, G, vt, kbias, RopeArgs{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (M + BQ - 1) / BQ;
@@ -718,18 +787,31 @@ size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
   return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)Hq * 4);
 }
 
+// ... then the rotated q [B, M, Hq, dh] and k [B, M, Hkv, dh] (bf16)
+size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh) {
+  return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * (Hq + Hkv) * dh * 2;
+}
+
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq,
                                   int Hkv, int dh, const float* key_score, const int32_t* pos, const float* gain,
-                                  const float* temp, float sm_scale, uint16_t* out, float* lse, void* ws,
-                                  hipStream_t s) {
+                                  const float* temp, float sm_scale, double rope_base, uint16_t* out, float* lse,
+                                  void* ws, hipStream_t s) {
   const int G = Hq / Hkv;
   const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
   uint16_t* vt = static_cast<uint16_t*>(ws);
   float* kbias = reinterpret_cast<float*>(vt + (size_t)B * Hkv * dh * Mp);
+  RopeArgs ra{};
+  const RopeArgs* rope = nullptr;
+  if (rope_base > 0.0) {
+    uint16_t* qr = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
+                                               gated_attention_workspace(B, M, Hq, Hkv, dh));
+    ra = RopeArgs{q, k, pos, rope_base, qr, qr + (size_t)B * M * Hq * dh};
+    rope = &ra;
+  }
 #define TG_ATTN_CASE(DHV, GV)                                                                                   \
   if (dh == DHV && G == GV)                                                                                     \
     return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, kbias, \
-                             s);
+                             rope, s);
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 4)

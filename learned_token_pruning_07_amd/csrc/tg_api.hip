@@ -38,7 +38,6 @@ int tg_version(void) { return 10000; }
 const char* tg_last_error(void) { return g_err; }
 
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
-  (void)K;
   if (op == TG_OP_GATE_SCORE) {
     if (d <= 0 || h <= 0) return 0;
     return tg::gate_score_workspace(h, d);  // the RMSNorm weight folded into W1 (bf16)
@@ -60,6 +59,11 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     // d = Hkv * d_h, h = Hq: an fp16 V^T copy (B * Hkv * d_h * round_up(M, 64)
     // values) and the fp32 key-score term of every query head (B * Hq * round_up(M, 64))
     return tg::gated_attention_workspace(B, N, h, 1, d);
+  }
+  if (op == TG_OP_GATED_ATTENTION_ROPE) {
+    // as TG_OP_GATED_ATTENTION with K = d_h, plus the rotated q and k (bf16)
+    if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
+    return tg::gated_attention_rope_workspace(B, N, h, d / K, K);
   }
   return 0;
 }
@@ -183,31 +187,57 @@ int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, i
                     "tg_gate_select");
 }
 
+}  // extern "C"
+
+namespace {
+
+int gated_attention_common(const char* name, const void* q, const void* k, const void* v, int B, int M, int Hq,
+                           int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
+                           const float* temp, float sm_scale, double rope_base, void* out, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
+  if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
+  if (M == 0) return TG_OK;
+  if (!q || !k || !v || !key_score || !pos || !gain || !temp || !out)
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(key_score) ||
+      !aligned4(pos) || !aligned4(gain) || !aligned4(temp) || (lse && !aligned4(lse)))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  if (!(sm_scale > 0.0f)) return fail(TG_EINVAL, "%s: sm_scale must be > 0", name);
+  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4) return fail(TG_EUNSUPPORTED, "%s: Hq/Hkv=%d not in {1,2,4}", name, G);
+  const size_t need = rope_base > 0.0 ? tg::gated_attention_rope_workspace(B, M, Hq, Hkv, d_h)
+                                      : tg::gated_attention_workspace(B, M, Hq, Hkv, d_h);
+  if (!ws || ws_bytes < need)
+    return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+  if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+  return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                               static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
+                                               pos, gain, temp, sm_scale, rope_base, static_cast<uint16_t*>(out),
+                                               lse, ws, reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
+}  // namespace
+
+extern "C" {
+
 int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,
                        const float* key_score, const int32_t* pos, const float* gain, const float* temp,
                        float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "tg_gated_attention: bad sizes");
-  if (Hq % Hkv != 0) return fail(TG_EINVAL, "tg_gated_attention: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
-  if (M == 0) return TG_OK;
-  if (!q || !k || !v || !key_score || !pos || !gain || !temp || !out)
-    return fail(TG_EINVAL, "tg_gated_attention: null pointer argument");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(key_score) ||
-      !aligned4(pos) || !aligned4(gain) || !aligned4(temp) || (lse && !aligned4(lse)))
-    return fail(TG_EINVAL, "tg_gated_attention: misaligned pointer");
-  if (!(sm_scale > 0.0f)) return fail(TG_EINVAL, "tg_gated_attention: sm_scale must be > 0");
-  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "tg_gated_attention: d_h=%d not in {64,128}", d_h);
-  const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4)
-    return fail(TG_EUNSUPPORTED, "tg_gated_attention: Hq/Hkv=%d not in {1,2,4}", G);
-  const size_t need = tg::gated_attention_workspace(B, M, Hq, Hkv, d_h);
-  if (!ws || ws_bytes < need)
-    return fail(TG_EINVAL, "tg_gated_attention: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gated_attention: misaligned workspace");
-  return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                               static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
-                                               pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse, ws,
-                                               reinterpret_cast<hipStream_t>(stream)),
-                    "tg_gated_attention");
+  return gated_attention_common("tg_gated_attention", q, k, v, B, M, Hq, Hkv, d_h, key_score, pos, gain, temp,
+                                sm_scale, 0.0, out, lse, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_rope(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,
+                            const float* key_score, const int32_t* pos, const float* gain, const float* temp,
+                            float sm_scale, double rope_base, void* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!(rope_base > 1.0) || !(rope_base < 1e300))
+    return fail(TG_EINVAL, "tg_gated_attention_rope: rope_base must be finite and > 1");
+  return gated_attention_common("tg_gated_attention_rope", q, k, v, B, M, Hq, Hkv, d_h, key_score, pos, gain,
+                                temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -44,12 +44,17 @@ hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, float
                               size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
                               void* resid_out, float* score_kept, void* ws, hipStream_t s);
 
+// rope_base > 0: q and k are first rotated (rotary embedding at the positions
+// pos, base rope_base) into the workspace, and the attention reads the copies.
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                   int M, int Hq, int Hkv, int dh, const float* key_score,
                                   const int32_t* pos, const float* gain, const float* temp,
-                                  float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s);
+                                  float sm_scale, double rope_base, uint16_t* out, float* lse, void* ws,
+                                  hipStream_t s);
 
-// Workspace bytes of launch_gated_attention: the fp16 V^T copy.
+// Workspace bytes of launch_gated_attention: the fp16 V^T copy and the
+// key-score terms; with the rotary embedding also the rotated q and k.
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh);
+size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh);
 
 }  // namespace tg

@@ -59,6 +59,10 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == 3392 * (8 * 128 * 2 + 16 * 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 0) == 2 * 64 * (2 * 64 * 2 + 4 * 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 0, 0) == 0   # Hq is required
+    # the rotary variant adds the rotated q [B, M, Hq, d_h] and k [B, M, Hkv, d_h] (bf16); K = d_h
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 3341, 8 * 128, 16, 128) == \
+        3392 * (8 * 128 * 2 + 16 * 4) + 3341 * (16 + 8) * 128 * 2
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 64, 2 * 64, 4, 0) == 0   # d_h is required
 
 
 def _err(lib):
@@ -165,6 +169,26 @@ def test_attention_validation(lib):
     assert call(ws=NULL) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(ws_bytes=1000) == tgb.TG_EINVAL
     assert call(ws=FAKE_ODD) == tgb.TG_EINVAL
+
+
+def test_attention_rope_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, M=64, Hq=16, Hkv=8, dh=128, ks=FAKE, pos=FAKE, gain=FAKE, temp=FAKE,
+                 scale=0.088, base=1e6, out=FAKE, lse=NULL, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.tg_gated_attention_rope(a["q"], a["k"], a["v"], a["B"], a["M"], a["Hq"], a["Hkv"], a["dh"],
+                                           a["ks"], a["pos"], a["gain"], a["temp"], a["scale"], a["base"], a["out"],
+                                           a["lse"], a["ws"], a["ws_bytes"], None)
+
+    assert call(base=1.0) == tgb.TG_EINVAL and "rope_base" in _err(lib)
+    assert call(base=float("nan")) == tgb.TG_EINVAL
+    assert call(base=float("inf")) == tgb.TG_EINVAL
+    assert call(dh=96) == tgb.TG_EUNSUPPORTED
+    assert call(q=NULL) == tgb.TG_EINVAL
+    # the plain attention's workspace is too small for the rotated copies
+    plain = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 8 * 128, 16, 0)
+    assert call(ws_bytes=plain) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(M=0, q=NULL) == tgb.TG_OK
 
 
 def test_python_binding_refuses_cpu_tensors():

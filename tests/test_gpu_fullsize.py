@@ -108,6 +108,25 @@ def test_attention_4k():
     say(f"  attn_4k max|err| O {e1:.3g} lse {e2:.3g}")
 
 
+def test_attention_rope_4k():
+    """As attn_4k with rotary embedding (base 1e6) at sparse original positions up to 32767."""
+    say("full size: attn_4k with rotary embedding")
+    rng = np.random.default_rng(11)
+    pos = np.sort(rng.choice(32768, size=(1, 4096), replace=False), axis=1).astype(np.int32)
+    c = wl.attn_case(seed=0, **dict(wl.ATTN_4K, pos=pos))
+    b = tg.tg_seq_rmsnorm(dev(c.b_raw), 64)
+    q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
+    out, lse = tg.tg_gated_attention_rope(q, k, v, b, dev(c.pos), dev(c.gain), dev(c.temp), 1e6, c.sm_scale,
+                                          want_lse=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(0, c.M, 128, [0, 63, 64, 65, 4095], seed=4)
+    bh = b.cpu().numpy()
+    O, L = oracle.gated_attention_rope(c.q, c.k, c.v, bh, c.pos, c.gain, c.temp, c.sm_scale, 1e6, rows=rows)
+    e1 = assert_close(wl.bf16_bits_to_f32(host_bits(out))[:, rows], O, TOL_BF16, "attn_4k rope O")
+    e2 = assert_close(lse.cpu().numpy()[:, :, rows], L, TOL_LSE, "attn_4k rope lse")
+    say(f"  attn_4k rope max|err| O {e1:.3g} lse {e2:.3g}")
+
+
 def test_stage_32k():
     """N=32768, r=64, K=3277, then token-gated attention layers (16q/8kv, d_h 128) on the compacted stream."""
     say("full size: stage_32k")

@@ -254,6 +254,34 @@ def test_gated_attention(dh, Hq, Hkv, M, pos, B):
     _attn_check(c, b)
 
 
+@pytest.mark.parametrize("dh,Hq,Hkv,M,pos,B,base", [
+    (128, 4, 2, 333, "sparse", 1, 1e6),
+    (128, 16, 8, 130, "sparse", 2, 1e4),
+    (64, 4, 1, 200, "arange", 1, 1e4),
+    (64, 2, 2, 97, "sparse", 1, 5e5),
+    (128, 4, 2, 300, "far", 1, 1e6),   # original positions up to 131071
+])
+def test_gated_attention_rope(dh, Hq, Hkv, M, pos, B, base):
+    say(f"gated_attention_rope dh={dh} Hq={Hq} Hkv={Hkv} M={M} pos={pos} B={B} base={base:g}")
+    if pos == "far":
+        rng = np.random.default_rng(M)
+        pos = np.sort(rng.choice(131072, size=(B, M), replace=False), axis=1).astype(np.int32)
+    c = wl.attn_case(M=M, Hq=Hq, Hkv=Hkv, dh=dh, seed=M * dh + Hq + 7, B=B, r_zero=min(10, M), pos=pos)
+    b = oracle.seq_rmsnorm(c.b_raw, min(10, M), 1e-6).astype(np.float32)
+    q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = poison_f32((c.B, c.Hq, c.M))
+    tg.tg_gated_attention_rope(q, k, v, dev(b), dev(c.pos), dev(c.gain), dev(c.temp), base, c.sm_scale, out=out,
+                               lse=lse)
+    O, L = oracle.gated_attention_rope(c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale, base)
+    e1 = assert_close(wl.bf16_bits_to_f32(host_bits(out)), O, TOL_BF16, "rope O")
+    e2 = assert_close(lse.cpu().numpy(), L, TOL_LSE, "rope lse")
+    say(f"  max |err| O {e1:.3g} lse {e2:.3g}")
+    # the rotation changes the result (positions are not all zero)
+    O0, _ = oracle.gated_attention(c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale)
+    assert np.abs(O0 - O).max() > 1e-2
+
+
 def test_gated_attention_plain_special_case():
     # b = 0, unit temperature, full-context positions: plain causal GQA attention
     c = wl.attn_case(M=150, Hq=4, Hkv=2, dh=128, seed=2, r_zero=150, gain=1.0, temp=1.0)
