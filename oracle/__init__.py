@@ -9,6 +9,7 @@ from .tokengate_ref import (  # noqa: F401
     gated_attention,
     gated_attention_gate_form,
     gated_attention_rope,
+    gated_attention_backward,
     bf16_round,
     rope,
     rope_inv_freq,

@@ -328,3 +328,63 @@ def gated_attention_rope(q, k, v, b_S, pos, gain, temp, sm_scale: float, base: f
     qr = bf16_round(rope(q, pos, base))
     kr = bf16_round(rope(k, pos, base))
     return gated_attention(qr, kr, v, b_S, pos, gain, temp, sm_scale, rows=rows)
+
+
+# --------------------------------------------------------------------------
+# Backward of the token-gated attention (Eq. 8), the path through which the
+# gate is trained: the key score b_j enters every logit of key j through
+# gain_h * b_j (paper Section 4, token-gated attention and "Putting everything
+# together"), so dL/db_j = sum_h gain_h sum_i dZ_{h,ij}.
+#
+# With z_ij = s_ij c_i + gain_h b_j, c_i = sm_scale / tau_{h,i}, s = q.k,
+# P = exp(z - lse) on j <= i and O = P V, for an upstream gradient dO:
+#   D_i   = dO_i . O_i
+#   dZ_ij = P_ij (dO_i . v_j - D_i)
+#   dq_i  = c_i sum_j dZ_ij k_j          dk_j = sum_i c_i dZ_ij q_i
+#   dv_j  = sum_i P_ij dO_i              db_j = sum_h gain_h sum_i dZ_{h,ij}
+#   dgain_h = sum_ij dZ_{h,ij} b_j       dtemp_h = -(1/temp_h) sum_ij dZ_{h,ij} s_ij c_i
+# Reading: like the usual flash-attention backward, D and P are formed from
+# the forward's own outputs O (bf16) and lse, which are inputs here.
+# --------------------------------------------------------------------------
+def gated_attention_backward(q, k, v, b_S, pos, gain, temp, sm_scale: float, O, lse, dO):
+    """Return ``(dq, dk, dv, db, dgain, dtemp)`` in float64."""
+    Q = widen(q)
+    Kx = widen(k)
+    V = widen(v)
+    b = widen(b_S)
+    P_ = np.asarray(pos)
+    g = widen(gain)
+    t = widen(temp)
+    Ox = widen(O)
+    L = widen(lse)
+    dOx = widen(dO)
+    B, M, Hq, dh = Q.shape
+    Hkv = Kx.shape[2]
+    group = Hq // Hkv
+    dq = np.zeros_like(Q)
+    dk = np.zeros_like(Kx)
+    dv = np.zeros_like(V)
+    db = np.zeros((B, M), np.float64)
+    dgain = np.zeros(Hq, np.float64)
+    dtemp = np.zeros(Hq, np.float64)
+    causal = np.arange(M)[None, :] <= np.arange(M)[:, None]
+    for bi in range(B):
+        for h in range(Hq):
+            kv = h // group
+            tau = t[h] * np.array([temperature_ratio(P_[bi, i], i) for i in range(M)])
+            c = sm_scale / tau
+            S = Q[bi, :, h, :] @ Kx[bi, :, kv, :].T
+            z = S * c[:, None] + g[h] * b[bi][None, :]
+            Pm = np.where(causal, np.exp(np.where(causal, z, 0.0) - L[bi, h][:, None]), 0.0)
+            dP = dOx[bi, :, h, :] @ V[bi, :, kv, :].T
+            D = np.sum(dOx[bi, :, h, :] * Ox[bi, :, h, :], axis=1)
+            dZ = Pm * (dP - D[:, None])
+            dS = dZ * c[:, None]
+            dq[bi, :, h, :] = dS @ Kx[bi, :, kv, :]
+            dk[bi, :, kv, :] += dS.T @ Q[bi, :, h, :]
+            dv[bi, :, kv, :] += Pm.T @ dOx[bi, :, h, :]
+            col = dZ.sum(axis=0)
+            db[bi] += g[h] * col
+            dgain[h] += float(col @ b[bi])
+            dtemp[h] += -float(np.sum(dS * S)) / t[h]
+    return dq, dk, dv, db, dgain, dtemp
