@@ -53,7 +53,8 @@ typedef enum {
   TG_OP_COMPACT = 3,
   TG_OP_GATED_ATTENTION = 4,
   TG_OP_GATE_SELECT = 5,
-  TG_OP_GATED_ATTENTION_ROPE = 6
+  TG_OP_GATED_ATTENTION_ROPE = 6,
+  TG_OP_GATED_ATTENTION_BACKWARD = 7
 } tg_op;
 
 /*
@@ -242,11 +243,59 @@ int tg_gated_attention_rope(const void* q, const void* k, const void* v,
                             double rope_base, void* out, float* lse, void* ws,
                             size_t ws_bytes, void* stream);
 
+/*
+ * tg_gated_attention_backward -- gradients of tg_gated_attention.  In the
+ * paper the key score reaches the loss only through the gain_h * b_j term of
+ * the token-gated attention logits (Section 4, token-gated attention, Eq. 8):
+ * that term is what trains the scorer despite the non-differentiable top-K,
+ * and the per-head gain and the temperature are trainable as well ("Putting
+ * everything together").  With z, c_i and lse as in tg_gated_attention,
+ * P_ij = exp(z_ij - lse_i) (j <= i) and the upstream gradient dO:
+ *     D_i      = dO_i . O_i
+ *     dZ_ij    = P_ij (dO_i . v_j - D_i)
+ *     d_q_i    = c_i sum_j dZ_ij k_j                 (per query head)
+ *     d_k_j    = sum_{h of the group} sum_i c_i dZ_ij q_i
+ *     d_v_j    = sum_{h of the group} sum_i P_ij dO_i
+ *     d_key_score_j = sum_h gain_h sum_i dZ_{h,ij}
+ *     d_gain_h = sum_{b,i,j} dZ_{h,ij} key_score_j
+ *     d_temp_h = -(1 / temp_h) sum_{b,i,j} dZ_{h,ij} (q_i . k_j) c_i
+ * P and D are formed from the forward's own outputs `out` and `lse`, as in
+ * the usual flash-attention backward.
+ *
+ *   q, k, v, key_score, pos, gain, temp, sm_scale, B, M, Hq, Hkv, d_h
+ *                    as passed to tg_gated_attention
+ *   out [B, M, Hq, d_h] bf16 and lse [B, Hq, M] fp32: that call's outputs
+ *   d_out [B, M, Hq, d_h] bf16: the gradient of the loss with respect to out
+ *   d_q [B, M, Hq, d_h], d_k and d_v [B, M, Hkv, d_h] bf16 (nearest even)
+ *   d_key_score [B, M] fp32; d_gain [Hq] and d_temp [Hq] fp32, summed over
+ *                    the batch.  Every output is overwritten, not accumulated.
+ *   ws, ws_bytes     workspace of at least tg_workspace_size(
+ *                    TG_OP_GATED_ATTENTION_BACKWARD, B, M, Hkv * d_h, Hq, d_h)
+ *                    bytes, 16-byte aligned, contents need no initialisation
+ *   d_h in {64, 128}; Hq / Hkv in {1, 2, 4}; B <= 65535.  With M == 0 only
+ *   d_gain and d_temp are written (zeros) and the other pointers may be NULL.
+ *   Products run on bf16 MFMA with fp32 accumulation (P and dZ c are rounded
+ *   to bf16 for the second products); the softmax terms are fp32; d_gain and
+ *   d_temp add their fp32 per-block partials in fp64.
+ */
+int tg_gated_attention_backward(const void* q, const void* k, const void* v,
+                                const void* out, const float* lse,
+                                const void* d_out, int B, int M, int Hq,
+                                int Hkv, int d_h, const float* key_score,
+                                const int32_t* pos, const float* gain,
+                                const float* temp, float sm_scale, void* d_q,
+                                void* d_k, void* d_v, float* d_key_score,
+                                float* d_gain, float* d_temp, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
  * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
  * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq).
  * For TG_OP_GATED_ATTENTION_ROPE pass the same and K = d_h; the size adds
  * 2 * B * M * (Hq + Hkv) * d_h.
+ * For TG_OP_GATED_ATTENTION_BACKWARD pass the same as for
+ * TG_OP_GATED_ATTENTION_ROPE; with Mp = round_up(M, 64) the size is
+ * B * Mp * (2 * (2 Hq + Hkv) * d_h + 12 Hq + 4 Hkv) + 8 * B * (Mp / 64) * Hq.
  * TG_OP_SEQ_RMSNORM and TG_OP_TOPK_SELECT depend on B and N only. */
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
 

@@ -22,10 +22,10 @@ LIB_PATH = os.path.join(_PKG, "libtokengate.so")
 TG_OK, TG_EINVAL, TG_EUNSUPPORTED, TG_EHIP = 0, 1, 2, 3
 TG_F32, TG_BF16 = 0, 1
 (TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION, TG_OP_GATE_SELECT,
- TG_OP_GATED_ATTENTION_ROPE) = range(7)
+ TG_OP_GATED_ATTENTION_ROPE, TG_OP_GATED_ATTENTION_BACKWARD) = range(8)
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
-            "tg_gated_attention_rope", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -54,6 +54,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_select.argtypes = [vp, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention_rope.argtypes = [vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, ctypes.c_double, vp, vp,
                                             vp, sz, vp]
+    lib.tg_gated_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp,
+                                                vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
@@ -61,7 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_version.argtypes = []
     lib.tg_version.restype = i
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
-                 "tg_gate_select", "tg_gated_attention_rope"):
+                 "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -330,6 +332,61 @@ def tg_gated_attention_rope(q, k, v, key_score, pos, gain, temp, rope_base: floa
     un-rotated.  ``ws`` from :func:`attention_rope_workspace`."""
     return _attention_call("tg_gated_attention_rope", q, k, v, key_score, pos, gain, temp, sm_scale, out, lse,
                            want_lse, ws, stream, rope_base=rope_base)
+
+
+def attention_backward_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for tg_gated_attention_backward at these sizes."""
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION_BACKWARD, B, M, Hkv * dh, Hq, dh))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def tg_gated_attention_backward(q, k, v, out, lse, d_out, key_score, pos, gain, temp, sm_scale: float | None = None,
+                                d_q=None, d_k=None, d_v=None, d_key_score=None, d_gain=None, d_temp=None, ws=None,
+                                stream=None):
+    """Gradients of tg_gated_attention from its outputs ``out`` and ``lse``
+    and the upstream gradient ``d_out``.  Returns ``(d_q, d_k, d_v,
+    d_key_score, d_gain, d_temp)``: bf16 like q/k/v, fp32 ``[B, M]``, and
+    fp32 ``[Hq]`` summed over the batch.  ``ws`` from
+    :func:`attention_backward_workspace`."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    B, M, Hq, dh = q.shape
+    Hkv = k.shape[2]
+    dev = q.device
+    _need(k, "k", torch.bfloat16, (B, M, Hkv, dh))
+    _need(v, "v", torch.bfloat16, (B, M, Hkv, dh))
+    _need(out, "out", torch.bfloat16, (B, M, Hq, dh))
+    _need(d_out, "d_out", torch.bfloat16, (B, M, Hq, dh))
+    _need(lse, "lse", torch.float32, (B, Hq, M))
+    _need(key_score, "key_score", torch.float32, (B, M))
+    _need(pos, "pos", torch.int32, (B, M))
+    _need(gain, "gain", torch.float32, (Hq,))
+    _need(temp, "temp", torch.float32, (Hq,))
+    if sm_scale is None:
+        sm_scale = dh ** -0.5
+    d_q = torch.empty_like(q) if d_q is None else d_q
+    d_k = torch.empty_like(k) if d_k is None else d_k
+    d_v = torch.empty_like(v) if d_v is None else d_v
+    if d_key_score is None:
+        d_key_score = torch.empty((B, M), dtype=torch.float32, device=dev)
+    if d_gain is None:
+        d_gain = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    if d_temp is None:
+        d_temp = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    _need(d_q, "d_q", torch.bfloat16, (B, M, Hq, dh))
+    _need(d_k, "d_k", torch.bfloat16, (B, M, Hkv, dh))
+    _need(d_v, "d_v", torch.bfloat16, (B, M, Hkv, dh))
+    _need(d_key_score, "d_key_score", torch.float32, (B, M))
+    _need(d_gain, "d_gain", torch.float32, (Hq,))
+    _need(d_temp, "d_temp", torch.float32, (Hq,))
+    if ws is None:
+        ws = attention_backward_workspace(B, M, Hq, Hkv, dh, dev)
+    _need(ws, "ws", torch.uint8)
+    _check(lib.tg_gated_attention_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
+        _ptr(gain), _ptr(temp), float(sm_scale), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_key_score), _ptr(d_gain),
+        _ptr(d_temp), _ptr(ws), ws.numel(), _stream(stream)))
+    return d_q, d_k, d_v, d_key_score, d_gain, d_temp
 
 
 def tg_workspace_size(op: int, B: int, N: int, d: int, h: int, K: int) -> int:

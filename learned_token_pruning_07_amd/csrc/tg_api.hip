@@ -65,6 +65,13 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
     return tg::gated_attention_rope_workspace(B, N, h, d / K, K);
   }
+  if (op == TG_OP_GATED_ATTENTION_BACKWARD) {
+    // N = M, d = Hkv * d_h, h = Hq, K = d_h: transposed Q, dO and K copies,
+    // per-row constants and the partial sums of the key-score, gain and
+    // temperature gradients
+    if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
+    return tg::gated_attention_backward_workspace(B, N, h, d / K, K);
+  }
   return 0;
 }
 
@@ -238,6 +245,47 @@ int tg_gated_attention_rope(const void* q, const void* k, const void* v, int B, 
     return fail(TG_EINVAL, "tg_gated_attention_rope: rope_base must be finite and > 1");
   return gated_attention_common("tg_gated_attention_rope", q, k, v, B, M, Hq, Hkv, d_h, key_score, pos, gain,
                                 temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                const void* d_out, int B, int M, int Hq, int Hkv, int d_h, const float* key_score,
+                                const int32_t* pos, const float* gain, const float* temp, float sm_scale, void* d_q,
+                                void* d_k, void* d_v, float* d_key_score, float* d_gain, float* d_temp, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const char* name = "tg_gated_attention_backward";
+  if (B <= 0 || B > 65535 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
+  if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
+  if (!gain || !temp || !d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned4(gain) || !aligned4(temp) || !aligned4(d_gain) || !aligned4(d_temp))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4) return fail(TG_EUNSUPPORTED, "%s: Hq/Hkv=%d not in {1,2,4}", name, G);
+  if (M > 0) {
+    if (!q || !k || !v || !out || !lse || !d_out || !key_score || !pos || !d_q || !d_k || !d_v || !d_key_score)
+      return fail(TG_EINVAL, "%s: null pointer argument", name);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(d_out) ||
+        !aligned16(d_q) || !aligned16(d_k) || !aligned16(d_v) || !aligned4(lse) || !aligned4(key_score) ||
+        !aligned4(pos) || !aligned4(d_key_score))
+      return fail(TG_EINVAL, "%s: misaligned pointer", name);
+    if (!(sm_scale > 0.0f)) return fail(TG_EINVAL, "%s: sm_scale must be > 0", name);
+    // buffer-resource ranges are 32-bit: every per-head plane must stay below 2 GiB
+    const long long Mp = (M + 63LL) / 64 * 64;
+    if ((long long)M * Hq * d_h * 2 >= (1LL << 31) || Mp * d_h * 2 >= (1LL << 31) ||
+        (long long)B * Hq * Mp * 4 >= (1LL << 31))
+      return fail(TG_EUNSUPPORTED, "%s: M=%d too large", name, M);
+    const size_t need = tg::gated_attention_backward_workspace(B, M, Hq, Hkv, d_h);
+    if (!ws || ws_bytes < need)
+      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+  }
+  return hip_status(
+      tg::launch_gated_attention_backward(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+          static_cast<const uint16_t*>(out), lse, static_cast<const uint16_t*>(d_out), B, M, Hq, Hkv, d_h, key_score,
+          pos, gain, temp, sm_scale, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
+          static_cast<uint16_t*>(d_v), d_key_score, d_gain, d_temp, ws, reinterpret_cast<hipStream_t>(stream)),
+      name);
 }
 
 }  // extern "C"

@@ -57,4 +57,14 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh);
 size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh);
 
+// Backward of the token-gated attention: dq, dk, dv (bf16), the key-score
+// gradient [B, M] and the gain and temperature gradients [Hq] (fp32).
+hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                           const uint16_t* out, const float* lse, const uint16_t* d_out, int B, int M,
+                                           int Hq, int Hkv, int dh, const float* key_score, const int32_t* pos,
+                                           const float* gain, const float* temp, float sm_scale, uint16_t* dq,
+                                           uint16_t* dk, uint16_t* dv, float* d_key_score, float* d_gain,
+                                           float* d_temp, void* ws, hipStream_t s);
+size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh);
+
 }  // namespace tg

@@ -10,6 +10,7 @@ from .tokengate_ref import (  # noqa: F401
     gated_attention_gate_form,
     gated_attention_rope,
     gated_attention_backward,
+    gated_attention_backward_l1,
     bf16_round,
     rope,
     rope_inv_freq,

@@ -388,3 +388,47 @@ def gated_attention_backward(q, k, v, b_S, pos, gain, temp, sm_scale: float, O, 
             dgain[h] += float(col @ b[bi])
             dtemp[h] += -float(np.sum(dS * S)) / t[h]
     return dq, dk, dv, db, dgain, dtemp
+
+
+def gated_attention_backward_l1(q, k, v, b_S, pos, gain, temp, sm_scale: float, O, lse, dO):
+    """Error scales for the backward: each gradient's sum with every summand
+    replaced by its absolute value (``sum |dZ| |k| c``, ``sum P |dO|``, ...).
+    A result whose summands carry relative errors up to u differs from the
+    exact sum by at most u times this L1 sum; the parity tests state their
+    tolerances in these units.  Returns the same six arrays as
+    :func:`gated_attention_backward`."""
+    Q = np.abs(widen(q))
+    Kx = np.abs(widen(k))
+    V = widen(v)
+    b = widen(b_S)
+    P_ = np.asarray(pos)
+    g = widen(gain)
+    t = widen(temp)
+    Ox = widen(O)
+    L = widen(lse)
+    dOx = widen(dO)
+    B, M, Hq, dh = Q.shape
+    Hkv = Kx.shape[2]
+    group = Hq // Hkv
+    out = [np.zeros_like(Q), np.zeros_like(Kx), np.zeros_like(V), np.zeros((B, M)), np.zeros(Hq), np.zeros(Hq)]
+    causal = np.arange(M)[None, :] <= np.arange(M)[:, None]
+    for bi in range(B):
+        for h in range(Hq):
+            kv = h // group
+            tau = t[h] * np.array([temperature_ratio(P_[bi, i], i) for i in range(M)])
+            c = sm_scale / tau
+            S = widen(q)[bi, :, h, :] @ widen(k)[bi, :, kv, :].T
+            z = S * c[:, None] + g[h] * b[bi][None, :]
+            Pm = np.where(causal, np.exp(np.where(causal, z, 0.0) - L[bi, h][:, None]), 0.0)
+            dP = dOx[bi, :, h, :] @ V[bi, :, kv, :].T
+            D = np.sum(dOx[bi, :, h, :] * Ox[bi, :, h, :], axis=1)
+            aZ = Pm * np.abs(dP - D[:, None])
+            aS = aZ * c[:, None]
+            out[0][bi, :, h, :] = aS @ Kx[bi, :, kv, :]
+            out[1][bi, :, kv, :] += aS.T @ Q[bi, :, h, :]
+            out[2][bi, :, kv, :] += Pm.T @ np.abs(dOx[bi, :, h, :])
+            col = aZ.sum(axis=0)
+            out[3][bi] += abs(g[h]) * col
+            out[4][h] += float(col @ np.abs(b[bi]))
+            out[5][h] += float(np.sum(aS * np.abs(S))) / t[h]
+    return tuple(out)

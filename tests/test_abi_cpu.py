@@ -197,3 +197,38 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         tgb.tg_gate_score(x, 0, torch.ones(16, dtype=torch.bfloat16), torch.zeros(64, 16, dtype=torch.bfloat16),
                           torch.zeros(64), torch.zeros(64, dtype=torch.bfloat16), torch.zeros(1))
+
+
+def test_attention_backward_workspace_size(lib):
+    for B, M, Hq, Hkv, dh in [(1, 3341, 16, 8, 128), (2, 100, 4, 4, 64), (1, 64, 8, 2, 128)]:
+        Mp = (M + 63) // 64 * 64
+        want = B * Mp * (2 * (2 * Hq + Hkv) * dh + 12 * Hq + 4 * Hkv) + 8 * B * (Mp // 64) * Hq
+        assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, B, M, Hkv * dh, Hq, dh) == want
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 0, 1024, 16, 128) == 0
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 64, 1000, 16, 128) == 0  # d % d_h != 0
+
+
+def test_attention_backward_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, B=1, M=64, Hq=16, Hkv=8, dh=128, ks=FAKE,
+                 pos=FAKE, gain=FAKE, temp=FAKE, scale=0.088, dq=FAKE, dk=FAKE, dv=FAKE, db=FAKE, dg=FAKE, dt=FAKE,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.tg_gated_attention_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["B"], a["M"],
+                                               a["Hq"], a["Hkv"], a["dh"], a["ks"], a["pos"], a["gain"], a["temp"],
+                                               a["scale"], a["dq"], a["dk"], a["dv"], a["db"], a["dg"], a["dt"],
+                                               a["ws"], a["ws_bytes"], None)
+
+    assert call(dh=96) == tgb.TG_EUNSUPPORTED
+    assert call(Hq=24, Hkv=3) == tgb.TG_EUNSUPPORTED          # group of 8
+    assert call(Hq=16, Hkv=6) == tgb.TG_EINVAL                # not a multiple
+    assert call(B=0) == tgb.TG_EINVAL and call(B=65536) == tgb.TG_EINVAL
+    assert call(M=-1) == tgb.TG_EINVAL
+    for name in ("q", "k", "v", "o", "lse", "do", "ks", "pos", "dq", "dk", "dv", "db", "dg", "dt", "gain", "temp"):
+        assert call(**{name: NULL}) == tgb.TG_EINVAL, name
+    assert call(do=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+    assert call(scale=0.0) == tgb.TG_EINVAL
+    need = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 64, 8 * 128, 16, 128)
+    assert call(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(ws=NULL) == tgb.TG_EINVAL
+    assert call(M=1 << 20, Hq=64, Hkv=16) == tgb.TG_EUNSUPPORTED  # a 32-bit buffer range would overflow

@@ -1,0 +1,140 @@
+"""GPU parity of the token-gated attention backward against the oracle.
+
+The forward outputs the backward consumes (O in bf16, lse in fp32) come from
+the oracle's forward, never from the GPU, so both sides differentiate the
+same point.  Tolerances are stated in units of the oracle's L1 scale of each
+output (the same sum with every summand replaced by its absolute value):
+  * d_q, d_k, d_v: the second products take dZ c, dZ and P rounded to bf16
+    (relative error <= 2^-9 per summand, so <= 2^-9 L1 in the sum), and the
+    result is rounded to bf16 (<= 2^-9 |result|).  Bound, with a factor 2
+    of slack for the fp32 terms: |err| <= 2^-8 (L1 + |ref|).
+  * d_key_score, d_gain, d_temp: fp32 throughout; the summands carry the
+    fp32 error of S, dP and D (about 1e-5 relative), so |err| <= 1e-4 L1.
+  * Every output also gets an absolute floor of 2^-16 rms(L1 of d_v), which
+    only matters where the sums vanish exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import learned_token_pruning_07_amd as tg
+from learned_token_pruning_07_amd import workloads as wl
+from _gpu_util import DEV, dev, dev_bits, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD_BF16 = 2.0 ** -8
+TOL_F32_SUMS = 1e-4
+
+
+def _close(got, ref, l1, tol, what, floor=0.0):
+    """|got - ref| <= tol (l1 + |ref|) + floor elementwise; returns max err / (l1 + |ref|)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output (unwritten element?)"
+    scale = np.asarray(l1, np.float64) + np.abs(ref)
+    err = np.abs(got - ref)
+    bad = err > tol * scale + floor
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol * scale - floor), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside {tol:.3g} x (L1 + |ref|); worst at "
+                             f"{i}: got {got[i]!r} ref {ref[i]!r} L1 {np.asarray(l1)[i]!r}")
+    return float(np.max(err / np.maximum(scale, 1e-300))) if err.size else 0.0
+
+
+def _inputs(M, Hq, Hkv, dh, pos, B, seed):
+    c = wl.attn_case(M=M, Hq=Hq, Hkv=Hkv, dh=dh, seed=seed, B=B, r_zero=min(10, M), pos=pos)
+    b = oracle.seq_rmsnorm(c.b_raw, min(10, M), 1e-6).astype(np.float32) if M > 0 else c.b_raw
+    rng = wl.make_rng(seed + 1)
+    dO = wl.f32_to_bf16_bits(rng.standard_normal((B, M, Hq, dh), dtype=np.float32))
+    return c, b, dO
+
+
+def _oracle_fwd(c, b, heads=None):
+    """Oracle forward; O rounded to bf16 bits, lse to fp32 (what a forward call hands over)."""
+    O, L = oracle.gated_attention(c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale)
+    return oracle.bf16_round(O), L.astype(np.float32)
+
+
+def _gpu(c, b, O_bits, lse, dO):
+    return tg.tg_gated_attention_backward(dev_bits(c.q), dev_bits(c.k), dev_bits(c.v), dev_bits(O_bits), dev(lse),
+                                          dev_bits(dO), dev(b), dev(c.pos), dev(c.gain), dev(c.temp), c.sm_scale)
+
+
+def _reference(c, b, O_bits, L, dO):
+    args = (c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale, O_bits, L, dO)
+    return oracle.gated_attention_backward(*args), oracle.gated_attention_backward_l1(*args)
+
+
+def _check(got, want, l1, what, tol_bf16=TOL_GRAD_BF16, tol_f32=TOL_F32_SUMS):
+    f = lambda t: wl.bf16_bits_to_f32(host_bits(t))
+    names = ["d_q", "d_k", "d_v", "d_key_score", "d_gain", "d_temp"]
+    # an absolute floor far below any rounding unit of the sums: where every
+    # summand cancels exactly (a single kept token), dP - D is fp32 noise
+    floor = 2.0 ** -16 * float(np.sqrt(np.mean(np.asarray(l1[2]) ** 2)))
+    e = []
+    for i, (name, x) in enumerate(zip(names, got)):
+        host = f(x) if x.dtype == torch.bfloat16 else x.cpu().numpy()
+        e.append(_close(host, want[i], l1[i], tol_bf16 if i < 3 else tol_f32, f"{what} {name}",
+                        floor))
+    say("  max err / (L1 + |ref|):  " + "  ".join(f"{n} {v:.2e}" for n, v in zip(names, e)))
+
+
+@pytest.mark.parametrize("dh,Hq,Hkv,M,pos,B", [
+    (128, 4, 2, 333, "sparse", 1),    # ragged: not a multiple of 32 or 64
+    (128, 16, 8, 130, "sparse", 2),   # two batch rows
+    (64, 4, 1, 200, "arange", 1),     # group of 4, d_h 64
+    (64, 2, 2, 97, "sparse", 1),      # group of 1
+    (128, 8, 2, 64, "sparse", 1),     # exactly one key block
+    (128, 4, 4, 31, "sparse", 1),     # shorter than one tile
+    (128, 2, 1, 1, "arange", 1),      # one kept token: only d_v = sum of d_out survives
+    (64, 8, 4, 700, "sparse", 1),     # many tiles, d_h 64
+])
+def test_attention_backward(dh, Hq, Hkv, M, pos, B):
+    say(f"attention backward dh={dh} Hq={Hq} Hkv={Hkv} M={M} pos={pos} B={B}")
+    c, b, dO = _inputs(M, Hq, Hkv, dh, pos, B, seed=M * dh + Hq + 11)
+    O_bits, L = _oracle_fwd(c, b)
+    got = _gpu(c, b, O_bits, L, dO)
+    want, l1 = _reference(c, b, O_bits, L, dO)
+    _check(got, want, l1, f"M={M}")
+
+
+def test_attention_backward_empty():
+    """M = 0: nothing to differentiate; the gain and temperature gradients are zero."""
+    z16 = torch.empty((1, 0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    z16k = torch.empty((1, 0, 2, 128), dtype=torch.bfloat16, device=DEV)
+    dg = torch.full((4,), float("nan"), device=DEV)
+    dt = torch.full((4,), float("nan"), device=DEV)
+    tg.tg_gated_attention_backward(z16, z16k, z16k, z16, torch.empty((1, 4, 0), device=DEV), z16,
+                                   torch.empty((1, 0), device=DEV), torch.empty((1, 0), dtype=torch.int32, device=DEV),
+                                   torch.ones(4, device=DEV), torch.ones(4, device=DEV), 0.088, d_gain=dg, d_temp=dt)
+    assert torch.all(dg == 0) and torch.all(dt == 0)
+
+
+def test_attention_backward_deterministic():
+    c, b, dO = _inputs(300, 4, 2, 128, "sparse", 1, seed=5)
+    O_bits, L = _oracle_fwd(c, b)
+    a = _gpu(c, b, O_bits, L, dO)
+    a2 = _gpu(c, b, O_bits, L, dO)
+    for x, y in zip(a, a2):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+
+
+def test_attention_backward_gradient_of_gpu_forward_is_consistent():
+    """The GPU forward's own O and lse fed to the GPU backward give the oracle's
+    gradients (the backward never sees oracle values here; the reference
+    does)."""
+    c, b, dO = _inputs(257, 4, 2, 128, "sparse", 1, seed=8)
+    q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
+    out, lse = tg.tg_gated_attention(q, k, v, dev(b), dev(c.pos), dev(c.gain), dev(c.temp), c.sm_scale,
+                                     want_lse=True)
+    got = tg.tg_gated_attention_backward(q, k, v, out, lse, dev_bits(dO), dev(b), dev(c.pos), dev(c.gain),
+                                         dev(c.temp), c.sm_scale)
+    O_bits, L = _oracle_fwd(c, b)
+    want, l1 = _reference(c, b, O_bits, L, dO)
+    # the GPU forward's O and lse differ from the oracle's by their own
+    # rounding (bf16 O, lse within 1e-4), which moves D and P: looser units
+    _check(got, want, l1, "gpu-forward", tol_bf16=2.0 ** -6, tol_f32=1e-2)

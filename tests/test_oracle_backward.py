@@ -117,3 +117,18 @@ def test_single_query_row():
         assert np.max(np.abs(g)) < 1e-13
     np.testing.assert_allclose(dv[0, 0, 0], dO[0, 0, 0] + dO[0, 0, 1], rtol=1e-14)
     np.testing.assert_allclose(dv[0, 0, 1], dO[0, 0, 2] + dO[0, 0, 3], rtol=1e-14)
+
+
+def test_l1_scales_bound_the_gradients():
+    """Triangle inequality everywhere, and equality where every summand has
+    one sign (d_v with a non-negative upstream gradient)."""
+    q, k, v, b, pos, gain, temp, sm, dO = _case(5, B=2, M=13, Hq=4, Hkv=2, dh=8)
+    O, lse = oracle.gated_attention(q, k, v, b, pos, gain, temp, sm)
+    g = oracle.gated_attention_backward(q, k, v, b, pos, gain, temp, sm, O, lse, dO)
+    l1 = oracle.gated_attention_backward_l1(q, k, v, b, pos, gain, temp, sm, O, lse, dO)
+    for x, m in zip(g, l1):
+        assert np.all(np.abs(x) <= m * (1 + 1e-12) + 1e-15)
+    dOp = np.abs(dO)
+    gp = oracle.gated_attention_backward(q, k, v, b, pos, gain, temp, sm, O, lse, dOp)
+    lp = oracle.gated_attention_backward_l1(q, k, v, b, pos, gain, temp, sm, O, lse, dOp)
+    np.testing.assert_allclose(gp[2], lp[2], rtol=1e-13)
