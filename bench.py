@@ -99,6 +99,40 @@ class Events:
         return sum(c for _, _, c in self.spans.get(name, []))
 
 
+def time_backward(torch, tg, qkv, b_S, kept_idx, layer, attn_out, heads, M, stream_reps=20):
+    """The backward of one token-gated attention layer at the stage's shape,
+    timed on its own (it is not part of the prefill step): the layer's
+    forward gives O and lse, a seeded bf16 upstream gradient stands in for
+    the loss, and HIP events on the launch stream bracket `stream_reps`
+    back-to-back calls.  Algorithmic work: the five products of the usual
+    flash-attention backward (S, dP, dV, dK, dQ), 2.5x the forward's flops."""
+    q, k, v = qkv
+    Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+    out, lse = tg.tg_gated_attention(q, k, v, b_S, kept_idx, layer.gain, layer.temp, want_lse=True)
+    g = torch.Generator(device=q.device).manual_seed(1234)
+    d_out = torch.randn(q.shape, generator=g, device=q.device).bfloat16()
+    ws = tg.attention_backward_workspace(1, M, Hq, Hkv, dh, q.device)
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty((1, M), device=q.device), torch.empty(Hq, device=q.device), torch.empty(Hq, device=q.device)]
+    call = lambda: tg.tg_gated_attention_backward(q, k, v, out, lse, d_out, b_S, kept_idx, layer.gain,  # noqa: E731
+                                                  layer.temp, None, *grads, ws=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(stream_reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / stream_reps
+    flops = 5 * dh * Hq * M * (M + 1)
+    tf = flops / (us * 1e-6) / 1e12
+    return {"call": "tg_gated_attention_backward", "avg_us": round(us, 3), "calls_timed": stream_reps,
+            "algorithmic_flops": flops, "achieved_TFLOPs": round(tf, 2),
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "shape": {"M": M, "Hq": Hq, "Hkv": Hkv, "d_h": dh}}
+
+
 def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -148,6 +182,8 @@ def main():
                     help="capture each phase of a step as a HIP graph once and replay it (slower on this ROCm: "
                          "a replay costs several microseconds more than direct launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separate timing of tg_gated_attention_backward at the attention shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -380,6 +416,11 @@ def main():
         "glue_qkv_ms_per_step": round(glue_ms, 4),
         "tokens_per_s_with_glue": round(N / ((ms_per_step + glue_ms) * 1e-3), 1),
     }
+
+    if layers and not args.no_backward:
+        out["attention_backward"] = time_backward(torch, tg, qkv[0], b_S, kept_idx, layers[0], attn_out, heads, M,
+                                                  stream_reps=20)
+        log(f"attention backward: {out['attention_backward']['avg_us']:.2f} us per call")
 
     if not args.no_cpu_baseline and layers:
         log("timing the CPU oracle on a bounded sample")

@@ -295,7 +295,7 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v,
  * 2 * B * M * (Hq + Hkv) * d_h.
  * For TG_OP_GATED_ATTENTION_BACKWARD pass the same as for
  * TG_OP_GATED_ATTENTION_ROPE; with Mp = round_up(M, 64) the size is
- * B * Mp * (2 * (2 Hq + Hkv) * d_h + 12 Hq + 4 Hkv) + 8 * B * (Mp / 64) * Hq.
+ * B * Mp * (12 Hq + 4 Hkv) + 8 * B * (Mp / 64) * Hq.
  * TG_OP_SEQ_RMSNORM and TG_OP_TOPK_SELECT depend on B and N only. */
 size_t tg_workspace_size(int op, int B, int N, int d, int h, int K);
 

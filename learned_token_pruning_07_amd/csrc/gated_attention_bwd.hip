@@ -14,30 +14,32 @@
 //   dgain_h = sum_{b,i,j} dZ_{h,ij} b_j,   dtemp_h = -(1/temp_h) sum_{b,i,j} dZ_{h,ij} (q_i . k_j) c_i
 //
 // Four kernels on one stream, all bf16 MFMA 32x32x16 with fp32 accumulation:
-//  * bwd_prepass: per 64-row block of a query head, D_i and the exponent
-//    constants c_i log2(e) and lse_i log2(e) (+inf beyond M, so padded rows
-//    get P = 0), and transposed copies Q^T and dO^T [B, Hq, dh, Mp]; per
-//    64-row block of a KV head, K^T [B, Hkv, dh, Mp].  Inside every 16-row
-//    group of a transposed row the middle two quads are swapped: that is the
-//    order in which an MFMA accumulator hands a lane its 8 rows of a 16-wide
-//    k-step, so accumulators feed the next product as B fragments directly.
+//  * bwd_rows: per query row and head, D_i and the exponent constants
+//    c_i log2(e) and lse_i log2(e) (+inf beyond M, so padded rows get P = 0).
 //  * bwd_dkdv: a workgroup owns 64 keys of one KV head, keeps their K and V
 //    fragments in registers and walks every 32-query tile of each of the G
 //    query heads from the diagonal down.  S = Q K^T and dP = dO V^T come out
 //    with one lane per key, so P and dS = dZ c are at once the B fragments of
-//    dV^T += dO^T P and dK^T += Q^T dS.  Four waves: two key halves x two
-//    query-tile parities, merged through LDS at the end.  The lane's running
-//    column sums of dZ give the key-score, gain and temperature partials.
-//    Tiles travel global -> LDS by buffer loads with the LDS-destination bit,
-//    double-buffered: step p + 1 is in flight while step p is computed.
+//    dV^T += dO^T P and dK^T += Q^T dS; their A fragments (dO^T, Q^T) are read
+//    from the row-major tiles with the LDS transpose load (ds_read_b64_tr_b16:
+//    a 16-lane group whose lanes point at 4 rows x 4 consecutive columns gets,
+//    per lane, one column's 4 rows).  An accumulator hands a lane the rows
+//    {4 gq .. 4 gq + 3, 8 + 4 gq .. 8 + 4 gq + 3} of each 16-wide k-step, so
+//    the two transpose loads of an A fragment start at rows 4 gq and 8 + 4 gq.
+//    Four waves: two key halves x two query-tile parities, merged through LDS
+//    at the end.  The lane's running column sums of dZ give the key-score,
+//    gain and temperature partials.
 //  * bwd_dq: a workgroup owns 32 (4/G) query rows of each of the G heads,
 //    keeps their Q and dO fragments in registers and walks the 32-key tiles
 //    up to the diagonal.  S^T = K Q^T and dP^T = V dO^T come out with one
-//    lane per query, so dZ^T is the B fragment of dQ^T += K^T dZ^T and c_i
-//    is applied once at the end.
+//    lane per query, so dZ^T is the B fragment of dQ^T += K^T dZ^T (K^T again
+//    by transpose loads) and c_i is applied once at the end.
 //  * bwd_reduce: db as the sum of the per-KV-head partials, dgain and dtemp
 //    as fixed-order sums of the per-block partials.  No atomics anywhere:
 //    the results are deterministic.
+// Tiles travel global -> LDS by buffer loads with the LDS-destination bit
+// into three-slot rings: the loads of step p + 2 are issued, between the
+// first and the second products of step p, while the matrix cores work.
 #include <math.h>
 
 #include "tg_device.h"
@@ -65,13 +67,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kRsrcCfg);
 }
 
-// Row held by slot s of a transposed 16-row group (self-inverse).
-__device__ __forceinline__ int slot_row(int s) {
-  const int q = (s >> 2) & 3;
-  const int kq = q == 1 ? 2 : (q == 2 ? 1 : q);
-  return (s & ~15) | (kq << 2) | (s & 3);
-}
-
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -91,88 +86,84 @@ template <int DH>
 __device__ __forceinline__ int row_tile_off(int r, int c) {
   return r * (2 * DH) + ((c ^ (r & 7)) << 4);
 }
-// ... and inside a staged [DH rows x 32] transposed tile (64-byte rows,
-// chunks swizzled by (d >> 2) & 3).
-__device__ __forceinline__ int tr_tile_off(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+// A fragment of X^T (rows d = 32 blk + (lane & 31), k = 16 tile rows) from a
+// staged row-major [32 x DH] tile X: two transpose loads, rows
+// 16 s + 4 gq + {0..3} then 16 s + 8 + 4 gq + {0..3} (the accumulator order
+// of the B fragment it meets).  Lane j of each 16-lane group points at row
+// base + (j >> 2), columns c0 + 4 (j & 3) .. + 3.
+template <int DH>
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int blk, int s, int lane) {
+  const int j = lane & 15, gq = lane >> 5;
+  const int col = 32 * blk + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  v4s h[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int row = 16 * s + 8 * hf + 4 * gq + (j >> 2);
+    const int off = row * (2 * DH) + (((col >> 3) ^ (row & 7)) << 4) + (((col >> 2) & 1) << 3);
+    h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(tile + off));
+  }
+  const u32x4 w = {__builtin_bit_cast(u32x2, h[0])[0], __builtin_bit_cast(u32x2, h[0])[1],
+                   __builtin_bit_cast(u32x2, h[1])[0], __builtin_bit_cast(u32x2, h[1])[1]};
+  return as_bf16x8(w);
+}
+
+// s_waitcnt vmcnt(N): at most N loads of this wave still in flight (loads
+// complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_loads_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Stages `n` 1 KiB DMA loads of a [32 x DH] row-major tile: load e fills LDS
+// slots 64 e + lane, slot Y holding row Y / (DH/8), chunk (Y % (DH/8)) ^ (row & 7).
+template <int DH>
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int row_bytes, int e,
+                                           int lane) {
+  constexpr int CH = DH / 8;
+  const int Y = e * 64 + lane;
+  const int row = Y / CH, c = (Y % CH) ^ (row & 7);
+  dma16(r, tile + e * 1024, row * row_bytes + c * 16, 0);
+}
 
 // ---------------------------------------------------------------------------
+// Per (query row, head): D_i = dO_i . O_i (fp32, fixed order: four threads per
+// row), c_i log2(e), lse_i log2(e); rows M .. Mp-1 get 0, +inf, 0.
 template <int DH>
-__global__ __launch_bounds__(kBwdThreads) void bwd_prepass_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ o,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const int32_t* __restrict__ pos,
-    const float* __restrict__ temp, float sm_scale, int M, int Mp, int Hq, int Hkv, uint16_t* __restrict__ qT,
-    uint16_t* __restrict__ doT, uint16_t* __restrict__ kTo, float* __restrict__ rowc, float* __restrict__ rowl,
-    float* __restrict__ rowD) {
-  constexpr int LS = DH + 2;  // LDS row stride in bf16 (odd word stride: conflict-free column reads)
-  constexpr int CH = DH / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t s_t[kPB * LS];
-  const int b = blockIdx.z, y = blockIdx.y, i0 = blockIdx.x * kPB;
-  const int tid = threadIdx.x;
-  const bool is_kv = y >= Hq;
-  const int hh = is_kv ? y - Hq : y;
-  const int H = is_kv ? Hkv : Hq;
-
-  // src rows (b, i0 .. i0 + 63, head hh) -> dst [b, hh, d, i0 + slot]; rows >= M give 0
-  auto transpose = [&](const uint16_t* src, uint16_t* dst) {
-    for (int c = tid; c < kPB * CH; c += kBwdThreads) {
-      const int r = c / CH, ch = c - (c / CH) * CH;
-      const int i = i0 + r;
-      const u32x4 v = i < M ? load16(src + (((size_t)b * M + i) * H + hh) * DH + ch * 8) : u32x4{0, 0, 0, 0};
-      uint32_t* wp = reinterpret_cast<uint32_t*>(s_t + r * LS + ch * 8);
-      wp[0] = v[0];
-      wp[1] = v[1];
-      wp[2] = v[2];
-      wp[3] = v[3];
-    }
-    __syncthreads();
-    uint16_t* base = dst + ((size_t)b * H + hh) * DH * Mp + i0;
-    for (int c = tid; c < DH * (kPB / 8); c += kBwdThreads) {
-      const int d = c / (kPB / 8), ch = c % (kPB / 8);
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = slot_row(ch * 8 + 2 * e), r1 = slot_row(ch * 8 + 2 * e + 1);
-        w[e] = (uint32_t)s_t[r0 * LS + d] | ((uint32_t)s_t[r1 * LS + d] << 16);
-      }
-      store16(base + (size_t)d * Mp + ch * 8, w);
-    }
-    __syncthreads();
-  };
-
-  if (is_kv) {
-    transpose(k, kTo);
-    return;
-  }
-  transpose(q, qT);
-  transpose(dout, doT);  // s_t keeps the dO block for D below
-
-  // D_i = dO_i . O_i: four threads per row, fixed order
-  const int r = tid >> 2, part = tid & 3;
-  const int i = i0 + r;
+__global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const int32_t* __restrict__ pos, const float* __restrict__ temp, float sm_scale, int M, int Mp, int Hq,
+    float* __restrict__ rowc, float* __restrict__ rowl, float* __restrict__ rowD) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int i = blockIdx.x * kPB + r;
   float acc = 0.0f;
   if (i < M) {
-    const uint16_t* op = o + (((size_t)b * M + i) * Hq + hh) * DH + part * (DH / 4);
-    const uint16_t* dp = s_t + r * LS + part * (DH / 4);
+    const size_t off = (((size_t)b * M + i) * Hq + h) * DH + part * (DH / 4);
 #pragma unroll
     for (int c = 0; c < DH / 32; ++c) {
-      const u32x4 ov = load16(op + c * 8);
+      const u32x4 ov = load16(o + off + c * 8), dv = load16(dout + off + c * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf16_lo(ov[e]), bf16_to_f32(dp[c * 8 + 2 * e]), acc);
-        acc = fmaf(bf16_hi(ov[e]), bf16_to_f32(dp[c * 8 + 2 * e + 1]), acc);
+        acc = fmaf(bf16_lo(ov[e]), bf16_lo(dv[e]), acc);
+        acc = fmaf(bf16_hi(ov[e]), bf16_hi(dv[e]), acc);
       }
     }
   }
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   if (part == 0) {
-    const size_t idx = ((size_t)b * Hq + hh) * Mp + i;
+    const size_t idx = ((size_t)b * Hq + h) * Mp + i;
     if (i < M) {
       const int p = pos[(size_t)b * M + i];
       float ratio = 1.0f;
       if (p != i) ratio = logf((float)max(p + 1, 2)) / logf((float)max(i + 1, 2));
-      rowc[idx] = sm_scale * kLog2e / (temp[hh] * ratio);
-      rowl[idx] = lse[((size_t)b * Hq + hh) * M + i] * kLog2e;
+      rowc[idx] = sm_scale * kLog2e / (temp[h] * ratio);
+      rowl[idx] = lse[((size_t)b * Hq + h) * M + i] * kLog2e;
       rowD[idx] = acc;
     } else {
       rowc[idx] = 0.0f;
@@ -186,22 +177,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prepass_kernel(
 template <int DH, int G>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ qT, const uint16_t* __restrict__ doT,
-    const float* __restrict__ rowc, const float* __restrict__ rowl, const float* __restrict__ rowD,
-    const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp, int Hq, int Hkv, int nkb,
-    int total_wg, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ dbp,
-    float* __restrict__ gpart, float* __restrict__ tpart) {
+    const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
+    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
+    int Hq, int Hkv, int nkb, int total_wg, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dbp, float* __restrict__ gpart, float* __restrict__ tpart) {
   constexpr int KS = DH / 16;       // k-steps over dh
   constexpr int DT = DH / 32;       // 32-row blocks of dK^T and dV^T
-  constexpr int CH = DH / 8;        // 16-byte chunks per row
   constexpr int TB = kT * DH * 2;   // bytes of a 32 x DH bf16 tile
-  constexpr int NI = TB / 1024;     // 1 KiB DMA instructions per tile
-  constexpr int RC = 4 * TB, RL = RC + 256, RD = RL + 256;
-  constexpr int UB = RD + 256;      // bytes of one staged unit (Q, dO, Q^T, dO^T, row constants)
+  constexpr int NI = TB / 1024;     // 1 KiB DMA loads per tile
+  constexpr int RC = 2 * TB, RL = RC + 256, RD = RL + 256;
+  constexpr int UB = RD + 256;      // bytes of one staged unit (Q, dO, row constants)
+  constexpr int NBUF = 3;
   constexpr int RED = 2 * DT * 2 * 16 * 64;  // floats of the parity merge area
-  static_assert(4 * UB >= (RED + 2 * 2 * G * 64) * 4, "merge area");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * UB];  // [buffer][parity] units
-  __shared__ float s_x[4 * G];
+  static_assert(NBUF * 2 * UB >= (RED + 2 * 2 * G * 64 + 4 * G) * 4, "merge area");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * 2 * UB];  // [slot][parity] units
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,43 +218,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     }
   }
   const float bj = j_ok ? kscore[(size_t)b * M + j] : 0.0f;
+  float kbias[G];  // gain_h log2(e) b_j of each head of the group
+#pragma unroll
+  for (int i = 0; i < G; ++i) kbias[i] = gain[g * G + i] * kLog2e * bj;
 
   // Unit u = 2 step + parity is staged by the two waves of that parity: key
-  // half 0 brings the row-major Q and dO tiles and the row constants, key
-  // half 1 the transposed tiles.
-  auto stage = [&](int step, int buf) __attribute__((always_inline)) {
+  // half 0 brings the Q tile and the row constants (NI + 3 loads), key half 1
+  // the dO tile (NI loads).  Rows >= M read 0.
+  auto stage = [&](int step) __attribute__((always_inline)) {
     const int u = 2 * step + par;
     if (u >= U) return;
     const int hl = u % G, t = t0 + u / G;
     const int h = g * G + hl;
-    unsigned char* base = smem + (buf * 2 + par) * UB;
+    unsigned char* base = smem + ((step % NBUF) * 2 + par) * UB;
+    const size_t row0 = (((size_t)b * M + t * kT) * Hq + h) * DH;
+    const int nrec = (int)(((long long)(M - 1 - t * kT) * Hq + 1) * DH * 2);
     if (kh == 0) {
-      const size_t row0 = (((size_t)b * M + t * kT) * Hq + h) * DH;
-      const int nrec = (int)(((long long)(M - 1 - t * kT) * Hq + 1) * DH * 2);  // rows >= M read 0
-      const auto rq = rsrc(q + row0, nrec), rdo = rsrc(dout + row0, nrec);
+      const auto rq = rsrc(q + row0, nrec);
 #pragma unroll
-      for (int e = 0; e < NI; ++e) {
-        const int Y = e * 64 + lane;
-        const int r = Y / CH, c = (Y % CH) ^ (r & 7);
-        const int voff = r * Hq * DH * 2 + c * 16;
-        dma16(rq, base + e * 1024, voff, 0);
-        dma16(rdo, base + TB + e * 1024, voff, 0);
-      }
+      for (int e = 0; e < NI; ++e) stage_rows<DH>(rq, base, Hq * DH * 2, e, lane);
       const size_t rr = ((size_t)b * Hq + h) * Mp + t * kT;  // 32 constants; lanes 32..63 read 0
       dma4(rsrc(rowc + rr, kT * 4), base + RC, lane * 4, 0);
       dma4(rsrc(rowl + rr, kT * 4), base + RL, lane * 4, 0);
       dma4(rsrc(rowD + rr, kT * 4), base + RD, lane * 4, 0);
     } else {
-      const size_t hb = ((size_t)b * Hq + h) * DH * Mp;
-      const auto rt = rsrc(qT + hb, DH * Mp * 2), rdt = rsrc(doT + hb, DH * Mp * 2);
+      const auto rdo = rsrc(dout + row0, nrec);
 #pragma unroll
-      for (int e = 0; e < NI; ++e) {
-        const int Y = e * 64 + lane;
-        const int d = Y >> 2, c = (Y & 3) ^ ((d >> 2) & 3);
-        const int voff = d * Mp * 2 + c * 16;
-        dma16(rt, base + 2 * TB + e * 1024, voff, t * kT * 2);
-        dma16(rdt, base + 3 * TB + e * 1024, voff, t * kT * 2);
-      }
+      for (int e = 0; e < NI; ++e) stage_rows<DH>(rdo, base + TB, Hq * DH * 2, e, lane);
     }
   };
 
@@ -278,27 +257,30 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < G; ++i) cs[i] = ta[i] = 0.0f;
 
-  stage(0, 0);
-  for (int p = 0; p < nsteps; ++p) {
-    wait_loads();
-    __syncthreads();  // step p is in LDS; every wave is done with the buffer step p + 1 reuses
-    if (p + 1 < nsteps) stage(p + 1, (p + 1) & 1);
-    const int u = 2 * p + par;
-    if (u >= U) continue;
-    const int hl = u % G, t = t0 + u / G;
-    if (t * kT + kT - 1 < kw0 || kw0 >= M) continue;  // every key of this wave lies above the tile
-    const unsigned char* base = smem + ((p & 1) * 2 + par) * UB;
-    const float kbh = gain[g * G + hl] * kLog2e * bj;
-
+  // One unit: S = Q K^T and dP = dO V^T, the softmax terms, then
+  // dV^T += dO^T P and dK^T += Q^T dS.  Fragments are read in batches ahead
+  // of their products.
+  auto step_dkdv = [&](const unsigned char* base, int hl, int t) __attribute__((always_inline)) {
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+    {
+      bf16x8 fq[KS], fd[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int off = row_tile_off<DH>(kl, 2 * s + gq);
-      S = mfma(lds_frag(base + off), kf[s], S);
-      dP = mfma(lds_frag(base + TB + off), vf[s], dP);
+      for (int s = 0; s < KS; ++s) {
+        const int off = row_tile_off<DH>(kl, 2 * s + gq);
+        fq[s] = lds_frag(base + off);
+        fd[s] = lds_frag(base + TB + off);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        S = mfma(fq[s], kf[s], S);
+        dP = mfma(fd[s], vf[s], dP);
+      }
     }
+    float kbh = kbias[0];
+#pragma unroll
+    for (int i = 1; i < G; ++i) kbh = i == hl ? kbias[i] : kbh;
     // rows of S and dP: queries t*32 + 8 i4 + 4 gq + jj; column: key j
     float Pv[16], Sv[16];
     float csum = 0.0f, tsum = 0.0f;
@@ -334,16 +316,37 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       const bf16x8 pb = pack8(Pv + 8 * s), sb = pack8(Sv + 8 * s);
 #pragma unroll
       for (int blk = 0; blk < DT; ++blk) {
-        const int off = tr_tile_off(32 * blk + kl, 2 * s + gq);
-        dVt[blk] = mfma(lds_frag(base + 3 * TB + off), pb, dVt[blk]);
-        dKt[blk] = mfma(lds_frag(base + 2 * TB + off), sb, dKt[blk]);
+        const bf16x8 fdo = tr_frag<DH>(base + TB, blk, s, lane), fqt = tr_frag<DH>(base, blk, s, lane);
+        dVt[blk] = mfma(fdo, pb, dVt[blk]);
+        dKt[blk] = mfma(fqt, sb, dKt[blk]);
       }
     }
-  }
+  };
 
+  stage(0);
+  stage(1);
+  for (int p = 0; p < nsteps; ++p) {
+    // step p's loads are done once at most step p + 1's remain in flight
+    if (2 * (p + 1) + par < U) {
+      if (kh == 0) wait_loads_le<NI + 3>();
+      else wait_loads_le<NI>();
+    } else {
+      wait_loads_le<0>();
+    }
+    __syncthreads();  // step p is in LDS; every wave is done with the slot step p + 2 reuses
+    const int u = 2 * p + par;
+    const int hl = u % G, t = t0 + u / G;
+    const bool run = u < U && t * kT + kT - 1 >= kw0 && kw0 < M;  // some key of this wave lies on/below the tile
+    const unsigned char* base = smem + ((p % NBUF) * 2 + par) * UB;
+    if (run) step_dkdv(base, hl, t);
+    // Issued after this step's transpose loads: the compiler makes an LDS
+    // transpose load wait for every LDS-destination load issued before it.
+    stage(p + 2);
+  }
   // ---- merge the two parities, write dK and dV, the key-score and scale partials ----
-  __syncthreads();  // the staging buffers are free
+  __syncthreads();  // the staging slots are free
   float* red = reinterpret_cast<float*>(smem);
+  float* s_x = red + RED + 2 * 2 * G * 64;  // per-wave sums of the two key halves
   float* mine = red + kh * (DT * 2 * 16 * 64);
   float* sums = red + RED + kh * (2 * G * 64);
   if (par == 1) {
@@ -418,19 +421,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 template <int DH, int G>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ kTi, const float* __restrict__ rowc,
-    const float* __restrict__ rowl, const float* __restrict__ rowD, const float* __restrict__ kscore,
-    const float* __restrict__ gain, int M, int Mp, int Hq, int Hkv, int nqb, int total_wg,
-    uint16_t* __restrict__ dq) {
+    const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
+    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
+    int Hq, int Hkv, int nqb, int total_wg, uint16_t* __restrict__ dq) {
   constexpr int RG = 4 / G;
   constexpr int BQ = 32 * RG;
-  constexpr int KS = DH / 16, DT = DH / 32, CH = DH / 8;
+  constexpr int KS = DH / 16, DT = DH / 32;
   constexpr int TB = kT * DH * 2;
   constexpr int NI = TB / 1024;
-  constexpr int BO = 3 * TB, UB = BO + 256;
-  constexpr int NX = 3 * NI / 4;  // DMA instructions per wave per tile (K, V, K^T)
-  static_assert(3 * NI % 4 == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * UB];
+  constexpr int BO = 2 * TB, UB = BO + 256;
+  constexpr int NBUF = 3;
+  constexpr int NX = 2 * NI / 4;  // DMA loads per wave per tile (K and V); wave 0 adds the key scores
+  static_assert(2 * NI % 4 == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NBUF * UB];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -463,12 +466,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 
   const uint16_t* kbase = k + ((size_t)b * M * Hkv + g) * DH;
   const uint16_t* vbase = v + ((size_t)b * M * Hkv + g) * DH;
-  const auto rkt = rsrc(kTi + ((size_t)b * Hkv + g) * DH * Mp, DH * Mp * 2);
   const auto rks = rsrc(kscore + (size_t)b * M, M * 4);
-  // Tile t: K, V (row-major, rows >= M read 0), K^T (transposed) and 64 key
-  // scores (those >= M read 0); instruction x = w + 4 n of the 3 NI.
-  auto stage = [&](int t, int buf) __attribute__((always_inline)) {
-    unsigned char* base = smem + buf * UB;
+  // Tile t: K and V rows (rows >= M read 0) and 64 key scores (those >= M
+  // read 0); load x = w + 4 n of the 2 NI goes to wave w.
+  auto stage = [&](int t) __attribute__((always_inline)) {
+    if (t >= ntk) return;
+    unsigned char* base = smem + (t % NBUF) * UB;
     const int nrec = (int)(((long long)(M - 1 - t * kT) * Hkv + 1) * DH * 2);
     const size_t roff = (size_t)t * kT * Hkv * DH;
     const auto rk = rsrc(kbase + roff, nrec), rv = rsrc(vbase + roff, nrec);
@@ -476,14 +479,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int n = 0; n < NX; ++n) {
       const int x = w + 4 * n;
       const int which = x / NI, e = x - (x / NI) * NI;
-      const int Y = e * 64 + lane;
-      if (which < 2) {
-        const int r = Y / CH, c = (Y % CH) ^ (r & 7);
-        dma16(which == 0 ? rk : rv, base + which * TB + e * 1024, r * Hkv * DH * 2 + c * 16, 0);
-      } else {
-        const int d = Y >> 2, c = (Y & 3) ^ ((d >> 2) & 3);
-        dma16(rkt, base + 2 * TB + e * 1024, d * Mp * 2 + c * 16, t * kT * 2);
-      }
+      stage_rows<DH>(which == 0 ? rk : rv, base + which * TB, Hkv * DH * 2, e, lane);
     }
     if (w == 0) dma4(rks, base + BO, (t * kT + lane) * 4, 0);
   };
@@ -494,21 +490,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQt[i][r] = 0.0f;
 
-  stage(0, 0);
-  for (int t = 0; t < ntk; ++t) {
-    wait_loads();
-    __syncthreads();
-    if (t + 1 < ntk) stage(t + 1, (t + 1) & 1);
-    if (qw0 >= M || t * kT > qw0 + 31) continue;  // no query of this wave reaches the tile
-    const unsigned char* base = smem + (t & 1) * UB;
+  auto step_dq = [&](const unsigned char* base, int t) __attribute__((always_inline)) {
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+    {
+      bf16x8 fk[KS], fv[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int off = row_tile_off<DH>(ql, 2 * s + gq);
-      S = mfma(lds_frag(base + off), qf[s], S);
-      dP = mfma(lds_frag(base + TB + off), df[s], dP);
+      for (int s = 0; s < KS; ++s) {
+        const int off = row_tile_off<DH>(ql, 2 * s + gq);
+        fk[s] = lds_frag(base + off);
+        fv[s] = lds_frag(base + TB + off);
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        S = mfma(fk[s], qf[s], S);
+        dP = mfma(fv[s], df[s], dP);
+      }
     }
     // rows of S^T and dP^T: keys t*32 + 8 i4 + 4 gq + jj; column: query qi
     float Z[16];
@@ -528,11 +526,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int s = 0; s < 2; ++s) {
       const bf16x8 zb = pack8(Z + 8 * s);
 #pragma unroll
-      for (int blk = 0; blk < DT; ++blk)
-        dQt[blk] = mfma(lds_frag(base + 2 * TB + tr_tile_off(32 * blk + ql, 2 * s + gq)), zb, dQt[blk]);
+      for (int blk = 0; blk < DT; ++blk) dQt[blk] = mfma(tr_frag<DH>(base, blk, s, lane), zb, dQt[blk]);
     }
-  }
+  };
 
+  const bool wave_rows = qw0 < M;
+  stage(0);
+  stage(1);
+  for (int t = 0; t < ntk; ++t) {
+    if (t + 1 < ntk) {
+      if (w == 0) wait_loads_le<NX + 1>();
+      else wait_loads_le<NX>();
+    } else {
+      wait_loads_le<0>();
+    }
+    __syncthreads();
+    const bool run = wave_rows && t * kT <= qw0 + 31;  // some query of this wave reaches the tile
+    if (run) step_dq(smem + (t % NBUF) * UB, t);
+    stage(t + 2);  // after this step's transpose loads (see the dK/dV kernel)
+  }
   if (q_ok) {
     const float sc = cq * kLn2;  // c_i (the exponent constant carries log2(e))
     uint16_t* qp = dq + (((size_t)b * M + qi) * Hq + h) * DH;
@@ -549,8 +561,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// db_j = sum over KV heads of the partials; the last block forms dgain and
-// dtemp from the per-(batch, key block) partials in a fixed order.
+// db_j = sum over KV heads of the partials.  The last block forms dgain and
+// dtemp: one wave per head, lanes over (batch, key block) partials, fp64 and
+// a fixed butterfly order.
 __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const float* __restrict__ dbp,
                                                                   const float* __restrict__ gpart,
                                                                   const float* __restrict__ tpart,
@@ -559,15 +572,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const float* __
                                                                   float* __restrict__ db, float* __restrict__ dgain,
                                                                   float* __restrict__ dtemp) {
   if (blockIdx.x == gridDim.x - 1) {
-    for (int h = threadIdx.x; h < Hq; h += blockDim.x) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int h = wv; h < Hq; h += kBwdThreads / 64) {
       double gs = 0.0, ts = 0.0;
-      for (int bi = 0; bi < B; ++bi)
-        for (int kb = 0; kb < nkb; ++kb) {
-          gs += gpart[((size_t)bi * nkb + kb) * Hq + h];
-          ts += tpart[((size_t)bi * nkb + kb) * Hq + h];
-        }
-      dgain[h] = (float)gs;
-      dtemp[h] = (float)(-(double)kLn2 * ts / (double)temp[h]);
+      for (int x = lane; x < B * nkb; x += 64) {
+        gs += gpart[(size_t)x * Hq + h];
+        ts += tpart[(size_t)x * Hq + h];
+      }
+      gs = wave_sum_f64(gs);
+      ts = wave_sum_f64(ts);
+      if (lane == 0) {
+        dgain[h] = (float)gs;
+        dtemp[h] = (float)(-(double)kLn2 * ts / (double)temp[h]);
+      }
     }
     return;
   }
@@ -586,11 +603,8 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint16_t* dk, uint16_t* dv, float* db, float* dgain, float* dtemp, void* ws, hipStream_t s) {
   const int Mp = (M + kPB - 1) / kPB * kPB;
   const int nkb = Mp / kKB;
-  const size_t qn = (size_t)B * Hq * DH * Mp, kn = (size_t)B * Hkv * DH * Mp, rn = (size_t)B * Hq * Mp;
-  uint16_t* qT = static_cast<uint16_t*>(ws);
-  uint16_t* doT = qT + qn;
-  uint16_t* kTw = doT + qn;
-  float* rowc = reinterpret_cast<float*>(kTw + kn);
+  const size_t rn = (size_t)B * Hq * Mp;
+  float* rowc = static_cast<float*>(ws);
   float* rowl = rowc + rn;
   float* rowD = rowl + rn;
   float* dbp = rowD + rn;
@@ -598,19 +612,19 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   float* tpart = gpart + (size_t)B * nkb * Hq;
 
   if (M > 0) {
-    hipLaunchKernelGGL((bwd_prepass_kernel<DH>), dim3(Mp / kPB, Hq + Hkv, B), dim3(kBwdThreads), 0, s, q, k, o, dout,
-                       lse, pos, temp, sm_scale, M, Mp, Hq, Hkv, qT, doT, kTw, rowc, rowl, rowD);
+    hipLaunchKernelGGL((bwd_rows_kernel<DH>), dim3(Mp / kPB, Hq, B), dim3(kBwdThreads), 0, s, o, dout, lse, pos,
+                       temp, sm_scale, M, Mp, Hq, rowc, rowl, rowD);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long ta = (long long)nkb * Hkv * B;
     const int nqb = (M + 32 * (4 / G) - 1) / (32 * (4 / G));
     const long long tb = (long long)nqb * Hkv * B;
     if (ta > 0x7FFFFFFF || tb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout, qT, doT,
-                       rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
+                       rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<DH, G>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout, kTw, rowc,
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, G>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
                        rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -624,14 +638,13 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 }  // namespace
 
-// Q^T and dO^T [B, Hq, dh, Mp] and K^T [B, Hkv, dh, Mp] (bf16), then fp32
-// c log2(e), lse log2(e) and D [B, Hq, Mp] each, the key-score partials
+// fp32 c log2(e), lse log2(e) and D [B, Hq, Mp] each, the key-score partials
 // [B, Hkv, Mp], and the gain and temperature partials [B, Mp/64, Hq] each.
 size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh) {
+  (void)dh;
   if (M <= 0) return 0;
   const size_t Mp = (size_t)(M + kPB - 1) / kPB * kPB;
-  return (size_t)B * Mp * ((size_t)(2 * Hq + Hkv) * dh * 2 + (size_t)3 * Hq * 4 + (size_t)Hkv * 4) +
-         (size_t)2 * B * (Mp / kKB) * Hq * 4;
+  return (size_t)B * Mp * ((size_t)3 * Hq * 4 + (size_t)Hkv * 4) + (size_t)2 * B * (Mp / kKB) * Hq * 4;
 }
 
 hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,

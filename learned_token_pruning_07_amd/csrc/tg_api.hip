@@ -66,9 +66,8 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     return tg::gated_attention_rope_workspace(B, N, h, d / K, K);
   }
   if (op == TG_OP_GATED_ATTENTION_BACKWARD) {
-    // N = M, d = Hkv * d_h, h = Hq, K = d_h: transposed Q, dO and K copies,
-    // per-row constants and the partial sums of the key-score, gain and
-    // temperature gradients
+    // N = M, d = Hkv * d_h, h = Hq, K = d_h: per-row constants and the
+    // partial sums of the key-score, gain and temperature gradients
     if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
     return tg::gated_attention_backward_workspace(B, N, h, d / K, K);
   }

@@ -202,7 +202,7 @@ def test_python_binding_refuses_cpu_tensors():
 def test_attention_backward_workspace_size(lib):
     for B, M, Hq, Hkv, dh in [(1, 3341, 16, 8, 128), (2, 100, 4, 4, 64), (1, 64, 8, 2, 128)]:
         Mp = (M + 63) // 64 * 64
-        want = B * Mp * (2 * (2 * Hq + Hkv) * dh + 12 * Hq + 4 * Hkv) + 8 * B * (Mp // 64) * Hq
+        want = B * Mp * (12 * Hq + 4 * Hkv) + 8 * B * (Mp // 64) * Hq
         assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, B, M, Hkv * dh, Hq, dh) == want
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 0, 1024, 16, 128) == 0
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 64, 1000, 16, 128) == 0  # d % d_h != 0

@@ -41,7 +41,7 @@ def _close(got, ref, l1, tol, what, floor=0.0):
         i = np.unravel_index(np.argmax(err - tol * scale - floor), err.shape)
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside {tol:.3g} x (L1 + |ref|); worst at "
                              f"{i}: got {got[i]!r} ref {ref[i]!r} L1 {np.asarray(l1)[i]!r}")
-    return float(np.max(err / np.maximum(scale, 1e-300))) if err.size else 0.0
+    return float(np.max(err / np.maximum(scale, floor / tol if floor else 1e-300))) if err.size else 0.0
 
 
 def _inputs(M, Hq, Hkv, dh, pos, B, seed):

@@ -96,12 +96,12 @@ def test_attention_4k():
     """Kept length 4096, 16q/8kv, d_h 128, N(0,1) Q/K/V, b seq-normed with 0 on the first 64, gain U(0.5,1.5), temp 1.2."""
     say("full size: attn_4k")
     c = wl.attn_case(seed=0, **wl.ATTN_4K)
-    b = tg.tg_seq_rmsnorm(dev(c.b_raw), 64)
+    bh = oracle.seq_rmsnorm(c.b_raw, 64, 1e-6).astype(np.float32)  # the attention's input, from the oracle
+    b = dev(bh)
     q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
     out, lse = tg.tg_gated_attention(q, k, v, b, dev(c.pos), dev(c.gain), dev(c.temp), c.sm_scale, want_lse=True)
     torch.cuda.synchronize()
     rows = _sample_rows(0, c.M, 192, [0, 63, 64, 65, 4095], seed=3)
-    bh = b.cpu().numpy()
     O, L = oracle.gated_attention(c.q, c.k, c.v, bh, c.pos, c.gain, c.temp, c.sm_scale, rows=rows)
     e1 = assert_close(wl.bf16_bits_to_f32(host_bits(out))[:, rows], O, TOL_BF16, "attn_4k O")
     e2 = assert_close(lse.cpu().numpy()[:, :, rows], L, TOL_LSE, "attn_4k lse")
@@ -114,17 +114,70 @@ def test_attention_rope_4k():
     rng = np.random.default_rng(11)
     pos = np.sort(rng.choice(32768, size=(1, 4096), replace=False), axis=1).astype(np.int32)
     c = wl.attn_case(seed=0, **dict(wl.ATTN_4K, pos=pos))
-    b = tg.tg_seq_rmsnorm(dev(c.b_raw), 64)
+    bh = oracle.seq_rmsnorm(c.b_raw, 64, 1e-6).astype(np.float32)
+    b = dev(bh)
     q, k, v = dev_bits(c.q), dev_bits(c.k), dev_bits(c.v)
     out, lse = tg.tg_gated_attention_rope(q, k, v, b, dev(c.pos), dev(c.gain), dev(c.temp), 1e6, c.sm_scale,
                                           want_lse=True)
     torch.cuda.synchronize()
     rows = _sample_rows(0, c.M, 128, [0, 63, 64, 65, 4095], seed=4)
-    bh = b.cpu().numpy()
     O, L = oracle.gated_attention_rope(c.q, c.k, c.v, bh, c.pos, c.gain, c.temp, c.sm_scale, 1e6, rows=rows)
     e1 = assert_close(wl.bf16_bits_to_f32(host_bits(out))[:, rows], O, TOL_BF16, "attn_4k rope O")
     e2 = assert_close(lse.cpu().numpy()[:, :, rows], L, TOL_LSE, "attn_4k rope lse")
     say(f"  attn_4k rope max|err| O {e1:.3g} lse {e2:.3g}")
+
+
+def test_attention_backward_4k():
+    """Backward at kept length 4096, 16q/8kv, d_h 128 (the attn_4k inputs, original positions spread over 32768,
+    a seeded N(0,1) upstream gradient), launched as the benchmark launches it.  The oracle differentiates the
+    first and the last KV-head group (query heads 0-1 and 14-15 with their KV head), which fixes d_q, d_k, d_v,
+    d_gain and d_temp of those heads exactly; d_key_score sums every head and is checked through shift
+    invariance: its sum over keys is sum_h gain_h sum_i dO_hi . (O_hi - bf16(O_hi)), which vanishes but for the
+    rounding of the O handed to the backward (fp32 noise allowed: 1e-4 of sum |d_key_score|)."""
+    from test_gpu_backward import TOL_GRAD_BF16, TOL_F32_SUMS, _close
+    say("full size: attention backward 4k")
+    rng = np.random.default_rng(21)
+    pos = np.concatenate([np.arange(64), np.sort(rng.choice(np.arange(64, 32768), 4096 - 64, replace=False))])
+    c = wl.attn_case(seed=0, **dict(wl.ATTN_4K, pos=pos[None].astype(np.int32)))
+    bh = oracle.seq_rmsnorm(c.b_raw, 64, 1e-6).astype(np.float32)
+    dO = wl.f32_to_bf16_bits(wl.make_rng(22).standard_normal(c.q.shape, dtype=np.float32))
+    # forward outputs from the oracle, per KV-head group (the groups are independent)
+    G = c.Hq // c.Hkv
+    O_bits = np.zeros(c.q.shape, np.uint16)
+    L = np.zeros((1, c.Hq, c.M), np.float32)
+    sl = lambda g: (slice(g * G, (g + 1) * G), slice(g, g + 1))  # noqa: E731
+    db_sum = 0.0
+    for g in range(c.Hkv):
+        hq, hk = sl(g)
+        O, Lg = oracle.gated_attention(c.q[:, :, hq], c.k[:, :, hk], c.v[:, :, hk], bh, c.pos, c.gain[hq],
+                                       c.temp[hq], c.sm_scale)
+        O_bits[:, :, hq] = oracle.bf16_round(O)
+        L[:, hq] = Lg
+        dev_o = np.sum(oracle.widen(dO[:, :, hq]) * (O - oracle.widen(O_bits[:, :, hq])), axis=(0, 1, 3))
+        db_sum += float(np.sum(c.gain[hq].astype(np.float64) * dev_o))
+    got = tg.tg_gated_attention_backward(dev_bits(c.q), dev_bits(c.k), dev_bits(c.v), dev_bits(O_bits), dev(L),
+                                         dev_bits(dO), dev(bh), dev(c.pos), dev(c.gain), dev(c.temp), c.sm_scale)
+    torch.cuda.synchronize()
+    dq, dk, dv, db, dgain, dtemp = [x.cpu() for x in got]
+    f = lambda t: wl.bf16_bits_to_f32(t.view(torch.int16).numpy().view(np.uint16))  # noqa: E731
+    for g in (0, c.Hkv - 1):
+        hq, hk = sl(g)
+        args = (c.q[:, :, hq], c.k[:, :, hk], c.v[:, :, hk], bh, c.pos, c.gain[hq], c.temp[hq], c.sm_scale,
+                O_bits[:, :, hq], L[:, hq], dO[:, :, hq])
+        want = oracle.gated_attention_backward(*args)
+        l1 = oracle.gated_attention_backward_l1(*args)
+        floor = 2.0 ** -16 * float(np.sqrt(np.mean(l1[2] ** 2)))
+        e = [_close(f(dq)[:, :, hq], want[0], l1[0], TOL_GRAD_BF16, f"4k group {g} d_q", floor),
+             _close(f(dk)[:, :, hk], want[1], l1[1], TOL_GRAD_BF16, f"4k group {g} d_k", floor),
+             _close(f(dv)[:, :, hk], want[2], l1[2], TOL_GRAD_BF16, f"4k group {g} d_v", floor),
+             _close(dgain.numpy()[hq], want[4], l1[4], TOL_F32_SUMS, f"4k group {g} d_gain", floor),
+             _close(dtemp.numpy()[hq], want[5], l1[5], TOL_F32_SUMS, f"4k group {g} d_temp", floor)]
+        say(f"  group {g}: max err/(L1+|ref|) dq {e[0]:.2e} dk {e[1]:.2e} dv {e[2]:.2e} dgain {e[3]:.2e} "
+            f"dtemp {e[4]:.2e}")
+    dbh = db.numpy().astype(np.float64)
+    assert np.all(np.isfinite(dbh))
+    assert abs(dbh.sum() - db_sum) <= 1e-4 * np.abs(dbh).sum(), (dbh.sum(), db_sum, np.abs(dbh).sum())
+    say(f"  d_key_score: sum {dbh.sum():.4g} (expected {db_sum:.4g}), sum |.| {np.abs(dbh).sum():.4g}")
 
 
 def test_stage_32k():
