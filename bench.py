@@ -133,6 +133,40 @@ def time_backward(torch, tg, qkv, b_S, kept_idx, layer, attn_out, heads, M, stre
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "shape": {"M": M, "Hq": Hq, "Hkv": Hkv, "d_h": dh}}
 
 
+STAGE_GATE_LAYER = 4  # the stage workload's gate layer L: layers 0..L hold full-length KV caches
+
+
+def time_kv_prune(torch, tg, kept_idx, N, M, heads, n_layers, reps=20):
+    """Post-prefill pruning of the K/V caches of layers 0..L (seeded bf16
+    caches of the prompt length N) to the stage's kept set, timed on its own
+    (it runs once after prefill, outside the step).  Algorithmic bytes: every
+    kept row read once and written once, K and V, every layer."""
+    Hkv, dh = heads["Hkv"], heads["dh"]
+    g = torch.Generator(device=kept_idx.device).manual_seed(4321)
+    shape = (n_layers, 1, N, Hkv, dh)
+    kc = torch.randn(shape, generator=g, device=kept_idx.device).bfloat16()
+    vc = torch.randn(shape, generator=g, device=kept_idx.device).bfloat16()
+    ko = torch.empty((n_layers, 1, M, Hkv, dh), dtype=torch.bfloat16, device=kept_idx.device)
+    vo = torch.empty_like(ko)
+    call = lambda: tg.tg_kv_cache_prune(kc, vc, kept_idx, k_out=ko, v_out=vo)  # noqa: E731
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nbytes = 2 * 2 * n_layers * M * Hkv * dh * 2 + 4 * M * 2 * n_layers
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del kc, vc
+    return {"call": "tg_kv_cache_prune", "avg_us": round(us, 3), "calls_timed": reps, "layers": n_layers,
+            "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "shape": {"N": N, "M": M, "Hkv": Hkv, "d_h": dh}}
+
+
 def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -182,6 +216,8 @@ def main():
                     help="capture each phase of a step as a HIP graph once and replay it (slower on this ROCm: "
                          "a replay costs several microseconds more than direct launches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv-prune", action="store_true",
+                    help="skip the separate timing of tg_kv_cache_prune (layers 0..L of the stage)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of tg_gated_attention_backward at the attention shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -421,6 +457,10 @@ def main():
         out["attention_backward"] = time_backward(torch, tg, qkv[0], b_S, kept_idx, layers[0], attn_out, heads, M,
                                                   stream_reps=20)
         log(f"attention backward: {out['attention_backward']['avg_us']:.2f} us per call")
+
+    if layers and not args.no_kv_prune and args.workload == "stage_32k":
+        out["kv_cache_prune"] = time_kv_prune(torch, tg, kept_idx, N, M, heads, n_layers=STAGE_GATE_LAYER + 1)
+        log(f"kv cache prune: {out['kv_cache_prune']['avg_us']:.2f} us per call")
 
     if not args.no_cpu_baseline and layers:
         log("timing the CPU oracle on a bounded sample")

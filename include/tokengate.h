@@ -288,6 +288,26 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v,
                                 float* d_gain, float* d_temp, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/*
+ * tg_kv_cache_prune -- post-prefill pruning of the KV cache of the layers at
+ * and below the gate (paper, Section 5, "Implementation and timing", and
+ * Appendix B: optionally, once prefill completes, those layers keep only the
+ * selected tokens, so that decoding holds the same kept entries at every
+ * layer).  For every layer l < n_layers and batch row b:
+ *     k_out[l, b, m] = k_cache[l, b, kept_idx[b, m]]   (and the same for v)
+ *
+ *   k_cache, v_cache [n_layers, B, N, Hkv, d_h] two-byte values (bf16)
+ *   kept_idx [B, M] int32: the kept set of tg_compact / tg_gate_select,
+ *                    ascending original indices (any order is accepted)
+ *   k_out, v_out [n_layers, B, M, Hkv, d_h]: the caller's buffers (they may
+ *                    not overlap the caches); rows are copied bit for bit
+ *   M in [0, N]; d_h a multiple of 8.  An index outside [0, N) leaves its
+ *   output row unwritten.  n_layers == 0 or M == 0 enqueue nothing.
+ */
+int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers,
+                      int B, int N, int Hkv, int d_h, const int32_t* kept_idx,
+                      int M, void* k_out, void* v_out, void* stream);
+
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
  * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
  * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq).

@@ -25,7 +25,7 @@ TG_F32, TG_BF16 = 0, 1
  TG_OP_GATED_ATTENTION_ROPE, TG_OP_GATED_ATTENTION_BACKWARD) = range(8)
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
-            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_kv_cache_prune", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -56,6 +56,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                             vp, sz, vp]
     lib.tg_gated_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp,
                                                 vp, vp, vp, vp, sz, vp]
+    lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
@@ -63,7 +64,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_version.argtypes = []
     lib.tg_version.restype = i
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
-                 "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward"):
+                 "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
+                 "tg_kv_cache_prune"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -387,6 +389,31 @@ def tg_gated_attention_backward(q, k, v, out, lse, d_out, key_score, pos, gain, 
         _ptr(gain), _ptr(temp), float(sm_scale), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_key_score), _ptr(d_gain),
         _ptr(d_temp), _ptr(ws), ws.numel(), _stream(stream)))
     return d_q, d_k, d_v, d_key_score, d_gain, d_temp
+
+
+def tg_kv_cache_prune(k_cache, v_cache, kept_idx, k_out=None, v_out=None, stream=None):
+    """Keep only the kept set in the K/V caches of the layers at and below the
+    gate: caches ``[layers, B, N, Hkv, dh]`` (2-byte elements), ``kept_idx
+    [B, M]`` int32 -> ``(k_out, v_out)`` ``[layers, B, M, Hkv, dh]``."""
+    lib = load_library()
+    _need(k_cache, "k_cache")
+    if k_cache.dim() != 5 or k_cache.element_size() != 2:
+        raise ValueError("k_cache must be [layers, B, N, Hkv, dh] with 2-byte elements")
+    L, B, N, Hkv, dh = k_cache.shape
+    _need(v_cache, "v_cache", k_cache.dtype, (L, B, N, Hkv, dh))
+    _need(kept_idx, "kept_idx", torch.int32)
+    if kept_idx.dim() != 2 or kept_idx.shape[0] != B:
+        raise ValueError("kept_idx must be [B, M]")
+    M = kept_idx.shape[1]
+    if k_out is None:
+        k_out = torch.empty((L, B, M, Hkv, dh), dtype=k_cache.dtype, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((L, B, M, Hkv, dh), dtype=k_cache.dtype, device=k_cache.device)
+    _need(k_out, "k_out", k_cache.dtype, (L, B, M, Hkv, dh))
+    _need(v_out, "v_out", k_cache.dtype, (L, B, M, Hkv, dh))
+    _check(lib.tg_kv_cache_prune(_ptr(k_cache), _ptr(v_cache), L, B, N, Hkv, dh, _ptr(kept_idx), M, _ptr(k_out),
+                                 _ptr(v_out), _stream(stream)))
+    return k_out, v_out
 
 
 def tg_workspace_size(op: int, B: int, N: int, d: int, h: int, K: int) -> int:

@@ -1,0 +1,70 @@
+// Post-prefill pruning of the KV cache of the layers at and below the gate
+// (TokenGate paper, Section 5, "Implementation and timing", with Appendix B:
+// once prefill is done, the KV cache of every layer l <= L may keep only the
+// selected tokens, so that decoding holds the same kept entries at every
+// layer).  A row gather for each layer and each of K and V:
+//     out[l][b, m] = cache[l][b, kept_idx[b, m]]
+// with rows of Hkv * d_h two-byte values.  One launch covers every layer and
+// both caches (grid z = 2 * layers); each thread moves kUnroll 16-byte chunks
+// spaced one workgroup apart, all loads in flight before the stores.
+#include "tg_device.h"
+#include "tg_internal.h"
+
+namespace tg {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void kv_prune_kernel(const uint8_t* __restrict__ k_cache,
+                                                            const uint8_t* __restrict__ v_cache, size_t row_bytes,
+                                                            int B, int N, int M, const int32_t* __restrict__ kept_idx,
+                                                            uint8_t* __restrict__ k_out, uint8_t* __restrict__ v_out) {
+  const int z = blockIdx.z;
+  const int l = z >> 1;
+  const bool is_v = (z & 1) != 0;
+  const int b = blockIdx.y;
+  const size_t cpr = row_bytes / 16;
+  const size_t total = (size_t)M * cpr;
+  const int32_t* ki = kept_idx + (size_t)b * M;
+  const uint8_t* src = (is_v ? v_cache : k_cache) + ((size_t)l * B + b) * (size_t)N * row_bytes;
+  uint8_t* dst = (is_v ? v_out : k_out) + ((size_t)l * B + b) * (size_t)M * row_bytes;
+  const size_t c0 = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  u32x4 v[kUnroll];
+  size_t off_out[kUnroll];
+  bool ok[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const size_t c = c0 + (size_t)u * kThreads;
+    ok[u] = c < total;
+    if (ok[u]) {
+      const size_t m = c / cpr, part = c - m * cpr;
+      const int32_t j = ki[m];
+      ok[u] = (uint32_t)j < (uint32_t)N;  // an index outside [0, N) leaves its row unwritten
+      if (ok[u]) v[u] = load16_stream(src + (size_t)j * row_bytes + part * 16);
+      off_out[u] = m * row_bytes + part * 16;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (ok[u]) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + off_out[u]));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, int B, int N, int Hkv,
+                                 int dh, const int32_t* kept_idx, int M, void* k_out, void* v_out, hipStream_t s) {
+  if (M <= 0 || n_layers <= 0) return hipSuccess;
+  const size_t row_bytes = (size_t)Hkv * dh * 2;
+  const size_t total = (size_t)M * (row_bytes / 16);
+  const size_t per_block = (size_t)kThreads * kUnroll;
+  const size_t grid = (total + per_block - 1) / per_block;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_prune_kernel, dim3((unsigned)grid, B, 2 * n_layers), dim3(kThreads), 0, s,
+                     static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), row_bytes, B, N, M,
+                     kept_idx, static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
+  return hipGetLastError();
+}
+
+}  // namespace tg

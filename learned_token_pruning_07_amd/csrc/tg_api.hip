@@ -287,4 +287,20 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v, con
       name);
 }
 
+int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, int B, int N, int Hkv, int d_h,
+                      const int32_t* kept_idx, int M, void* k_out, void* v_out, void* stream) {
+  const char* name = "tg_kv_cache_prune";
+  if (n_layers < 0 || n_layers > 32767 || B <= 0 || B > 65535 || N <= 0 || Hkv <= 0 || d_h <= 0)
+    return fail(TG_EINVAL, "%s: bad sizes", name);
+  if (d_h % 8 != 0) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not a multiple of 8", name, d_h);
+  if (M < 0 || M > N) return fail(TG_EINVAL, "%s: M=%d outside [0, N=%d]", name, M, N);
+  if (M == 0 || n_layers == 0) return TG_OK;
+  if (!k_cache || !v_cache || !kept_idx || !k_out || !v_out) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out) || !aligned4(kept_idx))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  return hip_status(tg::launch_kv_cache_prune(k_cache, v_cache, n_layers, B, N, Hkv, d_h, kept_idx, M, k_out, v_out,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
 }  // extern "C"

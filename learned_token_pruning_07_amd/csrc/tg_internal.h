@@ -67,4 +67,8 @@ hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k,
                                            float* d_temp, void* ws, hipStream_t s);
 size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh);
 
+// Row gather of the K and V caches of n_layers layers to the kept set.
+hipError_t launch_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, int B, int N, int Hkv,
+                                 int dh, const int32_t* kept_idx, int M, void* k_out, void* v_out, hipStream_t s);
+
 }  // namespace tg

@@ -11,6 +11,7 @@ from .tokengate_ref import (  # noqa: F401
     gated_attention_rope,
     gated_attention_backward,
     gated_attention_backward_l1,
+    kv_cache_prune,
     bf16_round,
     rope,
     rope_inv_freq,

@@ -432,3 +432,26 @@ def gated_attention_backward_l1(q, k, v, b_S, pos, gain, temp, sm_scale: float, 
             out[4][h] += float(col @ np.abs(b[bi]))
             out[5][h] += float(np.sum(aS * np.abs(S))) / t[h]
     return tuple(out)
+
+
+# --------------------------------------------------------------------------
+# Post-prefill KV-cache pruning of the layers at and below the gate.  Paper,
+# Section 5, "Implementation and timing" (with Appendix B): once prefill is
+# done, the KV cache of every layer l <= L may keep only the selected tokens,
+# so that decoding holds the same kept entries at every layer.  The plain
+# definition: a row gather of each layer's K and V cache by the kept set.
+# --------------------------------------------------------------------------
+def kv_cache_prune(k_cache, v_cache, kept_idx):
+    """``k_cache, v_cache [layers, B, N, Hkv, dh]`` (any dtype, rows copied as
+    they are), ``kept_idx [B, M]`` -> ``(k_out, v_out) [layers, B, M, Hkv, dh]``."""
+    k_cache = np.asarray(k_cache)
+    v_cache = np.asarray(v_cache)
+    idx = np.asarray(kept_idx)
+    L, B = k_cache.shape[:2]
+    M = idx.shape[1]
+    k_out = np.empty((L, B, M) + k_cache.shape[3:], k_cache.dtype)
+    v_out = np.empty_like(k_out)
+    for b in range(B):
+        k_out[:, b] = k_cache[:, b, idx[b]]
+        v_out[:, b] = v_cache[:, b, idx[b]]
+    return k_out, v_out

@@ -232,3 +232,22 @@ def test_attention_backward_validation(lib):
     assert call(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(ws=NULL) == tgb.TG_EINVAL
     assert call(M=1 << 20, Hq=64, Hkv=16) == tgb.TG_EUNSUPPORTED  # a 32-bit buffer range would overflow
+
+
+def test_kv_cache_prune_validation(lib):
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, L=5, B=1, N=100, H=8, dh=128, idx=FAKE, M=10, ko=FAKE, vo=FAKE)
+        a.update(kw)
+        return lib.tg_kv_cache_prune(a["k"], a["v"], a["L"], a["B"], a["N"], a["H"], a["dh"], a["idx"], a["M"],
+                                     a["ko"], a["vo"], None)
+
+    assert call(M=101) == tgb.TG_EINVAL and "outside" in _err(lib)
+    assert call(M=-1) == tgb.TG_EINVAL
+    assert call(dh=12) == tgb.TG_EUNSUPPORTED
+    assert call(L=-1) == tgb.TG_EINVAL and call(B=0) == tgb.TG_EINVAL and call(N=0) == tgb.TG_EINVAL
+    for name in ("k", "v", "idx", "ko", "vo"):
+        assert call(**{name: NULL}) == tgb.TG_EINVAL, name
+    assert call(ko=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+    # nothing to do: no GPU call is made
+    assert call(M=0, k=NULL) == tgb.TG_OK
+    assert call(L=0, k=NULL) == tgb.TG_OK
