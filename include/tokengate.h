@@ -181,6 +181,38 @@ int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, i
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same four steps with the prunable document anywhere in the prompt.
+ * The paper's prompt is x = [x_R, x_D] (Section 3); its public interface
+ * marks the prunable document with a placeholder inside the prompt (page 3),
+ * so text may also follow the document.  These entry points take the
+ * prunable span [span_begin, span_end) of every batch row in place of r.
+ * Every token outside the span is non-prunable: its score is 0 and it is
+ * always kept.  The kept set holds N - P + min(K, P) tokens, P = span_end -
+ * span_begin, in ascending original order: first the tokens before the span,
+ * then the kept span tokens, then the tokens after it.  The tokens after the
+ * span occupy the last N - span_end ranks of kept_idx and score_out.
+ * Arguments, workspaces and errors are otherwise those of the entry point
+ * without the suffix.  The plain entry points are the case span_end == N,
+ * bit for bit.  Requires 0 <= span_begin <= span_end <= N.
+ */
+int tg_gate_score_span(const void* resid, int dt, int B, int N, int d,
+                       int span_begin, int span_end, const void* norm_w,
+                       float eps_row, const void* W1, const float* b1, int h,
+                       const void* w2, const float* b2, float* score_raw,
+                       void* ws, size_t ws_bytes, void* stream);
+int tg_seq_rmsnorm_span(const float* score_raw, int B, int N, int span_begin,
+                        int span_end, float eps_seq, float* score, void* ws,
+                        size_t ws_bytes, void* stream);
+int tg_topk_select_span(const float* score, int B, int N, int span_begin,
+                        int span_end, int K, uint8_t* keep, void* ws,
+                        size_t ws_bytes, void* stream);
+int tg_gate_select_span(const float* score_raw, int B, int N, int span_begin,
+                        int span_end, float eps_seq, int K, const void* resid,
+                        int dt, int d, float* score, uint8_t* keep,
+                        int32_t* kept_idx, void* resid_out, float* score_out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tg_gated_attention -- token-gated causal GQA attention over the kept set
  * (paper Section 4: token-gated attention Eq. 5, head-wise gain Eq. 6,
  * temperature Eq. 7, combined as the key-bias form Eq. 8; Appendix C.4).

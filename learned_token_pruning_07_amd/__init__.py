@@ -25,7 +25,8 @@ TG_F32, TG_BF16 = 0, 1
  TG_OP_GATED_ATTENTION_ROPE, TG_OP_GATED_ATTENTION_BACKWARD) = range(8)
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
-            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_kv_cache_prune", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
+            "tg_topk_select_span", "tg_gate_select_span", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -57,6 +58,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gated_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp,
                                                 vp, vp, vp, vp, sz, vp]
     lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
+    lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
+    lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
+    lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
     lib.tg_last_error.argtypes = []
@@ -65,7 +70,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_version.restype = i
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
-                 "tg_kv_cache_prune"):
+                 "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
+                 "tg_gate_select_span"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -116,8 +122,9 @@ def gate_workspace(h: int, d: int, device="cuda") -> torch.Tensor:
 
 
 def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None, ws=None,
-                  stream=None):
-    """Row RMSNorm + scoring MLP -> raw scores ``[B, N]`` fp32 (0 for j < r).
+                  stream=None, span_end: int | None = None):
+    """Row RMSNorm + scoring MLP -> raw scores ``[B, N]`` fp32 (0 outside the
+    prunable span ``[r, span_end)``; ``span_end`` None means N).
 
     ``ws`` is a uint8 GPU tensor from :func:`gate_workspace` (allocated here
     when omitted)."""
@@ -136,8 +143,12 @@ def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, 
     if ws is None:
         ws = gate_workspace(h, d, resid.device)
     _need(ws, "ws", torch.uint8)
-    _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, _ptr(norm_w), eps_row, _ptr(W1), _ptr(b1), h,
-                             _ptr(w2), _ptr(b2), _ptr(score_raw), _ptr(ws), ws.numel(), _stream(stream)))
+    rest = (_ptr(norm_w), eps_row, _ptr(W1), _ptr(b1), h, _ptr(w2), _ptr(b2), _ptr(score_raw), _ptr(ws), ws.numel(),
+            _stream(stream))
+    if span_end is None:
+        _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, *rest))
+    else:
+        _check(lib.tg_gate_score_span(_ptr(resid), _dt(resid), B, N, d, r, span_end, *rest))
     return score_raw
 
 
@@ -163,8 +174,10 @@ def _ws_args(ws):
     return _ptr(ws), ws.numel()
 
 
-def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, ws=None, stream=None):
-    """Sequence RMSNorm of the raw scores -> ``[B, N]`` fp32 (0 for j < r).
+def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, ws=None, stream=None,
+                   span_end: int | None = None):
+    """Sequence RMSNorm of the raw scores -> ``[B, N]`` fp32 (0 outside the
+    prunable span ``[r, span_end)``; ``span_end`` None means N).
 
     ``ws``: from :func:`seq_rmsnorm_workspace` (allocated here when needed and omitted)."""
     lib = load_library()
@@ -176,12 +189,17 @@ def tg_seq_rmsnorm(score_raw, r: int, eps_seq: float = 1e-6, score=None, ws=None
     if ws is None:
         ws = seq_rmsnorm_workspace(B, N, score_raw.device)
     wp, wn = _ws_args(ws)
-    _check(lib.tg_seq_rmsnorm(_ptr(score_raw), B, N, r, eps_seq, _ptr(score), wp, wn, _stream(stream)))
+    if span_end is None:
+        _check(lib.tg_seq_rmsnorm(_ptr(score_raw), B, N, r, eps_seq, _ptr(score), wp, wn, _stream(stream)))
+    else:
+        _check(lib.tg_seq_rmsnorm_span(_ptr(score_raw), B, N, r, span_end, eps_seq, _ptr(score), wp, wn,
+                                       _stream(stream)))
     return score
 
 
-def tg_topk_select(score, r: int, K: int, keep=None, ws=None, stream=None):
-    """Keep mask ``[B, N]`` uint8 with r + min(K, N - r) ones per row.
+def tg_topk_select(score, r: int, K: int, keep=None, ws=None, stream=None, span_end: int | None = None):
+    """Keep mask ``[B, N]`` uint8 with :func:`kept_count` ones per row (the
+    prunable span is ``[r, span_end)``; ``span_end`` None means N).
 
     ``ws``: from :func:`topk_workspace` (allocated here when needed and omitted)."""
     lib = load_library()
@@ -193,13 +211,18 @@ def tg_topk_select(score, r: int, K: int, keep=None, ws=None, stream=None):
     if ws is None:
         ws = topk_workspace(B, N, score.device)
     wp, wn = _ws_args(ws)
-    _check(lib.tg_topk_select(_ptr(score), B, N, r, K, _ptr(keep), wp, wn, _stream(stream)))
+    if span_end is None:
+        _check(lib.tg_topk_select(_ptr(score), B, N, r, K, _ptr(keep), wp, wn, _stream(stream)))
+    else:
+        _check(lib.tg_topk_select_span(_ptr(score), B, N, r, span_end, K, _ptr(keep), wp, wn, _stream(stream)))
     return keep
 
 
-def kept_count(N: int, r: int, K: int) -> int:
-    """M = r + min(K, N - r): the number of kept tokens per sequence."""
-    return r + max(0, min(K, N - r))
+def kept_count(N: int, r: int, K: int, span_end: int | None = None) -> int:
+    """M = N - P + min(K, P), P = span_end - r (N - r by default): the number
+    of kept tokens per sequence."""
+    P = (N if span_end is None else span_end) - r
+    return N - P + max(0, min(K, P))
 
 
 def tg_compact(resid, keep, score, M: int, kept_idx=None, resid_out=None, score_out=None, stream=None):
@@ -233,7 +256,7 @@ def gate_select_workspace(B: int, N: int, device="cuda") -> torch.Tensor | None:
 
 
 def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, score=None, keep=None, kept_idx=None,
-                   resid_out=None, score_out=None, ws=None, stream=None):
+                   resid_out=None, score_out=None, ws=None, stream=None, span_end: int | None = None):
     """tg_seq_rmsnorm, tg_topk_select and tg_compact in one call (bit-identical results).
 
     Returns ``(kept_idx [B, M] int32, resid_out [B, M, d], score_out [B, M] fp32, keep [B, N] uint8,
@@ -245,7 +268,7 @@ def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, scor
     B, N, d = resid.shape
     _need(score_raw, "score_raw", torch.float32, (B, N))
     dev = resid.device
-    M = kept_count(N, r, K)
+    M = kept_count(N, r, K, span_end)
     if score is None:
         score = torch.empty((B, N), dtype=torch.float32, device=dev)
     if keep is None:
@@ -264,8 +287,12 @@ def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, scor
     if ws is None:
         ws = gate_select_workspace(B, N, dev)
     wp, wn = _ws_args(ws)
-    _check(lib.tg_gate_select(_ptr(score_raw), B, N, r, eps_seq, K, _ptr(resid), _dt(resid), d, _ptr(score),
-                              _ptr(keep), _ptr(kept_idx), _ptr(resid_out), _ptr(score_out), wp, wn, _stream(stream)))
+    rest = (eps_seq, K, _ptr(resid), _dt(resid), d, _ptr(score), _ptr(keep), _ptr(kept_idx), _ptr(resid_out),
+            _ptr(score_out), wp, wn, _stream(stream))
+    if span_end is None:
+        _check(lib.tg_gate_select(_ptr(score_raw), B, N, r, *rest))
+    else:
+        _check(lib.tg_gate_select_span(_ptr(score_raw), B, N, r, span_end, *rest))
     return kept_idx, resid_out, score_out, keep, score
 
 

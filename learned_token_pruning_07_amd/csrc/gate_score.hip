@@ -1,7 +1,10 @@
 // Row RMSNorm + scoring MLP (TokenGate paper, Section 4, "Scoring Network",
 // Eq. 1 and the first half of Eq. 3; Appendix C.4): for every prunable token j
 //     a~_j = a_j * w / sqrt(mean(a_j^2) + eps),   b~_j = w2 . silu(W1 a~_j + b1) + b2
-// and b~_j = 0 for the non-prunable tokens j < r.
+// and b~_j = 0 for the non-prunable tokens: those before the prunable span
+// [r, p1) (the question x_R) and, when the document is followed by more
+// non-prunable text, those after it (the span's end p1 is N for a prompt
+// [x_R, x_D]).
 //
 // bf16 path (the HBM-bound one):
 //  * A prepass folds the RMSNorm weight into the first layer once per call,
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void fold_norm_weight_kernel(const uint16
 
 template <int H, int ROWS, int WAVES, int NCH_FIXED>
 __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
-                                                                   int d, int r, float eps_row,
+                                                                   int d, int r, int p1, float eps_row,
                                                                    const uint16_t* __restrict__ W1w,
                                                                    const float* __restrict__ b1,
                                                                    const uint16_t* __restrict__ w2,
@@ -99,11 +102,12 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
   float* ob = out + (size_t)b * N;
 
   for (int j = blockIdx.x * THREADS + tid; j < r; j += gridDim.x * THREADS) ob[j] = 0.0f;
-  if (row0 >= N) return;  // whole workgroup: no barrier is skipped by part of it
+  for (int j = p1 + blockIdx.x * THREADS + tid; j < N; j += gridDim.x * THREADS) ob[j] = 0.0f;
+  if (row0 >= p1) return;  // whole workgroup: no barrier is skipped by part of it
 
-  // residual tile: rows past N read as 0 through the buffer range check
+  // residual tile: rows past the span read as 0 through the buffer range check
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(resid + ((size_t)b * N + row0) * d), (short)0, (int)((size_t)(N - row0) * d * 2),
+      const_cast<uint16_t*>(resid + ((size_t)b * N + row0) * d), (short)0, (int)((size_t)(p1 - row0) * d * 2),
       kBufferConfig);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W1w), (short)0, (int)((size_t)H * d * 2), kBufferConfig);
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
     }
   }
   __syncthreads();
-  if (tid < ROWS && row0 + tid < N) {
+  if (tid < ROWS && row0 + tid < p1) {
     float v = s_part[0][tid];
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) v += s_part[w][tid];
@@ -264,7 +268,7 @@ constexpr int kF32MaxD = 4096;
 constexpr int kF32MaxH = 1024;
 
 __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* __restrict__ resid, int N, int d,
-                                                                  int r, const float* __restrict__ norm_w,
+                                                                  int r, int p1, const float* __restrict__ norm_w,
                                                                   float eps_row, const float* __restrict__ W1,
                                                                   const float* __restrict__ b1, int h,
                                                                   const float* __restrict__ w2,
@@ -277,12 +281,13 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
   const int row0 = r + blockIdx.x * kF32Rows;
   float* ob = out + (size_t)b * N;
   for (int j = blockIdx.x * kThreads + tid; j < r; j += gridDim.x * kThreads) ob[j] = 0.0f;
-  if (row0 >= N) return;
+  for (int j = p1 + blockIdx.x * kThreads + tid; j < N; j += gridDim.x * kThreads) ob[j] = 0.0f;
+  if (row0 >= p1) return;
 
   // wave w normalises row row0 + w
   {
     const int row = row0 + wid;
-    const bool ok = row < N;
+    const bool ok = row < p1;
     const float* a = resid + ((size_t)b * N + (ok ? row : 0)) * d;
     float ssq = 0.0f;
     for (int k = lane; k < d; k += 64) {
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
     s_act[rr][n] = w2[n] * (u / (1.0f + expf(-u)));
   }
   __syncthreads();
-  if (tid < kF32Rows && row0 + tid < N) {
+  if (tid < kF32Rows && row0 + tid < p1) {
     float v = 0.0f;
     for (int n = 0; n < h; ++n) v += s_act[tid][n];
     ob[row0 + tid] = v + b2[0];
@@ -317,42 +322,42 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
 }
 
 template <int H, int ROWS, int WAVES>
-hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, float eps, const uint16_t* W1w,
+hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, int p1, float eps, const uint16_t* W1w,
                        const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
-  const int P = N - r;
+  const int P = p1 - r;
   const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
   // d = 2048 (the model width) gets a fully unrolled chunk loop: the compiler
   // then counts outstanding loads exactly instead of waiting for all of them
   // at the loop's back edge, which would void the prefetch ring
   if (d == 2048)
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 32>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid,
-                       N, d, r, eps, W1w, b1, w2, b2, out);
+                       N, d, r, p1, eps, W1w, b1, w2, b2, out);
   else
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 0>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid, N,
-                       d, r, eps, W1w, b1, w2, b2, out);
+                       d, r, p1, eps, W1w, b1, w2, b2, out);
   return hipGetLastError();
 }
 
 template <int H>
-hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, float eps, const uint16_t* W1w,
+hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int p1, float eps, const uint16_t* W1w,
                          const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
   // Every workgroup streams all of W1w through L1, so W1 bytes per token fall
   // with the tile height: 128-token tiles of 8 waves (each wave with the
   // registers of the 64-token layout's waves) once they still give about
   // every CU a workgroup, else 64-token tiles of 4 waves.
-  const int P = N - r;
+  const int P = p1 - r;
   if constexpr (H >= 128) {
     if ((long long)B * ((P + 127) / 128) >= kTallTileMinBlocks)
-      return launch_rows<H, 128, 8>(resid, B, N, d, r, eps, W1w, b1, w2, b2, out, s);
+      return launch_rows<H, 128, 8>(resid, B, N, d, r, p1, eps, W1w, b1, w2, b2, out, s);
   }
-  return launch_rows<H, 64, 4>(resid, B, N, d, r, eps, W1w, b1, w2, b2, out, s);
+  return launch_rows<H, 64, 4>(resid, B, N, d, r, p1, eps, W1w, b1, w2, b2, out, s);
 }
 
 }  // namespace
 
 size_t gate_score_workspace(int h, int d) { return (size_t)h * d * 2; }
 
-hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, const uint16_t* norm_w,
+hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1, const uint16_t* norm_w,
                                   float eps_row, const uint16_t* W1, const float* b1, int h, const uint16_t* w2,
                                   const float* b2, float* out, void* ws, hipStream_t s) {
   uint16_t* W1w = static_cast<uint16_t*>(ws);
@@ -362,23 +367,23 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
   if (e != hipSuccess) return e;
   switch (h) {
     case 64:
-      return launch_bf16_h<64>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<64>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
     case 128:
-      return launch_bf16_h<128>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<128>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
     case 256:
-      return launch_bf16_h<256>(resid, B, N, d, r, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<256>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, const float* norm_w,
+hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1, const float* norm_w,
                                  float eps_row, const float* W1, const float* b1, int h, const float* w2,
                                  const float* b2, float* out, hipStream_t s) {
   if (d > kF32MaxD || h > kF32MaxH) return hipErrorInvalidValue;
-  const int P = N - r;
+  const int P = p1 - r;
   const int nblk = P > 0 ? (P + kF32Rows - 1) / kF32Rows : 1;
-  hipLaunchKernelGGL(gate_score_f32_kernel, dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, norm_w, eps_row,
+  hipLaunchKernelGGL(gate_score_f32_kernel, dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, p1, norm_w, eps_row,
                      W1, b1, h, w2, b2, out);
   return hipGetLastError();
 }

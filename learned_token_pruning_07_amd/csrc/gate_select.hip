@@ -10,8 +10,9 @@
 //    to LDS with the first digit's histogram counted on the way, the shared
 //    LDS radix select finds the threshold, and the final pass in index order
 //    writes the keep mask, kept_idx and the kept scores through block-wide
-//    prefix counts (the non-prunable prefix [0, r) first, then the kept
-//    prunable tokens ascending).
+//    prefix counts (the non-prunable tokens before the span [r, p1) first,
+//    then the kept prunable tokens ascending, then the non-prunable tokens
+//    after the span).
 //  * the residual row gather of tg_compact, given kept_idx.
 // Longer rows run the three separate calls.
 #include "select_device.h"
@@ -27,7 +28,7 @@ constexpr int kItems = 16;  // consecutive prunable tokens per thread in the fin
 
 // score_raw and score may alias: every raw score is read before the
 // reduction's barriers, and nothing reads score_raw after them.
-__global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* score_raw, int N, int r, float eps,
+__global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* score_raw, int N, int r, int p1, float eps,
                                                                int K, float* score,
                                                                uint8_t* __restrict__ keep,
                                                                int32_t* __restrict__ kept_idx,
@@ -41,9 +42,9 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int P = N - r;
+  const int P = p1 - r;
   const int Kp = K < P ? K : P;
-  const int M = r + Kp;
+  const int M = N - P + Kp;
   const float* x = score_raw + (size_t)b * N;
   float* y = score + (size_t)b * N;
   uint8_t* kp = keep + (size_t)b * N;
@@ -56,14 +57,15 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
   f32x4 v[kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = sel::load_scores(x, (e * kThreads + tid) * 4, N, r, vec);
+  for (int e = 0; e < kVec; ++e) v[e] = sel::load_scores(x, (e * kThreads + tid) * 4, N, r, p1, vec);
   const double scale = sel::row_inv_rms(v, P, eps, s_part, &s_scale);  // (its barriers order the clear above)
 #pragma unroll
   for (int e = 0; e < kVec; ++e) {
     const int j = (e * kThreads + tid) * 4;
     f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
+    for (int i = 0; i < 4; ++i)  // exactly 0 outside the span, also when the scale is not finite
+      o[i] = (j + i >= r && j + i < p1) ? (float)((double)v[e][i] * scale) : 0.0f;
     if (vec && j + 4 <= N) {
       *reinterpret_cast<f32x4*>(y + j) = o;
     } else {
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
     // keys of the prunable scores (index j - r of the span) and the first digit
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (j + i >= r && j + i < N) {
+      if (j + i >= r && j + i < p1) {
         const uint32_t key = sel::order_key(o[i]);
         s_keys[sel::key_slot(j + i - r)] = key;
         atomicAdd(&s_hist[key >> 21], 1u);
@@ -83,11 +85,17 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
   }
 
   __syncthreads();  // every key and the first histogram are in LDS; y is written
-  // the non-prunable prefix is kept first, in order (its scores are 0)
+  // the non-prunable tokens before the span are kept first, those after it
+  // last (ranks r + K' ...), in order (their scores are 0)
   for (int j = tid; j < r; j += kThreads) {
     kp[j] = 1;
     ki[j] = j;
     sk[j] = 0.0f;
+  }
+  for (int j = p1 + tid; j < N; j += kThreads) {
+    kp[j] = 1;
+    ki[r + Kp + (j - p1)] = j;
+    sk[r + Kp + (j - p1)] = 0.0f;
   }
   if (Kp <= 0 || Kp == P) {
     // trivial budgets: every prunable token or none
@@ -179,19 +187,19 @@ size_t gate_select_workspace(int B, int N) {
   return a > t ? a : t;  // the two calls use it one after the other
 }
 
-hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, float eps, int K, const void* resid,
-                              size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
+hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, int p1, float eps, int K,
+                              const void* resid, size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
                               void* resid_out, float* score_kept, void* ws, hipStream_t s) {
-  const int P = N - r;
-  const int M = r + (K < P ? K : P);
+  const int P = p1 - r;
+  const int M = N - P + (K < P ? K : P);
   if (N > sel::kRowChunk) {
-    hipError_t e = launch_seq_rmsnorm(score_raw, B, N, r, eps, score, ws, s);
+    hipError_t e = launch_seq_rmsnorm(score_raw, B, N, r, p1, eps, score, ws, s);
     if (e != hipSuccess) return e;
-    e = launch_topk_select(score, B, N, r, K, keep, ws, s);
+    e = launch_topk_select(score, B, N, r, p1, K, keep, ws, s);
     if (e != hipSuccess) return e;
     return launch_compact(resid, row_bytes, B, N, keep, score, M, kept_idx, resid_out, score_kept, s);
   }
-  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, r, eps, K, score, keep,
+  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, r, p1, eps, K, score, keep,
                      kept_idx, score_kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

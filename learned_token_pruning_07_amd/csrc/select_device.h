@@ -24,7 +24,7 @@ constexpr int kLdsKeyWords = kLdsKeys + kLdsKeys / 16;
 __device__ __forceinline__ int key_slot(int j) { return j + (j >> 4); }
 
 // Four scores from x[j..j+3] (0 past N and below r).
-__device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r, bool vec) {
+__device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r, int p1, bool vec) {
   f32x4 v;
   if (vec && j + 4 <= N) {
     v = *reinterpret_cast<const f32x4*>(x + j);
@@ -33,7 +33,7 @@ __device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r
     for (int i = 0; i < 4; ++i) v[i] = j + i < N ? x[j + i] : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = j + i >= r ? v[i] : 0.0f;
+  for (int i = 0; i < 4; ++i) v[i] = (j + i >= r && j + i < p1) ? v[i] : 0.0f;
   return v;
 }
 

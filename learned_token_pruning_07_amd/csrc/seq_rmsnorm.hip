@@ -26,7 +26,7 @@ constexpr int kChunk = sel::kRowChunk;      // 32768 scores: the single-workgrou
 
 // Rows of up to kChunk scores.  `in` and `out` may alias (in-place
 // normalisation): every score is read before the barriers of the reduction.
-__global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, int N, int r, float eps,
+__global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, int N, int r, int p1, float eps,
                                                                float* out) {
   __shared__ double s_part[kThreads / 64];
   __shared__ double s_scale;
@@ -38,14 +38,15 @@ __global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, 
 
   f32x4 v[kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, (e * kThreads + tid) * 4, N, r, vec);
-  const double scale = sel::row_inv_rms(v, N - r, eps, s_part, &s_scale);
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, (e * kThreads + tid) * 4, N, r, p1, vec);
+  const double scale = sel::row_inv_rms(v, p1 - r, eps, s_part, &s_scale);
 #pragma unroll
   for (int e = 0; e < kVec; ++e) {
     const int j = (e * kThreads + tid) * 4;
     f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
+    for (int i = 0; i < 4; ++i)  // exactly 0 outside the span, also when the scale is not finite
+      o[i] = (j + i >= r && j + i < p1) ? (float)((double)v[e][i] * scale) : 0.0f;
     if (vec && j + 4 <= N) {
       *reinterpret_cast<f32x4*>(y + j) = o;
     } else {
@@ -70,7 +71,7 @@ __device__ __forceinline__ double block_sum_f64(double v, double* s_part) {
 }
 
 // partial[b, c] = sum of squares of the prunable scores in slice c of row b
-__global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* in, int N, int r,
+__global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* in, int N, int r, int p1,
                                                                   double* __restrict__ partial) {
   __shared__ double s_part[kSliceThreads / 64];
   const int b = blockIdx.y, c0 = blockIdx.x * kSlice, tid = threadIdx.x;
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* i
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   f32x4 v[kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, vec);
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, p1, vec);
   float part = 0.0f;
 #pragma unroll
   for (int e = 0; e < kVec; ++e)
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* i
 
 // Every workgroup of row b sums the row's partials in index order (the same
 // value in each), then scales its own slice.
-__global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* in, int N, int r, float eps,
+__global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* in, int N, int r, int p1, float eps,
                                                                   const double* __restrict__ partial, int nblk,
                                                                   float* out) {
   __shared__ double s_part[kSliceThreads / 64];
@@ -100,18 +101,19 @@ __global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* i
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
   f32x4 v[kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, vec);
+  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, p1, vec);
   double acc = 0.0;
   for (int c = tid; c < nblk; c += kSliceThreads) acc += partial[(size_t)b * nblk + c];
   const double t = block_sum_f64(acc, s_part);
-  const int P = N - r;
+  const int P = p1 - r;
   const double scale = P > 0 ? 1.0 / sqrt(t / (double)P + (double)eps) : 0.0;
 #pragma unroll
   for (int e = 0; e < kVec; ++e) {
     const int j = c0 + (e * kSliceThreads + tid) * 4;
     f32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (float)((double)v[e][i] * scale);
+    for (int i = 0; i < 4; ++i)  // exactly 0 outside the span, also when the scale is not finite
+      o[i] = (j + i >= r && j + i < p1) ? (float)((double)v[e][i] * scale) : 0.0f;
     if (vec && j + 4 <= N) {
       *reinterpret_cast<f32x4*>(y + j) = o;
     } else {
@@ -128,18 +130,18 @@ size_t seq_rmsnorm_workspace(int B, int N) {
   return N > kChunk ? (size_t)B * ((N + kSlice - 1) / kSlice) * sizeof(double) : 0;
 }
 
-hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out, void* ws,
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, float eps, float* out, void* ws,
                               hipStream_t s) {
   if (N <= kChunk) {
-    hipLaunchKernelGGL(seq_rmsnorm_kernel, dim3(B), dim3(kThreads), 0, s, in, N, r, eps, out);
+    hipLaunchKernelGGL(seq_rmsnorm_kernel, dim3(B), dim3(kThreads), 0, s, in, N, r, p1, eps, out);
     return hipGetLastError();
   }
   const int nblk = (N + kSlice - 1) / kSlice;
   double* partial = static_cast<double*>(ws);
-  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, partial);
+  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, eps, partial, nblk, out);
+  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, eps, partial, nblk, out);
   return hipGetLastError();
 }
 

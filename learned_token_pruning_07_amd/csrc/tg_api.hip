@@ -74,78 +74,81 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
   return 0;
 }
 
-int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
+static int gate_score_common(const char* name, const void* resid, int dt, int B, int N, int d, int r, int p1, const void* norm_w, float eps_row,
                   const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
                   void* ws, size_t ws_bytes, void* stream) {
-  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_gate_score: unknown dtype %d", dt);
-  if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "tg_gate_score: B, N, d, h must be > 0");
-  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_gate_score: r=%d outside [0, N=%d]", r, N);
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
+  if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: B, N, d, h must be > 0", name);
+  if (r < 0 || r > p1 || p1 > N)
+    return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
   if (!resid || !norm_w || !W1 || !b1 || !w2 || !b2 || !score_raw)
-    return fail(TG_EINVAL, "tg_gate_score: null pointer argument");
-  if (!(eps_row >= 0.0f)) return fail(TG_EINVAL, "tg_gate_score: eps_row must be >= 0");
-  if ((long long)B * N * d > (1LL << 40)) return fail(TG_EINVAL, "tg_gate_score: tensor too large");
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!(eps_row >= 0.0f)) return fail(TG_EINVAL, "%s: eps_row must be >= 0", name);
+  if ((long long)B * N * d > (1LL << 40)) return fail(TG_EINVAL, "%s: tensor too large", name);
   if (!aligned16(resid) || !aligned16(W1) || !aligned16(norm_w) || !aligned4(score_raw) || !aligned4(b1) ||
       !aligned4(b2))
-    return fail(TG_EINVAL, "tg_gate_score: resid, W1 and norm_w must be 16-byte aligned");
+    return fail(TG_EINVAL, "%s: resid, W1 and norm_w must be 16-byte aligned", name);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dt == TG_BF16) {
-    if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 needs d %% 64 == 0 (d=%d)", d);
+    if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "%s: bf16 needs d %% 64 == 0 (d=%d)", name, d);
     if (h != 64 && h != 128 && h != 256)
-      return fail(TG_EUNSUPPORTED, "tg_gate_score: bf16 supports h in {64,128,256} (h=%d)", h);
+      return fail(TG_EUNSUPPORTED, "%s: bf16 supports h in {64,128,256} (h=%d)", name, h);
     const size_t need = tg::gate_score_workspace(h, d);
     if (!ws || ws_bytes < need)
-      return fail(TG_EINVAL, "tg_gate_score: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gate_score: misaligned workspace");
-    if ((size_t)(N - r) * d * 2 > 0x7FFFFFFFull)
-      return fail(TG_EUNSUPPORTED, "tg_gate_score: a batch row above 2 GiB");
-    return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r,
+      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+    if ((size_t)(p1 - r) * d * 2 > 0x7FFFFFFFull)
+      return fail(TG_EUNSUPPORTED, "%s: a batch row above 2 GiB", name);
+    return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r, p1,
                                                  static_cast<const uint16_t*>(norm_w), eps_row,
                                                  static_cast<const uint16_t*>(W1), b1, h,
                                                  static_cast<const uint16_t*>(w2), b2, score_raw, ws, s),
-                      "tg_gate_score");
+                      name);
   }
   if (d % 4 != 0 || d > 4096 || h > 1024)
-    return fail(TG_EUNSUPPORTED, "tg_gate_score: fp32 needs d %% 4 == 0, d <= 4096, h <= 1024");
-  return hip_status(tg::launch_gate_score_f32(static_cast<const float*>(resid), B, N, d, r,
+    return fail(TG_EUNSUPPORTED, "%s: fp32 needs d %% 4 == 0, d <= 4096, h <= 1024", name);
+  return hip_status(tg::launch_gate_score_f32(static_cast<const float*>(resid), B, N, d, r, p1,
                                               static_cast<const float*>(norm_w), eps_row,
                                               static_cast<const float*>(W1), b1, h, static_cast<const float*>(w2),
                                               b2, score_raw, s),
-                    "tg_gate_score");
+                    name);
 }
 
-int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq, float* score, void* ws,
+static int seq_rmsnorm_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq, float* score, void* ws,
                    size_t ws_bytes, void* stream) {
-  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_seq_rmsnorm: B, N must be > 0");
-  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_seq_rmsnorm: r=%d outside [0, N=%d]", r, N);
-  if (!score_raw || !score) return fail(TG_EINVAL, "tg_seq_rmsnorm: null pointer argument");
-  if (!aligned4(score_raw) || !aligned4(score)) return fail(TG_EINVAL, "tg_seq_rmsnorm: misaligned pointer");
-  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "tg_seq_rmsnorm: eps_seq must be >= 0");
+  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "%s: B, N must be > 0", name);
+  if (r < 0 || r > p1 || p1 > N)
+    return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
+  if (!score_raw || !score) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned4(score_raw) || !aligned4(score)) return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_seq must be >= 0", name);
   const size_t need = tg::seq_rmsnorm_workspace(B, N);
   if (need > 0) {
     if (!ws || ws_bytes < need)
-      return fail(TG_EINVAL, "tg_seq_rmsnorm: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_seq_rmsnorm: misaligned workspace");
+      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
   }
-  return hip_status(tg::launch_seq_rmsnorm(score_raw, B, N, r, eps_seq, score, ws,
+  return hip_status(tg::launch_seq_rmsnorm(score_raw, B, N, r, p1, eps_seq, score, ws,
                                            reinterpret_cast<hipStream_t>(stream)),
-                    "tg_seq_rmsnorm");
+                    name);
 }
 
-int tg_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws, size_t ws_bytes,
+static int topk_select_common(const char* name, const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws, size_t ws_bytes,
                    void* stream) {
-  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "tg_topk_select: B, N must be > 0");
-  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_topk_select: r=%d outside [0, N=%d]", r, N);
-  if (K < 0) return fail(TG_EINVAL, "tg_topk_select: K=%d must be >= 0", K);
-  if (!score || !keep) return fail(TG_EINVAL, "tg_topk_select: null pointer argument");
-  if (!aligned4(score)) return fail(TG_EINVAL, "tg_topk_select: misaligned score");
+  if (B <= 0 || N <= 0) return fail(TG_EINVAL, "%s: B, N must be > 0", name);
+  if (r < 0 || r > p1 || p1 > N)
+    return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
+  if (K < 0) return fail(TG_EINVAL, "%s: K=%d must be >= 0", name, K);
+  if (!score || !keep) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned4(score)) return fail(TG_EINVAL, "%s: misaligned score", name);
   const size_t need = tg::topk_select_workspace(B, N);
   if (need > 0) {
     if (!ws || ws_bytes < need)
-      return fail(TG_EINVAL, "tg_topk_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_topk_select: misaligned workspace");
+      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
   }
-  return hip_status(tg::launch_topk_select(score, B, N, r, K, keep, ws, reinterpret_cast<hipStream_t>(stream)),
-                    "tg_topk_select");
+  return hip_status(tg::launch_topk_select(score, B, N, r, p1, K, keep, ws, reinterpret_cast<hipStream_t>(stream)),
+                    name);
 }
 
 int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* keep, const float* score, int M,
@@ -166,31 +169,82 @@ int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* ke
                     "tg_compact");
 }
 
-int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, int K, const void* resid, int dt,
+static int gate_select_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq, int K, const void* resid, int dt,
                    int d, float* score, uint8_t* keep, int32_t* kept_idx, void* resid_out, float* score_out,
                    void* ws, size_t ws_bytes, void* stream) {
-  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "tg_gate_select: unknown dtype %d", dt);
-  if (B <= 0 || N <= 0 || d <= 0) return fail(TG_EINVAL, "tg_gate_select: B, N, d must be > 0");
-  if (r < 0 || r > N) return fail(TG_EINVAL, "tg_gate_select: r=%d outside [0, N=%d]", r, N);
-  if (K < 0) return fail(TG_EINVAL, "tg_gate_select: K=%d must be >= 0", K);
-  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "tg_gate_select: eps_seq must be >= 0");
-  const int M = r + (K < N - r ? K : N - r);
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
+  if (B <= 0 || N <= 0 || d <= 0) return fail(TG_EINVAL, "%s: B, N, d must be > 0", name);
+  if (r < 0 || r > p1 || p1 > N)
+    return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
+  if (K < 0) return fail(TG_EINVAL, "%s: K=%d must be >= 0", name, K);
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_seq must be >= 0", name);
+  const int P = p1 - r;
+  const int M = N - P + (K < P ? K : P);
   if (!score_raw || !score || !keep || !resid || (M > 0 && (!kept_idx || !resid_out || !score_out)))
-    return fail(TG_EINVAL, "tg_gate_select: null pointer argument");
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
   const size_t row_bytes = (size_t)d * dt_size(dt);
-  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "tg_gate_select: row bytes must be a multiple of 16");
+  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "%s: row bytes must be a multiple of 16", name);
   if (!aligned4(score_raw) || !aligned4(score) || !aligned16(resid) ||
       (M > 0 && (!aligned16(resid_out) || !aligned4(kept_idx) || !aligned4(score_out))))
-    return fail(TG_EINVAL, "tg_gate_select: misaligned pointer");
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
   const size_t need = tg::gate_select_workspace(B, N);
   if (need > 0) {
     if (!ws || ws_bytes < need)
-      return fail(TG_EINVAL, "tg_gate_select: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    if (!aligned16(ws)) return fail(TG_EINVAL, "tg_gate_select: misaligned workspace");
+      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
   }
-  return hip_status(tg::launch_gate_select(score_raw, B, N, r, eps_seq, K, resid, row_bytes, score, keep, kept_idx,
+  return hip_status(tg::launch_gate_select(score_raw, B, N, r, p1, eps_seq, K, resid, row_bytes, score, keep, kept_idx,
                                            resid_out, score_out, ws, reinterpret_cast<hipStream_t>(stream)),
-                    "tg_gate_select");
+                    name);
+}
+
+int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
+                  const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
+                  void* ws, size_t ws_bytes, void* stream) {
+  return gate_score_common("tg_gate_score", resid, dt, B, N, d, r, N, norm_w, eps_row, W1, b1, h, w2, b2, score_raw,
+                           ws, ws_bytes, stream);
+}
+
+int tg_gate_score_span(const void* resid, int dt, int B, int N, int d, int span_begin, int span_end,
+                       const void* norm_w, float eps_row, const void* W1, const float* b1, int h, const void* w2,
+                       const float* b2, float* score_raw, void* ws, size_t ws_bytes, void* stream) {
+  return gate_score_common("tg_gate_score_span", resid, dt, B, N, d, span_begin, span_end, norm_w, eps_row, W1, b1,
+                           h, w2, b2, score_raw, ws, ws_bytes, stream);
+}
+
+int tg_seq_rmsnorm(const float* score_raw, int B, int N, int r, float eps_seq, float* score, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return seq_rmsnorm_common("tg_seq_rmsnorm", score_raw, B, N, r, N, eps_seq, score, ws, ws_bytes, stream);
+}
+
+int tg_seq_rmsnorm_span(const float* score_raw, int B, int N, int span_begin, int span_end, float eps_seq,
+                        float* score, void* ws, size_t ws_bytes, void* stream) {
+  return seq_rmsnorm_common("tg_seq_rmsnorm_span", score_raw, B, N, span_begin, span_end, eps_seq, score, ws,
+                            ws_bytes, stream);
+}
+
+int tg_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return topk_select_common("tg_topk_select", score, B, N, r, N, K, keep, ws, ws_bytes, stream);
+}
+
+int tg_topk_select_span(const float* score, int B, int N, int span_begin, int span_end, int K, uint8_t* keep,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return topk_select_common("tg_topk_select_span", score, B, N, span_begin, span_end, K, keep, ws, ws_bytes, stream);
+}
+
+int tg_gate_select(const float* score_raw, int B, int N, int r, float eps_seq, int K, const void* resid, int dt,
+                   int d, float* score, uint8_t* keep, int32_t* kept_idx, void* resid_out, float* score_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return gate_select_common("tg_gate_select", score_raw, B, N, r, N, eps_seq, K, resid, dt, d, score, keep, kept_idx,
+                            resid_out, score_out, ws, ws_bytes, stream);
+}
+
+int tg_gate_select_span(const float* score_raw, int B, int N, int span_begin, int span_end, float eps_seq, int K,
+                        const void* resid, int dt, int d, float* score, uint8_t* keep, int32_t* kept_idx,
+                        void* resid_out, float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  return gate_select_common("tg_gate_select_span", score_raw, B, N, span_begin, span_end, eps_seq, K, resid, dt, d,
+                            score, keep, kept_idx, resid_out, score_out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -8,7 +8,9 @@
 
 namespace tg {
 
-hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r,
+// Rows [r, p1) of each batch row are the prunable span (p1 = N for a prompt
+// [x_R, x_D]); every other row scores 0.
+hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1,
                                   const uint16_t* norm_w, float eps_row, const uint16_t* W1,
                                   const float* b1, int h, const uint16_t* w2, const float* b2,
                                   float* out, void* ws, hipStream_t s);
@@ -16,17 +18,17 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
 // Workspace bytes of launch_gate_score_bf16: the norm-weight-folded W1.
 size_t gate_score_workspace(int h, int d);
 
-hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r,
+hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1,
                                  const float* norm_w, float eps_row, const float* W1,
                                  const float* b1, int h, const float* w2, const float* b2,
                                  float* out, hipStream_t s);
 
 size_t seq_rmsnorm_workspace(int B, int N);
-hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, float eps, float* out, void* ws,
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, float eps, float* out, void* ws,
                               hipStream_t s);
 
 size_t topk_select_workspace(int B, int N);
-hipError_t launch_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws,
+hipError_t launch_topk_select(const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws,
                               hipStream_t s);
 
 hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,
@@ -38,10 +40,11 @@ hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int
                                  const int32_t* kept_idx, void* resid_out, hipStream_t s);
 
 // launch_seq_rmsnorm + launch_topk_select + launch_compact in sequence, bit
-// for bit (M = r + min(K, N - r)); two launches for rows of up to 32768 tokens.
+// for bit (M = N - P + min(K, P), P = p1 - r); two launches for rows of up to
+// 32768 tokens.
 size_t gate_select_workspace(int B, int N);
-hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, float eps, int K, const void* resid,
-                              size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
+hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, int p1, float eps, int K,
+                              const void* resid, size_t row_bytes, float* score, uint8_t* keep, int32_t* kept_idx,
                               void* resid_out, float* score_kept, void* ws, hipStream_t s);
 
 // rope_base > 0: q and k are first rotated (rotary embedding at the positions

@@ -35,7 +35,7 @@ constexpr int kItems = 16;  // consecutive keys per thread in the final pass
 
 // Spans of up to kLdsKeys prunable tokens (and the trivial budgets of any span).
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ score, int N, int r,
-                                                               int K, uint8_t* __restrict__ keep) {
+                                                               int p1, int K, uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_keys[sel::kLdsKeyWords];
   __shared__ uint32_t s_hist[2048];
   __shared__ __attribute__((aligned(16))) uint32_t s_wave[16];
@@ -45,10 +45,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   const int b = blockIdx.x;
   const float* sc = score + (size_t)b * N + r;
   uint8_t* kp = keep + (size_t)b * N;
-  const int P = N - r;
+  const int P = p1 - r;
   const int Kp = K < P ? K : P;
 
   for (int j = tid; j < r; j += kThreads) kp[j] = 1;
+  for (int j = p1 + tid; j < N; j += kThreads) kp[j] = 1;  // non-prunable tokens after the span
   if (Kp <= 0 || Kp == P) {
     const uint8_t v = Kp > 0 ? 1 : 0;
     for (int j = tid; j < P; j += kThreads) kp[r + j] = v;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kMThreads) void topk_ws_clear_kernel(uint32_t* __re
 // (which every workgroup re-derives from the previous histogram; workgroup 0
 // also records them for the next launch).
 template <int PASS>
-__global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ score, int N, int r, int Kp,
+__global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ score, int N, int r, int p1, int Kp,
                                                               uint32_t* __restrict__ ws) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_prev[2048];
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __res
   const int tid = threadIdx.x, b = blockIdx.y, c0 = blockIdx.x * kMChunk;
   const float* sc = score + (size_t)b * N + r;
   uint32_t* w = ws + (size_t)b * kWsWords;
-  const int P = N - r;
+  const int P = p1 - r;
   uint32_t key[kMItems];
   chunk_keys(sc, P, c0 + tid * kMItems, key);  // requested first
 
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __res
 }
 
 // keep: key > T, or key == T among the first k_eq such tokens by index
-__global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __restrict__ score, int N, int r, int Kp,
+__global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __restrict__ score, int N, int r, int p1, int Kp,
                                                                const uint32_t* __restrict__ ws,
                                                                uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_prev[1024];
@@ -255,12 +256,14 @@ __global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __re
   const float* sc = score + (size_t)b * N + r;
   const uint32_t* w = ws + (size_t)b * kWsWords;
   uint8_t* kp = keep + (size_t)b * N;
-  const int P = N - r;
+  const int P = p1 - r;
   const int j0 = c0 + tid * kMItems;
   uint32_t key[kMItems];
   chunk_keys(sc, P, j0, key);
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int j = tid; j < r; j += kMThreads) kp[j] = 1;
+    for (int j = p1 + tid; j < N; j += kMThreads) kp[j] = 1;
+  }
 
   for (int i = tid; i < 1024; i += kMThreads) s_prev[i] = w[kH2 + i];
   const uint32_t prefix = w[kState + 2], krem = w[kState + 3];
@@ -312,21 +315,21 @@ size_t topk_select_workspace(int B, int N) {
   return N > kLdsKeys ? (size_t)B * kWsWords * sizeof(uint32_t) : 0;
 }
 
-hipError_t launch_topk_select(const float* score, int B, int N, int r, int K, uint8_t* keep, void* ws,
+hipError_t launch_topk_select(const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws,
                               hipStream_t s) {
-  const int P = N - r;
+  const int P = p1 - r;
   const int Kp = K < P ? K : P;
   if (P <= kLdsKeys || Kp <= 0 || Kp == P) {  // (the single workgroup also settles the trivial budgets)
-    hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kThreads), 0, s, score, N, r, K, keep);
+    hipLaunchKernelGGL(topk_select_kernel, dim3(B), dim3(kThreads), 0, s, score, N, r, p1, K, keep);
     return hipGetLastError();
   }
   uint32_t* w = static_cast<uint32_t*>(ws);
   const dim3 grid((P + kMChunk - 1) / kMChunk, B);
   hipLaunchKernelGGL(topk_ws_clear_kernel, dim3(B), dim3(kMThreads), 0, s, w);
-  hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kMThreads), 0, s, score, N, r, Kp, w);
-  hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kMThreads), 0, s, score, N, r, Kp, w);
-  hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kMThreads), 0, s, score, N, r, Kp, w);
-  hipLaunchKernelGGL(topk_final_kernel, grid, dim3(kMThreads), 0, s, score, N, r, Kp, w, keep);
+  hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
+  hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
+  hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
+  hipLaunchKernelGGL(topk_final_kernel, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w, keep);
   return hipGetLastError();
 }
 

@@ -72,18 +72,20 @@ def score_rows(rows, norm_w, W1, b1, w2, b2, eps_row: float) -> np.ndarray:
     return out
 
 
-def gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float) -> np.ndarray:
+def gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float, span_end=None) -> np.ndarray:
     """Raw scores ``[B, N]`` for a residual ``[B, N, d]``.
 
-    Tokens ``j < r`` form the non-prunable set N (the question, which comes
-    first in the prompt x = [x_R, x_D]); their score is fixed to 0.
+    The prunable tokens are the span ``[r, span_end)`` (``span_end`` None: N,
+    the prompt x = [x_R, x_D] with the question first).  Every other token
+    is non-prunable and its score is fixed to 0.
     """
     a = np.asarray(resid)
     B, N, _ = a.shape
+    p1 = N if span_end is None else span_end
     out = np.zeros((B, N), np.float64)
     for bi in range(B):
-        if N > r:
-            out[bi, r:] = score_rows(a[bi, r:], norm_w, W1, b1, w2, b2, eps_row)
+        if p1 > r:
+            out[bi, r:p1] = score_rows(a[bi, r:p1], norm_w, W1, b1, w2, b2, eps_row)
     return out
 
 
@@ -96,17 +98,19 @@ def gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float) -> np.ndar
 # Readings: the mean square runs over the prunable span only, there is no
 # learnable gain, and eps sits inside the square root (so 0 maps to 0).
 # --------------------------------------------------------------------------
-def seq_rmsnorm(score_raw, r: int, eps_seq: float) -> np.ndarray:
+def seq_rmsnorm(score_raw, r: int, eps_seq: float, span_end=None) -> np.ndarray:
+    """Normalised scores; the prunable span is ``[r, span_end)`` (None: N)."""
     s = widen(score_raw)
     B, N = s.shape
+    p1 = N if span_end is None else span_end
     out = np.zeros((B, N), np.float64)
-    P = N - r
+    P = p1 - r
     if P <= 0:
         return out
     for bi in range(B):
-        x = s[bi, r:]
+        x = s[bi, r:p1]
         ms = np.sum(x * x) / P
-        out[bi, r:] = x / math.sqrt(ms + eps_seq)
+        out[bi, r:p1] = x / math.sqrt(ms + eps_seq)
     return out
 
 
@@ -117,19 +121,22 @@ def seq_rmsnorm(score_raw, r: int, eps_seq: float) -> np.ndarray:
 # Readings: K' = min(K, |P|); equal scores go to the lower index; -0.0 and
 # +0.0 are equal; a NaN score ranks below every number (including -inf).
 # --------------------------------------------------------------------------
-def topk_select(score, r: int, K: int) -> np.ndarray:
-    """Keep mask ``[B, N]`` (uint8) holding exactly r + min(K, N-r) ones."""
+def topk_select(score, r: int, K: int, span_end=None) -> np.ndarray:
+    """Keep mask ``[B, N]`` (uint8) holding exactly N - P + min(K, P) ones,
+    where the prunable span is ``[r, span_end)`` (None: N) of P tokens."""
     s = widen(score)
     B, N = s.shape
+    p1 = N if span_end is None else span_end
     keep = np.zeros((B, N), np.uint8)
     keep[:, :r] = 1
-    P = N - r
+    keep[:, p1:] = 1
+    P = p1 - r
     Kp = min(K, P)
     if Kp <= 0:
         return keep
     idx = np.arange(P)
     for bi in range(B):
-        b = s[bi, r:]
+        b = s[bi, r:p1]
         is_nan = np.isnan(b)
         neg = np.where(is_nan, 0.0, -b)
         # ascending order of (is_nan, -b, index): a stable total order

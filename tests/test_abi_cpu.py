@@ -251,3 +251,16 @@ def test_kv_cache_prune_validation(lib):
     # nothing to do: no GPU call is made
     assert call(M=0, k=NULL) == tgb.TG_OK
     assert call(L=0, k=NULL) == tgb.TG_OK
+
+
+def test_span_entry_points_validate_the_span(lib):
+    # a span outside [0, N] or reversed is refused before anything runs
+    assert lib.tg_seq_rmsnorm_span(FAKE, 1, 100, 50, 40, 1e-6, FAKE, NULL, 0, None) == tgb.TG_EINVAL
+    assert "span" in _err(lib)
+    assert lib.tg_seq_rmsnorm_span(FAKE, 1, 100, 0, 101, 1e-6, FAKE, NULL, 0, None) == tgb.TG_EINVAL
+    assert lib.tg_topk_select_span(FAKE, 1, 100, -1, 50, 5, FAKE, NULL, 0, None) == tgb.TG_EINVAL
+    assert lib.tg_gate_select_span(FAKE, 1, 100, 60, 50, 1e-6, 5, FAKE, tgb.TG_BF16, 64, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, NULL, 0, None) == tgb.TG_EINVAL
+    assert lib.tg_gate_score_span(FAKE, tgb.TG_BF16, 1, 100, 256, 10, 120, FAKE, 1e-6, FAKE, FAKE, 64, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 20, None) == tgb.TG_EINVAL
+    assert "tg_gate_score_span" in _err(lib)

@@ -1,0 +1,146 @@
+"""GPU parity of the gate with the prunable document anywhere in the prompt:
+the span entry points (prunable span [p0, p1), non-prunable text on both
+sides) against the oracle -- the scorer within the bf16/fp32 bars, the
+sequence norm within the fp32 bar, the selection bit for bit on the same
+scores, the fused call bit for bit against the separate span calls -- over
+the single-workgroup and the multi-launch (N > 32768) paths and the edge
+spans (no prefix, no suffix, empty span, the whole prompt)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import learned_token_pruning_07_amd as tg
+from learned_token_pruning_07_amd import workloads as wl
+from _gpu_util import DEV, TOL_BF16, TOL_F32, assert_close, dev, dev_bits, gate_dev, host_bits, poison_f32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,N,p0,p1,d,h", [
+    ("bf16", 3000, 40, 2500, 512, 128),
+    ("bf16", 2000, 0, 1900, 256, 64),
+    ("f32", 700, 30, 650, 128, 32),
+])
+def test_gate_score_span(dtype, N, p0, p1, d, h):
+    say(f"gate_score_span {dtype} N={N} span=[{p0},{p1}) d={d} h={h}")
+    c = wl.gate_case(N=N, r=p0, d=d, h=h, K=10, dtype=dtype, seed=N + d, B=2, w_std=0.1)
+    t = gate_dev(c)
+    out = poison_f32((2, N))
+    tg.tg_gate_score(t["resid"], p0, t["norm_w"], t["W1"], t["b1"], t["w2"], t["b2"], c.eps_row, score_raw=out,
+                     span_end=p1)
+    ref = oracle.gate_score(c.resid if dtype == "f32" else c.resid, p0, c.norm_w, c.W1, c.b1, c.w2, c.b2, c.eps_row,
+                            span_end=p1)
+    got = out.cpu().numpy()
+    assert_close(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, "score_raw span")
+    assert np.all(got[:, :p0] == 0) and np.all(got[:, p1:] == 0)
+
+
+def _raw(B, N, p0, p1, seed, kind="normal"):
+    rng = np.random.default_rng(seed)
+    if kind == "ties":
+        pool = np.array([-1.0, 0.0, -0.0, 1.0, np.inf, -np.inf, np.nan, 0.5], np.float32)
+        raw = pool[rng.integers(0, pool.size, size=(B, N))]
+    else:
+        raw = (rng.standard_normal((B, N)) * 3.0).astype(np.float32)
+    raw[:, :p0] = 0.0
+    raw[:, p1:] = 0.0
+    return raw
+
+
+@pytest.mark.parametrize("kind,B,N,p0,p1,K", [
+    ("normal", 2, 5000, 17, 4000, 500),
+    ("ties", 1, 3000, 0, 2000, 1234),
+    ("normal", 1, 70000, 64, 60000, 6000),   # multi-launch top-K and sequence norm
+    ("ties", 2, 40000, 7, 39000, 20000),
+    ("normal", 1, 1000, 10, 10, 5),          # empty span: everything kept
+    ("normal", 1, 1000, 0, 1000, 100),       # the whole prompt prunable
+    ("normal", 1, 1000, 300, 1000, 5000),    # budget above the span
+])
+def test_norm_and_topk_span(kind, B, N, p0, p1, K):
+    say(f"seq_rmsnorm/topk span {kind} B={B} N={N} span=[{p0},{p1}) K={K}")
+    raw = _raw(B, N, p0, p1, N + K, kind if kind == "normal" else "normal")
+    out = poison_f32((B, N))
+    tg.tg_seq_rmsnorm(dev(raw), p0, 1e-6, score=out, span_end=p1)
+    assert_close(out.cpu().numpy(), oracle.seq_rmsnorm(raw, p0, 1e-6, span_end=p1), TOL_F32, "seq_rmsnorm span")
+    s = _raw(B, N, p0, p1, N + 2 * K, kind)
+    keep = torch.full((B, N), 7, dtype=torch.uint8, device=DEV)
+    tg.tg_topk_select(dev(s), p0, K, keep=keep, span_end=p1)
+    ref = oracle.topk_select(s, p0, K, span_end=p1)
+    np.testing.assert_array_equal(keep.cpu().numpy(), ref)
+    assert np.all(ref.sum(axis=1) == tg.kept_count(N, p0, K, p1))
+
+
+@pytest.mark.parametrize("kind,dtype,B,N,p0,p1,K,d", [
+    ("normal", "bf16", 2, 5000, 17, 4000, 500, 256),
+    ("ties", "f32", 1, 3000, 0, 2900, 1234, 64),
+    ("normal", "bf16", 1, 32768, 64, 30000, 3000, 2048),  # the stage's size with trailing text
+    ("normal", "bf16", 1, 50000, 100, 45000, 4500, 128),  # multi-launch path
+    ("normal", "bf16", 1, 777, 700, 777, 10, 64),
+])
+def test_gate_select_span(kind, dtype, B, N, p0, p1, K, d):
+    say(f"gate_select span {kind} {dtype} B={B} N={N} span=[{p0},{p1}) K={K} d={d}")
+    raw = _raw(B, N, p0, p1, N + K + d, kind)
+    c = wl.gate_case(N=N, r=p0, d=d, h=8, K=K, dtype=dtype, seed=N + d, B=B)
+    put = dev_bits if dtype == "bf16" else dev
+    resid = put(c.resid)
+    M = tg.kept_count(N, p0, K, p1)
+    s_ref = tg.tg_seq_rmsnorm(dev(raw), p0, 1e-6, span_end=p1)
+    keep_ref = tg.tg_topk_select(s_ref, p0, K, span_end=p1)
+    ki_ref, ro_ref, so_ref = tg.tg_compact(resid, keep_ref, s_ref, M)
+    score = poison_f32((B, N))
+    keep = torch.full((B, N), 7, dtype=torch.uint8, device=DEV)
+    kept_idx = torch.full((B, M), -7, dtype=torch.int32, device=DEV)
+    resid_out = torch.full((B, M, d), float("nan"), dtype=resid.dtype, device=DEV)
+    score_out = poison_f32((B, M))
+    tg.tg_gate_select(dev(raw), resid, p0, K, 1e-6, score=score, keep=keep, kept_idx=kept_idx, resid_out=resid_out,
+                      score_out=score_out, span_end=p1)
+    bits = lambda t: t.cpu().numpy().view(np.uint8)  # noqa: E731
+    np.testing.assert_array_equal(bits(score), bits(s_ref))
+    np.testing.assert_array_equal(keep.cpu().numpy(), keep_ref.cpu().numpy())
+    np.testing.assert_array_equal(kept_idx.cpu().numpy(), ki_ref.cpu().numpy())
+    np.testing.assert_array_equal(bits(resid_out.view(torch.uint8)), bits(ro_ref.view(torch.uint8)))
+    np.testing.assert_array_equal(bits(score_out), bits(so_ref))
+    got = score.cpu().numpy()
+    ref = oracle.seq_rmsnorm(raw, p0, 1e-6, span_end=p1)
+    # (a NaN or infinity in the span makes the scale non-finite on both sides)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert_close(got[fin], ref[fin], TOL_F32, "gate_select span score")
+    k_or = oracle.topk_select(got, p0, K, span_end=p1)
+    np.testing.assert_array_equal(keep.cpu().numpy(), k_or)
+    ki, rs, bs = oracle.compact(c.resid, k_or, got)
+    np.testing.assert_array_equal(kept_idx.cpu().numpy(), ki)
+    got_rows = host_bits(resid_out) if dtype == "bf16" else resid_out.cpu().numpy()
+    np.testing.assert_array_equal(got_rows.view(np.uint8), rs.view(np.uint8))
+    np.testing.assert_array_equal(score_out.cpu().numpy().view(np.uint32), bs.view(np.uint32))
+
+
+def test_span_to_the_end_equals_prefix_entry_points():
+    N, r, K, d = 4000, 50, 300, 256
+    raw = _raw(1, N, r, N, 9)
+    c = wl.gate_case(N=N, r=r, d=d, h=8, K=K, dtype="bf16", seed=1)
+    resid = dev_bits(c.resid)
+    a = tg.tg_gate_select(dev(raw), resid, r, K)
+    b = tg.tg_gate_select(dev(raw), resid, r, K, span_end=N)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+@pytest.mark.parametrize("N,p0,p1", [(3000, 20, 2800), (40000, 5, 39000)])
+def test_norm_with_nonfinite_scores_keeps_zeros_outside_the_span(N, p0, p1):
+    """A NaN or an infinity inside the span makes the scale non-finite; the
+    non-prunable scores stay exactly 0 (the norm's definition), not 0 * NaN."""
+    raw = _raw(1, N, p0, p1, 3)
+    raw[0, p0 + 7] = np.nan
+    raw[0, p0 + 9] = np.inf
+    for span_end in (p1, None):
+        x = raw.copy()
+        if span_end is None:
+            x[:, p1:] = raw[:, p1:]
+        got = tg.tg_seq_rmsnorm(dev(x), p0, 1e-6, span_end=span_end).cpu().numpy()
+        ref = oracle.seq_rmsnorm(x, p0, 1e-6, span_end=span_end)
+        outside = np.ones(N, bool)
+        outside[p0:(N if span_end is None else span_end)] = False
+        assert np.all(got[0, outside] == 0) and np.all(ref[0, outside] == 0)
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
