@@ -36,6 +36,8 @@ def _check(kc, vc, idx, what):
     (5, 2, 1000, 8, 128, 333),
     (2, 1, 257, 1, 8, 257),     # every token kept: the identity
     (3, 3, 64, 4, 16, 1),
+    (1, 1, 300, 16, 256, 77),   # 8 KiB rows: two passes per row
+    (2, 1, 100, 3, 8, 50),      # 48-byte rows: 3 chunks, most lanes idle
 ])
 def test_kv_cache_prune(L, B, N, H, dh, M):
     say(f"kv_cache_prune L={L} B={B} N={N} H={H} dh={dh} M={M}")
