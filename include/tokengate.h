@@ -54,7 +54,8 @@ typedef enum {
   TG_OP_GATED_ATTENTION = 4,
   TG_OP_GATE_SELECT = 5,
   TG_OP_GATED_ATTENTION_ROPE = 6,
-  TG_OP_GATED_ATTENTION_BACKWARD = 7
+  TG_OP_GATED_ATTENTION_BACKWARD = 7,
+  TG_OP_GATED_ATTENTION_ROPE_BACKWARD = 8
 } tg_op;
 
 /*
@@ -319,6 +320,37 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v,
                                 void* d_k, void* d_v, float* d_key_score,
                                 float* d_gain, float* d_temp, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * tg_gated_attention_rope_backward -- gradients of tg_gated_attention_rope.
+ * q and k are rotated exactly as the forward rotates them (bf16 copies, so
+ * the products see the forward's operands), the gradients of
+ * tg_gated_attention_backward are formed with respect to the rotated q' and
+ * k' in fp32, and the transposed rotation maps them back:
+ *     d_q_j         = d_q'_j c + d_q'_{j+d_h/2} s
+ *     d_q_{j+d_h/2} = d_q'_{j+d_h/2} c - d_q'_j s        (and the same for k)
+ * with c, s the cosine and sine of the same angle, rounded once to bf16.  The
+ * rounding of q', k' to bf16 is passed through as the identity.  d_v,
+ * d_key_score, d_gain and d_temp are those of the rotated problem.
+ *
+ *   arguments as tg_gated_attention_backward, plus rope_base (> 1) as given
+ *   to the forward; out and lse are that forward's outputs
+ *   ws, ws_bytes     workspace of at least tg_workspace_size(
+ *                    TG_OP_GATED_ATTENTION_ROPE_BACKWARD, B, M, Hkv * d_h, Hq,
+ *                    d_h) bytes, 16-byte aligned: the backward's workspace
+ *                    rounded up to 16 bytes, then 6 * B * M * (Hq + Hkv) * d_h
+ */
+int tg_gated_attention_rope_backward(const void* q, const void* k,
+                                     const void* v, const void* out,
+                                     const float* lse, const void* d_out,
+                                     int B, int M, int Hq, int Hkv, int d_h,
+                                     const float* key_score,
+                                     const int32_t* pos, const float* gain,
+                                     const float* temp, float sm_scale,
+                                     double rope_base, void* d_q, void* d_k,
+                                     void* d_v, float* d_key_score,
+                                     float* d_gain, float* d_temp, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /*
  * tg_kv_cache_prune -- post-prefill pruning of the KV cache of the layers at

@@ -22,10 +22,10 @@ LIB_PATH = os.path.join(_PKG, "libtokengate.so")
 TG_OK, TG_EINVAL, TG_EUNSUPPORTED, TG_EHIP = 0, 1, 2, 3
 TG_F32, TG_BF16 = 0, 1
 (TG_OP_GATE_SCORE, TG_OP_SEQ_RMSNORM, TG_OP_TOPK_SELECT, TG_OP_COMPACT, TG_OP_GATED_ATTENTION, TG_OP_GATE_SELECT,
- TG_OP_GATED_ATTENTION_ROPE, TG_OP_GATED_ATTENTION_BACKWARD) = range(8)
+ TG_OP_GATED_ATTENTION_ROPE, TG_OP_GATED_ATTENTION_BACKWARD, TG_OP_GATED_ATTENTION_ROPE_BACKWARD) = range(9)
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
-            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
+            "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
@@ -57,6 +57,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                             vp, sz, vp]
     lib.tg_gated_attention_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, vp,
                                                 vp, vp, vp, vp, sz, vp]
+    lib.tg_gated_attention_rope_backward.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp, f,
+                                                     ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
@@ -70,7 +72,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_version.restype = i
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
-                 "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
+                 "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
                  "tg_gate_select_span"):
         getattr(lib, name).restype = i
     if path is None:
@@ -369,9 +371,26 @@ def attention_backward_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, dev
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
+def attention_rope_backward_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for tg_gated_attention_rope_backward at these sizes."""
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION_ROPE_BACKWARD, B, M, Hkv * dh, Hq, dh))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def tg_gated_attention_rope_backward(q, k, v, out, lse, d_out, key_score, pos, gain, temp, rope_base: float,
+                                     sm_scale: float | None = None, ws=None, stream=None, **outs):
+    """Gradients of tg_gated_attention_rope (q, k passed un-rotated, as to the
+    forward).  Same outputs as :func:`tg_gated_attention_backward`; ``ws`` from
+    :func:`attention_rope_backward_workspace`."""
+    if ws is None:
+        ws = attention_rope_backward_workspace(q.shape[0], q.shape[1], q.shape[2], k.shape[2], q.shape[3], q.device)
+    return tg_gated_attention_backward(q, k, v, out, lse, d_out, key_score, pos, gain, temp, sm_scale, ws=ws,
+                                       stream=stream, _rope_base=rope_base, **outs)
+
+
 def tg_gated_attention_backward(q, k, v, out, lse, d_out, key_score, pos, gain, temp, sm_scale: float | None = None,
                                 d_q=None, d_k=None, d_v=None, d_key_score=None, d_gain=None, d_temp=None, ws=None,
-                                stream=None):
+                                stream=None, _rope_base: float | None = None):
     """Gradients of tg_gated_attention from its outputs ``out`` and ``lse``
     and the upstream gradient ``d_out``.  Returns ``(d_q, d_k, d_v,
     d_key_score, d_gain, d_temp)``: bf16 like q/k/v, fp32 ``[B, M]``, and
@@ -411,10 +430,14 @@ def tg_gated_attention_backward(q, k, v, out, lse, d_out, key_score, pos, gain, 
     if ws is None:
         ws = attention_backward_workspace(B, M, Hq, Hkv, dh, dev)
     _need(ws, "ws", torch.uint8)
-    _check(lib.tg_gated_attention_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, M, Hq, Hkv, dh, _ptr(key_score), _ptr(pos),
-        _ptr(gain), _ptr(temp), float(sm_scale), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_key_score), _ptr(d_gain),
-        _ptr(d_temp), _ptr(ws), ws.numel(), _stream(stream)))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, M, Hq, Hkv, dh, _ptr(key_score),
+            _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale))
+    tail = (_ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(d_key_score), _ptr(d_gain), _ptr(d_temp), _ptr(ws), ws.numel(),
+            _stream(stream))
+    if _rope_base is None:
+        _check(lib.tg_gated_attention_backward(*head, *tail))
+    else:
+        _check(lib.tg_gated_attention_rope_backward(*head, float(_rope_base), *tail))
     return d_q, d_k, d_v, d_key_score, d_gain, d_temp
 
 

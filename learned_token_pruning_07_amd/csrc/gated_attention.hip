@@ -56,6 +56,7 @@
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
 
+#include "rope_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -104,26 +105,6 @@ struct RopeArgs {
   uint16_t* kr;
 };
 
-// Rotates one head row (x_i, x_{i+DH/2}) pairs i = i0 .. i0 + 7 by the angles
-// whose cosines and sines are c[], s[] (fp32, products fused), rounding the
-// results to bf16 (nearest even).
-template <int DH>
-__device__ __forceinline__ void rope_row8(const uint16_t* src, uint16_t* dst, int i0, const float (&c)[8],
-                                          const float (&s)[8]) {
-  constexpr int HALF = DH / 2;
-  const u32x4 a = load16(src + i0), bv = load16(src + HALF + i0);
-  u32x4 oa, ob;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float x1l = bf16_lo(a[j]), x1h = bf16_hi(a[j]), x2l = bf16_lo(bv[j]), x2h = bf16_hi(bv[j]);
-    const int il = 2 * j, ih = 2 * j + 1;
-    oa[j] = pack_bf16x2(fmaf(x1l, c[il], -(x2l * s[il])), fmaf(x1h, c[ih], -(x2h * s[ih])));
-    ob[j] = pack_bf16x2(fmaf(x2l, c[il], x1l * s[il]), fmaf(x2h, c[ih], x1h * s[ih]));
-  }
-  store16(dst + i0, oa);
-  store16(dst + HALF + i0, ob);
-}
-
 // Prepass, per 64-key block of KV head g:
 //   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
 //   in slot order, zero beyond M);
@@ -144,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
   __shared__ double s_freq[DH / 2];
   const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  if (ROPE && tid < DH / 2) s_freq[tid] = pow(ra.base, -2.0 * (double)tid / (double)DH);  // (ordered by the barrier below)
+  if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);  // (ordered by the barrier below)
   const float scale = 1.0f / (float)(1 << kVScaleLog2);
   constexpr int NL = kBK * DH / 8 / kThreads;  // 16-byte loads per thread, all issued before any use
   u32x4 w[NL];
@@ -184,25 +165,17 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
   }
   if constexpr (ROPE) {
     constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
-    constexpr double kInv2Pi = 0.15915494309189535, k2PiHi = 6.283185307179586, k2PiLo = 2.4492935982947064e-16;
     const int Hq = Hkv * G;
     for (int t = tid; t < kBK * PG; t += kThreads) {
       const int key = t / PG, i0 = (t % PG) * 8, m = m0 + key;
       if (m >= M) continue;
-      const double p = (double)ra.pos[(size_t)b * M + m];
       float c[8], sn[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double th = p * s_freq[i0 + i];
-        const double n = rint(th * kInv2Pi);
-        const double red = fma(-n, k2PiLo, fma(-n, k2PiHi, th));  // th - 2 pi n, |red| <= pi (+ rounding)
-        sincosf((float)red, &sn[i], &c[i]);
-      }
+      rope::sincos8((double)ra.pos[(size_t)b * M + m], s_freq, i0, c, sn);
       const size_t krow = (((size_t)b * M + m) * Hkv + g) * DH;
-      rope_row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
+      rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
       for (int hh = 0; hh < G; ++hh) {
         const size_t qrow = (((size_t)b * M + m) * Hq + g * G + hh) * DH;
-        rope_row8<DH>(ra.q + qrow, ra.qr + qrow, i0, c, sn);
+        rope::row8<DH>(ra.q + qrow, ra.qr + qrow, i0, c, sn);
       }
     }
   }

@@ -42,6 +42,7 @@
 // first and the second products of step p, while the matrix cores work.
 #include <math.h>
 
+#include "rope_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -53,6 +54,16 @@ constexpr int kPB = 64;   // rows per prepass block (Mp is a multiple of it)
 constexpr int kKB = 64;   // keys per dK/dV workgroup
 constexpr int kT = 32;    // queries per dK/dV tile, keys per dQ tile
 constexpr int kRsrcCfg = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
+
+size_t base_ws_bytes(int B, int M, int Hq, int Hkv) {
+  const size_t Mp = (size_t)(M + kPB - 1) / kPB * kPB;
+  return (size_t)B * Mp * ((size_t)3 * Hq * 4 + (size_t)Hkv * 4) + (size_t)2 * B * (Mp / kKB) * Hq * 4;
+}
+// where the rotary variant's buffers start in the workspace
+size_t rope_ws_offset(int B, int M, int Hq, int Hkv, int dh) {
+  (void)dh;
+  return (base_ws_bytes(B, M, Hq, Hkv) + 15) / 16 * 16;
+}
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
@@ -78,6 +89,15 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
   return as_bf16x8(w);
+}
+
+// Four consecutive results at element idx of a bf16 (nearest even) or fp32 output.
+template <bool F32>
+__device__ __forceinline__ void store4(void* base, size_t idx, float a, float b, float c, float d) {
+  if constexpr (F32)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{a, b, c, d};
+  else
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
 // Byte offset, inside a staged [32 rows x DH] bf16 tile, of row r's 16-byte
@@ -174,12 +194,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int DH, int G>
+template <int DH, int G, bool F32OUT>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
     const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
-    int Hq, int Hkv, int nkb, int total_wg, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int Hq, int Hkv, int nkb, int total_wg, void* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ dbp, float* __restrict__ gpart, float* __restrict__ tpart) {
   constexpr int KS = DH / 16;       // k-steps over dh
   constexpr int DT = DH / 32;       // 32-row blocks of dK^T and dV^T
@@ -374,8 +394,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         dVt[blk][r] += mine[((blk * 2 + 1) * 16 + r) * 64 + lane];
       }
     if (j_ok) {
-      uint16_t* kp = dk + (((size_t)b * M + j) * Hkv + g) * DH;
-      uint16_t* vp = dv + (((size_t)b * M + j) * Hkv + g) * DH;
+      const size_t row = (((size_t)b * M + j) * Hkv + g) * DH;
 #pragma unroll
       for (int blk = 0; blk < DT; ++blk)
 #pragma unroll
@@ -383,11 +402,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
           const int d0 = 32 * blk + 8 * i4 + 4 * gq;
           const int r = 4 * i4;
           // dS carried c log2(e); dk takes the factor ln 2 back
-          *reinterpret_cast<u32x2*>(kp + d0) =
-              u32x2{pack_bf16x2(dKt[blk][r] * kLn2, dKt[blk][r + 1] * kLn2),
-                    pack_bf16x2(dKt[blk][r + 2] * kLn2, dKt[blk][r + 3] * kLn2)};
-          *reinterpret_cast<u32x2*>(vp + d0) = u32x2{pack_bf16x2(dVt[blk][r], dVt[blk][r + 1]),
-                                                     pack_bf16x2(dVt[blk][r + 2], dVt[blk][r + 3])};
+          store4<F32OUT>(dk, row + d0, dKt[blk][r] * kLn2, dKt[blk][r + 1] * kLn2, dKt[blk][r + 2] * kLn2,
+                         dKt[blk][r + 3] * kLn2);
+          store4<false>(dv, row + d0, dVt[blk][r], dVt[blk][r + 1], dVt[blk][r + 2], dVt[blk][r + 3]);
         }
     }
     float dbs = 0.0f;
@@ -418,12 +435,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int DH, int G>
+template <int DH, int G, bool F32OUT>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
     const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
-    int Hq, int Hkv, int nqb, int total_wg, uint16_t* __restrict__ dq) {
+    int Hq, int Hkv, int nqb, int total_wg, void* __restrict__ dq) {
   constexpr int RG = 4 / G;
   constexpr int BQ = 32 * RG;
   constexpr int KS = DH / 16, DT = DH / 32;
@@ -547,16 +564,55 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   }
   if (q_ok) {
     const float sc = cq * kLn2;  // c_i (the exponent constant carries log2(e))
-    uint16_t* qp = dq + (((size_t)b * M + qi) * Hq + h) * DH;
+    const size_t row = (((size_t)b * M + qi) * Hq + h) * DH;
 #pragma unroll
     for (int blk = 0; blk < DT; ++blk)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d0 = 32 * blk + 8 * i4 + 4 * gq;
         const int r = 4 * i4;
-        *reinterpret_cast<u32x2*>(qp + d0) = u32x2{pack_bf16x2(dQt[blk][r] * sc, dQt[blk][r + 1] * sc),
-                                                   pack_bf16x2(dQt[blk][r + 2] * sc, dQt[blk][r + 3] * sc)};
+        store4<F32OUT>(dq, row + d0, dQt[blk][r] * sc, dQt[blk][r + 1] * sc, dQt[blk][r + 2] * sc,
+                       dQt[blk][r + 3] * sc);
       }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rotary embedding for the backward of the rotary variant, per 64-row block
+// of KV head g: ROTATE_BACK false rotates the K row of head g and the Q rows
+// of its G query heads into bf16 copies, exactly as the forward's prepass
+// does (so the products see the forward's operands); true applies the
+// transposed rotation to the fp32 gradients with respect to the rotated q
+// and k and rounds them to bf16.
+template <int DH, bool ROTATE_BACK>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rope_kernel(const void* __restrict__ q_in,
+                                                                const void* __restrict__ k_in,
+                                                                const int32_t* __restrict__ pos, double base, int M,
+                                                                int Hq, int Hkv, uint16_t* __restrict__ q_out,
+                                                                uint16_t* __restrict__ k_out) {
+  __shared__ double s_freq[DH / 2];
+  constexpr int PG = DH / 16;  // groups of 8 pairs per head row
+  const int m0 = blockIdx.x * kPB, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  if (threadIdx.x < DH / 2) s_freq[threadIdx.x] = rope::inv_freq(base, threadIdx.x, DH);
+  __syncthreads();
+  for (int t = threadIdx.x; t < kPB * PG; t += kBwdThreads) {
+    const int m = m0 + t / PG, i0 = (t % PG) * 8;
+    if (m >= M) continue;
+    float c[8], sn[8];
+    rope::sincos8((double)pos[(size_t)b * M + m], s_freq, i0, c, sn);
+    const size_t krow = (((size_t)b * M + m) * Hkv + g) * DH;
+    if constexpr (ROTATE_BACK)
+      rope::row8_transposed<DH>(static_cast<const float*>(k_in) + krow, k_out + krow, i0, c, sn);
+    else
+      rope::row8<DH>(static_cast<const uint16_t*>(k_in) + krow, k_out + krow, i0, c, sn);
+    for (int hh = 0; hh < G; ++hh) {
+      const size_t qrow = (((size_t)b * M + m) * Hq + g * G + hh) * DH;
+      if constexpr (ROTATE_BACK)
+        rope::row8_transposed<DH>(static_cast<const float*>(q_in) + qrow, q_out + qrow, i0, c, sn);
+      else
+        rope::row8<DH>(static_cast<const uint16_t*>(q_in) + qrow, q_out + qrow, i0, c, sn);
+    }
   }
 }
 
@@ -599,8 +655,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const float* __
 template <int DH, int G>
 hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                         const float* lse, const uint16_t* dout, int B, int M, int Hq, int Hkv, const float* ks,
-                        const int32_t* pos, const float* gain, const float* temp, float sm_scale, uint16_t* dq,
-                        uint16_t* dk, uint16_t* dv, float* db, float* dgain, float* dtemp, void* ws, hipStream_t s) {
+                        const int32_t* pos, const float* gain, const float* temp, float sm_scale, double rope_base,
+                        uint16_t* dq, uint16_t* dk, uint16_t* dv, float* db, float* dgain, float* dtemp, void* ws,
+                        hipStream_t s) {
   const int Mp = (M + kPB - 1) / kPB * kPB;
   const int nkb = Mp / kKB;
   const size_t rn = (size_t)B * Hq * Mp;
@@ -610,8 +667,22 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   float* dbp = rowD + rn;
   float* gpart = dbp + (size_t)B * Hkv * Mp;
   float* tpart = gpart + (size_t)B * nkb * Hq;
+  // rotary variant: rotated bf16 q and k, then fp32 gradients with respect to them
+  const bool rope = rope_base > 0.0;
+  unsigned char* rws = static_cast<unsigned char*>(ws) + rope_ws_offset(B, M, Hq, Hkv, DH);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(rws);
+  uint16_t* kr = qr + (size_t)B * M * Hq * DH;
+  float* dq32 = reinterpret_cast<float*>(kr + (size_t)B * M * Hkv * DH);
+  float* dk32 = dq32 + (size_t)B * M * Hq * DH;
 
   if (M > 0) {
+    const dim3 rope_grid(Mp / kPB, Hkv, B);
+    if (rope) {
+      hipLaunchKernelGGL((bwd_rope_kernel<DH, false>), rope_grid, dim3(kBwdThreads), 0, s, q, k, pos, rope_base, M,
+                         Hq, Hkv, qr, kr);
+      q = qr;
+      k = kr;
+    }
     hipLaunchKernelGGL((bwd_rows_kernel<DH>), dim3(Mp / kPB, Hq, B), dim3(kBwdThreads), 0, s, o, dout, lse, pos,
                        temp, sm_scale, M, Mp, Hq, rowc, rowl, rowD);
     hipError_t e = hipGetLastError();
@@ -620,14 +691,28 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     const int nqb = (M + 32 * (4 / G) - 1) / (32 * (4 / G));
     const long long tb = (long long)nqb * Hkv * B;
     if (ta > 0x7FFFFFFF || tb > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
-                       rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart);
+    if (rope)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, true>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk32, dv, dbp, gpart, tpart);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<DH, G>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
-                       rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq);
+    if (rope)
+      hipLaunchKernelGGL((bwd_dq_kernel<DH, G, true>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq32);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (rope) {
+      hipLaunchKernelGGL((bwd_rope_kernel<DH, true>), rope_grid, dim3(kBwdThreads), 0, s, dq32, dk32, pos,
+                         rope_base, M, Hq, Hkv, dq, dk);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   const size_t n = (size_t)B * M;
   const unsigned grid = (unsigned)((n + kBwdThreads - 1) / kBwdThreads) + 1;
@@ -643,21 +728,28 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh) {
   (void)dh;
   if (M <= 0) return 0;
-  const size_t Mp = (size_t)(M + kPB - 1) / kPB * kPB;
-  return (size_t)B * Mp * ((size_t)3 * Hq * 4 + (size_t)Hkv * 4) + (size_t)2 * B * (Mp / kKB) * Hq * 4;
+  return base_ws_bytes(B, M, Hq, Hkv);
+}
+
+// ... rounded up to 16 bytes, then the rotated q and k (bf16) and the fp32
+// gradients with respect to them
+size_t gated_attention_rope_backward_workspace(int B, int M, int Hq, int Hkv, int dh) {
+  if (M <= 0) return 0;
+  return rope_ws_offset(B, M, Hq, Hkv, dh) + (size_t)B * M * (Hq + Hkv) * dh * (2 + 4);
 }
 
 hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                            const uint16_t* out, const float* lse, const uint16_t* d_out, int B, int M,
                                            int Hq, int Hkv, int dh, const float* key_score, const int32_t* pos,
-                                           const float* gain, const float* temp, float sm_scale, uint16_t* dq,
+                                           const float* gain, const float* temp, float sm_scale, double rope_base,
+                                           uint16_t* dq,
                                            uint16_t* dk, uint16_t* dv, float* d_key_score, float* d_gain,
                                            float* d_temp, void* ws, hipStream_t s) {
   const int G = Hq / Hkv;
 #define TG_BWD_CASE(DHV, GV)                                                                                        \
   if (dh == DHV && G == GV)                                                                                         \
-    return launch_bwd_t<DHV, GV>(q, k, v, out, lse, d_out, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, dq, \
-                                 dk, dv, d_key_score, d_gain, d_temp, ws, s);
+    return launch_bwd_t<DHV, GV>(q, k, v, out, lse, d_out, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale,   \
+                                 rope_base, dq, dk, dv, d_key_score, d_gain, d_temp, ws, s);
   TG_BWD_CASE(128, 2)
   TG_BWD_CASE(128, 1)
   TG_BWD_CASE(128, 4)

@@ -71,6 +71,12 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
     return tg::gated_attention_backward_workspace(B, N, h, d / K, K);
   }
+  if (op == TG_OP_GATED_ATTENTION_ROPE_BACKWARD) {
+    // as TG_OP_GATED_ATTENTION_BACKWARD, then the rotated q and k (bf16) and
+    // the fp32 gradients with respect to them
+    if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K <= 0 || d % K != 0) return 0;
+    return tg::gated_attention_rope_backward_workspace(B, N, h, d / K, K);
+  }
   return 0;
 }
 
@@ -300,12 +306,11 @@ int tg_gated_attention_rope(const void* q, const void* k, const void* v, int B, 
                                 temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
 }
 
-int tg_gated_attention_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+static int attention_backward_common(const char* name, const void* q, const void* k, const void* v, const void* out, const float* lse,
                                 const void* d_out, int B, int M, int Hq, int Hkv, int d_h, const float* key_score,
-                                const int32_t* pos, const float* gain, const float* temp, float sm_scale, void* d_q,
+                                const int32_t* pos, const float* gain, const float* temp, float sm_scale, double rope_base, void* d_q,
                                 void* d_k, void* d_v, float* d_key_score, float* d_gain, float* d_temp, void* ws,
                                 size_t ws_bytes, void* stream) {
-  const char* name = "tg_gated_attention_backward";
   if (B <= 0 || B > 65535 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
   if (!gain || !temp || !d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
@@ -327,7 +332,8 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v, con
     if ((long long)M * Hq * d_h * 2 >= (1LL << 31) || Mp * d_h * 2 >= (1LL << 31) ||
         (long long)B * Hq * Mp * 4 >= (1LL << 31))
       return fail(TG_EUNSUPPORTED, "%s: M=%d too large", name, M);
-    const size_t need = tg::gated_attention_backward_workspace(B, M, Hq, Hkv, d_h);
+    const size_t need = rope_base > 0.0 ? tg::gated_attention_rope_backward_workspace(B, M, Hq, Hkv, d_h)
+                                        : tg::gated_attention_backward_workspace(B, M, Hq, Hkv, d_h);
     if (!ws || ws_bytes < need)
       return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
     if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
@@ -336,9 +342,32 @@ int tg_gated_attention_backward(const void* q, const void* k, const void* v, con
       tg::launch_gated_attention_backward(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
           static_cast<const uint16_t*>(out), lse, static_cast<const uint16_t*>(d_out), B, M, Hq, Hkv, d_h, key_score,
-          pos, gain, temp, sm_scale, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
+          pos, gain, temp, sm_scale, rope_base, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
           static_cast<uint16_t*>(d_v), d_key_score, d_gain, d_temp, ws, reinterpret_cast<hipStream_t>(stream)),
       name);
+}
+
+int tg_gated_attention_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                const void* d_out, int B, int M, int Hq, int Hkv, int d_h, const float* key_score,
+                                const int32_t* pos, const float* gain, const float* temp, float sm_scale, void* d_q,
+                                void* d_k, void* d_v, float* d_key_score, float* d_gain, float* d_temp, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return attention_backward_common("tg_gated_attention_backward", q, k, v, out, lse, d_out, B, M, Hq, Hkv, d_h,
+                                   key_score, pos, gain, temp, sm_scale, 0.0, d_q, d_k, d_v, d_key_score, d_gain,
+                                   d_temp, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_rope_backward(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                     const void* d_out, int B, int M, int Hq, int Hkv, int d_h,
+                                     const float* key_score, const int32_t* pos, const float* gain,
+                                     const float* temp, float sm_scale, double rope_base, void* d_q, void* d_k,
+                                     void* d_v, float* d_key_score, float* d_gain, float* d_temp, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!(rope_base > 1.0) || !(rope_base < 1e300))
+    return fail(TG_EINVAL, "tg_gated_attention_rope_backward: rope_base must be finite and > 1");
+  return attention_backward_common("tg_gated_attention_rope_backward", q, k, v, out, lse, d_out, B, M, Hq, Hkv, d_h,
+                                   key_score, pos, gain, temp, sm_scale, rope_base, d_q, d_k, d_v, d_key_score,
+                                   d_gain, d_temp, ws, ws_bytes, stream);
 }
 
 int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, int B, int N, int Hkv, int d_h,

@@ -65,10 +65,12 @@ size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh);
 hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                            const uint16_t* out, const float* lse, const uint16_t* d_out, int B, int M,
                                            int Hq, int Hkv, int dh, const float* key_score, const int32_t* pos,
-                                           const float* gain, const float* temp, float sm_scale, uint16_t* dq,
+                                           const float* gain, const float* temp, float sm_scale, double rope_base,
+                                           uint16_t* dq,
                                            uint16_t* dk, uint16_t* dv, float* d_key_score, float* d_gain,
                                            float* d_temp, void* ws, hipStream_t s);
 size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh);
+size_t gated_attention_rope_backward_workspace(int B, int M, int Hq, int Hkv, int dh);
 
 // Row gather of the K and V caches of n_layers layers to the kept set.
 hipError_t launch_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, int B, int N, int Hkv,

@@ -9,6 +9,7 @@ from .tokengate_ref import (  # noqa: F401
     gated_attention,
     gated_attention_gate_form,
     gated_attention_rope,
+    gated_attention_rope_backward,
     gated_attention_backward,
     gated_attention_backward_l1,
     kv_cache_prune,

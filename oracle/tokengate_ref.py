@@ -462,3 +462,25 @@ def kv_cache_prune(k_cache, v_cache, kept_idx):
         k_out[:, b] = k_cache[:, b, idx[b]]
         v_out[:, b] = v_cache[:, b, idx[b]]
     return k_out, v_out
+
+
+# --------------------------------------------------------------------------
+# Backward of the rotary variant: the gradients with respect to the rotated
+# q' = R q, k' = R k (the backward above, on the rotated operands), mapped
+# back by the transposed rotation R^T, i.e. the rotation by minus the angle.
+# With round_qk, q' and k' are rounded to bf16 as the forward rounds them and
+# that rounding is passed through as the identity (the straight-through
+# reading of a rounding step); without it, the composition is differentiated
+# exactly (used by the finite-difference pin).
+# --------------------------------------------------------------------------
+def gated_attention_rope_backward(q, k, v, b_S, pos, gain, temp, sm_scale: float, base: float, O, lse, dO,
+                                  round_qk: bool = True):
+    """Return ``(dq, dk, dv, db, dgain, dtemp)`` in float64 (dq, dk with
+    respect to the un-rotated q, k)."""
+    qr = rope(q, pos, base)
+    kr = rope(k, pos, base)
+    if round_qk:
+        qr, kr = bf16_round(qr), bf16_round(kr)
+    dqr, dkr, dv, db, dgain, dtemp = gated_attention_backward(qr, kr, v, b_S, pos, gain, temp, sm_scale, O, lse, dO)
+    neg = -np.asarray(pos, np.float64)
+    return rope(dqr, neg, base), rope(dkr, neg, base), dv, db, dgain, dtemp

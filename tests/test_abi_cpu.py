@@ -264,3 +264,20 @@ def test_span_entry_points_validate_the_span(lib):
     assert lib.tg_gate_score_span(FAKE, tgb.TG_BF16, 1, 100, 256, 10, 120, FAKE, 1e-6, FAKE, FAKE, 64, FAKE, FAKE,
                                   FAKE, FAKE, 1 << 20, None) == tgb.TG_EINVAL
     assert "tg_gate_score_span" in _err(lib)
+
+
+def test_attention_rope_backward_validation(lib):
+    def call(base=1e6, ws_bytes=1 << 30, **kw):
+        a = dict(q=FAKE, M=64)
+        a.update(kw)
+        return lib.tg_gated_attention_rope_backward(a["q"], FAKE, FAKE, FAKE, FAKE, FAKE, 1, a["M"], 16, 8, 128, FAKE,
+                                                    FAKE, FAKE, FAKE, 0.088, base, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                    FAKE, ws_bytes, None)
+
+    assert call(base=1.0) == tgb.TG_EINVAL and "rope_base" in _err(lib)
+    assert call(base=float("nan")) == tgb.TG_EINVAL
+    assert call(q=NULL) == tgb.TG_EINVAL
+    plain = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_BACKWARD, 1, 64, 8 * 128, 16, 128)
+    rope = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE_BACKWARD, 1, 64, 8 * 128, 16, 128)
+    assert rope == (plain + 15) // 16 * 16 + 6 * 64 * 24 * 128
+    assert call(ws_bytes=plain) == tgb.TG_EINVAL and "workspace" in _err(lib)

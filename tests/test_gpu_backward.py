@@ -138,3 +138,38 @@ def test_attention_backward_gradient_of_gpu_forward_is_consistent():
     # the GPU forward's O and lse differ from the oracle's by their own
     # rounding (bf16 O, lse within 1e-4), which moves D and P: looser units
     _check(got, want, l1, "gpu-forward", tol_bf16=2.0 ** -6, tol_f32=1e-2)
+
+
+def _pair_sum(x):
+    """|R^T g| <= |g_j| + |g_{j+d/2}| elementwise (|cos|, |sin| <= 1)."""
+    h = x.shape[-1] // 2
+    s = x[..., :h] + x[..., h:]
+    return np.concatenate([s, s], axis=-1)
+
+
+@pytest.mark.parametrize("dh,Hq,Hkv,M,pos,B,base", [
+    (128, 4, 2, 333, "sparse", 1, 1e6),
+    (128, 16, 8, 130, "sparse", 2, 1e4),
+    (64, 4, 1, 200, "arange", 1, 1e4),
+    (128, 4, 2, 300, "far", 1, 1e6),   # original positions up to 131071
+])
+def test_attention_rope_backward(dh, Hq, Hkv, M, pos, B, base):
+    """The rotary variant: the rotated-frame gradients within the same L1 units,
+    mapped back by the transposed rotation (whose L1 bound is the pair sum)."""
+    say(f"attention rope backward dh={dh} Hq={Hq} Hkv={Hkv} M={M} pos={pos} B={B} base={base:g}")
+    if pos == "far":
+        rng = np.random.default_rng(M)
+        pos = np.sort(rng.choice(131072, size=(B, M), replace=False), axis=1).astype(np.int32)
+    c, b, dO = _inputs(M, Hq, Hkv, dh, pos, B, seed=M * dh + Hq + 23)
+    O, L = oracle.gated_attention_rope(c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale, base)
+    O_bits, L = oracle.bf16_round(O), L.astype(np.float32)
+    got = tg.tg_gated_attention_rope_backward(dev_bits(c.q), dev_bits(c.k), dev_bits(c.v), dev_bits(O_bits), dev(L),
+                                              dev_bits(dO), dev(b), dev(c.pos), dev(c.gain), dev(c.temp), base,
+                                              c.sm_scale)
+    want = oracle.gated_attention_rope_backward(c.q, c.k, c.v, b, c.pos, c.gain, c.temp, c.sm_scale, base, O_bits, L,
+                                                dO)
+    qr = oracle.bf16_round(oracle.rope(c.q, c.pos, base))
+    kr = oracle.bf16_round(oracle.rope(c.k, c.pos, base))
+    l1 = list(oracle.gated_attention_backward_l1(qr, kr, c.v, b, c.pos, c.gain, c.temp, c.sm_scale, O_bits, L, dO))
+    l1[0], l1[1] = _pair_sum(l1[0]), _pair_sum(l1[1])
+    _check(got, want, l1, f"rope M={M}")

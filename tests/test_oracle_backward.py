@@ -132,3 +132,39 @@ def test_l1_scales_bound_the_gradients():
     gp = oracle.gated_attention_backward(q, k, v, b, pos, gain, temp, sm, O, lse, dOp)
     lp = oracle.gated_attention_backward_l1(q, k, v, b, pos, gain, temp, sm, O, lse, dOp)
     np.testing.assert_allclose(gp[2], lp[2], rtol=1e-13)
+
+
+def test_rope_backward_matches_finite_differences():
+    """The rotary variant without the bf16 rounding of q', k': central
+    differences of sum(dO * O) with O = Eq. 8 on rope(q), rope(k)."""
+    q, k, v, b, pos, gain, temp, sm, dO = _case(11, B=1, M=5, Hq=2, Hkv=1, dh=4)
+    base = 100.0
+    pos = pos * 37  # angles well away from 0
+
+    def loss(qx, kx):
+        O, _ = oracle.gated_attention(oracle.rope(qx, pos, base), oracle.rope(kx, pos, base), v, b, pos, gain, temp,
+                                      sm)
+        return float(np.sum(O * dO))
+
+    O, lse = oracle.gated_attention(oracle.rope(q, pos, base), oracle.rope(k, pos, base), v, b, pos, gain, temp, sm)
+    dq, dk, *_ = oracle.gated_attention_rope_backward(q, k, v, b, pos, gain, temp, sm, base, O, lse, dO,
+                                                      round_qk=False)
+    h = 1e-5
+    for x, g, which in ((q, dq, 0), (k, dk, 1)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = ((loss(xp, k) - loss(xm, k)) if which == 0 else (loss(q, xp) - loss(q, xm))) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_rope_backward_at_position_zero_is_the_plain_backward():
+    q, k, v, b, _, gain, temp, sm, dO = _case(12, B=1, M=6, Hq=4, Hkv=2, dh=8)
+    pos = np.zeros((1, 6), np.int64)
+    O, lse = oracle.gated_attention(q, k, v, b, pos, gain, temp, sm)
+    a = oracle.gated_attention_rope_backward(q, k, v, b, pos, gain, temp, sm, 1e4, O, lse, dO, round_qk=False)
+    p = oracle.gated_attention_backward(q, k, v, b, pos, gain, temp, sm, O, lse, dO)
+    for x, y in zip(a, p):
+        np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-15)
