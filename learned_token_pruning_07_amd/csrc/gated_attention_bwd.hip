@@ -116,16 +116,26 @@ typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 // of the B fragment it meets).  Lane j of each 16-lane group points at row
 // base + (j >> 2), columns c0 + 4 (j & 3) .. + 3.
 template <int DH>
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int blk, int s, int lane) {
+__device__ __forceinline__ int tr_off(int blk, int s, int hf, int lane) {
   const int j = lane & 15, gq = lane >> 5;
   const int col = 32 * blk + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int row = 16 * s + 8 * hf + 4 * gq + (j >> 2);
+  return row * (2 * DH) + (((col >> 3) ^ (row & 7)) << 4) + (((col >> 2) & 1) << 3);
+}
+// the same fragment from precomputed offsets (tr_off of hf = 0 and 1)
+__device__ __forceinline__ bf16x8 tr_frag_at(const unsigned char* tile, int off0, int off1) {
+  const v4s h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(tile + off0));
+  const v4s h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(tile + off1));
+  const u32x4 w = {__builtin_bit_cast(u32x2, h0)[0], __builtin_bit_cast(u32x2, h0)[1],
+                   __builtin_bit_cast(u32x2, h1)[0], __builtin_bit_cast(u32x2, h1)[1]};
+  return as_bf16x8(w);
+}
+template <int DH>
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* tile, int blk, int s, int lane) {
   v4s h[2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int row = 16 * s + 8 * hf + 4 * gq + (j >> 2);
-    const int off = row * (2 * DH) + (((col >> 3) ^ (row & 7)) << 4) + (((col >> 2) & 1) << 3);
-    h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(tile + off));
-  }
+  for (int hf = 0; hf < 2; ++hf)
+    h[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(tile + tr_off<DH>(blk, s, hf, lane)));
   const u32x4 w = {__builtin_bit_cast(u32x2, h[0])[0], __builtin_bit_cast(u32x2, h[0])[1],
                    __builtin_bit_cast(u32x2, h[1])[0], __builtin_bit_cast(u32x2, h[1])[1]};
   return as_bf16x8(w);
@@ -507,6 +517,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dQt[i][r] = 0.0f;
 
+  int toff[DT][2][2];  // transpose-load offsets of the K^T fragments, fixed per lane
+#pragma unroll
+  for (int blk = 0; blk < DT; ++blk)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) toff[blk][s][hf] = tr_off<DH>(blk, s, hf, lane);
   auto step_dq = [&](const unsigned char* base, int t) __attribute__((always_inline)) {
     f32x16 S, dP;
 #pragma unroll
@@ -543,7 +560,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int s = 0; s < 2; ++s) {
       const bf16x8 zb = pack8(Z + 8 * s);
 #pragma unroll
-      for (int blk = 0; blk < DT; ++blk) dQt[blk] = mfma(tr_frag<DH>(base, blk, s, lane), zb, dQt[blk]);
+      for (int blk = 0; blk < DT; ++blk)
+        dQt[blk] = mfma(tr_frag_at(base, toff[blk][s][0], toff[blk][s][1]), zb, dQt[blk]);
     }
   };
 

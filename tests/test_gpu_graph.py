@@ -1,6 +1,7 @@
 """The gated-prefill stage captured as one HIP graph: the gate (score, then
-selection and compaction in one call) and two token-gated attention layers on
-the compacted stream, replayed several times.  Each replay must reproduce the
+selection and compaction in one call), two token-gated attention layers on
+the compacted stream, the second layer's backward and the KV-cache pruning of
+two lower layers, replayed several times.  Each replay must reproduce the
 eager results bit for bit, also after the input buffer is refilled between
 replays (the graph reads the buffers live) and with eager work and
 synchronisations between the replays.  The library's calls launch kernels
@@ -49,6 +50,17 @@ class Stage:
         self.temp = torch.full((HQ,), 1.2, device=DEV)
         self.out = [torch.empty((1, M, HQ, DH), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
         self.attn_ws = tg.attention_workspace(1, M, HQ, HKV, DH, DEV)
+        self.lse = torch.empty((1, HQ, M), dtype=torch.float32, device=DEV)
+        # the last layer's backward and the KV-cache pruning of two lower layers
+        self.d_out = torch.randn(1, M, HQ, DH, device=DEV, generator=g).bfloat16()
+        self.grads = [torch.empty((1, M, HQ, DH), dtype=torch.bfloat16, device=DEV),
+                      torch.empty((1, M, HKV, DH), dtype=torch.bfloat16, device=DEV),
+                      torch.empty((1, M, HKV, DH), dtype=torch.bfloat16, device=DEV),
+                      torch.empty((1, M), dtype=torch.float32, device=DEV), torch.empty(HQ, device=DEV),
+                      torch.empty(HQ, device=DEV)]
+        self.bwd_ws = tg.attention_backward_workspace(1, M, HQ, HKV, DH, DEV)
+        self.kv = [torch.randn(2, 1, N, HKV, DH, device=DEV, generator=g).bfloat16() for _ in range(2)]
+        self.kv_out = [torch.empty((2, 1, M, HKV, DH), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
 
     def run(self):
         w, c = self.w, self.c
@@ -59,15 +71,20 @@ class Stage:
         for l in range(2):
             q, k, v = self.qkv[l]
             tg.tg_gated_attention(q, k, v, self.b_S, self.kept_idx, self.gain[l], self.temp, out=self.out[l],
-                                  ws=self.attn_ws)
+                                  lse=self.lse if l == 1 else None, ws=self.attn_ws)
+        q, k, v = self.qkv[1]
+        tg.tg_gated_attention_backward(q, k, v, self.out[1], self.lse, self.d_out, self.b_S, self.kept_idx,
+                                       self.gain[1], self.temp, None, *self.grads, ws=self.bwd_ws)
+        tg.tg_kv_cache_prune(self.kv[0], self.kv[1], self.kept_idx, k_out=self.kv_out[0], v_out=self.kv_out[1])
 
     def results(self):
-        return [t.clone() for t in (self.score, self.keep, self.kept_idx, self.resid_S, self.b_S, *self.out)]
+        return [t.clone() for t in (self.score, self.keep, self.kept_idx, self.resid_S, self.b_S, *self.out, self.lse,
+                                    *self.grads, *self.kv_out)]
 
     def poison(self):
-        for t in (self.score, self.b_S):
+        for t in (self.score, self.b_S, self.lse, *self.grads[3:]):
             t.fill_(float("nan"))
-        for t in (self.keep, self.kept_idx, self.resid_S, *self.out):
+        for t in (self.keep, self.kept_idx, self.resid_S, *self.out, *self.grads[:3], *self.kv_out):
             t.view(torch.uint8).fill_(0xA5)
 
 
