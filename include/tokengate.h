@@ -214,6 +214,38 @@ int tg_gate_select_span(const float* score_raw, int B, int N, int span_begin,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tg_gate_select_varlen -- tg_gate_select_span for a batch whose sequences
+ * differ in length, in the position of the prunable document and in the
+ * budget (serving batches several prompts; page 3's interface marks each
+ * prompt's document and takes a kept-token budget).  Row b of the padded
+ * [B, N] inputs holds a sequence of seq_len[b] tokens whose prunable span is
+ * [span_begin[b], span_end[b]) with budget K[b]; its tokens at or past
+ * seq_len[b] are padding: score 0, keep 0, never kept.  The row keeps
+ *     M_b = seq_len[b] - P_b + min(K[b], P_b)   tokens, P_b = span_end[b] - span_begin[b],
+ * written packed at rows cu_kept[b] .. cu_kept[b+1]-1 of kept_idx (indices
+ * within the row), resid_out and score_out, in the order of the span
+ * entry points.
+ *
+ *   seq_len, span_begin, span_end, K [B] and cu_kept [B + 1]: int32 DEVICE
+ *                    arrays (cu_kept[0] = 0, cu_kept[b+1] = cu_kept[b] + M_b);
+ *                    values are clamped into 0 <= span_begin <= span_end <=
+ *                    seq_len <= N and K >= 0, and a row never writes more
+ *                    than cu_kept[b+1] - cu_kept[b] kept tokens
+ *   max_kept         host int, at least every M_b (sizes the gather's grid)
+ *   score [B, N], keep [B, N]: as tg_gate_select (per row)
+ *   kept_idx [cu_kept[B]] int32, resid_out [cu_kept[B], d], score_out
+ *                    [cu_kept[B]] fp32: packed outputs
+ * Rows of up to 32768 tokens (one workgroup per row); no workspace.
+ */
+int tg_gate_select_varlen(const float* score_raw, int B, int N,
+                          const int32_t* seq_len, const int32_t* span_begin,
+                          const int32_t* span_end, const int32_t* K,
+                          const int32_t* cu_kept, int max_kept, float eps_seq,
+                          const void* resid, int dt, int d, float* score,
+                          uint8_t* keep, int32_t* kept_idx, void* resid_out,
+                          float* score_out, void* stream);
+
+/*
  * tg_gated_attention -- token-gated causal GQA attention over the kept set
  * (paper Section 4: token-gated attention Eq. 5, head-wise gain Eq. 6,
  * temperature Eq. 7, combined as the key-bias form Eq. 8; Appendix C.4).

@@ -26,7 +26,7 @@ TG_F32, TG_BF16 = 0, 1
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
-            "tg_topk_select_span", "tg_gate_select_span", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -63,6 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
     lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
@@ -73,7 +74,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
-                 "tg_gate_select_span"):
+                 "tg_gate_select_span", "tg_gate_select_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -296,6 +297,49 @@ def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, scor
     else:
         _check(lib.tg_gate_select_span(_ptr(score_raw), B, N, r, span_end, *rest))
     return kept_idx, resid_out, score_out, keep, score
+
+
+def varlen_kept_counts(seq_len, span_begin, span_end, K):
+    """Host-side M_b = len_b - P_b + min(K_b, P_b) of a varying-length batch
+    (lists or arrays of ints), with the same clamping as the kernel."""
+    out = []
+    for n, p0, p1, k in zip(seq_len, span_begin, span_end, K):
+        p1 = min(max(int(p1), 0), int(n))
+        p0 = min(max(int(p0), 0), p1)
+        P = p1 - p0
+        out.append(int(n) - P + min(max(int(k), 0), P))
+    return out
+
+
+def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, eps_seq: float = 1e-6, score=None,
+                          keep=None, stream=None):
+    """Gate selection of a batch of sequences of different lengths, spans and
+    budgets (per-row host lists).  Returns ``(kept_idx, resid_out, score_out,
+    keep, score, cu_kept)`` with the kept rows packed: row b's are
+    ``cu_kept[b] .. cu_kept[b+1]-1`` (``cu_kept`` a host list)."""
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    dev = resid.device
+    Ms = varlen_kept_counts(seq_len, span_begin, span_end, K)
+    cu = [0]
+    for m in Ms:
+        cu.append(cu[-1] + m)
+    T = cu[-1]
+    arr = lambda x: torch.tensor([int(v) for v in x], dtype=torch.int32, device=dev)  # noqa: E731
+    rows = [arr(seq_len), arr(span_begin), arr(span_end), arr(K), arr(cu)]
+    if score is None:
+        score = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, N), dtype=torch.uint8, device=dev)
+    kept_idx = torch.empty((max(T, 1),), dtype=torch.int32, device=dev)
+    resid_out = torch.empty((max(T, 1), d), dtype=resid.dtype, device=dev)
+    score_out = torch.empty((max(T, 1),), dtype=torch.float32, device=dev)
+    _check(lib.tg_gate_select_varlen(_ptr(score_raw), B, N, *[_ptr(t) for t in rows], max(Ms) if Ms else 0, eps_seq,
+                                     _ptr(resid), _dt(resid), d, _ptr(score), _ptr(keep), _ptr(kept_idx),
+                                     _ptr(resid_out), _ptr(score_out), _stream(stream)))
+    return kept_idx[:T], resid_out[:T], score_out[:T], keep, score, cu
 
 
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:

@@ -139,6 +139,41 @@ __global__ __launch_bounds__(kGatherThreads) void compact_gather_kernel(const ui
   }
 }
 
+// Packed rows of varying count: batch row b owns output rows
+// [cu_kept[b], cu_kept[b + 1]); chunk c of row b covers its kept row c / cpr.
+__global__ __launch_bounds__(kGatherThreads) void compact_gather_varlen_kernel(
+    const uint8_t* __restrict__ resid, size_t row_bytes, int N, const int32_t* __restrict__ cu_kept,
+    const int32_t* __restrict__ kept_idx, uint8_t* __restrict__ out) {
+  const int b = blockIdx.y;
+  const size_t cpr = row_bytes / 16;
+  const int o0 = cu_kept[b];
+  const int Mb = cu_kept[b + 1] - o0;
+  const size_t total = Mb > 0 ? (size_t)Mb * cpr : 0;
+  const int32_t* ki = kept_idx + o0;
+  const uint8_t* src = resid + (size_t)b * N * row_bytes;
+  uint8_t* dst = out + (size_t)o0 * row_bytes;
+  const size_t c0 = (size_t)blockIdx.x * kGatherThreads * kGatherUnroll + threadIdx.x;
+  u32x4 v[kGatherUnroll];
+  size_t off_out[kGatherUnroll];
+  bool ok[kGatherUnroll];
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    const size_t c = c0 + (size_t)u * kGatherThreads;
+    ok[u] = o0 >= 0 && c < total;
+    if (ok[u]) {
+      const size_t m = c / cpr, part = c - m * cpr;
+      const int32_t j = ki[m];
+      ok[u] = (uint32_t)j < (uint32_t)N;
+      if (ok[u]) v[u] = load16_stream(src + (size_t)j * row_bytes + part * 16);
+      off_out[u] = m * row_bytes + part * 16;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherUnroll; ++u) {
+    if (ok[u]) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + off_out[u]));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
@@ -149,6 +184,18 @@ hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int
   const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
   hipLaunchKernelGGL(compact_gather_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
                      reinterpret_cast<const uint8_t*>(resid), row_bytes, N, M, kept_idx,
+                     reinterpret_cast<uint8_t*>(resid_out));
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int B, int N, const int32_t* cu_kept,
+                                        int max_kept, const int32_t* kept_idx, void* resid_out, hipStream_t s) {
+  if (max_kept <= 0) return hipSuccess;
+  const size_t total = (size_t)max_kept * (row_bytes / 16);
+  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
+  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  hipLaunchKernelGGL(compact_gather_varlen_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
+                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, cu_kept, kept_idx,
                      reinterpret_cast<uint8_t*>(resid_out));
   return hipGetLastError();
 }

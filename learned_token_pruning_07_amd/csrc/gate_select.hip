@@ -28,8 +28,12 @@ constexpr int kItems = 16;  // consecutive prunable tokens per thread in the fin
 
 // score_raw and score may alias: every raw score is read before the
 // reduction's barriers, and nothing reads score_raw after them.
-__global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* score_raw, int N, int r, int p1, float eps,
-                                                               int K, float* score,
+// With vr.len set, batch row b has its own valid length, span and budget
+// (clamped into range: 0 <= span_begin <= span_end <= len <= N, K >= 0) and
+// writes its kept tokens at kept_idx + cu_kept[b], at most cu_kept[b + 1] -
+// cu_kept[b] of them; tokens at or past len are padding (score 0, not kept).
+__global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* score_raw, int N, int r_all, int p1_all,
+                                                               float eps, int K_all, VarlenRows vr, float* score,
                                                                uint8_t* __restrict__ keep,
                                                                int32_t* __restrict__ kept_idx,
                                                                float* __restrict__ score_kept) {
@@ -42,14 +46,27 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  int Nb = N, r = r_all, p1 = p1_all, K = K_all;
+  if (vr.len != nullptr) {
+    Nb = min(max(vr.len[b], 0), N);
+    p1 = min(max(vr.span_end[b], 0), Nb);
+    r = min(max(vr.span_begin[b], 0), p1);
+    K = max(vr.K[b], 0);
+  }
   const int P = p1 - r;
   const int Kp = K < P ? K : P;
-  const int M = N - P + Kp;
+  const int M = Nb - P + Kp;  // kept tokens of this row
+  size_t out0 = (size_t)b * M;
+  int lim = M;  // ranks this row may write
+  if (vr.len != nullptr) {
+    out0 = (size_t)max(vr.cu_kept[b], 0);
+    lim = min(M, vr.cu_kept[b + 1] - vr.cu_kept[b]);
+  }
   const float* x = score_raw + (size_t)b * N;
   float* y = score + (size_t)b * N;
   uint8_t* kp = keep + (size_t)b * N;
-  int32_t* ki = kept_idx + (size_t)b * M;
-  float* sk = score_kept + (size_t)b * M;
+  int32_t* ki = kept_idx + out0;
+  float* sk = score_kept + out0;
 
   for (int i = tid; i < 2048; i += kThreads) s_hist[i] = 0;
 
@@ -89,20 +106,26 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
   // last (ranks r + K' ...), in order (their scores are 0)
   for (int j = tid; j < r; j += kThreads) {
     kp[j] = 1;
-    ki[j] = j;
-    sk[j] = 0.0f;
+    if (j < lim) {
+      ki[j] = j;
+      sk[j] = 0.0f;
+    }
   }
-  for (int j = p1 + tid; j < N; j += kThreads) {
+  for (int j = p1 + tid; j < Nb; j += kThreads) {
     kp[j] = 1;
-    ki[r + Kp + (j - p1)] = j;
-    sk[r + Kp + (j - p1)] = 0.0f;
+    const int rank = r + Kp + (j - p1);
+    if (rank < lim) {
+      ki[rank] = j;
+      sk[rank] = 0.0f;
+    }
   }
+  for (int j = Nb + tid; j < N; j += kThreads) kp[j] = 0;  // padding of a shorter row
   if (Kp <= 0 || Kp == P) {
     // trivial budgets: every prunable token or none
     const bool all = Kp > 0;
     for (int j = tid; j < P; j += kThreads) {
       kp[r + j] = all ? 1 : 0;
-      if (all) {
+      if (all && r + j < lim) {
         ki[r + j] = r + j;
         sk[r + j] = y[r + j];
       }
@@ -157,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
     // busiest lane has kept tokens, not one per item)
     for (uint32_t f = flags; f != 0u; f &= f - 1u) {
       const int e = __builtin_ctz(f);
-      if ((int)dst < M) {  // exactly M tokens are kept; never write past the row
+      if ((int)dst < lim) {  // exactly M tokens are kept; never write past the row
         const uint32_t key = s_keys[sel::key_slot(j0 + e)];
         ki[dst] = r + j0 + e;
         // the key holds the score exactly, except that -0.0 and +0.0 share a
@@ -199,11 +222,22 @@ hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, int p
     if (e != hipSuccess) return e;
     return launch_compact(resid, row_bytes, B, N, keep, score, M, kept_idx, resid_out, score_kept, s);
   }
-  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, r, p1, eps, K, score, keep,
-                     kept_idx, score_kept);
+  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, r, p1, eps, K, VarlenRows{},
+                     score, keep, kept_idx, score_kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_compact_gather(resid, row_bytes, B, N, M, kept_idx, resid_out, s);
+}
+
+hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,
+                                     const void* resid, size_t row_bytes, float* score, uint8_t* keep,
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, hipStream_t s) {
+  if (N > sel::kRowChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, 0, N, eps, 0, vr, score, keep,
+                     kept_idx, score_kept);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_compact_gather_varlen(resid, row_bytes, B, N, vr.cu_kept, max_kept, kept_idx, resid_out, s);
 }
 
 }  // namespace tg

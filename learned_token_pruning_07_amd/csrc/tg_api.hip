@@ -386,4 +386,30 @@ int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, in
                     name);
 }
 
+int tg_gate_select_varlen(const float* score_raw, int B, int N, const int32_t* seq_len, const int32_t* span_begin,
+                          const int32_t* span_end, const int32_t* K, const int32_t* cu_kept, int max_kept,
+                          float eps_seq, const void* resid, int dt, int d, float* score, uint8_t* keep,
+                          int32_t* kept_idx, void* resid_out, float* score_out, void* stream) {
+  const char* name = "tg_gate_select_varlen";
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
+  if (B <= 0 || B > 65535 || N <= 0 || d <= 0) return fail(TG_EINVAL, "%s: B, N, d must be > 0", name);
+  if (N > 32768) return fail(TG_EUNSUPPORTED, "%s: rows of up to 32768 tokens (N=%d)", name, N);
+  if (max_kept < 0 || max_kept > N) return fail(TG_EINVAL, "%s: max_kept=%d outside [0, N=%d]", name, max_kept, N);
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_seq must be >= 0", name);
+  if (!score_raw || !seq_len || !span_begin || !span_end || !K || !cu_kept || !resid || !score || !keep ||
+      !kept_idx || !resid_out || !score_out)
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
+  const size_t row_bytes = (size_t)d * dt_size(dt);
+  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "%s: row bytes must be a multiple of 16", name);
+  if (!aligned4(score_raw) || !aligned4(score) || !aligned16(resid) || !aligned16(resid_out) ||
+      !aligned4(kept_idx) || !aligned4(score_out) || !aligned4(seq_len) || !aligned4(span_begin) ||
+      !aligned4(span_end) || !aligned4(K) || !aligned4(cu_kept))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  return hip_status(tg::launch_gate_select_varlen(score_raw, B, N,
+                                                  tg::VarlenRows{seq_len, span_begin, span_end, K, cu_kept}, max_kept,
+                                                  eps_seq, resid, row_bytes, score, keep, kept_idx, resid_out,
+                                                  score_out, reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
 }  // extern "C"

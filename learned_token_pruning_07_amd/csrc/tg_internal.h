@@ -39,6 +39,26 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
 hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
                                  const int32_t* kept_idx, void* resid_out, hipStream_t s);
 
+// Per-row lengths, spans, budgets and output offsets of a varying-length
+// batch (device arrays of B, B, B, B and B + 1 entries); all null for a
+// uniform batch.
+struct VarlenRows {
+  const int32_t* len;
+  const int32_t* span_begin;
+  const int32_t* span_end;
+  const int32_t* K;
+  const int32_t* cu_kept;
+};
+
+// out[cu_kept[b] + m] = resid[b, kept_idx[cu_kept[b] + m]] for m < cu_kept[b + 1] - cu_kept[b] <= max_kept
+hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int B, int N, const int32_t* cu_kept,
+                                        int max_kept, const int32_t* kept_idx, void* resid_out, hipStream_t s);
+
+// gate selection of a varying-length batch (rows of up to 32768 tokens)
+hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,
+                                     const void* resid, size_t row_bytes, float* score, uint8_t* keep,
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, hipStream_t s);
+
 // launch_seq_rmsnorm + launch_topk_select + launch_compact in sequence, bit
 // for bit (M = N - P + min(K, P), P = p1 - r); two launches for rows of up to
 // 32768 tokens.

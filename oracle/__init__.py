@@ -6,6 +6,7 @@ benchmark's CPU-baseline leg.  It shares no code with the HIP library.
 from .tokengate_ref import (  # noqa: F401
     compact,
     gate_score,
+    gate_select_varlen,
     gated_attention,
     gated_attention_gate_form,
     gated_attention_rope,

@@ -484,3 +484,35 @@ def gated_attention_rope_backward(q, k, v, b_S, pos, gain, temp, sm_scale: float
     dqr, dkr, dv, db, dgain, dtemp = gated_attention_backward(qr, kr, v, b_S, pos, gain, temp, sm_scale, O, lse, dO)
     neg = -np.asarray(pos, np.float64)
     return rope(dqr, neg, base), rope(dkr, neg, base), dv, db, dgain, dtemp
+
+
+# --------------------------------------------------------------------------
+# A batch of sequences of different lengths, document spans and budgets
+# (padded to a common N): each row is the single-sequence gate on its first
+# seq_len[b] tokens; padding tokens score 0 and are never kept; the kept sets
+# are concatenated in batch order.
+# --------------------------------------------------------------------------
+def gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, eps_seq: float):
+    """Return ``(kept_idx, resid_S, b_S, keep, score, cu_kept)`` with the kept
+    rows of all sequences packed (row b's at cu_kept[b] .. cu_kept[b+1]-1)."""
+    raw = widen(score_raw)
+    res = np.asarray(resid)
+    B, N = raw.shape
+    score = np.zeros((B, N), np.float64)
+    keep = np.zeros((B, N), np.uint8)
+    ki, rows, bs, cu = [], [], [], [0]
+    for b in range(B):
+        n = int(seq_len[b])
+        p1 = min(max(int(span_end[b]), 0), n)
+        p0 = min(max(int(span_begin[b]), 0), p1)
+        k = max(int(K[b]), 0)
+        sc = seq_rmsnorm(raw[b:b + 1, :n], p0, eps_seq, span_end=p1)
+        kp = topk_select(sc, p0, k, span_end=p1)
+        i, r, s = compact(res[b:b + 1, :n], kp, sc)
+        score[b, :n] = sc[0]
+        keep[b, :n] = kp[0]
+        ki.append(i[0])
+        rows.append(r[0])
+        bs.append(s[0])
+        cu.append(cu[-1] + i.shape[1])
+    return np.concatenate(ki), np.concatenate(rows), np.concatenate(bs), keep, score, cu

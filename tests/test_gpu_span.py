@@ -144,3 +144,47 @@ def test_norm_with_nonfinite_scores_keeps_zeros_outside_the_span(N, p0, p1):
         outside[p0:(N if span_end is None else span_end)] = False
         assert np.all(got[0, outside] == 0) and np.all(ref[0, outside] == 0)
         np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+
+
+@pytest.mark.parametrize("dtype,N,rows", [
+    # (seq_len, span_begin, span_end, K) per row
+    ("bf16", 4096, [(4096, 32, 4000, 400), (1500, 0, 1500, 150), (3000, 100, 100, 50), (2048, 64, 2000, 0)]),
+    ("f32", 777, [(777, 10, 700, 70), (300, 5, 250, 500)]),
+    ("bf16", 32768, [(32768, 64, 32768, 3277), (20000, 64, 19000, 2000)]),
+])
+def test_gate_select_varlen(dtype, N, rows):
+    """Each row equals the span entry point on its own first seq_len tokens,
+    bit for bit, with the kept rows packed at the row offsets; and the oracle."""
+    B = len(rows)
+    say(f"gate_select_varlen {dtype} N={N} rows={rows}")
+    lens, p0s, p1s, Ks = (list(x) for x in zip(*rows))
+    rng = np.random.default_rng(N + B)
+    raw = (rng.standard_normal((B, N)) * 3.0).astype(np.float32)
+    d = 256 if dtype == "bf16" else 64
+    c = wl.gate_case(N=N, r=0, d=d, h=8, K=1, dtype=dtype, seed=N + d, B=B)
+    put = dev_bits if dtype == "bf16" else dev
+    resid = put(c.resid)
+    ki, ro, so, keep, score, cu = tg.tg_gate_select_varlen(dev(raw), resid, lens, p0s, p1s, Ks)
+    bits = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()  # noqa: E731
+    for b, (n, p0, p1, K) in enumerate(rows):
+        ki1, ro1, so1, keep1, score1 = tg.tg_gate_select(dev(np.ascontiguousarray(raw[b:b + 1, :n])),
+                                                         resid[b:b + 1, :n].contiguous(), p0, K, span_end=p1)
+        sl = slice(cu[b], cu[b + 1])
+        assert np.array_equal(ki[sl].cpu().numpy(), ki1[0].cpu().numpy())
+        assert np.array_equal(bits(ro[sl]), bits(ro1[0]))
+        assert np.array_equal(bits(so[sl]), bits(so1[0]))
+        assert np.array_equal(keep[b, :n].cpu().numpy(), keep1[0].cpu().numpy())
+        assert np.array_equal(bits(score[b, :n]), bits(score1[0]))
+        assert torch.all(keep[b, n:] == 0) and torch.all(score[b, n:] == 0)
+    # the oracle: scores within the fp32 bar, selection and compaction on the GPU's scores
+    oki, ors, obs, okeep, osc, ocu = oracle.gate_select_varlen(raw, c.resid, lens, p0s, p1s, Ks, 1e-6)
+    assert ocu == cu
+    got = score.cpu().numpy()
+    assert_close(got, osc, TOL_F32, "varlen score")
+    for b, (n, p0, p1, K) in enumerate(rows):
+        k_or = oracle.topk_select(got[b:b + 1, :n], p0, K, span_end=p1)
+        assert np.array_equal(keep[b, :n].cpu().numpy(), k_or[0])
+        i_or, r_or, s_or = oracle.compact(c.resid[b:b + 1, :n], k_or, got[b:b + 1, :n])
+        assert np.array_equal(ki[cu[b]:cu[b + 1]].cpu().numpy(), i_or[0])
+        host_rows = host_bits(ro[cu[b]:cu[b + 1]]) if dtype == "bf16" else ro[cu[b]:cu[b + 1]].cpu().numpy()
+        assert np.array_equal(host_rows.view(np.uint8), r_or[0].view(np.uint8))

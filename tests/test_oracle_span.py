@@ -80,3 +80,34 @@ def test_span_kept_order():
     assert np.array_equal(ki[:p0], np.arange(p0)) and np.array_equal(ki[-(N - p1):], np.arange(p1, N))
     assert np.all(np.diff(ki) > 0) and np.all((ki[p0:p0 + K] >= p0) & (ki[p0:p0 + K] < p1))
     assert np.all(b_S[0, :p0] == 0) and np.all(b_S[0, -(N - p1):] == 0)
+
+
+def test_varlen_uniform_rows_equal_the_batched_gate():
+    """Rows of one length, span and budget give the uniform batched gate."""
+    rng = np.random.default_rng(3)
+    B, N, p0, p1, K = 3, 50, 6, 44, 9
+    raw = rng.standard_normal((B, N))
+    resid = rng.standard_normal((B, N, 8)).astype(np.float32)
+    ki, rs, bs, keep, score, cu = oracle.gate_select_varlen(raw, resid, [N] * B, [p0] * B, [p1] * B, [K] * B, 1e-6)
+    sc = oracle.seq_rmsnorm(raw, p0, 1e-6, span_end=p1)
+    kp = oracle.topk_select(sc, p0, K, span_end=p1)
+    i2, r2, s2 = oracle.compact(resid, kp, sc)
+    assert cu == [0, i2.shape[1], 2 * i2.shape[1], 3 * i2.shape[1]]
+    assert np.array_equal(ki, i2.reshape(-1)) and np.array_equal(rs, r2.reshape(-1, 8))
+    assert np.array_equal(bs, s2.reshape(-1)) and np.array_equal(keep, kp) and np.array_equal(score, sc)
+
+
+def test_varlen_padding_changes_nothing():
+    """Padding tokens (any scores, any rows) past a row's length are ignored."""
+    rng = np.random.default_rng(4)
+    N, n = 60, 41
+    raw = rng.standard_normal((1, N))
+    resid = rng.standard_normal((1, N, 8)).astype(np.float32)
+    a = oracle.gate_select_varlen(raw, resid, [n], [3], [35], [7], 1e-6)
+    raw2, resid2 = raw.copy(), resid.copy()
+    raw2[0, n:] = 1e9
+    resid2[0, n:] = -7.0
+    b = oracle.gate_select_varlen(raw2, resid2, [n], [3], [35], [7], 1e-6)
+    for x, y in zip(a[:5], b[:5]):
+        assert np.array_equal(x, y)
+    assert np.all(a[3][0, n:] == 0) and np.all(a[4][0, n:] == 0)
