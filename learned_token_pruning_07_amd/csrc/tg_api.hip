@@ -80,9 +80,10 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
   return 0;
 }
 
-static int gate_score_common(const char* name, const void* resid, int dt, int B, int N, int d, int r, int p1, const void* norm_w, float eps_row,
-                  const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
-                  void* ws, size_t ws_bytes, void* stream) {
+static int gate_score_common(const char* name, const void* resid, int dt, int B, int N, int d, int r, int p1,
+                             const void* norm_w, float eps_row, const void* W1, const float* b1, int h,
+                             const void* w2, const float* b2, float* score_raw, void* ws, size_t ws_bytes,
+                             void* stream) {
   if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
   if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: B, N, d, h must be > 0", name);
   if (r < 0 || r > p1 || p1 > N)
@@ -120,8 +121,8 @@ static int gate_score_common(const char* name, const void* resid, int dt, int B,
                     name);
 }
 
-static int seq_rmsnorm_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq, float* score, void* ws,
-                   size_t ws_bytes, void* stream) {
+static int seq_rmsnorm_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq,
+                              float* score, void* ws, size_t ws_bytes, void* stream) {
   if (B <= 0 || N <= 0) return fail(TG_EINVAL, "%s: B, N must be > 0", name);
   if (r < 0 || r > p1 || p1 > N)
     return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
@@ -139,8 +140,8 @@ static int seq_rmsnorm_common(const char* name, const float* score_raw, int B, i
                     name);
 }
 
-static int topk_select_common(const char* name, const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws, size_t ws_bytes,
-                   void* stream) {
+static int topk_select_common(const char* name, const float* score, int B, int N, int r, int p1, int K, uint8_t* keep,
+                              void* ws, size_t ws_bytes, void* stream) {
   if (B <= 0 || N <= 0) return fail(TG_EINVAL, "%s: B, N must be > 0", name);
   if (r < 0 || r > p1 || p1 > N)
     return fail(TG_EINVAL, "%s: prunable span [%d, %d) outside [0, N=%d]", name, r, p1, N);
@@ -175,9 +176,9 @@ int tg_compact(const void* resid, int dt, int B, int N, int d, const uint8_t* ke
                     "tg_compact");
 }
 
-static int gate_select_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq, int K, const void* resid, int dt,
-                   int d, float* score, uint8_t* keep, int32_t* kept_idx, void* resid_out, float* score_out,
-                   void* ws, size_t ws_bytes, void* stream) {
+static int gate_select_common(const char* name, const float* score_raw, int B, int N, int r, int p1, float eps_seq,
+                              int K, const void* resid, int dt, int d, float* score, uint8_t* keep, int32_t* kept_idx,
+                              void* resid_out, float* score_out, void* ws, size_t ws_bytes, void* stream) {
   if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
   if (B <= 0 || N <= 0 || d <= 0) return fail(TG_EINVAL, "%s: B, N, d must be > 0", name);
   if (r < 0 || r > p1 || p1 > N)
@@ -306,11 +307,12 @@ int tg_gated_attention_rope(const void* q, const void* k, const void* v, int B, 
                                 temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
 }
 
-static int attention_backward_common(const char* name, const void* q, const void* k, const void* v, const void* out, const float* lse,
-                                const void* d_out, int B, int M, int Hq, int Hkv, int d_h, const float* key_score,
-                                const int32_t* pos, const float* gain, const float* temp, float sm_scale, double rope_base, void* d_q,
-                                void* d_k, void* d_v, float* d_key_score, float* d_gain, float* d_temp, void* ws,
-                                size_t ws_bytes, void* stream) {
+static int attention_backward_common(const char* name, const void* q, const void* k, const void* v, const void* out,
+                                     const float* lse, const void* d_out, int B, int M, int Hq, int Hkv, int d_h,
+                                     const float* key_score, const int32_t* pos, const float* gain, const float* temp,
+                                     float sm_scale, double rope_base, void* d_q, void* d_k, void* d_v,
+                                     float* d_key_score, float* d_gain, float* d_temp, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (B <= 0 || B > 65535 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
   if (!gain || !temp || !d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);

@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kMThreads) void topk_ws_clear_kernel(uint32_t* __re
 // (which every workgroup re-derives from the previous histogram; workgroup 0
 // also records them for the next launch).
 template <int PASS>
-__global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ score, int N, int r, int p1, int Kp,
+__global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ score, int N, int r, int p1,
+                                                              int Kp,
                                                               uint32_t* __restrict__ ws) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_prev[2048];
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __res
 }
 
 // keep: key > T, or key == T among the first k_eq such tokens by index
-__global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __restrict__ score, int N, int r, int p1, int Kp,
+__global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __restrict__ score, int N, int r, int p1,
+                                                               int Kp,
                                                                const uint32_t* __restrict__ ws,
                                                                uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_prev[1024];
