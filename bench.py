@@ -226,8 +226,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; the gated-prefill path runs on a single MI355X "
-              "(multi-GPU sharding is described in DESIGN.md, not run). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: the gated-prefill path is measured on one MI355X only; a multi-GPU run is not "
+              "implemented (the batch and head dimensions shard without communication). Use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
   TG_OK = 0,
   TG_EINVAL = 1,        /* null pointer, bad size, bad alignment */
-  TG_EUNSUPPORTED = 2,  /* a valid request this build does not implement */
+  TG_EUNSUPPORTED = 2,  /* a valid request the library does not implement */
   TG_EHIP = 3           /* a HIP launch or runtime error */
 } tg_status;
 
