@@ -214,6 +214,21 @@ int tg_gate_select_span(const float* score_raw, int B, int N, int span_begin,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tg_gate_score_varlen -- tg_gate_score for a varying-length batch: row b is
+ * scored on its own prunable span [span_begin[b], span_end[b]) (int32 DEVICE
+ * arrays of B entries, clamped into [0, N]); every other token of the row,
+ * padding included, scores 0.  max_span (host) must be at least every span's
+ * length: it sizes the grid, and a longer span is cut to max_span tokens.
+ * Otherwise as tg_gate_score (same workspace).
+ */
+int tg_gate_score_varlen(const void* resid, int dt, int B, int N, int d,
+                         const int32_t* span_begin, const int32_t* span_end,
+                         int max_span, const void* norm_w, float eps_row,
+                         const void* W1, const float* b1, int h,
+                         const void* w2, const float* b2, float* score_raw,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tg_gate_select_varlen -- tg_gate_select_span for a batch whose sequences
  * differ in length, in the position of the prunable document and in the
  * budget (serving batches several prompts; page 3's interface marks each

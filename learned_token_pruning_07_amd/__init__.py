@@ -26,7 +26,7 @@ TG_F32, TG_BF16 = 0, 1
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
-            "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -63,6 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_gate_score_varlen.argtypes = [vp, i, i, i, i, vp, vp, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
     lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
@@ -74,7 +75,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
-                 "tg_gate_select_span", "tg_gate_select_varlen"):
+                 "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -309,6 +310,29 @@ def varlen_kept_counts(seq_len, span_begin, span_end, K):
         P = p1 - p0
         out.append(int(n) - P + min(max(int(k), 0), P))
     return out
+
+
+def tg_gate_score_varlen(resid, span_begin, span_end, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None,
+                         ws=None, stream=None):
+    """Raw scores ``[B, N]`` of a varying-length batch: row b scored on its span
+    ``[span_begin[b], span_end[b])`` (host lists), 0 elsewhere."""
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    h = W1.shape[0]
+    dev = resid.device
+    if score_raw is None:
+        score_raw = torch.empty((B, N), dtype=torch.float32, device=dev)
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    if ws is None:
+        ws = gate_workspace(h, d, dev)
+    sb = torch.tensor([int(x) for x in span_begin], dtype=torch.int32, device=dev)
+    se = torch.tensor([int(x) for x in span_end], dtype=torch.int32, device=dev)
+    max_span = max([max(0, min(int(e), N) - max(0, int(b_))) for b_, e in zip(span_begin, span_end)] + [0])
+    _check(lib.tg_gate_score_varlen(_ptr(resid), _dt(resid), B, N, d, _ptr(sb), _ptr(se), max_span, _ptr(norm_w),
+                                    eps_row, _ptr(W1), _ptr(b1), h, _ptr(w2), _ptr(b2), _ptr(score_raw), _ptr(ws),
+                                    ws.numel(), _stream(stream)))
+    return score_raw
 
 
 def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, eps_seq: float = 1e-6, score=None,

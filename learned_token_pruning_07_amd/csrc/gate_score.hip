@@ -78,7 +78,9 @@ __global__ __launch_bounds__(kThreads) void fold_norm_weight_kernel(const uint16
 
 template <int H, int ROWS, int WAVES, int NCH_FIXED>
 __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
-                                                                   int d, int r, int p1, float eps_row,
+                                                                   int d, int r_in, int p1_in,
+                                                                   const int32_t* __restrict__ span_begin,
+                                                                   const int32_t* __restrict__ span_end, float eps_row,
                                                                    const uint16_t* __restrict__ W1w,
                                                                    const float* __restrict__ b1,
                                                                    const uint16_t* __restrict__ w2,
@@ -98,6 +100,12 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
+  int r = r_in, p1 = p1_in;  // per-row spans of a varying-length batch, clamped into [0, N]
+  if (span_begin != nullptr) {  // (a span longer than the grid's p1_in - r_in rows is cut to it)
+    p1 = min(max(span_end[b], 0), N);
+    r = min(max(span_begin[b], 0), p1);
+    p1 = min(p1, r + (p1_in - r_in));
+  }
   const int row0 = r + blockIdx.x * ROWS;
   float* ob = out + (size_t)b * N;
 
@@ -268,7 +276,10 @@ constexpr int kF32MaxD = 4096;
 constexpr int kF32MaxH = 1024;
 
 __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* __restrict__ resid, int N, int d,
-                                                                  int r, int p1, const float* __restrict__ norm_w,
+                                                                  int r_in, int p1_in,
+                                                                  const int32_t* __restrict__ span_begin,
+                                                                  const int32_t* __restrict__ span_end,
+                                                                  const float* __restrict__ norm_w,
                                                                   float eps_row, const float* __restrict__ W1,
                                                                   const float* __restrict__ b1, int h,
                                                                   const float* __restrict__ w2,
@@ -278,6 +289,12 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
   __shared__ float s_act[kF32Rows][kF32MaxH];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.y;
+  int r = r_in, p1 = p1_in;
+  if (span_begin != nullptr) {  // (a span longer than the grid's p1_in - r_in rows is cut to it)
+    p1 = min(max(span_end[b], 0), N);
+    r = min(max(span_begin[b], 0), p1);
+    p1 = min(p1, r + (p1_in - r_in));
+  }
   const int row0 = r + blockIdx.x * kF32Rows;
   float* ob = out + (size_t)b * N;
   for (int j = blockIdx.x * kThreads + tid; j < r; j += gridDim.x * kThreads) ob[j] = 0.0f;
@@ -322,7 +339,8 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
 }
 
 template <int H, int ROWS, int WAVES>
-hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, int p1, float eps, const uint16_t* W1w,
+hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                       const int32_t* se, float eps, const uint16_t* W1w,
                        const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
   const int P = p1 - r;
   const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
@@ -331,15 +349,16 @@ hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, int p1
   // at the loop's back edge, which would void the prefetch ring
   if (d == 2048)
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 32>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid,
-                       N, d, r, p1, eps, W1w, b1, w2, b2, out);
+                       N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out);
   else
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 0>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid, N,
-                       d, r, p1, eps, W1w, b1, w2, b2, out);
+                       d, r, p1, sb, se, eps, W1w, b1, w2, b2, out);
   return hipGetLastError();
 }
 
 template <int H>
-hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int p1, float eps, const uint16_t* W1w,
+hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                         const int32_t* se, float eps, const uint16_t* W1w,
                          const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
   // Every workgroup streams all of W1w through L1, so W1 bytes per token fall
   // with the tile height: 128-token tiles of 8 waves (each wave with the
@@ -348,16 +367,17 @@ hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int 
   const int P = p1 - r;
   if constexpr (H >= 128) {
     if ((long long)B * ((P + 127) / 128) >= kTallTileMinBlocks)
-      return launch_rows<H, 128, 8>(resid, B, N, d, r, p1, eps, W1w, b1, w2, b2, out, s);
+      return launch_rows<H, 128, 8>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, s);
   }
-  return launch_rows<H, 64, 4>(resid, B, N, d, r, p1, eps, W1w, b1, w2, b2, out, s);
+  return launch_rows<H, 64, 4>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, s);
 }
 
 }  // namespace
 
 size_t gate_score_workspace(int h, int d) { return (size_t)h * d * 2; }
 
-hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1, const uint16_t* norm_w,
+hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                                  const int32_t* se, const uint16_t* norm_w,
                                   float eps_row, const uint16_t* W1, const float* b1, int h, const uint16_t* w2,
                                   const float* b2, float* out, void* ws, hipStream_t s) {
   uint16_t* W1w = static_cast<uint16_t*>(ws);
@@ -367,23 +387,24 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
   if (e != hipSuccess) return e;
   switch (h) {
     case 64:
-      return launch_bf16_h<64>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<64>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
     case 128:
-      return launch_bf16_h<128>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<128>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
     case 256:
-      return launch_bf16_h<256>(resid, B, N, d, r, p1, eps_row, W1w, b1, w2, b2, out, s);
+      return launch_bf16_h<256>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
     default:
       return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1, const float* norm_w,
+hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                                 const int32_t* se, const float* norm_w,
                                  float eps_row, const float* W1, const float* b1, int h, const float* w2,
                                  const float* b2, float* out, hipStream_t s) {
   if (d > kF32MaxD || h > kF32MaxH) return hipErrorInvalidValue;
   const int P = p1 - r;
   const int nblk = P > 0 ? (P + kF32Rows - 1) / kF32Rows : 1;
-  hipLaunchKernelGGL(gate_score_f32_kernel, dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, p1, norm_w, eps_row,
+  hipLaunchKernelGGL(gate_score_f32_kernel, dim3(nblk, B), dim3(kThreads), 0, s, resid, N, d, r, p1, sb, se, norm_w, eps_row,
                      W1, b1, h, w2, b2, out);
   return hipGetLastError();
 }

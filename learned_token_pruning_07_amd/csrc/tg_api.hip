@@ -81,6 +81,7 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
 }
 
 static int gate_score_common(const char* name, const void* resid, int dt, int B, int N, int d, int r, int p1,
+                             const int32_t* sb, const int32_t* se,
                              const void* norm_w, float eps_row, const void* W1, const float* b1, int h,
                              const void* w2, const float* b2, float* score_raw, void* ws, size_t ws_bytes,
                              void* stream) {
@@ -106,7 +107,7 @@ static int gate_score_common(const char* name, const void* resid, int dt, int B,
     if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
     if ((size_t)(p1 - r) * d * 2 > 0x7FFFFFFFull)
       return fail(TG_EUNSUPPORTED, "%s: a batch row above 2 GiB", name);
-    return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r, p1,
+    return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r, p1, sb, se,
                                                  static_cast<const uint16_t*>(norm_w), eps_row,
                                                  static_cast<const uint16_t*>(W1), b1, h,
                                                  static_cast<const uint16_t*>(w2), b2, score_raw, ws, s),
@@ -114,7 +115,7 @@ static int gate_score_common(const char* name, const void* resid, int dt, int B,
   }
   if (d % 4 != 0 || d > 4096 || h > 1024)
     return fail(TG_EUNSUPPORTED, "%s: fp32 needs d %% 4 == 0, d <= 4096, h <= 1024", name);
-  return hip_status(tg::launch_gate_score_f32(static_cast<const float*>(resid), B, N, d, r, p1,
+  return hip_status(tg::launch_gate_score_f32(static_cast<const float*>(resid), B, N, d, r, p1, sb, se,
                                               static_cast<const float*>(norm_w), eps_row,
                                               static_cast<const float*>(W1), b1, h, static_cast<const float*>(w2),
                                               b2, score_raw, s),
@@ -208,14 +209,14 @@ static int gate_select_common(const char* name, const float* score_raw, int B, i
 int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
                   const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
                   void* ws, size_t ws_bytes, void* stream) {
-  return gate_score_common("tg_gate_score", resid, dt, B, N, d, r, N, norm_w, eps_row, W1, b1, h, w2, b2, score_raw,
+  return gate_score_common("tg_gate_score", resid, dt, B, N, d, r, N, nullptr, nullptr, norm_w, eps_row, W1, b1, h, w2, b2, score_raw,
                            ws, ws_bytes, stream);
 }
 
 int tg_gate_score_span(const void* resid, int dt, int B, int N, int d, int span_begin, int span_end,
                        const void* norm_w, float eps_row, const void* W1, const float* b1, int h, const void* w2,
                        const float* b2, float* score_raw, void* ws, size_t ws_bytes, void* stream) {
-  return gate_score_common("tg_gate_score_span", resid, dt, B, N, d, span_begin, span_end, norm_w, eps_row, W1, b1,
+  return gate_score_common("tg_gate_score_span", resid, dt, B, N, d, span_begin, span_end, nullptr, nullptr, norm_w, eps_row, W1, b1,
                            h, w2, b2, score_raw, ws, ws_bytes, stream);
 }
 
@@ -412,6 +413,18 @@ int tg_gate_select_varlen(const float* score_raw, int B, int N, const int32_t* s
                                                   eps_seq, resid, row_bytes, score, keep, kept_idx, resid_out,
                                                   score_out, reinterpret_cast<hipStream_t>(stream)),
                     name);
+}
+
+int tg_gate_score_varlen(const void* resid, int dt, int B, int N, int d, const int32_t* span_begin,
+                         const int32_t* span_end, int max_span, const void* norm_w, float eps_row, const void* W1,
+                         const float* b1, int h, const void* w2, const float* b2, float* score_raw, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (max_span < 0 || max_span > N)
+    return fail(TG_EINVAL, "tg_gate_score_varlen: max_span=%d outside [0, N=%d]", max_span, N);
+  if (!span_begin || !span_end || !aligned4(span_begin) || !aligned4(span_end))
+    return fail(TG_EINVAL, "tg_gate_score_varlen: span arrays must be 4-byte aligned device pointers");
+  return gate_score_common("tg_gate_score_varlen", resid, dt, B, N, d, 0, max_span, span_begin, span_end, norm_w,
+                           eps_row, W1, b1, h, w2, b2, score_raw, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -10,7 +10,11 @@ namespace tg {
 
 // Rows [r, p1) of each batch row are the prunable span (p1 = N for a prompt
 // [x_R, x_D]); every other row scores 0.
+// With span_begin/span_end (device [B] arrays) set, row b's span comes from
+// them (clamped into [0, N]) and [r, p1) only sizes the grid (p1 - r = the
+// longest span).
 hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1,
+                                  const int32_t* span_begin, const int32_t* span_end,
                                   const uint16_t* norm_w, float eps_row, const uint16_t* W1,
                                   const float* b1, int h, const uint16_t* w2, const float* b2,
                                   float* out, void* ws, hipStream_t s);
@@ -19,6 +23,7 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
 size_t gate_score_workspace(int h, int d);
 
 hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1,
+                                 const int32_t* span_begin, const int32_t* span_end,
                                  const float* norm_w, float eps_row, const float* W1,
                                  const float* b1, int h, const float* w2, const float* b2,
                                  float* out, hipStream_t s);

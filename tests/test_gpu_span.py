@@ -188,3 +188,25 @@ def test_gate_select_varlen(dtype, N, rows):
         assert np.array_equal(ki[cu[b]:cu[b + 1]].cpu().numpy(), i_or[0])
         host_rows = host_bits(ro[cu[b]:cu[b + 1]]) if dtype == "bf16" else ro[cu[b]:cu[b + 1]].cpu().numpy()
         assert np.array_equal(host_rows.view(np.uint8), r_or[0].view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,N,spans", [
+    ("bf16", 3000, [(32, 2900), (0, 1000), (500, 500), (100, 3000)]),
+    ("f32", 600, [(10, 550), (0, 300)]),
+])
+def test_gate_score_varlen(dtype, N, spans):
+    """Each row scored on its own span equals the span entry point on that row."""
+    B = len(spans)
+    say(f"gate_score_varlen {dtype} N={N} spans={spans}")
+    d, h = (512, 128) if dtype == "bf16" else (128, 32)
+    c = wl.gate_case(N=N, r=0, d=d, h=h, K=10, dtype=dtype, seed=N + d + B, B=B, w_std=0.1)
+    t = gate_dev(c)
+    sb, se = [s[0] for s in spans], [s[1] for s in spans]
+    got = tg.tg_gate_score_varlen(t["resid"], sb, se, t["norm_w"], t["W1"], t["b1"], t["w2"], t["b2"], c.eps_row,
+                                  score_raw=poison_f32((B, N))).cpu().numpy()
+    for b, (p0, p1) in enumerate(spans):
+        one = tg.tg_gate_score(t["resid"][b:b + 1].contiguous(), p0, t["norm_w"], t["W1"], t["b1"], t["w2"],
+                               t["b2"], c.eps_row, span_end=p1).cpu().numpy()
+        np.testing.assert_array_equal(got[b].view(np.uint32), one[0].view(np.uint32))
+        ref = oracle.gate_score(c.resid[b:b + 1], p0, c.norm_w, c.W1, c.b1, c.w2, c.b2, c.eps_row, span_end=p1)
+        assert_close(got[b:b + 1], ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"varlen score row {b}")
