@@ -210,3 +210,21 @@ def test_gate_score_varlen(dtype, N, spans):
         np.testing.assert_array_equal(got[b].view(np.uint32), one[0].view(np.uint32))
         ref = oracle.gate_score(c.resid[b:b + 1], p0, c.norm_w, c.W1, c.b1, c.w2, c.b2, c.eps_row, span_end=p1)
         assert_close(got[b:b + 1], ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"varlen score row {b}")
+
+
+def test_gate_select_varlen_clamps_row_parameters():
+    """Out-of-range per-row values are clamped (span end past the length, a
+    negative budget, a span start past the end) and give exactly the results
+    of the clamped values."""
+    N, d = 2000, 64
+    rng = np.random.default_rng(77)
+    raw = (rng.standard_normal((3, N)) * 3.0).astype(np.float32)
+    c = wl.gate_case(N=N, r=0, d=d, h=8, K=1, dtype="bf16", seed=5, B=3)
+    resid = dev_bits(c.resid)
+    wild = dict(seq_len=[1500, 1800, 2000], span_begin=[10, 50, 1900], span_end=[1900, 1700, 1800], K=[100, -5, 30])
+    tame = dict(seq_len=[1500, 1800, 2000], span_begin=[10, 50, 1800], span_end=[1500, 1700, 1800], K=[100, 0, 30])
+    a = tg.tg_gate_select_varlen(dev(raw), resid, **wild)
+    b = tg.tg_gate_select_varlen(dev(raw), resid, **tame)
+    assert a[5] == b[5]
+    for x, y in zip(a[:5], b[:5]):
+        assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
