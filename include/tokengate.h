@@ -295,6 +295,31 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tg_gated_attention_varlen -- tg_gated_attention over the packed kept rows of
+ * a varying-length batch (the output layout of tg_gate_select_varlen).
+ * Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [T, Hq, d_h],
+ * k and v [T, Hkv, d_h], key_score [T], pos [T] and out [T, Hq, d_h]; lse,
+ * when given, holds sequence b's [Hq, M_b] block (head-major, as the batched
+ * entry point's [B, Hq, M] for B = 1) at offset cu_seqlens[b] * Hq.
+ * Causality and the temperature's ranks run within each sequence.
+ *
+ *   cu_seqlens [B + 1] int32 HOST array (cu_seqlens[0] = 0, non-decreasing)
+ *   ws, ws_bytes     workspace of at least tg_workspace_size(
+ *                    TG_OP_GATED_ATTENTION, 1, max_b M_b, Hkv * d_h, Hq, 0)
+ *                    bytes: the sequences run one after the other on the
+ *                    stream as batches of one and share it
+ * Each sequence is validated and launched as tg_gated_attention; on an error
+ * the sequences before it have been enqueued.
+ */
+int tg_gated_attention_varlen(const void* q, const void* k, const void* v,
+                              int B, const int32_t* cu_seqlens, int Hq,
+                              int Hkv, int d_h, const float* key_score,
+                              const int32_t* pos, const float* gain,
+                              const float* temp, float sm_scale, void* out,
+                              float* lse, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * tg_gated_attention_rope -- tg_gated_attention on rotary-embedded queries and
  * keys.  The paper keeps every kept token's original position for the
  * position encoding of the layers above the gate (Appendix C.4); this entry

@@ -26,7 +26,8 @@ TG_F32, TG_BF16 = 0, 1
 
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
-            "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
+            "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -63,6 +64,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_gated_attention_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_gate_score_varlen.argtypes = [vp, i, i, i, i, vp, vp, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
     lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -75,7 +77,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for name in ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gated_attention",
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
-                 "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen"):
+                 "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
+                 "tg_gated_attention_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -364,6 +367,41 @@ def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, ep
                                      _ptr(resid), _dt(resid), d, _ptr(score), _ptr(keep), _ptr(kept_idx),
                                      _ptr(resid_out), _ptr(score_out), _stream(stream)))
     return kept_idx[:T], resid_out[:T], score_out[:T], keep, score, cu
+
+
+def tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, sm_scale: float | None = None,
+                              out=None, lse=None, ws=None, stream=None):
+    """Token-gated attention over packed sequences: q ``[T, Hq, dh]``, k/v
+    ``[T, Hkv, dh]``, key_score/pos ``[T]``, ``cu_seqlens`` a host list of B + 1
+    row offsets (e.g. from :func:`tg_gate_select_varlen`).  Returns ``out``
+    (and ``lse`` when given: sequence b's [Hq, M_b] block at cu_seqlens[b] * Hq)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    T, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    _need(k, "k", torch.bfloat16, (T, Hkv, dh))
+    _need(v, "v", torch.bfloat16, (T, Hkv, dh))
+    _need(key_score, "key_score", torch.float32, (T,))
+    _need(pos, "pos", torch.int32, (T,))
+    cu = [int(x) for x in cu_seqlens]
+    if cu[0] != 0 or cu[-1] != T:
+        raise ValueError("cu_seqlens must start at 0 and end at the number of packed rows")
+    B = len(cu) - 1
+    if sm_scale is None:
+        sm_scale = dh ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (T, Hq, dh))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (T * Hq,))
+    max_m = max([cu[i + 1] - cu[i] for i in range(B)] + [0])
+    if ws is None:
+        ws = attention_workspace(1, max(max_m, 1), Hq, Hkv, dh, q.device)
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    _check(lib.tg_gated_attention_varlen(_ptr(q), _ptr(k), _ptr(v), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
+                                         _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
+    return (out, lse) if lse is not None else out
 
 
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:

@@ -427,4 +427,36 @@ int tg_gate_score_varlen(const void* resid, int dt, int B, int N, int d, const i
                            eps_row, W1, b1, h, w2, b2, score_raw, ws, ws_bytes, stream);
 }
 
+int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B, const int32_t* cu_seqlens, int Hq,
+                              int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
+                              const float* temp, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  const char* name = "tg_gated_attention_varlen";
+  if (B <= 0 || !cu_seqlens) return fail(TG_EINVAL, "%s: B must be > 0 and cu_seqlens given", name);
+  if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
+  int max_m = 0;
+  for (int b = 0; b < B; ++b) {
+    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (m < 0) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
+    max_m = m > max_m ? m : max_m;
+  }
+  const size_t need = max_m > 0 ? tg::gated_attention_workspace(1, max_m, Hq, Hkv, d_h) : 0;
+  if (max_m > 0 && (!ws || ws_bytes < need))
+    return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+  // every sequence runs as a batch of one on the same stream, one after the
+  // other, so they can share the workspace
+  for (int b = 0; b < B; ++b) {
+    const size_t t0 = (size_t)cu_seqlens[b];
+    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (m == 0) continue;
+    const int rc = gated_attention_common(
+        name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
+        static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp,
+        sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws, ws_bytes,
+        stream);
+    if (rc != TG_OK) return rc;
+  }
+  return TG_OK;
+}
+
 }  // extern "C"

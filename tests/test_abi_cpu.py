@@ -281,3 +281,16 @@ def test_attention_rope_backward_validation(lib):
     rope = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE_BACKWARD, 1, 64, 8 * 128, 16, 128)
     assert rope == (plain + 15) // 16 * 16 + 6 * 64 * 24 * 128
     assert call(ws_bytes=plain) == tgb.TG_EINVAL and "workspace" in _err(lib)
+
+
+def test_attention_varlen_validation(lib):
+    def call(cu, ws_bytes=1 << 30):
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        return lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, len(cu) - 1, arr, 16, 8, 128, FAKE, FAKE, FAKE, FAKE,
+                                             0.088, FAKE, NULL, FAKE, ws_bytes, None)
+
+    assert call([1, 5]) == tgb.TG_EINVAL and "cu_seqlens[0]" in _err(lib)
+    assert call([0, 5, 3]) == tgb.TG_EINVAL and "non-decreasing" in _err(lib)
+    small = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 100, 8 * 128, 16, 0)
+    assert call([0, 100, 300], ws_bytes=small) == tgb.TG_EINVAL and "workspace" in _err(lib)  # sized by the longest
+    assert call([0, 0, 0]) == tgb.TG_OK  # nothing to do: no GPU call

@@ -228,3 +228,36 @@ def test_gate_select_varlen_clamps_row_parameters():
     assert a[5] == b[5]
     for x, y in zip(a[:5], b[:5]):
         assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
+
+
+def test_varlen_gate_then_attention():
+    """A varying-length batch end to end: per-row scores and selection, then
+    the token-gated attention of each packed sequence; every sequence's output
+    equals the batched call on that sequence alone, and the oracle."""
+    N, d, Hq, Hkv, dh = 3000, 256, 4, 2, 128
+    rows = [(3000, 20, 2900, 300), (1700, 0, 1600, 100), (2500, 64, 2500, 0)]
+    lens, p0s, p1s, Ks = (list(x) for x in zip(*rows))
+    c = wl.gate_case(N=N, r=0, d=d, h=64, K=1, dtype="bf16", seed=31, B=len(rows), w_std=0.1)
+    t = gate_dev(c)
+    raw = tg.tg_gate_score_varlen(t["resid"], p0s, p1s, t["norm_w"], t["W1"], t["b1"], t["w2"], t["b2"], c.eps_row)
+    ki, ro, so, keep, score, cu = tg.tg_gate_select_varlen(raw, t["resid"], lens, p0s, p1s, Ks)
+    T = cu[-1]
+    a = wl.attn_case(M=T, Hq=Hq, Hkv=Hkv, dh=dh, seed=32, r_zero=0)
+    q, k, v = (dev_bits(x[0]) for x in (a.q, a.k, a.v))
+    gain, temp = dev(a.gain), dev(a.temp)
+    lse = torch.empty(T * Hq, dtype=torch.float32, device=DEV)
+    out, lse = tg.tg_gated_attention_varlen(q, k, v, cu, so, ki, gain, temp, a.sm_scale, lse=lse)
+    bsc = so.cpu().numpy()
+    kin = ki.cpu().numpy()
+    for b in range(len(rows)):
+        s0, s1 = cu[b], cu[b + 1]
+        m = s1 - s0
+        o1, l1 = tg.tg_gated_attention(q[None, s0:s1].contiguous(), k[None, s0:s1].contiguous(),
+                                       v[None, s0:s1].contiguous(), so[None, s0:s1].contiguous(),
+                                       ki[None, s0:s1].contiguous(), gain, temp, a.sm_scale, want_lse=True)
+        assert torch.equal(out[s0:s1].view(torch.int16), o1[0].view(torch.int16))
+        assert torch.equal(lse[s0 * Hq:s1 * Hq].view(torch.int32), l1.reshape(-1).view(torch.int32))
+        O, L = oracle.gated_attention(a.q[:, s0:s1], a.k[:, s0:s1], a.v[:, s0:s1], bsc[None, s0:s1],
+                                      kin[None, s0:s1], a.gain, a.temp, a.sm_scale)
+        assert_close(wl.bf16_bits_to_f32(host_bits(out[None, s0:s1])), O, TOL_BF16, f"varlen attention {b}")
+        assert m == tg.varlen_kept_counts([lens[b]], [p0s[b]], [p1s[b]], [Ks[b]])[0]
