@@ -425,6 +425,29 @@ int tg_gated_attention_rope_backward(const void* q, const void* k,
                                      size_t ws_bytes, void* stream);
 
 /*
+ * tg_gated_attention_backward_varlen -- tg_gated_attention_backward over the
+ * packed sequences of tg_gated_attention_varlen (same layouts: rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1; out and lse as that call wrote them).
+ * d_gain and d_temp are [B, Hq]: sequence b's gradients in row b (sum the
+ * rows for the batch's gradient).  cu_seqlens is a HOST array; the workspace
+ * is tg_workspace_size(TG_OP_GATED_ATTENTION_BACKWARD, 1, max_b M_b, Hkv *
+ * d_h, Hq, d_h) bytes, shared by the sequences, which run one after the
+ * other on the stream as batches of one.
+ */
+int tg_gated_attention_backward_varlen(const void* q, const void* k,
+                                       const void* v, const void* out,
+                                       const float* lse, const void* d_out,
+                                       int B, const int32_t* cu_seqlens,
+                                       int Hq, int Hkv, int d_h,
+                                       const float* key_score,
+                                       const int32_t* pos, const float* gain,
+                                       const float* temp, float sm_scale,
+                                       void* d_q, void* d_k, void* d_v,
+                                       float* d_key_score, float* d_gain,
+                                       float* d_temp, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/*
  * tg_kv_cache_prune -- post-prefill pruning of the KV cache of the layers at
  * and below the gate (paper, Section 5, "Implementation and timing", and
  * Appendix B: optionally, once prefill completes, those layers keep only the

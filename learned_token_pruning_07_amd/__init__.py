@@ -27,7 +27,7 @@ TG_F32, TG_BF16 = 0, 1
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
-            "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_backward_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
+    lib.tg_gated_attention_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f,
+                                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_gate_score_varlen.argtypes = [vp, i, i, i, i, vp, vp, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
@@ -78,7 +80,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
-                 "tg_gated_attention_varlen"):
+                 "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -402,6 +404,40 @@ def tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, s
                                          _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse),
                                          _ptr(ws), ws.numel(), _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key_score, pos, gain, temp,
+                                       sm_scale: float | None = None, ws=None, stream=None):
+    """Gradients of :func:`tg_gated_attention_varlen` (same packed layouts;
+    ``lse`` as it wrote it).  Returns ``(d_q, d_k, d_v, d_key_score, d_gain
+    [B, Hq], d_temp [B, Hq])``: per-sequence gain and temperature gradients."""
+    lib = load_library()
+    T, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    for t_, n_, shp in ((q, "q", (T, Hq, dh)), (k, "k", (T, Hkv, dh)), (v, "v", (T, Hkv, dh)),
+                        (out, "out", (T, Hq, dh)), (d_out, "d_out", (T, Hq, dh))):
+        _need(t_, n_, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (T * Hq,))
+    _need(key_score, "key_score", torch.float32, (T,))
+    _need(pos, "pos", torch.int32, (T,))
+    cu = [int(x) for x in cu_seqlens]
+    if cu[0] != 0 or cu[-1] != T:
+        raise ValueError("cu_seqlens must start at 0 and end at the number of packed rows")
+    B = len(cu) - 1
+    if sm_scale is None:
+        sm_scale = dh ** -0.5
+    dev = q.device
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty(T, device=dev),
+             torch.empty((B, Hq), device=dev), torch.empty((B, Hq), device=dev)]
+    max_m = max([cu[i + 1] - cu[i] for i in range(B)] + [0])
+    if ws is None:
+        ws = attention_backward_workspace(1, max(max_m, 1), Hq, Hkv, dh, dev)
+    cu_arr = (ctypes.c_int32 * len(cu))(*cu)
+    _check(lib.tg_gated_attention_backward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
+        _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), *[_ptr(g_) for g_ in grads], _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return tuple(grads)
 
 
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:

@@ -261,3 +261,35 @@ def test_varlen_gate_then_attention():
                                       kin[None, s0:s1], a.gain, a.temp, a.sm_scale)
         assert_close(wl.bf16_bits_to_f32(host_bits(out[None, s0:s1])), O, TOL_BF16, f"varlen attention {b}")
         assert m == tg.varlen_kept_counts([lens[b]], [p0s[b]], [p1s[b]], [Ks[b]])[0]
+
+
+def test_varlen_attention_backward_equals_per_sequence_calls():
+    """The packed backward gives, per sequence, the batched backward of that
+    sequence alone bit for bit (gain and temperature gradients per row); the
+    batched backward is held to the oracle in test_gpu_backward."""
+    Hq, Hkv, dh = 4, 2, 128
+    cu = [0, 300, 300, 750, 1000]   # includes an empty sequence
+    T = cu[-1]
+    a = wl.attn_case(M=T, Hq=Hq, Hkv=Hkv, dh=dh, seed=41, r_zero=0)
+    q, k, v = (dev_bits(x[0]) for x in (a.q, a.k, a.v))
+    rng = np.random.default_rng(42)
+    b = rng.standard_normal(T).astype(np.float32)
+    pos = np.concatenate([np.sort(rng.choice(3 * max(n, 1), n, replace=False)) for n in np.diff(cu)]).astype(np.int32)
+    dO_bits = wl.f32_to_bf16_bits(rng.standard_normal((T, Hq, dh), dtype=np.float32))
+    gain, temp = dev(a.gain), dev(a.temp)
+    lse = torch.empty(T * Hq, dtype=torch.float32, device=DEV)
+    out, lse = tg.tg_gated_attention_varlen(q, k, v, cu, dev(b), dev(pos), gain, temp, a.sm_scale, lse=lse)
+    g = tg.tg_gated_attention_backward_varlen(q, k, v, out, lse, dev_bits(dO_bits), cu, dev(b), dev(pos), gain, temp,
+                                              a.sm_scale)
+    for i in range(len(cu) - 1):
+        s0, s1 = cu[i], cu[i + 1]
+        if s1 == s0:
+            assert torch.all(g[4][i] == 0) and torch.all(g[5][i] == 0)
+            continue
+        one = tg.tg_gated_attention_backward(
+            q[None, s0:s1].contiguous(), k[None, s0:s1].contiguous(), v[None, s0:s1].contiguous(),
+            out[None, s0:s1].contiguous(), lse[s0 * Hq:s1 * Hq].reshape(1, Hq, s1 - s0).contiguous(),
+            dev_bits(dO_bits[None, s0:s1]), dev(b[None, s0:s1]), dev(pos[None, s0:s1]), gain, temp, a.sm_scale)
+        for x, y in zip((g[0][s0:s1], g[1][s0:s1], g[2][s0:s1], g[3][s0:s1], g[4][i], g[5][i]),
+                        (one[0][0], one[1][0], one[2][0], one[3][0], one[4], one[5])):
+            assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
