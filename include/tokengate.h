@@ -22,9 +22,14 @@
  *    before anything is enqueued; on any error nothing is enqueued and
  *    tg_last_error() describes the problem.  No C++ exception crosses the ABI.
  *  - Results are deterministic: the same inputs give the same output bits.
- *  - Batch rows are independent; every batch row has the same N, r and K.
+ *  - Batch rows are independent; every batch row has the same N, r and K,
+ *    except in the _varlen entry points, which take per-row values.
  *  - The non-prunable tokens (the question x_R of the prompt x = [x_R, x_D])
  *    are the first r tokens of each sequence; tokens r..N-1 are prunable.
+ *    The _span entry points take the prunable span [span_begin, span_end)
+ *    instead, with non-prunable text on both sides.
+ *  - Sizes and the cu_seqlens offsets of the attention _varlen entry points
+ *    are host values; every tensor is a device pointer.
  *  - bf16 is IEEE bfloat16 stored in 16 bits; fp32 is IEEE binary32.
  */
 #ifndef TOKENGATE_H
