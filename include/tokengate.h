@@ -313,8 +313,7 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
  *                    TG_OP_GATED_ATTENTION, 1, max_b M_b, Hkv * d_h, Hq, 0)
  *                    bytes: the sequences run one after the other on the
  *                    stream as batches of one and share it
- * Each sequence is validated and launched as tg_gated_attention; on an error
- * the sequences before it have been enqueued.
+ * Every sequence is validated as tg_gated_attention before any is launched.
  */
 int tg_gated_attention_varlen(const void* q, const void* k, const void* v,
                               int B, const int32_t* cu_seqlens, int Hq,

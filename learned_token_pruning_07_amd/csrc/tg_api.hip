@@ -262,7 +262,8 @@ namespace {
 int gated_attention_common(const char* name, const void* q, const void* k, const void* v, int B, int M, int Hq,
                            int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
                            const float* temp, float sm_scale, double rope_base, void* out, float* lse, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           size_t ws_bytes, void* stream,
+                           bool launch = true) {
   if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
   if (M == 0) return TG_OK;
@@ -280,6 +281,7 @@ int gated_attention_common(const char* name, const void* q, const void* k, const
   if (!ws || ws_bytes < need)
     return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
   if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+  if (!launch) return TG_OK;
   return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
                                                pos, gain, temp, sm_scale, rope_base, static_cast<uint16_t*>(out),
@@ -313,7 +315,7 @@ static int attention_backward_common(const char* name, const void* q, const void
                                      const float* key_score, const int32_t* pos, const float* gain, const float* temp,
                                      float sm_scale, double rope_base, void* d_q, void* d_k, void* d_v,
                                      float* d_key_score, float* d_gain, float* d_temp, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     void* stream, bool launch = true) {
   if (B <= 0 || B > 65535 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
   if (!gain || !temp || !d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
@@ -341,6 +343,7 @@ static int attention_backward_common(const char* name, const void* q, const void
       return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
     if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
   }
+  if (!launch) return TG_OK;
   return hip_status(
       tg::launch_gated_attention_backward(
           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
@@ -444,17 +447,19 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B
   if (max_m > 0 && (!ws || ws_bytes < need))
     return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
   // every sequence runs as a batch of one on the same stream, one after the
-  // other, so they can share the workspace
-  for (int b = 0; b < B; ++b) {
-    const size_t t0 = (size_t)cu_seqlens[b];
-    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (m == 0) continue;
-    const int rc = gated_attention_common(
-        name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
-        static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp,
-        sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws, ws_bytes,
-        stream);
-    if (rc != TG_OK) return rc;
+  // other, so they can share the workspace; all are validated before any runs
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int b = 0; b < B; ++b) {
+      const size_t t0 = (size_t)cu_seqlens[b];
+      const int m = cu_seqlens[b + 1] - cu_seqlens[b];
+      if (m == 0) continue;
+      const int rc = gated_attention_common(
+          name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
+          static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain,
+          temp, sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws,
+          ws_bytes, stream, pass == 1);
+      if (rc != TG_OK) return rc;
+    }
   }
   return TG_OK;
 }
@@ -480,17 +485,20 @@ int tg_gated_attention_backward_varlen(const void* q, const void* k, const void*
   if (!d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
   // one batch-of-one backward per sequence, in order on the stream (shared
   // workspace); sequence b's gain and temperature gradients go to row b
-  for (int b = 0; b < B; ++b) {
-    const size_t t0 = (size_t)cu_seqlens[b];
-    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-    const size_t qo = t0 * Hq * d_h, ko = t0 * Hkv * d_h;
-    const int rc = attention_backward_common(
-        name, static_cast<const uint16_t*>(q) + qo, static_cast<const uint16_t*>(k) + ko,
-        static_cast<const uint16_t*>(v) + ko, static_cast<const uint16_t*>(out) + qo, lse ? lse + t0 * Hq : nullptr,
-        static_cast<const uint16_t*>(d_out) + qo, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp, sm_scale,
-        0.0, static_cast<uint16_t*>(d_q) + qo, static_cast<uint16_t*>(d_k) + ko, static_cast<uint16_t*>(d_v) + ko,
-        d_key_score + t0, d_gain + (size_t)b * Hq, d_temp + (size_t)b * Hq, ws, ws_bytes, stream);
-    if (rc != TG_OK) return rc;
+  for (int pass = 0; pass < 2; ++pass) {  // all sequences are validated before any runs
+    for (int b = 0; b < B; ++b) {
+      const size_t t0 = (size_t)cu_seqlens[b];
+      const int m = cu_seqlens[b + 1] - cu_seqlens[b];
+      const size_t qo = t0 * Hq * d_h, ko = t0 * Hkv * d_h;
+      const int rc = attention_backward_common(
+          name, static_cast<const uint16_t*>(q) + qo, static_cast<const uint16_t*>(k) + ko,
+          static_cast<const uint16_t*>(v) + ko, static_cast<const uint16_t*>(out) + qo,
+          lse ? lse + t0 * Hq : nullptr, static_cast<const uint16_t*>(d_out) + qo, 1, m, Hq, Hkv, d_h,
+          key_score + t0, pos + t0, gain, temp, sm_scale, 0.0, static_cast<uint16_t*>(d_q) + qo,
+          static_cast<uint16_t*>(d_k) + ko, static_cast<uint16_t*>(d_v) + ko, d_key_score + t0,
+          d_gain + (size_t)b * Hq, d_temp + (size_t)b * Hq, ws, ws_bytes, stream, pass == 1);
+      if (rc != TG_OK) return rc;
+    }
   }
   return TG_OK;
 }

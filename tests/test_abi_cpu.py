@@ -294,3 +294,15 @@ def test_attention_varlen_validation(lib):
     small = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 100, 8 * 128, 16, 0)
     assert call([0, 100, 300], ws_bytes=small) == tgb.TG_EINVAL and "workspace" in _err(lib)  # sized by the longest
     assert call([0, 0, 0]) == tgb.TG_OK  # nothing to do: no GPU call
+
+
+def test_attention_varlen_validates_every_sequence_first(lib):
+    """A bad second sequence is refused before the first is launched (no GPU
+    call is made here: a launch would fail on this CPU-only machine)."""
+    cu = (ctypes.c_int32 * 3)(0, 100, 200)
+    # sequence 1 fine, sequence 2 fine in size, but d_h unsupported for both -> refused up front
+    assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 96, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE,
+                                         NULL, FAKE, 1 << 30, None) == tgb.TG_EUNSUPPORTED
+    # misaligned key_score for the second sequence only (offset 100 * 4 bytes keeps alignment, so use the base)
+    assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 128, FAKE_ODD, FAKE, FAKE, FAKE, 0.088,
+                                         FAKE, NULL, FAKE, 1 << 30, None) == tgb.TG_EINVAL
