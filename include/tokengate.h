@@ -310,10 +310,13 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
  *
  *   cu_seqlens [B + 1] int32 HOST array (cu_seqlens[0] = 0, non-decreasing)
  *   ws, ws_bytes     workspace of at least tg_workspace_size(
- *                    TG_OP_GATED_ATTENTION, 1, max_b M_b, Hkv * d_h, Hq, 0)
- *                    bytes: the sequences run one after the other on the
- *                    stream as batches of one and share it
- * Every sequence is validated as tg_gated_attention before any is launched.
+ *                    TG_OP_GATED_ATTENTION, 1, T + 63 * B, Hkv * d_h, Hq, 0)
+ *                    bytes, T = cu_seqlens[B] (every sequence's fp16 V^T copy
+ *                    and key-score terms, each padded to 64 rows, side by
+ *                    side), 16-byte aligned
+ * Every sequence is validated as tg_gated_attention (a batch of one) before
+ * anything is launched.  Up to 64 non-empty sequences share one launch of
+ * each kernel (longest first); empty sequences are skipped.
  */
 int tg_gated_attention_varlen(const void* q, const void* k, const void* v,
                               int B, const int32_t* cu_seqlens, int Hq,

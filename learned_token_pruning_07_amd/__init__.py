@@ -396,9 +396,8 @@ def tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, s
     _need(out, "out", torch.bfloat16, (T, Hq, dh))
     if lse is not None:
         _need(lse, "lse", torch.float32, (T * Hq,))
-    max_m = max([cu[i + 1] - cu[i] for i in range(B)] + [0])
-    if ws is None:
-        ws = attention_workspace(1, max(max_m, 1), Hq, Hkv, dh, q.device)
+    if ws is None:  # every sequence padded to 64 rows, side by side
+        ws = attention_workspace(1, max(T + 63 * B, 1), Hq, Hkv, dh, q.device)
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
     _check(lib.tg_gated_attention_varlen(_ptr(q), _ptr(k), _ptr(v), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
                                          _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse),

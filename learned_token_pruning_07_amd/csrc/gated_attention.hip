@@ -56,6 +56,9 @@
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "rope_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
@@ -105,6 +108,35 @@ struct RopeArgs {
   uint16_t* kr;
 };
 
+// Sequences of one varying-length launch, longest first.  Sequence s owns
+// packed rows t0[s] .. t0[s] + m[s] - 1 of q, k, v, out, key_score and pos,
+// padded key slots p0[s] .. p0[s] + roundup(m[s], 64) - 1 of V^T and the
+// key-score terms, prepass blocks pb0[s] .. pb0[s+1] - 1 and attention
+// workgroups wg0[s] .. wg0[s+1] - 1 (before the XCD remap).  Passed by value:
+// the kernel reads it from its argument segment.
+constexpr int kMaxSeqsPerLaunch = 64;
+struct SeqTable {
+  int n;
+  int t0[kMaxSeqsPerLaunch];
+  int m[kMaxSeqsPerLaunch];
+  int p0[kMaxSeqsPerLaunch];
+  int pb0[kMaxSeqsPerLaunch + 1];
+  int wg0[kMaxSeqsPerLaunch + 1];
+};
+
+// the last s < n with first[s] <= x (first[0] = 0 <= x)
+__device__ __forceinline__ int seq_of(const int* first, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // Prepass, per 64-key block of KV head g:
 //   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
 //   in slot order, zero beyond M);
@@ -115,15 +147,34 @@ struct RopeArgs {
 //   half form: pair (x_i, x_{i+DH/2}) turns by pos * base^(-2i/DH)).  The
 //   angle is formed and reduced modulo 2 pi in fp64, so that its fp32 sine
 //   and cosine are accurate to a few ulp at any position.
-template <int DH, bool ROPE>
+// VARLEN: the blocks of the table's sequences, one grid row per KV head.
+template <int DH, bool ROPE, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* __restrict__ v,
                                                                 const float* __restrict__ key_score,
-                                                                const float* __restrict__ gain, int M, int Mp,
-                                                                int Hkv, int G, uint16_t* __restrict__ vt,
-                                                                float* __restrict__ kbias, RopeArgs ra) {
+                                                                const float* __restrict__ gain, int M_all,
+                                                                int Mp_all, int Hkv, int G,
+                                                                uint16_t* __restrict__ vt,
+                                                                float* __restrict__ kbias, RopeArgs ra,
+                                                                const SeqTable st) {
   __shared__ uint16_t sT[DH][kBK + 2];
   __shared__ double s_freq[DH / 2];
-  const int m0 = blockIdx.x * kBK, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y;
+  int m0, M, Mp;
+  size_t T0, P0;  // first packed row and first padded key slot of this sequence
+  if constexpr (VARLEN) {
+    const int sq = seq_of(st.pb0, st.n, blockIdx.x);
+    M = st.m[sq];
+    Mp = (M + kBK - 1) / kBK * kBK;
+    m0 = (blockIdx.x - st.pb0[sq]) * kBK;
+    T0 = (size_t)st.t0[sq];
+    P0 = (size_t)st.p0[sq];
+  } else {
+    M = M_all;
+    Mp = Mp_all;
+    m0 = blockIdx.x * kBK;
+    T0 = (size_t)blockIdx.z * M;
+    P0 = (size_t)blockIdx.z * Mp;
+  }
   const int tid = threadIdx.x;
   if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);  // (ordered by the barrier below)
   const float scale = 1.0f / (float)(1 << kVScaleLog2);
@@ -134,12 +185,12 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     const int c = tid + e * kThreads;
     const int key = c / (DH / 8), part = c % (DH / 8);
     const int m = m0 + key;
-    w[e] = m < M ? load16(v + (((size_t)b * M + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
+    w[e] = m < M ? load16(v + ((T0 + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
   }
   const int Hq = Hkv * G;
   for (int c = tid; c < G * kBK; c += kThreads) {
     const int hq = g * G + c / kBK, m = m0 + c % kBK;
-    kbias[((size_t)b * Hq + hq) * Mp + m] = m < M ? key_score[(size_t)b * M + m] * (gain[hq] * kLog2e) : 0.0f;
+    kbias[P0 * Hq + (size_t)hq * Mp + m] = m < M ? key_score[T0 + m] * (gain[hq] * kLog2e) : 0.0f;
   }
 #pragma unroll
   for (int e = 0; e < NL; ++e) {
@@ -161,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       o[i] = (uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i)] | ((uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i + 1)] << 16);
-    store16(vt + (((size_t)b * Hkv + g) * DH + d) * Mp + m0 + kc * 8, o);
+    store16(vt + P0 * Hkv * DH + ((size_t)g * DH + d) * Mp + m0 + kc * 8, o);
   }
   if constexpr (ROPE) {
     constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
@@ -170,11 +221,11 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
       const int key = t / PG, i0 = (t % PG) * 8, m = m0 + key;
       if (m >= M) continue;
       float c[8], sn[8];
-      rope::sincos8((double)ra.pos[(size_t)b * M + m], s_freq, i0, c, sn);
-      const size_t krow = (((size_t)b * M + m) * Hkv + g) * DH;
+      rope::sincos8((double)ra.pos[T0 + m], s_freq, i0, c, sn);
+      const size_t krow = ((T0 + m) * Hkv + g) * DH;
       rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
       for (int hh = 0; hh < G; ++hh) {
-        const size_t qrow = (((size_t)b * M + m) * Hq + g * G + hh) * DH;
+        const size_t qrow = ((T0 + m) * Hq + g * G + hh) * DH;
         rope::row8<DH>(ra.q + qrow, ra.qr + qrow, i0, c, sn);
       }
     }
@@ -198,12 +249,12 @@ __device__ __forceinline__ void buffer_load4_to_lds(__amdgpu_buffer_rsrc_t rsrc,
 // s_waitcnt vmcnt(0): wait for every load of this wave, LDS-destination ones included
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DH, int G>
+template <int DH, int G, bool VARLEN>
 __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
-    const float* __restrict__ kbias, int M, int Mp, int Hq, int Hkv, const int32_t* __restrict__ pos,
-    const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb,
-    int total_wg) {
+    const float* __restrict__ kbias, int M_all, int Mp_all, int Hq, int Hkv, const int32_t* __restrict__ pos,
+    const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb_all,
+    int total_wg, const SeqTable st) {
   constexpr int RG = 4 / G;        // 32-row groups per head
   constexpr int BQ = 32 * RG;      // query rows per workgroup
   constexpr int KS = DH / 16;      // k-steps of S^T = K Q^T
@@ -228,9 +279,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   const int wid = wall & 3;        // wave index inside the group
   const int tid = threadIdx.x & (kThreads - 1);  // thread index inside the group
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bg = logical / nqb;
-  const int qb = nqb - 1 - (logical - bg * nqb);
-  const int b = bg / Hkv, g = bg - b * Hkv;
+  // this workgroup's sequence (its length M, first packed row T0, first
+  // padded key slot P0), KV head g and query block qb (the longest first)
+  int M, Mp, g, qb;
+  size_t T0, P0;
+  if constexpr (VARLEN) {
+    const int sq = seq_of(st.wg0, st.n, logical);
+    M = st.m[sq];
+    Mp = (M + kBK - 1) / kBK * kBK;
+    const int nqb = (M + BQ - 1) / BQ, local = logical - st.wg0[sq];
+    g = local / nqb;
+    qb = nqb - 1 - (local - g * nqb);
+    T0 = (size_t)st.t0[sq];
+    P0 = (size_t)st.p0[sq];
+  } else {
+    M = M_all;
+    Mp = Mp_all;
+    const int bg = logical / nqb_all;
+    qb = nqb_all - 1 - (logical - bg * nqb_all);
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    T0 = (size_t)b * M;
+    P0 = (size_t)b * Mp;
+  }
   const int q0 = qb * BQ;
   const int kv_end = min(M, q0 + BQ);
   const int nkb = (kv_end + kBK - 1) / kBK;
@@ -250,13 +321,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   // range check returns 0 for keys >= M -- the check covers the per-lane
   // offset only, not a scalar offset.  V^T and the key-score rows are padded
   // to Mp keys, so their tiles are always in range and take a scalar offset.
-  const uint16_t* k_base = k + ((size_t)b * M * Hkv + g) * DH;
+  const uint16_t* k_base = k + (T0 * Hkv + g) * DH;
   const long long k_bytes = (((long long)M - 1) * Hkv + 1) * DH * 2;  // up to the end of head g's last row
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(vt + ((size_t)b * Hkv + g) * DH * Mp), (short)0, (int)((size_t)DH * Mp * 2),
+      const_cast<uint16_t*>(vt + P0 * Hkv * DH + (size_t)g * DH * Mp), (short)0, (int)((size_t)DH * Mp * 2),
       kBufferConfig);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(kbias + ((size_t)b * Hq + g * G) * Mp), (short)0, G * Mp * 4, kBufferConfig);
+      const_cast<float*>(kbias + P0 * Hq + (size_t)g * G * Mp), (short)0, G * Mp * 4, kBufferConfig);
   // Load e of this wave fills LDS bytes [1024 C, 1024 C + 1024) of the tile,
   // C = wid * NI + e: 16-byte slot Y = 64 C + lane sits at row Y / chunks-per-row,
   // position p, and holds chunk p ^ (row & 7) of that row.
@@ -564,11 +635,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   // Q fragments and the original position are requested while the first
   // tile is in flight; one wait covers all of them
   {
-    const uint16_t* qp = q + (((size_t)b * M + (q_ok ? qi : 0)) * Hq + hq) * DH + gq * 8;
+    const uint16_t* qp = q + ((T0 + (q_ok ? qi : 0)) * Hq + hq) * DH + gq * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? load16(qp + ks * 16) : u32x4{0, 0, 0, 0});
   }
-  const int p_orig = pos[(size_t)b * M + (q_ok ? qi : 0)];
+  const int p_orig = pos[T0 + (q_ok ? qi : 0)];
   const float t_h = temp[hq];
   wait_vmem();
   if (q_ok) {
@@ -710,10 +781,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     for (int r0 = 0; r0 < 32; r0 += RPI) {
       const int r = r0 + lane / HCH, c = lane % HCH;
       const u32x4 w = *reinterpret_cast<const u32x4*>(ob + r * HROW + ((c ^ (r & (HCH - 1))) * 16));
-      if (rbase + r < M) store16(out + (((size_t)b * M + rbase + r) * Hq + hq) * DH + g * (DH / 2) + c * 8, w);
+      if (rbase + r < M) store16(out + ((T0 + rbase + r) * Hq + hq) * DH + g * (DH / 2) + c * 8, w);
     }
     if (lse != nullptr && g == 0 && gq == 0 && q_ok)
-      lse[((size_t)b * Hq + hq) * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
+      lse[T0 * Hq + (size_t)hq * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
   };
   if (grp == 0)
     hand_over(IntConst<0>{});
@@ -733,13 +804,13 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   constexpr int BQ = 32 * (4 / G);
   const int Mp = (M + kBK - 1) / kBK * kBK;
   if (rope != nullptr) {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, true>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain,
-                       M, Mp, Hkv, G, vt, kbias, *rope);
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
+                       gain, M, Mp, Hkv, G, vt, kbias, *rope, SeqTable{});
     q = rope->qr;  // the main kernel reads the rotated copies
     k = rope->kr;
   } else {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks, gain,
-                       M, Mp, Hkv, G, vt, kbias, RopeArgs{});
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
+                       gain, M, Mp, Hkv, G, vt, kbias, RopeArgs{}, SeqTable{});
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -747,8 +818,23 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   const long long total = (long long)nqb * Hkv * B;
   if (total <= 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt, kbias, M,
-                     Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total);
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G, false>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
+                     kbias, M, Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total, SeqTable{});
+  return hipGetLastError();
+}
+
+// One prepass and one attention launch over the sequences of a table.
+template <int DH, int G>
+hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SeqTable& st, int Hq,
+                           int Hkv, const float* ks, const int32_t* pos, const float* gain, const float* temp,
+                           float sm_scale, uint16_t* out, float* lse, uint16_t* vt, float* kbias, hipStream_t s) {
+  hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads), 0,
+                     s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int total = st.wg0[st.n];
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
+                     kbias, 0, 0, Hq, Hkv, pos, temp, sm_scale, out, lse, 0, total, st);
   return hipGetLastError();
 }
 
@@ -763,6 +849,67 @@ size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
 // ... then the rotated q [B, M, Hq, dh] and k [B, M, Hkv, dh] (bf16)
 size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh) {
   return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * (Hq + Hkv) * dh * 2;
+}
+
+size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens) {
+  size_t slots = 0;
+  for (int b = 0; b < B; ++b) slots += (size_t)(cu_seqlens[b + 1] - cu_seqlens[b] + kBK - 1) / kBK * kBK;
+  return slots;
+}
+
+hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
+                                         const int32_t* cu_seqlens, int Hq, int Hkv, int dh, const float* key_score,
+                                         const int32_t* pos, const float* gain, const float* temp, float sm_scale,
+                                         uint16_t* out, float* lse, void* ws, hipStream_t s) {
+  const int G = Hq / Hkv;
+  constexpr int BQ_G[5] = {0, 128, 64, 0, 32};  // query rows per workgroup by group size
+  if (G != 1 && G != 2 && G != 4) return hipErrorInvalidValue;
+  // the non-empty sequences, longest first: their heavy query blocks start first
+  std::vector<int> order;
+  for (int b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] > cu_seqlens[b]) order.push_back(b);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int c) {
+    return cu_seqlens[a + 1] - cu_seqlens[a] > cu_seqlens[c + 1] - cu_seqlens[c];
+  });
+  const size_t slots = gated_attention_varlen_slots(B, cu_seqlens);
+  uint16_t* vt = static_cast<uint16_t*>(ws);
+  float* kbias = reinterpret_cast<float*>(vt + slots * Hkv * dh);
+  size_t p = 0;
+  for (size_t i = 0; i < order.size(); i += kMaxSeqsPerLaunch) {
+    SeqTable st{};
+    st.n = (int)std::min(order.size() - i, (size_t)kMaxSeqsPerLaunch);
+    long long pb = 0, wg = 0;
+    for (int j = 0; j < st.n; ++j) {
+      const int b = order[i + j], m = cu_seqlens[b + 1] - cu_seqlens[b];
+      const int mp = (m + kBK - 1) / kBK * kBK;
+      if (p + mp > 0x7FFFFFFF) return hipErrorInvalidValue;
+      st.t0[j] = cu_seqlens[b];
+      st.m[j] = m;
+      st.p0[j] = (int)p;
+      st.pb0[j] = (int)pb;
+      st.wg0[j] = (int)wg;
+      p += mp;
+      pb += mp / kBK;
+      wg += (long long)((m + BQ_G[G] - 1) / BQ_G[G]) * Hkv;
+      if (wg > 0x7FFFFFFF / kAttnThreads) return hipErrorInvalidValue;
+    }
+    st.pb0[st.n] = (int)pb;
+    st.wg0[st.n] = (int)wg;
+    hipError_t e = hipErrorInvalidValue;
+#define TG_ATTN_VARLEN_CASE(DHV, GV)                                                                          \
+  if (dh == DHV && G == GV)                                                                                   \
+    e = launch_varlen_t<DHV, GV>(q, k, v, st, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, kbias, \
+                                 s);
+    TG_ATTN_VARLEN_CASE(128, 2)
+    TG_ATTN_VARLEN_CASE(128, 1)
+    TG_ATTN_VARLEN_CASE(128, 4)
+    TG_ATTN_VARLEN_CASE(64, 2)
+    TG_ATTN_VARLEN_CASE(64, 1)
+    TG_ATTN_VARLEN_CASE(64, 4)
+#undef TG_ATTN_VARLEN_CASE
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq,

@@ -437,31 +437,30 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B
   const char* name = "tg_gated_attention_varlen";
   if (B <= 0 || !cu_seqlens) return fail(TG_EINVAL, "%s: B must be > 0 and cu_seqlens given", name);
   if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
-  int max_m = 0;
+  for (int b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
+  const size_t slots = tg::gated_attention_varlen_slots(B, cu_seqlens);
+  if (slots == 0) return TG_OK;
+  if (slots > 0x7FFFFFFF) return fail(TG_EINVAL, "%s: %zu padded rows exceed the 32-bit index range", name, slots);
+  // all sequences' V^T copies and key-score terms sit side by side
+  const size_t need = tg::gated_attention_workspace(1, (int)slots, Hq, Hkv, d_h);
+  if (!ws || ws_bytes < need) return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+  // each sequence is validated as a batch of one; then the batch is launched
   for (int b = 0; b < B; ++b) {
+    const size_t t0 = (size_t)cu_seqlens[b];
     const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (m < 0) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
-    max_m = m > max_m ? m : max_m;
+    if (m == 0) continue;
+    const int rc = gated_attention_common(
+        name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
+        static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp,
+        sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws, ws_bytes,
+        stream, false);
+    if (rc != TG_OK) return rc;
   }
-  const size_t need = max_m > 0 ? tg::gated_attention_workspace(1, max_m, Hq, Hkv, d_h) : 0;
-  if (max_m > 0 && (!ws || ws_bytes < need))
-    return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
-  // every sequence runs as a batch of one on the same stream, one after the
-  // other, so they can share the workspace; all are validated before any runs
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int b = 0; b < B; ++b) {
-      const size_t t0 = (size_t)cu_seqlens[b];
-      const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-      if (m == 0) continue;
-      const int rc = gated_attention_common(
-          name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
-          static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain,
-          temp, sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws,
-          ws_bytes, stream, pass == 1);
-      if (rc != TG_OK) return rc;
-    }
-  }
-  return TG_OK;
+  return hip_status(tg::launch_gated_attention_varlen(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), B,
+      cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse, ws,
+      static_cast<hipStream_t>(stream)), name);
 }
 
 int tg_gated_attention_backward_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,

@@ -80,6 +80,18 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
                                   float sm_scale, double rope_base, uint16_t* out, float* lse, void* ws,
                                   hipStream_t s);
 
+// Packed sequences of a varying-length batch (cu_seqlens a host array of B + 1
+// row offsets): one prepass and one attention launch per 64 non-empty
+// sequences, all sequences' V^T copies and key-score terms side by side in
+// the workspace (gated_attention_workspace(1, slots) bytes, slots from
+// gated_attention_varlen_slots).
+hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
+                                         const int32_t* cu_seqlens, int Hq, int Hkv, int dh, const float* key_score,
+                                         const int32_t* pos, const float* gain, const float* temp, float sm_scale,
+                                         uint16_t* out, float* lse, void* ws, hipStream_t s);
+// sum over the sequences of the length rounded up to 64 key slots
+size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens);
+
 // Workspace bytes of launch_gated_attention: the fp16 V^T copy and the
 // key-score terms; with the rotary embedding also the rotated q and k.
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh);

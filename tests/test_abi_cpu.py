@@ -306,3 +306,13 @@ def test_attention_varlen_validates_every_sequence_first(lib):
     # misaligned key_score for the second sequence only (offset 100 * 4 bytes keeps alignment, so use the base)
     assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 128, FAKE_ODD, FAKE, FAKE, FAKE, 0.088,
                                          FAKE, NULL, FAKE, 1 << 30, None) == tgb.TG_EINVAL
+
+
+def test_attention_varlen_workspace_covers_every_sequence(lib):
+    """The packed call needs every sequence's padded rows side by side:
+    2 x 128 rows x (8 x 128 x 2 + 16 x 4) bytes for two sequences of 100."""
+    cu = (ctypes.c_int32 * 3)(0, 100, 200)
+    need = 256 * (8 * 128 * 2 + 16 * 4)
+    assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 128, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE,
+                                         NULL, FAKE, need - 1, None) == tgb.TG_EINVAL
+    assert b"workspace" in lib.tg_last_error()

@@ -293,3 +293,43 @@ def test_varlen_attention_backward_equals_per_sequence_calls():
         for x, y in zip((g[0][s0:s1], g[1][s0:s1], g[2][s0:s1], g[3][s0:s1], g[4][i], g[5][i]),
                         (one[0][0], one[1][0], one[2][0], one[3][0], one[4], one[5])):
             assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("dh,Hq,Hkv", [(128, 8, 4), (128, 4, 4), (64, 8, 2)])
+def test_varlen_attention_many_sequences(dh, Hq, Hkv):
+    """150 packed sequences (more than one launch's 64), lengths 0 .. 400 with
+    the tile edges 1, 63, 64, 65, 127, 129 and empty ones among them: every
+    sequence equals the batched call on it alone bit for bit, every output row
+    and lse entry is written, and every 15th sequence is held to the oracle."""
+    rng = np.random.default_rng(dh + Hq * 7 + Hkv)
+    lens = list(rng.integers(0, 401, size=142)) + [0, 1, 63, 64, 65, 127, 129, 0]
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+    T = cu[-1]
+    say(f"varlen attention dh={dh} Hq={Hq} Hkv={Hkv} sequences={len(lens)} rows={T}")
+    a = wl.attn_case(M=T, Hq=Hq, Hkv=Hkv, dh=dh, seed=dh + Hq, r_zero=0)
+    q, k, v = (dev_bits(x[0]) for x in (a.q, a.k, a.v))
+    b = rng.standard_normal(T).astype(np.float32)
+    pos = np.concatenate([np.sort(rng.choice(3 * max(n, 1), n, replace=False)) for n in lens]).astype(np.int32)
+    gain, temp = dev(a.gain), dev(a.temp)
+    out = torch.full((T, Hq, dh), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((T * Hq,), float("nan"), dtype=torch.float32, device=DEV)
+    tg.tg_gated_attention_varlen(q, k, v, cu, dev(b), dev(pos), gain, temp, a.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    checked = 0
+    for i, m in enumerate(lens):
+        s0, s1 = cu[i], cu[i + 1]
+        if m == 0:
+            continue
+        o1, l1 = tg.tg_gated_attention(q[None, s0:s1].contiguous(), k[None, s0:s1].contiguous(),
+                                       v[None, s0:s1].contiguous(), dev(b[None, s0:s1]), dev(pos[None, s0:s1]), gain,
+                                       temp, a.sm_scale, want_lse=True)
+        assert torch.equal(out[s0:s1].view(torch.int16), o1[0].view(torch.int16)), f"sequence {i} (M={m})"
+        assert torch.equal(lse[s0 * Hq:s1 * Hq].view(torch.int32), l1.reshape(-1).view(torch.int32)), f"lse {i}"
+        if i % 15 == 0:
+            O, _ = oracle.gated_attention(a.q[:, s0:s1], a.k[:, s0:s1], a.v[:, s0:s1], b[None, s0:s1],
+                                          pos[None, s0:s1], a.gain, a.temp, a.sm_scale)
+            assert_close(wl.bf16_bits_to_f32(host_bits(out[None, s0:s1])), O, TOL_BF16, f"varlen oracle {i}")
+            checked += 1
+    assert checked >= 5
