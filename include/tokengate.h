@@ -436,10 +436,14 @@ int tg_gated_attention_rope_backward(const void* q, const void* k,
  * packed sequences of tg_gated_attention_varlen (same layouts: rows
  * cu_seqlens[b] .. cu_seqlens[b+1]-1; out and lse as that call wrote them).
  * d_gain and d_temp are [B, Hq]: sequence b's gradients in row b (sum the
- * rows for the batch's gradient).  cu_seqlens is a HOST array; the workspace
- * is tg_workspace_size(TG_OP_GATED_ATTENTION_BACKWARD, 1, max_b M_b, Hkv *
- * d_h, Hq, d_h) bytes, shared by the sequences, which run one after the
- * other on the stream as batches of one.
+ * rows for the batch's gradient; an empty sequence's rows are 0).
+ * cu_seqlens is a HOST array; the workspace is at least tg_workspace_size(
+ * TG_OP_GATED_ATTENTION_BACKWARD, 1, T + 63 * B, Hkv * d_h, Hq, d_h) bytes,
+ * T = cu_seqlens[B] (every sequence's row constants and partials, each
+ * padded to 64 rows, side by side).  Every sequence is validated as
+ * tg_gated_attention_backward (a batch of one) before anything is launched;
+ * up to 64 sequences share one launch of each kernel (longest first), and
+ * each sequence's results equal that batch-of-one call's bit for bit.
  */
 int tg_gated_attention_backward_varlen(const void* q, const void* k,
                                        const void* v, const void* out,

@@ -428,9 +428,8 @@ def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key
     dev = q.device
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty(T, device=dev),
              torch.empty((B, Hq), device=dev), torch.empty((B, Hq), device=dev)]
-    max_m = max([cu[i + 1] - cu[i] for i in range(B)] + [0])
-    if ws is None:
-        ws = attention_backward_workspace(1, max(max_m, 1), Hq, Hkv, dh, dev)
+    if ws is None:  # every sequence padded to 64 rows, side by side
+        ws = attention_backward_workspace(1, max(T + 63 * B, 1), Hq, Hkv, dh, dev)
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
     _check(lib.tg_gated_attention_backward_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),

@@ -124,19 +124,6 @@ struct SeqTable {
   int wg0[kMaxSeqsPerLaunch + 1];
 };
 
-// the last s < n with first[s] <= x (first[0] = 0 <= x)
-__device__ __forceinline__ int seq_of(const int* first, int n, int x) {
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (first[mid] <= x)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 // Prepass, per 64-key block of KV head g:
 //   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
 //   in slot order, zero beyond M);

@@ -42,6 +42,9 @@
 // first and the second products of step p, while the matrix cores work.
 #include <math.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "rope_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
@@ -160,20 +163,48 @@ __device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t r, unsigned ch
   dma16(r, tile + e * 1024, row * row_bytes + c * 16, 0);
 }
 
+// Sequences of one varying-length backward launch (longest first; empty ones
+// take no work).  Sequence s owns packed rows t0[s] .. t0[s] + m[s] - 1,
+// padded row slots p0[s] .. p0[s] + roundup(m[s], 64) - 1 of the row
+// constants and partials, 64-row blocks pb0[s] .. pb0[s+1] - 1 (the rows
+// kernel; the dK/dV workgroups are Hkv per block), dQ workgroups qb0[s] ..
+// qb0[s+1] - 1, and row out_row[s] of the gain and temperature gradients.
+// n = 0: an equal-length batch, indexed by the grid's batch coordinate.
+constexpr int kMaxBwdSeqs = 64;
+struct BwdSeqTable {
+  int n;
+  int t0[kMaxBwdSeqs];
+  int m[kMaxBwdSeqs];
+  int p0[kMaxBwdSeqs];
+  int out_row[kMaxBwdSeqs];
+  int pb0[kMaxBwdSeqs + 1];
+  int qb0[kMaxBwdSeqs + 1];
+};
+
 // ---------------------------------------------------------------------------
 // Per (query row, head): D_i = dO_i . O_i (fp32, fixed order: four threads per
 // row), c_i log2(e), lse_i log2(e); rows M .. Mp-1 get 0, +inf, 0.
 template <int DH>
 __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    const int32_t* __restrict__ pos, const float* __restrict__ temp, float sm_scale, int M, int Mp, int Hq,
-    float* __restrict__ rowc, float* __restrict__ rowl, float* __restrict__ rowD) {
-  const int b = blockIdx.z, h = blockIdx.y;
+    const int32_t* __restrict__ pos, const float* __restrict__ temp, float sm_scale, int M_all, int Mp_all, int Hq,
+    float* __restrict__ rowc, float* __restrict__ rowl, float* __restrict__ rowD, const BwdSeqTable st) {
+  const int h = blockIdx.y;
+  int M = M_all, Mp = Mp_all, blk = blockIdx.x;
+  size_t T0 = (size_t)blockIdx.z * M_all, P0 = (size_t)blockIdx.z * Mp_all;
+  if (st.n > 0) {
+    const int sq = seq_of(st.pb0, st.n, blockIdx.x);
+    M = st.m[sq];
+    Mp = (M + kPB - 1) / kPB * kPB;
+    blk = blockIdx.x - st.pb0[sq];
+    T0 = (size_t)st.t0[sq];
+    P0 = (size_t)st.p0[sq];
+  }
   const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
-  const int i = blockIdx.x * kPB + r;
+  const int i = blk * kPB + r;
   float acc = 0.0f;
   if (i < M) {
-    const size_t off = (((size_t)b * M + i) * Hq + h) * DH + part * (DH / 4);
+    const size_t off = ((T0 + i) * Hq + h) * DH + part * (DH / 4);
 #pragma unroll
     for (int c = 0; c < DH / 32; ++c) {
       const u32x4 ov = load16(o + off + c * 8), dv = load16(dout + off + c * 8);
@@ -187,13 +218,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_rows_kernel(
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   if (part == 0) {
-    const size_t idx = ((size_t)b * Hq + h) * Mp + i;
+    const size_t idx = P0 * Hq + (size_t)h * Mp + i;
     if (i < M) {
-      const int p = pos[(size_t)b * M + i];
+      const int p = pos[T0 + i];
       float ratio = 1.0f;
       if (p != i) ratio = logf((float)max(p + 1, 2)) / logf((float)max(i + 1, 2));
       rowc[idx] = sm_scale * kLog2e / (temp[h] * ratio);
-      rowl[idx] = lse[((size_t)b * Hq + h) * M + i] * kLog2e;
+      rowl[idx] = lse[T0 * Hq + (size_t)h * M + i] * kLog2e;
       rowD[idx] = acc;
     } else {
       rowc[idx] = 0.0f;
@@ -208,9 +239,9 @@ template <int DH, int G, bool F32OUT>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
-    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
-    int Hq, int Hkv, int nkb, int total_wg, void* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ dbp, float* __restrict__ gpart, float* __restrict__ tpart) {
+    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M_all,
+    int Mp_all, int Hq, int Hkv, int nkb, int total_wg, void* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dbp, float* __restrict__ gpart, float* __restrict__ tpart, const BwdSeqTable st) {
   constexpr int KS = DH / 16;       // k-steps over dh
   constexpr int DT = DH / 32;       // 32-row blocks of dK^T and dV^T
   constexpr int TB = kT * DH * 2;   // bytes of a 32 x DH bf16 tile
@@ -226,9 +257,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kh = w & 1, par = w >> 1;
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bg = logical / nkb;
-  const int kb = logical - bg * nkb;  // lowest key blocks (most query tiles) first
-  const int b = bg / Hkv, g = bg - b * Hkv;
+  // sequence (length M, first packed row T0, first padded slot P0), KV head
+  // g and key block kb: the lowest key blocks (most query tiles) first
+  int M = M_all, Mp = Mp_all, g, kb;
+  size_t T0, P0;
+  if (st.n > 0) {
+    const int sq = seq_of(st.pb0, st.n, logical / Hkv);
+    M = st.m[sq];
+    Mp = (M + kPB - 1) / kPB * kPB;
+    const int nk = st.pb0[sq + 1] - st.pb0[sq], local = logical - Hkv * st.pb0[sq];
+    g = local / nk;
+    kb = local - g * nk;
+    T0 = (size_t)st.t0[sq];
+    P0 = (size_t)st.p0[sq];
+  } else {
+    const int bg = logical / nkb;
+    kb = logical - bg * nkb;
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    T0 = (size_t)b * M;
+    P0 = (size_t)b * Mp;
+  }
   const int key0 = kb * kKB, kw0 = key0 + 32 * kh;
   const int kl = lane & 31, gq = lane >> 5;
   const int j = kw0 + kl;  // this lane's key
@@ -240,14 +289,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 
   bf16x8 kf[KS], vf[KS];
   {
-    const size_t off = (((size_t)b * M + (j_ok ? j : 0)) * Hkv + g) * DH + gq * 8;
+    const size_t off = ((T0 + (j_ok ? j : 0)) * Hkv + g) * DH + gq * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       kf[s] = as_bf16x8(j_ok ? load16(k + off + s * 16) : u32x4{0, 0, 0, 0});
       vf[s] = as_bf16x8(j_ok ? load16(v + off + s * 16) : u32x4{0, 0, 0, 0});
     }
   }
-  const float bj = j_ok ? kscore[(size_t)b * M + j] : 0.0f;
+  const float bj = j_ok ? kscore[T0 + j] : 0.0f;
   float kbias[G];  // gain_h log2(e) b_j of each head of the group
 #pragma unroll
   for (int i = 0; i < G; ++i) kbias[i] = gain[g * G + i] * kLog2e * bj;
@@ -261,13 +310,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int hl = u % G, t = t0 + u / G;
     const int h = g * G + hl;
     unsigned char* base = smem + ((step % NBUF) * 2 + par) * UB;
-    const size_t row0 = (((size_t)b * M + t * kT) * Hq + h) * DH;
+    const size_t row0 = ((T0 + t * kT) * Hq + h) * DH;
     const int nrec = (int)(((long long)(M - 1 - t * kT) * Hq + 1) * DH * 2);
     if (kh == 0) {
       const auto rq = rsrc(q + row0, nrec);
 #pragma unroll
       for (int e = 0; e < NI; ++e) stage_rows<DH>(rq, base, Hq * DH * 2, e, lane);
-      const size_t rr = ((size_t)b * Hq + h) * Mp + t * kT;  // 32 constants; lanes 32..63 read 0
+      const size_t rr = P0 * Hq + (size_t)h * Mp + t * kT;  // 32 constants; lanes 32..63 read 0
       dma4(rsrc(rowc + rr, kT * 4), base + RC, lane * 4, 0);
       dma4(rsrc(rowl + rr, kT * 4), base + RL, lane * 4, 0);
       dma4(rsrc(rowD + rr, kT * 4), base + RD, lane * 4, 0);
@@ -404,7 +453,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         dVt[blk][r] += mine[((blk * 2 + 1) * 16 + r) * 64 + lane];
       }
     if (j_ok) {
-      const size_t row = (((size_t)b * M + j) * Hkv + g) * DH;
+      const size_t row = ((T0 + j) * Hkv + g) * DH;
 #pragma unroll
       for (int blk = 0; blk < DT; ++blk)
 #pragma unroll
@@ -426,7 +475,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       gw[i] = wave_sum_f32(gq == 0 ? bj * c : 0.0f);
       tw[i] = wave_sum_f32(ta[i] + sums[(G + i) * 64 + lane]);
     }
-    if (gq == 0 && j_ok) dbp[((size_t)b * Hkv + g) * Mp + j] = dbs;
+    if (gq == 0 && j_ok) dbp[P0 * Hkv + (size_t)g * Mp + j] = dbs;
   }
   __syncthreads();
   if (par == 0 && lane == 0) {
@@ -438,7 +487,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   }
   __syncthreads();
   if (w == 0 && lane < G) {
-    const size_t o = ((size_t)b * nkb + kb) * Hq + g * G + lane;
+    const size_t o = (P0 / kKB + kb) * Hq + g * G + lane;
     gpart[o] = s_x[lane] + s_x[2 * G + lane];
     tpart[o] = s_x[G + lane] + s_x[3 * G + lane];
   }
@@ -449,8 +498,8 @@ template <int DH, int G, bool F32OUT>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
-    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M, int Mp,
-    int Hq, int Hkv, int nqb, int total_wg, void* __restrict__ dq) {
+    const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M_all,
+    int Mp_all, int Hq, int Hkv, int nqb, int total_wg, void* __restrict__ dq, const BwdSeqTable st) {
   constexpr int RG = 4 / G;
   constexpr int BQ = 32 * RG;
   constexpr int KS = DH / 16, DT = DH / 32;
@@ -465,9 +514,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bg = logical / nqb;
-  const int qb = nqb - 1 - (logical - bg * nqb);  // heaviest (latest) query blocks first
-  const int b = bg / Hkv, g = bg - b * Hkv;
+  // sequence, KV head g and query block qb: the heaviest (latest) first
+  int M = M_all, Mp = Mp_all, g, qb;
+  size_t T0, P0;
+  if (st.n > 0) {
+    const int sq = seq_of(st.qb0, st.n, logical);
+    M = st.m[sq];
+    Mp = (M + kPB - 1) / kPB * kPB;
+    const int nq = (M + BQ - 1) / BQ, local = logical - st.qb0[sq];
+    g = local / nq;
+    qb = nq - 1 - (local - g * nq);
+    T0 = (size_t)st.t0[sq];
+    P0 = (size_t)st.p0[sq];
+  } else {
+    const int bg = logical / nqb;
+    qb = nqb - 1 - (logical - bg * nqb);
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    T0 = (size_t)b * M;
+    P0 = (size_t)b * Mp;
+  }
   const int q0 = qb * BQ;
   const int h = g * G + w / RG;
   const int qw0 = q0 + 32 * (w % RG);
@@ -478,22 +544,22 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 
   bf16x8 qf[KS], df[KS];
   {
-    const size_t off = (((size_t)b * M + (q_ok ? qi : 0)) * Hq + h) * DH + gq * 8;
+    const size_t off = ((T0 + (q_ok ? qi : 0)) * Hq + h) * DH + gq * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       qf[s] = as_bf16x8(q_ok ? load16(q + off + s * 16) : u32x4{0, 0, 0, 0});
       df[s] = as_bf16x8(q_ok ? load16(dout + off + s * 16) : u32x4{0, 0, 0, 0});
     }
   }
-  const size_t ridx = ((size_t)b * Hq + h) * Mp + (q_ok ? qi : 0);
+  const size_t ridx = P0 * Hq + (size_t)h * Mp + (q_ok ? qi : 0);
   const float cq = q_ok ? rowc[ridx] : 0.0f;
   const float lq = q_ok ? rowl[ridx] : INFINITY;
   const float Dq = q_ok ? rowD[ridx] : 0.0f;
   const float gl2 = gain[h] * kLog2e;
 
-  const uint16_t* kbase = k + ((size_t)b * M * Hkv + g) * DH;
-  const uint16_t* vbase = v + ((size_t)b * M * Hkv + g) * DH;
-  const auto rks = rsrc(kscore + (size_t)b * M, M * 4);
+  const uint16_t* kbase = k + (T0 * Hkv + g) * DH;
+  const uint16_t* vbase = v + (T0 * Hkv + g) * DH;
+  const auto rks = rsrc(kscore + T0, M * 4);
   // Tile t: K and V rows (rows >= M read 0) and 64 key scores (those >= M
   // read 0); load x = w + 4 n of the 2 NI goes to wave w.
   auto stage = [&](int t) __attribute__((always_inline)) {
@@ -582,7 +648,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   }
   if (q_ok) {
     const float sc = cq * kLn2;  // c_i (the exponent constant carries log2(e))
-    const size_t row = (((size_t)b * M + qi) * Hq + h) * DH;
+    const size_t row = ((T0 + qi) * Hq + h) * DH;
 #pragma unroll
     for (int blk = 0; blk < DT; ++blk)
 #pragma unroll
@@ -644,7 +710,42 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_reduce_kernel(const float* __
                                                                   const float* __restrict__ temp, int B, int M,
                                                                   int Mp, int Hq, int Hkv, int nkb,
                                                                   float* __restrict__ db, float* __restrict__ dgain,
-                                                                  float* __restrict__ dtemp) {
+                                                                  float* __restrict__ dtemp, const BwdSeqTable st) {
+  if (st.n > 0) {
+    // the last n blocks: sequence s's gain and temperature gradients, in the
+    // order a batch-of-one call takes; the others: db over its padded slots
+    const int first_gain_block = gridDim.x - st.n;
+    if ((int)blockIdx.x >= first_gain_block) {
+      const int sq = blockIdx.x - first_gain_block;
+      const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+      const int nk = st.pb0[sq + 1] - st.pb0[sq];
+      const size_t x0 = (size_t)st.p0[sq] / kKB;
+      for (int h = wv; h < Hq; h += kBwdThreads / 64) {
+        double gs = 0.0, ts = 0.0;
+        for (int x = lane; x < nk; x += 64) {
+          gs += gpart[(x0 + x) * Hq + h];
+          ts += tpart[(x0 + x) * Hq + h];
+        }
+        gs = wave_sum_f64(gs);
+        ts = wave_sum_f64(ts);
+        if (lane == 0) {
+          dgain[(size_t)st.out_row[sq] * Hq + h] = (float)gs;
+          dtemp[(size_t)st.out_row[sq] * Hq + h] = (float)(-(double)kLn2 * ts / (double)temp[h]);
+        }
+      }
+      return;
+    }
+    const int slot = blockIdx.x * blockDim.x + threadIdx.x;
+    if (slot >= st.pb0[st.n] * kPB) return;
+    const int sq = seq_of(st.pb0, st.n, slot / kPB);
+    const int m = st.m[sq], mp = (m + kPB - 1) / kPB * kPB, jj = slot - st.pb0[sq] * kPB;
+    if (jj >= m) return;
+    const size_t P0 = (size_t)st.p0[sq];
+    float s = 0.0f;
+    for (int g = 0; g < Hkv; ++g) s += dbp[P0 * Hkv + (size_t)g * mp + jj];
+    db[(size_t)st.t0[sq] + jj] = s;
+    return;
+  }
   if (blockIdx.x == gridDim.x - 1) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for (int h = wv; h < Hq; h += kBwdThreads / 64) {
@@ -702,7 +803,7 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
       k = kr;
     }
     hipLaunchKernelGGL((bwd_rows_kernel<DH>), dim3(Mp / kPB, Hq, B), dim3(kBwdThreads), 0, s, o, dout, lse, pos,
-                       temp, sm_scale, M, Mp, Hq, rowc, rowl, rowD);
+                       temp, sm_scale, M, Mp, Hq, rowc, rowl, rowD, BwdSeqTable{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long ta = (long long)nkb * Hkv * B;
@@ -711,18 +812,20 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (ta > 0x7FFFFFFF || tb > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (rope)
       hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, true>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk32, dv, dbp, gpart, tpart);
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk32, dv, dbp, gpart, tpart,
+                         BwdSeqTable{});
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3((unsigned)ta), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart);
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nkb, (int)ta, dk, dv, dbp, gpart, tpart,
+                         BwdSeqTable{});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (rope)
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, true>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq32);
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq32, BwdSeqTable{});
     else
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq);
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq, BwdSeqTable{});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (rope) {
@@ -735,7 +838,41 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const size_t n = (size_t)B * M;
   const unsigned grid = (unsigned)((n + kBwdThreads - 1) / kBwdThreads) + 1;
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kBwdThreads), 0, s, dbp, gpart, tpart, temp, B, M, Mp, Hq,
-                     Hkv, M > 0 ? nkb : 0, db, dgain, dtemp);
+                     Hkv, M > 0 ? nkb : 0, db, dgain, dtemp, BwdSeqTable{});
+  return hipGetLastError();
+}
+
+// One launch of each kernel over the sequences of a table (no rotary variant).
+template <int DH, int G>
+hipError_t launch_bwd_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                               const float* lse, const uint16_t* dout, const BwdSeqTable& st, int Hq, int Hkv,
+                               const float* ks, const int32_t* pos, const float* gain, const float* temp,
+                               float sm_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* db, float* dgain,
+                               float* dtemp, size_t slots, void* ws, hipStream_t s) {
+  const size_t rn = (size_t)Hq * slots;
+  float* rowc = static_cast<float*>(ws);
+  float* rowl = rowc + rn;
+  float* rowD = rowl + rn;
+  float* dbp = rowD + rn;
+  float* gpart = dbp + (size_t)Hkv * slots;
+  float* tpart = gpart + slots / kKB * Hq;
+  const int nblk = st.pb0[st.n];
+  hipError_t e;
+  if (nblk > 0) {
+    hipLaunchKernelGGL((bwd_rows_kernel<DH>), dim3(nblk, Hq, 1), dim3(kBwdThreads), 0, s, o, dout, lse, pos, temp,
+                       sm_scale, 0, 0, Hq, rowc, rowl, rowD, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ta = nblk * Hkv;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3(ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc, rowl,
+                       rowD, ks, gain, 0, 0, Hq, Hkv, 0, ta, dk, dv, dbp, gpart, tpart, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                       rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const unsigned grid = (unsigned)(((size_t)nblk * kPB + kBwdThreads - 1) / kBwdThreads) + st.n;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(grid), dim3(kBwdThreads), 0, s, dbp, gpart, tpart, temp, 0, 0, 0, Hq, Hkv,
+                     0, db, dgain, dtemp, st);
   return hipGetLastError();
 }
 
@@ -754,6 +891,69 @@ size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh)
 size_t gated_attention_rope_backward_workspace(int B, int M, int Hq, int Hkv, int dh) {
   if (M <= 0) return 0;
   return rope_ws_offset(B, M, Hq, Hkv, dh) + (size_t)B * M * (Hq + Hkv) * dh * (2 + 4);
+}
+
+size_t gated_attention_backward_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv) {
+  size_t slots = 0;
+  for (int b = 0; b < B; ++b) slots += (size_t)(cu_seqlens[b + 1] - cu_seqlens[b] + kPB - 1) / kPB * kPB;
+  return slots * (size_t)(12 * Hq + 4 * Hkv) + 8 * (slots / kKB) * Hq;
+}
+
+hipError_t launch_gated_attention_backward_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                                  const uint16_t* out, const float* lse, const uint16_t* d_out, int B,
+                                                  const int32_t* cu_seqlens, int Hq, int Hkv, int dh,
+                                                  const float* key_score, const int32_t* pos, const float* gain,
+                                                  const float* temp, float sm_scale, uint16_t* dq, uint16_t* dk,
+                                                  uint16_t* dv, float* d_key_score, float* d_gain, float* d_temp,
+                                                  void* ws, hipStream_t s) {
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4) return hipErrorInvalidValue;
+  const int BQ = 32 * (4 / G);
+  // every sequence (the empty ones get zero gain and temperature gradients), longest first
+  std::vector<int> order(B);
+  for (int b = 0; b < B; ++b) order[b] = b;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int c) {
+    return cu_seqlens[a + 1] - cu_seqlens[a] > cu_seqlens[c + 1] - cu_seqlens[c];
+  });
+  size_t slots = 0;
+  for (int b = 0; b < B; ++b) slots += (size_t)(cu_seqlens[b + 1] - cu_seqlens[b] + kPB - 1) / kPB * kPB;
+  size_t p = 0;
+  for (size_t i = 0; i < order.size(); i += kMaxBwdSeqs) {
+    BwdSeqTable st{};
+    st.n = (int)std::min(order.size() - i, (size_t)kMaxBwdSeqs);
+    long long pb = 0, qw = 0;
+    for (int j = 0; j < st.n; ++j) {
+      const int b = order[i + j], m = cu_seqlens[b + 1] - cu_seqlens[b];
+      const int mp = (m + kPB - 1) / kPB * kPB;
+      if (p + mp > 0x7FFFFFFF) return hipErrorInvalidValue;
+      st.t0[j] = cu_seqlens[b];
+      st.m[j] = m;
+      st.p0[j] = (int)p;
+      st.out_row[j] = b;
+      st.pb0[j] = (int)pb;
+      st.qb0[j] = (int)qw;
+      p += mp;
+      pb += mp / kPB;
+      qw += (long long)((m + BQ - 1) / BQ) * Hkv;
+      if (pb * Hkv > 0x7FFFFFFF / kBwdThreads || qw > 0x7FFFFFFF / kBwdThreads) return hipErrorInvalidValue;
+    }
+    st.pb0[st.n] = (int)pb;
+    st.qb0[st.n] = (int)qw;
+    hipError_t e = hipErrorInvalidValue;
+#define TG_BWD_VARLEN_CASE(DHV, GV)                                                                              \
+  if (dh == DHV && G == GV)                                                                                      \
+    e = launch_bwd_varlen_t<DHV, GV>(q, k, v, out, lse, d_out, st, Hq, Hkv, key_score, pos, gain, temp, sm_scale, \
+                                     dq, dk, dv, d_key_score, d_gain, d_temp, slots, ws, s);
+    TG_BWD_VARLEN_CASE(128, 2)
+    TG_BWD_VARLEN_CASE(128, 1)
+    TG_BWD_VARLEN_CASE(128, 4)
+    TG_BWD_VARLEN_CASE(64, 2)
+    TG_BWD_VARLEN_CASE(64, 1)
+    TG_BWD_VARLEN_CASE(64, 4)
+#undef TG_BWD_VARLEN_CASE
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gated_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -472,34 +472,37 @@ int tg_gated_attention_backward_varlen(const void* q, const void* k, const void*
   const char* name = "tg_gated_attention_backward_varlen";
   if (B <= 0 || !cu_seqlens) return fail(TG_EINVAL, "%s: B must be > 0 and cu_seqlens given", name);
   if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
-  int max_m = 0;
-  for (int b = 0; b < B; ++b) {
-    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-    if (m < 0) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
-    max_m = m > max_m ? m : max_m;
-  }
-  const size_t need = max_m > 0 ? tg::gated_attention_backward_workspace(1, max_m, Hq, Hkv, d_h) : 0;
-  if (max_m > 0 && (!ws || ws_bytes < need))
+  for (int b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
+  if ((size_t)cu_seqlens[B] + 63 * (size_t)B > 0x7FFFFFFF)
+    return fail(TG_EINVAL, "%s: the padded rows exceed the 32-bit index range", name);
+  // every sequence's row constants and partials sit side by side
+  const size_t need = tg::gated_attention_backward_varlen_workspace(B, cu_seqlens, Hq, Hkv);
+  if (need > 0 && (!ws || ws_bytes < need))
     return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
   if (!d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
-  // one batch-of-one backward per sequence, in order on the stream (shared
-  // workspace); sequence b's gain and temperature gradients go to row b
-  for (int pass = 0; pass < 2; ++pass) {  // all sequences are validated before any runs
-    for (int b = 0; b < B; ++b) {
-      const size_t t0 = (size_t)cu_seqlens[b];
-      const int m = cu_seqlens[b + 1] - cu_seqlens[b];
-      const size_t qo = t0 * Hq * d_h, ko = t0 * Hkv * d_h;
-      const int rc = attention_backward_common(
-          name, static_cast<const uint16_t*>(q) + qo, static_cast<const uint16_t*>(k) + ko,
-          static_cast<const uint16_t*>(v) + ko, static_cast<const uint16_t*>(out) + qo,
-          lse ? lse + t0 * Hq : nullptr, static_cast<const uint16_t*>(d_out) + qo, 1, m, Hq, Hkv, d_h,
-          key_score + t0, pos + t0, gain, temp, sm_scale, 0.0, static_cast<uint16_t*>(d_q) + qo,
-          static_cast<uint16_t*>(d_k) + ko, static_cast<uint16_t*>(d_v) + ko, d_key_score + t0,
-          d_gain + (size_t)b * Hq, d_temp + (size_t)b * Hq, ws, ws_bytes, stream, pass == 1);
-      if (rc != TG_OK) return rc;
-    }
+  // each sequence is validated as a batch of one; then the batch is launched
+  // (sequence b's gain and temperature gradients go to row b)
+  for (int b = 0; b < B; ++b) {
+    const size_t t0 = (size_t)cu_seqlens[b];
+    const int m = cu_seqlens[b + 1] - cu_seqlens[b];
+    const size_t qo = t0 * Hq * d_h, ko = t0 * Hkv * d_h;
+    const int rc = attention_backward_common(
+        name, static_cast<const uint16_t*>(q) + qo, static_cast<const uint16_t*>(k) + ko,
+        static_cast<const uint16_t*>(v) + ko, static_cast<const uint16_t*>(out) + qo, lse ? lse + t0 * Hq : nullptr,
+        static_cast<const uint16_t*>(d_out) + qo, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp, sm_scale,
+        0.0, static_cast<uint16_t*>(d_q) + qo, static_cast<uint16_t*>(d_k) + ko, static_cast<uint16_t*>(d_v) + ko,
+        d_key_score + t0, d_gain + (size_t)b * Hq, d_temp + (size_t)b * Hq, ws, ws_bytes, stream, false);
+    if (rc != TG_OK) return rc;
   }
-  return TG_OK;
+  return hip_status(tg::launch_gated_attention_backward_varlen(
+                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(out), lse,
+                        static_cast<const uint16_t*>(d_out), B, cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp,
+                        sm_scale, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
+                        static_cast<uint16_t*>(d_v), d_key_score, d_gain, d_temp, ws,
+                        static_cast<hipStream_t>(stream)),
+                    name);
 }
 
 }  // extern "C"

@@ -122,4 +122,20 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
   return x * q + (x < rem ? x : rem) + (id >> 3);
 }
 
+// The last s < n with first[s] <= x, for non-decreasing first[] with
+// first[0] = 0 <= x (the sequence of a block or workgroup in a varlen table;
+// empty sequences, whose first equals the next one's, are never returned
+// for x < first[n]).
+__device__ __forceinline__ int seq_of(const int* first, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 }  // namespace tg

@@ -333,3 +333,42 @@ def test_varlen_attention_many_sequences(dh, Hq, Hkv):
             assert_close(wl.bf16_bits_to_f32(host_bits(out[None, s0:s1])), O, TOL_BF16, f"varlen oracle {i}")
             checked += 1
     assert checked >= 5
+
+
+@pytest.mark.parametrize("dh,Hq,Hkv", [(128, 4, 2), (64, 8, 2)])
+def test_varlen_attention_backward_many_sequences(dh, Hq, Hkv):
+    """100 packed sequences (two launches of 64), lengths 0 .. 300 with tile
+    edges and empty ones: per sequence the packed backward equals the batched
+    backward of that sequence alone bit for bit; empty sequences get zero gain
+    and temperature gradients."""
+    rng = np.random.default_rng(dh * 3 + Hq)
+    lens = list(rng.integers(0, 301, size=93)) + [0, 1, 31, 32, 33, 64, 0]
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+    T = cu[-1]
+    say(f"varlen attention backward dh={dh} Hq={Hq} Hkv={Hkv} sequences={len(lens)} rows={T}")
+    a = wl.attn_case(M=T, Hq=Hq, Hkv=Hkv, dh=dh, seed=dh + 5, r_zero=0)
+    q, k, v = (dev_bits(x[0]) for x in (a.q, a.k, a.v))
+    b = rng.standard_normal(T).astype(np.float32)
+    pos = np.concatenate([np.sort(rng.choice(3 * max(n, 1), n, replace=False)) for n in lens]).astype(np.int32)
+    dO_bits = wl.f32_to_bf16_bits(rng.standard_normal((T, Hq, dh), dtype=np.float32))
+    gain, temp = dev(a.gain), dev(a.temp)
+    out, lse = tg.tg_gated_attention_varlen(q, k, v, cu, dev(b), dev(pos), gain, temp, a.sm_scale,
+                                            lse=torch.empty(T * Hq, dtype=torch.float32, device=DEV))
+    g = tg.tg_gated_attention_backward_varlen(q, k, v, out, lse, dev_bits(dO_bits), cu, dev(b), dev(pos), gain, temp,
+                                              a.sm_scale)
+    torch.cuda.synchronize()
+    for i, m in enumerate(lens):
+        s0, s1 = cu[i], cu[i + 1]
+        if m == 0:
+            assert torch.all(g[4][i] == 0) and torch.all(g[5][i] == 0)
+            continue
+        one = tg.tg_gated_attention_backward(
+            q[None, s0:s1].contiguous(), k[None, s0:s1].contiguous(), v[None, s0:s1].contiguous(),
+            out[None, s0:s1].contiguous(), lse[s0 * Hq:s1 * Hq].reshape(1, Hq, m).contiguous(),
+            dev_bits(dO_bits[None, s0:s1]), dev(b[None, s0:s1]), dev(pos[None, s0:s1]), gain, temp, a.sm_scale)
+        for n_, x, y in zip(("d_q", "d_k", "d_v", "d_key_score", "d_gain", "d_temp"),
+                            (g[0][s0:s1], g[1][s0:s1], g[2][s0:s1], g[3][s0:s1], g[4][i], g[5][i]),
+                            (one[0][0], one[1][0], one[2][0], one[3][0], one[4], one[5])):
+            assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), \
+                f"sequence {i} (M={m}) {n_}"
