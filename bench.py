@@ -133,6 +133,58 @@ def time_backward(torch, tg, qkv, b_S, kept_idx, layer, attn_out, heads, M, stre
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "shape": {"M": M, "Hq": Hq, "Hkv": Hkv, "d_h": dh}}
 
 
+def time_varlen(torch, tg, layer, heads, M, n_seq=16, reps=20):
+    """Token-gated attention over a packed batch of `n_seq` gated prompts
+    (kept lengths uniform in [M/8, M], seeded; random bf16 q, k, v, scores and
+    sorted original positions), timed on its own: one tg_gated_attention_varlen
+    call, and for context the same sequences as one batch-of-one
+    tg_gated_attention call each.  Algorithmic work: the forward's two causal
+    products per sequence, 2 d_h Hq m (m + 1) flops."""
+    Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+    g = torch.Generator().manual_seed(2468)
+    lens = torch.randint(max(M // 8, 1), M + 1, (n_seq,), generator=g).tolist()
+    cu = [0]
+    for m in lens:
+        cu.append(cu[-1] + m)
+    T = cu[-1]
+    dev = layer.gain.device
+    q = torch.randn((T, Hq, dh), generator=g).bfloat16().to(dev)
+    k = torch.randn((T, Hkv, dh), generator=g).bfloat16().to(dev)
+    v = torch.randn((T, Hkv, dh), generator=g).bfloat16().to(dev)
+    ks = torch.randn(T, generator=g).to(dev)
+    pos = torch.cat([torch.sort(torch.randperm(4 * m, generator=g)[:m]).values for m in lens]).int().to(dev)
+    out = torch.empty_like(q)
+    ws = tg.attention_workspace(1, T + 63 * n_seq, Hq, Hkv, dh, dev)
+    packed = lambda: tg.tg_gated_attention_varlen(q, k, v, cu, ks, pos, layer.gain, layer.temp,  # noqa: E731
+                                                  out=out, ws=ws)
+    views = [(q[None, a:b], k[None, a:b], v[None, a:b], ks[None, a:b], pos[None, a:b], out[None, a:b])
+             for a, b in zip(cu[:-1], cu[1:])]
+
+    def per_sequence():
+        for qq, kk, vv, ss, pp, oo in views:
+            tg.tg_gated_attention(qq, kk, vv, ss, pp, layer.gain, layer.temp, out=oo, ws=ws)
+
+    res = {}
+    for name, call in (("avg_us", packed), ("per_sequence_calls_us", per_sequence)):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 3)
+    flops = sum(2 * dh * Hq * m * (m + 1) for m in lens)
+    tf = flops / (res["avg_us"] * 1e-6) / 1e12
+    return {"call": "tg_gated_attention_varlen", "avg_us": res["avg_us"], "calls_timed": reps,
+            "per_sequence_calls_us": res["per_sequence_calls_us"], "algorithmic_flops": flops,
+            "achieved_TFLOPs": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "shape": {"sequences": n_seq, "rows": T, "min_M": min(lens), "max_M": max(lens), "Hq": Hq,
+                      "Hkv": Hkv, "d_h": dh}}
+
+
 STAGE_GATE_LAYER = 4  # the stage workload's gate layer L: layers 0..L hold full-length KV caches
 
 
@@ -218,6 +270,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv-prune", action="store_true",
                     help="skip the separate timing of tg_kv_cache_prune (layers 0..L of the stage)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed varying-length attention timing")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of tg_gated_attention_backward at the attention shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -454,6 +508,8 @@ def main():
         "tokens_per_s_with_glue": round(N / ((ms_per_step + glue_ms) * 1e-3), 1),
     }
 
+    if layers and not args.no_varlen:
+        out["varlen_attention"] = time_varlen(torch, tg, layers[0], heads, M)
     if layers and not args.no_backward:
         out["attention_backward"] = time_backward(torch, tg, qkv[0], b_S, kept_idx, layers[0], attn_out, heads, M,
                                                   stream_reps=20)
