@@ -129,3 +129,53 @@ def test_stage_graph_replays_match_eager():
         torch.cuda.synchronize()
         _same(st.results(), ref[1 - which], f"eager pass after replay {rep}")
     say("  4 replays and 4 eager passes bit-identical")
+
+
+def test_varlen_graph_replays_match_eager():
+    """The packed varying-length attention and its backward captured in one
+    graph (72 sequences: two launches of each kernel; their sequence tables
+    travel in the kernel arguments): every replay, with its outputs poisoned
+    before it and eager work after it, equals the eager call bit for bit."""
+    lens = [300, 0, 129, 64, 1, 500] * 12
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+    T, B = cu[-1], len(lens)
+    say(f"graph: varlen attention + backward, {B} sequences, {T} rows")
+    g = torch.Generator(device=DEV).manual_seed(9)
+    q = torch.randn(T, HQ, DH, device=DEV, generator=g).bfloat16()
+    k = torch.randn(T, HKV, DH, device=DEV, generator=g).bfloat16()
+    v = torch.randn(T, HKV, DH, device=DEV, generator=g).bfloat16()
+    d_out = torch.randn(T, HQ, DH, device=DEV, generator=g).bfloat16()
+    ks = torch.randn(T, device=DEV, generator=g)
+    pos = torch.cat([torch.arange(m, dtype=torch.int32, device=DEV) * 3 for m in lens])
+    gain, temp = torch.rand(HQ, device=DEV, generator=g) + 0.5, torch.full((HQ,), 1.2, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(T * HQ, dtype=torch.float32, device=DEV)
+    ws_f = tg.attention_workspace(1, T + 63 * B, HQ, HKV, DH, DEV)
+    ws_b = tg.attention_backward_workspace(1, T + 63 * B, HQ, HKV, DH, DEV)
+
+    def run():
+        tg.tg_gated_attention_varlen(q, k, v, cu, ks, pos, gain, temp, out=out, lse=lse, ws=ws_f)
+        return tg.tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu, ks, pos, gain, temp, ws=ws_b)
+
+    ref_grads = [x.clone() for x in run()]
+    torch.cuda.synchronize()
+    ref = [out.clone(), lse.clone()] + ref_grads
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        grads = run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in [out, lse] + list(grads):
+            x.view(torch.uint8).fill_(0xFF)  # NaN in both dtypes
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, y, name in zip([out, lse] + list(grads), ref, ["out", "lse", "d_q", "d_k", "d_v", "d_key_score",
+                                                              "d_gain", "d_temp"]):
+            assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), \
+                f"replay {rep}: {name}"
+        # eager work between replays (the batched attention on another shape)
+        tg.tg_gated_attention(q[None, :500].contiguous(), k[None, :500].contiguous(), v[None, :500].contiguous(),
+                              ks[None, :500].contiguous(), torch.arange(500, dtype=torch.int32, device=DEV)[None],
+                              gain, temp)
+        torch.cuda.synchronize()
+    say("  3 replays bit-identical")
