@@ -285,12 +285,17 @@ int tg_gate_select_varlen(const float* score_raw, int B, int N,
  *   out [B, M, Hq, d_h] bf16 (fp32 accumulate, round to nearest even)
  *   lse [B, Hq, M] fp32, or NULL to skip it
  *   ws, ws_bytes  workspace of at least tg_workspace_size(TG_OP_GATED_ATTENTION,
- *                 B, M, Hkv * d_h, Hq, 0) bytes, 16-byte aligned (holds an fp16
- *                 transposed copy of V and the per-head key-score term
- *                 gain[h] * key_score[j]; contents need no initialisation)
+ *                 B, M, Hkv * d_h, Hq, d_h) bytes, 16-byte aligned (holds an
+ *                 fp16 transposed copy of V, the per-head key-score term
+ *                 gain[h] * key_score[j] and the scale of each 64-key tile of
+ *                 V; contents need no initialisation)
  * Precision: Q.K^T runs on bf16 MFMA; the softmax numerator and V enter the
- * P.V product as fp16 (V scaled by 2^-8, so |v| up to 1.6e7 is exact and
- * larger magnitudes saturate).
+ * P.V product as fp16, fp32 accumulation.  Each 64-key tile of a KV head's V
+ * is scaled by a power of two that puts its largest |v| in [2^14, 2^15)
+ * (for tile maxima in [2^-36, 2^65)), so every value within a factor 2^28
+ * of its tile's largest converts exactly; the factor is taken out of the
+ * softmax numerator, which therefore keeps fp16's 11 significant bits
+ * relative to the row's largest contribution.
  * Supported: d_h in {64, 128}; Hq / Hkv in {1, 2, 4}.  M == 0 is a no-op.
  */
 int tg_gated_attention(const void* q, const void* k, const void* v,
@@ -310,7 +315,7 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
  *
  *   cu_seqlens [B + 1] int32 HOST array (cu_seqlens[0] = 0, non-decreasing)
  *   ws, ws_bytes     workspace of at least tg_workspace_size(
- *                    TG_OP_GATED_ATTENTION, 1, T + 63 * B, Hkv * d_h, Hq, 0)
+ *                    TG_OP_GATED_ATTENTION, 1, T + 63 * B, Hkv * d_h, Hq, d_h)
  *                    bytes, T = cu_seqlens[B] (every sequence's fp16 V^T copy
  *                    and key-score terms, each padded to 64 rows, side by
  *                    side), 16-byte aligned
@@ -479,8 +484,9 @@ int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers,
                       int M, void* k_out, void* v_out, void* stream);
 
 /* Workspace bytes an entry point needs for the given sizes (0 when none).
- * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h and
- * h = Hq; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * Hq).
+ * For TG_OP_GATED_ATTENTION pass N = M (kept length), d = Hkv * d_h, h = Hq
+ * and K = d_h; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * (Hq +
+ * Hkv)).  K = 0 gives the size for the largest Hkv (= Hq), an upper bound.
  * For TG_OP_GATED_ATTENTION_ROPE pass the same and K = d_h; the size adds
  * 2 * B * M * (Hq + Hkv) * d_h.
  * For TG_OP_GATED_ATTENTION_BACKWARD pass the same as for

@@ -440,7 +440,7 @@ def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key
 
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:
     """A workspace tensor large enough for tg_gated_attention at these sizes."""
-    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, Hq, 0))
+    n = int(load_library().tg_workspace_size(TG_OP_GATED_ATTENTION, B, M, Hkv * dh, Hq, dh))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 

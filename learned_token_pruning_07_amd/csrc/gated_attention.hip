@@ -34,13 +34,17 @@
 //  * The P.V product runs in fp16 (v_mfma_f32_32x32x16_f16): the softmax
 //    numerator P lies in [0, 2^15], where fp16 keeps 11 significant bits
 //    against bf16's 8, so rounding P costs 8x less.  V is converted once per
-//    call by a prepass into V^T (key-contiguous) fp16 scaled by 2^-8: bf16
-//    values convert exactly up to |v| = 65504 * 2^8 (larger values saturate),
-//    values below 2^-6 land in fp16's subnormal range with an absolute error
-//    under 2^-16.  The 2^8 is folded into the final 1/l.  Inside every 16-key
-//    group of V^T the middle two quads of keys are swapped, so that the 8
-//    keys one lane contributes to a 16-key P.V step (4 at 4*gq, 4 at
-//    8 + 4*gq) form one 16-byte chunk.
+//    call by a prepass into V^T (key-contiguous) fp16.  Each 64-key tile of
+//    a KV head is scaled by its own power of two 2^e, chosen from the tile's
+//    largest magnitude so that it lands in [2^14, 2^15): every bf16 value
+//    within 2^28 of the tile's largest converts exactly.  The factor moves
+//    to the numerators: the tile's key terms carry -e, so the kernel's
+//    numerator is P 2^-e and the product P 2^-e . V 2^e is unchanged, and
+//    the row sum, which needs P itself, multiplies the tile's numerator sum
+//    by 2^e (one product per half tile).  Inside every 16-key group of V^T
+//    the middle two quads of keys are swapped, so that the 8 keys one lane
+//    contributes to a 16-key P.V step (4 at 4*gq, 4 at 8 + 4*gq) form one
+//    16-byte chunk.
 //  * Tiles travel from global memory straight into LDS (buffer loads with the
 //    LDS-destination bit: each lane's 16 bytes land at the wave's LDS base +
 //    16 * lane), so staging costs no registers and no LDS store
@@ -51,7 +55,8 @@
 //    16-byte chunks XOR-swizzled by (row & 7), which keeps the fragment reads
 //    free of bank conflicts; the lane-to-chunk map of each load applies the
 //    same swizzle.  The prepass also writes the key-score term of every query
-//    head, gain_h * log2(e) * b_j, so that tile too is a plain copy.
+//    head, gain_h * log2(e) * b_j - e, and a row holding the tile's 2^e, so
+//    that those tiles too are plain copies.
 //  * Grid: heaviest causal query blocks first, remapped so that every
 //    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
 #include <math.h>
@@ -69,12 +74,32 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;  // keys per tile
 
-constexpr int kVScaleLog2 = 8;  // V^T holds fp16(V * 2^-8)
+// V^T tile scale exponents: the tile's largest |v| times 2^e lies in
+// [2^14, 2^15) when e is inside this range (tile maxima in [2^-36, 2^65)).
+// The range keeps the row sum, which carries 2^e, far inside fp32, and
+// bounds the spread of e between tiles (see the kernel's row sum).
+constexpr int kVExpMin = -50, kVExpMax = 50;
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
 // Outside the steady state the running max is only moved (and the
 // accumulator rescaled) when a half tile's max exceeds it by more than this
 // many log2 units; P stays <= 2^8 there.
 constexpr float kRescaleSlack = 8.0f;
+
+#ifdef TG_DIAG_COUNTERS
+// Test build only (libtokengate_diag.so): how often the kernel took its rare
+// paths, one count per wave and event.  0: a steady-state half whose
+// numerators left the fp16-safe range and was redone with a new reference;
+// 1: a mid-row move of the running max outside the steady state.
+__device__ unsigned long long g_diag_count[4];
+#define TG_DIAG_HIT(i)                                                  \
+  do {                                                                  \
+    if ((threadIdx.x & 63) == 0) atomicAdd(&g_diag_count[i], 1ull);     \
+  } while (0)
+#else
+#define TG_DIAG_HIT(i) \
+  do {                 \
+  } while (0)
+#endif
 
 template <int V>
 struct IntConst {
@@ -125,10 +150,14 @@ struct SeqTable {
 };
 
 // Prepass, per 64-key block of KV head g:
-//   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 (scaled by 2^-8, keys
-//   in slot order, zero beyond M);
-//   key-score term kb [B, Hq, Mp] fp32 = gain_h * log2(e) * key_score for the
-//   G query heads of g (zero beyond M);
+//   e = the block's scale exponent: 141 - (exponent field of the largest
+//   bf16 magnitude), clamped to [kVExpMin, kVExpMax], so that the largest
+//   |v| 2^e lies in [2^14, 2^15);
+//   V [B, M, Hkv, DH] bf16 -> V^T [B, Hkv, DH, Mp] fp16 = V 2^e (round to
+//   nearest even, keys in slot order, zero beyond M);
+//   key-score rows kb [B, Hkv, G + 1, Mp] fp32: row hh < G holds
+//   gain_h * log2(e) * key_score - e for query head h = g G + hh (zero
+//   beyond M), row G holds 2^e for every key of the block;
 //   with ROPE, also the rotary embedding of the block's K rows (head g) and Q
 //   rows (the G query heads of g) at their original positions (the rotate-
 //   half form: pair (x_i, x_{i+DH/2}) turns by pos * base^(-2i/DH)).  The
@@ -145,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
                                                                 const SeqTable st) {
   __shared__ uint16_t sT[DH][kBK + 2];
   __shared__ double s_freq[DH / 2];
+  __shared__ uint32_t s_mag[kThreads / 64];
   const int g = blockIdx.y;
   int m0, M, Mp;
   size_t T0, P0;  // first packed row and first padded key slot of this sequence
@@ -163,8 +193,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     P0 = (size_t)blockIdx.z * Mp;
   }
   const int tid = threadIdx.x;
-  if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);  // (ordered by the barrier below)
-  const float scale = 1.0f / (float)(1 << kVScaleLog2);
+  if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);  // (ordered by the barriers below)
   constexpr int NL = kBK * DH / 8 / kThreads;  // 16-byte loads per thread, all issued before any use
   u32x4 w[NL];
 #pragma unroll
@@ -174,10 +203,28 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     const int m = m0 + key;
     w[e] = m < M ? load16(v + ((T0 + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
   }
+  // the block's largest bf16 magnitude (sign cleared; NaN and inf compare
+  // above every finite value), as an integer max over the bit patterns
+  uint32_t mag = 0;
+#pragma unroll
+  for (int e = 0; e < NL; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mag = max(mag, max(w[e][i] & 0x7FFFu, (w[e][i] >> 16) & 0x7FFFu));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
+  if ((tid & 63) == 0) s_mag[tid >> 6] = mag;
+  __syncthreads();
+#pragma unroll
+  for (int wv = 0; wv < kThreads / 64; ++wv) mag = max(mag, s_mag[wv]);
+  const int ex = min(max(141 - (int)(mag >> 7), kVExpMin), kVExpMax);
+  const float scale = __uint_as_float((uint32_t)(ex + 127) << 23);  // 2^ex, exact
   const int Hq = Hkv * G;
-  for (int c = tid; c < G * kBK; c += kThreads) {
-    const int hq = g * G + c / kBK, m = m0 + c % kBK;
-    kbias[P0 * Hq + (size_t)hq * Mp + m] = m < M ? key_score[T0 + m] * (gain[hq] * kLog2e) : 0.0f;
+  const size_t kb_row = P0 * (size_t)(Hq + Hkv) + (size_t)g * (G + 1) * Mp;
+  for (int c = tid; c < (G + 1) * kBK; c += kThreads) {
+    const int hh = c / kBK, m = m0 + c % kBK;
+    float val = scale;
+    if (hh < G) val = m < M ? fmaf(key_score[T0 + m], gain[g * G + hh] * kLog2e, (float)-ex) : 0.0f;
+    kbias[kb_row + (size_t)hh * Mp + m] = val;
   }
 #pragma unroll
   for (int e = 0; e < NL; ++e) {
@@ -185,9 +232,8 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     const int key = c / (DH / 8), part = c % (DH / 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // round toward zero: exact for every in-range value, saturates beyond
-      const uint32_t h2 = __builtin_bit_cast(
-          uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[e][i]) * scale, bf16_hi(w[e][i]) * scale));
+      // exact for every value within 2^28 below the block's largest
+      const uint32_t h2 = pack_f16x2(bf16_lo(w[e][i]) * scale, bf16_hi(w[e][i]) * scale);
       sT[part * 8 + 2 * i][key] = (uint16_t)(h2 & 0xFFFFu);
       sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
     }
@@ -203,7 +249,6 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
   }
   if constexpr (ROPE) {
     constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
-    const int Hq = Hkv * G;
     for (int t = tid; t < kBK * PG; t += kThreads) {
       const int key = t / PG, i0 = (t % PG) * 8, m = m0 + key;
       if (m >= M) continue;
@@ -251,7 +296,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   constexpr int VROW = kBK * 2;     // bytes of a V^T row (64 keys, fp16)
   constexpr int TILE = kBK * DH * 2;           // bytes of a K tile = bytes of a V^T tile
   constexpr int NI = TILE / 1024 / 4;          // 1 KiB loads per wave per tile, for each of K and V^T
-  constexpr int BIAS = G * kBK * 4;            // bytes of a key-score tile (G heads)
+  constexpr int BIAS = (G + 1) * kBK * 4;      // bytes of a key-score tile (G heads, then the V^T scale row)
   constexpr int V_BASE = 2 * kGroups * TILE, B_BASE = 4 * kGroups * TILE;
   constexpr int LDS_BYTES = B_BASE + 3 * kGroups * BIAS;
   static_assert(NI >= 1 && NI * 4 * 1024 == TILE, "tile shape");
@@ -314,7 +359,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       const_cast<uint16_t*>(vt + P0 * Hkv * DH + (size_t)g * DH * Mp), (short)0, (int)((size_t)DH * Mp * 2),
       kBufferConfig);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(kbias + P0 * Hq + (size_t)g * G * Mp), (short)0, G * Mp * 4, kBufferConfig);
+      const_cast<float*>(kbias + P0 * (Hq + Hkv) + (size_t)g * (G + 1) * Mp), (short)0, (G + 1) * Mp * 4,
+      kBufferConfig);
   // Load e of this wave fills LDS bytes [1024 C, 1024 C + 1024) of the tile,
   // C = wid * NI + e: 16-byte slot Y = 64 C + lane sits at row Y / chunks-per-row,
   // position p, and holds chunk p ^ (row & 7) of that row.
@@ -350,8 +396,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       buffer_load16_to_lds(v_rsrc, vd + e * 1024, v_off[e], (grp + kGroups * t) * kBK * 2);
   };
   auto issue_b = [&](int t) __attribute__((always_inline)) {
+    const int soff = (grp + kGroups * t) * kBK * 4;
     if (wid < G)  // one 256-byte row per query head
-      buffer_load4_to_lds(b_rsrc, b_tile(t % 3) + wid * kBK, (wid * Mp + lane) * 4, (grp + kGroups * t) * kBK * 4);
+      buffer_load4_to_lds(b_rsrc, b_tile(t % 3) + wid * kBK, (wid * Mp + lane) * 4, soff);
+    if (wid == G % 4)  // and the tile's V^T scale row
+      buffer_load4_to_lds(b_rsrc, b_tile(t % 3) + G * kBK, (G * Mp + lane) * 4, soff);
   };
   // this lane's fragment chunks: K row ql (and ql + 32) chunk 2ks + gq; V^T row
   // 32t + ql chunk 2st + gq -- both swizzled by ql & 7
@@ -407,6 +456,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   auto softmax = [&](int h, f32x16& s, bool diag, uint32_t (&pk)[8], bool& resc,
                      float& alpha) __attribute__((always_inline)) {
     const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (h & 1) * 32 + gq * 4;
+    const float sc = b_tile((h >> 1) % 3)[G * kBK];  // the tile's V^T scale 2^e
     // logits (log2 domain); lane holds keys key0 + 8(i/4) + 4gq + (i%4)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -429,6 +479,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       mloc = max3f(__uint_as_float(pr[0]), __uint_as_float(pr[1]), __uint_as_float(pr[1]));
     }
     resc = __ballot(mloc > m_run + kRescaleSlack) != 0;  // wave-uniform
+    if (resc && m_run != -INFINITY) TG_DIAG_HIT(1);
     const float m_new = resc ? fmaxf(m_run, mloc) : m_run;
     alpha = m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -446,7 +497,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       pk[i / 2] = pack_f16x2(p0, p1);
       pk[i / 2 + 1] = pack_f16x2(p2, p3);
     }
-    l_run = fmaf(l_run, alpha, l0 + l1);
+    l_run = fmaf(l0 + l1, sc, l_run * alpha);
   };
   auto rescale = [&](bool resc, float alpha) __attribute__((always_inline)) {
     if (resc) {
@@ -495,6 +546,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     constexpr int NS = 2 * KS;
     static_assert(2 * DT == KS && 16 % NS == 0, "slot plan");
     const float* bt = b_tile((h >> 1) % 3) + hloc * kBK + (1 - SB) * 32 + gq * 4;
+    const float sc = b_tile((h >> 1) % 3)[G * kBK];  // the tile's V^T scale 2^e
     u32x4 fr[NS];
     auto read_frag = [&](int r) __attribute__((always_inline)) {
       if (r & 1) {
@@ -544,7 +596,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
         }
         if (v == 12) {
           ovf = __ballot(!(l <= 32768.0f)) != 0;  // wave-uniform; catches inf too
-          l_run = l_prev + l;
+          l_run = fmaf(l, sc, l_prev);
           asm volatile("" ::"v"(l_run));
         }
       }
@@ -553,6 +605,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     if (ovf) {
       // some numerator left the safe range: move the reference up to the
       // row's true max and redo this half's numerators
+      TG_DIAG_HIT(0);
       const float x0 = max3f(s[0], s[1], s[2]), x1 = max3f(s[3], s[4], s[5]), x2 = max3f(s[6], s[7], s[8]);
       const float x3 = max3f(s[9], s[10], s[11]), x4 = max3f(s[12], s[13], s[14]);
       float mloc = max3f(max3f(x0, x1, x2), x3, max3f(x4, s[15], s[15]));
@@ -567,7 +620,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
         l2 += p0 + p1;
         pc[e / 2] = pack_f16x2(p0, p1);
       }
-      l_run = fmaf(l_prev, alpha, l2);
+      l_run = fmaf(l2, sc, l_prev * alpha);
 #pragma unroll
       for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -749,7 +802,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       }
     if (!wave_rows) return;
     const float l_tot = pair_sum(l_run);
-    const float inv = (float)(1 << kVScaleLog2) / l_tot;
+    const float inv = 1.0f / l_tot;
     unsigned char* ob = smem + (512 + 2 * DH2 * 4 * 256) * 16 + wall * 32 * HROW;
 #pragma unroll
     for (int j = 0; j < DH2; ++j)
@@ -827,10 +880,10 @@ hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t*
 
 }  // namespace
 
-// fp16 V^T [B, Hkv, dh, Mp], then the fp32 key-score terms [B, Hq, Mp]
+// fp16 V^T [B, Hkv, dh, Mp], then the fp32 key-score rows [B, Hkv, G + 1, Mp]
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
   const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
-  return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)Hq * 4);
+  return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)(Hq + Hkv) * 4);
 }
 
 // ... then the rotated q [B, M, Hq, dh] and k [B, M, Hkv, dh] (bf16)
@@ -930,3 +983,19 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 }
 
 }  // namespace tg
+
+#ifdef TG_DIAG_COUNTERS
+// Reads (and with reset != 0 clears) the rare-path counters of the test
+// build on the current device.  Not part of the library's interface.
+extern "C" int tg_diag_attention_counters(unsigned long long* out4, int reset) {
+  if (hipMemcpyFromSymbol(out4, HIP_SYMBOL(tg::g_diag_count), 4 * sizeof(unsigned long long), 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return 3;
+  if (reset) {
+    const unsigned long long zero[4] = {0, 0, 0, 0};
+    if (hipMemcpyToSymbol(HIP_SYMBOL(tg::g_diag_count), zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
+      return 3;
+  }
+  return 0;
+}
+#endif

@@ -55,10 +55,14 @@ size_t tg_workspace_size(int op, int B, int N, int d, int h, int K) {
     return tg::gate_select_workspace(B, N);  // rows longer than 32768 only
   }
   if (op == TG_OP_GATED_ATTENTION) {
-    if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return 0;
-    // d = Hkv * d_h, h = Hq: an fp16 V^T copy (B * Hkv * d_h * round_up(M, 64)
-    // values) and the fp32 key-score term of every query head (B * Hq * round_up(M, 64))
-    return tg::gated_attention_workspace(B, N, h, 1, d);
+    if (B <= 0 || N <= 0 || d <= 0 || h <= 0 || K < 0) return 0;
+    // d = Hkv * d_h, h = Hq, K = d_h: an fp16 V^T copy (B * Hkv * d_h *
+    // round_up(M, 64) values), the fp32 key-score term of every query head and
+    // the V^T tile scales of every KV head (B * (Hq + Hkv) * round_up(M, 64)).
+    // K = 0 sizes for the largest Hkv (= Hq).
+    if (K > 0) return d % K == 0 ? tg::gated_attention_workspace(B, N, h, d / K, K) : 0;
+    const size_t Mp = (size_t)(N + 63) / 64 * 64;
+    return (size_t)B * Mp * ((size_t)d * 2 + (size_t)h * 8);
   }
   if (op == TG_OP_GATED_ATTENTION_ROPE) {
     // as TG_OP_GATED_ATTENTION with K = d_h, plus the rotated q and k (bf16)
@@ -439,6 +443,9 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B
   if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
   for (int b = 0; b < B; ++b)
     if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
+  if (Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
+  if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
+  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
   const size_t slots = tg::gated_attention_varlen_slots(B, cu_seqlens);
   if (slots == 0) return TG_OK;
   if (slots > 0x7FFFFFFF) return fail(TG_EINVAL, "%s: %zu padded rows exceed the 32-bit index range", name, slots);

@@ -56,12 +56,18 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_GATE_SELECT, 1, 32768, 2048, 0, 0) == 0
     assert lib.tg_workspace_size(tgb.TG_OP_GATE_SELECT, 2, 131072, 2048, 0, 0) == 2 * (2048 + 2048 + 1024 + 4) * 4
     # attention: fp16 V^T copy and fp32 per-head key-score terms, kept length padded to 64 keys
-    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == 3392 * (8 * 128 * 2 + 16 * 4)
-    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 0) == 2 * 64 * (2 * 64 * 2 + 4 * 4)
-    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 0, 0) == 0   # Hq is required
+    # V^T (fp16) plus one key-term row per query head and one V^T scale row per KV head
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 128) == \
+        3392 * (8 * 128 * 2 + (16 + 8) * 4)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 2, 64, 2 * 64, 4, 64) == 2 * 64 * (2 * 64 * 2 + 6 * 4)
+    # K = 0: sized for the largest possible Hkv (= Hq)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 3341, 8 * 128, 16, 0) == \
+        3392 * (8 * 128 * 2 + 32 * 4)
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 0, 64) == 0   # Hq is required
+    assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 4, 48) == 0   # d_h must divide d
     # the rotary variant adds the rotated q [B, M, Hq, d_h] and k [B, M, Hkv, d_h] (bf16); K = d_h
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 3341, 8 * 128, 16, 128) == \
-        3392 * (8 * 128 * 2 + 16 * 4) + 3341 * (16 + 8) * 128 * 2
+        3392 * (8 * 128 * 2 + (16 + 8) * 4) + 3341 * (16 + 8) * 128 * 2
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 64, 2 * 64, 4, 0) == 0   # d_h is required
 
 
@@ -296,6 +302,21 @@ def test_attention_varlen_validation(lib):
     assert call([0, 0, 0]) == tgb.TG_OK  # nothing to do: no GPU call
 
 
+def test_attention_varlen_checks_heads_before_sizing(lib):
+    """Bad head counts are refused as such, before the workspace is sized."""
+    cu = (ctypes.c_int32 * 2)(0, 100)
+
+    def call(Hq, Hkv, dh=128):
+        return lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 1, cu, Hq, Hkv, dh, FAKE, FAKE, FAKE, FAKE, 0.088,
+                                             FAKE, NULL, FAKE, 1 << 30, None)
+
+    assert call(-16, 8) == tgb.TG_EINVAL and "bad sizes" in _err(lib)
+    assert call(16, -8) == tgb.TG_EINVAL and "bad sizes" in _err(lib)
+    assert call(16, 0) == tgb.TG_EINVAL and "bad sizes" in _err(lib)
+    assert call(12, 8) == tgb.TG_EINVAL and "multiple" in _err(lib)
+    assert call(16, 8, dh=96) == tgb.TG_EUNSUPPORTED and "d_h" in _err(lib)
+
+
 def test_attention_varlen_validates_every_sequence_first(lib):
     """A bad second sequence is refused before the first is launched (no GPU
     call is made here: a launch would fail on this CPU-only machine)."""
@@ -312,7 +333,7 @@ def test_attention_varlen_workspace_covers_every_sequence(lib):
     """The packed call needs every sequence's padded rows side by side:
     2 x 128 rows x (8 x 128 x 2 + 16 x 4) bytes for two sequences of 100."""
     cu = (ctypes.c_int32 * 3)(0, 100, 200)
-    need = 256 * (8 * 128 * 2 + 16 * 4)
+    need = 256 * (8 * 128 * 2 + (16 + 8) * 4)
     assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 128, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE,
                                          NULL, FAKE, need - 1, None) == tgb.TG_EINVAL
     assert b"workspace" in lib.tg_last_error()
