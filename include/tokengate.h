@@ -97,6 +97,28 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r,
                   float* score_raw, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tg_gate_score_noalloc -- tg_gate_score for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same computation and the same result bits,
+ * with no workspace argument.  The folded W1 goes to a fixed scratch array
+ * of 4 MiB inside the library instead (one per device, held until the
+ * process ends), so h * d * 2 must not exceed 4194304 bytes (h = 256 allows
+ * d up to 8192); larger sizes return TG_EINVAL.  Nothing is allocated, on
+ * the device or by any library routine.  The first call on a device looks
+ * up that device's scratch address (no allocation, no enqueue).  Every call
+ * on one device shares that device's scratch: calls on one stream are
+ * ordered, but calls that may overlap on one device (other streams, other
+ * threads) race on it and must be serialised by the caller.  The fp32 path
+ * needs no scratch.  Arguments, supported shapes and errors are otherwise
+ * those of tg_gate_score.
+ */
+int tg_gate_score_noalloc(const void* resid, int dt, int B, int N, int d, int r,
+                          const void* norm_w, float eps_row,
+                          const void* W1, const float* b1, int h,
+                          const void* w2, const float* b2,
+                          float* score_raw, void* stream);
+
+/*
  * tg_seq_rmsnorm -- RMSNorm of the scalar scores along the sequence (paper
  * Section 4, "Scoring Network", second half of Eq. 3; scores of
  * non-prunable tokens are fixed to zero).

@@ -27,7 +27,8 @@ TG_F32, TG_BF16 = 0, 1
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
-            "tg_gated_attention_backward_varlen", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_workspace_size", "tg_last_error",
+            "tg_version")
 
 _lib = None
 
@@ -62,6 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                                      ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
+    lib.tg_gate_score_noalloc.argtypes = [vp, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
     lib.tg_gated_attention_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f,
@@ -80,7 +82,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
-                 "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen"):
+                 "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -158,6 +160,29 @@ def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, 
         _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, *rest))
     else:
         _check(lib.tg_gate_score_span(_ptr(resid), _dt(resid), B, N, d, r, span_end, *rest))
+    return score_raw
+
+
+def tg_gate_score_noalloc(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None,
+                          stream=None):
+    """:func:`tg_gate_score` without a workspace: the library's fixed 4 MiB
+    scratch holds the folded W1 (h * d * 2 bytes at most 4 MiB).  Calls that may
+    overlap on one device race on that scratch.  ``score_raw`` must be given
+    by callers that may not allocate."""
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    h = W1.shape[0]
+    _need(norm_w, "norm_w", resid.dtype, (d,))
+    _need(W1, "W1", resid.dtype, (h, d))
+    _need(b1, "b1", torch.float32, (h,))
+    _need(w2, "w2", resid.dtype, (h,))
+    _need(b2, "b2", torch.float32, (1,))
+    if score_raw is None:
+        score_raw = torch.empty((B, N), dtype=torch.float32, device=resid.device)
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    _check(lib.tg_gate_score_noalloc(_ptr(resid), _dt(resid), B, N, d, r, _ptr(norm_w), eps_row, _ptr(W1), _ptr(b1),
+                                     h, _ptr(w2), _ptr(b2), _ptr(score_raw), _stream(stream)))
     return score_raw
 
 

@@ -32,6 +32,8 @@
 //    order.
 // fp32 path (small parity workloads): plain fp32 FMA with the normalised rows
 // staged in LDS.
+#include <mutex>
+
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -375,6 +377,32 @@ hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int 
 }  // namespace
 
 size_t gate_score_workspace(int h, int d) { return (size_t)h * d * 2; }
+
+// A fixed scratch array for callers that cannot allocate (tg_gate_score_noalloc):
+// it holds the folded W1 in place of a caller's workspace.  Each device that
+// runs the library has its own copy, kept until the process ends.  In host
+// code the name is only a stand-in for the symbol: kernels and copies use the
+// device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kGateScoreScratchBytes];
+
+hipError_t gate_score_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
                                   const int32_t* se, const uint16_t* norm_w,

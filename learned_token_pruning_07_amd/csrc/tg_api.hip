@@ -88,7 +88,7 @@ static int gate_score_common(const char* name, const void* resid, int dt, int B,
                              const int32_t* sb, const int32_t* se,
                              const void* norm_w, float eps_row, const void* W1, const float* b1, int h,
                              const void* w2, const float* b2, float* score_raw, void* ws, size_t ws_bytes,
-                             void* stream) {
+                             void* stream, bool static_scratch = false) {
   if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
   if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: B, N, d, h must be > 0", name);
   if (r < 0 || r > p1 || p1 > N)
@@ -106,11 +106,21 @@ static int gate_score_common(const char* name, const void* resid, int dt, int B,
     if (h != 64 && h != 128 && h != 256)
       return fail(TG_EUNSUPPORTED, "%s: bf16 supports h in {64,128,256} (h=%d)", name, h);
     const size_t need = tg::gate_score_workspace(h, d);
-    if (!ws || ws_bytes < need)
-      return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
-    if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+    if (static_scratch) {
+      if (need > tg::kGateScoreScratchBytes)
+        return fail(TG_EINVAL, "%s: h * d * 2 = %zu bytes exceeds the %zu-byte static scratch", name, need,
+                    tg::kGateScoreScratchBytes);
+    } else {
+      if (!ws || ws_bytes < need)
+        return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+      if (!aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+    }
     if ((size_t)(p1 - r) * d * 2 > 0x7FFFFFFFull)
       return fail(TG_EUNSUPPORTED, "%s: a batch row above 2 GiB", name);
+    if (static_scratch) {  // every argument is valid: look up this device's scratch
+      const int rc = hip_status(tg::gate_score_scratch(&ws), name);
+      if (rc != TG_OK) return rc;
+    }
     return hip_status(tg::launch_gate_score_bf16(static_cast<const uint16_t*>(resid), B, N, d, r, p1, sb, se,
                                                  static_cast<const uint16_t*>(norm_w), eps_row,
                                                  static_cast<const uint16_t*>(W1), b1, h,
@@ -215,6 +225,13 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const v
                   void* ws, size_t ws_bytes, void* stream) {
   return gate_score_common("tg_gate_score", resid, dt, B, N, d, r, N, nullptr, nullptr, norm_w, eps_row, W1, b1, h, w2, b2, score_raw,
                            ws, ws_bytes, stream);
+}
+
+int tg_gate_score_noalloc(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
+                          const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
+                          void* stream) {
+  return gate_score_common("tg_gate_score_noalloc", resid, dt, B, N, d, r, N, nullptr, nullptr, norm_w, eps_row, W1,
+                           b1, h, w2, b2, score_raw, nullptr, 0, stream, true);
 }
 
 int tg_gate_score_span(const void* resid, int dt, int B, int N, int d, int span_begin, int span_end,

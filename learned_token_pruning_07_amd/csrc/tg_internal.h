@@ -22,6 +22,12 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
 // Workspace bytes of launch_gate_score_bf16: the norm-weight-folded W1.
 size_t gate_score_workspace(int h, int d);
 
+// The scorer's static scratch (for callers that cannot allocate): its size,
+// and its device address on the current device (looked up on the first call
+// per device, then cached).
+constexpr size_t kGateScoreScratchBytes = size_t(4) << 20;
+hipError_t gate_score_scratch(void** ptr);
+
 hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1,
                                  const int32_t* span_begin, const int32_t* span_end,
                                  const float* norm_w, float eps_row, const float* W1,

@@ -337,3 +337,15 @@ def test_attention_varlen_workspace_covers_every_sequence(lib):
     assert lib.tg_gated_attention_varlen(FAKE, FAKE, FAKE, 2, cu, 16, 8, 128, FAKE, FAKE, FAKE, FAKE, 0.088, FAKE,
                                          NULL, FAKE, need - 1, None) == tgb.TG_EINVAL
     assert b"workspace" in lib.tg_last_error()
+
+
+def test_gate_score_noalloc_refuses_oversized_weights(lib):
+    """The no-allocation scorer holds the folded W1 in a fixed 4 MiB scratch:
+    256 x 16384 bf16 (8 MiB) is refused before anything is launched."""
+    def call(d, h=256, dt=tgb.TG_BF16):
+        return lib.tg_gate_score_noalloc(FAKE, dt, 1, 8, d, 0, FAKE, 1e-6, FAKE, FAKE, h, FAKE, FAKE, FAKE, None)
+
+    assert call(16384) == tgb.TG_EINVAL and "static scratch" in _err(lib)
+    assert call(8192 + 64) == tgb.TG_EINVAL and "static scratch" in _err(lib)
+    assert call(100) == tgb.TG_EUNSUPPORTED  # the plain scorer's shape rules still apply
+    assert call(2048, h=96) == tgb.TG_EUNSUPPORTED
