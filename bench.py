@@ -13,9 +13,11 @@ One step = one pass of the whole path over one input:
 (--separate-gate runs tg_seq_rmsnorm, tg_topk_select and tg_compact instead
 of tg_gate_select; the results are the same bit for bit)
 with every input already resident in HBM.  Calls are launched directly on
-one stream with no host synchronisation; --graph captures each phase of a
-step (each gate call, the run of attention calls) once as a HIP graph and
-replays it instead.  The residual is rotated over
+one stream with no host synchronisation; --graph also captures each whole
+step once as one HIP graph from the padded entry points (the budget read
+from device memory, launches sized by the kept length padded to a multiple
+of 256, as one graph per padded length serves every budget of its bucket)
+and times its replays.  The residual is rotated over
 several copies (> the 256 MiB Infinity Cache) so the HBM-bound kernels read
 HBM.  The per-layer Q/K/V are the upper layers' projections of the compacted
 stream (seeded random weights); they are produced before the timed region by
@@ -219,6 +221,64 @@ def time_kv_prune(torch, tg, kept_idx, N, M, heads, n_layers, reps=20):
             "shape": {"N": N, "M": M, "Hkv": Hkv, "d_h": dh}}
 
 
+def time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, heads, steps, warmup):
+    """Each whole step (scorer, selection with the budget read from device
+    memory, every attention layer) captured once as one HIP graph per residual
+    copy, with the padded entry points: the launches are sized by the kept
+    length padded to a multiple of 256, so the same graph would serve any
+    budget of that bucket.  Timed by HIP events around `steps` replays."""
+    dev = resids[0].device
+    N, r, K, d, M = c.N, c.r, c.K, c.d, c.M
+    M_pad = min(N, -(-M // 256) * 256)
+    Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+    K_dev = torch.full((1,), K, dtype=torch.int32, device=dev)
+    score = torch.empty((1, N), dtype=torch.float32, device=dev)
+    keep = torch.empty((1, N), dtype=torch.uint8, device=dev)
+    kept_idx = torch.zeros((1, M_pad), dtype=torch.int32, device=dev)
+    resid_S = torch.zeros((1, M_pad, d), dtype=torch.bfloat16, device=dev)
+    b_S = torch.zeros((1, M_pad), dtype=torch.float32, device=dev)
+    kept_count = torch.empty((1,), dtype=torch.int32, device=dev)
+    out = torch.empty((1, M_pad, Hq, dh), dtype=torch.bfloat16, device=dev)
+    ws = tg.attention_workspace(1, M_pad, Hq, Hkv, dh, dev)
+
+    def gate(x):
+        tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score, ws=gate_ws)
+        tg.tg_gate_select_padded(score, x, r, K_dev, M_pad, c.eps_seq, score=score, keep=keep, kept_idx=kept_idx,
+                                 resid_out=resid_S, score_out=b_S, kept_count=kept_count)
+
+    gate(resids[0])
+    torch.cuda.synchronize()
+    qkv = [p.qkv(resid_S) for p in layers]  # glue on the padded stream, outside the graph
+
+    def run(x):
+        gate(x)
+        for l, p in enumerate(layers):
+            q, k, v = qkv[l]
+            tg.tg_gated_attention_padded(q, k, v, kept_count, b_S, kept_idx, p.gain, p.temp, out=out, ws=ws)
+
+    graphs = []
+    for x in resids:
+        run(x)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(x)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": e0.elapsed_time(e1) / steps, "M_pad": M_pad, "kept": int(kept_count.item()),
+            "entry_points": ["tg_gate_score", "tg_gate_select_padded", "tg_gated_attention_padded"],
+            "graphs": len(graphs)}
+
+
 def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -265,8 +325,9 @@ def main():
     ap.add_argument("--separate-gate", action="store_true",
                     help="run sequence norm, top-K and compaction as three calls instead of tg_gate_select")
     ap.add_argument("--graph", action="store_true",
-                    help="capture each phase of a step as a HIP graph once and replay it (slower on this ROCm: "
-                         "a replay costs several microseconds more than direct launches)")
+                    help="after the direct-launch timing, capture each whole step as one HIP graph (padded entry "
+                         "points: budget in device memory, kept length padded to a multiple of 256) and time "
+                         "its replays; value and ms_per_step then come from the replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv-prune", action="store_true",
                     help="skip the separate timing of tg_kv_cache_prune (layers 0..L of the stage)")
@@ -396,29 +457,8 @@ def main():
             ph.append(("gated_attention", attention_layers, len(layers)))
         return ph
 
-    graphs = {}
-    if args.graph:
-        # each phase of a step is captured once as a HIP graph (per residual
-        # copy for the gate phases) and replayed; events between the replays
-        # time the phases.  The calls allocate nothing, so capture is legal.
-        for i in range(ncopy):  # eager warm-up of every call shape first
-            for _, fn, _ in step_phases(i):
-                fn()
-        torch.cuda.synchronize()
-        for i in range(ncopy):
-            for name, fn, _ in step_phases(i):
-                key = (i if name != "gated_attention" else 0, name)
-                if key not in graphs:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g):
-                        fn()
-                    graphs[key] = g
-        torch.cuda.synchronize()
-
     def step(i, ev=None):
         for name, fn, calls in step_phases(i):
-            if graphs:
-                fn = graphs[(i % ncopy if name != "gated_attention" else 0, name)].replay
             if ev:
                 ev.phase(name, fn, calls=calls)
             else:
@@ -439,8 +479,15 @@ def main():
     t_end = ev.last
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies, "
-        f"{'HIP graph replays' if args.graph else 'direct launches'})")
+    log(f"{ms_per_step:.4f} ms/step over {args.steps} steps ({ncopy} residual copies, direct launches)")
+    direct_ms = ms_per_step
+    graph_info = None
+    if args.graph and not args.separate_gate and N <= 32768:
+        graph_info = time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, heads, args.steps,
+                                args.warmup)
+        ms_per_step = graph_info["ms_per_step"]
+        log(f"{ms_per_step:.4f} ms/step over {args.steps} graph replays (padded kept length "
+            f"{graph_info['M_pad']})")
 
     # ---------------- figures ----------------
     e = 2
@@ -498,7 +545,7 @@ def main():
                    "residual_copies": ncopy},
         "roofline": roofline,
         "kernels": kernels,
-        "launch": "hip_graph" if args.graph else "direct",
+        "launch": "hip_graph" if graph_info else "direct",
         "gate_op": {"calls": ["tg_gate_score"] + ["tg_" + n for n in sel_phases],
                     "avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
                     "achieved_GBs": round(gate_bytes / (gate_us * 1e-6) / 1e9, 1),
@@ -507,6 +554,9 @@ def main():
         "glue_qkv_ms_per_step": round(glue_ms, 4),
         "tokens_per_s_with_glue": round(N / ((ms_per_step + glue_ms) * 1e-3), 1),
     }
+    if graph_info:
+        out["direct_ms_per_step"] = round(direct_ms, 5)
+        out["graph"] = {k: v for k, v in graph_info.items() if k != "ms_per_step"}
 
     if layers and not args.no_varlen:
         out["varlen_attention"] = time_varlen(torch, tg, layers[0], heads, M)

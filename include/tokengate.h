@@ -327,6 +327,48 @@ int tg_gated_attention(const void* q, const void* k, const void* v,
                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The pruned forward replayed as one captured graph per padded length (paper
+ * Section 5, "Implementation and timing": the forward after pruning is
+ * captured as one CUDA graph per padded length).  The two entry points below
+ * read the budget and the kept length from device memory, and size their
+ * launches by a padded length M_pad fixed at capture time, so one captured
+ * graph serves every budget whose kept set fits M_pad: the caller writes the
+ * budget K into device memory before each replay.
+ *
+ * tg_gate_select_padded -- tg_gate_select with the budget of row b read from
+ * K[b] (device int32; negative values count as 0) and the kept set written
+ * into M_pad rows per batch row.  The budget is cut to M_pad - r, so row b
+ * keeps M_b = r + min(K[b], N - r, M_pad - r) <= M_pad tokens, written to
+ * kept_count[b] (device int32), and its outputs fill the first M_b rows of
+ * kept_idx [B, M_pad], resid_out [B, M_pad, d] and score_out [B, M_pad];
+ * rows M_b .. M_pad - 1 are left untouched.  score and keep are as in
+ * tg_gate_select.  For the same K every output equals tg_gate_select's bit
+ * for bit.  Requires r <= M_pad <= N <= 32768; no workspace.
+ */
+int tg_gate_select_padded(const float* score_raw, int B, int N, int r,
+                          float eps_seq, const int32_t* K, int M_pad,
+                          const void* resid, int dt, int d, float* score,
+                          uint8_t* keep, int32_t* kept_idx, void* resid_out,
+                          float* score_out, int32_t* kept_count, void* stream);
+
+/*
+ * tg_gated_attention_padded -- tg_gated_attention where batch row b uses the
+ * first M_b = kept_count[b] (device int32, clamped to [0, M_pad]) rows of
+ * tensors laid out with the padded length M_pad: q [B, M_pad, Hq, d_h],
+ * k, v [B, M_pad, Hkv, d_h], key_score and pos [B, M_pad], out [B, M_pad,
+ * Hq, d_h], lse [B, Hq, M_pad] (or NULL).  Rows M_b .. M_pad - 1 are neither
+ * read nor written.  Each row's results equal tg_gated_attention's for M =
+ * M_b bit for bit.  The workspace is tg_gated_attention's for M = M_pad.
+ */
+int tg_gated_attention_padded(const void* q, const void* k, const void* v,
+                              int B, int M_pad, const int32_t* kept_count,
+                              int Hq, int Hkv, int d_h, const float* key_score,
+                              const int32_t* pos, const float* gain,
+                              const float* temp, float sm_scale, void* out,
+                              float* lse, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
  * tg_gated_attention_varlen -- tg_gated_attention over the packed kept rows of
  * a varying-length batch (the output layout of tg_gate_select_varlen).
  * Sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [T, Hq, d_h],

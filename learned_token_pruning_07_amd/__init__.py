@@ -27,8 +27,8 @@ TG_F32, TG_BF16 = 0, 1
 EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "tg_gate_select", "tg_gated_attention",
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
-            "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_workspace_size", "tg_last_error",
-            "tg_version")
+            "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_gate_select_padded",
+            "tg_gated_attention_padded", "tg_workspace_size", "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_score_noalloc.argtypes = [vp, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp]
+    lib.tg_gate_select_padded.argtypes = [vp, i, i, i, f, vp, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.tg_gated_attention_padded.argtypes = [vp, vp, vp, i, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
     lib.tg_gated_attention_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f,
@@ -82,7 +84,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gate_select", "tg_gated_attention_rope", "tg_gated_attention_backward",
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
-                 "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc"):
+                 "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc",
+                 "tg_gate_select_padded", "tg_gated_attention_padded"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -328,6 +331,75 @@ def tg_gate_select(score_raw, resid, r: int, K: int, eps_seq: float = 1e-6, scor
     else:
         _check(lib.tg_gate_select_span(_ptr(score_raw), B, N, r, span_end, *rest))
     return kept_idx, resid_out, score_out, keep, score
+
+
+def tg_gate_select_padded(score_raw, resid, r: int, K, M_pad: int, eps_seq: float = 1e-6, score=None, keep=None,
+                          kept_idx=None, resid_out=None, score_out=None, kept_count=None, stream=None):
+    """:func:`tg_gate_select` with the budgets ``K`` (int32 GPU tensor ``[B]``)
+    read on the device and the kept sets written into ``M_pad`` rows per batch
+    row.  Returns ``(kept_idx [B, M_pad], resid_out [B, M_pad, d], score_out
+    [B, M_pad], kept_count [B] int32, keep, score)``; row b's first
+    ``kept_count[b]`` rows are its kept set (the rest untouched).  No host
+    value depends on K, so the call can be captured once and replayed with
+    new budgets."""
+    lib = load_library()
+    _need(resid, "resid")
+    B, N, d = resid.shape
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    _need(K, "K", torch.int32, (B,))
+    dev = resid.device
+    if score is None:
+        score = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if keep is None:
+        keep = torch.empty((B, N), dtype=torch.uint8, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, M_pad), dtype=torch.int32, device=dev)
+    if resid_out is None:
+        resid_out = torch.empty((B, M_pad, d), dtype=resid.dtype, device=dev)
+    if score_out is None:
+        score_out = torch.empty((B, M_pad), dtype=torch.float32, device=dev)
+    if kept_count is None:
+        kept_count = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(score, "score", torch.float32, (B, N))
+    _need(keep, "keep", torch.uint8, (B, N))
+    _need(kept_idx, "kept_idx", torch.int32, (B, M_pad))
+    _need(resid_out, "resid_out", resid.dtype, (B, M_pad, d))
+    _need(score_out, "score_out", torch.float32, (B, M_pad))
+    _need(kept_count, "kept_count", torch.int32, (B,))
+    _check(lib.tg_gate_select_padded(_ptr(score_raw), B, N, r, eps_seq, _ptr(K), M_pad, _ptr(resid), _dt(resid), d,
+                                     _ptr(score), _ptr(keep), _ptr(kept_idx), _ptr(resid_out), _ptr(score_out),
+                                     _ptr(kept_count), _stream(stream)))
+    return kept_idx, resid_out, score_out, kept_count, keep, score
+
+
+def tg_gated_attention_padded(q, k, v, kept_count, key_score, pos, gain, temp, sm_scale: float | None = None,
+                              out=None, lse=None, ws=None, stream=None):
+    """:func:`tg_gated_attention` on tensors padded to ``M_pad`` rows (q ``[B,
+    M_pad, Hq, dh]`` ...), where batch row b uses its first ``kept_count[b]``
+    rows (int32 GPU tensor ``[B]``, read on the device).  Returns ``out`` (and
+    ``lse [B, Hq, M_pad]`` when given)."""
+    lib = load_library()
+    _need(q, "q", torch.bfloat16)
+    B, M_pad, Hq, dh = q.shape
+    Hkv = k.shape[2]
+    _need(k, "k", torch.bfloat16, (B, M_pad, Hkv, dh))
+    _need(v, "v", torch.bfloat16, (B, M_pad, Hkv, dh))
+    _need(kept_count, "kept_count", torch.int32, (B,))
+    _need(key_score, "key_score", torch.float32, (B, M_pad))
+    _need(pos, "pos", torch.int32, (B, M_pad))
+    if sm_scale is None:
+        sm_scale = dh ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (B, M_pad, Hq, dh))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, M_pad))
+    if ws is None:
+        ws = attention_workspace(B, M_pad, Hq, Hkv, dh, q.device)
+    _check(lib.tg_gated_attention_padded(_ptr(q), _ptr(k), _ptr(v), B, M_pad, _ptr(kept_count), Hq, Hkv, dh,
+                                         _ptr(key_score), _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale),
+                                         _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return (out, lse) if lse is not None else out
 
 
 def varlen_kept_counts(seq_len, span_begin, span_end, K):

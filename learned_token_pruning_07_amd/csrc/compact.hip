@@ -141,13 +141,15 @@ __global__ __launch_bounds__(kGatherThreads) void compact_gather_kernel(const ui
 
 // Packed rows of varying count: batch row b owns output rows
 // [cu_kept[b], cu_kept[b + 1]); chunk c of row b covers its kept row c / cpr.
+// With count set instead (pad rows per batch row), batch row b owns output
+// rows [b pad, b pad + count[b]).
 __global__ __launch_bounds__(kGatherThreads) void compact_gather_varlen_kernel(
     const uint8_t* __restrict__ resid, size_t row_bytes, int N, const int32_t* __restrict__ cu_kept,
-    const int32_t* __restrict__ kept_idx, uint8_t* __restrict__ out) {
+    const int32_t* __restrict__ count, int pad, const int32_t* __restrict__ kept_idx, uint8_t* __restrict__ out) {
   const int b = blockIdx.y;
   const size_t cpr = row_bytes / 16;
-  const int o0 = cu_kept[b];
-  const int Mb = cu_kept[b + 1] - o0;
+  const int o0 = count != nullptr ? b * pad : cu_kept[b];
+  const int Mb = count != nullptr ? min(max(count[b], 0), pad) : cu_kept[b + 1] - o0;
   const size_t total = Mb > 0 ? (size_t)Mb * cpr : 0;
   const int32_t* ki = kept_idx + o0;
   const uint8_t* src = resid + (size_t)b * N * row_bytes;
@@ -195,7 +197,19 @@ hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int
   const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
   const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
   hipLaunchKernelGGL(compact_gather_varlen_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
-                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, cu_kept, kept_idx,
+                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, cu_kept, nullptr, 0, kept_idx,
+                     reinterpret_cast<uint8_t*>(resid_out));
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_gather_padded(const void* resid, size_t row_bytes, int B, int N, const int32_t* count,
+                                        int pad, const int32_t* kept_idx, void* resid_out, hipStream_t s) {
+  if (pad <= 0) return hipSuccess;
+  const size_t total = (size_t)pad * (row_bytes / 16);
+  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
+  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  hipLaunchKernelGGL(compact_gather_varlen_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
+                     reinterpret_cast<const uint8_t*>(resid), row_bytes, N, nullptr, count, pad, kept_idx,
                      reinterpret_cast<uint8_t*>(resid_out));
   return hipGetLastError();
 }

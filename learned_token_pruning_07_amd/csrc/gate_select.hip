@@ -52,6 +52,9 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
     p1 = min(max(vr.span_end[b], 0), Nb);
     r = min(max(vr.span_begin[b], 0), p1);
     K = max(vr.K[b], 0);
+  } else if (vr.K != nullptr) {
+    // budget from the device, cut so that the kept set fits the pad rows
+    K = min(max(vr.K[b], 0), vr.pad - (N - (p1 - r)));
   }
   const int P = p1 - r;
   const int Kp = K < P ? K : P;
@@ -61,6 +64,9 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
   if (vr.len != nullptr) {
     out0 = (size_t)max(vr.cu_kept[b], 0);
     lim = min(M, vr.cu_kept[b + 1] - vr.cu_kept[b]);
+  } else if (vr.K != nullptr) {
+    out0 = (size_t)b * vr.pad;
+    if (tid == 0) vr.kept_count[b] = M;
   }
   const float* x = score_raw + (size_t)b * N;
   float* y = score + (size_t)b * N;
@@ -227,6 +233,19 @@ hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, int p
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_compact_gather(resid, row_bytes, B, N, M, kept_idx, resid_out, s);
+}
+
+hipError_t launch_gate_select_padded(const float* score_raw, int B, int N, int r, float eps, const int32_t* K,
+                                     int pad, const void* resid, size_t row_bytes, float* score, uint8_t* keep,
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, int32_t* kept_count,
+                                     hipStream_t s) {
+  if (N > sel::kRowChunk) return hipErrorInvalidValue;
+  VarlenRows vr{nullptr, nullptr, nullptr, K, nullptr, pad, kept_count};
+  hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, r, N, eps, 0, vr, score, keep,
+                     kept_idx, score_kept);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_compact_gather_padded(resid, row_bytes, B, N, kept_count, pad, kept_idx, resid_out, s);
 }
 
 hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,

@@ -171,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
                                                                 int Mp_all, int Hkv, int G,
                                                                 uint16_t* __restrict__ vt,
                                                                 float* __restrict__ kbias, RopeArgs ra,
-                                                                const SeqTable st) {
+                                                                const SeqTable st,
+                                                                const int32_t* __restrict__ m_dev) {
   __shared__ uint16_t sT[DH][kBK + 2];
   __shared__ double s_freq[DH / 2];
   __shared__ uint32_t s_mag[kThreads / 64];
@@ -189,7 +190,11 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     M = M_all;
     Mp = Mp_all;
     m0 = blockIdx.x * kBK;
-    T0 = (size_t)blockIdx.z * M;
+    if (m_dev != nullptr) {  // this row's kept length; its blocks past it have nothing to do
+      M = min(max(m_dev[blockIdx.z], 0), M_all);
+      if (m0 >= M) return;
+    }
+    T0 = (size_t)blockIdx.z * M_all;
     P0 = (size_t)blockIdx.z * Mp;
   }
   const int tid = threadIdx.x;
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
     const float* __restrict__ kbias, int M_all, int Mp_all, int Hq, int Hkv, const int32_t* __restrict__ pos,
     const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb_all,
-    int total_wg, const SeqTable st) {
+    int total_wg, const SeqTable st, const int32_t* __restrict__ m_dev) {
   constexpr int RG = 4 / G;        // 32-row groups per head
   constexpr int BQ = 32 * RG;      // query rows per workgroup
   constexpr int KS = DH / 16;      // k-steps of S^T = K Q^T
@@ -328,12 +333,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     M = M_all;
     Mp = Mp_all;
     const int bg = logical / nqb_all;
-    qb = nqb_all - 1 - (logical - bg * nqb_all);
     const int b = bg / Hkv;
     g = bg - b * Hkv;
-    T0 = (size_t)b * M;
+    int nqb = nqb_all;
+    if (m_dev != nullptr) {  // this row's kept length (M_all is the padded length)
+      M = min(max(m_dev[b], 0), M_all);
+      nqb = (M + BQ - 1) / BQ;
+    }
+    const int local = logical - bg * nqb_all;
+    if (local >= nqb) return;  // a query block past the kept length (the whole workgroup)
+    qb = nqb - 1 - local;
+    T0 = (size_t)b * M_all;
     P0 = (size_t)b * Mp;
   }
+  const int lse_ld = VARLEN ? M : M_all;  // lse rows: [Hq, M] per sequence, [Hq, M_all] per batch row
   const int q0 = qb * BQ;
   const int kv_end = min(M, q0 + BQ);
   const int nkb = (kv_end + kBK - 1) / kBK;
@@ -824,7 +837,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       if (rbase + r < M) store16(out + ((T0 + rbase + r) * Hq + hq) * DH + g * (DH / 2) + c * 8, w);
     }
     if (lse != nullptr && g == 0 && gq == 0 && q_ok)
-      lse[T0 * Hq + (size_t)hq * M + qi] = (m_run + __log2f(l_tot)) * kLn2;
+      lse[T0 * Hq + (size_t)hq * lse_ld + qi] = (m_run + __log2f(l_tot)) * kLn2;
   };
   if (grp == 0)
     hand_over(IntConst<0>{});
@@ -840,17 +853,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
 template <int DH, int G>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq, int Hkv,
                     const float* ks, const int32_t* pos, const float* gain, const float* temp, float sm_scale,
-                    uint16_t* out, float* lse, uint16_t* vt, float* kbias, const RopeArgs* rope, hipStream_t s) {
+                    uint16_t* out, float* lse, uint16_t* vt, float* kbias, const RopeArgs* rope, hipStream_t s,
+                    const int32_t* m_dev) {
   constexpr int BQ = 32 * (4 / G);
   const int Mp = (M + kBK - 1) / kBK * kBK;
   if (rope != nullptr) {
     hipLaunchKernelGGL((attn_prepass_kernel<DH, true, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
-                       gain, M, Mp, Hkv, G, vt, kbias, *rope, SeqTable{});
+                       gain, M, Mp, Hkv, G, vt, kbias, *rope, SeqTable{}, m_dev);
     q = rope->qr;  // the main kernel reads the rotated copies
     k = rope->kr;
   } else {
     hipLaunchKernelGGL((attn_prepass_kernel<DH, false, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
-                       gain, M, Mp, Hkv, G, vt, kbias, RopeArgs{}, SeqTable{});
+                       gain, M, Mp, Hkv, G, vt, kbias, RopeArgs{}, SeqTable{}, m_dev);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -859,7 +873,7 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   if (total <= 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gated_attn_kernel<DH, G, false>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
-                     kbias, M, Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total, SeqTable{});
+                     kbias, M, Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total, SeqTable{}, m_dev);
   return hipGetLastError();
 }
 
@@ -869,12 +883,12 @@ hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int Hkv, const float* ks, const int32_t* pos, const float* gain, const float* temp,
                            float sm_scale, uint16_t* out, float* lse, uint16_t* vt, float* kbias, hipStream_t s) {
   hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads), 0,
-                     s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st);
+                     s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = st.wg0[st.n];
   hipLaunchKernelGGL((gated_attn_kernel<DH, G, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
-                     kbias, 0, 0, Hq, Hkv, pos, temp, sm_scale, out, lse, 0, total, st);
+                     kbias, 0, 0, Hq, Hkv, pos, temp, sm_scale, out, lse, 0, total, st, nullptr);
   return hipGetLastError();
 }
 
@@ -955,7 +969,7 @@ hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, c
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq,
                                   int Hkv, int dh, const float* key_score, const int32_t* pos, const float* gain,
                                   const float* temp, float sm_scale, double rope_base, uint16_t* out, float* lse,
-                                  void* ws, hipStream_t s) {
+                                  void* ws, hipStream_t s, const int32_t* m_dev) {
   const int G = Hq / Hkv;
   const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
   uint16_t* vt = static_cast<uint16_t*>(ws);
@@ -971,7 +985,7 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 #define TG_ATTN_CASE(DHV, GV)                                                                                   \
   if (dh == DHV && G == GV)                                                                                     \
     return launch_t<DHV, GV>(q, k, v, B, M, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, kbias, \
-                             rope, s);
+                             rope, s, m_dev);
   TG_ATTN_CASE(128, 2)
   TG_ATTN_CASE(128, 1)
   TG_ATTN_CASE(128, 4)

@@ -284,14 +284,14 @@ int gated_attention_common(const char* name, const void* q, const void* k, const
                            int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
                            const float* temp, float sm_scale, double rope_base, void* out, float* lse, void* ws,
                            size_t ws_bytes, void* stream,
-                           bool launch = true) {
+                           bool launch = true, const int32_t* m_dev = nullptr) {
   if (B <= 0 || M < 0 || Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
   if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
   if (M == 0) return TG_OK;
   if (!q || !k || !v || !key_score || !pos || !gain || !temp || !out)
     return fail(TG_EINVAL, "%s: null pointer argument", name);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(key_score) ||
-      !aligned4(pos) || !aligned4(gain) || !aligned4(temp) || (lse && !aligned4(lse)))
+      !aligned4(pos) || !aligned4(gain) || !aligned4(temp) || (lse && !aligned4(lse)) || !aligned4(m_dev))
     return fail(TG_EINVAL, "%s: misaligned pointer", name);
   if (!(sm_scale > 0.0f)) return fail(TG_EINVAL, "%s: sm_scale must be > 0", name);
   if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
@@ -306,7 +306,7 @@ int gated_attention_common(const char* name, const void* q, const void* k, const
   return hip_status(tg::launch_gated_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                                static_cast<const uint16_t*>(v), B, M, Hq, Hkv, d_h, key_score,
                                                pos, gain, temp, sm_scale, rope_base, static_cast<uint16_t*>(out),
-                                               lse, ws, reinterpret_cast<hipStream_t>(stream)),
+                                               lse, ws, reinterpret_cast<hipStream_t>(stream), m_dev),
                     name);
 }
 
@@ -319,6 +319,15 @@ int tg_gated_attention(const void* q, const void* k, const void* v, int B, int M
                        float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return gated_attention_common("tg_gated_attention", q, k, v, B, M, Hq, Hkv, d_h, key_score, pos, gain, temp,
                                 sm_scale, 0.0, out, lse, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_padded(const void* q, const void* k, const void* v, int B, int M_pad,
+                              const int32_t* kept_count, int Hq, int Hkv, int d_h, const float* key_score,
+                              const int32_t* pos, const float* gain, const float* temp, float sm_scale, void* out,
+                              float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!kept_count) return fail(TG_EINVAL, "tg_gated_attention_padded: null pointer argument");
+  return gated_attention_common("tg_gated_attention_padded", q, k, v, B, M_pad, Hq, Hkv, d_h, key_score, pos, gain,
+                                temp, sm_scale, 0.0, out, lse, ws, ws_bytes, stream, true, kept_count);
 }
 
 int tg_gated_attention_rope(const void* q, const void* k, const void* v, int B, int M, int Hq, int Hkv, int d_h,
@@ -436,6 +445,30 @@ int tg_gate_select_varlen(const float* score_raw, int B, int N, const int32_t* s
                                                   tg::VarlenRows{seq_len, span_begin, span_end, K, cu_kept}, max_kept,
                                                   eps_seq, resid, row_bytes, score, keep, kept_idx, resid_out,
                                                   score_out, reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
+int tg_gate_select_padded(const float* score_raw, int B, int N, int r, float eps_seq, const int32_t* K, int M_pad,
+                          const void* resid, int dt, int d, float* score, uint8_t* keep, int32_t* kept_idx,
+                          void* resid_out, float* score_out, int32_t* kept_count, void* stream) {
+  const char* name = "tg_gate_select_padded";
+  if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
+  if (B <= 0 || B > 65535 || N <= 0 || d <= 0) return fail(TG_EINVAL, "%s: B, N, d must be > 0", name);
+  if (N > 32768) return fail(TG_EUNSUPPORTED, "%s: rows of up to 32768 tokens (N=%d)", name, N);
+  if (r < 0 || r > N) return fail(TG_EINVAL, "%s: r=%d outside [0, N=%d]", name, r, N);
+  if (M_pad < r || M_pad > N)
+    return fail(TG_EINVAL, "%s: M_pad=%d outside [r=%d, N=%d]", name, M_pad, r, N);
+  if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_seq must be >= 0", name);
+  if (!score_raw || !K || !resid || !score || !keep || !kept_idx || !resid_out || !score_out || !kept_count)
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
+  const size_t row_bytes = (size_t)d * dt_size(dt);
+  if (row_bytes % 16 != 0) return fail(TG_EUNSUPPORTED, "%s: row bytes must be a multiple of 16", name);
+  if (!aligned4(score_raw) || !aligned4(score) || !aligned16(resid) || !aligned16(resid_out) ||
+      !aligned4(kept_idx) || !aligned4(score_out) || !aligned4(K) || !aligned4(kept_count))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  return hip_status(tg::launch_gate_select_padded(score_raw, B, N, r, eps_seq, K, M_pad, resid, row_bytes, score,
+                                                  keep, kept_idx, resid_out, score_out, kept_count,
+                                                  reinterpret_cast<hipStream_t>(stream)),
                     name);
 }
 

@@ -52,23 +52,39 @@ hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int
 
 // Per-row lengths, spans, budgets and output offsets of a varying-length
 // batch (device arrays of B, B, B, B and B + 1 entries); all null for a
-// uniform batch.
+// uniform batch.  With len null but K set, the rows are uniform in length
+// and span but take their budgets from K (device), write their kept tokens
+// at rows b * pad of the outputs and their kept counts to kept_count[b].
 struct VarlenRows {
   const int32_t* len;
   const int32_t* span_begin;
   const int32_t* span_end;
   const int32_t* K;
   const int32_t* cu_kept;
+  int pad = 0;
+  int32_t* kept_count = nullptr;
 };
 
 // out[cu_kept[b] + m] = resid[b, kept_idx[cu_kept[b] + m]] for m < cu_kept[b + 1] - cu_kept[b] <= max_kept
 hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int B, int N, const int32_t* cu_kept,
                                         int max_kept, const int32_t* kept_idx, void* resid_out, hipStream_t s);
 
+// out[b * pad + m] = resid[b, kept_idx[b * pad + m]] for m < count[b] (clamped to [0, pad])
+hipError_t launch_compact_gather_padded(const void* resid, size_t row_bytes, int B, int N, const int32_t* count,
+                                        int pad, const int32_t* kept_idx, void* resid_out, hipStream_t s);
+
 // gate selection of a varying-length batch (rows of up to 32768 tokens)
 hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,
                                      const void* resid, size_t row_bytes, float* score, uint8_t* keep,
                                      int32_t* kept_idx, void* resid_out, float* score_kept, hipStream_t s);
+
+// gate selection with per-row budgets from a device array and outputs padded
+// to pad rows per batch row (rows of up to 32768 tokens); the kept counts go
+// to kept_count (device) and the gather reads them from there
+hipError_t launch_gate_select_padded(const float* score_raw, int B, int N, int r, float eps, const int32_t* K,
+                                     int pad, const void* resid, size_t row_bytes, float* score, uint8_t* keep,
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, int32_t* kept_count,
+                                     hipStream_t s);
 
 // launch_seq_rmsnorm + launch_topk_select + launch_compact in sequence, bit
 // for bit (M = N - P + min(K, P), P = p1 - r); two launches for rows of up to
@@ -80,11 +96,14 @@ hipError_t launch_gate_select(const float* score_raw, int B, int N, int r, int p
 
 // rope_base > 0: q and k are first rotated (rotary embedding at the positions
 // pos, base rope_base) into the workspace, and the attention reads the copies.
+// m_dev (may be null): per-row kept lengths [B] on the device, each clamped
+// to [0, M]; the tensors keep their [B, M, ...] layout (M the padded length)
+// and row b uses only its first m_dev[b] rows.
 hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                   int M, int Hq, int Hkv, int dh, const float* key_score,
                                   const int32_t* pos, const float* gain, const float* temp,
                                   float sm_scale, double rope_base, uint16_t* out, float* lse, void* ws,
-                                  hipStream_t s);
+                                  hipStream_t s, const int32_t* m_dev = nullptr);
 
 // Packed sequences of a varying-length batch (cu_seqlens a host array of B + 1
 // row offsets): one prepass and one attention launch per 64 non-empty

@@ -349,3 +349,27 @@ def test_gate_score_noalloc_refuses_oversized_weights(lib):
     assert call(8192 + 64) == tgb.TG_EINVAL and "static scratch" in _err(lib)
     assert call(100) == tgb.TG_EUNSUPPORTED  # the plain scorer's shape rules still apply
     assert call(2048, h=96) == tgb.TG_EUNSUPPORTED
+
+
+def test_padded_entry_points_validate(lib):
+    """The budget and the kept length come from device memory; the host sizes
+    (padded length, r, N) are checked before anything is launched."""
+    def sel(N=4096, r=32, M_pad=512, kc=FAKE, K=FAKE):
+        return lib.tg_gate_select_padded(FAKE, 1, N, r, 1e-6, K, M_pad, FAKE, tgb.TG_BF16, 512, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, kc, None)
+
+    assert sel(M_pad=31) == tgb.TG_EINVAL and "M_pad" in _err(lib)      # below r
+    assert sel(M_pad=4097) == tgb.TG_EINVAL and "M_pad" in _err(lib)    # above N
+    assert sel(N=40000, M_pad=512) == tgb.TG_EUNSUPPORTED
+    assert sel(kc=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert sel(K=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+
+    def attn(kc=FAKE, ws_bytes=1 << 30, dh=128):
+        return lib.tg_gated_attention_padded(FAKE, FAKE, FAKE, 1, 512, kc, 16, 8, dh, FAKE, FAKE, FAKE, FAKE, 0.088,
+                                             FAKE, NULL, FAKE, ws_bytes, None)
+
+    assert attn(kc=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert attn(kc=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+    assert attn(dh=96) == tgb.TG_EUNSUPPORTED
+    need = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 512, 8 * 128, 16, 128)
+    assert attn(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)

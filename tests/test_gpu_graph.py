@@ -179,3 +179,107 @@ def test_varlen_graph_replays_match_eager():
                               gain, temp)
         torch.cuda.synchronize()
     say("  3 replays bit-identical")
+
+
+def test_padded_graph_serves_every_budget_of_its_bucket():
+    """One graph per padded kept length (paper, Section 5, "Implementation and
+    timing": the pruned forward is captured once per padded length).  The gate
+    (scorer, then the selection with its budget read from device memory) and
+    two attention layers sized by M_pad are captured once; replays at several
+    budgets, each set by writing K into device memory, equal the plain entry
+    points called with that budget bit for bit, leave the rows past the kept
+    length untouched, and match the oracle.  A budget past the bucket is cut
+    to it."""
+    import oracle
+    from _gpu_util import TOL_BF16, TOL_LSE, assert_close, host_bits
+
+    M_pad = 512
+    budgets = [100, 333, 480, 700, 100]  # kept 132, 365, 512, 512 (cut), 132
+    c, w = _gate_inputs(3)
+    resid = dev_bits(c.resid)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    qkv = [(torch.randn(1, M_pad, HQ, DH, device=DEV, generator=g).bfloat16(),
+            torch.randn(1, M_pad, HKV, DH, device=DEV, generator=g).bfloat16(),
+            torch.randn(1, M_pad, HKV, DH, device=DEV, generator=g).bfloat16()) for _ in range(2)]
+    gains = [torch.rand(HQ, device=DEV, generator=g) + 0.5 for _ in range(2)]
+    temp = torch.full((HQ,), 1.2, device=DEV)
+    K_dev = torch.zeros(1, dtype=torch.int32, device=DEV)
+    score = torch.empty((1, N), dtype=torch.float32, device=DEV)
+    keep = torch.empty((1, N), dtype=torch.uint8, device=DEV)
+    kept_idx = torch.empty((1, M_pad), dtype=torch.int32, device=DEV)
+    resid_S = torch.empty((1, M_pad, D), dtype=torch.bfloat16, device=DEV)
+    b_S = torch.empty((1, M_pad), dtype=torch.float32, device=DEV)
+    kept_count = torch.empty(1, dtype=torch.int32, device=DEV)
+    outs = [torch.empty((1, M_pad, HQ, DH), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    lse = torch.empty((1, HQ, M_pad), dtype=torch.float32, device=DEV)
+    gate_ws = tg.gate_workspace(H, D, DEV)
+    attn_ws = tg.attention_workspace(1, M_pad, HQ, HKV, DH, DEV)
+
+    def run_padded():
+        tg.tg_gate_score(resid, R, w["norm_w"], w["W1"], w["b1"], w["w2"], w["b2"], c.eps_row, score_raw=score,
+                         ws=gate_ws)
+        tg.tg_gate_select_padded(score, resid, R, K_dev, M_pad, c.eps_seq, score=score, keep=keep, kept_idx=kept_idx,
+                                 resid_out=resid_S, score_out=b_S, kept_count=kept_count)
+        for l in range(2):
+            q, k, v = qkv[l]
+            tg.tg_gated_attention_padded(q, k, v, kept_count, b_S, kept_idx, gains[l], temp, out=outs[l],
+                                         lse=lse if l == 1 else None, ws=attn_ws)
+
+    def eager(Kb):
+        """The plain entry points at budget Kb (host M), on fresh buffers."""
+        Kc = min(Kb, M_pad - R)
+        raw = tg.tg_gate_score(resid, R, w["norm_w"], w["W1"], w["b1"], w["w2"], w["b2"], c.eps_row)
+        ki, rs, bs, kp, sc = tg.tg_gate_select(raw, resid, R, Kc, c.eps_seq)
+        M = ki.shape[1]
+        res = [sc, kp, ki, rs, bs]
+        for l in range(2):
+            q, k, v = (t[:, :M].contiguous() for t in qkv[l])
+            o, ls = tg.tg_gated_attention(q, k, v, bs, ki, gains[l], temp, want_lse=True)
+            res += [o, ls]
+        return M, res
+
+    K_dev.fill_(budgets[0])
+    run_padded()  # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_padded()
+    torch.cuda.synchronize()
+    say(f"graph: gate N={N} + 2 attention layers, padded kept length {M_pad}")
+    for rep, Kb in enumerate(budgets):
+        for t in (score, b_S, lse):
+            t.fill_(float("nan"))
+        for t in (keep, kept_idx, resid_S, *outs):
+            t.view(torch.uint8).fill_(0xA5)
+        K_dev.fill_(Kb)
+        graph.replay()
+        torch.cuda.synchronize()
+        M, ref = eager(Kb)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert int(kept_count.item()) == M
+        got = [score, keep, kept_idx[:, :M], resid_S[:, :M], b_S[:, :M], outs[0][:, :M], None, outs[1][:, :M],
+               lse[:, :, :M]]
+        names = ["score", "keep", "kept_idx", "resid_S", "b_S", "out0", None, "out1", "lse1"]
+        for x, y, name in zip(got, ref, names):
+            if x is None:
+                continue
+            assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), \
+                f"replay {rep} (K={Kb}): {name} differs from the plain calls"
+        # rows past the kept length are untouched
+        assert bool((kept_idx[:, M:].view(torch.uint8) == 0xA5).all())
+        assert bool((outs[0][:, M:].view(torch.uint8) == 0xA5).all())
+        assert bool(torch.isnan(lse[:, :, M:]).all())
+        # the oracle: selection and compaction on the GPU's scores, attention
+        # of layer 1 on the kept set
+        sc = score.cpu().numpy()
+        k_ref = oracle.topk_select(sc, R, min(Kb, M_pad - R))
+        np.testing.assert_array_equal(keep.cpu().numpy(), k_ref)
+        ki, rs, bs = oracle.compact(c.resid, k_ref, sc)
+        np.testing.assert_array_equal(kept_idx[:, :M].cpu().numpy(), ki)
+        np.testing.assert_array_equal(host_bits(resid_S[:, :M]), rs)
+        q, k, v = (host_bits(t[:, :M]) for t in qkv[1])
+        O, L = oracle.gated_attention(q, k, v, bs.astype(np.float32), ki, gains[1].cpu().numpy(),
+                                      temp.cpu().numpy(), DH ** -0.5)
+        assert_close(wl.bf16_bits_to_f32(host_bits(outs[1][:, :M])), O, TOL_BF16, f"K={Kb} O")
+        assert_close(lse[:, :, :M].cpu().numpy(), L, TOL_LSE, f"K={Kb} lse")
+        say(f"  replay {rep}: K={Kb} -> M={M}, bit-identical to the plain calls, oracle-checked")
