@@ -8,8 +8,10 @@ token-gated causal GQA attention calls (16q / 8kv heads, d_h 128) on the
 compacted stream.
 
 One step = one pass of the whole path over one input:
-    tg_gate_score -> tg_gate_select (sequence norm, top-K, compaction)
+    tg_gate_score_folded -> tg_gate_select (sequence norm, top-K, compaction)
     -> 24 x tg_gated_attention
+(the scorer's first-layer weights are folded with the RMSNorm weight once,
+by tg_gate_fold_weights, as a model would at load time)
 (--separate-gate runs tg_seq_rmsnorm, tg_topk_select and tg_compact instead
 of tg_gate_select; the results are the same bit for bit)
 with every input already resident in HBM.  Calls are launched directly on
@@ -221,14 +223,14 @@ def time_kv_prune(torch, tg, kept_idx, N, M, heads, n_layers, reps=20):
             "shape": {"N": N, "M": M, "Hkv": Hkv, "d_h": dh}}
 
 
-def time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, heads, steps, warmup):
+def time_graph(torch, tg, resids, c, W1f, b1, w2, b2, layers, heads, steps, warmup):
     """Each whole step (scorer, selection with the budget read from device
     memory, every attention layer) captured once as one HIP graph per residual
     copy, with the padded entry points: the launches are sized by the kept
     length padded to a multiple of 256, so the same graph would serve any
     budget of that bucket.  Timed by HIP events around `steps` replays."""
     dev = resids[0].device
-    N, r, K, d, M = c.N, c.r, c.K, c.d, c.M
+    N, r, K, d, M, h = c.N, c.r, c.K, c.d, c.M, c.h
     M_pad = min(N, -(-M // 256) * 256)
     Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
     K_dev = torch.full((1,), K, dtype=torch.int32, device=dev)
@@ -242,7 +244,7 @@ def time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, he
     ws = tg.attention_workspace(1, M_pad, Hq, Hkv, dh, dev)
 
     def gate(x):
-        tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score, ws=gate_ws)
+        tg.tg_gate_score_folded(x, r, W1f, h, b1, w2, b2, c.eps_row, score_raw=score)
         tg.tg_gate_select_padded(score, x, r, K_dev, M_pad, c.eps_seq, score=score, keep=keep, kept_idx=kept_idx,
                                  resid_out=resid_S, score_out=b_S, kept_count=kept_count)
 
@@ -275,20 +277,178 @@ def time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, he
     e1.record()
     torch.cuda.synchronize()
     return {"ms_per_step": e0.elapsed_time(e1) / steps, "M_pad": M_pad, "kept": int(kept_count.item()),
-            "entry_points": ["tg_gate_score", "tg_gate_select_padded", "tg_gated_attention_padded"],
+            "entry_points": ["tg_gate_score_folded", "tg_gate_select_padded", "tg_gated_attention_padded"],
             "graphs": len(graphs)}
 
 
+def time_phases(torch, phases, steps, warmup):
+    """Per-phase average microseconds (HIP events on the launch stream at the
+    phase boundaries) and the step time, over `steps` steps; phases is a
+    list of (name, call(step_index))."""
+    for i in range(warmup):
+        for _, fn in phases:
+            fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(phases) + 1)]
+    ev[0].record()
+    n = 0
+    for i in range(steps):
+        for _, fn in phases:
+            fn(i)
+            n += 1
+            ev[n].record()
+    torch.cuda.synchronize()
+    per = {}
+    for j, (name, _) in enumerate(phases):
+        per[name] = 1000.0 * sum(ev[i * len(phases) + j].elapsed_time(ev[i * len(phases) + j + 1])
+                                 for i in range(steps)) / steps
+    return per, ev[0].elapsed_time(ev[-1]) / steps
+
+
+def sub_records(torch, tg, wl, stage_glue, heads, steps=10, warmup=3):
+    """The metric's other lengths, measured with the same calls as the main
+    step: gate_16k (N = 16384, the gate op alone) and sweep_128k (N = 131072,
+    heavy-tailed rows, budgets 1/5/10/25 % of the prunable tokens, each gate
+    followed by one token-gated attention layer on its kept set)."""
+    import numpy as np
+    dev = "cuda:0"
+    e = 2
+    Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def gate_setup(c):
+        ncopy = max(1, -(-(512 << 20) // (c.N * c.d * 2)))
+        x0 = bits(c.resid)
+        xs = [x0] + [x0.clone() for _ in range(ncopy - 1)]
+        W1f = tg.tg_gate_fold_weights(bits(c.W1), bits(c.norm_w))
+        return xs, W1f, torch.from_numpy(c.b1).to(dev), bits(c.w2), torch.from_numpy(c.b2).to(dev)
+
+    def gate_figures(c, M, per):
+        P = c.N - c.r
+        sb = P * c.d * e + c.h * c.d * e + 4 * c.N
+        gb = 4 * P + 4 * c.N + c.N + 12 * M + 2 * M * c.d * e
+        f = {"gate_score_us": round(per["gate_score"], 3),
+             "gate_score_hbm_frac": round(sb / (per["gate_score"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+             "gate_select_us": round(per["gate_select"], 3),
+             "gate_op_hbm_frac": round((sb + gb) / ((per["gate_score"] + per["gate_select"]) * 1e-6) / 1e9
+                                       / PEAK_HBM_GBS, 4)}
+        return f
+
+    out = {}
+    # gate_16k: the gate op alone
+    c = wl.preset_gate_case("gate_16k")
+    xs, W1f, b1, w2, b2 = gate_setup(c)
+    score = torch.empty((1, c.N), dtype=torch.float32, device=dev)
+    keep = torch.empty((1, c.N), dtype=torch.uint8, device=dev)
+    ki = torch.empty((1, c.M), dtype=torch.int32, device=dev)
+    rs = torch.empty((1, c.M, c.d), dtype=torch.bfloat16, device=dev)
+    bs = torch.empty((1, c.M), dtype=torch.float32, device=dev)
+    phases = [("gate_score", lambda i: tg.tg_gate_score_folded(xs[i % len(xs)], c.r, W1f, c.h, b1, w2, b2, c.eps_row,
+                                                                 score_raw=score)),
+              ("gate_select", lambda i: tg.tg_gate_select(score, xs[i % len(xs)], c.r, c.K, c.eps_seq, score=score,
+                                                          keep=keep, kept_idx=ki, resid_out=rs, score_out=bs))]
+    per, ms = time_phases(torch, phases, steps, warmup)
+    out["gate_16k"] = {"N": c.N, "K": c.K, "M": c.M, "ms_per_step": round(ms, 5),
+                       "tokens_per_s": round(c.N / (ms * 1e-3), 1), **gate_figures(c, c.M, per)}
+    del xs, c
+    # sweep_128k: one residual, four budgets
+    c = wl.preset_gate_case("sweep_128k", K=1)
+    xs, W1f, b1, w2, b2 = gate_setup(c)
+    score = torch.empty((1, c.N), dtype=torch.float32, device=dev)
+    sel_ws = tg.gate_select_workspace(1, c.N, dev)
+    rows = []
+    for n, K in enumerate(wl.sweep_budgets(c.N, c.r)):
+        M = tg.kept_count(c.N, c.r, K)
+        ki = torch.empty((1, M), dtype=torch.int32, device=dev)
+        rs = torch.empty((1, M, c.d), dtype=torch.bfloat16, device=dev)
+        bs = torch.empty((1, M), dtype=torch.float32, device=dev)
+        keep = torch.empty((1, c.N), dtype=torch.uint8, device=dev)
+        tg.tg_gate_score_folded(xs[0], c.r, W1f, c.h, b1, w2, b2, c.eps_row, score_raw=score)
+        tg.tg_gate_select(score, xs[0], c.r, K, c.eps_seq, score=score, keep=keep, kept_idx=ki, resid_out=rs,
+                          score_out=bs, ws=sel_ws)
+        lay = stage_glue.stage_layers(1, c.d, seed0=500 + n, **heads)[0]
+        q, k, v = lay.qkv(rs)
+        ao = torch.empty((1, M, Hq, dh), dtype=torch.bfloat16, device=dev)
+        aws = tg.attention_workspace(1, M, Hq, Hkv, dh, dev)
+        phases = [("gate_score", lambda i: tg.tg_gate_score_folded(xs[0], c.r, W1f, c.h, b1, w2, b2, c.eps_row,
+                                                                     score_raw=score)),
+                  ("gate_select", lambda i: tg.tg_gate_select(score, xs[0], c.r, K, c.eps_seq, score=score,
+                                                              keep=keep, kept_idx=ki, resid_out=rs, score_out=bs,
+                                                              ws=sel_ws)),
+                  ("attention", lambda i: tg.tg_gated_attention(q, k, v, bs, ki, lay.gain, lay.temp, out=ao, ws=aws))]
+        per, ms = time_phases(torch, phases, steps, warmup)
+        flops = 2 * dh * Hq * M * (M + 1)
+        tf = flops / (per["attention"] * 1e-6) / 1e12
+        rows.append({"frac": wl.SWEEP_FRACTIONS[n], "K": K, "M": M, "ms_per_step": round(ms, 5),
+                     "tokens_per_s": round(c.N / (ms * 1e-3), 1), **gate_figures(c, M, per),
+                     "attention_us": round(per["attention"], 3), "attention_TFLOPs": round(tf, 2),
+                     "attention_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del q, k, v, ao, aws, ki, rs, bs
+    out["sweep_128k"] = {"N": c.N, "r": c.r, "budgets": rows}
+    return out
+
+
+def ceilings(torch, reps=5):
+    """Measured ceilings of this device, for context beside the spec peaks: a
+    plain device-to-device copy of 1 GiB (bytes read + written per second)
+    and a large bf16 GEMM through torch (hipBLASLt), 8192^3."""
+    dev = "cuda:0"
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).bfloat16()
+    b = torch.randn(8192, 8192, device=dev).bfloat16()
+    res = {}
+    for name, fn, work in (("copy", lambda: dst.copy_(src), 2 * (1 << 30)),
+                           ("gemm_bf16", lambda: torch.mm(a, b), 2 * 8192 ** 3)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = work * reps / (e0.elapsed_time(e1) * 1e-3)
+    del src, dst, a, b
+    return {"copy_GBs": round(res["copy"] / 1e9, 1), "copy_frac_of_spec": round(res["copy"] / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_bf16_TFLOPs": round(res["gemm_bf16"] / 1e12, 1),
+            "gemm_bf16_frac_of_spec": round(res["gemm_bf16"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gemm_shape": [8192, 8192, 8192]}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=1024):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+    """The oracle, as it stands, on a bounded sample of the same workload,
+    once with its BLAS thread pool at its default size and once on one
+    thread (elementwise numpy steps are single-threaded either way)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    full = _cpu_sample(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows)
+    with threadpool_limits(limits=1):
+        one = _cpu_sample(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows)
+    return {"value": full["value"], "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": full["sample"], "seconds_per_step": full["seconds_per_step"], "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
+            "single_thread": {"value": one["value"], "seconds_per_step": one["seconds_per_step"], "cores": 1}}
+
+
+def _cpu_sample(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows):
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
     t0 = time.perf_counter()
     raw = oracle.gate_score(c.resid, c.r, c.norm_w, c.W1, c.b1, c.w2, c.b2, c.eps_row)
     b = oracle.seq_rmsnorm(raw, c.r, c.eps_seq)
@@ -305,7 +465,7 @@ def cpu_baseline(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows=10
     t_layer = t_rows * M / R
     per_step = t_gate + n_layers * t_layer
     return {
-        "value": c.N / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "value": c.N / per_step,
         "sample": (f"gate (score, seq-norm, top-K, compaction) on the full N={c.N} input: {t_gate:.2f} s; "
                    f"one attention layer on {R} of {M} query rows (all {q.shape[2]} heads): {t_rows:.2f} s, "
                    f"extrapolated linearly to {M} rows x {n_layers} layers"),
@@ -329,6 +489,9 @@ def main():
                          "points: budget in device memory, kept length padded to a multiple of 256) and time "
                          "its replays; value and ms_per_step then come from the replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="skip the gate_16k and sweep_128k (1/5/10/25 %%) records of the metric's other lengths")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured copy and bf16 GEMM ceilings")
     ap.add_argument("--no-kv-prune", action="store_true",
                     help="skip the separate timing of tg_kv_cache_prune (layers 0..L of the stage)")
     ap.add_argument("--no-varlen", action="store_true",
@@ -401,7 +564,7 @@ def main():
     kept_idx = torch.empty((1, M), dtype=torch.int32, device=dev)
     resid_S = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
     b_S = torch.empty((1, M), dtype=torch.float32, device=dev)
-    gate_ws = tg.gate_workspace(h, d, dev)
+    W1f = tg.tg_gate_fold_weights(W1, norm_w)      # once per weight set
     seq_ws = tg.seq_rmsnorm_workspace(1, N, dev)   # None up to N = 32768
     topk_ws = tg.topk_workspace(1, N, dev)
     sel_ws = tg.gate_select_workspace(1, N, dev)   # None up to N = 32768
@@ -409,8 +572,8 @@ def main():
 
     def gate_calls(x):
         """The gate's library calls on residual x, as (phase name, call)."""
-        calls = [("gate_score", lambda: tg.tg_gate_score(x, r, norm_w, W1, b1, w2, b2, c.eps_row, score_raw=score,
-                                                          ws=gate_ws))]
+        calls = [("gate_score", lambda: tg.tg_gate_score_folded(x, r, W1f, h, b1, w2, b2, c.eps_row,
+                                                                 score_raw=score))]
         if args.separate_gate:
             calls += [("seq_rmsnorm", lambda: tg.tg_seq_rmsnorm(score, r, c.eps_seq, score=score, ws=seq_ws)),
                       ("topk_select", lambda: tg.tg_topk_select(score, r, K, keep=keep, ws=topk_ws)),
@@ -483,8 +646,7 @@ def main():
     direct_ms = ms_per_step
     graph_info = None
     if args.graph and not args.separate_gate and N <= 32768:
-        graph_info = time_graph(torch, tg, resids, c, norm_w, W1, b1, w2, b2, gate_ws, layers, heads, args.steps,
-                                args.warmup)
+        graph_info = time_graph(torch, tg, resids, c, W1f, b1, w2, b2, layers, heads, args.steps, args.warmup)
         ms_per_step = graph_info["ms_per_step"]
         log(f"{ms_per_step:.4f} ms/step over {args.steps} graph replays (padded kept length "
             f"{graph_info['M_pad']})")
@@ -533,6 +695,13 @@ def main():
         roofline = {"kernel": dom, "bound": "hbm", "achieved": a["achieved_GBs"], "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": a["hbm_frac"], "traffic": None}
     roofline["traffic"] = _traffic(dom_file)
+    ceil = None if args.no_ceilings else ceilings(torch)
+    if ceil:
+        if roofline["unit"] == "TFLOP/s":
+            roofline["measured_ceiling"] = ceil["gemm_bf16_TFLOPs"]
+        else:
+            roofline["measured_ceiling"] = ceil["copy_GBs"]
+        roofline["frac_of_measured_ceiling"] = round(roofline["achieved"] / roofline["measured_ceiling"], 4)
 
     value = N / (ms_per_step * 1e-3)
     out = {
@@ -546,7 +715,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "launch": "hip_graph" if graph_info else "direct",
-        "gate_op": {"calls": ["tg_gate_score"] + ["tg_" + n for n in sel_phases],
+        "gate_op": {"calls": ["tg_gate_score_folded"] + ["tg_" + n for n in sel_phases],
                     "avg_us": round(gate_us, 3), "algorithmic_bytes": gate_bytes,
                     "achieved_GBs": round(gate_bytes / (gate_us * 1e-6) / 1e9, 1),
                     "hbm_frac": round(gate_bytes / (gate_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
@@ -554,6 +723,8 @@ def main():
         "glue_qkv_ms_per_step": round(glue_ms, 4),
         "tokens_per_s_with_glue": round(N / ((ms_per_step + glue_ms) * 1e-3), 1),
     }
+    if ceil:
+        out["ceilings"] = ceil
     if graph_info:
         out["direct_ms_per_step"] = round(direct_ms, 5)
         out["graph"] = {k: v for k, v in graph_info.items() if k != "ms_per_step"}
@@ -568,6 +739,10 @@ def main():
     if layers and not args.no_kv_prune and args.workload == "stage_32k":
         out["kv_cache_prune"] = time_kv_prune(torch, tg, kept_idx, N, M, heads, n_layers=STAGE_GATE_LAYER + 1)
         log(f"kv cache prune: {out['kv_cache_prune']['avg_us']:.2f} us per call")
+
+    if not args.no_sub_records and args.workload == "stage_32k":
+        log("sub-records: gate_16k and sweep_128k at 1/5/10/25 %")
+        out["sub_records"] = sub_records(torch, tg, wl, stage_glue, heads)
 
     if not args.no_cpu_baseline and layers:
         log("timing the CPU oracle on a bounded sample")

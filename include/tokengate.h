@@ -97,6 +97,30 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r,
                   float* score_raw, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tg_gate_score splits into a weight preparation and the scorer proper, so
+ * that a caller whose weights do not change folds them once (at load time)
+ * instead of on every call:
+ *
+ * tg_gate_fold_weights -- writes W1 with the RMSNorm weight folded in,
+ * bf16(W1[n][c] * norm_w[c]), in the order the scorer's kernels read it
+ * (an opaque layout of h * d bf16 values), to W1_folded.  W1, norm_w as for
+ * tg_gate_score; dt must be TG_BF16; folded_bytes >= h * d * 2
+ * (= tg_workspace_size(TG_OP_GATE_SCORE, ...)); W1_folded 16-byte aligned.
+ *
+ * tg_gate_score_folded -- tg_gate_score with the folded weights in place of
+ * W1 and norm_w; no workspace.  For the same inputs the scores equal
+ * tg_gate_score's bit for bit.  Same shapes and errors as tg_gate_score's
+ * bf16 path.
+ */
+int tg_gate_fold_weights(const void* W1, const void* norm_w, int dt, int h,
+                         int d, void* W1_folded, size_t folded_bytes,
+                         void* stream);
+int tg_gate_score_folded(const void* resid, int dt, int B, int N, int d, int r,
+                         const void* W1_folded, float eps_row, const float* b1,
+                         int h, const void* w2, const float* b2,
+                         float* score_raw, void* stream);
+
+/*
  * tg_gate_score_noalloc -- tg_gate_score for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc): the same computation and the same result bits,

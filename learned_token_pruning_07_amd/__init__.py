@@ -28,7 +28,8 @@ EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
             "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_gate_select_padded",
-            "tg_gated_attention_padded", "tg_workspace_size", "tg_last_error", "tg_version")
+            "tg_gated_attention_padded", "tg_gate_fold_weights", "tg_gate_score_folded", "tg_workspace_size",
+            "tg_last_error", "tg_version")
 
 _lib = None
 
@@ -64,6 +65,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_kv_cache_prune.argtypes = [vp, vp, i, i, i, i, i, vp, i, vp, vp, vp]
     lib.tg_gate_score_span.argtypes = [vp, i, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_score_noalloc.argtypes = [vp, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp]
+    lib.tg_gate_fold_weights.argtypes = [vp, vp, i, i, i, vp, sz, vp]
+    lib.tg_gate_score_folded.argtypes = [vp, i, i, i, i, i, vp, f, vp, i, vp, vp, vp, vp]
     lib.tg_gate_select_padded.argtypes = [vp, i, i, i, f, vp, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp]
     lib.tg_gated_attention_padded.argtypes = [vp, vp, vp, i, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
@@ -85,7 +88,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span", "tg_topk_select_span",
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
                  "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc",
-                 "tg_gate_select_padded", "tg_gated_attention_padded"):
+                 "tg_gate_select_padded", "tg_gated_attention_padded", "tg_gate_fold_weights",
+                 "tg_gate_score_folded"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -163,6 +167,39 @@ def tg_gate_score(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, 
         _check(lib.tg_gate_score(_ptr(resid), _dt(resid), B, N, d, r, *rest))
     else:
         _check(lib.tg_gate_score_span(_ptr(resid), _dt(resid), B, N, d, r, span_end, *rest))
+    return score_raw
+
+
+def tg_gate_fold_weights(W1, norm_w, out=None, stream=None):
+    """W1 [h, d] bf16 with the RMSNorm weight folded in, in the scorer's
+    fragment order: a uint8 GPU tensor of h * d * 2 bytes for
+    :func:`tg_gate_score_folded` (fold once per weight set)."""
+    lib = load_library()
+    h, d = W1.shape
+    _need(W1, "W1", torch.bfloat16, (h, d))
+    _need(norm_w, "norm_w", torch.bfloat16, (d,))
+    if out is None:
+        out = torch.empty(h * d * 2, dtype=torch.uint8, device=W1.device)
+    _need(out, "out", torch.uint8)
+    _check(lib.tg_gate_fold_weights(_ptr(W1), _ptr(norm_w), TG_BF16, h, d, _ptr(out), out.numel(), _stream(stream)))
+    return out
+
+
+def tg_gate_score_folded(resid, r: int, W1_folded, h: int, b1, w2, b2, eps_row: float = 1e-6, score_raw=None,
+                         stream=None):
+    """:func:`tg_gate_score` (bf16) on weights folded by :func:`tg_gate_fold_weights`."""
+    lib = load_library()
+    _need(resid, "resid", torch.bfloat16)
+    B, N, d = resid.shape
+    _need(W1_folded, "W1_folded", torch.uint8, (h * d * 2,))
+    _need(b1, "b1", torch.float32, (h,))
+    _need(w2, "w2", torch.bfloat16, (h,))
+    _need(b2, "b2", torch.float32, (1,))
+    if score_raw is None:
+        score_raw = torch.empty((B, N), dtype=torch.float32, device=resid.device)
+    _need(score_raw, "score_raw", torch.float32, (B, N))
+    _check(lib.tg_gate_score_folded(_ptr(resid), TG_BF16, B, N, d, r, _ptr(W1_folded), eps_row, _ptr(b1), h, _ptr(w2),
+                                    _ptr(b2), _ptr(score_raw), _stream(stream)))
     return score_raw
 
 

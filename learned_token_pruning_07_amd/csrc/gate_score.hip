@@ -404,15 +404,25 @@ hipError_t gate_score_scratch(void** ptr) {
   return hipSuccess;
 }
 
+hipError_t launch_gate_fold(const uint16_t* W1, const uint16_t* norm_w, int h, int d, void* W1f, hipStream_t s) {
+  hipLaunchKernelGGL(fold_norm_weight_kernel, dim3((h * d / 8 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                     W1, norm_w, d, h, static_cast<uint16_t*>(W1f));
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
                                   const int32_t* se, const uint16_t* norm_w,
                                   float eps_row, const uint16_t* W1, const float* b1, int h, const uint16_t* w2,
                                   const float* b2, float* out, void* ws, hipStream_t s) {
-  uint16_t* W1w = static_cast<uint16_t*>(ws);
-  hipLaunchKernelGGL(fold_norm_weight_kernel, dim3((h * d / 8 + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                     W1, norm_w, d, h, W1w);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_gate_fold(W1, norm_w, h, d, ws, s);
   if (e != hipSuccess) return e;
+  return launch_gate_score_folded(resid, B, N, d, r, p1, sb, se, eps_row, static_cast<const uint16_t*>(ws), b1, h,
+                                  w2, b2, out, s);
+}
+
+hipError_t launch_gate_score_folded(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                                    const int32_t* se, float eps_row, const uint16_t* W1w, const float* b1, int h,
+                                    const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
   switch (h) {
     case 64:
       return launch_bf16_h<64>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);

@@ -95,7 +95,19 @@ __device__ unsigned long long g_diag_count[4];
   do {                                                                  \
     if ((threadIdx.x & 63) == 0) atomicAdd(&g_diag_count[i], 1ull);     \
   } while (0)
+// Per-workgroup timeline of the last launch (100 MHz real-time counter):
+// [logical id | qb << 32, entry, prologue done, first step done, steady
+// loop done, all key tiles done, exit, 0] for the first kDiagWG workgroups.
+constexpr int kDiagWG = 8192;
+__device__ unsigned long long g_diag_wg[kDiagWG][8];
+#define TG_DIAG_STAMP(k) \
+  do {                   \
+    diag_t[k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
 #else
+#define TG_DIAG_STAMP(k) \
+  do {                   \
+  } while (0)
 #define TG_DIAG_HIT(i) \
   do {                 \
   } while (0)
@@ -347,6 +359,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     P0 = (size_t)b * Mp;
   }
   const int lse_ld = VARLEN ? M : M_all;  // lse rows: [Hq, M] per sequence, [Hq, M_all] per batch row
+#ifdef TG_DIAG_COUNTERS
+  unsigned long long diag_t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  diag_t[0] = (unsigned long long)(unsigned)logical | ((unsigned long long)(unsigned)qb << 32);
+#endif
+  TG_DIAG_STAMP(1);
   const int q0 = qb * BQ;
   const int kv_end = min(M, q0 + BQ);
   const int nkb = (kv_end + kBK - 1) / kBK;
@@ -701,6 +718,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     cq = sm_scale * kLog2e / (t_h * ratio);
   }
   __syncthreads();
+  TG_DIAG_STAMP(2);
   if (t_exists(1)) {
     issue_k(1);
     issue_b(1);
@@ -712,6 +730,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   step(0, sa, sb, pa, pb);  // no P.V yet: half -1 is never computed
   wait_vmem();
   __syncthreads();
+  TG_DIAG_STAMP(3);
   auto stage = [&](int i) __attribute__((always_inline)) {
     if (t_exists(i + 2)) {
       issue_k(i + 2);
@@ -752,6 +771,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
       __syncthreads();
     };
     for (; i < n_steady; ++i) iter(i);
+    TG_DIAG_STAMP(4);
     // leave it: the pending scores go back to the plain form
 #pragma unroll
     for (int e = 0; e < 16; ++e) sb[e] -= cm[e];
@@ -763,6 +783,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     wait_vmem();
     __syncthreads();
   }
+  TG_DIAG_STAMP(5);
 
   // Merge the two groups' online-softmax states (the tile buffers are free
   // now).  Each group finalises half of the output columns: group g keeps
@@ -848,6 +869,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     finish(IntConst<0>{});
   else
     finish(IntConst<1>{});
+#ifdef TG_DIAG_COUNTERS
+  TG_DIAG_STAMP(6);
+  if (threadIdx.x == 0 && blockIdx.x < kDiagWG)
+    for (int k = 0; k < 8; ++k) g_diag_wg[blockIdx.x][k] = diag_t[k];
+#endif
 }
 
 template <int DH, int G>
@@ -1001,6 +1027,12 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 #ifdef TG_DIAG_COUNTERS
 // Reads (and with reset != 0 clears) the rare-path counters of the test
 // build on the current device.  Not part of the library's interface.
+extern "C" int tg_diag_attention_timeline(unsigned long long* out, int n_wg) {
+  if (n_wg < 0 || n_wg > tg::kDiagWG) return 1;
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(tg::g_diag_wg), (size_t)n_wg * 8 * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 3;
+}
+
 extern "C" int tg_diag_attention_counters(unsigned long long* out4, int reset) {
   if (hipMemcpyFromSymbol(out4, HIP_SYMBOL(tg::g_diag_count), 4 * sizeof(unsigned long long), 0,
                           hipMemcpyDeviceToHost) != hipSuccess)

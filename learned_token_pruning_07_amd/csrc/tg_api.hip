@@ -227,6 +227,47 @@ int tg_gate_score(const void* resid, int dt, int B, int N, int d, int r, const v
                            ws, ws_bytes, stream);
 }
 
+int tg_gate_fold_weights(const void* W1, const void* norm_w, int dt, int h, int d, void* W1_folded,
+                         size_t folded_bytes, void* stream) {
+  const char* name = "tg_gate_fold_weights";
+  if (dt != TG_BF16) return fail(TG_EUNSUPPORTED, "%s: only the bf16 scorer takes folded weights", name);
+  if (d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: d, h must be > 0", name);
+  if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "%s: bf16 needs d %% 64 == 0 (d=%d)", name, d);
+  if (h != 64 && h != 128 && h != 256)
+    return fail(TG_EUNSUPPORTED, "%s: bf16 supports h in {64,128,256} (h=%d)", name, h);
+  if (!W1 || !norm_w || !W1_folded) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned16(W1) || !aligned16(norm_w) || !aligned16(W1_folded))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  const size_t need = tg::gate_score_workspace(h, d);
+  if (folded_bytes < need) return fail(TG_EINVAL, "%s: %zu bytes needed, %zu given", name, need, folded_bytes);
+  return hip_status(tg::launch_gate_fold(static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(norm_w), h,
+                                         d, W1_folded, reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
+int tg_gate_score_folded(const void* resid, int dt, int B, int N, int d, int r, const void* W1_folded,
+                         float eps_row, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
+                         void* stream) {
+  const char* name = "tg_gate_score_folded";
+  if (dt != TG_BF16) return fail(TG_EUNSUPPORTED, "%s: only the bf16 scorer takes folded weights", name);
+  if (B <= 0 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: B, N, d, h must be > 0", name);
+  if (r < 0 || r > N) return fail(TG_EINVAL, "%s: r=%d outside [0, N=%d]", name, r, N);
+  if (!resid || !W1_folded || !b1 || !w2 || !b2 || !score_raw) return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!(eps_row >= 0.0f)) return fail(TG_EINVAL, "%s: eps_row must be >= 0", name);
+  if ((long long)B * N * d > (1LL << 40)) return fail(TG_EINVAL, "%s: tensor too large", name);
+  if (!aligned16(resid) || !aligned16(W1_folded) || !aligned4(score_raw) || !aligned4(b1) || !aligned4(b2))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "%s: bf16 needs d %% 64 == 0 (d=%d)", name, d);
+  if (h != 64 && h != 128 && h != 256)
+    return fail(TG_EUNSUPPORTED, "%s: bf16 supports h in {64,128,256} (h=%d)", name, h);
+  if ((size_t)(N - r) * d * 2 > 0x7FFFFFFFull) return fail(TG_EUNSUPPORTED, "%s: a batch row above 2 GiB", name);
+  return hip_status(tg::launch_gate_score_folded(static_cast<const uint16_t*>(resid), B, N, d, r, N, nullptr,
+                                                 nullptr, eps_row, static_cast<const uint16_t*>(W1_folded), b1, h,
+                                                 static_cast<const uint16_t*>(w2), b2, score_raw,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
 int tg_gate_score_noalloc(const void* resid, int dt, int B, int N, int d, int r, const void* norm_w, float eps_row,
                           const void* W1, const float* b1, int h, const void* w2, const float* b2, float* score_raw,
                           void* stream) {

@@ -21,6 +21,13 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
 
 // Workspace bytes of launch_gate_score_bf16: the norm-weight-folded W1.
 size_t gate_score_workspace(int h, int d);
+// Its two halves: W1 with the norm weight folded in (fragment order, h * d
+// bf16 values), and the scorer on an already folded W1.
+hipError_t launch_gate_fold(const uint16_t* W1, const uint16_t* norm_w, int h, int d, void* W1f, hipStream_t s);
+hipError_t launch_gate_score_folded(const uint16_t* resid, int B, int N, int d, int r, int p1,
+                                    const int32_t* span_begin, const int32_t* span_end, float eps_row,
+                                    const uint16_t* W1f, const float* b1, int h, const uint16_t* w2,
+                                    const float* b2, float* out, hipStream_t s);
 
 // The scorer's static scratch (for callers that cannot allocate): its size,
 // and its device address on the current device (looked up on the first call

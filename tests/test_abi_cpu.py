@@ -373,3 +373,19 @@ def test_padded_entry_points_validate(lib):
     assert attn(dh=96) == tgb.TG_EUNSUPPORTED
     need = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 512, 8 * 128, 16, 128)
     assert attn(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
+
+
+def test_fold_weights_and_folded_scorer_validate(lib):
+    assert lib.tg_gate_fold_weights(FAKE, FAKE, tgb.TG_F32, 256, 2048, FAKE, 1 << 20, None) == tgb.TG_EUNSUPPORTED
+    assert lib.tg_gate_fold_weights(FAKE, FAKE, tgb.TG_BF16, 256, 2048, FAKE, 256 * 2048 * 2 - 1, None) == \
+        tgb.TG_EINVAL and "needed" in _err(lib)
+    assert lib.tg_gate_fold_weights(FAKE, FAKE, tgb.TG_BF16, 96, 2048, FAKE, 1 << 30, None) == tgb.TG_EUNSUPPORTED
+    assert lib.tg_gate_fold_weights(FAKE_ODD, FAKE, tgb.TG_BF16, 256, 2048, FAKE, 1 << 30, None) == tgb.TG_EINVAL
+
+    def score(r=0, N=64, d=2048, h=256, dt=tgb.TG_BF16, w=FAKE):
+        return lib.tg_gate_score_folded(FAKE, dt, 1, N, d, r, w, 1e-6, FAKE, h, FAKE, FAKE, FAKE, None)
+
+    assert score(dt=tgb.TG_F32) == tgb.TG_EUNSUPPORTED
+    assert score(r=65) == tgb.TG_EINVAL
+    assert score(w=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert score(d=100) == tgb.TG_EUNSUPPORTED

@@ -60,6 +60,26 @@ def test_gate_score_bf16(h, N, r, d, B, extras):
     assert np.all(out.cpu().numpy()[:, :r] == 0.0)
 
 
+@pytest.mark.parametrize("h,N,r,d,B", [(256, 1000, 37, 512, 2), (128, 40000, 64, 2048, 1), (64, 333, 0, 128, 1)])
+def test_gate_score_folded_equals_gate_score(h, N, r, d, B):
+    """Weights folded once (tg_gate_fold_weights), then tg_gate_score_folded:
+    bit for bit the scores of tg_gate_score (which folds on every call), with
+    a non-unit norm weight; N = 40000 takes the 128-token tiles."""
+    say(f"gate_score_folded h={h} N={N} r={r} d={d} B={B}")
+    c = wl.gate_case(N=N, r=r, d=d, h=h, K=1, dtype="bf16", seed=h + N, B=B)
+    c.norm_w = wl.f32_to_bf16_bits(wl.make_rng(3).uniform(0.5, 1.5, size=d).astype(np.float32))
+    t = gate_dev(c)
+    ref = tg.tg_gate_score(t["resid"], c.r, t["norm_w"], t["W1"], t["b1"], t["w2"], t["b2"], c.eps_row)
+    folded = tg.tg_gate_fold_weights(t["W1"], t["norm_w"])
+    got = tg.tg_gate_score_folded(t["resid"], c.r, folded, h, t["b1"], t["w2"], t["b2"], c.eps_row,
+                                  score_raw=poison_f32((B, N)))
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    rows = np.unique(np.concatenate([np.arange(min(N, 300)), np.arange(max(0, N - 50), N)]))
+    want = _oracle_scores(c)[:, rows]
+    assert_close(got.cpu().numpy()[:, rows], want, TOL_BF16, "folded scores")
+
+
 def test_gate_score_zero_mlp_is_exact_zero():
     # the scoring MLP starts at zero output, so every score (and b) is exactly 0
     for dtype in ("bf16", "f32"):
