@@ -57,8 +57,13 @@
 //    same swizzle.  The prepass also writes the key-score term of every query
 //    head, gain_h * log2(e) * b_j - e, and a row holding the tile's 2^e, so
 //    that those tiles too are plain copies.
-//  * Grid: heaviest causal query blocks first, remapped so that every
-//    workgroup of one KV head lands on the same XCD (shared L2 for its K/V).
+//  * Grid (batched rows): a persistent grid of one workgroup per CU works
+//    through the query blocks, heaviest causal blocks first, in a snake
+//    order that pairs each workgroup's heavy and light blocks; every block
+//    of one KV head stays on one XCD (shared L2 for its K/V).  A workgroup
+//    requests its next block's Q fragments as soon as it has written the
+//    current block's output.  Varying-length launches run one workgroup
+//    per query block, heaviest first.
 #include <math.h>
 
 #include <algorithm>
@@ -95,16 +100,27 @@ __device__ unsigned long long g_diag_count[4];
   do {                                                                  \
     if ((threadIdx.x & 63) == 0) atomicAdd(&g_diag_count[i], 1ull);     \
   } while (0)
-// Per-workgroup timeline of the last launch (100 MHz real-time counter):
-// [logical id | qb << 32, entry, prologue done, first step done, steady
-// loop done, all key tiles done, exit, 0] for the first kDiagWG workgroups.
+// Per-block timeline of the last launch (100 MHz real-time counter), by block
+// id (slab * query blocks + qb, or the workgroup of a varying-length launch):
+// [logical workgroup | qb << 32, start, prologue done, first step done,
+// steady loop done, all key tiles done, end, round] for ids below kDiagWG.
 constexpr int kDiagWG = 8192;
 __device__ unsigned long long g_diag_wg[kDiagWG][8];
+// finer stamps of the prologue and first step: [before the first loads,
+// after their wait, after the first step's loads are issued, after its wait]
+__device__ unsigned long long g_diag_pro[kDiagWG][4];
 #define TG_DIAG_STAMP(k) \
   do {                   \
     diag_t[k] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
+#define TG_DIAG_PSTAMP(k) \
+  do {                    \
+    diag_p[k] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
 #else
+#define TG_DIAG_PSTAMP(k) \
+  do {                    \
+  } while (0)
 #define TG_DIAG_STAMP(k) \
   do {                   \
   } while (0)
@@ -221,7 +237,8 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     w[e] = m < M ? load16(v + ((T0 + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
   }
   // the block's largest bf16 magnitude (sign cleared; NaN and inf compare
-  // above every finite value), as an integer max over the bit patterns
+  // above every finite value), as an integer max over the bit patterns: one
+  // value per wave here, combined after the transpose's barrier
   uint32_t mag = 0;
 #pragma unroll
   for (int e = 0; e < NL; ++e)
@@ -230,6 +247,18 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
   if ((tid & 63) == 0) s_mag[tid >> 6] = mag;
+  // transpose the raw bf16 block through LDS; the conversion happens on the
+  // way out, once the block's scale is known
+#pragma unroll
+  for (int e = 0; e < NL; ++e) {
+    const int c = tid + e * kThreads;
+    const int key = c / (DH / 8), part = c % (DH / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sT[part * 8 + 2 * i][key] = (uint16_t)(w[e][i] & 0xFFFFu);
+      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(w[e][i] >> 16);
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int wv = 0; wv < kThreads / 64; ++wv) mag = max(mag, s_mag[wv]);
@@ -243,25 +272,17 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     if (hh < G) val = m < M ? fmaf(key_score[T0 + m], gain[g * G + hh] * kLog2e, (float)-ex) : 0.0f;
     kbias[kb_row + (size_t)hh * Mp + m] = val;
   }
-#pragma unroll
-  for (int e = 0; e < NL; ++e) {
-    const int c = tid + e * kThreads;
-    const int key = c / (DH / 8), part = c % (DH / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // exact for every value within 2^28 below the block's largest
-      const uint32_t h2 = pack_f16x2(bf16_lo(w[e][i]) * scale, bf16_hi(w[e][i]) * scale);
-      sT[part * 8 + 2 * i][key] = (uint16_t)(h2 & 0xFFFFu);
-      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(h2 >> 16);
-    }
-  }
-  __syncthreads();
+  // fp16 V 2^ex, round to nearest even: exact for every value within 2^28
+  // below the block's largest
+  auto to_f16 = [&](uint16_t lo, uint16_t hi) {
+    return pack_f16x2(__uint_as_float((uint32_t)lo << 16) * scale, __uint_as_float((uint32_t)hi << 16) * scale);
+  };
   for (int c = tid; c < DH * (kBK / 8); c += kThreads) {
     const int d = c / (kBK / 8), kc = c % (kBK / 8);
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i)] | ((uint32_t)sT[d][vt_slot_key(kc * 8 + 2 * i + 1)] << 16);
+      o[i] = to_f16(sT[d][vt_slot_key(kc * 8 + 2 * i)], sT[d][vt_slot_key(kc * 8 + 2 * i + 1)]);
     store16(vt + P0 * Hkv * DH + ((size_t)g * DH + d) * Mp + m0 + kc * 8, o);
   }
   if constexpr (ROPE) {
@@ -298,12 +319,66 @@ __device__ __forceinline__ void buffer_load4_to_lds(__amdgpu_buffer_rsrc_t rsrc,
 // s_waitcnt vmcnt(0): wait for every load of this wave, LDS-destination ones included
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The attention kernel's scalar arguments.  The kernel reads them from its
+// argument segment at the start of every block it works on (not once), so
+// that its loop over blocks carries only the segment's address in registers.
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* vt;
+  const float* kbias;
+  const int32_t* pos;
+  const float* temp;
+  uint16_t* out;
+  float* lse;
+  const int32_t* m_dev;
+  int M_all, Mp_all, Hq, Hkv, nqb_all, total_wg, n_slabs;
+  float sm_scale;
+};
+typedef const __attribute__((address_space(4))) AttnArgs* AttnArgsPtr;
+
+// The persistent schedule of the batched launch.  Slab = batch row x KV head;
+// level L of a slab is its query block nqb - 1 - L (the heaviest first).
+// Round r hands rank r P + w to workgroup w when r is even and rank
+// r P + P - 1 - w when it is odd (P workgroups deal out a partition), so each
+// workgroup's heavy and light blocks pair up and a workgroup moves to its
+// next block without a new dispatch.  When the slabs divide evenly over the
+// 8 XCDs, XCD x deals out only the slabs x, x + 8, ... among its own
+// workgroups (consecutive logical ids share an XCD), so each KV head's K/V
+// tiles stay in one L2.  Returns 0 past the workgroup's last block, 1 when
+// round r has nothing for it (a query block past a short row's kept length),
+// 2 with the block's batch row b, KV head g, query block qb and the row's
+// kept length M.  Everything is derived from the argument segment here, so
+// no schedule value stays live while a block runs.
+template <int BQ>
+__device__ __forceinline__ int sched_block(AttnArgsPtr ap, int rnd, int& b, int& g, int& qb, int& M) {
+  const int total_wg = ap->total_wg, n_slabs = ap->n_slabs, nqb_all = ap->nqb_all, Hkv = ap->Hkv;
+  const int logical = xcd_logical_id(blockIdx.x, total_wg);
+  const bool by_xcd = n_slabs % 8 == 0 && total_wg % 8 == 0;
+  const int sched_p = by_xcd ? total_wg / 8 : total_wg;  // workgroups dealing out one partition
+  const int sched_x = logical / sched_p, sched_w = logical - sched_x * sched_p;
+  const int slabs_here = by_xcd ? n_slabs / 8 : n_slabs;
+  const int rank = rnd * sched_p + ((rnd & 1) ? sched_p - 1 - sched_w : sched_w);
+  if (rank >= slabs_here * nqb_all) return 0;
+  const int level = rank / slabs_here, j = rank - level * slabs_here;
+  const int slab = by_xcd ? sched_x + 8 * j : j;
+  b = slab / Hkv;
+  g = slab - b * Hkv;
+  M = ap->M_all;
+  int nqb = nqb_all;
+  if (ap->m_dev != nullptr) {  // this row's kept length (M_all is the padded length)
+    M = min(max(ap->m_dev[b], 0), M);
+    nqb = (M + BQ - 1) / BQ;
+  }
+  if (level >= nqb) return 1;
+  qb = nqb - 1 - level;
+  return 2;
+}
+
 template <int DH, int G, bool VARLEN>
-__global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt,
-    const float* __restrict__ kbias, int M_all, int Mp_all, int Hq, int Hkv, const int32_t* __restrict__ pos,
-    const float* __restrict__ temp, float sm_scale, uint16_t* __restrict__ out, float* __restrict__ lse, int nqb_all,
-    int total_wg, const SeqTable st, const int32_t* __restrict__ m_dev) {
+__global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnArgs args, const SeqTable st) {
+  (void)args;  // read through the argument segment below (it is the first argument)
+  const AttnArgsPtr args_seg = (AttnArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int RG = 4 / G;        // 32-row groups per head
   constexpr int BQ = 32 * RG;      // query rows per workgroup
   constexpr int KS = DH / 16;      // k-steps of S^T = K Q^T
@@ -322,17 +397,44 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   // [buf][group] K tiles, then [buf][group] V^T tiles, then [buf][group][head] key-score tiles
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
 
-  const int lane = threadIdx.x & 63;
-  const int wall = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: branches stay scalar
+  // This lane's Q fragments and the original position of its query.  The
+  // next block's are requested as soon as the current block has written its
+  // output (they then belong to round pre_round).
+  bf16x8 qf[DH / 16];
+  int p_pre = 0, pre_round = -1;
+  for (int round = 0;; ++round) {
+  // Every value of the block is derived afresh inside the loop (the thread
+  // index and the argument segment pass through empty asm statements), so
+  // nothing is hoisted out of it and kept live across the whole block.
+  unsigned tix = threadIdx.x;
+  asm volatile("" : "+v"(tix));
+  const int lane = tix & 63;
+  const int wall = __builtin_amdgcn_readfirstlane(tix >> 6);  // wave-uniform: branches stay scalar
   const int grp = wall >> 2;       // key-range group of this wave
   const int wid = wall & 3;        // wave index inside the group
-  const int tid = threadIdx.x & (kThreads - 1);  // thread index inside the group
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  // this workgroup's sequence (its length M, first packed row T0, first
-  // padded key slot P0), KV head g and query block qb (the longest first)
+  const int tid = tix & (kThreads - 1);  // thread index inside the group
+  AttnArgsPtr ap = args_seg;
+  asm volatile("" : "+s"(ap));  // reload the arguments for this block
+  const uint16_t* __restrict__ q = ap->q;
+  const uint16_t* __restrict__ k = ap->k;
+  const uint16_t* __restrict__ vt = ap->vt;
+  const float* __restrict__ kbias = ap->kbias;
+  const int32_t* __restrict__ pos = ap->pos;
+  const float* __restrict__ temp = ap->temp;
+  uint16_t* __restrict__ out = ap->out;
+  float* __restrict__ lse = ap->lse;
+  const int32_t* __restrict__ m_dev = ap->m_dev;
+  const int M_all = ap->M_all, Mp_all = ap->Mp_all, Hq = ap->Hq, Hkv = ap->Hkv, nqb_all = ap->nqb_all;
+  const int total_wg = ap->total_wg, n_slabs = ap->n_slabs;
+  const float sm_scale = ap->sm_scale;
+  // this block's sequence (its length M, first packed row T0, first padded
+  // key slot P0), KV head g and query block qb
   int M, Mp, g, qb;
   size_t T0, P0;
+  int item;  // a unique id of the block (timeline of the counting build)
   if constexpr (VARLEN) {
+    if (round > 0) break;
+    const int logical = xcd_logical_id(blockIdx.x, total_wg);
     const int sq = seq_of(st.wg0, st.n, logical);
     M = st.m[sq];
     Mp = (M + kBK - 1) / kBK * kBK;
@@ -341,27 +443,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     qb = nqb - 1 - (local - g * nqb);
     T0 = (size_t)st.t0[sq];
     P0 = (size_t)st.p0[sq];
+    item = logical;
   } else {
-    M = M_all;
+    int b;
+    const int st_b = sched_block<BQ>(ap, round, b, g, qb, M);
+    if (st_b == 0) break;
+    if (st_b == 1) continue;  // (the whole workgroup)
     Mp = Mp_all;
-    const int bg = logical / nqb_all;
-    const int b = bg / Hkv;
-    g = bg - b * Hkv;
-    int nqb = nqb_all;
-    if (m_dev != nullptr) {  // this row's kept length (M_all is the padded length)
-      M = min(max(m_dev[b], 0), M_all);
-      nqb = (M + BQ - 1) / BQ;
-    }
-    const int local = logical - bg * nqb_all;
-    if (local >= nqb) return;  // a query block past the kept length (the whole workgroup)
-    qb = nqb - 1 - local;
     T0 = (size_t)b * M_all;
     P0 = (size_t)b * Mp;
+    item = (b * Hkv + g) * nqb_all + qb;
   }
+  if (round > 0) __syncthreads();  // every wave is done with the previous block's LDS
   const int lse_ld = VARLEN ? M : M_all;  // lse rows: [Hq, M] per sequence, [Hq, M_all] per batch row
 #ifdef TG_DIAG_COUNTERS
   unsigned long long diag_t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  diag_t[0] = (unsigned long long)(unsigned)logical | ((unsigned long long)(unsigned)qb << 32);
+  unsigned long long diag_p[4] = {0, 0, 0, 0};
+  diag_t[0] = (unsigned long long)blockIdx.x | ((unsigned long long)(unsigned)qb << 32);
+  diag_t[7] = (unsigned long long)(unsigned)round;
 #endif
   TG_DIAG_STAMP(1);
   const int q0 = qb * BQ;
@@ -438,7 +537,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   auto k_frag_off = [&](int ks) { return ql * KROW + (((2 * ks + gq) ^ q7) << 4); };
   auto v_frag_off = [&](int st) { return ql * VROW + (((2 * st + gq) ^ q7) << 4); };
 
-  bf16x8 qf[KS];      // this lane's Q fragments (filled in the prologue below)
   float cq = 0.0f;    // per-query logit scale in the log2 domain
   f32x16 o[DT];
 #pragma unroll
@@ -698,20 +796,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     n_steady = min(n_steady, hmax >= 3 ? ((hmax - 3) >> 1) + 1 : 0);
   }
   n_steady = __builtin_amdgcn_readfirstlane(n_steady);
+  TG_DIAG_PSTAMP(0);
   if (t_exists(0)) {
     issue_k(0);
     issue_b(0);
   }
   // Q fragments and the original position are requested while the first
-  // tile is in flight; one wait covers all of them
-  {
+  // tile is in flight (unless the previous block requested them); one wait
+  // covers all of them
+  int p_orig = p_pre;
+  if (pre_round != round) {
     const uint16_t* qp = q + ((T0 + (q_ok ? qi : 0)) * Hq + hq) * DH + gq * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? load16(qp + ks * 16) : u32x4{0, 0, 0, 0});
+    p_orig = pos[T0 + (q_ok ? qi : 0)];
   }
-  const int p_orig = pos[T0 + (q_ok ? qi : 0)];
   const float t_h = temp[hq];
   wait_vmem();
+  TG_DIAG_PSTAMP(1);
   if (q_ok) {
     float ratio = 1.0f;
     if (p_orig != qi) ratio = logf((float)max(p_orig + 1, 2)) / logf((float)max(qi + 1, 2));
@@ -728,7 +830,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
   uint32_t pa[8], pb[8];
   if (h_mine(0)) qk(0, sa);
   step(0, sa, sb, pa, pb);  // no P.V yet: half -1 is never computed
+  TG_DIAG_PSTAMP(2);
   wait_vmem();
+  TG_DIAG_PSTAMP(3);
   __syncthreads();
   TG_DIAG_STAMP(3);
   auto stage = [&](int i) __attribute__((always_inline)) {
@@ -784,7 +888,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     __syncthreads();
   }
   TG_DIAG_STAMP(5);
-
   // Merge the two groups' online-softmax states (the tile buffers are free
   // now).  Each group finalises half of the output columns: group g keeps
   // O^T tiles [g DT/2, (g+1) DT/2) and hands its other tiles, with m and l,
@@ -869,11 +972,45 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(
     finish(IntConst<0>{});
   else
     finish(IntConst<1>{});
+  if constexpr (!VARLEN) {
+    // request the next block's Q fragments and positions now: they land
+    // while this block's output stores drain and the next block sets up
+    AttnArgsPtr an = args_seg;
+    asm volatile("" : "+s"(an));
+    int b_n, g_n, qb_n, M_n;
+    if (sched_block<BQ>(an, round + 1, b_n, g_n, qb_n, M_n) == 2) {
+      const int qi_n = qb_n * BQ + (wid % RG) * 32 + ql;
+      const bool ok = qi_n < M_n;
+      const size_t row = (size_t)b_n * an->M_all + (ok ? qi_n : 0);
+      const uint16_t* qp = an->q + (row * an->Hq + g_n * G + hloc) * DH + gq * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ok ? load16(qp + ks * 16) : u32x4{0, 0, 0, 0});
+      p_pre = an->pos[row];
+      pre_round = round + 1;
+    }
+  }
+
 #ifdef TG_DIAG_COUNTERS
   TG_DIAG_STAMP(6);
-  if (threadIdx.x == 0 && blockIdx.x < kDiagWG)
-    for (int k = 0; k < 8; ++k) g_diag_wg[blockIdx.x][k] = diag_t[k];
+  if (tix == 0 && item < kDiagWG) {
+    for (int k = 0; k < 8; ++k) g_diag_wg[item][k] = diag_t[k];
+    for (int k = 0; k < 4; ++k) g_diag_pro[item][k] = diag_p[k];
+  }
 #endif
+  }  // the next block of this workgroup
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <int DH, int G>
@@ -898,8 +1035,11 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   const long long total = (long long)nqb * Hkv * B;
   if (total <= 0) return hipSuccess;
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G, false>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
-                     kbias, M, Mp, Hq, Hkv, pos, temp, sm_scale, out, lse, nqb, (int)total, SeqTable{}, m_dev);
+  // a persistent grid of one workgroup per CU (each holds a CU's LDS)
+  const int grid = (int)std::min<long long>(total, device_cu_count());
+  const AttnArgs a{q, k, vt, kbias, pos, temp, out, lse, m_dev, M, Mp, Hq, Hkv, nqb, grid, Hkv * B, sm_scale};
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G, false>), dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a,
+                     SeqTable{});
   return hipGetLastError();
 }
 
@@ -913,8 +1053,8 @@ hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = st.wg0[st.n];
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, q, k, vt,
-                     kbias, 0, 0, Hq, Hkv, pos, temp, sm_scale, out, lse, 0, total, st, nullptr);
+  const AttnArgs a{q, k, vt, kbias, pos, temp, out, lse, nullptr, 0, 0, Hq, Hkv, 0, total, 0, sm_scale};
+  hipLaunchKernelGGL((gated_attn_kernel<DH, G, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, a, st);
   return hipGetLastError();
 }
 
@@ -1030,6 +1170,12 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 extern "C" int tg_diag_attention_timeline(unsigned long long* out, int n_wg) {
   if (n_wg < 0 || n_wg > tg::kDiagWG) return 1;
   return hipMemcpyFromSymbol(out, HIP_SYMBOL(tg::g_diag_wg), (size_t)n_wg * 8 * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 3;
+}
+
+extern "C" int tg_diag_attention_prologue(unsigned long long* out, int n_wg) {
+  if (n_wg < 0 || n_wg > tg::kDiagWG) return 1;
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(tg::g_diag_pro), (size_t)n_wg * 4 * sizeof(unsigned long long), 0,
                              hipMemcpyDeviceToHost) == hipSuccess ? 0 : 3;
 }
 
