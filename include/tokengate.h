@@ -439,7 +439,9 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v,
  *   ws, ws_bytes     workspace of at least tg_workspace_size(
  *                    TG_OP_GATED_ATTENTION_ROPE, B, M, Hkv * d_h, Hq, d_h) bytes,
  *                    16-byte aligned (tg_gated_attention's workspace followed
- *                    by the rotated q and k; contents need no initialisation)
+ *                    by the rotated k and the cosines and sines of every
+ *                    row's angles; q is rotated inside the attention kernel
+ *                    from those; contents need no initialisation)
  */
 int tg_gated_attention_rope(const void* q, const void* k, const void* v,
                             int B, int M, int Hq, int Hkv, int d_h,
@@ -447,6 +449,24 @@ int tg_gated_attention_rope(const void* q, const void* k, const void* v,
                             const float* gain, const float* temp, float sm_scale,
                             double rope_base, void* out, float* lse, void* ws,
                             size_t ws_bytes, void* stream);
+
+/*
+ * tg_gated_attention_rope_varlen -- tg_gated_attention_varlen with the rotary
+ * embedding of tg_gated_attention_rope: every packed row of q and k turns by
+ * its own original position pos[t] (Appendix C.4: kept tokens keep their
+ * positions in every prompt of the batch).  Each sequence's results equal
+ * tg_gated_attention_rope's for that sequence alone, bit for bit.  The
+ * workspace is at least tg_workspace_size(TG_OP_GATED_ATTENTION_ROPE, 1,
+ * T + 63 * B, Hkv * d_h, Hq, d_h) bytes, T = cu_seqlens[B].  Otherwise as
+ * tg_gated_attention_varlen.
+ */
+int tg_gated_attention_rope_varlen(const void* q, const void* k, const void* v,
+                                   int B, const int32_t* cu_seqlens, int Hq,
+                                   int Hkv, int d_h, const float* key_score,
+                                   const int32_t* pos, const float* gain,
+                                   const float* temp, float sm_scale,
+                                   double rope_base, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tg_gated_attention_backward -- gradients of tg_gated_attention.  In the
@@ -576,7 +596,7 @@ int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers,
  * and K = d_h; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * (Hq +
  * Hkv)).  K = 0 gives the size for the largest Hkv (= Hq), an upper bound.
  * For TG_OP_GATED_ATTENTION_ROPE pass the same and K = d_h; the size adds
- * 2 * B * M * (Hq + Hkv) * d_h.
+ * B * M * d_h * (2 * Hkv + 4).
  * For TG_OP_GATED_ATTENTION_BACKWARD pass the same as for
  * TG_OP_GATED_ATTENTION_ROPE; with Mp = round_up(M, 64) the size is
  * B * Mp * (12 Hq + 4 Hkv) + 8 * B * (Mp / 64) * Hq.

@@ -28,7 +28,8 @@ EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "
             "tg_gated_attention_rope", "tg_gated_attention_backward", "tg_gated_attention_rope_backward", "tg_kv_cache_prune", "tg_gate_score_span", "tg_seq_rmsnorm_span",
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
             "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_gate_select_padded",
-            "tg_gated_attention_padded", "tg_gate_fold_weights", "tg_gate_score_folded", "tg_workspace_size",
+            "tg_gated_attention_padded", "tg_gate_fold_weights", "tg_gate_score_folded",
+            "tg_gated_attention_rope_varlen", "tg_workspace_size",
             "tg_last_error", "tg_version")
 
 _lib = None
@@ -74,6 +75,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gated_attention_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f,
                                                        vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
+    lib.tg_gated_attention_rope_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, ctypes.c_double,
+                                                   vp, vp, vp, sz, vp]
     lib.tg_gate_score_varlen.argtypes = [vp, i, i, i, i, vp, vp, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
     lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -89,7 +92,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
                  "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc",
                  "tg_gate_select_padded", "tg_gated_attention_padded", "tg_gate_fold_weights",
-                 "tg_gate_score_folded"):
+                 "tg_gate_score_folded", "tg_gated_attention_rope_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -506,7 +509,7 @@ def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, ep
 
 
 def tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, sm_scale: float | None = None,
-                              out=None, lse=None, ws=None, stream=None):
+                              out=None, lse=None, ws=None, stream=None, rope_base: float | None = None):
     """Token-gated attention over packed sequences: q ``[T, Hq, dh]``, k/v
     ``[T, Hkv, dh]``, key_score/pos ``[T]``, ``cu_seqlens`` a host list of B + 1
     row offsets (e.g. from :func:`tg_gate_select_varlen`).  Returns ``out``
@@ -531,12 +534,26 @@ def tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, s
     if lse is not None:
         _need(lse, "lse", torch.float32, (T * Hq,))
     if ws is None:  # every sequence padded to 64 rows, side by side
-        ws = attention_workspace(1, max(T + 63 * B, 1), Hq, Hkv, dh, q.device)
+        mk = attention_workspace if rope_base is None else attention_rope_workspace
+        ws = mk(1, max(T + 63 * B, 1), Hq, Hkv, dh, q.device)
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
-    _check(lib.tg_gated_attention_varlen(_ptr(q), _ptr(k), _ptr(v), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
-                                         _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), _ptr(out), _ptr(lse),
-                                         _ptr(ws), ws.numel(), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), B, cu_arr, Hq, Hkv, dh, _ptr(key_score), _ptr(pos), _ptr(gain), _ptr(temp),
+            float(sm_scale))
+    tail = (_ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream))
+    if rope_base is None:
+        _check(lib.tg_gated_attention_varlen(*args, *tail))
+    else:
+        _check(lib.tg_gated_attention_rope_varlen(*args, float(rope_base), *tail))
     return (out, lse) if lse is not None else out
+
+
+def tg_gated_attention_rope_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, rope_base: float,
+                                   sm_scale: float | None = None, out=None, lse=None, ws=None, stream=None):
+    """:func:`tg_gated_attention_varlen` with the rotary embedding of
+    :func:`tg_gated_attention_rope` (each packed row turned by its own
+    original position ``pos``)."""
+    return tg_gated_attention_varlen(q, k, v, cu_seqlens, key_score, pos, gain, temp, sm_scale, out=out, lse=lse,
+                                     ws=ws, stream=stream, rope_base=rope_base)
 
 
 def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key_score, pos, gain, temp,

@@ -152,12 +152,14 @@ __device__ __forceinline__ int vt_slot_key(int s) {
 
 // Rotary position embedding inputs of the prepass: q, k and the positions,
 // the base, and where the rotated copies go (same layouts as q and k).
+// rotated copy of k, and a table of the cosines and sines of every row's
+// angles ([rows, DH/2] pairs (cos, sin), fp32) from which the attention
+// kernel rotates its Q fragments.
 struct RopeArgs {
-  const uint16_t* q;
   const uint16_t* k;
   const int32_t* pos;
   double base;
-  uint16_t* qr;
+  float* tab;
   uint16_t* kr;
 };
 
@@ -186,11 +188,12 @@ struct SeqTable {
 //   key-score rows kb [B, Hkv, G + 1, Mp] fp32: row hh < G holds
 //   gain_h * log2(e) * key_score - e for query head h = g G + hh (zero
 //   beyond M), row G holds 2^e for every key of the block;
-//   with ROPE, also the rotary embedding of the block's K rows (head g) and Q
-//   rows (the G query heads of g) at their original positions (the rotate-
-//   half form: pair (x_i, x_{i+DH/2}) turns by pos * base^(-2i/DH)).  The
-//   angle is formed and reduced modulo 2 pi in fp64, so that its fp32 sine
-//   and cosine are accurate to a few ulp at any position.
+//   with ROPE, also the rotary embedding of the block's K rows (head g) at
+//   their original positions (the rotate-half form: pair (x_i, x_{i+DH/2})
+//   turns by pos * base^(-2i/DH)) and, in the blocks of KV head 0, the
+//   table of those angles' cosines and sines for the attention kernel's Q
+//   rotation.  The angle is formed and reduced modulo 2 pi in fp64, so that
+//   its fp32 sine and cosine are accurate to a few ulp at any position.
 // VARLEN: the blocks of the table's sequences, one grid row per KV head.
 template <int DH, bool ROPE, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* __restrict__ v,
@@ -294,9 +297,11 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
       rope::sincos8((double)ra.pos[T0 + m], s_freq, i0, c, sn);
       const size_t krow = ((T0 + m) * Hkv + g) * DH;
       rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
-      for (int hh = 0; hh < G; ++hh) {
-        const size_t qrow = ((T0 + m) * Hq + g * G + hh) * DH;
-        rope::row8<DH>(ra.q + qrow, ra.qr + qrow, i0, c, sn);
+      if (g == 0) {  // the row's (cos, sin) pairs i0 .. i0 + 7
+        float* tb = ra.tab + (T0 + m) * DH + 2 * i0;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2)
+          *reinterpret_cast<f32x4*>(tb + 2 * i) = f32x4{c[i], sn[i], c[i + 1], sn[i + 1]};
       }
     }
   }
@@ -332,6 +337,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   const int32_t* m_dev;
+  const float* rope_tab;  // (cos, sin) of every row's rotary angles, or null: q is used as given
   int M_all, Mp_all, Hq, Hkv, nqb_all, total_wg, n_slabs;
   float sm_scale;
 };
@@ -375,7 +381,9 @@ __device__ __forceinline__ int sched_block(AttnArgsPtr ap, int rnd, int& b, int&
   return 2;
 }
 
-template <int DH, int G, bool VARLEN>
+// ROPE: the Q fragments are rotated by the prepass's angle table after they
+// land (the plain instance carries none of that code or its registers).
+template <int DH, int G, bool VARLEN, bool ROPE>
 __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnArgs args, const SeqTable st) {
   (void)args;  // read through the argument segment below (it is the first argument)
   const AttnArgsPtr args_seg = (AttnArgsPtr)__builtin_amdgcn_kernarg_segment_ptr();
@@ -812,8 +820,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
     p_orig = pos[T0 + (q_ok ? qi : 0)];
   }
   const float t_h = temp[hq];
+  // rotary embedding: this lane's fragments ks and ks + KS/2 hold the pairs
+  // (x_i, x_{i + DH/2}), i = 16 ks + 8 gq + e; their cosines and sines come
+  // from the prepass's table row of this query
+  const float* __restrict__ rope_tab = ap->rope_tab;
+  f32x4 rt[KS / 2][4];  // rt[ks][u] = (cos, sin) of pairs 2u and 2u + 1 of fragment ks
+  if constexpr (ROPE) {
+    const float* tr = rope_tab + (T0 + (q_ok ? qi : 0)) * DH + 16 * gq;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rt[ks][u] = *reinterpret_cast<const f32x4*>(tr + 32 * ks + 4 * u);
+  }
   wait_vmem();
   TG_DIAG_PSTAMP(1);
+  if constexpr (ROPE) {  // exactly the prepass's rotation of k: fused fp32 products, bf16 nearest even
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      const u32x4 a = __builtin_bit_cast(u32x4, qf[ks]), bv = __builtin_bit_cast(u32x4, qf[ks + KS / 2]);
+      u32x4 oa, ob;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // word j: elements e = 2j (low half) and 2j + 1 (high half)
+        const float cl = rt[ks][j][0], sl = rt[ks][j][1], ch = rt[ks][j][2], sh = rt[ks][j][3];
+        const float x1l = bf16_lo(a[j]), x1h = bf16_hi(a[j]), x2l = bf16_lo(bv[j]), x2h = bf16_hi(bv[j]);
+        oa[j] = pack_bf16x2(fmaf(x1l, cl, -(x2l * sl)), fmaf(x1h, ch, -(x2h * sh)));
+        ob[j] = pack_bf16x2(fmaf(x2l, cl, x1l * sl), fmaf(x2h, ch, x1h * sh));
+      }
+      qf[ks] = as_bf16x8(oa);
+      qf[ks + KS / 2] = as_bf16x8(ob);
+    }
+  }
   if (q_ok) {
     float ratio = 1.0f;
     if (p_orig != qi) ratio = logf((float)max(p_orig + 1, 2)) / logf((float)max(qi + 1, 2));
@@ -1023,8 +1059,7 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   if (rope != nullptr) {
     hipLaunchKernelGGL((attn_prepass_kernel<DH, true, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
                        gain, M, Mp, Hkv, G, vt, kbias, *rope, SeqTable{}, m_dev);
-    q = rope->qr;  // the main kernel reads the rotated copies
-    k = rope->kr;
+    k = rope->kr;  // the main kernel reads the rotated k and rotates its Q fragments itself
   } else {
     hipLaunchKernelGGL((attn_prepass_kernel<DH, false, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
                        gain, M, Mp, Hkv, G, vt, kbias, RopeArgs{}, SeqTable{}, m_dev);
@@ -1037,9 +1072,14 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
   // a persistent grid of one workgroup per CU (each holds a CU's LDS)
   const int grid = (int)std::min<long long>(total, device_cu_count());
-  const AttnArgs a{q, k, vt, kbias, pos, temp, out, lse, m_dev, M, Mp, Hq, Hkv, nqb, grid, Hkv * B, sm_scale};
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G, false>), dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a,
-                     SeqTable{});
+  const AttnArgs a{q,   k,   vt,  kbias, pos,  temp,     out, lse, m_dev, rope != nullptr ? rope->tab : nullptr,
+                   M,   Mp,  Hq,  Hkv,   nqb,  grid,     Hkv * B,  sm_scale};
+  if (rope != nullptr)
+    hipLaunchKernelGGL((gated_attn_kernel<DH, G, false, true>), dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a,
+                       SeqTable{});
+  else
+    hipLaunchKernelGGL((gated_attn_kernel<DH, G, false, false>), dim3((unsigned)grid), dim3(kAttnThreads), 0, s, a,
+                       SeqTable{});
   return hipGetLastError();
 }
 
@@ -1047,14 +1087,26 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
 template <int DH, int G>
 hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const SeqTable& st, int Hq,
                            int Hkv, const float* ks, const int32_t* pos, const float* gain, const float* temp,
-                           float sm_scale, uint16_t* out, float* lse, uint16_t* vt, float* kbias, hipStream_t s) {
-  hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads), 0,
-                     s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st, nullptr);
+                           float sm_scale, uint16_t* out, float* lse, uint16_t* vt, float* kbias,
+                           const RopeArgs* rope, hipStream_t s) {
+  if (rope != nullptr) {
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads),
+                       0, s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, *rope, st, nullptr);
+    k = rope->kr;
+  } else {
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads),
+                       0, s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st, nullptr);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = st.wg0[st.n];
-  const AttnArgs a{q, k, vt, kbias, pos, temp, out, lse, nullptr, 0, 0, Hq, Hkv, 0, total, 0, sm_scale};
-  hipLaunchKernelGGL((gated_attn_kernel<DH, G, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, a, st);
+  const AttnArgs a{q, k, vt, kbias, pos, temp, out, lse, nullptr, rope != nullptr ? rope->tab : nullptr,
+                   0, 0, Hq, Hkv, 0, total, 0, sm_scale};
+  if (rope != nullptr)
+    hipLaunchKernelGGL((gated_attn_kernel<DH, G, true, true>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, a, st);
+  else
+    hipLaunchKernelGGL((gated_attn_kernel<DH, G, true, false>), dim3((unsigned)total), dim3(kAttnThreads), 0, s, a,
+                       st);
   return hipGetLastError();
 }
 
@@ -1066,9 +1118,18 @@ size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
   return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)(Hq + Hkv) * 4);
 }
 
-// ... then the rotated q [B, M, Hq, dh] and k [B, M, Hkv, dh] (bf16)
+// ... then the rotated k [B, M, Hkv, dh] (bf16) and the angle table [B, M,
+// dh / 2] (cos, sin) (fp32)
 size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh) {
-  return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * (Hq + Hkv) * dh * 2;
+  (void)Hq;
+  return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * dh * ((size_t)Hkv * 2 + 4);
+}
+
+// the varying-length rotary call: after the other workspace (slots padded
+// rows), the rotated k and the angle table of the T packed rows
+size_t gated_attention_rope_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv, int dh) {
+  const size_t slots = gated_attention_varlen_slots(B, cu_seqlens);
+  return gated_attention_workspace(1, (int)slots, Hq, Hkv, dh) + (size_t)cu_seqlens[B] * dh * ((size_t)Hkv * 2 + 4);
 }
 
 size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens) {
@@ -1080,7 +1141,7 @@ size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens) {
 hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                          const int32_t* cu_seqlens, int Hq, int Hkv, int dh, const float* key_score,
                                          const int32_t* pos, const float* gain, const float* temp, float sm_scale,
-                                         uint16_t* out, float* lse, void* ws, hipStream_t s) {
+                                         double rope_base, uint16_t* out, float* lse, void* ws, hipStream_t s) {
   const int G = Hq / Hkv;
   constexpr int BQ_G[5] = {0, 128, 64, 0, 32};  // query rows per workgroup by group size
   if (G != 1 && G != 2 && G != 4) return hipErrorInvalidValue;
@@ -1094,6 +1155,15 @@ hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, c
   const size_t slots = gated_attention_varlen_slots(B, cu_seqlens);
   uint16_t* vt = static_cast<uint16_t*>(ws);
   float* kbias = reinterpret_cast<float*>(vt + slots * Hkv * dh);
+  RopeArgs ra{};
+  const RopeArgs* rope = nullptr;
+  if (rope_base > 0.0) {  // rotated k and the angle table, by packed row, after the other workspace
+    unsigned char* rw = static_cast<unsigned char*>(ws) + gated_attention_workspace(1, (int)slots, Hq, Hkv, dh);
+    const size_t T = (size_t)cu_seqlens[B];
+    uint16_t* kr = reinterpret_cast<uint16_t*>(rw);
+    ra = RopeArgs{k, pos, rope_base, reinterpret_cast<float*>(kr + T * Hkv * dh), kr};
+    rope = &ra;
+  }
   size_t p = 0;
   for (size_t i = 0; i < order.size(); i += kMaxSeqsPerLaunch) {
     SeqTable st{};
@@ -1119,7 +1189,7 @@ hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, c
 #define TG_ATTN_VARLEN_CASE(DHV, GV)                                                                          \
   if (dh == DHV && G == GV)                                                                                   \
     e = launch_varlen_t<DHV, GV>(q, k, v, st, Hq, Hkv, key_score, pos, gain, temp, sm_scale, out, lse, vt, kbias, \
-                                 s);
+                                 rope, s);
     TG_ATTN_VARLEN_CASE(128, 2)
     TG_ATTN_VARLEN_CASE(128, 1)
     TG_ATTN_VARLEN_CASE(128, 4)
@@ -1142,10 +1212,10 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
   float* kbias = reinterpret_cast<float*>(vt + (size_t)B * Hkv * dh * Mp);
   RopeArgs ra{};
   const RopeArgs* rope = nullptr;
-  if (rope_base > 0.0) {
-    uint16_t* qr = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
+  if (rope_base > 0.0) {  // rotated k, then the angle table
+    uint16_t* kr = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) +
                                                gated_attention_workspace(B, M, Hq, Hkv, dh));
-    ra = RopeArgs{q, k, pos, rope_base, qr, qr + (size_t)B * M * Hq * dh};
+    ra = RopeArgs{k, pos, rope_base, reinterpret_cast<float*>(kr + (size_t)B * M * Hkv * dh), kr};
     rope = &ra;
   }
 #define TG_ATTN_CASE(DHV, GV)                                                                                   \

@@ -525,11 +525,10 @@ int tg_gate_score_varlen(const void* resid, int dt, int B, int N, int d, const i
                            eps_row, W1, b1, h, w2, b2, score_raw, ws, ws_bytes, stream);
 }
 
-int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B, const int32_t* cu_seqlens, int Hq,
-                              int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
-                              const float* temp, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                              void* stream) {
-  const char* name = "tg_gated_attention_varlen";
+static int attention_varlen_common(const char* name, const void* q, const void* k, const void* v, int B,
+                                   const int32_t* cu_seqlens, int Hq, int Hkv, int d_h, const float* key_score,
+                                   const int32_t* pos, const float* gain, const float* temp, float sm_scale,
+                                   double rope_base, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (B <= 0 || !cu_seqlens) return fail(TG_EINVAL, "%s: B must be > 0 and cu_seqlens given", name);
   if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
   for (int b = 0; b < B; ++b)
@@ -540,8 +539,10 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B
   const size_t slots = tg::gated_attention_varlen_slots(B, cu_seqlens);
   if (slots == 0) return TG_OK;
   if (slots > 0x7FFFFFFF) return fail(TG_EINVAL, "%s: %zu padded rows exceed the 32-bit index range", name, slots);
-  // all sequences' V^T copies and key-score terms sit side by side
-  const size_t need = tg::gated_attention_workspace(1, (int)slots, Hq, Hkv, d_h);
+  // all sequences' V^T copies and key-score terms sit side by side (then,
+  // with the rotary embedding, the rotated k and the angle table by packed row)
+  const size_t need = rope_base > 0.0 ? tg::gated_attention_rope_varlen_workspace(B, cu_seqlens, Hq, Hkv, d_h)
+                                      : tg::gated_attention_workspace(1, (int)slots, Hq, Hkv, d_h);
   if (!ws || ws_bytes < need) return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
   // each sequence is validated as a batch of one; then the batch is launched
   for (int b = 0; b < B; ++b) {
@@ -551,14 +552,32 @@ int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B
     const int rc = gated_attention_common(
         name, static_cast<const uint16_t*>(q) + t0 * Hq * d_h, static_cast<const uint16_t*>(k) + t0 * Hkv * d_h,
         static_cast<const uint16_t*>(v) + t0 * Hkv * d_h, 1, m, Hq, Hkv, d_h, key_score + t0, pos + t0, gain, temp,
-        sm_scale, 0.0, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws, ws_bytes,
-        stream, false);
+        sm_scale, rope_base, static_cast<uint16_t*>(out) + t0 * Hq * d_h, lse ? lse + t0 * Hq : nullptr, ws,
+        ws_bytes, stream, false);
     if (rc != TG_OK) return rc;
   }
   return hip_status(tg::launch_gated_attention_varlen(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), B,
-      cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp, sm_scale, static_cast<uint16_t*>(out), lse, ws,
-      static_cast<hipStream_t>(stream)), name);
+      cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp, sm_scale, rope_base, static_cast<uint16_t*>(out), lse,
+      ws, static_cast<hipStream_t>(stream)), name);
+}
+
+int tg_gated_attention_varlen(const void* q, const void* k, const void* v, int B, const int32_t* cu_seqlens, int Hq,
+                              int Hkv, int d_h, const float* key_score, const int32_t* pos, const float* gain,
+                              const float* temp, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return attention_varlen_common("tg_gated_attention_varlen", q, k, v, B, cu_seqlens, Hq, Hkv, d_h, key_score, pos,
+                                 gain, temp, sm_scale, 0.0, out, lse, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_rope_varlen(const void* q, const void* k, const void* v, int B, const int32_t* cu_seqlens,
+                                   int Hq, int Hkv, int d_h, const float* key_score, const int32_t* pos,
+                                   const float* gain, const float* temp, float sm_scale, double rope_base, void* out,
+                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!(rope_base > 1.0) || !(rope_base < 1e300))
+    return fail(TG_EINVAL, "tg_gated_attention_rope_varlen: rope_base must be finite and > 1");
+  return attention_varlen_common("tg_gated_attention_rope_varlen", q, k, v, B, cu_seqlens, Hq, Hkv, d_h, key_score,
+                                 pos, gain, temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
 }
 
 int tg_gated_attention_backward_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,

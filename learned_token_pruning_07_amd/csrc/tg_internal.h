@@ -119,7 +119,7 @@ hipError_t launch_gated_attention(const uint16_t* q, const uint16_t* k, const ui
 // gated_attention_varlen_slots).
 hipError_t launch_gated_attention_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B,
                                          const int32_t* cu_seqlens, int Hq, int Hkv, int dh, const float* key_score,
-                                         const int32_t* pos, const float* gain, const float* temp, float sm_scale,
+                                         const int32_t* pos, const float* gain, const float* temp, float sm_scale, double rope_base,
                                          uint16_t* out, float* lse, void* ws, hipStream_t s);
 // sum over the sequences of the length rounded up to 64 key slots
 size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens);
@@ -128,6 +128,8 @@ size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens);
 // key-score terms; with the rotary embedding also the rotated q and k.
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh);
 size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh);
+// the rotary varying-length call's workspace (rope_base > 0)
+size_t gated_attention_rope_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv, int dh);
 
 // Backward of the token-gated attention: dq, dk, dv (bf16), the key-score
 // gradient [B, M] and the gain and temperature gradients [Hq] (fp32).

@@ -67,7 +67,7 @@ def test_version_and_workspace(lib):
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 4, 48) == 0   # d_h must divide d
     # the rotary variant adds the rotated q [B, M, Hq, d_h] and k [B, M, Hkv, d_h] (bf16); K = d_h
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 3341, 8 * 128, 16, 128) == \
-        3392 * (8 * 128 * 2 + (16 + 8) * 4) + 3341 * (16 + 8) * 128 * 2
+        3392 * (8 * 128 * 2 + (16 + 8) * 4) + 3341 * 128 * (2 * 8 + 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 64, 2 * 64, 4, 0) == 0   # d_h is required
 
 
