@@ -572,6 +572,34 @@ int tg_gated_attention_backward_varlen(const void* q, const void* k,
                                        size_t ws_bytes, void* stream);
 
 /*
+ * tg_gated_attention_rope_backward_varlen -- gradients of
+ * tg_gated_attention_rope_varlen (q and k passed un-rotated, as to that
+ * call; every packed row turned by its own original position pos[t],
+ * Appendix C.4).  d_q and d_k are with respect to the un-rotated q and k
+ * (the transposed rotation of the gradients with respect to the rotated
+ * ones, as tg_gated_attention_rope_backward).  The workspace is at least
+ * tg_workspace_size(TG_OP_GATED_ATTENTION_ROPE_BACKWARD, 1, T + 63 * B,
+ * Hkv * d_h, Hq, d_h) bytes, T = cu_seqlens[B].  Each sequence's results
+ * equal tg_gated_attention_rope_backward's for that sequence alone (a batch
+ * of one), bit for bit.  Otherwise as tg_gated_attention_backward_varlen.
+ */
+int tg_gated_attention_rope_backward_varlen(const void* q, const void* k,
+                                            const void* v, const void* out,
+                                            const float* lse,
+                                            const void* d_out, int B,
+                                            const int32_t* cu_seqlens, int Hq,
+                                            int Hkv, int d_h,
+                                            const float* key_score,
+                                            const int32_t* pos,
+                                            const float* gain,
+                                            const float* temp, float sm_scale,
+                                            double rope_base, void* d_q,
+                                            void* d_k, void* d_v,
+                                            float* d_key_score, float* d_gain,
+                                            float* d_temp, void* ws,
+                                            size_t ws_bytes, void* stream);
+
+/*
  * tg_kv_cache_prune -- post-prefill pruning of the KV cache of the layers at
  * and below the gate (paper, Section 5, "Implementation and timing", and
  * Appendix B: optionally, once prefill completes, those layers keep only the

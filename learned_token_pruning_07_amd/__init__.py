@@ -29,7 +29,7 @@ EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
             "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_gate_select_padded",
             "tg_gated_attention_padded", "tg_gate_fold_weights", "tg_gate_score_folded",
-            "tg_gated_attention_rope_varlen", "tg_workspace_size",
+            "tg_gated_attention_rope_varlen", "tg_gated_attention_rope_backward_varlen", "tg_workspace_size",
             "tg_last_error", "tg_version")
 
 _lib = None
@@ -74,6 +74,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_topk_select_span.argtypes = [vp, i, i, i, i, i, vp, vp, sz, vp]
     lib.tg_gated_attention_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f,
                                                        vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tg_gated_attention_rope_backward_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp,
+                                                            f, ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_gated_attention_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_gated_attention_rope_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, ctypes.c_double,
                                                    vp, vp, vp, sz, vp]
@@ -92,7 +94,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen",
                  "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc",
                  "tg_gate_select_padded", "tg_gated_attention_padded", "tg_gate_fold_weights",
-                 "tg_gate_score_folded", "tg_gated_attention_rope_varlen"):
+                 "tg_gate_score_folded", "tg_gated_attention_rope_varlen",
+                 "tg_gated_attention_rope_backward_varlen"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -557,10 +560,13 @@ def tg_gated_attention_rope_varlen(q, k, v, cu_seqlens, key_score, pos, gain, te
 
 
 def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key_score, pos, gain, temp,
-                                       sm_scale: float | None = None, ws=None, stream=None):
+                                       sm_scale: float | None = None, ws=None, stream=None,
+                                       rope_base: float | None = None):
     """Gradients of :func:`tg_gated_attention_varlen` (same packed layouts;
     ``lse`` as it wrote it).  Returns ``(d_q, d_k, d_v, d_key_score, d_gain
-    [B, Hq], d_temp [B, Hq])``: per-sequence gain and temperature gradients."""
+    [B, Hq], d_temp [B, Hq])``: per-sequence gain and temperature gradients.
+    With ``rope_base`` the gradients of the rotary variant (q and k passed
+    un-rotated)."""
     lib = load_library()
     T, Hq, dh = q.shape
     Hkv = k.shape[1]
@@ -580,13 +586,25 @@ def tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty(T, device=dev),
              torch.empty((B, Hq), device=dev), torch.empty((B, Hq), device=dev)]
     if ws is None:  # every sequence padded to 64 rows, side by side
-        ws = attention_backward_workspace(1, max(T + 63 * B, 1), Hq, Hkv, dh, dev)
+        wsf = attention_backward_workspace if rope_base is None else attention_rope_backward_workspace
+        ws = wsf(1, max(T + 63 * B, 1), Hq, Hkv, dh, dev)
     cu_arr = (ctypes.c_int32 * len(cu))(*cu)
-    _check(lib.tg_gated_attention_backward_varlen(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
-        _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale), *[_ptr(g_) for g_ in grads], _ptr(ws), ws.numel(),
-        _stream(stream)))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), B, cu_arr, Hq, Hkv, dh, _ptr(key_score),
+            _ptr(pos), _ptr(gain), _ptr(temp), float(sm_scale))
+    tail = (*[_ptr(g_) for g_ in grads], _ptr(ws), ws.numel(), _stream(stream))
+    if rope_base is None:
+        _check(lib.tg_gated_attention_backward_varlen(*head, *tail))
+    else:
+        _check(lib.tg_gated_attention_rope_backward_varlen(*head, float(rope_base), *tail))
     return tuple(grads)
+
+
+def tg_gated_attention_rope_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key_score, pos, gain, temp,
+                                            rope_base: float, sm_scale: float | None = None, ws=None, stream=None):
+    """Gradients of :func:`tg_gated_attention_rope_varlen` (q and k passed
+    un-rotated); outputs as :func:`tg_gated_attention_backward_varlen`."""
+    return tg_gated_attention_backward_varlen(q, k, v, out, lse, d_out, cu_seqlens, key_score, pos, gain, temp,
+                                              sm_scale, ws=ws, stream=stream, rope_base=rope_base)
 
 
 def attention_workspace(B: int, M: int, Hq: int, Hkv: int, dh: int, device="cuda") -> torch.Tensor:

@@ -67,6 +67,9 @@ size_t rope_ws_offset(int B, int M, int Hq, int Hkv, int dh) {
   (void)dh;
   return (base_ws_bytes(B, M, Hq, Hkv) + 15) / 16 * 16;
 }
+size_t rope_varlen_ws_offset(int B, const int32_t* cu_seqlens, int Hq, int Hkv) {
+  return (gated_attention_backward_varlen_workspace(B, cu_seqlens, Hq, Hkv) + 15) / 16 * 16;
+}
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
@@ -842,13 +845,15 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   return hipGetLastError();
 }
 
-// One launch of each kernel over the sequences of a table (no rotary variant).
+// One launch of each kernel over the sequences of a table.  With dq32 and
+// dk32 set (the rotary variant, q and k already rotated), dq and dk go out
+// in fp32 with respect to the rotated q and k.
 template <int DH, int G>
 hipError_t launch_bwd_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                                const float* lse, const uint16_t* dout, const BwdSeqTable& st, int Hq, int Hkv,
                                const float* ks, const int32_t* pos, const float* gain, const float* temp,
                                float sm_scale, uint16_t* dq, uint16_t* dk, uint16_t* dv, float* db, float* dgain,
-                               float* dtemp, size_t slots, void* ws, hipStream_t s) {
+                               float* dtemp, size_t slots, void* ws, float* dq32, float* dk32, hipStream_t s) {
   const size_t rn = (size_t)Hq * slots;
   float* rowc = static_cast<float*>(ws);
   float* rowl = rowc + rn;
@@ -863,11 +868,19 @@ hipError_t launch_bwd_varlen_t(const uint16_t* q, const uint16_t* k, const uint1
                        sm_scale, 0, 0, Hq, rowc, rowl, rowD, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int ta = nblk * Hkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3(ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc, rowl,
-                       rowD, ks, gain, 0, 0, Hq, Hkv, 0, ta, dk, dv, dbp, gpart, tpart, st);
+    if (dk32 != nullptr)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, true>), dim3(ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
+                         rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, ta, dk32, dv, dbp, gpart, tpart, st);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3(ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
+                         rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, ta, dk, dv, dbp, gpart, tpart, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                       rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq, st);
+    if (dq32 != nullptr)
+      hipLaunchKernelGGL((bwd_dq_kernel<DH, G, true>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq32, st);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
+                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)(((size_t)nblk * kPB + kBwdThreads - 1) / kBwdThreads) + st.n;
@@ -899,16 +912,49 @@ size_t gated_attention_backward_varlen_workspace(int B, const int32_t* cu_seqlen
   return slots * (size_t)(12 * Hq + 4 * Hkv) + 8 * (slots / kKB) * Hq;
 }
 
+// ... rounded up to 16 bytes, then the rotated q and k (bf16) and the fp32
+// gradients with respect to them, by packed row
+size_t gated_attention_rope_backward_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv, int dh) {
+  return rope_varlen_ws_offset(B, cu_seqlens, Hq, Hkv) + (size_t)cu_seqlens[B] * (Hq + Hkv) * dh * (2 + 4);
+}
+
 hipError_t launch_gated_attention_backward_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                   const uint16_t* out, const float* lse, const uint16_t* d_out, int B,
                                                   const int32_t* cu_seqlens, int Hq, int Hkv, int dh,
                                                   const float* key_score, const int32_t* pos, const float* gain,
-                                                  const float* temp, float sm_scale, uint16_t* dq, uint16_t* dk,
-                                                  uint16_t* dv, float* d_key_score, float* d_gain, float* d_temp,
-                                                  void* ws, hipStream_t s) {
+                                                  const float* temp, float sm_scale, double rope_base, uint16_t* dq,
+                                                  uint16_t* dk, uint16_t* dv, float* d_key_score, float* d_gain,
+                                                  float* d_temp, void* ws, hipStream_t s) {
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4) return hipErrorInvalidValue;
+  if (dh != 64 && dh != 128) return hipErrorInvalidValue;
   const int BQ = 32 * (4 / G);
+  // rotary variant: every packed row of q and k turned by its own position
+  // (the rows of all sequences at once, as one row block of T rows), the
+  // kernels on the rotated copies with fp32 gradients, then the transposed
+  // rotation of those
+  const size_t T = (size_t)cu_seqlens[B];
+  const bool rope = rope_base > 0.0 && T > 0;
+  uint16_t *qr = nullptr, *kr = nullptr;
+  float *dq32 = nullptr, *dk32 = nullptr;
+  const dim3 rope_grid((unsigned)((T + kPB - 1) / kPB), Hkv, 1);
+  if (rope) {
+    unsigned char* rws = static_cast<unsigned char*>(ws) + rope_varlen_ws_offset(B, cu_seqlens, Hq, Hkv);
+    qr = reinterpret_cast<uint16_t*>(rws);
+    kr = qr + T * Hq * dh;
+    dq32 = reinterpret_cast<float*>(kr + T * Hkv * dh);
+    dk32 = dq32 + T * Hq * dh;
+    if (dh == 128)
+      hipLaunchKernelGGL((bwd_rope_kernel<128, false>), rope_grid, dim3(kBwdThreads), 0, s, q, k, pos, rope_base,
+                         (int)T, Hq, Hkv, qr, kr);
+    else
+      hipLaunchKernelGGL((bwd_rope_kernel<64, false>), rope_grid, dim3(kBwdThreads), 0, s, q, k, pos, rope_base,
+                         (int)T, Hq, Hkv, qr, kr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    q = qr;
+    k = kr;
+  }
   // every sequence (the empty ones get zero gain and temperature gradients), longest first
   std::vector<int> order(B);
   for (int b = 0; b < B; ++b) order[b] = b;
@@ -943,7 +989,7 @@ hipError_t launch_gated_attention_backward_varlen(const uint16_t* q, const uint1
 #define TG_BWD_VARLEN_CASE(DHV, GV)                                                                              \
   if (dh == DHV && G == GV)                                                                                      \
     e = launch_bwd_varlen_t<DHV, GV>(q, k, v, out, lse, d_out, st, Hq, Hkv, key_score, pos, gain, temp, sm_scale, \
-                                     dq, dk, dv, d_key_score, d_gain, d_temp, slots, ws, s);
+                                     dq, dk, dv, d_key_score, d_gain, d_temp, slots, ws, dq32, dk32, s);
     TG_BWD_VARLEN_CASE(128, 2)
     TG_BWD_VARLEN_CASE(128, 1)
     TG_BWD_VARLEN_CASE(128, 4)
@@ -952,6 +998,15 @@ hipError_t launch_gated_attention_backward_varlen(const uint16_t* q, const uint1
     TG_BWD_VARLEN_CASE(64, 4)
 #undef TG_BWD_VARLEN_CASE
     if (e != hipSuccess) return e;
+  }
+  if (rope) {
+    if (dh == 128)
+      hipLaunchKernelGGL((bwd_rope_kernel<128, true>), rope_grid, dim3(kBwdThreads), 0, s, dq32, dk32, pos,
+                         rope_base, (int)T, Hq, Hkv, dq, dk);
+    else
+      hipLaunchKernelGGL((bwd_rope_kernel<64, true>), rope_grid, dim3(kBwdThreads), 0, s, dq32, dk32, pos, rope_base,
+                         (int)T, Hq, Hkv, dq, dk);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

@@ -580,21 +580,26 @@ int tg_gated_attention_rope_varlen(const void* q, const void* k, const void* v, 
                                  pos, gain, temp, sm_scale, rope_base, out, lse, ws, ws_bytes, stream);
 }
 
-int tg_gated_attention_backward_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
-                                       const void* d_out, int B, const int32_t* cu_seqlens, int Hq, int Hkv, int d_h,
-                                       const float* key_score, const int32_t* pos, const float* gain,
-                                       const float* temp, float sm_scale, void* d_q, void* d_k, void* d_v,
-                                       float* d_key_score, float* d_gain, float* d_temp, void* ws, size_t ws_bytes,
-                                       void* stream) {
-  const char* name = "tg_gated_attention_backward_varlen";
+static int attention_backward_varlen_common(const char* name, const void* q, const void* k, const void* v,
+                                            const void* out, const float* lse, const void* d_out, int B,
+                                            const int32_t* cu_seqlens, int Hq, int Hkv, int d_h,
+                                            const float* key_score, const int32_t* pos, const float* gain,
+                                            const float* temp, float sm_scale, double rope_base, void* d_q,
+                                            void* d_k, void* d_v, float* d_key_score, float* d_gain, float* d_temp,
+                                            void* ws, size_t ws_bytes, void* stream) {
   if (B <= 0 || !cu_seqlens) return fail(TG_EINVAL, "%s: B must be > 0 and cu_seqlens given", name);
   if (cu_seqlens[0] != 0) return fail(TG_EINVAL, "%s: cu_seqlens[0] must be 0", name);
   for (int b = 0; b < B; ++b)
     if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
   if ((size_t)cu_seqlens[B] + 63 * (size_t)B > 0x7FFFFFFF)
     return fail(TG_EINVAL, "%s: the padded rows exceed the 32-bit index range", name);
-  // every sequence's row constants and partials sit side by side
-  const size_t need = tg::gated_attention_backward_varlen_workspace(B, cu_seqlens, Hq, Hkv);
+  if (rope_base > 0.0 && (d_h != 64 && d_h != 128))
+    return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
+  // every sequence's row constants and partials sit side by side (then, for
+  // the rotary variant, the rotated q and k and their fp32 gradients)
+  const size_t need = rope_base > 0.0 && cu_seqlens[B] > 0
+                          ? tg::gated_attention_rope_backward_varlen_workspace(B, cu_seqlens, Hq, Hkv, d_h)
+                          : tg::gated_attention_backward_varlen_workspace(B, cu_seqlens, Hq, Hkv);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
   if (!d_gain || !d_temp) return fail(TG_EINVAL, "%s: null pointer argument", name);
@@ -616,10 +621,34 @@ int tg_gated_attention_backward_varlen(const void* q, const void* k, const void*
                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                         static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(out), lse,
                         static_cast<const uint16_t*>(d_out), B, cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp,
-                        sm_scale, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
+                        sm_scale, rope_base, static_cast<uint16_t*>(d_q), static_cast<uint16_t*>(d_k),
                         static_cast<uint16_t*>(d_v), d_key_score, d_gain, d_temp, ws,
                         static_cast<hipStream_t>(stream)),
                     name);
+}
+
+int tg_gated_attention_backward_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                       const void* d_out, int B, const int32_t* cu_seqlens, int Hq, int Hkv, int d_h,
+                                       const float* key_score, const int32_t* pos, const float* gain,
+                                       const float* temp, float sm_scale, void* d_q, void* d_k, void* d_v,
+                                       float* d_key_score, float* d_gain, float* d_temp, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  return attention_backward_varlen_common("tg_gated_attention_backward_varlen", q, k, v, out, lse, d_out, B,
+                                          cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp, sm_scale, 0.0, d_q,
+                                          d_k, d_v, d_key_score, d_gain, d_temp, ws, ws_bytes, stream);
+}
+
+int tg_gated_attention_rope_backward_varlen(const void* q, const void* k, const void* v, const void* out,
+                                            const float* lse, const void* d_out, int B, const int32_t* cu_seqlens,
+                                            int Hq, int Hkv, int d_h, const float* key_score, const int32_t* pos,
+                                            const float* gain, const float* temp, float sm_scale, double rope_base,
+                                            void* d_q, void* d_k, void* d_v, float* d_key_score, float* d_gain,
+                                            float* d_temp, void* ws, size_t ws_bytes, void* stream) {
+  if (!(rope_base > 1.0) || !(rope_base < 1e300))
+    return fail(TG_EINVAL, "tg_gated_attention_rope_backward_varlen: rope_base must be finite and > 1");
+  return attention_backward_varlen_common("tg_gated_attention_rope_backward_varlen", q, k, v, out, lse, d_out, B,
+                                          cu_seqlens, Hq, Hkv, d_h, key_score, pos, gain, temp, sm_scale, rope_base,
+                                          d_q, d_k, d_v, d_key_score, d_gain, d_temp, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

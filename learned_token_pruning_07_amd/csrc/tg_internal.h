@@ -144,15 +144,17 @@ size_t gated_attention_backward_workspace(int B, int M, int Hq, int Hkv, int dh)
 // Packed sequences (host cu_seqlens, B + 1 offsets): one launch of each kernel
 // per 64 sequences, every sequence's row constants and partials side by side
 // in the workspace (gated_attention_backward_varlen_workspace bytes); d_gain
-// and d_temp [B, Hq].
+// and d_temp [B, Hq].  rope_base > 0: q and k rotated by their positions
+// first (gated_attention_rope_backward_varlen_workspace bytes).
 hipError_t launch_gated_attention_backward_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                   const uint16_t* out, const float* lse, const uint16_t* d_out, int B,
                                                   const int32_t* cu_seqlens, int Hq, int Hkv, int dh,
                                                   const float* key_score, const int32_t* pos, const float* gain,
-                                                  const float* temp, float sm_scale, uint16_t* dq, uint16_t* dk,
-                                                  uint16_t* dv, float* d_key_score, float* d_gain, float* d_temp,
-                                                  void* ws, hipStream_t s);
+                                                  const float* temp, float sm_scale, double rope_base, uint16_t* dq,
+                                                  uint16_t* dk, uint16_t* dv, float* d_key_score, float* d_gain,
+                                                  float* d_temp, void* ws, hipStream_t s);
 size_t gated_attention_backward_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv);
+size_t gated_attention_rope_backward_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv, int dh);
 size_t gated_attention_rope_backward_workspace(int B, int M, int Hq, int Hkv, int dh);
 
 // Row gather of the K and V caches of n_layers layers to the kept set.

@@ -389,3 +389,27 @@ def test_fold_weights_and_folded_scorer_validate(lib):
     assert score(r=65) == tgb.TG_EINVAL
     assert score(w=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
     assert score(d=100) == tgb.TG_EUNSUPPORTED
+
+
+def test_attention_rope_backward_varlen_validation(lib):
+    """The rotary packed backward refuses a bad base and sizes its workspace as
+    the packed backward's (each sequence padded to 64 rows) rounded to 16
+    bytes, then T rows of rotated q and k (bf16) and their fp32 gradients;
+    the documented tg_workspace_size bound covers it."""
+    cu = (ctypes.c_int32 * 3)(0, 100, 200)
+    Hq, Hkv, dh = 16, 8, 128
+
+    def call(base=1e6, ws_bytes=1 << 30, dh_=dh):
+        return lib.tg_gated_attention_rope_backward_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, cu, Hq, Hkv, dh_,
+                                                           FAKE, FAKE, FAKE, FAKE, 0.088, base, FAKE, FAKE, FAKE,
+                                                           FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert call(base=0.5) == tgb.TG_EINVAL and "rope_base" in _err(lib)
+    assert call(base=float("inf")) == tgb.TG_EINVAL
+    assert call(dh_=96) == tgb.TG_EUNSUPPORTED and "d_h" in _err(lib)
+    slots = 256
+    plain = slots * (12 * Hq + 4 * Hkv) + 8 * (slots // 64) * Hq
+    need = (plain + 15) // 16 * 16 + 200 * (Hq + Hkv) * dh * 6
+    assert call(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    bound = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE_BACKWARD, 1, 200 + 63 * 2, Hkv * dh, Hq, dh)
+    assert bound >= need

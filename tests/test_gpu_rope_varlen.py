@@ -15,6 +15,7 @@ import torch
 import oracle
 import learned_token_pruning_07_amd as tg
 from learned_token_pruning_07_amd import workloads as wl
+import test_gpu_backward as bwd
 from _gpu_util import DEV, TOL_BF16, TOL_LSE, assert_close, dev, dev_bits, host_bits, poison_f32, say
 
 pytestmark = pytest.mark.gpu
@@ -67,3 +68,59 @@ def test_rope_varlen_equals_per_sequence_calls(dh, Hq, Hkv, base):
         e2 = assert_close(l1.cpu().numpy(), L, TOL_LSE, f"sequence {i} lse")
         say(f"  sequence {i} (M={s1 - s0}): bit-identical to the single-sequence call; max |err| O {e1:.3g} "
             f"lse {e2:.3g}")
+
+
+@pytest.mark.parametrize("dh,Hq,Hkv,base", [(128, 4, 2, 1e6), (64, 8, 2, 1e4)])
+def test_rope_varlen_backward_equals_per_sequence_calls(dh, Hq, Hkv, base):
+    """The packed rotary backward gives, per sequence, the batch-of-one rotary
+    backward bit for bit (d_q and d_k with respect to the un-rotated inputs;
+    gain and temperature gradients per row, zero for an empty sequence);
+    every 4th sequence is held to the oracle's rotary backward."""
+    rng = np.random.default_rng(dh + 3 * Hq)
+    lens = list(rng.integers(0, 301, size=66)) + [0, 1, 31, 32, 33, 64, 65, 0]
+    rng.shuffle(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(int).tolist()
+    T = cu[-1]
+    say(f"rope varlen backward dh={dh} Hq={Hq} Hkv={Hkv} base={base:g} sequences={len(lens)} rows={T}")
+    a = wl.attn_case(M=T, Hq=Hq, Hkv=Hkv, dh=dh, seed=dh + 11, r_zero=0)
+    q, k, v = (dev_bits(x[0]) for x in (a.q, a.k, a.v))
+    b = rng.standard_normal(T).astype(np.float32)
+    # original positions up to 16 x each kept length (sparse kept sets of long prompts)
+    pos = np.concatenate([np.sort(rng.choice(16 * max(n, 1), n, replace=False)) for n in lens]).astype(np.int32)
+    dO_bits = wl.f32_to_bf16_bits(rng.standard_normal((T, Hq, dh), dtype=np.float32))
+    gain, temp = dev(a.gain), dev(a.temp)
+    out, lse = tg.tg_gated_attention_rope_varlen(q, k, v, cu, dev(b), dev(pos), gain, temp, base, a.sm_scale,
+                                                 lse=torch.empty(T * Hq, dtype=torch.float32, device=DEV))
+    g = tg.tg_gated_attention_rope_backward_varlen(q, k, v, out, lse, dev_bits(dO_bits), cu, dev(b), dev(pos), gain,
+                                                   temp, base, a.sm_scale)
+    torch.cuda.synchronize()
+    checked = 0
+    for i, m in enumerate(lens):
+        s0, s1 = cu[i], cu[i + 1]
+        if m == 0:
+            assert torch.all(g[4][i] == 0) and torch.all(g[5][i] == 0)
+            continue
+        one = tg.tg_gated_attention_rope_backward(
+            q[None, s0:s1].contiguous(), k[None, s0:s1].contiguous(), v[None, s0:s1].contiguous(),
+            out[None, s0:s1].contiguous(), lse[s0 * Hq:s1 * Hq].reshape(1, Hq, m).contiguous(),
+            dev_bits(dO_bits[None, s0:s1]), dev(b[None, s0:s1]), dev(pos[None, s0:s1]), gain, temp, base,
+            a.sm_scale)
+        for n_, x, y in zip(("d_q", "d_k", "d_v", "d_key_score", "d_gain", "d_temp"),
+                            (g[0][s0:s1], g[1][s0:s1], g[2][s0:s1], g[3][s0:s1], g[4][i], g[5][i]),
+                            (one[0][0], one[1][0], one[2][0], one[3][0], one[4], one[5])):
+            assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), \
+                f"sequence {i} (M={m}) {n_}"
+        if i % 4 == 0 and m >= 16:
+            O_bits = host_bits(out[None, s0:s1])
+            L = lse[s0 * Hq:s1 * Hq].reshape(1, Hq, m).cpu().numpy()
+            args = (a.q[:, s0:s1], a.k[:, s0:s1], a.v[:, s0:s1], b[None, s0:s1], pos[None, s0:s1], a.gain, a.temp,
+                    a.sm_scale)
+            want = oracle.gated_attention_rope_backward(*args, base, O_bits, L, dO_bits[None, s0:s1])
+            qr = oracle.bf16_round(oracle.rope(args[0], args[4], base))
+            kr = oracle.bf16_round(oracle.rope(args[1], args[4], base))
+            l1 = list(oracle.gated_attention_backward_l1(qr, kr, *args[2:], O_bits, L, dO_bits[None, s0:s1]))
+            l1[0], l1[1] = bwd._pair_sum(l1[0]), bwd._pair_sum(l1[1])
+            got = [x[None] for x in (g[0][s0:s1], g[1][s0:s1], g[2][s0:s1], g[3][s0:s1])] + [g[4][i], g[5][i]]
+            bwd._check(got, want, l1, f"rope varlen sequence {i} (M={m})")
+            checked += 1
+    assert checked >= 3
