@@ -301,7 +301,13 @@ int tg_gate_score_varlen(const void* resid, int dt, int B, int N, int d,
  *   score [B, N], keep [B, N]: as tg_gate_select (per row)
  *   kept_idx [cu_kept[B]] int32, resid_out [cu_kept[B], d], score_out
  *                    [cu_kept[B]] fp32: packed outputs
- * Rows of up to 32768 tokens (one workgroup per row); no workspace.
+ *   ws, ws_bytes     tg_workspace_size(TG_OP_GATE_SELECT, B, N, 0, 0, 0)
+ *                    bytes (none, ws may be NULL, when N <= 32768)
+ * A row of up to 32768 tokens is selected by one workgroup; a longer one
+ * (rows of any length <= N) by the sliced normalisation, the chunked
+ * selection and the compaction scan of the separate calls.  Either way each
+ * row's results equal tg_gate_select_span's on that row alone (its first
+ * seq_len[b] tokens), bit for bit.
  */
 int tg_gate_select_varlen(const float* score_raw, int B, int N,
                           const int32_t* seq_len, const int32_t* span_begin,
@@ -309,7 +315,8 @@ int tg_gate_select_varlen(const float* score_raw, int B, int N,
                           const int32_t* cu_kept, int max_kept, float eps_seq,
                           const void* resid, int dt, int d, float* score,
                           uint8_t* keep, int32_t* kept_idx, void* resid_out,
-                          float* score_out, void* stream);
+                          float* score_out, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * tg_gated_attention -- token-gated causal GQA attention over the kept set

@@ -80,7 +80,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gated_attention_rope_varlen.argtypes = [vp, vp, vp, i, vp, i, i, i, vp, vp, vp, vp, f, ctypes.c_double,
                                                    vp, vp, vp, sz, vp]
     lib.tg_gate_score_varlen.argtypes = [vp, i, i, i, i, vp, vp, i, vp, f, vp, vp, i, vp, vp, vp, vp, sz, vp]
-    lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp]
+    lib.tg_gate_select_varlen.argtypes = [vp, i, i, vp, vp, vp, vp, vp, i, f, vp, i, i, vp, vp, vp, vp, vp, vp, sz,
+                                          vp]
     lib.tg_gate_select_span.argtypes = [vp, i, i, i, i, f, i, vp, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.tg_workspace_size.restype = sz
@@ -481,11 +482,12 @@ def tg_gate_score_varlen(resid, span_begin, span_end, norm_w, W1, b1, w2, b2, ep
 
 
 def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, eps_seq: float = 1e-6, score=None,
-                          keep=None, stream=None):
+                          keep=None, ws=None, stream=None):
     """Gate selection of a batch of sequences of different lengths, spans and
     budgets (per-row host lists).  Returns ``(kept_idx, resid_out, score_out,
     keep, score, cu_kept)`` with the kept rows packed: row b's are
-    ``cu_kept[b] .. cu_kept[b+1]-1`` (``cu_kept`` a host list)."""
+    ``cu_kept[b] .. cu_kept[b+1]-1`` (``cu_kept`` a host list).  Rows longer
+    than 32768 tokens use a workspace (allocated here unless ``ws`` is given)."""
     lib = load_library()
     _need(resid, "resid")
     B, N, d = resid.shape
@@ -505,9 +507,12 @@ def tg_gate_select_varlen(score_raw, resid, seq_len, span_begin, span_end, K, ep
     kept_idx = torch.empty((max(T, 1),), dtype=torch.int32, device=dev)
     resid_out = torch.empty((max(T, 1), d), dtype=resid.dtype, device=dev)
     score_out = torch.empty((max(T, 1),), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = int(lib.tg_workspace_size(TG_OP_GATE_SELECT, B, N, 0, 0, 0))
+        ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
     _check(lib.tg_gate_select_varlen(_ptr(score_raw), B, N, *[_ptr(t) for t in rows], max(Ms) if Ms else 0, eps_seq,
                                      _ptr(resid), _dt(resid), d, _ptr(score), _ptr(keep), _ptr(kept_idx),
-                                     _ptr(resid_out), _ptr(score_out), _stream(stream)))
+                                     _ptr(resid_out), _ptr(score_out), _ptr(ws), ws.numel(), _stream(stream)))
     return kept_idx[:T], resid_out[:T], score_out[:T], keep, score, cu
 
 

@@ -44,18 +44,29 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s_wave) 
   return t;
 }
 
+// With vr.len set: rows of a varying-length batch longer than
+// kVarlenOneGroupRow tokens only, row b writing at most cu_kept[b + 1] -
+// cu_kept[b] entries from cu_kept[b] on.
 __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_t* __restrict__ keep,
                                                                     const float* __restrict__ score, int N,
-                                                                    int M, int32_t* __restrict__ kept_idx,
+                                                                    int M, VarlenRows vr,
+                                                                    int32_t* __restrict__ kept_idx,
                                                                     float* __restrict__ score_out) {
   __shared__ __attribute__((aligned(16))) uint32_t s_wave[kScanThreads / 64];
   const int b = blockIdx.y;
-  const uint8_t* kp = keep + (size_t)b * N;
-  const float* sc = score + (size_t)b * N;
-  int32_t* ki = kept_idx + (size_t)b * M;
-  float* so = score_out + (size_t)b * M;
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * kScanChunk;
+  size_t out0 = (size_t)b * M;
+  if (vr.len != nullptr) {
+    const RowSpec rs = varlen_row(vr, b, N);
+    if (rs.len <= kVarlenOneGroupRow || c0 >= rs.len) return;  // (no kept token past the length)
+    out0 = (size_t)max(vr.cu_kept[b], 0);
+    M = vr.cu_kept[b + 1] - vr.cu_kept[b];
+  }
+  const uint8_t* kp = keep + (size_t)b * N;
+  const float* sc = score + (size_t)b * N;
+  int32_t* ki = kept_idx + out0;
+  float* so = score_out + out0;
 
   // this chunk: kScanItems consecutive tokens per thread (requested first, so
   // their latency overlaps the count below)
@@ -219,10 +230,18 @@ hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, con
                           hipStream_t s) {
   if (M <= 0) return hipSuccess;
   hipLaunchKernelGGL(compact_scan_kernel, dim3((N + kScanChunk - 1) / kScanChunk, B), dim3(kScanThreads), 0, s,
-                     keep, score, N, M, kept_idx, score_out);
+                     keep, score, N, M, VarlenRows{}, kept_idx, score_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_compact_gather(resid, row_bytes, B, N, M, kept_idx, resid_out, s);
+}
+
+hipError_t launch_compact_scan_long_rows(const uint8_t* keep, const float* score, int B, int N, VarlenRows vr,
+                                         int32_t* kept_idx, float* score_out, hipStream_t s) {
+  if (N <= kVarlenOneGroupRow) return hipSuccess;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3((N + kScanChunk - 1) / kScanChunk, B), dim3(kScanThreads), 0, s,
+                     keep, score, N, 0, vr, kept_idx, score_out);
+  return hipGetLastError();
 }
 
 }  // namespace tg

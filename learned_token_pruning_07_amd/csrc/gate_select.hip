@@ -14,7 +14,10 @@
 //    then the kept prunable tokens ascending, then the non-prunable tokens
 //    after the span).
 //  * the residual row gather of tg_compact, given kept_idx.
-// Longer rows run the three separate calls.
+// Longer rows run the three separate calls; in a varying-length batch, the
+// rows longer than 32768 tokens take their multi-workgroup kernels (which
+// skip the short rows) after the one-workgroup kernel (which skips the long
+// ones).
 #include "select_device.h"
 #include "tg_device.h"
 #include "tg_internal.h"
@@ -25,6 +28,7 @@ namespace {
 constexpr int kThreads = sel::kRowThreads;
 constexpr int kVec = sel::kRowVec;
 constexpr int kItems = 16;  // consecutive prunable tokens per thread in the final pass
+static_assert(sel::kRowChunk == kVarlenOneGroupRow, "the one-workgroup row limit");
 
 // score_raw and score may alias: every raw score is read before the
 // reduction's barriers, and nothing reads score_raw after them.
@@ -48,10 +52,12 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
   const int b = blockIdx.x;
   int Nb = N, r = r_all, p1 = p1_all, K = K_all;
   if (vr.len != nullptr) {
-    Nb = min(max(vr.len[b], 0), N);
-    p1 = min(max(vr.span_end[b], 0), Nb);
-    r = min(max(vr.span_begin[b], 0), p1);
-    K = max(vr.K[b], 0);
+    const RowSpec rs = varlen_row(vr, b, N);
+    if (rs.len > kVarlenOneGroupRow) return;  // a longer row takes the sliced kernels
+    Nb = rs.len;
+    p1 = rs.p1;
+    r = rs.r;
+    K = rs.K;
   } else if (vr.K != nullptr) {
     // budget from the device, cut so that the kept set fits the pad rows
     K = min(max(vr.K[b], 0), vr.pad - (N - (p1 - r)));
@@ -107,6 +113,8 @@ __global__ __launch_bounds__(kThreads) void gate_select_kernel(const float* scor
     }
   }
 
+  // padding of a short row in a batch wider than one workgroup's chunk
+  for (int j = kThreads * kVec * 4 + tid; j < N; j += kThreads) y[j] = 0.0f;
   __syncthreads();  // every key and the first histogram are in LDS; y is written
   // the non-prunable tokens before the span are kept first, those after it
   // last (ranks r + K' ...), in order (their scores are 0)
@@ -250,12 +258,24 @@ hipError_t launch_gate_select_padded(const float* score_raw, int B, int N, int r
 
 hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,
                                      const void* resid, size_t row_bytes, float* score, uint8_t* keep,
-                                     int32_t* kept_idx, void* resid_out, float* score_kept, hipStream_t s) {
-  if (N > sel::kRowChunk) return hipErrorInvalidValue;
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, void* ws,
+                                     hipStream_t s) {
+  // rows of up to 32768 tokens: one workgroup each (the longer rows return at once)
   hipLaunchKernelGGL(gate_select_kernel, dim3(B), dim3(kThreads), 0, s, score_raw, N, 0, N, eps, 0, vr, score, keep,
                      kept_idx, score_kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (N > sel::kRowChunk) {
+    // the longer rows: sliced normalisation, chunked selection, compaction
+    // scan (each kernel skips the short rows), as the separate calls take
+    // them for a uniform batch
+    e = launch_seq_rmsnorm_long_rows(score_raw, B, N, vr, eps, score, ws, s);
+    if (e != hipSuccess) return e;
+    e = launch_topk_select_long_rows(score, B, N, vr, keep, ws, s);
+    if (e != hipSuccess) return e;
+    e = launch_compact_scan_long_rows(keep, score, B, N, vr, kept_idx, score_kept, s);
+    if (e != hipSuccess) return e;
+  }
   return launch_compact_gather_varlen(resid, row_bytes, B, N, vr.cu_kept, max_kept, kept_idx, resid_out, s);
 }
 

@@ -23,6 +23,7 @@ using sel::load_scores;
 constexpr int kThreads = sel::kRowThreads;
 constexpr int kVec = sel::kRowVec;           // 16-byte loads per thread
 constexpr int kChunk = sel::kRowChunk;      // 32768 scores: the single-workgroup limit
+static_assert(kChunk == kVarlenOneGroupRow, "the one-workgroup row limit");
 
 // Rows of up to kChunk scores.  `in` and `out` may alias (in-place
 // normalisation): every score is read before the barriers of the reduction.
@@ -70,11 +71,19 @@ __device__ __forceinline__ double block_sum_f64(double v, double* s_part) {
   return t;
 }
 
-// partial[b, c] = sum of squares of the prunable scores in slice c of row b
+// partial[b, c] = sum of squares of the prunable scores in slice c of row b.
+// With vr.len set, row b takes its own span, and a row of up to
+// kVarlenOneGroupRow tokens is left to the one-workgroup kernel.
 __global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* in, int N, int r, int p1,
-                                                                  double* __restrict__ partial) {
+                                                                  VarlenRows vr, double* __restrict__ partial) {
   __shared__ double s_part[kSliceThreads / 64];
   const int b = blockIdx.y, c0 = blockIdx.x * kSlice, tid = threadIdx.x;
+  if (vr.len != nullptr) {
+    const RowSpec rs = varlen_row(vr, b, N);
+    if (rs.len <= kVarlenOneGroupRow) return;
+    r = rs.r;
+    p1 = rs.p1;
+  }
   const float* x = in + (size_t)b * N;
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   f32x4 v[kVec];
@@ -90,12 +99,20 @@ __global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* i
 }
 
 // Every workgroup of row b sums the row's partials in index order (the same
-// value in each), then scales its own slice.
+// value in each), then scales its own slice.  A slice past a shorter row's
+// last prunable token adds an exact 0 to that sum, so a row normalises to
+// the same bits in a wider batch.
 __global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* in, int N, int r, int p1, float eps,
-                                                                  const double* __restrict__ partial, int nblk,
-                                                                  float* out) {
+                                                                  VarlenRows vr, const double* __restrict__ partial,
+                                                                  int nblk, float* out) {
   __shared__ double s_part[kSliceThreads / 64];
   const int b = blockIdx.y, c0 = blockIdx.x * kSlice, tid = threadIdx.x;
+  if (vr.len != nullptr) {
+    const RowSpec rs = varlen_row(vr, b, N);
+    if (rs.len <= kVarlenOneGroupRow) return;
+    r = rs.r;
+    p1 = rs.p1;
+  }
   const float* x = in + (size_t)b * N;
   float* y = out + (size_t)b * N;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
@@ -138,10 +155,25 @@ hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, floa
   }
   const int nblk = (N + kSlice - 1) / kSlice;
   double* partial = static_cast<double*>(ws);
-  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, partial);
+  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, VarlenRows{},
+                     partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, eps, partial, nblk, out);
+  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, r, p1, eps, VarlenRows{},
+                     partial, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_rmsnorm_long_rows(const float* in, int B, int N, VarlenRows vr, float eps, float* out,
+                                        void* ws, hipStream_t s) {
+  if (N <= kVarlenOneGroupRow) return hipSuccess;
+  const int nblk = (N + kSlice - 1) / kSlice;
+  double* partial = static_cast<double*>(ws);
+  hipLaunchKernelGGL(seq_sumsq_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, 0, 0, vr, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seq_scale_kernel, dim3(nblk, B), dim3(kSliceThreads), 0, s, in, N, 0, 0, eps, vr, partial, nblk,
+                     out);
   return hipGetLastError();
 }
 

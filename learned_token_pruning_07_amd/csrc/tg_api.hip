@@ -466,11 +466,16 @@ int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers, in
 int tg_gate_select_varlen(const float* score_raw, int B, int N, const int32_t* seq_len, const int32_t* span_begin,
                           const int32_t* span_end, const int32_t* K, const int32_t* cu_kept, int max_kept,
                           float eps_seq, const void* resid, int dt, int d, float* score, uint8_t* keep,
-                          int32_t* kept_idx, void* resid_out, float* score_out, void* stream) {
+                          int32_t* kept_idx, void* resid_out, float* score_out, void* ws, size_t ws_bytes,
+                          void* stream) {
   const char* name = "tg_gate_select_varlen";
   if (dt != TG_BF16 && dt != TG_F32) return fail(TG_EINVAL, "%s: unknown dtype %d", name, dt);
   if (B <= 0 || B > 65535 || N <= 0 || d <= 0) return fail(TG_EINVAL, "%s: B, N, d must be > 0", name);
-  if (N > 32768) return fail(TG_EUNSUPPORTED, "%s: rows of up to 32768 tokens (N=%d)", name, N);
+  // rows longer than 32768 tokens take the sliced kernels and their workspace
+  const size_t need = tg::gate_select_workspace(B, N);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);
+  if (need > 0 && !aligned16(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
   if (max_kept < 0 || max_kept > N) return fail(TG_EINVAL, "%s: max_kept=%d outside [0, N=%d]", name, max_kept, N);
   if (!(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_seq must be >= 0", name);
   if (!score_raw || !seq_len || !span_begin || !span_end || !K || !cu_kept || !resid || !score || !keep ||
@@ -485,7 +490,7 @@ int tg_gate_select_varlen(const float* score_raw, int B, int N, const int32_t* s
   return hip_status(tg::launch_gate_select_varlen(score_raw, B, N,
                                                   tg::VarlenRows{seq_len, span_begin, span_end, K, cu_kept}, max_kept,
                                                   eps_seq, resid, row_bytes, score, keep, kept_idx, resid_out,
-                                                  score_out, reinterpret_cast<hipStream_t>(stream)),
+                                                  score_out, ws, reinterpret_cast<hipStream_t>(stream)),
                     name);
 }
 

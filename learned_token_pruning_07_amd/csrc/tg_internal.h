@@ -41,22 +41,6 @@ hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r,
                                  const float* b1, int h, const float* w2, const float* b2,
                                  float* out, hipStream_t s);
 
-size_t seq_rmsnorm_workspace(int B, int N);
-hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, float eps, float* out, void* ws,
-                              hipStream_t s);
-
-size_t topk_select_workspace(int B, int N);
-hipError_t launch_topk_select(const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws,
-                              hipStream_t s);
-
-hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,
-                          const float* score, int M, int32_t* kept_idx, void* resid_out,
-                          float* score_out, hipStream_t s);
-
-// resid_out[m] = resid[kept_idx[m]] for m < M (the row gather of launch_compact)
-hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
-                                 const int32_t* kept_idx, void* resid_out, hipStream_t s);
-
 // Per-row lengths, spans, budgets and output offsets of a varying-length
 // batch (device arrays of B, B, B, B and B + 1 entries); all null for a
 // uniform batch.  With len null but K set, the rows are uniform in length
@@ -72,6 +56,52 @@ struct VarlenRows {
   int32_t* kept_count = nullptr;
 };
 
+// Row b of a varying-length batch: its length, prunable span [r, p1) and
+// budget, clamped into 0 <= r <= p1 <= len <= N and K >= 0.
+struct RowSpec {
+  int len, r, p1, K;
+};
+__device__ __forceinline__ RowSpec varlen_row(const VarlenRows& vr, int b, int N) {
+  RowSpec rs;
+  rs.len = min(max(vr.len[b], 0), N);
+  rs.p1 = min(max(vr.span_end[b], 0), rs.len);
+  rs.r = min(max(vr.span_begin[b], 0), rs.p1);
+  rs.K = max(vr.K[b], 0);
+  return rs;
+}
+// A varying-length row of up to this many tokens is selected by one
+// workgroup; the kernels of the longer rows skip it.
+constexpr int kVarlenOneGroupRow = 32768;
+
+size_t seq_rmsnorm_workspace(int B, int N);
+hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, float eps, float* out, void* ws,
+                              hipStream_t s);
+// the sliced normalisation of the rows of a varying-length batch longer than
+// kVarlenOneGroupRow tokens (N > kVarlenOneGroupRow; the others are untouched)
+hipError_t launch_seq_rmsnorm_long_rows(const float* in, int B, int N, VarlenRows vr, float eps, float* out,
+                                        void* ws, hipStream_t s);
+
+size_t topk_select_workspace(int B, int N);
+hipError_t launch_topk_select(const float* score, int B, int N, int r, int p1, int K, uint8_t* keep, void* ws,
+                              hipStream_t s);
+// the chunked selection of those long rows (every budget, trivial ones
+// included; keep 0 past a row's length)
+hipError_t launch_topk_select_long_rows(const float* score, int B, int N, VarlenRows vr, uint8_t* keep, void* ws,
+                                        hipStream_t s);
+
+hipError_t launch_compact(const void* resid, size_t row_bytes, int B, int N, const uint8_t* keep,
+                          const float* score, int M, int32_t* kept_idx, void* resid_out,
+                          float* score_out, hipStream_t s);
+
+// kept_idx and score_out of those long rows from their keep masks, at rows
+// cu_kept[b] .. cu_kept[b + 1] - 1
+hipError_t launch_compact_scan_long_rows(const uint8_t* keep, const float* score, int B, int N, VarlenRows vr,
+                                         int32_t* kept_idx, float* score_out, hipStream_t s);
+
+// resid_out[m] = resid[kept_idx[m]] for m < M (the row gather of launch_compact)
+hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
+                                 const int32_t* kept_idx, void* resid_out, hipStream_t s);
+
 // out[cu_kept[b] + m] = resid[b, kept_idx[cu_kept[b] + m]] for m < cu_kept[b + 1] - cu_kept[b] <= max_kept
 hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int B, int N, const int32_t* cu_kept,
                                         int max_kept, const int32_t* kept_idx, void* resid_out, hipStream_t s);
@@ -80,10 +110,14 @@ hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int
 hipError_t launch_compact_gather_padded(const void* resid, size_t row_bytes, int B, int N, const int32_t* count,
                                         int pad, const int32_t* kept_idx, void* resid_out, hipStream_t s);
 
-// gate selection of a varying-length batch (rows of up to 32768 tokens)
+// gate selection of a varying-length batch: rows of up to 32768 tokens in
+// one workgroup each, longer ones (N > 32768) through the sliced
+// normalisation, the chunked selection and the compaction scan, with
+// gate_select_workspace(B, N) bytes of workspace
 hipError_t launch_gate_select_varlen(const float* score_raw, int B, int N, VarlenRows vr, int max_kept, float eps,
                                      const void* resid, size_t row_bytes, float* score, uint8_t* keep,
-                                     int32_t* kept_idx, void* resid_out, float* score_kept, hipStream_t s);
+                                     int32_t* kept_idx, void* resid_out, float* score_kept, void* ws,
+                                     hipStream_t s);
 
 // gate selection with per-row budgets from a device array and outputs padded
 // to pad rows per batch row (rows of up to 32768 tokens); the kept counts go

@@ -196,21 +196,38 @@ __global__ __launch_bounds__(kMThreads) void topk_ws_clear_kernel(uint32_t* __re
   for (int i = threadIdx.x; i < kWsWords; i += kMThreads) w[i] = 0;
 }
 
+// Row b's span and budget: the uniform ones, or with vr.len set its own
+// (a row of up to kVarlenOneGroupRow tokens is not this path's: skip = true).
+__device__ __forceinline__ bool long_row(const VarlenRows& vr, int b, int N, int& r, int& p1, int& Kp, int& len) {
+  len = N;
+  if (vr.len == nullptr) return true;
+  const RowSpec rs = varlen_row(vr, b, N);
+  r = rs.r;
+  p1 = rs.p1;
+  Kp = min(rs.K, p1 - r);
+  len = rs.len;
+  return rs.len > kVarlenOneGroupRow;
+}
+
 // Histogram of digit PASS over the keys that match the digits already chosen
 // (which every workgroup re-derives from the previous histogram; workgroup 0
 // also records them for the next launch).
 template <int PASS>
 __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ score, int N, int r, int p1,
-                                                              int Kp,
+                                                              int Kp, VarlenRows vr,
                                                               uint32_t* __restrict__ ws) {
   __shared__ uint32_t s_hist[2048];
   __shared__ uint32_t s_prev[2048];
   __shared__ __attribute__((aligned(16))) uint32_t s_wave[kMThreads / 64];
   __shared__ uint32_t s_sel[3];
   const int tid = threadIdx.x, b = blockIdx.y, c0 = blockIdx.x * kMChunk;
+  int len;
+  if (!long_row(vr, b, N, r, p1, Kp, len)) return;
+  const int P = p1 - r;
+  // chunks past the span, and the trivial budgets (settled by the final pass)
+  if (c0 >= P || Kp <= 0 || Kp == P) return;
   const float* sc = score + (size_t)b * N + r;
   uint32_t* w = ws + (size_t)b * kWsWords;
-  const int P = p1 - r;
   uint32_t key[kMItems];
   chunk_keys(sc, P, c0 + tid * kMItems, key);  // requested first
 
@@ -247,25 +264,37 @@ __global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __res
 }
 
 // keep: key > T, or key == T among the first k_eq such tokens by index
+// (tokens outside the span: 1 up to the row's length, 0 past it)
 __global__ __launch_bounds__(kMThreads) void topk_final_kernel(const float* __restrict__ score, int N, int r, int p1,
-                                                               int Kp,
+                                                               int Kp, VarlenRows vr,
                                                                const uint32_t* __restrict__ ws,
                                                                uint8_t* __restrict__ keep) {
   __shared__ uint32_t s_prev[1024];
   __shared__ __attribute__((aligned(16))) uint32_t s_wave[kMThreads / 64];
   __shared__ uint32_t s_sel[3];
   const int tid = threadIdx.x, b = blockIdx.y, c0 = blockIdx.x * kMChunk;
+  int len;
+  if (!long_row(vr, b, N, r, p1, Kp, len)) return;
   const float* sc = score + (size_t)b * N + r;
   const uint32_t* w = ws + (size_t)b * kWsWords;
   uint8_t* kp = keep + (size_t)b * N;
   const int P = p1 - r;
   const int j0 = c0 + tid * kMItems;
-  uint32_t key[kMItems];
-  chunk_keys(sc, P, j0, key);
   if (blockIdx.x == 0) {
     for (int j = tid; j < r; j += kMThreads) kp[j] = 1;
-    for (int j = p1 + tid; j < N; j += kMThreads) kp[j] = 1;
+    for (int j = p1 + tid; j < len; j += kMThreads) kp[j] = 1;
+    for (int j = len + tid; j < N; j += kMThreads) kp[j] = 0;
   }
+  if (c0 >= P) return;
+  if (Kp <= 0 || Kp == P) {
+    // trivial budgets: every prunable token of the chunk or none
+    const uint8_t v = Kp > 0 ? 1 : 0;
+    for (int e = 0; e < kMItems; ++e)
+      if (j0 + e < P) kp[r + j0 + e] = v;
+    return;
+  }
+  uint32_t key[kMItems];
+  chunk_keys(sc, P, j0, key);
 
   for (int i = tid; i < 1024; i += kMThreads) s_prev[i] = w[kH2 + i];
   const uint32_t prefix = w[kState + 2], krem = w[kState + 3];
@@ -328,10 +357,24 @@ hipError_t launch_topk_select(const float* score, int B, int N, int r, int p1, i
   uint32_t* w = static_cast<uint32_t*>(ws);
   const dim3 grid((P + kMChunk - 1) / kMChunk, B);
   hipLaunchKernelGGL(topk_ws_clear_kernel, dim3(B), dim3(kMThreads), 0, s, w);
-  hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
-  hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
-  hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w);
-  hipLaunchKernelGGL(topk_final_kernel, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, w, keep);
+  const VarlenRows none{};
+  hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, none, w);
+  hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, none, w);
+  hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, none, w);
+  hipLaunchKernelGGL(topk_final_kernel, grid, dim3(kMThreads), 0, s, score, N, r, p1, Kp, none, w, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_select_long_rows(const float* score, int B, int N, VarlenRows vr, uint8_t* keep, void* ws,
+                                        hipStream_t s) {
+  if (N <= kVarlenOneGroupRow) return hipSuccess;
+  uint32_t* w = static_cast<uint32_t*>(ws);
+  const dim3 grid((N + kMChunk - 1) / kMChunk, B);  // every span fits N
+  hipLaunchKernelGGL(topk_ws_clear_kernel, dim3(B), dim3(kMThreads), 0, s, w);
+  hipLaunchKernelGGL(topk_hist_kernel<0>, grid, dim3(kMThreads), 0, s, score, N, 0, 0, 0, vr, w);
+  hipLaunchKernelGGL(topk_hist_kernel<1>, grid, dim3(kMThreads), 0, s, score, N, 0, 0, 0, vr, w);
+  hipLaunchKernelGGL(topk_hist_kernel<2>, grid, dim3(kMThreads), 0, s, score, N, 0, 0, 0, vr, w);
+  hipLaunchKernelGGL(topk_final_kernel, grid, dim3(kMThreads), 0, s, score, N, 0, 0, 0, vr, w, keep);
   return hipGetLastError();
 }
 

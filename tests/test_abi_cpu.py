@@ -413,3 +413,20 @@ def test_attention_rope_backward_varlen_validation(lib):
     assert call(ws_bytes=need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
     bound = lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE_BACKWARD, 1, 200 + 63 * 2, Hkv * dh, Hq, dh)
     assert bound >= need
+
+
+def test_gate_select_varlen_long_rows_need_the_workspace(lib):
+    """Rows past 32768 tokens are selected by the sliced kernels, which need
+    the workspace of TG_OP_GATE_SELECT at the padded width N."""
+    B, N = 2, 70000
+    arr = lambda: FAKE  # noqa: E731
+
+    def call(ws, ws_bytes):
+        return lib.tg_gate_select_varlen(FAKE, B, N, arr(), arr(), arr(), arr(), arr(), 1000, 1e-6, FAKE,
+                                         tgb.TG_BF16, 256, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+    need = lib.tg_workspace_size(tgb.TG_OP_GATE_SELECT, B, N, 0, 0, 0)
+    assert need == max(B * 9 * 8, B * 5124 * 4)  # 9 fp64 slice sums per row vs the digit histograms
+    assert call(NULL, 0) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(FAKE, need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(FAKE_ODD, need) == tgb.TG_EINVAL and "misaligned" in _err(lib)

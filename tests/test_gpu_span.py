@@ -212,6 +212,50 @@ def test_gate_score_varlen(dtype, N, spans):
         assert_close(got[b:b + 1], ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"varlen score row {b}")
 
 
+@pytest.mark.parametrize("N,rows,ties", [
+    # rows past 32768 tokens beside short ones: a budget inside the span, an
+    # empty span, K = 0, K = P, a short row in the wide batch
+    (131072, [(131072, 64, 131072, 13107), (65536, 0, 60000, 6000), (20000, 64, 19000, 2000),
+              (40000, 100, 100, 50), (50000, 0, 50000, 50000), (70000, 10, 69000, 0)], False),
+    # coarse scores (many equal keys): the budgets fall inside runs of ties
+    (98304, [(98304, 0, 98304, 9830), (32769, 1, 32769, 3000), (32768, 0, 32768, 3277)], True),
+])
+def test_gate_select_varlen_long_rows(N, rows, ties):
+    """Rows longer than 32768 tokens in a varying-length batch: each row equals
+    the span entry point on its own first seq_len tokens bit for bit (the long
+    ones there take the separate sliced calls), keep and score are 0 past each
+    row's length, and the selection is the oracle's top-K on the GPU's scores."""
+    B = len(rows)
+    say(f"gate_select_varlen long rows N={N} rows={rows} ties={ties}")
+    lens, p0s, p1s, Ks = (list(x) for x in zip(*rows))
+    rng = np.random.default_rng(N + B)
+    raw = (rng.standard_normal((B, N)) * 3.0).astype(np.float32)
+    if ties:
+        raw = np.round(raw * 2.0).astype(np.float32) / 2.0
+    c = wl.gate_case(N=N, r=0, d=64, h=8, K=1, dtype="bf16", seed=N + 1, B=B)
+    resid = dev_bits(c.resid)
+    ki, ro, so, keep, score, cu = tg.tg_gate_select_varlen(dev(raw), resid, lens, p0s, p1s, Ks)
+    torch.cuda.synchronize()
+    bits = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()  # noqa: E731
+    got = score.cpu().numpy()
+    for b, (n, p0, p1, K) in enumerate(rows):
+        ki1, ro1, so1, keep1, score1 = tg.tg_gate_select(dev(np.ascontiguousarray(raw[b:b + 1, :n])),
+                                                         resid[b:b + 1, :n].contiguous(), p0, K, span_end=p1)
+        sl = slice(cu[b], cu[b + 1])
+        assert cu[b + 1] - cu[b] == n - (p1 - p0) + min(K, p1 - p0)
+        assert np.array_equal(ki[sl].cpu().numpy(), ki1[0].cpu().numpy()), f"row {b} kept_idx"
+        assert np.array_equal(bits(ro[sl]), bits(ro1[0])), f"row {b} resid_out"
+        assert np.array_equal(bits(so[sl]), bits(so1[0])), f"row {b} score_out"
+        assert np.array_equal(keep[b, :n].cpu().numpy(), keep1[0].cpu().numpy()), f"row {b} keep"
+        assert np.array_equal(bits(score[b, :n]), bits(score1[0])), f"row {b} score"
+        assert torch.all(keep[b, n:] == 0) and torch.all(score[b, n:] == 0), f"row {b} padding"
+        k_or = oracle.topk_select(got[b:b + 1, :n], p0, K, span_end=p1)
+        assert np.array_equal(keep[b, :n].cpu().numpy(), k_or[0]), f"row {b} vs oracle top-K"
+        ref = oracle.seq_rmsnorm(raw[b:b + 1, :n], p0, 1e-6, span_end=p1)
+        assert_close(got[b:b + 1, :n], ref, TOL_F32, f"row {b} normalised scores")
+        say(f"  row {b} (len {n}, span [{p0}, {p1}), K {K}): {cu[b + 1] - cu[b]} kept, bit-identical")
+
+
 def test_gate_select_varlen_clamps_row_parameters():
     """Out-of-range per-row values are clamped (span end past the length, a
     negative budget, a span start past the end) and give exactly the results
