@@ -137,6 +137,41 @@ def time_backward(torch, tg, qkv, b_S, kept_idx, layer, attn_out, heads, M, stre
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "shape": {"M": M, "Hq": Hq, "Hkv": Hkv, "d_h": dh}}
 
 
+def time_rope(torch, tg, qkv, b_S, kept_idx, layer, heads, M, base=1e6, reps=20, rounds=3):
+    """The rotary variant of one attention layer beside the plain call, at the
+    stage's shape: q and k turned by the kept tokens' original positions
+    (kept_idx) inside the call.  Rounds of `reps` plain calls, then `reps`
+    rotary calls, alternate on the launch stream (HIP events around each
+    block); the best round of each is reported, and their ratio."""
+    q, k, v = qkv
+    Hq, Hkv, dh = heads["Hq"], heads["Hkv"], heads["dh"]
+    out = torch.empty((1, M, Hq, dh), dtype=torch.bfloat16, device=q.device)
+    ws_p = tg.attention_workspace(1, M, Hq, Hkv, dh, q.device)
+    ws_r = tg.attention_rope_workspace(1, M, Hq, Hkv, dh, q.device)
+    plain = lambda: tg.tg_gated_attention(q, k, v, b_S, kept_idx, layer.gain, layer.temp, out=out,  # noqa: E731
+                                          ws=ws_p)
+    rope = lambda: tg.tg_gated_attention_rope(q, k, v, b_S, kept_idx, layer.gain, layer.temp, base,  # noqa: E731
+                                              out=out, ws=ws_r)
+    for fn in (plain, rope, plain, rope):
+        fn()
+    torch.cuda.synchronize()
+    best = {"plain": float("inf"), "rope": float("inf")}
+    for _ in range(rounds):
+        for name, fn in (("plain", plain), ("rope", rope)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best[name] = min(best[name], e0.elapsed_time(e1) * 1e3 / reps)
+    flops = 2 * dh * Hq * M * (M + 1)
+    return {"call": "tg_gated_attention_rope", "rope_base": base, "plain_us": round(best["plain"], 3),
+            "rope_us": round(best["rope"], 3), "rope_over_plain": round(best["rope"] / best["plain"], 4),
+            "rope_mfma_frac": round(flops / (best["rope"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "calls_per_round": reps, "rounds": rounds}
+
+
 def time_varlen(torch, tg, layer, heads, M, n_seq=16, reps=20):
     """Token-gated attention over a packed batch of `n_seq` gated prompts
     (kept lengths uniform in [M/8, M], seeded; random bf16 q, k, v, scores and
@@ -496,6 +531,8 @@ def main():
                     help="skip the separate timing of tg_kv_cache_prune (layers 0..L of the stage)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed varying-length attention timing")
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip the rotary attention timing beside the plain call")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of tg_gated_attention_backward at the attention shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -731,6 +768,10 @@ def main():
 
     if layers and not args.no_varlen:
         out["varlen_attention"] = time_varlen(torch, tg, layers[0], heads, M)
+    if layers and not args.no_rope:
+        out["rope_attention"] = time_rope(torch, tg, qkv[0], b_S, kept_idx, layers[0], heads, M)
+        log(f"rotary attention: {out['rope_attention']['rope_us']:.2f} us per call, "
+            f"{out['rope_attention']['rope_over_plain']:.3f} x the plain call")
     if layers and not args.no_backward:
         out["attention_backward"] = time_backward(torch, tg, qkv[0], b_S, kept_idx, layers[0], attn_out, heads, M,
                                                   stream_reps=20)

@@ -631,7 +631,8 @@ int tg_kv_cache_prune(const void* k_cache, const void* v_cache, int n_layers,
  * and K = d_h; the size is B * round_up(M, 64) * (2 * Hkv * d_h + 4 * (Hq +
  * Hkv)).  K = 0 gives the size for the largest Hkv (= Hq), an upper bound.
  * For TG_OP_GATED_ATTENTION_ROPE pass the same and K = d_h; the size adds
- * B * M * d_h * (2 * Hkv + 4).
+ * B * M * d_h * 2 * Hkv (the rotated k) + B * round_up(M, 64) * d_h * 4
+ * (the angle table).
  * For TG_OP_GATED_ATTENTION_BACKWARD pass the same as for
  * TG_OP_GATED_ATTENTION_ROPE; with Mp = round_up(M, 64) the size is
  * B * Mp * (12 Hq + 4 Hkv) + 8 * B * (Mp / 64) * Hq.

@@ -78,6 +78,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;  // keys per tile
+constexpr int kRopeRows = 16;  // rows whose rotary angles the prepass holds in LDS at a time
 
 // V^T tile scale exponents: the tile's largest |v| times 2^e lies in
 // [2^14, 2^15) when e is inside this range (tile maxima in [2^-36, 2^65)).
@@ -178,6 +179,19 @@ struct SeqTable {
   int pb0[kMaxSeqsPerLaunch + 1];
   int wg0[kMaxSeqsPerLaunch + 1];
 };
+
+// The rotary angle table, by padded key slot, in the attention kernel's
+// fragment order: for slots 32 n .. 32 n + 31 (one wave's queries), piece
+// (ks, u) of lane l = 32 gq + (slot & 31) is the f32x4 (cos, sin, cos, sin) of
+// pairs 16 ks + 8 gq + 2u and + 1 (ks < DH / 32, u < 4), and the 64 lanes'
+// pieces of one (ks, u) are 1 KiB contiguous, so each load of the kernel's
+// Q rotation reads whole cache lines.  Pairs i0 .. i0 + 7 (i0 a multiple of
+// 8) of a slot are pieces u = 0..3, 64 pieces apart, from the one returned.
+template <int DH>
+__device__ __forceinline__ f32x4* rope_tab_piece(float* tab, size_t slot, int i0) {
+  const int ks = i0 >> 4, gq = (i0 >> 3) & 1;
+  return reinterpret_cast<f32x4*>(tab) + ((slot >> 5) * (DH / 32) + ks) * 4 * 64 + gq * 32 + (slot & 31);
+}
 
 // Prepass, per 64-key block of KV head g:
 //   e = the block's scale exponent: 141 - (exponent field of the largest
@@ -289,20 +303,49 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     store16(vt + P0 * Hkv * DH + ((size_t)g * DH + d) * Mp + m0 + kc * 8, o);
   }
   if constexpr (ROPE) {
+    // The angles of a row are formed once, by one of the Hkv blocks of its
+    // 64-key block (rows g R .. g R + R - 1, R = ceil(64 / Hkv)), which then
+    // turns that row's K for every KV head and writes its table row; up to
+    // kRopeRows rows at a time, their (cos, sin) pairs in LDS.
     constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
-    for (int t = tid; t < kBK * PG; t += kThreads) {
-      const int key = t / PG, i0 = (t % PG) * 8, m = m0 + key;
-      if (m >= M) continue;
-      float c[8], sn[8];
-      rope::sincos8((double)ra.pos[T0 + m], s_freq, i0, c, sn);
-      const size_t krow = ((T0 + m) * Hkv + g) * DH;
-      rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
-      if (g == 0) {  // the row's (cos, sin) pairs i0 .. i0 + 7
-        float* tb = ra.tab + (T0 + m) * DH + 2 * i0;
+    __shared__ f32x2 s_cs[kRopeRows][DH / 2];
+    const int R = (kBK + Hkv - 1) / Hkv;
+    const int r_hi = min(kBK, (g + 1) * R);
+    for (int c0 = g * R; c0 < r_hi; c0 += kRopeRows) {  // (block-uniform)
+      const int nr = min(kRopeRows, r_hi - c0);
+      for (int t = tid; t < nr * PG; t += kThreads) {
+        const int rr = t / PG, i0 = (t % PG) * 8, m = m0 + c0 + rr;
+        // the table holds pairs i0 .. i0 + 7 of slot P0 + m as 4 pieces (the
+        // padding slots past M hold zeros: their queries turn into 0)
+        f32x4* tb = rope_tab_piece<DH>(ra.tab, P0 + m, i0);
+        if (m >= M) {
 #pragma unroll
-        for (int i = 0; i < 8; i += 2)
-          *reinterpret_cast<f32x4*>(tb + 2 * i) = f32x4{c[i], sn[i], c[i + 1], sn[i + 1]};
+          for (int u = 0; u < 4; ++u) tb[u * 64] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          continue;
+        }
+        float c[8], sn[8];
+        rope::sincos8((double)ra.pos[T0 + m], s_freq, i0, c, sn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) tb[u * 64] = f32x4{c[2 * u], sn[2 * u], c[2 * u + 1], sn[2 * u + 1]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_cs[rr][i0 + i] = f32x2{c[i], sn[i]};
       }
+      __syncthreads();
+      // consecutive threads: the 16-byte pieces of one row's heads, in memory order
+      for (int t = tid; t < nr * PG * Hkv; t += kThreads) {
+        const int i0 = (t % PG) * 8, gg = (t / PG) % Hkv, rr = t / (PG * Hkv), m = m0 + c0 + rr;
+        if (m >= M) continue;
+        float c[8], sn[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x2 cs = s_cs[rr][i0 + i];
+          c[i] = cs[0];
+          sn[i] = cs[1];
+        }
+        const size_t krow = ((T0 + m) * Hkv + gg) * DH;
+        rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
+      }
+      __syncthreads();  // (before the next rows' pairs overwrite LDS)
     }
   }
 }
@@ -337,7 +380,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   const int32_t* m_dev;
-  const float* rope_tab;  // (cos, sin) of every row's rotary angles, or null: q is used as given
+  const float* rope_tab;  // the angle table (rope_tab_piece layout), or null: q is used as given
   int M_all, Mp_all, Hq, Hkv, nqb_all, total_wg, n_slabs;
   float sm_scale;
 };
@@ -379,6 +422,19 @@ __device__ __forceinline__ int sched_block(AttnArgsPtr ap, int rnd, int& b, int&
   if (level >= nqb) return 1;
   qb = nqb - 1 - level;
   return 2;
+}
+
+// The (cos, sin) pieces of one lane's query fragments from the angle table
+// (rope_tab_piece's layout): slot0 = the wave's first query slot (a multiple
+// of 32), rt[ks][u] covers pairs 16 ks + 8 gq + 2u and + 1 of query slot0 +
+// (lane & 31).  Every load reads 1 KiB contiguous.
+template <int DH>
+__device__ __forceinline__ void load_rope_row(const float* tab, size_t slot0, int lane, f32x4 (&rt)[DH / 32][4]) {
+  const f32x4* tb = reinterpret_cast<const f32x4*>(tab) + (slot0 >> 5) * (DH / 32) * 4 * 64 + lane;
+#pragma unroll
+  for (int ks = 0; ks < DH / 32; ++ks)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rt[ks][u] = tb[(ks * 4 + u) * 64];
 }
 
 // ROPE: the Q fragments are rotated by the prepass's angle table after they
@@ -822,15 +878,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   const float t_h = temp[hq];
   // rotary embedding: this lane's fragments ks and ks + KS/2 hold the pairs
   // (x_i, x_{i + DH/2}), i = 16 ks + 8 gq + e; their cosines and sines come
-  // from the prepass's table row of this query
-  const float* __restrict__ rope_tab = ap->rope_tab;
-  f32x4 rt[KS / 2][4];  // rt[ks][u] = (cos, sin) of pairs 2u and 2u + 1 of fragment ks
+  // from the prepass's table of this query's slot (held only in the prologue:
+  // a copy carried over from the previous block would not fit the registers)
+  f32x4 rt[KS / 2][4];
   if constexpr (ROPE) {
-    const float* tr = rope_tab + (T0 + (q_ok ? qi : 0)) * DH + 16 * gq;
+    if (wave_rows) {  // (the wave's 32 slots lie inside the sequence's padded slots)
+      load_rope_row<DH>(ap->rope_tab, P0 + rbase, lane, rt);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
+      for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rt[ks][u] = *reinterpret_cast<const f32x4*>(tr + 32 * ks + 4 * u);
+        for (int u = 0; u < 4; ++u) rt[ks][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
   wait_vmem();
   TG_DIAG_PSTAMP(1);
@@ -1118,18 +1177,19 @@ size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {
   return (size_t)B * Mp * ((size_t)Hkv * dh * 2 + (size_t)(Hq + Hkv) * 4);
 }
 
-// ... then the rotated k [B, M, Hkv, dh] (bf16) and the angle table [B, M,
-// dh / 2] (cos, sin) (fp32)
+// ... then the rotated k [B, M, Hkv, dh] (bf16) and the angle table, dh / 2
+// (cos, sin) pairs of every padded slot [B, Mp] (fp32)
 size_t gated_attention_rope_workspace(int B, int M, int Hq, int Hkv, int dh) {
-  (void)Hq;
-  return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * dh * ((size_t)Hkv * 2 + 4);
+  const size_t Mp = (size_t)(M + kBK - 1) / kBK * kBK;
+  return gated_attention_workspace(B, M, Hq, Hkv, dh) + (size_t)B * M * dh * Hkv * 2 + (size_t)B * Mp * dh * 4;
 }
 
 // the varying-length rotary call: after the other workspace (slots padded
-// rows), the rotated k and the angle table of the T packed rows
+// rows), the rotated k of the T packed rows and the angle table of the slots
 size_t gated_attention_rope_varlen_workspace(int B, const int32_t* cu_seqlens, int Hq, int Hkv, int dh) {
   const size_t slots = gated_attention_varlen_slots(B, cu_seqlens);
-  return gated_attention_workspace(1, (int)slots, Hq, Hkv, dh) + (size_t)cu_seqlens[B] * dh * ((size_t)Hkv * 2 + 4);
+  return gated_attention_workspace(1, (int)slots, Hq, Hkv, dh) + (size_t)cu_seqlens[B] * dh * Hkv * 2 +
+         slots * dh * 4;
 }
 
 size_t gated_attention_varlen_slots(int B, const int32_t* cu_seqlens) {

@@ -665,41 +665,68 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Rotary embedding for the backward of the rotary variant, per 64-row block
-// of KV head g: ROTATE_BACK false rotates the K row of head g and the Q rows
-// of its G query heads into bf16 copies, exactly as the forward's prepass
-// does (so the products see the forward's operands); true applies the
-// transposed rotation to the fp32 gradients with respect to the rotated q
-// and k and rounds them to bf16.
+// Rotary embedding for the backward of the rotary variant, per 64-row block,
+// its rows shared out over the grid's Hkv blocks: ROTATE_BACK false rotates
+// the K rows of every KV head and the Q rows of every query head into bf16
+// copies, exactly as the forward rotates them (so the products see the
+// forward's operands); true applies the transposed rotation to the fp32
+// gradients with respect to the rotated q and k and rounds them to bf16.
 template <int DH, bool ROTATE_BACK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_rope_kernel(const void* __restrict__ q_in,
                                                                 const void* __restrict__ k_in,
                                                                 const int32_t* __restrict__ pos, double base, int M,
                                                                 int Hq, int Hkv, uint16_t* __restrict__ q_out,
                                                                 uint16_t* __restrict__ k_out) {
+  constexpr int kRows = 16;  // rows whose angles sit in LDS at a time
   __shared__ double s_freq[DH / 2];
+  __shared__ f32x2 s_cs[kRows][DH / 2];
   constexpr int PG = DH / 16;  // groups of 8 pairs per head row
+  // The angles of a row are formed once, by one of the Hkv blocks of its
+  // 64-row block (rows g R .. g R + R - 1, R = ceil(64 / Hkv)), which turns
+  // that row of every K and Q head.
   const int m0 = blockIdx.x * kPB, g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
+  const int nh = Hkv + Hq;  // head rows of one position: K heads first, then Q heads
   if (threadIdx.x < DH / 2) s_freq[threadIdx.x] = rope::inv_freq(base, threadIdx.x, DH);
   __syncthreads();
-  for (int t = threadIdx.x; t < kPB * PG; t += kBwdThreads) {
-    const int m = m0 + t / PG, i0 = (t % PG) * 8;
-    if (m >= M) continue;
-    float c[8], sn[8];
-    rope::sincos8((double)pos[(size_t)b * M + m], s_freq, i0, c, sn);
-    const size_t krow = (((size_t)b * M + m) * Hkv + g) * DH;
-    if constexpr (ROTATE_BACK)
-      rope::row8_transposed<DH>(static_cast<const float*>(k_in) + krow, k_out + krow, i0, c, sn);
-    else
-      rope::row8<DH>(static_cast<const uint16_t*>(k_in) + krow, k_out + krow, i0, c, sn);
-    for (int hh = 0; hh < G; ++hh) {
-      const size_t qrow = (((size_t)b * M + m) * Hq + g * G + hh) * DH;
-      if constexpr (ROTATE_BACK)
-        rope::row8_transposed<DH>(static_cast<const float*>(q_in) + qrow, q_out + qrow, i0, c, sn);
-      else
-        rope::row8<DH>(static_cast<const uint16_t*>(q_in) + qrow, q_out + qrow, i0, c, sn);
+  const int R = (kPB + Hkv - 1) / Hkv;
+  const int r_hi = min(kPB, (g + 1) * R);
+  for (int c0 = g * R; c0 < r_hi; c0 += kRows) {  // (block-uniform)
+    const int nr = min(kRows, r_hi - c0);
+    for (int t = threadIdx.x; t < nr * PG; t += kBwdThreads) {
+      const int rr = t / PG, i0 = (t % PG) * 8, m = m0 + c0 + rr;
+      if (m >= M) continue;
+      float c[8], sn[8];
+      rope::sincos8((double)pos[(size_t)b * M + m], s_freq, i0, c, sn);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_cs[rr][i0 + i] = f32x2{c[i], sn[i]};
     }
+    __syncthreads();
+    for (int t = threadIdx.x; t < nr * PG * nh; t += kBwdThreads) {
+      const int i0 = (t % PG) * 8, hh = (t / PG) % nh, rr = t / (PG * nh), m = m0 + c0 + rr;
+      if (m >= M) continue;
+      float c[8], sn[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x2 cs = s_cs[rr][i0 + i];
+        c[i] = cs[0];
+        sn[i] = cs[1];
+      }
+      const size_t row = (size_t)b * M + m;
+      if (hh < Hkv) {
+        const size_t krow = (row * Hkv + hh) * DH;
+        if constexpr (ROTATE_BACK)
+          rope::row8_transposed<DH>(static_cast<const float*>(k_in) + krow, k_out + krow, i0, c, sn);
+        else
+          rope::row8<DH>(static_cast<const uint16_t*>(k_in) + krow, k_out + krow, i0, c, sn);
+      } else {
+        const size_t qrow = (row * Hq + (hh - Hkv)) * DH;
+        if constexpr (ROTATE_BACK)
+          rope::row8_transposed<DH>(static_cast<const float*>(q_in) + qrow, q_out + qrow, i0, c, sn);
+        else
+          rope::row8<DH>(static_cast<const uint16_t*>(q_in) + qrow, q_out + qrow, i0, c, sn);
+      }
+    }
+    __syncthreads();  // (before the next rows' pairs overwrite LDS)
   }
 }
 

@@ -545,7 +545,8 @@ static int attention_varlen_common(const char* name, const void* q, const void* 
   if (slots == 0) return TG_OK;
   if (slots > 0x7FFFFFFF) return fail(TG_EINVAL, "%s: %zu padded rows exceed the 32-bit index range", name, slots);
   // all sequences' V^T copies and key-score terms sit side by side (then,
-  // with the rotary embedding, the rotated k and the angle table by packed row)
+  // with the rotary embedding, the rotated k by packed row and the angle
+  // table by padded slot)
   const size_t need = rope_base > 0.0 ? tg::gated_attention_rope_varlen_workspace(B, cu_seqlens, Hq, Hkv, d_h)
                                       : tg::gated_attention_workspace(1, (int)slots, Hq, Hkv, d_h);
   if (!ws || ws_bytes < need) return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name, need, ws_bytes);

@@ -65,9 +65,10 @@ def test_version_and_workspace(lib):
         3392 * (8 * 128 * 2 + 32 * 4)
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 0, 64) == 0   # Hq is required
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION, 1, 64, 2 * 64, 4, 48) == 0   # d_h must divide d
-    # the rotary variant adds the rotated q [B, M, Hq, d_h] and k [B, M, Hkv, d_h] (bf16); K = d_h
+    # the rotary variant adds the rotated k [B, M, Hkv, d_h] (bf16) and the angle table of the
+    # padded slots [B, round_up(M, 64), d_h / 2] (cos, sin) (fp32); K = d_h
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 3341, 8 * 128, 16, 128) == \
-        3392 * (8 * 128 * 2 + (16 + 8) * 4) + 3341 * 128 * (2 * 8 + 4)
+        3392 * (8 * 128 * 2 + (16 + 8) * 4) + 3341 * 128 * 2 * 8 + 3392 * 128 * 4
     assert lib.tg_workspace_size(tgb.TG_OP_GATED_ATTENTION_ROPE, 1, 64, 2 * 64, 4, 0) == 0   # d_h is required
 
 
