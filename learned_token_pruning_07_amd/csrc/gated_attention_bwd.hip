@@ -307,12 +307,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   // Unit u = 2 step + parity is staged by the two waves of that parity: key
   // half 0 brings the Q tile and the row constants (NI + 3 loads), key half 1
   // the dO tile (NI loads).  Rows >= M read 0.
-  auto stage = [&](int step) __attribute__((always_inline)) {
+  auto stage = [&](int step, int slot) __attribute__((always_inline)) {
     const int u = 2 * step + par;
     if (u >= U) return;
     const int hl = u % G, t = t0 + u / G;
     const int h = g * G + hl;
-    unsigned char* base = smem + ((step % NBUF) * 2 + par) * UB;
+    unsigned char* base = smem + (slot * 2 + par) * UB;
     const size_t row0 = ((T0 + t * kT) * Hq + h) * DH;
     const int nrec = (int)(((long long)(M - 1 - t * kT) * Hq + 1) * DH * 2);
     if (kh == 0) {
@@ -339,10 +339,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
   for (int i = 0; i < G; ++i) cs[i] = ta[i] = 0.0f;
 
+  // This lane's LDS offsets inside a staged tile, formed once: the swizzled
+  // chunk of fragment s is row_tile_off(kl, 2 s + gq) = rto[s & 3] + 128 (s >> 2),
+  // and the transpose loads of tr_frag sit at tro[blk & 1] + 128 (blk >> 1) +
+  // (16 s + 8 hf) 2 DH (the swizzle only sees the row's low 3 bits, which are
+  // the lane's own).  The empty asm statements keep them in registers rather
+  // than re-derived at every use.
+  int rto[4], tro[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rto[i] = row_tile_off<DH>(kl, 2 * i + gq);
+    asm volatile("" : "+v"(rto[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    tro[i] = tr_off<DH>(i, 0, 0, lane);
+    asm volatile("" : "+v"(tro[i]));
+  }
+  auto frag_off = [&](int s_) { return rto[s_ & 3] + 128 * (s_ >> 2); };
+  auto trf = [&](const unsigned char* tile, int blk, int s_) __attribute__((always_inline)) {
+    const int o = tro[blk & 1] + 128 * (blk >> 1) + 16 * s_ * 2 * DH;
+    return tr_frag_at(tile, o, o + 8 * 2 * DH);
+  };
+
   // One unit: S = Q K^T and dP = dO V^T, the softmax terms, then
   // dV^T += dO^T P and dK^T += Q^T dS.  Fragments are read in batches ahead
   // of their products.
-  auto step_dkdv = [&](const unsigned char* base, int hl, int t) __attribute__((always_inline)) {
+  auto step_dkdv = [&](const unsigned char* base, int hl, int t, bool run) __attribute__((always_inline)) {
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
@@ -350,7 +373,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       bf16x8 fq[KS], fd[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int off = row_tile_off<DH>(kl, 2 * s + gq);
+        const int off = frag_off(s);
         fq[s] = lds_frag(base + off);
         fd[s] = lds_frag(base + TB + off);
       }
@@ -377,7 +400,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         const int r = 4 * i4 + jj;
         const int qi = t * kT + 8 * i4 + 4 * gq + jj;
         const float z = fmaf(S[r], c4[jj], kbh) - l4[jj];
-        const float P = j <= qi ? __builtin_amdgcn_exp2f(z) : 0.0f;
+        const float P = run && j <= qi ? __builtin_amdgcn_exp2f(z) : 0.0f;
         const float dZ = P * (dP[r] - d4[jj]);
         const float dS = dZ * c4[jj];
         csum += dZ;
@@ -398,15 +421,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
       const bf16x8 pb = pack8(Pv + 8 * s), sb = pack8(Sv + 8 * s);
 #pragma unroll
       for (int blk = 0; blk < DT; ++blk) {
-        const bf16x8 fdo = tr_frag<DH>(base + TB, blk, s, lane), fqt = tr_frag<DH>(base, blk, s, lane);
+        const bf16x8 fdo = trf(base + TB, blk, s), fqt = trf(base, blk, s);
         dVt[blk] = mfma(fdo, pb, dVt[blk]);
         dKt[blk] = mfma(fqt, sb, dKt[blk]);
       }
     }
   };
 
-  stage(0);
-  stage(1);
+  // Every step runs its products (a skipped unit contributes exact zeros: its
+  // P is 0), so a slot that is never staged -- the last unit of an odd count
+  // -- must hold finite values: the staging area starts zeroed.
+  for (int i = threadIdx.x; i < NBUF * 2 * UB / 16; i += kBwdThreads)
+    reinterpret_cast<u32x4*>(smem)[i] = u32x4{0, 0, 0, 0};
+  __syncthreads();
+  stage(0, 0);
+  stage(1, 1);
+  int slot = 0;  // p % NBUF, carried instead of divided
   for (int p = 0; p < nsteps; ++p) {
     // step p's loads are done once at most step p + 1's remain in flight
     if (2 * (p + 1) + par < U) {
@@ -419,11 +449,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int u = 2 * p + par;
     const int hl = u % G, t = t0 + u / G;
     const bool run = u < U && t * kT + kT - 1 >= kw0 && kw0 < M;  // some key of this wave lies on/below the tile
-    const unsigned char* base = smem + ((p % NBUF) * 2 + par) * UB;
-    if (run) step_dkdv(base, hl, t);
+    const unsigned char* base = smem + (slot * 2 + par) * UB;
+    step_dkdv(base, hl, t, run);
     // Issued after this step's transpose loads: the compiler makes an LDS
     // transpose load wait for every LDS-destination load issued before it.
-    stage(p + 2);
+    stage(p + 2, slot == 0 ? NBUF - 1 : slot - 1);
+    slot = slot == NBUF - 1 ? 0 : slot + 1;
   }
   // ---- merge the two parities, write dK and dV, the key-score and scale partials ----
   __syncthreads();  // the staging slots are free
@@ -565,9 +596,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   const auto rks = rsrc(kscore + T0, M * 4);
   // Tile t: K and V rows (rows >= M read 0) and 64 key scores (those >= M
   // read 0); load x = w + 4 n of the 2 NI goes to wave w.
-  auto stage = [&](int t) __attribute__((always_inline)) {
+  auto stage = [&](int t, int slot_t) __attribute__((always_inline)) {
     if (t >= ntk) return;
-    unsigned char* base = smem + (t % NBUF) * UB;
+    unsigned char* base = smem + slot_t * UB;
     const int nrec = (int)(((long long)(M - 1 - t * kT) * Hkv + 1) * DH * 2);
     const size_t roff = (size_t)t * kT * Hkv * DH;
     const auto rk = rsrc(kbase + roff, nrec), rv = rsrc(vbase + roff, nrec);
@@ -593,7 +624,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) toff[blk][s][hf] = tr_off<DH>(blk, s, hf, lane);
-  auto step_dq = [&](const unsigned char* base, int t) __attribute__((always_inline)) {
+  int rto[4];  // row_tile_off(ql, 2 s + gq) = rto[s & 3] + 128 (s >> 2), formed once
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rto[i] = row_tile_off<DH>(ql, 2 * i + gq);
+    asm volatile("" : "+v"(rto[i]));
+  }
+  auto step_dq = [&](const unsigned char* base, int t, bool run) __attribute__((always_inline)) {
     f32x16 S, dP;
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
@@ -601,7 +638,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
       bf16x8 fk[KS], fv[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int off = row_tile_off<DH>(ql, 2 * s + gq);
+        const int off = rto[s & 3] + 128 * (s >> 2);
         fk[s] = lds_frag(base + off);
         fv[s] = lds_frag(base + TB + off);
       }
@@ -621,7 +658,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
         const int r = 4 * i4 + jj;
         const int key = t * kT + 8 * i4 + 4 * gq + jj;
         const float z = fmaf(S[r], cq, gl2 * b4[jj]) - lq;
-        const float P = key <= qi ? __builtin_amdgcn_exp2f(z) : 0.0f;
+        const float P = run && key <= qi ? __builtin_amdgcn_exp2f(z) : 0.0f;
         Z[r] = P * (dP[r] - Dq);
       }
     }
@@ -635,8 +672,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
   };
 
   const bool wave_rows = qw0 < M;
-  stage(0);
-  stage(1);
+  stage(0, 0);
+  stage(1, 1);
+  int slot = 0;  // t % NBUF, carried instead of divided
   for (int t = 0; t < ntk; ++t) {
     if (t + 1 < ntk) {
       if (w == 0) wait_loads_le<NX + 1>();
@@ -645,9 +683,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
       wait_loads_le<0>();
     }
     __syncthreads();
+    // every step runs its products (every tile t < ntk is staged; a tile
+    // past this wave's queries has P = 0 and contributes exact zeros)
     const bool run = wave_rows && t * kT <= qw0 + 31;  // some query of this wave reaches the tile
-    if (run) step_dq(smem + (t % NBUF) * UB, t);
-    stage(t + 2);  // after this step's transpose loads (see the dK/dV kernel)
+    step_dq(smem + slot * UB, t, run);
+    stage(t + 2, slot == 0 ? NBUF - 1 : slot - 1);  // after this step's transpose loads (see the dK/dV kernel)
+    slot = slot == NBUF - 1 ? 0 : slot + 1;
   }
   if (q_ok) {
     const float sc = cq * kLn2;  // c_i (the exponent constant carries log2(e))
