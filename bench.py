@@ -508,6 +508,164 @@ def _cpu_sample(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows):
     }
 
 
+# ---------------------------------------------------------------------------
+# Profile summaries (CPU only): rocprofv3 CSV output -> the files under profiles/
+STAGE_SHAPE = dict(N=32768, r=64, d=2048, h=256, M=3341, Hq=16, Hkv=8, dh=128, kv_layers=STAGE_GATE_LAYER + 1)
+PROFILE_RUN_FLAGS = "--no-cpu-baseline --no-sub-records --no-ceilings --no-varlen --no-rope"
+# library call -> (source file, kernels of one call at the stage shape)
+PROFILE_CALLS = {
+    "tg_gated_attention": ("gated_attention.hip",
+                           ["attn_prepass_kernel<128, false, false>", "gated_attn_kernel<128, 2, false, false>"]),
+    "tg_gate_score_folded": ("gate_score.hip", ["gate_score_bf16_kernel<256, 128, 8, 32>"]),
+    "tg_gate_select": ("gate_select.hip", ["gate_select_kernel", "compact_gather_kernel"]),
+    "tg_gated_attention_backward": ("gated_attention_bwd.hip",
+                                    ["bwd_rows_kernel<128>", "bwd_dkdv_kernel<128, 2, false>",
+                                     "bwd_dq_kernel<128, 2, false>", "bwd_reduce_kernel"]),
+    "tg_kv_cache_prune": ("kv_prune.hip", ["kv_prune_kernel"]),
+}
+
+
+def stage_algorithmic_bytes():
+    """Bytes each library call must move at the stage shape (inputs read once,
+    outputs written once)."""
+    S = STAGE_SHAPE
+    N, r, d, h, M, Hq, Hkv, dh = (S[k] for k in ("N", "r", "d", "h", "M", "Hq", "Hkv", "dh"))
+    P = N - r
+    return {
+        # residual span, W1 (bf16), raw scores out
+        "tg_gate_score_folded": P * d * 2 + h * d * 2 + 4 * N,
+        # raw scores in, normalised scores, keep mask, kept_idx and kept scores out, kept_idx read back by the
+        # gather, kept rows read and written
+        "tg_gate_select": 4 * P + 4 * N + N + 12 * M + 2 * M * d * 2,
+        # q, k, v in, out written (bf16); key scores and positions
+        "tg_gated_attention": M * dh * 2 * (2 * Hq + 2 * Hkv) + 8 * M,
+        # q, k, v, out, d_out in (bf16), lse, key scores, positions; d_q, d_k, d_v (bf16), d_key_score out
+        "tg_gated_attention_backward": 2 * M * dh * (3 * Hq + 2 * Hkv) + 4 * M * Hq + 8 * M
+                                       + 2 * M * dh * (Hq + 2 * Hkv) + 4 * M,
+        # the kept rows of every layer's K and V read and written, kept_idx
+        "tg_kv_cache_prune": S["kv_layers"] * 2 * M * Hkv * dh * 2 * 2 + 4 * M,
+    }
+
+
+def _short_kernel(name: str) -> str:
+    """'void tg::(anonymous namespace)::k<1, 2>(args...)' -> 'k<1, 2>'."""
+    n = name[5:] if name.startswith("void ") else name
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and i > 0 and not n[:i].endswith("anonymous namespace") and \
+                not n[i:].startswith("(anonymous"):
+            n = n[:i]
+            break
+    return n.replace("tg::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+
+
+def _csv_rows(root, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(root, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {root}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _counter_kib(root):
+    """Average counter value (KiB) per dispatch of every kernel in a --pmc run."""
+    acc = {}
+    for r in _csv_rows(root, "counter_collection.csv"):
+        acc.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_profiles(run_dir: str):
+    """Writes profiles/kernel_trace_stage_32k.txt, profiles/hbm_traffic_stage_32k.txt and
+    profiles/traffic.json from the rocprofv3 output of the commands they list,
+    run from the repository root with their -d directories under run_dir."""
+    prof = os.path.join(ROOT, "profiles")
+    cmds = {
+        "trace": f"rocprofv3 --kernel-trace --stats --output-format csv -d {{dir}}/trace -o stage -- "
+                 f"python3 bench.py --steps 5 --warmup 2 {PROFILE_RUN_FLAGS}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {{dir}}/fetch -o stage -- "
+                 f"python3 bench.py --steps 2 --warmup 1 {PROFILE_RUN_FLAGS}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {{dir}}/write -o stage -- "
+                 f"python3 bench.py --steps 2 --warmup 1 {PROFILE_RUN_FLAGS}",
+        "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/copy_fetch -o copy -- "
+                      "python3 bench.py --copy-calibration",
+        "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/copy_write -o copy -- "
+                      "python3 bench.py --copy-calibration",
+    }
+    S = STAGE_SHAPE
+    head = (f"stage_32k (N={S['N']}, r={S['r']}, K=3277 -> M={S['M']}, d={S['d']}, h={S['h']}, "
+            f"{S['Hq']}q/{S['Hkv']}kv heads, d_h {S['dh']}, 24 gated attention layers)")
+    # ---- kernel trace ----
+    stats = _csv_rows(os.path.join(run_dir, "trace"), "kernel_stats.csv")
+    lines = [f"# Kernel trace: {head}", "", "Commands (repository root, one MI355X):",
+             "    " + cmds["trace"].format(dir="<dir>"),
+             "    python3 bench.py --summarize-profiles <dir>   (writes this file)", "",
+             "rocprofv3 --stats summary (durations in microseconds).  Cijk_* are the Q/K/V projection glue",
+             "(hipBLASLt GEMMs, outside the library and outside the timed step); __amd_rocclr_* and at::native",
+             "kernels are torch copies, fills and draws of the set-up.", "",
+             f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}"]
+    avg = {}
+    for r in stats:
+        k = _short_kernel(r["Name"])
+        avg[k] = float(r["AverageNs"]) / 1e3
+        lines.append(f"{k[:58]:58s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    lines += ["", "Per library call at the stage shape (sum of its kernels' averages):"]
+    for call, (_, ks) in PROFILE_CALLS.items():
+        if all(k in avg for k in ks):
+            parts = " + ".join(f"{avg[k]:.2f}" for k in ks)
+            lines.append(f"    {call} = {' + '.join(ks)}")
+            lines.append(f"        = {parts} = {sum(avg[k] for k in ks):.2f} us")
+    lines += ["", "bench.py times the same calls with HIP events on the launch stream; its per-call averages",
+              "include the gaps between kernels, so they read slightly above these sums."]
+    open(os.path.join(prof, "kernel_trace_stage_32k.txt"), "w").write("\n".join(lines) + "\n")
+    # ---- HBM traffic ----
+    fetch, write = _counter_kib(os.path.join(run_dir, "fetch")), _counter_kib(os.path.join(run_dir, "write"))
+    cf, cw = _counter_kib(os.path.join(run_dir, "copy_fetch")), _counter_kib(os.path.join(run_dir, "copy_write"))
+    copy_k = [k for k in cf if "copyBuffer" in k]
+    if not copy_k:
+        raise SystemExit("no copy kernel in the calibration runs")
+    nbytes = 1 << 30
+    fscale = nbytes / (cf[copy_k[0]] * 1024)  # bytes moved per KiB of counter
+    wscale = nbytes / (cw[copy_k[0]] * 1024)
+    algo = stage_algorithmic_bytes()
+    srcdir = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc")
+    t = {"calibration": {"copy_bytes": nbytes, "fetch_kib_read": cf[copy_k[0]], "write_kib_read": cw[copy_k[0]],
+                         "fetch_scale": fscale, "write_scale": wscale},
+         "commands": [cmds[k].format(dir="<dir>") for k in ("fetch", "write", "copy_fetch", "copy_write")],
+         "shape": S}
+    lines = [f"# HBM traffic per library call: {head}", "", "Commands (repository root):"]
+    lines += ["    " + cmds[k].format(dir="<dir>") for k in ("fetch", "write", "copy_fetch", "copy_write")]
+    lines += ["    python3 bench.py --summarize-profiles <dir>   (writes this file)", "",
+              f"Calibration: a plain 1 GiB device copy (torch copy_ -> {copy_k[0]}) reads FETCH_SIZE "
+              f"{cf[copy_k[0]]:.1f} KiB and WRITE_SIZE {cw[copy_k[0]]:.1f} KiB per dispatch for 1048576 KiB moved",
+              f"each way: below, one FETCH_SIZE KiB counts as {fscale:.4f} KiB read and one WRITE_SIZE KiB as "
+              f"{wscale:.4f} KiB written.", "",
+              f"{'call / kernel':48s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} {'bytes (scaled)':>16s}"]
+    for call, (src, ks) in PROFILE_CALLS.items():
+        if not all(k in fetch and k in write for k in ks):
+            lines.append(f"{call}: not in the counter runs")
+            continue
+        tot = 0.0
+        for k in ks:
+            b = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
+            tot += b
+            lines.append(f"  {k[:46]:46s} {fetch[k]:11.1f} {write[k]:11.1f} {b / 1e6:13.2f} MB")
+        lines.append(f"{call:48s} {'':11s} {'':11s} {tot / 1e6:13.2f} MB   algorithmic {algo[call] / 1e6:.2f} MB "
+                     f"(ratio {tot / algo[call]:.3f})")
+        t[src] = {"call": call, "kernels": ks, "bytes_per_launch": tot, "algorithmic_bytes": algo[call],
+                  "fetch_kib": {k: fetch[k] for k in ks}, "write_kib": {k: write[k] for k in ks},
+                  "source_sha256": _sha(os.path.join(srcdir, src))}
+    open(os.path.join(prof, "hbm_traffic_stage_32k.txt"), "w").write("\n".join(lines) + "\n")
+    json.dump(t, open(os.path.join(prof, "traffic.json"), "w"), indent=1)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,10 +693,16 @@ def main():
                     help="skip the rotary attention timing beside the plain call")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of tg_gated_attention_backward at the attention shape")
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                    help="(CPU only) turn the rocprofv3 output of the profile commands, run with their -d "
+                         "directories under DIR, into the summaries under profiles/, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
 
     if args.gpus != 1:
         print("bench.py: the gated-prefill path is measured on one MI355X only; a multi-GPU run is not "
@@ -731,7 +895,8 @@ def main():
         a = kernels[dom]
         roofline = {"kernel": dom, "bound": "hbm", "achieved": a["achieved_GBs"], "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": a["hbm_frac"], "traffic": None}
-    roofline["traffic"] = _traffic(dom_file)
+    # (the committed counters are per call at the stage shape)
+    roofline["traffic"] = _traffic(dom_file) if args.workload == "stage_32k" and n_layers == 24 else None
     ceil = None if args.no_ceilings else ceilings(torch)
     if ceil:
         if roofline["unit"] == "TFLOP/s":
