@@ -434,9 +434,14 @@ def ceilings(torch, reps=5):
     dst = torch.empty_like(src)
     a = torch.randn(8192, 8192, device=dev).bfloat16()
     b = torch.randn(8192, 8192, device=dev).bfloat16()
+    # the scorer's first layer as a plain library GEMM (no norm, no epilogue,
+    # the [N, h] product written out): residual [32768, 2048] x W1^T [2048, 256]
+    xs = torch.randn(32768, 2048, device=dev).bfloat16()
+    w1 = torch.randn(256, 2048, device=dev).bfloat16()
     res = {}
     for name, fn, work in (("copy", lambda: dst.copy_(src), 2 * (1 << 30)),
-                           ("gemm_bf16", lambda: torch.mm(a, b), 2 * 8192 ** 3)):
+                           ("gemm_bf16", lambda: torch.mm(a, b), 2 * 8192 ** 3),
+                           ("gemm_scorer", lambda: torch.mm(xs, w1.t()), 32768 * 2048 * 2)):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
@@ -447,11 +452,14 @@ def ceilings(torch, reps=5):
         e1.record()
         torch.cuda.synchronize()
         res[name] = work * reps / (e0.elapsed_time(e1) * 1e-3)
-    del src, dst, a, b
+    del src, dst, a, b, xs, w1
+    scorer_us = 32768 * 2048 * 2 / res["gemm_scorer"] * 1e6  # (work counted as the residual bytes read)
     return {"copy_GBs": round(res["copy"] / 1e9, 1), "copy_frac_of_spec": round(res["copy"] / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_bf16_TFLOPs": round(res["gemm_bf16"] / 1e12, 1),
             "gemm_bf16_frac_of_spec": round(res["gemm_bf16"] / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "gemm_shape": [8192, 8192, 8192]}
+            "gemm_shape": [8192, 8192, 8192],
+            "scorer_gemm_library_us": round(scorer_us, 2), "scorer_gemm_shape": [32768, 2048, 256],
+            "scorer_gemm_residual_GBs": round(res["gemm_scorer"] / 1e9, 1)}
 
 
 def cpu_model() -> str:
