@@ -172,6 +172,60 @@ def time_rope(torch, tg, qkv, b_S, kept_idx, layer, heads, M, base=1e6, reps=20,
             "calls_per_round": reps, "rounds": rounds}
 
 
+def time_fused_gate(torch, tg, resids, c, W1f, b1, w2, b2, reps=20, rounds=3):
+    """The whole gate as one tg_gate call (the scorer whose last workgroup of
+    each batch row runs that row's selection, then the gather) beside the
+    separate calls the step makes (tg_gate_score_folded, tg_gate_select), at
+    the step's shape: rounds of `reps` calls of each alternate on the launch
+    stream, the best round of each is reported, and the outputs of the two
+    are compared bit for bit."""
+    dev = resids[0].device
+    B, N = 1, c.N
+    M = tg.kept_count(N, c.r, c.K)
+
+    def outs():
+        return (torch.empty((B, N), dtype=torch.float32, device=dev),
+                torch.empty((B, N), dtype=torch.float32, device=dev),
+                torch.empty((B, N), dtype=torch.uint8, device=dev),
+                torch.empty((B, M), dtype=torch.int32, device=dev),
+                torch.empty((B, M, c.d), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, M), dtype=torch.float32, device=dev))
+
+    o_sep, o_fus = outs(), outs()
+    counters = tg.gate_counters(B, dev)
+
+    def separate(i):
+        raw, score, keep, ki, ro, so = o_sep
+        x = resids[i % len(resids)]
+        tg.tg_gate_score_folded(x, c.r, W1f, c.h, b1, w2, b2, c.eps_row, score_raw=raw)
+        tg.tg_gate_select(raw, x, c.r, c.K, c.eps_seq, score=score, keep=keep, kept_idx=ki, resid_out=ro,
+                          score_out=so)
+
+    def fused(i):
+        raw, score, keep, ki, ro, so = o_fus
+        tg.tg_gate(resids[i % len(resids)], c.r, c.K, W1f, c.h, b1, w2, b2, c.eps_row, c.eps_seq, score_raw=raw,
+                   score=score, keep=keep, kept_idx=ki, resid_out=ro, score_out=so, counters=counters)
+
+    for fn in (separate, fused, separate, fused):
+        fn(0)
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.uint8), b.view(torch.uint8)) for a, b in zip(o_sep, o_fus))
+    best = {"separate": float("inf"), "fused": float("inf")}
+    for _ in range(rounds):
+        for name, fn in (("separate", separate), ("fused", fused)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            best[name] = min(best[name], e0.elapsed_time(e1) * 1e3 / reps)
+    return {"call": "tg_gate", "separate_calls": ["tg_gate_score_folded", "tg_gate_select"],
+            "separate_us": round(best["separate"], 3), "fused_us": round(best["fused"], 3),
+            "fused_over_separate": round(best["fused"] / best["separate"], 4), "bit_identical": bool(same),
+            "calls_per_round": reps, "rounds": rounds}
+
+
 def time_varlen(torch, tg, layer, heads, M, n_seq=16, reps=20):
     """Token-gated attention over a packed batch of `n_seq` gated prompts
     (kept lengths uniform in [M/8, M], seeded; random bf16 q, k, v, scores and
@@ -519,7 +573,7 @@ def _cpu_sample(c, layer0_qkv, kept_idx, b_S, gain, temp, n_layers, max_rows):
 # ---------------------------------------------------------------------------
 # Profile summaries (CPU only): rocprofv3 CSV output -> the files under profiles/
 STAGE_SHAPE = dict(N=32768, r=64, d=2048, h=256, M=3341, Hq=16, Hkv=8, dh=128, kv_layers=STAGE_GATE_LAYER + 1)
-PROFILE_RUN_FLAGS = "--no-cpu-baseline --no-sub-records --no-ceilings --no-varlen --no-rope"
+PROFILE_RUN_FLAGS = "--no-cpu-baseline --no-sub-records --no-ceilings --no-varlen --no-rope --no-fused-gate"
 # library call -> (source file, kernels of one call at the stage shape)
 PROFILE_CALLS = {
     "tg_gated_attention": ("gated_attention.hip",
@@ -699,6 +753,8 @@ def main():
                     help="skip the packed varying-length attention timing")
     ap.add_argument("--no-rope", action="store_true",
                     help="skip the rotary attention timing beside the plain call")
+    ap.add_argument("--no-fused-gate", action="store_true",
+                    help="skip the timing of the one-call gate (tg_gate) beside the separate calls")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separate timing of tg_gated_attention_backward at the attention shape")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
@@ -945,6 +1001,10 @@ def main():
         out["rope_attention"] = time_rope(torch, tg, qkv[0], b_S, kept_idx, layers[0], heads, M)
         log(f"rotary attention: {out['rope_attention']['rope_us']:.2f} us per call, "
             f"{out['rope_attention']['rope_over_plain']:.3f} x the plain call")
+    if not args.no_fused_gate:
+        out["fused_gate"] = time_fused_gate(torch, tg, resids, c, W1f, b1, w2, b2)
+        log(f"one-call gate: {out['fused_gate']['fused_us']:.2f} us vs {out['fused_gate']['separate_us']:.2f} us "
+            f"for the separate calls (bit-identical: {out['fused_gate']['bit_identical']})")
     if layers and not args.no_backward:
         out["attention_backward"] = time_backward(torch, tg, qkv[0], b_S, kept_idx, layers[0], attn_out, heads, M,
                                                   stream_reps=20)

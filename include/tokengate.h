@@ -121,6 +121,34 @@ int tg_gate_score_folded(const void* resid, int dt, int B, int N, int d, int r,
                          float* score_raw, void* stream);
 
 /*
+ * tg_gate -- the whole gate in one call: the scoring network on folded
+ * weights (tg_gate_score_folded), then the sequence RMSNorm, the top-K
+ * selector and the compaction of tg_gate_select (paper, Section 4: "Scoring
+ * Network" Eq. 1 and Eq. 3, "Top-K Selector" Eq. 4; App. C.4).  Two
+ * launches: the scorer, in which the last workgroup of each batch row to
+ * finish its scores runs that row's selection (found by counting the row's
+ * finished workgroups, so no workgroup waits for another), then the gather
+ * of the kept residual rows.  Every output equals tg_gate_score_folded
+ * followed by tg_gate_select bit for bit.
+ *
+ *   resid, dt (TG_BF16 only), B, N (<= 32768), d, r, W1_folded, eps_row,
+ *   b1, h, w2, b2    as tg_gate_score_folded (score_raw [B, N] fp32 receives
+ *                    the raw scores)
+ *   eps_seq, K, score, keep, kept_idx, resid_out, score_out
+ *                    as tg_gate_select (score may be score_raw: in place)
+ *   ws, ws_bytes     B 32-bit words of ZEROS, 4-byte aligned: the row
+ *                    counters.  The call leaves them zero, so one buffer
+ *                    zeroed once serves every later call.  Calls that share
+ *                    a counter buffer must not overlap in time.
+ */
+int tg_gate(const void* resid, int dt, int B, int N, int d, int r,
+            const void* W1_folded, float eps_row, const float* b1, int h,
+            const void* w2, const float* b2, float eps_seq, int K,
+            float* score_raw, float* score, uint8_t* keep, int32_t* kept_idx,
+            void* resid_out, float* score_out, void* ws, size_t ws_bytes,
+            void* stream);
+
+/*
  * tg_gate_score_noalloc -- tg_gate_score for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid hipMalloc): the same computation and the same result bits,

@@ -29,7 +29,7 @@ EXPORTED = ("tg_gate_score", "tg_seq_rmsnorm", "tg_topk_select", "tg_compact", "
             "tg_topk_select_span", "tg_gate_select_span", "tg_gate_select_varlen", "tg_gate_score_varlen", "tg_gated_attention_varlen",
             "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc", "tg_gate_select_padded",
             "tg_gated_attention_padded", "tg_gate_fold_weights", "tg_gate_score_folded",
-            "tg_gated_attention_rope_varlen", "tg_gated_attention_rope_backward_varlen", "tg_workspace_size",
+            "tg_gated_attention_rope_varlen", "tg_gated_attention_rope_backward_varlen", "tg_gate", "tg_workspace_size",
             "tg_last_error", "tg_version")
 
 _lib = None
@@ -68,6 +68,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.tg_gate_score_noalloc.argtypes = [vp, i, i, i, i, i, vp, f, vp, vp, i, vp, vp, vp, vp]
     lib.tg_gate_fold_weights.argtypes = [vp, vp, i, i, i, vp, sz, vp]
     lib.tg_gate_score_folded.argtypes = [vp, i, i, i, i, i, vp, f, vp, i, vp, vp, vp, vp]
+    lib.tg_gate.argtypes = [vp, i, i, i, i, i, vp, f, vp, i, vp, vp, f, i, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tg_gate_select_padded.argtypes = [vp, i, i, i, f, vp, i, vp, i, i, vp, vp, vp, vp, vp, vp, vp]
     lib.tg_gated_attention_padded.argtypes = [vp, vp, vp, i, i, vp, i, i, i, vp, vp, vp, vp, f, vp, vp, vp, sz, vp]
     lib.tg_seq_rmsnorm_span.argtypes = [vp, i, i, i, i, f, vp, vp, sz, vp]
@@ -96,7 +97,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                  "tg_gated_attention_varlen", "tg_gated_attention_backward_varlen", "tg_gate_score_noalloc",
                  "tg_gate_select_padded", "tg_gated_attention_padded", "tg_gate_fold_weights",
                  "tg_gate_score_folded", "tg_gated_attention_rope_varlen",
-                 "tg_gated_attention_rope_backward_varlen"):
+                 "tg_gated_attention_rope_backward_varlen", "tg_gate"):
         getattr(lib, name).restype = i
     if path is None:
         _lib = lib
@@ -208,6 +209,47 @@ def tg_gate_score_folded(resid, r: int, W1_folded, h: int, b1, w2, b2, eps_row: 
     _check(lib.tg_gate_score_folded(_ptr(resid), TG_BF16, B, N, d, r, _ptr(W1_folded), eps_row, _ptr(b1), h, _ptr(w2),
                                     _ptr(b2), _ptr(score_raw), _stream(stream)))
     return score_raw
+
+
+def gate_counters(B: int, device="cuda") -> torch.Tensor:
+    """The row counters :func:`tg_gate` takes: B zeroed 32-bit words (every
+    call leaves them zero, so one buffer serves all later calls that do not
+    overlap in time)."""
+    return torch.zeros(max(B, 1), dtype=torch.int32, device=device)
+
+
+def tg_gate(resid, r: int, K: int, W1_folded, h: int, b1, w2, b2, eps_row: float = 1e-6, eps_seq: float = 1e-6,
+            score_raw=None, score=None, keep=None, kept_idx=None, resid_out=None, score_out=None, counters=None,
+            stream=None):
+    """The whole gate in one call (bf16, N <= 32768): :func:`tg_gate_score_folded`
+    then :func:`tg_gate_select`, bit for bit, in two launches.  Returns
+    ``(kept_idx, resid_out, score_out, keep, score)`` as :func:`tg_gate_select`;
+    ``counters`` from :func:`gate_counters` (made here when omitted)."""
+    lib = load_library()
+    _need(resid, "resid", torch.bfloat16)
+    B, N, d = resid.shape
+    _need(W1_folded, "W1_folded", torch.uint8, (h * d * 2,))
+    dev = resid.device
+    M = kept_count(N, r, K)
+    if score_raw is None:
+        score_raw = torch.empty((B, N), dtype=torch.float32, device=dev)
+    if score is None:
+        score = score_raw
+    if keep is None:
+        keep = torch.empty((B, N), dtype=torch.uint8, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((B, M), dtype=torch.int32, device=dev)
+    if resid_out is None:
+        resid_out = torch.empty((B, M, d), dtype=resid.dtype, device=dev)
+    if score_out is None:
+        score_out = torch.empty((B, M), dtype=torch.float32, device=dev)
+    if counters is None:
+        counters = gate_counters(B, dev)
+    _need(counters, "counters", torch.int32)
+    _check(lib.tg_gate(_ptr(resid), TG_BF16, B, N, d, r, _ptr(W1_folded), eps_row, _ptr(b1), h, _ptr(w2), _ptr(b2),
+                       eps_seq, K, _ptr(score_raw), _ptr(score), _ptr(keep), _ptr(kept_idx), _ptr(resid_out),
+                       _ptr(score_out), _ptr(counters), counters.numel() * 4, _stream(stream)))
+    return kept_idx, resid_out, score_out, keep, score
 
 
 def tg_gate_score_noalloc(resid, r: int, norm_w, W1, b1, w2, b2, eps_row: float = 1e-6, score_raw=None,

@@ -34,11 +34,25 @@
 // staged in LDS.
 #include <mutex>
 
+#include "gate_select_row.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
 namespace tg {
 namespace {
+
+// The selection part of the fused gate (tg_gate): the row's last workgroup
+// to finish its scores runs it, found by counting finished workgroups in
+// count[b] (left at zero for the next call).
+struct FusedSelect {
+  float eps_seq;
+  int K;
+  float* score;
+  uint8_t* keep;
+  int32_t* kept_idx;
+  float* score_kept;
+  uint32_t* count;
+};
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -78,7 +92,11 @@ __global__ __launch_bounds__(kThreads) void fold_norm_weight_kernel(const uint16
   store16(W1f + (size_t)u * 8, o);
 }
 
-template <int H, int ROWS, int WAVES, int NCH_FIXED>
+// s_waitcnt vmcnt(0): every store (and load) this wave issued has completed
+// at its L2 (a workgroup barrier alone does not wait for them)
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int H, int ROWS, int WAVES, int NCH_FIXED, bool FUSED = false>
 __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint16_t* __restrict__ resid, int N,
                                                                    int d, int r_in, int p1_in,
                                                                    const int32_t* __restrict__ span_begin,
@@ -87,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
                                                                    const float* __restrict__ b1,
                                                                    const uint16_t* __restrict__ w2,
                                                                    const float* __restrict__ b2,
-                                                                   float* __restrict__ out) {
+                                                                   float* __restrict__ out, const FusedSelect fs) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int RT = ROWS / 16;               // 16-row MFMA tiles (each wave covers every row)
   constexpr int CT = H / (WAVES * 16);        // 16-column MFMA tiles per wave
@@ -95,9 +113,14 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
   constexpr int GR = RT / WAVES;              // row tiles whose sum of squares this wave computes
   static_assert(AL >= 1 && CT >= 1 && GR >= 1 && AL * THREADS == ROWS * kTpr && GR * WAVES == RT, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * kLda];
-  __shared__ float s_inv[ROWS];
-  __shared__ float s_part[WAVES][ROWS];
+  // LDS: the residual chunks, 1/rms and the per-wave partials of the h -> 1
+  // sum (the fused gate's selection reuses the same bytes afterwards)
+  constexpr size_t kScoreLds = (size_t)2 * ROWS * kLda * 2 + ROWS * 4 + (size_t)WAVES * ROWS * 4;
+  constexpr size_t kLdsBytes = FUSED && selrow::kSelLdsBytes > kScoreLds ? selrow::kSelLdsBytes : kScoreLds;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  auto& sA = *reinterpret_cast<uint16_t(*)[2][ROWS * kLda]>(smem);
+  auto& s_inv = *reinterpret_cast<float(*)[ROWS]>(smem + (size_t)2 * ROWS * kLda * 2);
+  auto& s_part = *reinterpret_cast<float(*)[WAVES][ROWS]>(smem + (size_t)2 * ROWS * kLda * 2 + ROWS * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,12 +136,14 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
 
   for (int j = blockIdx.x * THREADS + tid; j < r; j += gridDim.x * THREADS) ob[j] = 0.0f;
   for (int j = p1 + blockIdx.x * THREADS + tid; j < N; j += gridDim.x * THREADS) ob[j] = 0.0f;
-  if (row0 >= p1) return;  // whole workgroup: no barrier is skipped by part of it
+  // whole workgroup: no barrier is skipped by part of it (the fused gate's
+  // workgroups all reach its count, an empty tile with a zero-size range)
+  if (!FUSED && row0 >= p1) return;
 
   // residual tile: rows past the span read as 0 through the buffer range check
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(resid + ((size_t)b * N + row0) * d), (short)0, (int)((size_t)(p1 - row0) * d * 2),
-      kBufferConfig);
+      const_cast<uint16_t*>(resid + ((size_t)b * N + row0) * d), (short)0,
+      (int)((size_t)max(p1 - row0, 0) * d * 2), kBufferConfig);
   const __amdgpu_buffer_rsrc_t w_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W1w), (short)0, (int)((size_t)H * d * 2), kBufferConfig);
   // slot e of this thread: row (tid + 256 e) / kTpr, columns kp*8 .. kp*8+7 of each chunk
@@ -270,6 +295,30 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
     for (int w = 1; w < WAVES; ++w) v += s_part[w][tid];
     ob[row0 + tid] = v + b2[0];
   }
+  if constexpr (FUSED) {
+    // the row's last workgroup to finish runs the selection on all of its
+    // scores.  Every wave waits until its score stores have reached its L2;
+    // after the barrier, thread 0's release (one write-back of this XCD's L2
+    // per workgroup) makes them visible device-wide before the workgroup is
+    // counted.  Only the last workgroup acquires (invalidating its caches)
+    // before it reads the others' scores: an acquire in every workgroup would
+    // evict the W1 tiles that the running workgroups stream from L2.
+    wait_own_stores();
+    __syncthreads();  // (also: every read of s_part is done; LDS is free)
+    uint32_t* s_flag = reinterpret_cast<uint32_t*>(smem);
+    if (tid == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(fs.count + b, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      *s_flag = done == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    __syncthreads();  // every thread has the flag before the selection reuses LDS
+    if (!last) return;  // (workgroup-uniform)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    selrow::gate_select_row<THREADS>(out, N, r_in, p1_in, fs.eps_seq, fs.K, VarlenRows{}, fs.score, fs.keep,
+                                     fs.kept_idx, fs.score_kept, b, selrow::carve_sel_lds(smem));
+    if (tid == 0) fs.count[b] = 0u;  // zero again for the next call
+  }
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -343,25 +392,35 @@ __global__ __launch_bounds__(kThreads) void gate_score_f32_kernel(const float* _
 template <int H, int ROWS, int WAVES>
 hipError_t launch_rows(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
                        const int32_t* se, float eps, const uint16_t* W1w,
-                       const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
+                       const float* b1, const uint16_t* w2, const float* b2, float* out, const FusedSelect* fs,
+                       hipStream_t s) {
   const int P = p1 - r;
   const int nblk = P > 0 ? (P + ROWS - 1) / ROWS : 1;
   // d = 2048 (the model width) gets a fully unrolled chunk loop: the compiler
   // then counts outstanding loads exactly instead of waiting for all of them
   // at the loop's back edge, which would void the prefetch ring
-  if (d == 2048)
+  if (fs != nullptr) {
+    if (d == 2048)
+      hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 32, true>), dim3(nblk, B), dim3(64 * WAVES), 0, s,
+                         resid, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, *fs);
+    else
+      hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 0, true>), dim3(nblk, B), dim3(64 * WAVES), 0, s,
+                         resid, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, *fs);
+  } else if (d == 2048) {
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 32>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid,
-                       N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out);
-  else
+                       N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, FusedSelect{});
+  } else {
     hipLaunchKernelGGL((gate_score_bf16_kernel<H, ROWS, WAVES, 0>), dim3(nblk, B), dim3(64 * WAVES), 0, s, resid, N,
-                       d, r, p1, sb, se, eps, W1w, b1, w2, b2, out);
+                       d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, FusedSelect{});
+  }
   return hipGetLastError();
 }
 
 template <int H>
 hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
                          const int32_t* se, float eps, const uint16_t* W1w,
-                         const float* b1, const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
+                         const float* b1, const uint16_t* w2, const float* b2, float* out, const FusedSelect* fs,
+                         hipStream_t s) {
   // Every workgroup streams all of W1w through L1, so W1 bytes per token fall
   // with the tile height: 128-token tiles of 8 waves (each wave with the
   // registers of the 64-token layout's waves) once they still give about
@@ -369,9 +428,24 @@ hipError_t launch_bf16_h(const uint16_t* resid, int B, int N, int d, int r, int 
   const int P = p1 - r;
   if constexpr (H >= 128) {
     if ((long long)B * ((P + 127) / 128) >= kTallTileMinBlocks)
-      return launch_rows<H, 128, 8>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, s);
+      return launch_rows<H, 128, 8>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, fs, s);
   }
-  return launch_rows<H, 64, 4>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, s);
+  return launch_rows<H, 64, 4>(resid, B, N, d, r, p1, sb, se, eps, W1w, b1, w2, b2, out, fs, s);
+}
+
+hipError_t launch_folded_h(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
+                           const int32_t* se, float eps_row, const uint16_t* W1w, const float* b1, int h,
+                           const uint16_t* w2, const float* b2, float* out, const FusedSelect* fs, hipStream_t s) {
+  switch (h) {
+    case 64:
+      return launch_bf16_h<64>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, fs, s);
+    case 128:
+      return launch_bf16_h<128>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, fs, s);
+    case 256:
+      return launch_bf16_h<256>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, fs, s);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -423,16 +497,21 @@ hipError_t launch_gate_score_bf16(const uint16_t* resid, int B, int N, int d, in
 hipError_t launch_gate_score_folded(const uint16_t* resid, int B, int N, int d, int r, int p1, const int32_t* sb,
                                     const int32_t* se, float eps_row, const uint16_t* W1w, const float* b1, int h,
                                     const uint16_t* w2, const float* b2, float* out, hipStream_t s) {
-  switch (h) {
-    case 64:
-      return launch_bf16_h<64>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
-    case 128:
-      return launch_bf16_h<128>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
-    case 256:
-      return launch_bf16_h<256>(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, w2, b2, out, s);
-    default:
-      return hipErrorInvalidValue;
-  }
+  return launch_folded_h(resid, B, N, d, r, p1, sb, se, eps_row, W1w, b1, h, w2, b2, out, nullptr, s);
+}
+
+hipError_t launch_gate_fused(const uint16_t* resid, int B, int N, int d, int r, const uint16_t* W1w, float eps_row,
+                             const float* b1, int h, const uint16_t* w2, const float* b2, float eps_seq, int K,
+                             float* score_raw, float* score, uint8_t* keep, int32_t* kept_idx, uint16_t* resid_out,
+                             float* score_kept, uint32_t* count, hipStream_t s) {
+  if (N > sel::kRowChunk) return hipErrorInvalidValue;
+  const FusedSelect fs{eps_seq, K, score, keep, kept_idx, score_kept, count};
+  hipError_t e = launch_folded_h(resid, B, N, d, r, N, nullptr, nullptr, eps_row, W1w, b1, h, w2, b2, score_raw,
+                                 &fs, s);
+  if (e != hipSuccess) return e;
+  const int P = N - r;
+  const int M = N - P + (K < P ? K : P);
+  return launch_compact_gather(resid, (size_t)d * 2, B, N, M, kept_idx, resid_out, s);
 }
 
 hipError_t launch_gate_score_f32(const float* resid, int B, int N, int d, int r, int p1, const int32_t* sb,

@@ -37,28 +37,67 @@ __device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r
   return v;
 }
 
-// Block-wide 1 / sqrt(mean of squares + eps) of a row whose scores this
-// thread holds in v (zeros outside the prunable span), P prunable scores.
-// Each thread's sum of squares (32 terms) is fp32; thread and wave partials
-// are combined in fp64 in a fixed order.  0 when P == 0.  Contains barriers.
-__device__ __forceinline__ double row_inv_rms(const f32x4 (&v)[kRowVec], int P, float eps, double* s_part,
-                                              double* s_scale) {
-  const int tid = threadIdx.x;
+// A workgroup of THREADS threads (a divisor of kRowThreads) stands in for
+// the kRowThreads threads of the row layout: thread t plays the parts of
+// threads t + s THREADS, s < kRowThreads / THREADS, and holds their groups
+// in v[s kRowVec + e].  Every result below is the same bit for bit whatever
+// THREADS is.
+template <int THREADS>
+constexpr int kRowParts = kRowThreads / THREADS;
+
+// Fixed-order fp32 sum of squares of one row-layout thread's kRowVec groups.
+__device__ __forceinline__ float part_sum_squares(const f32x4* v) {
   float part = 0.0f;
 #pragma unroll
   for (int e = 0; e < kRowVec; ++e)
 #pragma unroll
     for (int i = 0; i < 4; ++i) part = fmaf(v[e][i], v[e][i], part);
-  double acc = wave_sum_f64((double)part);
-  if ((tid & 63) == 0) s_part[tid >> 6] = acc;
+  return part;
+}
+
+// The row reduction in two halves: rms_part adds part s's fp32 sum of
+// squares (row-layout threads tid + s THREADS) to the fp64 wave partials in
+// s_part (kRowThreads / 64 doubles); rms_finish combines them in a fixed
+// order into 1 / sqrt(mean of squares + eps) over P prunable scores (0 when
+// P == 0).  rms_finish contains barriers.
+template <int THREADS>
+__device__ __forceinline__ void rms_part(float part, int s, double* s_part) {
+  static_assert(kRowThreads % THREADS == 0 && THREADS % 64 == 0, "row parts");
+  // the lanes of this wave are row-layout threads of one row-layout wave
+  const double acc = wave_sum_f64((double)part);
+  if ((threadIdx.x & 63) == 0) s_part[(threadIdx.x >> 6) + s * (THREADS / 64)] = acc;
+}
+__device__ __forceinline__ double rms_finish(int P, float eps, double* s_part, double* s_scale) {
   __syncthreads();
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     double t = 0.0;
     for (int w = 0; w < kRowThreads / 64; ++w) t += s_part[w];
     *s_scale = P > 0 ? 1.0 / sqrt(t / (double)P + (double)eps) : 0.0;
   }
   __syncthreads();
   return *s_scale;
+}
+
+// Block-wide 1 / sqrt(mean of squares + eps) of a row from the fp32 sums of
+// squares of this thread's parts: wave and block partials are combined in
+// fp64 in a fixed order.  Contains barriers.
+template <int THREADS = kRowThreads>
+__device__ __forceinline__ double row_inv_rms_parts(const float (&part)[kRowParts<THREADS>], int P, float eps,
+                                                    double* s_part, double* s_scale) {
+#pragma unroll
+  for (int s = 0; s < kRowParts<THREADS>; ++s) rms_part<THREADS>(part[s], s, s_part);
+  return rms_finish(P, eps, s_part, s_scale);
+}
+
+// The same, from the row-layout groups this thread holds in v (zeros outside
+// the prunable span): v[s kRowVec + e] is group e of part s.
+template <int THREADS = kRowThreads>
+__device__ __forceinline__ double row_inv_rms(const f32x4 (&v)[kRowVec * kRowParts<THREADS>], int P, float eps,
+                                              double* s_part, double* s_scale) {
+  float part[kRowParts<THREADS>];
+#pragma unroll
+  for (int s = 0; s < kRowParts<THREADS>; ++s) part[s] = part_sum_squares(v + s * kRowVec);
+  return row_inv_rms_parts<THREADS>(part, P, eps, s_part, s_scale);
 }
 
 // Order-preserving key: larger score -> larger key; -0.0 folds onto +0.0;
@@ -86,7 +125,9 @@ struct Threshold {
 // Block-wide radix select over P keys in LDS (key_slot order) for the K'-th
 // largest, 0 < K' < P, three digits [31:21], [20:10], [9:0].  On entry
 // s_hist holds the histogram of digit [31:21] of all P keys (2048 bins).
-// s_wave holds 16 words, s_sel 3.  Contains barriers.
+// s_wave holds 16 words, s_sel 3.  Contains barriers.  Integer counting
+// only: the threshold does not depend on THREADS.
+template <int THREADS = kRowThreads>
 __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, int P, uint32_t Kp, uint32_t* s_hist,
                                                       uint32_t* s_wave, uint32_t* s_sel) {
   const int tid = threadIdx.x;
@@ -96,21 +137,21 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     if (pass > 0) {
-      for (int i = tid; i < nb; i += kRowThreads) s_hist[i] = 0;
+      for (int i = tid; i < nb; i += THREADS) s_hist[i] = 0;
       __syncthreads();
       // batches of kBatch keys per thread: every LDS read of a batch is issued
       // before any is tested
       constexpr int kBatch = 8;
-      for (int j0 = tid; j0 < P; j0 += kBatch * kRowThreads) {
+      for (int j0 = tid; j0 < P; j0 += kBatch * THREADS) {
         uint32_t key[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const int j = j0 + u * kRowThreads;
+          const int j = j0 + u * THREADS;
           key[u] = j < P ? s_keys[key_slot(j)] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-          if (j0 + u * kRowThreads < P && (key[u] & pmask) == prefix)
+          if (j0 + u * THREADS < P && (key[u] & pmask) == prefix)
             atomicAdd(&s_hist[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
       }
     }
@@ -118,11 +159,11 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
     // Bins in descending digit order; thread t owns descending bins
     // [t*per, t*per + per).  Find the bin where the running count from the
     // top first reaches krem.
-    const int per = nb / kRowThreads;  // 2 or 1
+    const int per = nb / THREADS;  // bins per thread
     uint32_t local = 0;
     for (int e = 0; e < per; ++e) local += s_hist[nb - 1 - (tid * per + e)];
     uint32_t tot;
-    uint32_t cum = block_excl_scan_u32<kRowThreads / 64>(local, s_wave, tot);
+    uint32_t cum = block_excl_scan_u32<THREADS / 64>(local, s_wave, tot);
     for (int e = 0; e < per; ++e) {
       const int digit = nb - 1 - (tid * per + e);
       const uint32_t c = s_hist[digit];

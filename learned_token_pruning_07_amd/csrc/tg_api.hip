@@ -275,6 +275,39 @@ int tg_gate_score_noalloc(const void* resid, int dt, int B, int N, int d, int r,
                            b1, h, w2, b2, score_raw, nullptr, 0, stream, true);
 }
 
+int tg_gate(const void* resid, int dt, int B, int N, int d, int r, const void* W1_folded, float eps_row,
+            const float* b1, int h, const void* w2, const float* b2, float eps_seq, int K, float* score_raw,
+            float* score, uint8_t* keep, int32_t* kept_idx, void* resid_out, float* score_out, void* ws,
+            size_t ws_bytes, void* stream) {
+  const char* name = "tg_gate";
+  if (dt != TG_BF16) return fail(TG_EUNSUPPORTED, "%s: the fused gate takes a bf16 residual", name);
+  if (B <= 0 || B > 65535 || N <= 0 || d <= 0 || h <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);
+  if (N > 32768) return fail(TG_EUNSUPPORTED, "%s: rows of up to 32768 tokens (N=%d)", name, N);
+  if (r < 0 || r > N) return fail(TG_EINVAL, "%s: r=%d outside [0, N=%d]", name, r, N);
+  if (K < 0) return fail(TG_EINVAL, "%s: K=%d must be >= 0", name, K);
+  if (!(eps_row >= 0.0f) || !(eps_seq >= 0.0f)) return fail(TG_EINVAL, "%s: eps_row and eps_seq must be >= 0", name);
+  const int P = N - r;
+  const int M = N - P + (K < P ? K : P);
+  if (!resid || !W1_folded || !b1 || !w2 || !b2 || !score_raw || !score || !keep ||
+      (M > 0 && (!kept_idx || !resid_out || !score_out)))
+    return fail(TG_EINVAL, "%s: null pointer argument", name);
+  if (!aligned16(resid) || !aligned16(W1_folded) || !aligned4(b1) || !aligned4(b2) || !aligned4(score_raw) ||
+      !aligned4(score) || (M > 0 && (!aligned16(resid_out) || !aligned4(kept_idx) || !aligned4(score_out))))
+    return fail(TG_EINVAL, "%s: misaligned pointer", name);
+  if (d % 64 != 0) return fail(TG_EUNSUPPORTED, "%s: needs d %% 64 == 0 (d=%d)", name, d);
+  if (h != 64 && h != 128 && h != 256) return fail(TG_EUNSUPPORTED, "%s: h in {64,128,256} (h=%d)", name, h);
+  // one counting word per batch row, zero on entry and left zero
+  if (!ws || ws_bytes < (size_t)B * 4) return fail(TG_EINVAL, "%s: workspace of %zu bytes needed, %zu given", name,
+                                                   (size_t)B * 4, ws_bytes);
+  if (!aligned4(ws)) return fail(TG_EINVAL, "%s: misaligned workspace", name);
+  return hip_status(tg::launch_gate_fused(static_cast<const uint16_t*>(resid), B, N, d, r,
+                                          static_cast<const uint16_t*>(W1_folded), eps_row, b1, h,
+                                          static_cast<const uint16_t*>(w2), b2, eps_seq, K, score_raw, score, keep,
+                                          kept_idx, static_cast<uint16_t*>(resid_out), score_out,
+                                          static_cast<uint32_t*>(ws), reinterpret_cast<hipStream_t>(stream)),
+                    name);
+}
+
 int tg_gate_score_span(const void* resid, int dt, int B, int N, int d, int span_begin, int span_end,
                        const void* norm_w, float eps_row, const void* W1, const float* b1, int h, const void* w2,
                        const float* b2, float* score_raw, void* ws, size_t ws_bytes, void* stream) {

@@ -73,6 +73,15 @@ __device__ __forceinline__ RowSpec varlen_row(const VarlenRows& vr, int b, int N
 // workgroup; the kernels of the longer rows skip it.
 constexpr int kVarlenOneGroupRow = 32768;
 
+// The whole gate in two launches (bf16 residual, N <= 32768): the folded
+// scorer, whose last workgroup of each row runs that row's selection
+// (count: B zeroed words, left zeroed), then the kept rows' gather.  The
+// results equal launch_gate_score_folded + launch_gate_select bit for bit.
+hipError_t launch_gate_fused(const uint16_t* resid, int B, int N, int d, int r, const uint16_t* W1w, float eps_row,
+                             const float* b1, int h, const uint16_t* w2, const float* b2, float eps_seq, int K,
+                             float* score_raw, float* score, uint8_t* keep, int32_t* kept_idx, uint16_t* resid_out,
+                             float* score_kept, uint32_t* count, hipStream_t s);
+
 size_t seq_rmsnorm_workspace(int B, int N);
 hipError_t launch_seq_rmsnorm(const float* in, int B, int N, int r, int p1, float eps, float* out, void* ws,
                               hipStream_t s);

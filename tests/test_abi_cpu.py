@@ -431,3 +431,33 @@ def test_gate_select_varlen_long_rows_need_the_workspace(lib):
     assert call(NULL, 0) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(FAKE, need - 1) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(FAKE_ODD, need) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+
+
+def test_gate_fused_validation(lib):
+    """tg_gate: bf16 rows of up to 32768 tokens, d a multiple of 64, h of
+    64 / 128 / 256, and B zeroed counting words in the workspace."""
+    args = dict(resid=FAKE, dt=tgb.TG_BF16, B=2, N=4096, d=256, r=4, W1=FAKE, eps_row=1e-6, b1=FAKE, h=128,
+                w2=FAKE, b2=FAKE, eps_seq=1e-6, K=100, raw=FAKE, score=FAKE, keep=FAKE, ki=FAKE, ro=FAKE, so=FAKE,
+                ws=FAKE, ws_bytes=8)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.tg_gate(a["resid"], a["dt"], a["B"], a["N"], a["d"], a["r"], a["W1"], a["eps_row"], a["b1"],
+                           a["h"], a["w2"], a["b2"], a["eps_seq"], a["K"], a["raw"], a["score"], a["keep"], a["ki"],
+                           a["ro"], a["so"], a["ws"], a["ws_bytes"], None)
+
+    assert call(dt=tgb.TG_F32) == tgb.TG_EUNSUPPORTED and "bf16" in _err(lib)
+    assert call(N=32769) == tgb.TG_EUNSUPPORTED and "32768" in _err(lib)
+    assert call(N=0) == tgb.TG_EINVAL
+    assert call(B=0) == tgb.TG_EINVAL
+    assert call(r=4097) == tgb.TG_EINVAL and "outside" in _err(lib)
+    assert call(K=-1) == tgb.TG_EINVAL
+    assert call(eps_seq=-1.0) == tgb.TG_EINVAL
+    assert call(resid=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert call(ki=NULL) == tgb.TG_EINVAL and "null" in _err(lib)
+    assert call(resid=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+    assert call(d=136) == tgb.TG_EUNSUPPORTED
+    assert call(h=96) == tgb.TG_EUNSUPPORTED
+    assert call(ws=NULL, ws_bytes=0) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(ws_bytes=7) == tgb.TG_EINVAL and "workspace" in _err(lib)
+    assert call(ws=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
