@@ -18,8 +18,11 @@
 //    cross-workgroup traffic, fixed summation order).
 //  * The residual tile streams HBM -> registers -> LDS in 64-column chunks:
 //    loads run kDepth chunks ahead in a register ring (enough bytes in flight
-//    per CU to cover HBM latency), LDS is double-buffered.  Wave w computes
-//    every row of the tile x its h/4 hidden units with
+//    per CU to cover HBM latency), LDS is double-buffered.  A chunk row is
+//    128 bytes whose 16-byte units are XOR-swizzled by the row's low three
+//    bits: the fragment reads (16 rows x 4 units per k-step) are then free of
+//    bank conflicts on gfx950, where padded 144-byte rows conflicted 2-way.
+//    Wave w computes every row of the tile x its h/4 hidden units with
 //    v_mfma_f32_16x16x32_bf16 (fp32 accumulate), its W1w slice streaming from
 //    L2 straight into B fragments one chunk ahead.  All global loads are raw
 //    buffer loads with a scalar chunk offset: the loop issues no address
@@ -57,7 +60,7 @@ struct FusedSelect {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kKC = 64;             // residual columns per chunk
-constexpr int kLda = kKC + 8;       // padded LDS row (bf16): conflict-free fragment reads
+constexpr int kLda = kKC;           // LDS row (bf16): 128 bytes, 16-byte units XOR-swizzled by row & 7
 constexpr int kTpr = kKC / 8;       // threads per row per chunk (16 bytes each)
 constexpr int kBufferConfig = 0x00020000;  // raw buffer resource word 3 (gfx9 family, 32-bit data)
 constexpr int kDepth = 4;           // residual chunks in flight per workgroup
@@ -153,11 +156,10 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
   for (int e = 0; e < AL; ++e) {
     const int row = (tid + THREADS * e) / kTpr;
     a_off[e] = (row * d + kp * 8) * 2;
-    a_lds[e] = row * kLda + kp * 8;
+    a_lds[e] = row * kLda + ((kp ^ (row & 7)) * 8);
   }
   // this lane's B fragments in the fragment-ordered W1w (see fold_norm_weight_kernel)
   const int ncol0 = wid * (H / WAVES) + (lane & 15);
-  const int kq = (lane >> 4) * 8;  // k offset of this lane inside a 32-wide k-step
   constexpr int kStepBytes = WAVES * CT * 64 * 16;  // one (chunk, k-step) of W1w: H / 16 KiB
   int w_off[CT];
 #pragma unroll
@@ -233,7 +235,8 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
           bf16x8 af[RT];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
-            af[rt] = *reinterpret_cast<const bf16x8*>(&sA[buf][(rt * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
+            af[rt] = *reinterpret_cast<const bf16x8*>(
+                &sA[buf][(rt * 16 + (lane & 15)) * kLda + (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
 #pragma unroll
           for (int i = 0; i < GR; ++i) {
             const bf16x8 gf = *reinterpret_cast<const bf16x8*>(
-                &sA[buf][((wid + WAVES * i) * 16 + (lane & 15)) * kLda + ks * 32 + kq]);
+                &sA[buf][((wid + WAVES * i) * 16 + (lane & 15)) * kLda + (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
             gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, gf, gram[i], 0, 0, 0);
           }
         }

@@ -449,6 +449,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   constexpr int DT = DH / 32;      // 32-row tiles of O^T
   constexpr int KROW = DH * 2;      // bytes of a K row in LDS (unpadded, swizzled)
   constexpr int KCH = DH / 8;       // its 16-byte chunks
+  // LDS swizzles: row r of a tile holds its 16-byte chunk u at position
+  // u ^ h(r).  With h = r & 7 the fragment reads (32 rows x 2 chunks per
+  // MFMA) conflict 2-way on gfx950; folding row bit 3 in removes that: into
+  // chunk bit 3 for 256-byte K rows (h = r & 15), into chunk bit 0 for
+  // 128-byte rows (V^T, and K at DH = 64).
+  auto swz_k = [](int r) { return DH == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1)); };
+  auto swz_v = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
   constexpr int VROW = kBK * 2;     // bytes of a V^T row (64 keys, fp16)
   constexpr int TILE = kBK * DH * 2;           // bytes of a K tile = bytes of a V^T tile
   constexpr int NI = TILE / 1024 / 4;          // 1 KiB loads per wave per tile, for each of K and V^T
@@ -561,9 +568,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
 #pragma unroll
   for (int e = 0; e < NI; ++e) {
     const int Y = (wid * NI + e) * 64 + lane;
-    const int kr = Y / KCH, kc = (Y % KCH) ^ (kr & 7);
+    const int kr = Y / KCH, kc = (Y % KCH) ^ swz_k(kr);
     k_off[e] = kr * Hkv * DH * 2 + kc * 16;
-    const int vr = Y / (VROW / 16), vc = (Y % (VROW / 16)) ^ (vr & 7);
+    const int vr = Y / (VROW / 16), vc = (Y % (VROW / 16)) ^ swz_v(vr);
     v_off[e] = vr * Mp * 2 + vc * 16;
   }
   auto k_tile = [&](int buf) { return smem + (buf * kGroups + grp) * TILE; };
@@ -598,8 +605,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   // this lane's fragment chunks: K row ql (and ql + 32) chunk 2ks + gq; V^T row
   // 32t + ql chunk 2st + gq -- both swizzled by ql & 7
   const int q7 = ql & 7;
-  auto k_frag_off = [&](int ks) { return ql * KROW + (((2 * ks + gq) ^ q7) << 4); };
-  auto v_frag_off = [&](int st) { return ql * VROW + (((2 * st + gq) ^ q7) << 4); };
+  auto k_frag_off = [&](int ks) { return ql * KROW + (((2 * ks + gq) ^ swz_k(ql)) << 4); };
+  auto v_frag_off = [&](int st) { return ql * VROW + (((2 * st + gq) ^ swz_v(ql)) << 4); };
 
   float cq = 0.0f;    // per-query logit scale in the log2 domain
   f32x16 o[DT];
@@ -713,15 +720,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   f32x16 cm;
   auto cm_value = [&]() { return (m_run == -INFINITY || cq == 0.0f) ? 0.0f : -m_run / cq; };
   // This lane's fragment chunks, as loop-invariant LDS offsets: with
-  // c = q7 >> 1 and e = q7 & 1, chunk (2j + gq) ^ q7 = 2 (j ^ c) + (gq ^ e),
-  // so K k-step ks sits at k_lane[ks & 3] + 128 (ks >> 2) and V^T step st at
-  // v_lane[st]; ring slot and half tile only add constants.
+  // c = q7 >> 1, e = q7 & 1 and b3 = bit 3 of ql, V^T chunk (2j + gq) ^ swz_v(ql)
+  // = 2 (j ^ c) + (gq ^ e ^ b3), so V^T step st sits at v_lane[st].  K chunk
+  // (2 ks + gq) ^ swz_k(ql) adds 8 ((ks >> 2) ^ b3) at DH = 128: k_lane[j]
+  // holds the b3 term, whose 128-byte bit is the only set bit 7 of the
+  // offset, so k-step ks sits at k_lane[ks & 3] ^ (128 (ks >> 2)).  Ring slot
+  // and half tile only add constants.
   int k_lane[4], v_lane[4];
+  const int b3 = (ql >> 3) & 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int sw = 32 * (j ^ (q7 >> 1)) + 16 * (gq ^ (q7 & 1));
-    k_lane[j] = grp * TILE + ql * KROW + sw;
-    v_lane[j] = V_BASE + grp * TILE + ql * VROW + sw;
+    const int swv = 32 * (j ^ (q7 >> 1)) + 16 * (gq ^ (q7 & 1) ^ b3);
+    const int swk = DH == 128 ? 32 * (j ^ (q7 >> 1)) + 16 * (gq ^ (q7 & 1)) + 128 * b3 : swv;
+    k_lane[j] = grp * TILE + ql * KROW + swk;
+    v_lane[j] = V_BASE + grp * TILE + ql * VROW + swv;
   }
   // Steady-state step: SB = 0 for an iteration's first step (h = 2i + 1),
   // 1 for its second (h = 2i + 2); kb / vb are the lane bases of the
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
         fr[r] = *reinterpret_cast<const u32x4*>(smem + vb[2 * SB + p / DT] + (p % DT) * 32 * VROW);
       } else {
         const int ks = r >> 1;
-        fr[r] = *reinterpret_cast<const u32x4*>(smem + kb[ks & 3] + SB * 32 * KROW + 128 * (ks >> 2));
+        fr[r] = *reinterpret_cast<const u32x4*>(smem + (kb[ks & 3] ^ (128 * (ks >> 2))) + SB * 32 * KROW);
       }
     };
     f32x4 bb[4];
