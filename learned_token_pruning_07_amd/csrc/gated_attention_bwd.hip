@@ -106,11 +106,30 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
-// Byte offset, inside a staged [32 rows x DH] bf16 tile, of row r's 16-byte
-// chunk c (chunks swizzled by r & 7: conflict-free fragment reads).
+// Row r of a staged [32 rows x DH] bf16 tile holds its 16-byte chunk c at
+// position c ^ tile_swz(r).  gfx950 serves 16 lanes of an LDS read per
+// cycle from 64 four-byte banks (a 256-byte period), so a read is
+// conflict-free when those 16 lanes cover distinct banks.  The fragment
+// reads (16 rows, one chunk each) need tile_swz to be one-to-one on r mod 16
+// (on each parity of r for 128-byte rows); the transpose loads (4 rows x 32
+// bytes per 16 lanes) need tile_swz(r) >> 1 to differ within every aligned
+// group of 4 rows (of 2 same-parity rows for 128-byte rows).  r & 7 met
+// neither at DH = 128 (both reads conflicted 2-way).
+template <int DH>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (DH == 128) return ((r >> 2) & 1) | ((r & 3) << 1) | (r & 8);  // bits b2 b0 b1 b3
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
+// The byte-offset bit holding the chunk bit that row bit 3 flips (chunk bit
+// 3 at DH = 128, chunk bit 0 at DH = 64): rows r and r + 8 of the same lane
+// differ in their offsets by 8 rows and this bit.
+template <int DH>
+constexpr int kRow8Flip = DH == 128 ? 128 : 16;
+
+// Byte offset, inside a staged [32 rows x DH] bf16 tile, of row r's 16-byte chunk c.
 template <int DH>
 __device__ __forceinline__ int row_tile_off(int r, int c) {
-  return r * (2 * DH) + ((c ^ (r & 7)) << 4);
+  return r * (2 * DH) + ((c ^ tile_swz<DH>(r)) << 4);
 }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -126,7 +145,7 @@ __device__ __forceinline__ int tr_off(int blk, int s, int hf, int lane) {
   const int j = lane & 15, gq = lane >> 5;
   const int col = 32 * blk + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
   const int row = 16 * s + 8 * hf + 4 * gq + (j >> 2);
-  return row * (2 * DH) + (((col >> 3) ^ (row & 7)) << 4) + (((col >> 2) & 1) << 3);
+  return row * (2 * DH) + (((col >> 3) ^ tile_swz<DH>(row)) << 4) + (((col >> 2) & 1) << 3);
 }
 // the same fragment from precomputed offsets (tr_off of hf = 0 and 1)
 __device__ __forceinline__ bf16x8 tr_frag_at(const unsigned char* tile, int off0, int off1) {
@@ -156,13 +175,13 @@ __device__ __forceinline__ void wait_loads_le() {
 }
 
 // Stages `n` 1 KiB DMA loads of a [32 x DH] row-major tile: load e fills LDS
-// slots 64 e + lane, slot Y holding row Y / (DH/8), chunk (Y % (DH/8)) ^ (row & 7).
+// slots 64 e + lane, slot Y holding row Y / (DH/8), chunk (Y % (DH/8)) ^ tile_swz(row).
 template <int DH>
 __device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t r, unsigned char* tile, int row_bytes, int e,
                                            int lane) {
   constexpr int CH = DH / 8;
   const int Y = e * 64 + lane;
-  const int row = Y / CH, c = (Y % CH) ^ (row & 7);
+  const int row = Y / CH, c = (Y % CH) ^ tile_swz<DH>(row);
   dma16(r, tile + e * 1024, row * row_bytes + c * 16, 0);
 }
 
@@ -340,11 +359,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   for (int i = 0; i < G; ++i) cs[i] = ta[i] = 0.0f;
 
   // This lane's LDS offsets inside a staged tile, formed once: the swizzled
-  // chunk of fragment s is row_tile_off(kl, 2 s + gq) = rto[s & 3] + 128 (s >> 2),
-  // and the transpose loads of tr_frag sit at tro[blk & 1] + 128 (blk >> 1) +
-  // (16 s + 8 hf) 2 DH (the swizzle only sees the row's low 3 bits, which are
-  // the lane's own).  The empty asm statements keep them in registers rather
-  // than re-derived at every use.
+  // chunk of fragment s is row_tile_off(kl, 2 s + gq) = rto[s & 3] ^ 128 (s >> 2)
+  // (chunk bit 3 is offset bit 7, clear in rto), and the transpose loads of
+  // tr_frag sit at o = tro[blk & 1] + 128 (blk >> 1) + 16 s 2 DH for the first
+  // 8 rows and (o ^ kRow8Flip) + 8 2 DH for the next 8 (the swizzle sees only
+  // the row's low 4 bits: the lane's own, and bit 3 for the second 8 rows).
+  // The empty asm statements keep them in registers rather than re-derived
+  // at every use.
   int rto[4], tro[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -356,10 +377,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     tro[i] = tr_off<DH>(i, 0, 0, lane);
     asm volatile("" : "+v"(tro[i]));
   }
-  auto frag_off = [&](int s_) { return rto[s_ & 3] + 128 * (s_ >> 2); };
+  auto frag_off = [&](int s_) { return rto[s_ & 3] ^ (128 * (s_ >> 2)); };
   auto trf = [&](const unsigned char* tile, int blk, int s_) __attribute__((always_inline)) {
     const int o = tro[blk & 1] + 128 * (blk >> 1) + 16 * s_ * 2 * DH;
-    return tr_frag_at(tile, o, o + 8 * 2 * DH);
+    return tr_frag_at(tile, o, (o ^ kRow8Flip<DH>) + 8 * 2 * DH);
   };
 
   // One unit: S = Q K^T and dP = dO V^T, the softmax terms, then
@@ -624,7 +645,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) toff[blk][s][hf] = tr_off<DH>(blk, s, hf, lane);
-  int rto[4];  // row_tile_off(ql, 2 s + gq) = rto[s & 3] + 128 (s >> 2), formed once
+  int rto[4];  // row_tile_off(ql, 2 s + gq) = rto[s & 3] ^ 128 (s >> 2), formed once
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     rto[i] = row_tile_off<DH>(ql, 2 * i + gq);
@@ -638,7 +659,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
       bf16x8 fk[KS], fv[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int off = rto[s & 3] + 128 * (s >> 2);
+        const int off = rto[s & 3] ^ (128 * (s >> 2));
         fk[s] = lds_frag(base + off);
         fv[s] = lds_frag(base + TB + off);
       }
