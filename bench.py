@@ -578,7 +578,7 @@ PROFILE_RUN_FLAGS = "--no-cpu-baseline --no-sub-records --no-ceilings --no-varle
 PROFILE_CALLS = {
     "tg_gated_attention": ("gated_attention.hip",
                            ["attn_prepass_kernel<128, false, false>", "gated_attn_kernel<128, 2, false, false>"]),
-    "tg_gate_score_folded": ("gate_score.hip", ["gate_score_bf16_kernel<256, 128, 8, 32>"]),
+    "tg_gate_score_folded": ("gate_score.hip", ["gate_score_bf16_kernel<256, 128, 8, 32, false>"]),
     "tg_gate_select": ("gate_select.hip", ["gate_select_kernel", "compact_gather_kernel"]),
     "tg_gated_attention_backward": ("gated_attention_bwd.hip",
                                     ["bwd_rows_kernel<128>", "bwd_dkdv_kernel<128, 2, false>",
