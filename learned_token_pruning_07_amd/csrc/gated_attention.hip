@@ -1117,18 +1117,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   }  // the next block of this workgroup
 }
 
-// Compute units of the current device (cached per device).
-int device_cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 template <int DH, int G>
 hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int M, int Hq, int Hkv,
@@ -1192,6 +1180,19 @@ hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t*
 }
 
 }  // namespace
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // fp16 V^T [B, Hkv, dh, Mp], then the fp32 key-score rows [B, Hkv, G + 1, Mp]
 size_t gated_attention_workspace(int B, int M, int Hq, int Hkv, int dh) {

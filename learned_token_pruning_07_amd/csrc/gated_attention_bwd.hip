@@ -549,12 +549,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Query block of the idx-th dQ workgroup of a slab (n blocks, heaviest =
+// last): the first p (the CUs of an XCD, which dispatches the slab's first
+// p workgroups one per CU and the next p into the same CUs' second slots)
+// take the blocks heaviest first, the rest lightest first, so a CU's two
+// workgroups pair a heavy block with a light one.  A bijection of [0, n)
+// for any p >= 1.
+__device__ __forceinline__ int paired_block(int idx, int n, int p) {
+  return idx < p ? n - 1 - idx : idx - p;
+}
+
 template <int DH, int G, bool F32OUT>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ rowc, const float* __restrict__ rowl,
     const float* __restrict__ rowD, const float* __restrict__ kscore, const float* __restrict__ gain, int M_all,
-    int Mp_all, int Hq, int Hkv, int nqb, int total_wg, void* __restrict__ dq, const BwdSeqTable st) {
+    int Mp_all, int Hq, int Hkv, int nqb, int total_wg, int pair_p, void* __restrict__ dq, const BwdSeqTable st) {
   constexpr int RG = 4 / G;
   constexpr int BQ = 32 * RG;
   constexpr int KS = DH / 16, DT = DH / 32;
@@ -578,12 +588,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     Mp = (M + kPB - 1) / kPB * kPB;
     const int nq = (M + BQ - 1) / BQ, local = logical - st.qb0[sq];
     g = local / nq;
-    qb = nq - 1 - (local - g * nq);
+    qb = paired_block(local - g * nq, nq, pair_p);
     T0 = (size_t)st.t0[sq];
     P0 = (size_t)st.p0[sq];
   } else {
     const int bg = logical / nqb;
-    qb = nqb - 1 - (logical - bg * nqb);
+    qb = paired_block(logical - bg * nqb, nqb, pair_p);
     const int b = bg / Hkv;
     g = bg - b * Hkv;
     T0 = (size_t)b * M;
@@ -912,12 +922,13 @@ hipError_t launch_bwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          BwdSeqTable{});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int pair_p = std::max(1, device_cu_count() / 8);  // CUs of one XCD
     if (rope)
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, true>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq32, BwdSeqTable{});
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, pair_p, dq32, BwdSeqTable{});
     else
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3((unsigned)tb), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, dq, BwdSeqTable{});
+                         rowc, rowl, rowD, ks, gain, M, Mp, Hq, Hkv, nqb, (int)tb, pair_p, dq, BwdSeqTable{});
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (rope) {
@@ -964,12 +975,13 @@ hipError_t launch_bwd_varlen_t(const uint16_t* q, const uint16_t* k, const uint1
       hipLaunchKernelGGL((bwd_dkdv_kernel<DH, G, false>), dim3(ta), dim3(kBwdThreads), 0, s, q, k, v, dout, rowc,
                          rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, ta, dk, dv, dbp, gpart, tpart, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int pair_p = std::max(1, device_cu_count() / 8);  // CUs of one XCD
     if (dq32 != nullptr)
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, true>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq32, st);
+                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], pair_p, dq32, st);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<DH, G, false>), dim3(st.qb0[st.n]), dim3(kBwdThreads), 0, s, q, k, v, dout,
-                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], dq, st);
+                         rowc, rowl, rowD, ks, gain, 0, 0, Hq, Hkv, 0, st.qb0[st.n], pair_p, dq, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)(((size_t)nblk * kPB + kBwdThreads - 1) / kBwdThreads) + st.n;

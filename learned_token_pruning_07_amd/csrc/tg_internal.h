@@ -8,6 +8,9 @@
 
 namespace tg {
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 // Rows [r, p1) of each batch row are the prunable span (p1 = N for a prompt
 // [x_R, x_D]); every other row scores 0.
 // With span_begin/span_end (device [B] arrays) set, row b's span comes from
