@@ -632,8 +632,9 @@ static int attention_backward_varlen_common(const char* name, const void* q, con
     if (cu_seqlens[b + 1] < cu_seqlens[b]) return fail(TG_EINVAL, "%s: cu_seqlens must be non-decreasing", name);
   if ((size_t)cu_seqlens[B] + 63 * (size_t)B > 0x7FFFFFFF)
     return fail(TG_EINVAL, "%s: the padded rows exceed the 32-bit index range", name);
-  if (rope_base > 0.0 && (d_h != 64 && d_h != 128))
-    return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
+  if (Hq <= 0 || Hkv <= 0) return fail(TG_EINVAL, "%s: bad sizes", name);  // (before any size is derived from them)
+  if (Hq % Hkv != 0) return fail(TG_EINVAL, "%s: Hq=%d not a multiple of Hkv=%d", name, Hq, Hkv);
+  if (d_h != 64 && d_h != 128) return fail(TG_EUNSUPPORTED, "%s: d_h=%d not in {64,128}", name, d_h);
   // every sequence's row constants and partials sit side by side (then, for
   // the rotary variant, the rotated q and k and their fp32 gradients)
   const size_t need = rope_base > 0.0 && cu_seqlens[B] > 0

@@ -461,3 +461,25 @@ def test_gate_fused_validation(lib):
     assert call(ws=NULL, ws_bytes=0) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(ws_bytes=7) == tgb.TG_EINVAL and "workspace" in _err(lib)
     assert call(ws=FAKE_ODD) == tgb.TG_EINVAL and "misaligned" in _err(lib)
+
+
+def test_attention_backward_varlen_sizes_checked_before_the_workspace(lib):
+    """Bad head counts and d_h are reported as such, not as a workspace of
+    some size derived from them (both packed backward entry points)."""
+    cu = (ctypes.c_int32 * 3)(0, 100, 200)
+
+    def call(Hq, Hkv, dh, rope):
+        if rope:
+            return lib.tg_gated_attention_rope_backward_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, cu, Hq, Hkv, dh,
+                                                               FAKE, FAKE, FAKE, FAKE, 0.088, 1e6, FAKE, FAKE, FAKE,
+                                                               FAKE, FAKE, FAKE, NULL, 0, None)
+        return lib.tg_gated_attention_backward_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, cu, Hq, Hkv, dh, FAKE,
+                                                      FAKE, FAKE, FAKE, 0.088, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                      NULL, 0, None)
+
+    for rope in (False, True):
+        assert call(-16, 8, 128, rope) == tgb.TG_EINVAL and "bad sizes" in _err(lib)
+        assert call(16, 0, 128, rope) == tgb.TG_EINVAL and "bad sizes" in _err(lib)
+        assert call(16, 6, 128, rope) == tgb.TG_EINVAL and "multiple" in _err(lib)
+        assert call(16, 8, 96, rope) == tgb.TG_EUNSUPPORTED and "d_h" in _err(lib)
+        assert call(16, 8, 128, rope) == tgb.TG_EINVAL and "workspace" in _err(lib)
