@@ -100,8 +100,8 @@ __device__ __forceinline__ void gate_select_row(const float* score_raw, int N, i
   constexpr int kHeld = kHold ? PARTS : 1;
   f32x4 v[kVec * kHeld];
   auto load_part = [&](int s, f32x4* vs) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) vs[e] = sel::load_scores(x, (e * kThreads + tid + s * THREADS) * 4, N, r, p1, vec);
+    sel::load_score_groups<kVec>(vs, x, [&](int e) { return (e * kThreads + tid + s * THREADS) * 4; }, N, r, p1,
+                                 vec);
   };
   // normalised scores of part s out to y; its prunable keys to LDS with the first digit's histogram
   auto emit_part = [&](int s, const f32x4* vs, double scale) __attribute__((always_inline)) {
@@ -132,11 +132,8 @@ __device__ __forceinline__ void gate_select_row(const float* score_raw, int N, i
   };
   double scale;
   if constexpr (kHold) {
-#pragma unroll
-    for (int s = 0; s < PARTS; ++s)
-#pragma unroll
-      for (int e = 0; e < kVec; ++e)
-        v[s * kVec + e] = sel::load_scores(x, (e * kThreads + tid + s * THREADS) * 4, N, r, p1, vec);
+    sel::load_score_groups<PARTS * kVec>(
+        v, x, [&](int q) { return ((q % kVec) * kThreads + tid + (q / kVec) * THREADS) * 4; }, N, r, p1, vec);
     scale = sel::row_inv_rms<THREADS>(v, P, eps, L.part, L.scale);  // (its barriers order the clear above)
 #pragma unroll
     for (int s = 0; s < PARTS; ++s) emit_part(s, v + s * kVec, scale);
@@ -231,18 +228,31 @@ __device__ __forceinline__ void gate_select_row(const float* score_raw, int N, i
     for (int e = 0; e < kItems; ++e) packed[e >> 2] |= ((flags >> e) & 1u) << (8 * (e & 3));
     // one pair of stores per kept token of this thread, ranks dst, dst + 1, ...
     // (a loop over the set bits: the wave issues as many store rounds as its
-    // busiest lane has kept tokens, not one per item)
+    // busiest lane has kept tokens, not one per item).  The key holds the
+    // score exactly, except that -0.0 and +0.0 share a key and every NaN maps
+    // to key 0: those kept tokens are marked and re-read afterwards, outside
+    // this loop (a global load inside it made every round wait for the
+    // round's stores).
+    const uint32_t dst0 = dst;
+    uint32_t reread = 0;  // bit e: kept token j0 + e needs its exact score
     for (uint32_t f = flags; f != 0u; f &= f - 1u) {
       const int e = __builtin_ctz(f);
       if ((int)dst < lim) {  // exactly M tokens are kept; never write past the row
         const uint32_t key = s_keys[sel::key_slot(j0 + e)];
         ki[dst] = r + j0 + e;
-        // the key holds the score exactly, except that -0.0 and +0.0 share a
-        // key and every NaN maps to key 0: only those re-read the score
         const float from_key = sel::key_score(key);
-        sk[dst] = (key == 0u || from_key == 0.0f) ? y[r + j0 + e] : from_key;
+        sk[dst] = from_key;
+        reread |= (key == 0u || from_key == 0.0f) ? (1u << e) : 0u;
       }
       ++dst;
+    }
+    if (__ballot(reread != 0u) != 0) {  // (rare; wave-uniform)
+      uint32_t d = dst0;
+      for (uint32_t f = flags; f != 0u; f &= f - 1u) {
+        const int e = __builtin_ctz(f);
+        if ((reread >> e) & 1u) sk[d] = y[r + j0 + e];  // (d < lim: only such tokens were marked)
+        ++d;
+      }
     }
     if (vec_store && j0 + kItems <= P) {
       store16(kp + r + j0, u32x4{packed[0], packed[1], packed[2], packed[3]});

@@ -23,18 +23,37 @@ constexpr int kLdsKeys = 32768;
 constexpr int kLdsKeyWords = kLdsKeys + kLdsKeys / 16;
 __device__ __forceinline__ int key_slot(int j) { return j + (j >> 4); }
 
-// Four scores from x[j..j+3] (0 past N and below r).
-__device__ __forceinline__ f32x4 load_scores(const float* x, int j, int N, int r, int p1, bool vec) {
-  f32x4 v;
-  if (vec && j + 4 <= N) {
-    v = *reinterpret_cast<const f32x4*>(x + j);
+// NV groups of four scores, group e from x[jf(e) .. jf(e) + 3] (j a multiple
+// of 4; 0 outside [r, p1) and past N).  Every load is issued before any is
+// used: a row that is 16-byte aligned (`aligned`, from the caller) with
+// N % 4 == 0 takes one 16-byte load per group (a group past the row reads
+// the row's first group, then masked), any other row takes four clamped
+// 4-byte loads per group.  Loading one group at a time, with a branch per
+// group between the two forms and the mask right after, made the compiler
+// wait for each group's load before issuing the next.
+template <int NV, typename JF>
+__device__ __forceinline__ void load_score_groups(f32x4* v, const float* x, JF jf, int N, int r, int p1,
+                                                  bool aligned) {
+  if (aligned && (N & 3) == 0) {  // (wave-uniform)
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int j = jf(e);
+      v[e] = *reinterpret_cast<const f32x4*>(x + (j + 4 <= N ? j : 0));
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = j + i < N ? x[j + i] : 0.0f;
+    for (int e = 0; e < NV; ++e) {
+      const int j = jf(e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[e][i] = x[min(j + i, N - 1)];
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (j + i >= r && j + i < p1) ? v[i] : 0.0f;
-  return v;
+  for (int e = 0; e < NV; ++e) {
+    const int j = jf(e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[e][i] = (j + i >= r && j + i < p1 && j + i < N) ? v[e][i] : 0.0f;
+  }
 }
 
 // A workgroup of THREADS threads (a divisor of kRowThreads) stands in for

@@ -19,7 +19,6 @@
 namespace tg {
 namespace {
 
-using sel::load_scores;
 constexpr int kThreads = sel::kRowThreads;
 constexpr int kVec = sel::kRowVec;           // 16-byte loads per thread
 constexpr int kChunk = sel::kRowChunk;      // 32768 scores: the single-workgroup limit
@@ -38,8 +37,7 @@ __global__ __launch_bounds__(kThreads) void seq_rmsnorm_kernel(const float* in, 
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
 
   f32x4 v[kVec];
-#pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, (e * kThreads + tid) * 4, N, r, p1, vec);
+  sel::load_score_groups<kVec>(v, x, [&](int e) { return (e * kThreads + tid) * 4; }, N, r, p1, vec);
   const double scale = sel::row_inv_rms(v, p1 - r, eps, s_part, &s_scale);
 #pragma unroll
   for (int e = 0; e < kVec; ++e) {
@@ -87,8 +85,7 @@ __global__ __launch_bounds__(kSliceThreads) void seq_sumsq_kernel(const float* i
   const float* x = in + (size_t)b * N;
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
   f32x4 v[kVec];
-#pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, p1, vec);
+  sel::load_score_groups<kVec>(v, x, [&](int e) { return c0 + (e * kSliceThreads + tid) * 4; }, N, r, p1, vec);
   float part = 0.0f;
 #pragma unroll
   for (int e = 0; e < kVec; ++e)
@@ -117,8 +114,7 @@ __global__ __launch_bounds__(kSliceThreads) void seq_scale_kernel(const float* i
   float* y = out + (size_t)b * N;
   const bool vec = ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
   f32x4 v[kVec];
-#pragma unroll
-  for (int e = 0; e < kVec; ++e) v[e] = load_scores(x, c0 + (e * kSliceThreads + tid) * 4, N, r, p1, vec);
+  sel::load_score_groups<kVec>(v, x, [&](int e) { return c0 + (e * kSliceThreads + tid) * 4; }, N, r, p1, vec);
   double acc = 0.0;
   for (int c = tid; c < nblk; c += kSliceThreads) acc += partial[(size_t)b * nblk + c];
   const double t = block_sum_f64(acc, s_part);
