@@ -74,10 +74,12 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
   uint32_t flags = 0;  // bit e: token j0 + e is kept
   float sv[kScanItems];
 #pragma unroll
-  for (int e = 0; e < kScanItems; ++e) {
-    const int j = j0 + e;
-    flags |= (j < N && kp[j] != 0) ? (1u << e) : 0u;
-    sv[e] = j < N ? sc[j] : 0.0f;
+  for (int e = 0; e < kScanItems; ++e) {  // (clamped, unconditional loads: masked ones would each be waited for)
+    const int j = j0 + e, jc = min(j, N - 1);
+    const uint8_t kv = kp[jc];
+    const float x = sc[jc];
+    flags |= (j < N && kv != 0) ? (1u << e) : 0u;
+    sv[e] = j < N ? x : 0.0f;
   }
 
   // ones before this chunk; every load of a batch is issued before any is used
@@ -89,8 +91,11 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
 #pragma unroll
       for (int u = 0; u < kCountUnroll; ++u) {
         const int q = q0 + u * kScanThreads + tid;
-        w[u] = q < n16 ? load16(kp + (size_t)q * 16) : u32x4{0, 0, 0, 0};
+        w[u] = load16(kp + (size_t)min(q, n16 - 1) * 16);  // (q0 < n16, so n16 >= 1)
       }
+#pragma unroll
+      for (int u = 0; u < kCountUnroll; ++u)
+        if (q0 + u * kScanThreads + tid >= n16) w[u] = u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < kCountUnroll; ++u)
         cnt += nonzero_bytes(w[u][0]) + nonzero_bytes(w[u][1]) + nonzero_bytes(w[u][2]) + nonzero_bytes(w[u][3]);

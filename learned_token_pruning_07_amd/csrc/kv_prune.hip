@@ -41,13 +41,17 @@ __global__ __launch_bounds__(kThreads) void kv_prune_kernel(const uint8_t* __res
   for (int i = 0; i < kRowsPerWave; ++i) jrow[i] = m0 + i < M ? ki[m0 + i] : -1;
   for (int c0 = 0; c0 < cpr; c0 += 64 * kMaxCpl) {
     u32x4 v[kRowsPerWave][kMaxCpl];
+    // every load is issued unconditionally (a row or chunk that is not moved
+    // reads the cache's first chunk instead, and its store is skipped): a
+    // masked load per chunk made the compiler wait for each before the next
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const bool ok = (uint32_t)jrow[i] < (uint32_t)N;  // an index outside [0, N) leaves its row unwritten
+      const size_t row_off = ok ? (size_t)jrow[i] * row_bytes : 0;
 #pragma unroll
       for (int c = 0; c < kMaxCpl; ++c) {
         const int ch = c0 + c * 64 + lane;
-        if (ok && ch < cpr) v[i][c] = load16_stream(src + (size_t)jrow[i] * row_bytes + (size_t)ch * 16);
+        v[i][c] = load16_stream(src + row_off + (size_t)(ch < cpr ? ch : 0) * 16);
       }
     }
 #pragma unroll

@@ -163,8 +163,11 @@ __device__ __forceinline__ void chunk_keys(const float* sc, int P, int j0, uint3
       for (int e = 0; e < 4; ++e) key[q * 4 + e] = order_key(__uint_as_float(w[e]));
     }
   } else {
+    float x[kMItems];  // clamped, unconditional loads, all issued before any is used
 #pragma unroll
-    for (int e = 0; e < kMItems; ++e) key[e] = j0 + e < P ? order_key(sc[j0 + e]) : 0u;
+    for (int e = 0; e < kMItems; ++e) x[e] = sc[min(j0 + e, P - 1)];
+#pragma unroll
+    for (int e = 0; e < kMItems; ++e) key[e] = j0 + e < P ? order_key(x[e]) : 0u;
   }
 }
 
