@@ -193,6 +193,16 @@ __device__ __forceinline__ f32x4* rope_tab_piece(float* tab, size_t slot, int i0
   return reinterpret_cast<f32x4*>(tab) + ((slot >> 5) * (DH / 32) + ks) * 4 * 64 + gq * 32 + (slot & 31);
 }
 
+// One prepass workgroup per 64-key block: DH threads, thread t owning the 8
+// d values 8 (t mod DH/8) .. + 7 of the 8 keys whose V^T slots form chunk
+// t / (DH/8) of the block's rows (keys 16 n + 4 v + {0..3, 8..11}, n = chunk / 2,
+// v = chunk mod 2, in slot order).  Its 8 loads read those keys' 16-byte
+// pieces (DH/8 consecutive lanes read one whole row), and the transposition
+// to V^T rows happens in registers: word p of its piece of row d packs the
+// keys of slots 8 chunk + 2p and + 1.
+template <int DH>
+constexpr int kPreThreads = DH;
+
 // Prepass, per 64-key block of KV head g:
 //   e = the block's scale exponent: 141 - (exponent field of the largest
 //   bf16 magnitude), clamped to [kVExpMin, kVExpMax], so that the largest
@@ -210,17 +220,19 @@ __device__ __forceinline__ f32x4* rope_tab_piece(float* tab, size_t slot, int i0
 //   its fp32 sine and cosine are accurate to a few ulp at any position.
 // VARLEN: the blocks of the table's sequences, one grid row per KV head.
 template <int DH, bool ROPE, bool VARLEN>
-__global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* __restrict__ v,
-                                                                const float* __restrict__ key_score,
-                                                                const float* __restrict__ gain, int M_all,
-                                                                int Mp_all, int Hkv, int G,
-                                                                uint16_t* __restrict__ vt,
-                                                                float* __restrict__ kbias, RopeArgs ra,
-                                                                const SeqTable st,
-                                                                const int32_t* __restrict__ m_dev) {
-  __shared__ uint16_t sT[DH][kBK + 2];
+__global__ __launch_bounds__(kPreThreads<DH>) void attn_prepass_kernel(const uint16_t* __restrict__ v,
+                                                                       const float* __restrict__ key_score,
+                                                                       const float* __restrict__ gain, int M_all,
+                                                                       int Mp_all, int Hkv, int G,
+                                                                       uint16_t* __restrict__ vt,
+                                                                       float* __restrict__ kbias, RopeArgs ra,
+                                                                       const SeqTable st,
+                                                                       const int32_t* __restrict__ m_dev) {
+  constexpr int kT = kPreThreads<DH>;
+  constexpr int kNW = kT / 64;
+  static_assert(kT % 64 == 0 && kBK == 64, "prepass layout");
   __shared__ double s_freq[DH / 2];
-  __shared__ uint32_t s_mag[kThreads / 64];
+  __shared__ uint32_t s_mag[kNW];
   const int g = blockIdx.y;
   int m0, M, Mp;
   size_t T0, P0;  // first packed row and first padded key slot of this sequence
@@ -243,66 +255,72 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     P0 = (size_t)blockIdx.z * Mp;
   }
   const int tid = threadIdx.x;
-  if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);  // (ordered by the barriers below)
-  constexpr int NL = kBK * DH / 8 / kThreads;  // 16-byte loads per thread, all issued before any use
-  u32x4 w[NL];
+  if (ROPE && tid < DH / 2) s_freq[tid] = rope::inv_freq(ra.base, tid, DH);
+  constexpr int CPR = DH / 8;       // 16-byte pieces per row
+  const int dc = tid % CPR;         // this thread's d values: 8 dc .. 8 dc + 7
+  const int ch = tid / CPR;         // its chunk of the block's V^T rows (slots 8 ch .. 8 ch + 7)
+  const int kbase = 16 * (ch >> 1) + 4 * (ch & 1);
+  auto key_of = [&](int j) { return kbase + (j & 3) + 8 * (j >> 2); };  // key in slot 8 ch + j
+  // The block's rows of head g through a range-checked resource that ends
+  // with row M - 1: a key at or past M reads zeros, with no select.
+  const int nvalid = min(M - m0, kBK);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(v + ((T0 + m0) * Hkv + g) * DH), (short)0, ((nvalid - 1) * Hkv + 1) * DH * 2,
+      kBufferConfig);
+  u32x4 w[8];
 #pragma unroll
-  for (int e = 0; e < NL; ++e) {
-    const int c = tid + e * kThreads;
-    const int key = c / (DH / 8), part = c % (DH / 8);
-    const int m = m0 + key;
-    w[e] = m < M ? load16(v + ((T0 + m) * Hkv + g) * DH + part * 8) : u32x4{0, 0, 0, 0};
-  }
+  for (int j = 0; j < 8; ++j)
+    w[j] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, key_of(j) * Hkv * DH * 2 + dc * 16, 0, 0));
+  // The key-score rows: value c of the block is row c / 64, key m0 + c mod 64;
+  // thread t writes c = t + u kT, all of key mk.  Its key score and gains are
+  // requested with the V loads (clamped in-bounds, masked later), so that
+  // nothing waits on a load once the scale is known.  (G <= 4.)
+  constexpr int kKbIt = (5 * kBK + kT - 1) / kT;
+  const int mk = m0 + (tid & (kBK - 1));
+  const float ksv = key_score[T0 + min(mk, M - 1)];
+  float gk[kKbIt];
+#pragma unroll
+  for (int u = 0; u < kKbIt; ++u) gk[u] = gain[g * G + min((tid + u * kT) / kBK, G - 1)];
   // the block's largest bf16 magnitude (sign cleared; NaN and inf compare
-  // above every finite value), as an integer max over the bit patterns: one
-  // value per wave here, combined after the transpose's barrier
+  // above every finite value), as an integer max over the bit patterns
   uint32_t mag = 0;
 #pragma unroll
-  for (int e = 0; e < NL; ++e)
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mag = max(mag, max(w[e][i] & 0x7FFFu, (w[e][i] >> 16) & 0x7FFFu));
+    for (int i = 0; i < 4; ++i) mag = max(mag, max(w[j][i] & 0x7FFFu, (w[j][i] >> 16) & 0x7FFFu));
+  mag = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max_u32(mag), 63);
+  if constexpr (kNW > 1) {
+    if ((tid & 63) == 0) s_mag[tid >> 6] = mag;
+    __syncthreads();
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mag = max(mag, (uint32_t)__shfl_xor((int)mag, off, 64));
-  if ((tid & 63) == 0) s_mag[tid >> 6] = mag;
-  // transpose the raw bf16 block through LDS; the conversion happens on the
-  // way out, once the block's scale is known
-#pragma unroll
-  for (int e = 0; e < NL; ++e) {
-    const int c = tid + e * kThreads;
-    const int key = c / (DH / 8), part = c % (DH / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sT[part * 8 + 2 * i][key] = (uint16_t)(w[e][i] & 0xFFFFu);
-      sT[part * 8 + 2 * i + 1][key] = (uint16_t)(w[e][i] >> 16);
-    }
+    for (int wv = 0; wv < kNW; ++wv) mag = max(mag, s_mag[wv]);
   }
-  __syncthreads();
-#pragma unroll
-  for (int wv = 0; wv < kThreads / 64; ++wv) mag = max(mag, s_mag[wv]);
   const int ex = min(max(141 - (int)(mag >> 7), kVExpMin), kVExpMax);
   const float scale = __uint_as_float((uint32_t)(ex + 127) << 23);  // 2^ex, exact
-  const int Hq = Hkv * G;
-  const size_t kb_row = P0 * (size_t)(Hq + Hkv) + (size_t)g * (G + 1) * Mp;
-  for (int c = tid; c < (G + 1) * kBK; c += kThreads) {
-    const int hh = c / kBK, m = m0 + c % kBK;
-    float val = scale;
-    if (hh < G) val = m < M ? fmaf(key_score[T0 + m], gain[g * G + hh] * kLog2e, (float)-ex) : 0.0f;
-    kbias[kb_row + (size_t)hh * Mp + m] = val;
-  }
   // fp16 V 2^ex, round to nearest even: exact for every value within 2^28
-  // below the block's largest
-  auto to_f16 = [&](uint16_t lo, uint16_t hi) {
-    return pack_f16x2(__uint_as_float((uint32_t)lo << 16) * scale, __uint_as_float((uint32_t)hi << 16) * scale);
-  };
-  for (int c = tid; c < DH * (kBK / 8); c += kThreads) {
-    const int d = c / (kBK / 8), kc = c % (kBK / 8);
+  // below the block's largest.  Row 8 dc + i, word p: keys of slots 8 ch + 2p, + 1.
+  uint16_t* vt_row = vt + P0 * Hkv * DH + ((size_t)g * DH + dc * 8) * Mp + m0 + ch * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
     u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = to_f16(sT[d][vt_slot_key(kc * 8 + 2 * i)], sT[d][vt_slot_key(kc * 8 + 2 * i + 1)]);
-    store16(vt + P0 * Hkv * DH + ((size_t)g * DH + d) * Mp + m0 + kc * 8, o);
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = w[2 * p][i >> 1], b = w[2 * p + 1][i >> 1];
+      o[p] = (i & 1) ? pack_f16x2(bf16_hi(a) * scale, bf16_hi(b) * scale)
+                     : pack_f16x2(bf16_lo(a) * scale, bf16_lo(b) * scale);
+    }
+    store16(vt_row + (size_t)i * Mp, o);
+  }
+  const int Hq = Hkv * G;
+  float* kb = kbias + P0 * (size_t)(Hq + Hkv) + (size_t)g * (G + 1) * Mp + mk;
+#pragma unroll
+  for (int u = 0; u < kKbIt; ++u) {
+    const int hh = (tid + u * kT) / kBK;
+    if (hh <= G) kb[(size_t)hh * Mp] = hh == G ? scale : (mk < M ? fmaf(ksv, gk[u] * kLog2e, (float)-ex) : 0.0f);
   }
   if constexpr (ROPE) {
+    __syncthreads();  // s_freq is written
     // The angles of a row are formed once, by one of the Hkv blocks of its
     // 64-key block (rows g R .. g R + R - 1, R = ceil(64 / Hkv)), which then
     // turns that row's K for every KV head and writes its table row; up to
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
     const int r_hi = min(kBK, (g + 1) * R);
     for (int c0 = g * R; c0 < r_hi; c0 += kRopeRows) {  // (block-uniform)
       const int nr = min(kRopeRows, r_hi - c0);
-      for (int t = tid; t < nr * PG; t += kThreads) {
+      for (int t = tid; t < nr * PG; t += kT) {
         const int rr = t / PG, i0 = (t % PG) * 8, m = m0 + c0 + rr;
         // the table holds pairs i0 .. i0 + 7 of slot P0 + m as 4 pieces (the
         // padding slots past M hold zeros: their queries turn into 0)
@@ -332,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void attn_prepass_kernel(const uint16_t* 
       }
       __syncthreads();
       // consecutive threads: the 16-byte pieces of one row's heads, in memory order
-      for (int t = tid; t < nr * PG * Hkv; t += kThreads) {
+      for (int t = tid; t < nr * PG * Hkv; t += kT) {
         const int i0 = (t % PG) * 8, gg = (t / PG) % Hkv, rr = t / (PG * Hkv), m = m0 + c0 + rr;
         if (m >= M) continue;
         float c[8], sn[8];
@@ -1126,11 +1144,11 @@ hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   constexpr int BQ = 32 * (4 / G);
   const int Mp = (M + kBK - 1) / kBK * kBK;
   if (rope != nullptr) {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, false>), dim3(Mp / kBK, Hkv, B), dim3(kPreThreads<DH>), 0, s, v, ks,
                        gain, M, Mp, Hkv, G, vt, kbias, *rope, SeqTable{}, m_dev);
     k = rope->kr;  // the main kernel reads the rotated k and rotates its Q fragments itself
   } else {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, false>), dim3(Mp / kBK, Hkv, B), dim3(kThreads), 0, s, v, ks,
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, false>), dim3(Mp / kBK, Hkv, B), dim3(kPreThreads<DH>), 0, s, v, ks,
                        gain, M, Mp, Hkv, G, vt, kbias, RopeArgs{}, SeqTable{}, m_dev);
   }
   hipError_t e = hipGetLastError();
@@ -1159,11 +1177,11 @@ hipError_t launch_varlen_t(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float sm_scale, uint16_t* out, float* lse, uint16_t* vt, float* kbias,
                            const RopeArgs* rope, hipStream_t s) {
   if (rope != nullptr) {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads),
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, true, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kPreThreads<DH>),
                        0, s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, *rope, st, nullptr);
     k = rope->kr;
   } else {
-    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kThreads),
+    hipLaunchKernelGGL((attn_prepass_kernel<DH, false, true>), dim3((unsigned)st.pb0[st.n], Hkv, 1), dim3(kPreThreads<DH>),
                        0, s, v, ks, gain, 0, 0, Hkv, G, vt, kbias, RopeArgs{}, st, nullptr);
   }
   hipError_t e = hipGetLastError();

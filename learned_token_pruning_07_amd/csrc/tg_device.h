@@ -86,6 +86,20 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
   return x;
 }
 
+// Running maximum over the 64 lanes of a wave, on the same DPP lane moves
+// (lanes shifted in from outside a row read 0, the identity): lane 63 ends
+// with the wave's maximum.
+__device__ __forceinline__ uint32_t wave_incl_max_u32(uint32_t x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 1, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 2, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 4, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowShr + 8, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast15, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kRowBcast31, 0xC, 0xF, false));
+  return x;
+}
+
 // Exclusive prefix sum over a whole block of NW waves (blockDim.x == 64 NW,
 // NW a multiple of 4, at most 16).  `s_wave` holds NW words of LDS, 16-byte
 // aligned.  Returns the exclusive prefix of `v`; `total` receives the block
