@@ -641,29 +641,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   auto h_mine = [&](int h) { return h >= 0 && grp + kGroups * (h >> 1) < nkb && wave_rows && h_key0(h) <= rbase + 31; };
 
   // S^T = K Q^T of half h: one 32 x 32 accumulation chain over DH
+  // (Every fragment read of qk and pv is issued before the first product:
+  // read-then-use per product left one LDS latency exposed per MFMA in the
+  // steps outside the steady loop.)
   auto qk = [&](int h, f32x16& s) __attribute__((always_inline)) {
     const unsigned char* kt = k_tile((h >> 1) & 1) + (h & 1) * 32 * KROW;
+    bf16x8 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(ka[ks]));  // all reads issued, then one wait
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + k_frag_off(ks));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-    }
+    for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s, 0, 0, 0);
   };
   // O^T += V^T P^T over the two 16-key steps of half h
   auto pv = [&](int h, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
     const unsigned char* vt_l = v_tile((h >> 1) & 1);
+    u32x4 vw[2][DT];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+        vw[sh][t] = *reinterpret_cast<const u32x4*>(vt_l + t * 32 * VROW + v_frag_off((h & 1) * 2 + sh));
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(vw[sh][t]));
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
       const u32x4 pw = {pk[sh * 4], pk[sh * 4 + 1], pk[sh * 4 + 2], pk[sh * 4 + 3]};
       const f16x8 pf = as_f16x8(pw);
-      const int st = (h & 1) * 2 + sh;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(vt_l + t * 32 * VROW + v_frag_off(st));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw), pf, o[t], 0, 0, 0);
-      }
+      for (int t = 0; t < DT; ++t) o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vw[sh][t]), pf, o[t], 0, 0, 0);
     }
   };
   // Online softmax of half h's scores, without branches: the running max
