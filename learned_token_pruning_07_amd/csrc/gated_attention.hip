@@ -320,17 +320,36 @@ __global__ __launch_bounds__(kPreThreads<DH>) void attn_prepass_kernel(const uin
     if (hh <= G) kb[(size_t)hh * Mp] = hh == G ? scale : (mk < M ? fmaf(ksv, gk[u] * kLog2e, (float)-ex) : 0.0f);
   }
   if constexpr (ROPE) {
-    __syncthreads();  // s_freq is written
     // The angles of a row are formed once, by one of the Hkv blocks of its
     // 64-key block (rows g R .. g R + R - 1, R = ceil(64 / Hkv)), which then
     // turns that row's K for every KV head and writes its table row; up to
-    // kRopeRows rows at a time, their (cos, sin) pairs in LDS.
+    // kRopeRows rows at a time, their (cos, sin) pairs in LDS.  Item t of a
+    // pass is pairs 8 (t mod PG) .. + 7 of row t / (PG Hkv), head
+    // (t / PG) mod Hkv (consecutive threads: one row's heads in memory
+    // order).  A thread's first kIt items of a pass request their K pieces
+    // before the angles are formed (clamped to row M - 1; rows at or past M
+    // are skipped), so that the loads overlap that work.
     constexpr int PG = DH / 2 / 8;  // groups of 8 pairs per head row
+    constexpr int kIt = 4;
     __shared__ f32x2 s_cs[kRopeRows][DH / 2];
     const int R = (kBK + Hkv - 1) / Hkv;
     const int r_hi = min(kBK, (g + 1) * R);
+    __syncthreads();  // s_freq is written
     for (int c0 = g * R; c0 < r_hi; c0 += kRopeRows) {  // (block-uniform)
       const int nr = min(kRopeRows, r_hi - c0);
+      const int n_items = nr * PG * Hkv;
+      u32x4 ka[kIt], kp[kIt];
+      auto item_row = [&](int t) { return ((T0 + min(m0 + c0 + t / (PG * Hkv), M - 1)) * Hkv + (t / PG) % Hkv) * DH; };
+      auto load_items = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kIt; ++u) {
+          const int t = t0 + u * kT, i0 = (t % PG) * 8;
+          const uint16_t* src = ra.k + item_row(t);
+          ka[u] = load16(src + i0);
+          kp[u] = load16(src + DH / 2 + i0);
+        }
+      };
+      load_items(tid);
       for (int t = tid; t < nr * PG; t += kT) {
         const int rr = t / PG, i0 = (t % PG) * 8, m = m0 + c0 + rr;
         // the table holds pairs i0 .. i0 + 7 of slot P0 + m as 4 pieces (the
@@ -349,19 +368,21 @@ __global__ __launch_bounds__(kPreThreads<DH>) void attn_prepass_kernel(const uin
         for (int i = 0; i < 8; ++i) s_cs[rr][i0 + i] = f32x2{c[i], sn[i]};
       }
       __syncthreads();
-      // consecutive threads: the 16-byte pieces of one row's heads, in memory order
-      for (int t = tid; t < nr * PG * Hkv; t += kT) {
-        const int i0 = (t % PG) * 8, gg = (t / PG) % Hkv, rr = t / (PG * Hkv), m = m0 + c0 + rr;
-        if (m >= M) continue;
-        float c[8], sn[8];
+      for (int t0 = tid; t0 < n_items; t0 += kIt * kT) {
+        if (t0 != tid) load_items(t0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const f32x2 cs = s_cs[rr][i0 + i];
-          c[i] = cs[0];
-          sn[i] = cs[1];
+        for (int u = 0; u < kIt; ++u) {
+          const int t = t0 + u * kT, i0 = (t % PG) * 8, rr = t / (PG * Hkv);
+          if (t >= n_items || m0 + c0 + rr >= M) continue;
+          float c[8], sn[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const f32x2 cs = s_cs[rr][i0 + i];
+            c[i] = cs[0];
+            sn[i] = cs[1];
+          }
+          rope::row8_rotate<DH>(ka[u], kp[u], ra.kr + item_row(t), i0, c, sn);
         }
-        const size_t krow = ((T0 + m) * Hkv + gg) * DH;
-        rope::row8<DH>(ra.k + krow, ra.kr + krow, i0, c, sn);
       }
       __syncthreads();  // (before the next rows' pairs overwrite LDS)
     }

@@ -34,11 +34,12 @@ __device__ __forceinline__ double inv_freq(double base, int i, int DH) {
 // Rotates one head row, pairs i = i0 .. i0 + 7, by the angles whose cosines
 // and sines are c[], s[] (fp32, products fused), rounding to bf16 (nearest
 // even).
+// row8_rotate takes the two 16-byte pieces already loaded: a = pairs' first
+// elements x_{i0..i0+7}, bv = their partners x_{DH/2+i0..}.
 template <int DH>
-__device__ __forceinline__ void row8(const uint16_t* src, uint16_t* dst, int i0, const float (&c)[8],
-                                     const float (&s)[8]) {
+__device__ __forceinline__ void row8_rotate(u32x4 a, u32x4 bv, uint16_t* dst, int i0, const float (&c)[8],
+                                            const float (&s)[8]) {
   constexpr int HALF = DH / 2;
-  const u32x4 a = load16(src + i0), bv = load16(src + HALF + i0);
   u32x4 oa, ob;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -49,6 +50,11 @@ __device__ __forceinline__ void row8(const uint16_t* src, uint16_t* dst, int i0,
   }
   store16(dst + i0, oa);
   store16(dst + HALF + i0, ob);
+}
+template <int DH>
+__device__ __forceinline__ void row8(const uint16_t* src, uint16_t* dst, int i0, const float (&c)[8],
+                                     const float (&s)[8]) {
+  row8_rotate<DH>(load16(src + i0), load16(src + DH / 2 + i0), dst, i0, c, s);
 }
 
 // The transposed rotation of a gradient row (fp32 in, bf16 out): for the
