@@ -1037,6 +1037,33 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
 #pragma unroll
     for (int e = 0; e < 16; ++e) sb[e] -= cm[e];
   }
+  // The next block's schedule and the offsets of its Q fragments and
+  // position (scalar reads from the argument segment), taken before the
+  // tail iterations so that their latency passes under them; the loads
+  // themselves wait until this block's last scores are computed.
+  // Unconditional loads through a range-checked resource: a row past the
+  // kept length (or no next block) reads zeros, with no select.  The
+  // fragments then load straight into the registers they live in; a
+  // conditional load (zero default, then a masked load) made the compiler
+  // copy them over and wait for the loads, which exposed their whole
+  // latency at every block transition.
+  __amdgpu_buffer_rsrc_t q_rsrc_n;
+  int q_off_n = 0;
+  const int32_t* pos_n = nullptr;
+  bool has_next = false;
+  if constexpr (!VARLEN) {
+    AttnArgsPtr an = args_seg;
+    asm volatile("" : "+s"(an));
+    int b_n = 0, g_n = 0, qb_n = 0, M_n = 0;
+    has_next = sched_block<BQ>(an, round + 1, b_n, g_n, qb_n, M_n) == 2;
+    const int qi_n = qb_n * BQ + (wid % RG) * 32 + ql;
+    const bool ok = has_next && qi_n < M_n;
+    pos_n = an->pos + (size_t)b_n * an->M_all + (ok ? qi_n : 0);
+    const uint16_t* qbase = an->q + (size_t)b_n * an->M_all * an->Hq * DH;
+    q_rsrc_n = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qbase), (short)0,
+                                                 (int)((size_t)M_n * an->Hq * DH * 2), kBufferConfig);
+    q_off_n = ok ? (int)(((size_t)qi_n * an->Hq + g_n * G + hloc) * DH * 2 + gq * 16) : (int)0x7FFFFFF0;
+  }
   for (; i < nit; ++i) {
     stage(i);
     step(2 * i + 1, sb, sa, pb, pa);
@@ -1046,30 +1073,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void gated_attn_kernel(const AttnA
   }
   TG_DIAG_STAMP(5);
   if constexpr (!VARLEN) {
-    // request the next block's Q fragments and positions now (this block's
+    // request the next block's Q fragments and position now (this block's
     // scores are all done, so its Q fragments are free): they land while the
     // groups merge, the output is written and the next block sets up
-    AttnArgsPtr an = args_seg;
-    asm volatile("" : "+s"(an));
-    int b_n = 0, g_n = 0, qb_n = 0, M_n = 0;
-    const bool has_next = sched_block<BQ>(an, round + 1, b_n, g_n, qb_n, M_n) == 2;
-    // unconditional loads through a range-checked resource: a row past the
-    // kept length (or no next block) reads zeros, with no select.  The
-    // fragments then load straight into the registers they live in; a
-    // conditional load (zero default, then a masked load) made the compiler
-    // copy them over and wait for the loads right here, which exposed their
-    // whole latency at every block transition
-    const int qi_n = qb_n * BQ + (wid % RG) * 32 + ql;
-    const bool ok = has_next && qi_n < M_n;
-    const size_t row = (size_t)b_n * an->M_all + (ok ? qi_n : 0);
-    const uint16_t* qbase = an->q + (size_t)b_n * an->M_all * an->Hq * DH;
-    const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(qbase), (short)0, (int)((size_t)M_n * an->Hq * DH * 2), kBufferConfig);
-    const int q_off = ok ? (int)(((size_t)qi_n * an->Hq + g_n * G + hloc) * DH * 2 + gq * 16) : (int)0x7FFFFFF0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = as_bf16x8(__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_off, ks * 32, 0)));
-    p_pre = an->pos[row];
+      qf[ks] = as_bf16x8(
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc_n, q_off_n, ks * 32, 0)));
+    p_pre = *pos_n;
     pre_round = has_next ? round + 1 : -1;
   }
   // Merge the two groups' online-softmax states (the tile buffers are free
