@@ -109,6 +109,43 @@ __device__ __forceinline__ void gate_select_row(const float* score_raw, int N, i
     for (int e = 0; e < kVec; ++e) {
       const int j = (e * kThreads + tid + s * THREADS) * 4;
       const f32x4 vv = vs[e];
+      // Three wave-uniform cases for the wave's 64 groups of this e (scores
+      // jw .. jw + 255): none in the prunable span (zeros out, no keys); all
+      // in it with r % 4 == 0, so that a group's 4 key slots are consecutive
+      // (straight-line form); otherwise the masked form below, whose
+      // per-score branches cost exec mask saves and restores.
+      const int jw = (e * kThreads + (tid & ~63) + s * THREADS) * 4;
+      if (jw >= p1 || jw + 256 <= r) {
+        if (jw < N) {
+          if (vec && j + 4 <= N) {
+            *reinterpret_cast<f32x4*>(y + j) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (j + i < N) y[j + i] = 0.0f;
+          }
+        }
+        continue;
+      }
+      if ((r & 3) == 0 && jw >= r && jw + 256 <= p1) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (float)((double)vv[i] * scale);
+        if (vec) {
+          *reinterpret_cast<f32x4*>(y + j) = o;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) y[j + i] = o[i];
+        }
+        const int slot = sel::key_slot(j - r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t key = sel::order_key(o[i]);
+          s_keys[slot + i] = key;
+          atomicAdd(&s_hist[key >> 21], 1u);
+        }
+        continue;
+      }
       f32x4 o;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // exactly 0 outside the span, also when the scale is not finite

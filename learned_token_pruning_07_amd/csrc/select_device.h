@@ -121,11 +121,13 @@ __device__ __forceinline__ double row_inv_rms(const f32x4 (&v)[kRowVec * kRowPar
 
 // Order-preserving key: larger score -> larger key; -0.0 folds onto +0.0;
 // every NaN maps to key 0, below -inf (whose key is 0x007FFFFF).
+// (Branch-free: a positive score sets the top bit, a negative one flips
+// every bit; -0.0 would land at 0x7FFFFFFF, just below +0.0's 0x80000000.)
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
-  if (u == 0x80000000u) u = 0u;                      // -0.0 -> +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f);
+  uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  k = k == 0x7FFFFFFFu ? 0x80000000u : k;  // -0.0 -> +0.0
+  return f != f ? 0u : k;                  // NaN
 }
 
 // The score of a key (the inverse of order_key for every non-NaN score other
