@@ -233,30 +233,33 @@ __device__ __forceinline__ void gate_select_row(const float* score_raw, int N, i
   uint32_t out_base = r;  // kept tokens before the current chunk
   for (int c0 = 0; c0 < P; c0 += THREADS * kItems) {
     const int j0 = c0 + tid * kItems;
-    uint32_t keys[kItems];
-    uint32_t n_eq = 0;
+    // This thread's keys, read unconditionally (items past P read key P - 1
+    // and are masked off), compared to T as bit masks: conditional reads made
+    // the compiler wait for each read before the next, and per-item branches
+    // cost exec-mask saves and restores.
+    const int nv = min(max(P - j0, 0), kItems);
+    const uint32_t vmask = (1u << nv) - 1u;
+    uint32_t gtm = 0, eqm = 0;  // bit e: key of token j0 + e is > T, == T
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
-      const int j = j0 + e;
-      keys[e] = j < P ? s_keys[sel::key_slot(j)] : 0u;
-      n_eq += (j < P && keys[e] == T) ? 1u : 0u;
+      const uint32_t key = s_keys[sel::key_slot(min(j0 + e, P - 1))];
+      gtm |= (key > T ? 1u : 0u) << e;
+      eqm |= (key == T ? 1u : 0u) << e;
     }
-    uint32_t eq_tot = 0, rank = 0;
-    if (!all_ties) rank = eq_base + block_excl_scan_u32<THREADS / 64>(n_eq, s_wave, eq_tot);  // (block-uniform branch)
-    uint32_t flags = 0;  // bit e: token j0 + e is kept
+    gtm &= vmask;
+    eqm &= vmask;
+    uint32_t eq_tot = 0;
+    uint32_t flags = gtm | eqm;  // bit e: token j0 + e is kept
+    if (!all_ties) {             // (block-uniform) only the first k_eq keys equal to T, in index order
+      uint32_t rank = eq_base + block_excl_scan_u32<THREADS / 64>(__builtin_popcount(eqm), s_wave, eq_tot);
+      uint32_t keep_eq = 0;
 #pragma unroll
-    for (int e = 0; e < kItems; ++e) {
-      const int j = j0 + e;
-      bool kept = false;
-      if (j < P) {
-        if (keys[e] > T) {
-          kept = true;
-        } else if (keys[e] == T) {
-          kept = all_ties || rank < k_eq;
-          ++rank;
-        }
+      for (int e = 0; e < kItems; ++e) {
+        const uint32_t b = (eqm >> e) & 1u;
+        keep_eq |= (b & (rank < k_eq ? 1u : 0u)) << e;
+        rank += b;
       }
-      flags |= kept ? (1u << e) : 0u;
+      flags = gtm | keep_eq;
     }
     uint32_t tot;
     uint32_t dst = out_base + block_excl_scan_u32<THREADS / 64>(__builtin_popcount(flags), s_wave, tot);

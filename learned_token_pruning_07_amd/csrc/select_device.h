@@ -148,10 +148,21 @@ struct Threshold {
 // s_hist holds the histogram of digit [31:21] of all P keys (2048 bins).
 // s_wave holds 16 words, s_sel 3.  Contains barriers.  Integer counting
 // only: the threshold does not depend on THREADS.
+// Thread t owns keys t + q THREADS.  The second pass reads all of them and
+// marks in a bit mask (bit q) those whose first digit is the selected one;
+// the third pass re-reads only the marked keys, the only ones that can
+// carry the selected 22-bit prefix (a few percent of the keys for spread-out
+// scores), instead of all P again.
 template <int THREADS = kRowThreads>
 __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, int P, uint32_t Kp, uint32_t* s_hist,
                                                       uint32_t* s_wave, uint32_t* s_sel) {
   const int tid = threadIdx.x;
+  constexpr int kBatch = 8;
+  constexpr int kBatches = (kLdsKeys + kBatch * THREADS - 1) / (kBatch * THREADS);
+  constexpr int kMaskWords = (kBatches * kBatch + 31) / 32;
+  uint32_t marked[kMaskWords];
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) marked[w] = 0u;
   uint32_t prefix = 0, pmask = 0, krem = Kp;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
@@ -160,10 +171,14 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
     if (pass > 0) {
       for (int i = tid; i < nb; i += THREADS) s_hist[i] = 0;
       __syncthreads();
+    }
+    if (pass == 1) {
       // batches of kBatch keys per thread: every LDS read of a batch is issued
       // before any is tested
-      constexpr int kBatch = 8;
-      for (int j0 = tid; j0 < P; j0 += kBatch * THREADS) {
+#pragma unroll
+      for (int bt = 0; bt < kBatches; ++bt) {
+        const int j0 = tid + bt * kBatch * THREADS;
+        if (bt * kBatch * THREADS >= P) break;  // (block-uniform)
         uint32_t key[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -171,10 +186,20 @@ __device__ __forceinline__ Threshold radix_select_lds(const uint32_t* s_keys, in
           key[u] = j < P ? s_keys[key_slot(j)] : 0u;
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-          if (j0 + u * THREADS < P && (key[u] & pmask) == prefix)
-            atomicAdd(&s_hist[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+        for (int u = 0; u < kBatch; ++u) {
+          const bool hit = j0 + u * THREADS < P && (key[u] & pmask) == prefix;
+          if (hit) atomicAdd(&s_hist[(key[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+          const int q = bt * kBatch + u;
+          marked[q >> 5] |= (hit ? 1u : 0u) << (q & 31);
+        }
       }
+    } else if (pass == 2) {
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w)
+        for (uint32_t f = marked[w]; f != 0u; f &= f - 1u) {
+          const uint32_t key = s_keys[key_slot(tid + (w * 32 + __builtin_ctz(f)) * THREADS)];
+          if ((key & pmask) == prefix) atomicAdd(&s_hist[key & (uint32_t)(nb - 1)], 1u);
+        }
     }
     __syncthreads();
     // Bins in descending digit order; thread t owns descending bins
