@@ -11,7 +11,9 @@
 //    writes, in ascending original order, kept_idx[m] = j and
 //    score_out[m] = score[j].
 //  * compact_gather: a streaming 16-byte row copy resid_out[m] = resid[kept_idx[m]],
-//    the HBM-bound part (2 * M * row_bytes).
+//    the HBM-bound part (2 * M * row_bytes), a wave per kGatherRowsPerWave
+//    kept rows (row_gather.h).
+#include "row_gather.h"
 #include "tg_device.h"
 #include "tg_internal.h"
 
@@ -23,7 +25,7 @@ constexpr int kScanItems = 8;                             // consecutive tokens 
 constexpr int kScanChunk = kScanThreads * kScanItems;     // tokens per workgroup
 constexpr int kCountUnroll = 8;                           // 16-byte mask loads in flight per thread
 constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 4;
+constexpr int kGatherRowsPerBlock = (kGatherThreads / 64) * kGatherRowsPerWave;
 
 // number of non-zero bytes of a 32-bit word
 __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
@@ -119,77 +121,35 @@ __global__ __launch_bounds__(kScanThreads) void compact_scan_kernel(const uint8_
   }
 }
 
-// One thread copies kGatherUnroll 16-byte chunks spaced kGatherThreads apart;
-// chunk c of batch row b covers kept row c / cpr, part c % cpr.
+// Batch row b: kept rows m0 .. m0 + kGatherRowsPerWave - 1 per wave.
 __global__ __launch_bounds__(kGatherThreads) void compact_gather_kernel(const uint8_t* __restrict__ resid,
                                                                         size_t row_bytes, int N, int M,
                                                                         const int32_t* __restrict__ kept_idx,
                                                                         uint8_t* __restrict__ out) {
   const int b = blockIdx.y;
-  const size_t cpr = row_bytes / 16;
-  const size_t total = (size_t)M * cpr;
-  const int32_t* ki = kept_idx + (size_t)b * M;
-  const uint8_t* src = resid + (size_t)b * N * row_bytes;
-  uint8_t* dst = out + (size_t)b * M * row_bytes;
-  const size_t c0 = (size_t)blockIdx.x * kGatherThreads * kGatherUnroll + threadIdx.x;
-  u32x4 v[kGatherUnroll];
-  size_t off_out[kGatherUnroll];
-  bool ok[kGatherUnroll];
-#pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    const size_t c = c0 + (size_t)u * kGatherThreads;
-    ok[u] = c < total;
-    if (ok[u]) {
-      const size_t m = c / cpr, part = c - m * cpr;
-      const int32_t j = ki[m];
-      // a keep mask with fewer ones than M leaves kept_idx entries unwritten;
-      // never follow an index outside [0, N)
-      ok[u] = (uint32_t)j < (uint32_t)N;
-      if (ok[u]) v[u] = load16_stream(src + (size_t)j * row_bytes + part * 16);
-      off_out[u] = m * row_bytes + part * 16;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    if (ok[u]) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + off_out[u]));
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = (blockIdx.x * (kGatherThreads / 64) + wave) * kGatherRowsPerWave;
+  if (m0 >= M) return;
+  // (a keep mask with fewer ones than M leaves kept_idx entries unwritten;
+  // the gather never follows an index outside [0, N))
+  gather_rows_wave(resid + (size_t)b * N * row_bytes, out + (size_t)b * M * row_bytes, row_bytes, N, M,
+                   kept_idx + (size_t)b * M, m0, lane);
 }
 
 // Packed rows of varying count: batch row b owns output rows
-// [cu_kept[b], cu_kept[b + 1]); chunk c of row b covers its kept row c / cpr.
-// With count set instead (pad rows per batch row), batch row b owns output
-// rows [b pad, b pad + count[b]).
+// [cu_kept[b], cu_kept[b + 1]).  With count set instead (pad rows per batch
+// row), batch row b owns output rows [b pad, b pad + count[b]).
 __global__ __launch_bounds__(kGatherThreads) void compact_gather_varlen_kernel(
     const uint8_t* __restrict__ resid, size_t row_bytes, int N, const int32_t* __restrict__ cu_kept,
     const int32_t* __restrict__ count, int pad, const int32_t* __restrict__ kept_idx, uint8_t* __restrict__ out) {
   const int b = blockIdx.y;
-  const size_t cpr = row_bytes / 16;
   const int o0 = count != nullptr ? b * pad : cu_kept[b];
   const int Mb = count != nullptr ? min(max(count[b], 0), pad) : cu_kept[b + 1] - o0;
-  const size_t total = Mb > 0 ? (size_t)Mb * cpr : 0;
-  const int32_t* ki = kept_idx + o0;
-  const uint8_t* src = resid + (size_t)b * N * row_bytes;
-  uint8_t* dst = out + (size_t)o0 * row_bytes;
-  const size_t c0 = (size_t)blockIdx.x * kGatherThreads * kGatherUnroll + threadIdx.x;
-  u32x4 v[kGatherUnroll];
-  size_t off_out[kGatherUnroll];
-  bool ok[kGatherUnroll];
-#pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    const size_t c = c0 + (size_t)u * kGatherThreads;
-    ok[u] = o0 >= 0 && c < total;
-    if (ok[u]) {
-      const size_t m = c / cpr, part = c - m * cpr;
-      const int32_t j = ki[m];
-      ok[u] = (uint32_t)j < (uint32_t)N;
-      if (ok[u]) v[u] = load16_stream(src + (size_t)j * row_bytes + part * 16);
-      off_out[u] = m * row_bytes + part * 16;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kGatherUnroll; ++u) {
-    if (ok[u]) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst + off_out[u]));
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = (blockIdx.x * (kGatherThreads / 64) + wave) * kGatherRowsPerWave;
+  if (o0 < 0 || m0 >= Mb) return;
+  gather_rows_wave(resid + (size_t)b * N * row_bytes, out + (size_t)o0 * row_bytes, row_bytes, N, Mb,
+                   kept_idx + o0, m0, lane);
 }
 
 }  // namespace
@@ -197,9 +157,7 @@ __global__ __launch_bounds__(kGatherThreads) void compact_gather_varlen_kernel(
 hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int N, int M,
                                  const int32_t* kept_idx, void* resid_out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  const size_t total = (size_t)M * (row_bytes / 16);
-  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
-  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  const unsigned grid = (unsigned)(((size_t)M + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
   hipLaunchKernelGGL(compact_gather_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
                      reinterpret_cast<const uint8_t*>(resid), row_bytes, N, M, kept_idx,
                      reinterpret_cast<uint8_t*>(resid_out));
@@ -209,9 +167,7 @@ hipError_t launch_compact_gather(const void* resid, size_t row_bytes, int B, int
 hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int B, int N, const int32_t* cu_kept,
                                         int max_kept, const int32_t* kept_idx, void* resid_out, hipStream_t s) {
   if (max_kept <= 0) return hipSuccess;
-  const size_t total = (size_t)max_kept * (row_bytes / 16);
-  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
-  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  const unsigned grid = (unsigned)(((size_t)max_kept + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
   hipLaunchKernelGGL(compact_gather_varlen_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
                      reinterpret_cast<const uint8_t*>(resid), row_bytes, N, cu_kept, nullptr, 0, kept_idx,
                      reinterpret_cast<uint8_t*>(resid_out));
@@ -221,9 +177,7 @@ hipError_t launch_compact_gather_varlen(const void* resid, size_t row_bytes, int
 hipError_t launch_compact_gather_padded(const void* resid, size_t row_bytes, int B, int N, const int32_t* count,
                                         int pad, const int32_t* kept_idx, void* resid_out, hipStream_t s) {
   if (pad <= 0) return hipSuccess;
-  const size_t total = (size_t)pad * (row_bytes / 16);
-  const size_t per_block = (size_t)kGatherThreads * kGatherUnroll;
-  const unsigned grid = (unsigned)((total + per_block - 1) / per_block);
+  const unsigned grid = (unsigned)(((size_t)pad + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
   hipLaunchKernelGGL(compact_gather_varlen_kernel, dim3(grid, B), dim3(kGatherThreads), 0, s,
                      reinterpret_cast<const uint8_t*>(resid), row_bytes, N, nullptr, count, pad, kept_idx,
                      reinterpret_cast<uint8_t*>(resid_out));
