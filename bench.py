@@ -51,17 +51,33 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# every source a call's kernels are compiled from, beyond its own file
+PROFILE_DEPS = {
+    "gated_attention.hip": ["rope_device.h", "tg_device.h"],
+    "gate_score.hip": ["gate_select_row.h", "select_device.h", "row_gather.h", "compact.hip", "tg_device.h"],
+    "gate_select.hip": ["gate_select_row.h", "select_device.h", "row_gather.h", "compact.hip", "tg_device.h"],
+    "gated_attention_bwd.hip": ["rope_device.h", "tg_device.h"],
+    "kv_prune.hip": ["row_gather.h", "tg_device.h"],
+}
+
+
+def _sources_sha(kernel_file: str):
+    """sha256 over the kernel file and the sources it depends on."""
+    d = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc")
+    files = [kernel_file] + PROFILE_DEPS.get(kernel_file, [])
+    return hashlib.sha256("".join(_sha(os.path.join(d, f)) for f in files).encode()).hexdigest()
+
+
 def _traffic(kernel_file: str):
     """HBM bytes per launch from committed rocprofv3 --pmc counters, if they
-    were taken on the current source of the kernel; else None."""
+    were taken on the current sources of the kernel; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         t = json.load(open(p))
-        src = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc", kernel_file)
         ent = t.get(kernel_file)
-        if not ent or ent.get("source_sha256") != _sha(src):
+        if not ent or ent.get("sources_sha256") != _sources_sha(kernel_file):
             return None
         return float(ent["bytes_per_launch"])
     except Exception:
@@ -696,7 +712,7 @@ def summarize_profiles(run_dir: str):
     fscale = nbytes / (cf[copy_k[0]] * 1024)  # bytes moved per KiB of counter
     wscale = nbytes / (cw[copy_k[0]] * 1024)
     algo = stage_algorithmic_bytes()
-    srcdir = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc")
+    srcdir = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc")  # noqa: F841
     t = {"calibration": {"copy_bytes": nbytes, "fetch_kib_read": cf[copy_k[0]], "write_kib_read": cw[copy_k[0]],
                          "fetch_scale": fscale, "write_scale": wscale},
          "commands": [cmds[k].format(dir="<dir>") for k in ("fetch", "write", "copy_fetch", "copy_write")],
@@ -722,7 +738,7 @@ def summarize_profiles(run_dir: str):
                      f"(ratio {tot / algo[call]:.3f})")
         t[src] = {"call": call, "kernels": ks, "bytes_per_launch": tot, "algorithmic_bytes": algo[call],
                   "fetch_kib": {k: fetch[k] for k in ks}, "write_kib": {k: write[k] for k in ks},
-                  "source_sha256": _sha(os.path.join(srcdir, src))}
+                  "sources": [src] + PROFILE_DEPS.get(src, []), "sources_sha256": _sources_sha(src)}
     open(os.path.join(prof, "hbm_traffic_stage_32k.txt"), "w").write("\n".join(lines) + "\n")
     json.dump(t, open(os.path.join(prof, "traffic.json"), "w"), indent=1)
     print("\n".join(lines))
