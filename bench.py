@@ -712,7 +712,6 @@ def summarize_profiles(run_dir: str):
     fscale = nbytes / (cf[copy_k[0]] * 1024)  # bytes moved per KiB of counter
     wscale = nbytes / (cw[copy_k[0]] * 1024)
     algo = stage_algorithmic_bytes()
-    srcdir = os.path.join(ROOT, "learned_token_pruning_07_amd", "csrc")  # noqa: F841
     t = {"calibration": {"copy_bytes": nbytes, "fetch_kib_read": cf[copy_k[0]], "write_kib_read": cw[copy_k[0]],
                          "fetch_scale": fscale, "write_scale": wscale},
          "commands": [cmds[k].format(dir="<dir>") for k in ("fetch", "write", "copy_fetch", "copy_write")],
