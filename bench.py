@@ -741,6 +741,52 @@ def summarize_profiles(run_dir: str):
     open(os.path.join(prof, "hbm_traffic_stage_32k.txt"), "w").write("\n".join(lines) + "\n")
     json.dump(t, open(os.path.join(prof, "traffic.json"), "w"), indent=1)
     print("\n".join(lines))
+    bench_line = os.path.join(run_dir, "bench.json")
+    if os.path.exists(bench_line):
+        summarize_bench_line(bench_line, os.path.join(prof, "bench_stage_32k.txt"))
+
+
+def summarize_bench_line(path: str, dst: str):
+    """profiles/bench_stage_32k.txt: the figures of one default bench.py line
+    (the step, per-call times, roofline, the measured ceilings, the other
+    lengths and the CPU oracle), from `python3 bench.py > <dir>/bench.json`."""
+    d = json.loads(open(path).read().strip().splitlines()[-1])
+    L = [f"# bench.py line: {d['config'].get('workload')} on one MI355X", "",
+         "Command (repository root):", "    python3 bench.py > <dir>/bench.json",
+         "    python3 bench.py --summarize-profiles <dir>   (writes this file)", "",
+         f"{d['metric']}", f"value {d['value']:.4g} {d['unit']}; {d['ms_per_step']:.4f} ms per step "
+         f"({d['steps']} steps after {d['warmup']} warm-up, dtype {d['dtype']})", "",
+         f"{'call':24s} {'us/call':>9s} {'per step':>9s} {'HBM frac':>9s} {'MFMA frac':>10s}"]
+    for k, v in d["kernels"].items():
+        L.append(f"{k:24s} {v['avg_us']:9.2f} {v['launches_per_step']:9d} {v.get('hbm_frac', 0):9.3f} "
+                 f"{v.get('mfma_frac', 0):10.3f}")
+    r = d["roofline"]
+    L += ["", f"roofline ({r['kernel']}, {r['bound']}): {r['achieved']:.1f} of {r['peak']:.0f} {r['unit']} = "
+          f"{r['frac']:.4f} of the spec peak; {r.get('frac_of_measured_ceiling', 0):.4f} of the measured bf16 GEMM "
+          f"rate; counter traffic {r['traffic'] / 1e6 if r.get('traffic') else float('nan'):.2f} MB per call"]
+    c = d.get("ceilings")
+    if c:
+        L += ["", "measured ceilings (same box, same run):",
+              f"  device copy of 1 GiB: {c['copy_GBs']:.0f} GB/s = {c['copy_frac_of_spec']:.3f} of 8 TB/s",
+              f"  bf16 GEMM {c['gemm_shape']} through torch (hipBLASLt): {c['gemm_bf16_TFLOPs']:.0f} TFLOP/s = "
+              f"{c['gemm_bf16_frac_of_spec']:.3f} of 2.5 PFLOP/s",
+              f"  the scorer's product {c['scorer_gemm_shape']} as a library GEMM: {c['scorer_gemm_library_us']:.2f} us "
+              f"({c['scorer_gemm_residual_GBs']:.0f} GB/s of residual)"]
+    for name, rec in (d.get("sub_records") or {}).items():
+        L.append("")
+        for b in rec.get("budgets", [rec]):
+            L.append(f"{name} N={rec['N']} M={b['M']}: {b['ms_per_step'] * 1000:.1f} us per step, "
+                     f"{b['tokens_per_s'] / 1e6:.1f} M tokens/s; score {b['gate_score_us']:.1f} us "
+                     f"({b['gate_score_hbm_frac']:.3f} HBM), selection {b['gate_select_us']:.1f} us"
+                     + (f", attention {b['attention_us']:.1f} us ({b['attention_mfma_frac']:.3f} MFMA)"
+                        if "attention_us" in b else ""))
+    cb = d.get("cpu_baseline")
+    if cb:
+        st = cb.get("single_thread", {})
+        L += ["", f"CPU oracle ({cb.get('cpu_model')}, {cb['cores']} threads): {cb['value']:.0f} {cb['unit']}; "
+              f"one thread: {st.get('value', float('nan')):.0f}", f"  sample: {cb['sample']}"]
+    open(dst, "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
 
 
 def main():

@@ -230,28 +230,39 @@ __global__ __launch_bounds__(64 * WAVES) void gate_score_bf16_kernel(const uint1
         const u32x4 (&bcur)[2][CT] = wb[j % kWDepth];
         if (c + kWDepth - 1 < nch) load_b(c + kWDepth - 1, wb[(j + kWDepth - 1) % kWDepth]);
         if (c + kDepth < nch) load_a(c + kDepth, ra[j % kDepth]);
+        bf16x8 af[2][RT], gf[2][GR];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 af[RT];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
-            af[rt] = *reinterpret_cast<const bf16x8*>(
+            af[ks][rt] = *reinterpret_cast<const bf16x8*>(
                 &sA[buf][(rt * 16 + (lane & 15)) * kLda + (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
+#pragma unroll
+          for (int i = 0; i < GR; ++i)
+            gf[ks][i] = *reinterpret_cast<const bf16x8*>(
+                &sA[buf][((wid + WAVES * i) * 16 + (lane & 15)) * kLda + (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
-              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], as_bf16x8(bcur[ks][ct]), acc[rt][ct],
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][rt], as_bf16x8(bcur[ks][ct]), acc[rt][ct],
                                                                     0, 0, 0);
           // Gram tile of this wave's rows: its diagonal is the rows' sum of squares
 #pragma unroll
-          for (int i = 0; i < GR; ++i) {
-            const bf16x8 gf = *reinterpret_cast<const bf16x8*>(
-                &sA[buf][((wid + WAVES * i) * 16 + (lane & 15)) * kLda + (((ks * 4 + (lane >> 4)) ^ (lane & 7)) * 8)]);
-            gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf, gf, gram[i], 0, 0, 0);
-          }
+          for (int i = 0; i < GR; ++i) gram[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(gf[ks][i], gf[ks][i], gram[i], 0, 0, 0);
         }
         if (more) store_a(buf ^ 1, ra[(j + 1) % kDepth]);
+        // Fixed issue order per chunk: the global loads, then every fragment
+        // reads, then the products (each waits only for its own fragments),
+        // then the LDS stores.  Left to itself the compiler read one fragment
+        // just before the two products that use it and waited for it there.
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * CT + AL, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RT + GR), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * (RT * CT + GR), 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, AL, 0);
         __syncthreads();
       }
     }
