@@ -81,10 +81,53 @@ def main():
             {"pos": [0, 3], "O": [10.0, (10 + 40 * se) / (1 + 2 * se)], "lse": [1.0, 0.5 + math.log(1 + 2 * se)]},
         ],
     }
+    rope = rope_worked()
     for name, obj in [("score_worked", score), ("seqnorm_worked", seq), ("topk_worked", topk),
-                      ("attention_worked", attn)]:
+                      ("attention_worked", attn), ("rope_attention_worked", rope)]:
         with open(os.path.join(HERE, name + ".json"), "w") as f:
             json.dump(obj, f, indent=1)
+
+
+def rope_worked():
+    """Rotary attention at the original positions, d_h = 2 (one pair, angle pos
+    radians at any base), through the relative-angle identity."""
+    q = [[1.0, 0.0], [2.0, 1.0], [0.0, 2.0]]
+    k = [[1.0, 1.0], [1.0, -1.0], [2.0, 0.0]]
+    v = [[1.0, 0.0], [0.0, 1.0], [3.0, -2.0]]
+    b = [0.0, 1.0, -1.0]
+    pos = [0, 2, 5]
+    gain = 0.5
+
+    def s_rel(a, c, delta):
+        # q_i R(pos_i) . k_j R(pos_j) = (a.c) cos(delta) + (a2 c1 - a1 c2) sin(delta), delta = pos_j - pos_i
+        return (a[0] * c[0] + a[1] * c[1]) * math.cos(delta) + (a[1] * c[0] - a[0] * c[1]) * math.sin(delta)
+
+    O, lse = [], []
+    for i in range(3):
+        ratio = 1.0 if pos[i] == i else math.log(max(pos[i] + 1, 2)) / math.log(max(i + 1, 2))
+        z = [s_rel(q[i], k[j], pos[j] - pos[i]) / ratio + gain * b[j] for j in range(i + 1)]
+        mx = max(z)
+        w = [math.exp(x - mx) for x in z]
+        tot = sum(w)
+        O.append([sum(w[j] * v[j][c] for j in range(i + 1)) / tot for c in range(2)])
+        lse.append(mx + math.log(tot))
+    return {
+        "source": "TokenGate paper, Appendix C.4 (kept tokens keep their original positions for the position "
+                  "encoding) with Section 4, Eq. 8 and the Eq. 7 log-ratio reading; rotate-half rotary embedding "
+                  "(pair (x_i, x_{i + d/2}) turned by pos * base^(-2i/d)).",
+        "derivation": [
+            "One head, d_h = 2: the single pair turns by pos radians (base^0 = 1), so the base does not matter.",
+            "R(t) (x1, x2) = (x1 cos t - x2 sin t, x2 cos t + x1 sin t); R(a)^T R(b) = R(b - a), so "
+            "R(p_i) q . R(p_j) k = (q.k) cos(p_j - p_i) + (q2 k1 - q1 k2) sin(p_j - p_i).",
+            "z_ij = that product * sm_scale / (temp * ratio_i) + gain * b_j with sm_scale = temp = 1, gain = 0.5; "
+            "ratio_0 = 1 (pos 0 = rank 0), ratio_1 = ln 3 / ln 2, ratio_2 = ln 6 / ln 3.",
+            "O_i = sum_j softmax_j(z_i) v_j and lse_i = ln sum_j exp z_ij over j <= i.",
+            "The oracle rounds the rotated q and k to bf16 (relative error <= 2^-9 per element): with |q|, |k| <= "
+            "2.3 every logit moves by at most ~0.02, so O and lse agree to 0.05.",
+        ],
+        "q": q, "k": k, "v": v, "b": b, "pos": pos, "gain": gain, "base": 10000.0, "tol": 0.05,
+        "O": O, "lse": lse,
+    }
 
 
 if __name__ == "__main__":

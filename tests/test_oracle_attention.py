@@ -212,3 +212,27 @@ def test_rope_attention_at_position_zero_equals_plain():
     O2, L2 = oracle.gated_attention(c.q, c.k, c.v, b, zeros, c.gain, c.temp, c.sm_scale)
     np.testing.assert_array_equal(O1, O2)
     np.testing.assert_array_equal(L1, L2)
+
+
+def test_rope_attention_worked_example():
+    """Rotary attention at sparse original positions against a hand-derived
+    closed form (d_h = 2), within the bf16 rounding of the rotated q and k;
+    the same inputs rotated the wrong way, or by rank instead of position,
+    land far outside that bound."""
+    g = json.load(open(os.path.join(GOLD, "rope_attention_worked.json")))
+    q = np.array(g["q"], np.float32).reshape(1, 3, 1, 2)
+    k = np.array(g["k"], np.float32).reshape(1, 3, 1, 2)
+    v = np.array(g["v"], np.float32).reshape(1, 3, 1, 2)
+    b = np.array([g["b"]], np.float64)
+    pos = np.array([g["pos"]], np.int32)
+    gain, one = np.full(1, g["gain"]), np.ones(1)
+    O, L = oracle.gated_attention_rope(q, k, v, b, pos, gain, one, 1.0, g["base"])
+    np.testing.assert_allclose(O[0, :, 0, :], g["O"], rtol=0, atol=g["tol"])
+    np.testing.assert_allclose(L[0, 0], g["lse"], rtol=0, atol=g["tol"])
+    # teeth: negated angles (the transposed rotation) and rank-based angles miss by far more
+    for wrong in (-pos, np.broadcast_to(np.arange(3, dtype=np.int32), (1, 3))):
+        qr = oracle.bf16_round(oracle.rope(q, wrong, g["base"]))
+        kr = oracle.bf16_round(oracle.rope(k, wrong, g["base"]))
+        Ow, Lw = oracle.gated_attention(qr, kr, v, b, pos, gain, one, 1.0)
+        assert np.abs(Ow[0, :, 0, :] - np.array(g["O"])).max() > 4 * g["tol"] or \
+            np.abs(Lw[0, 0] - np.array(g["lse"])).max() > 4 * g["tol"]
