@@ -744,6 +744,37 @@ def summarize_profiles(run_dir: str):
     bench_line = os.path.join(run_dir, "bench.json")
     if os.path.exists(bench_line):
         summarize_bench_line(bench_line, os.path.join(prof, "bench_stage_32k.txt"))
+    for name, (wflags, what) in OTHER_TRACES.items():
+        if os.path.isdir(os.path.join(run_dir, "trace_" + name)):
+            summarize_other_trace(run_dir, name, wflags, what, prof)
+
+
+# kernel traces at the metric's other lengths: directory suffix -> (bench.py workload flags, description)
+OTHER_TRACES = {
+    "gate_16k": ("--workload gate_16k", "gate_16k (N=16384, r=64, K=1638 -> M=1702, d=2048, h=256): "
+                                        "scorer and fused selection"),
+    "sweep_128k_f25": ("--workload sweep_128k --frac 0.25",
+                       "sweep_128k at a 25 % budget (N=131072, r=128, K=32736 -> M=32864, d=2048, h=256; "
+                       "one gated attention layer, 16q/8kv, d_h 128)"),
+}
+
+
+def summarize_other_trace(run_dir: str, name: str, wflags: str, what: str, prof: str):
+    """profiles/kernel_trace_<name>.txt from a rocprofv3 kernel trace of that workload."""
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/trace_{name} -o run -- "
+           f"python3 bench.py {wflags} --steps 5 --warmup 2 {PROFILE_RUN_FLAGS} --no-backward --no-kv-prune")
+    stats = _csv_rows(os.path.join(run_dir, "trace_" + name), "kernel_stats.csv")
+    lines = [f"# Kernel trace: {what}", "", "Commands (repository root, one MI355X):", "    " + cmd,
+             "    python3 bench.py --summarize-profiles <dir>   (writes this file)", "",
+             "rocprofv3 --stats summary (durations in microseconds); __amd_rocclr_*, at::native and Cijk_* kernels",
+             "are torch copies, fills, draws and the Q/K/V projection glue of the set-up, outside the timed step.", "",
+             f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total%':>7s}"]
+    for r in stats:
+        k = _short_kernel(r["Name"])
+        lines.append(f"{k[:58]:58s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} {float(r['Percentage']):7.2f}")
+    open(os.path.join(prof, f"kernel_trace_{name}.txt"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_bench_line(path: str, dst: str):
